@@ -1,0 +1,384 @@
+// fastweight.hpp -- gfx950 kernels for the SwiGLU fast weight f(x) = (silu(x W0) * (x W2)) W1
+// (row-vector form; bias free). Shared by the LaCT layer and its linear-attention form.
+//
+// Stored layouts (per (sequence, head) pair, operand type OpT):
+//   W0T, W2T [rh][H]  -- W0, W2 transposed: row j holds the input weights of hidden unit j
+//   W1       [rh][H]  -- row j holds the output weights of hidden unit j
+//   W1T      [H][rh]
+// Token tensors are [pair][N][H] in the I/O type, step sizes [pair][N] float.
+//
+// grad_kernel: for a token range of one chunk and a block of 64 hidden units, computes the
+// positive partial sums
+//     P0 = K^T X0,  P1 = (eta*H)^T V,  P2 = K^T X2   (stored transposed as [j][c])
+// with A = K W0, Bm = K W2, D = eta * (V W1^T), H = silu(A)*Bm, X0 = D*Bm*silu'(A),
+// X2 = D*silu(A). The loss -sum eta <f(k), v> has gradients G0 = -P0, G1 = -P1, G2 = -P2
+// ("Test-Time Training Done Right" notes, section 2.2; the chain rule through the SwiGLU).
+// In linear-attention mode only P1 = phi(K)^T diag(eta) V is formed (the chunk aggregate of
+// the scan form; KV-binding summary page, "Prerequisites -> Linear attention").
+// Every hidden unit j only touches column j of W0/W2 and row j of W1, so hidden-unit blocks
+// are independent; token ranges are summed afterwards in a fixed order.
+//
+// apply_kernel: O = (silu(Q W0) * (Q W2)) W1 for a tile of 64 query tokens, streaming the
+// hidden dimension in blocks of 64.
+#pragma once
+#include "common.hpp"
+
+namespace ttt {
+
+constexpr int RB = 64;   // hidden units per block
+constexpr int TT = 64;   // tokens per tile
+constexpr int NWAVE = 4; // waves per workgroup (256 threads)
+
+template <class T> struct Pad { static constexpr int v = 16 / sizeof(T); };  // 16-byte row pad
+
+// Load one K-step fragment of a token row from global memory, converting to the operand type.
+template <class IoT, class OpT> struct FragIo;
+template <class OpT> struct FragIo<bf16_t, OpT> {
+  __device__ __forceinline__ static typename Mfma<OpT>::frag load(const bf16_t* p) {
+    u16x8 v = *reinterpret_cast<const u16x8*>(p);
+    typename Mfma<OpT>::frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = Mfma<OpT>::from_f32(bf16_to_f32(v[e]));
+    return f;
+  }
+};
+template <> struct FragIo<float, float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+};
+
+template <class OpT> __device__ __forceinline__ typename Mfma<OpT>::frag zero_frag() {
+  typename Mfma<OpT>::frag f;
+  if constexpr (Mfma<OpT>::KSUB == 1) {
+    f = 0.f;
+  } else {
+#pragma unroll
+    for (int e = 0; e < Mfma<OpT>::KSUB; ++e) f[e] = Mfma<OpT>::from_f32(0.f);
+  }
+  return f;
+}
+
+template <class OpT> __device__ __forceinline__ OpT frag_elem(const typename Mfma<OpT>::frag& f, int e) {
+  if constexpr (Mfma<OpT>::KSUB == 1) {
+    return f;
+  } else {
+    return f[e];
+  }
+}
+
+struct GradArgs {
+  const void* K;          // [pair][N][H] I/O type
+  const void* V;
+  const float* eta;       // [pair][N]
+  int64_t tok_pair_stride;   // elements between pairs in K/V (= N*H)
+  int64_t eta_pair_stride;   // (= N)
+  int t_base;             // first token of the region (chunk start)
+  int seg_len;            // tokens per grid.y segment
+  int t_limit;            // one past the last token of the region
+  const void* W0T;        // [rh][H] operand type, per pair
+  const void* W2T;
+  const void* W1;
+  int64_t w_pair_stride;  // elements between pairs of the shadows
+  int rh;
+  float* out;             // partial sums, fp32
+  int64_t out_y_stride;   // between grid.y segments
+  int64_t out_pair_stride;
+  int64_t out_mat_stride; // between P0 / P1 / P2 (= rh*H)
+};
+
+// LDS bytes of grad_kernel<OpT, H, LINATTN>.
+template <class OpT, int H, bool LINATTN>
+constexpr int grad_lds_bytes() {
+  constexpr int P = Pad<OpT>::v;
+  constexpr int nW = LINATTN ? 2 : 3;
+  constexpr int nMid = LINATTN ? 1 : 3;
+  return (nW * RB * (H + P) + 2 * H * (TT + P) + nMid * RB * (TT + P)) * (int)sizeof(OpT) +
+         TT * 4 + 16 * 4;
+}
+
+// grid: x = hidden block (rh/64), y = token segment, z = pair. block: 256 threads.
+template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID>
+__global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
+  typedef Mfma<OpT> M;
+  constexpr int P = Pad<OpT>::v;
+  constexpr int LDW = H + P;        // W block row stride
+  constexpr int LDT = TT + P;       // transposed token-tile / mid row stride
+  constexpr int nW = LINATTN ? 2 : 3;
+  constexpr int nMid = LINATTN ? 1 : 3;
+  constexpr int NMAT = LINATTN ? 1 : 3;
+  constexpr int CB = H / 32;                       // 32-wide column blocks of H
+  constexpr int NQ = NMAT * 2 * CB;                // gradient C tiles per workgroup
+  constexpr int NT = (NQ + NWAVE - 1) / NWAVE;     // per wave
+  constexpr int KS = H / M::KSTEP;                 // K steps over H
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  OpT* Wb = reinterpret_cast<OpT*>(smem);                    // [nW][RB][LDW]
+  OpT* Kt = Wb + nW * RB * LDW;                              // [H][LDT]
+  OpT* Vt = Kt + H * LDT;                                    // [H][LDT]
+  OpT* Mid = Vt + H * LDT;                                   // [nMid][RB][LDT]
+  float* eta_s = reinterpret_cast<float*>(Mid + nMid * RB * LDT);  // [TT]
+  float* red = eta_s + TT;                                   // [16]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int jb = blockIdx.x, seg = blockIdx.y, pair = blockIdx.z;
+  const int t_begin = a.t_base + seg * a.seg_len;
+  const int t_end = min(t_begin + a.seg_len, a.t_limit);
+
+  const IoT* Kp = reinterpret_cast<const IoT*>(a.K) + pair * a.tok_pair_stride;
+  const IoT* Vp = reinterpret_cast<const IoT*>(a.V) + pair * a.tok_pair_stride;
+  const float* ep = a.eta + pair * a.eta_pair_stride;
+
+  // --- stage this hidden block of the fast weights ---------------------------------------
+  {
+    const OpT* src[3] = {reinterpret_cast<const OpT*>(a.W0T), reinterpret_cast<const OpT*>(a.W2T),
+                         reinterpret_cast<const OpT*>(a.W1)};
+    constexpr int VPR = H * (int)sizeof(OpT) / 16;  // 16-byte vectors per row
+    for (int m = 0; m < nW; ++m) {
+      const OpT* s = src[m] + pair * a.w_pair_stride + (int64_t)jb * RB * H;
+      for (int i = tid; i < RB * VPR; i += 256) {
+        const int row = i / VPR, v = i % VPR;
+        *reinterpret_cast<u32x4*>(Wb + (m * RB + row) * LDW + v * (16 / sizeof(OpT))) =
+            *reinterpret_cast<const u32x4*>(s + row * H + v * (16 / sizeof(OpT)));
+      }
+    }
+  }
+
+  // --- power-of-two scale keeping eta-scaled intermediates in the operand range ---------
+  float scale = 1.f;
+  if constexpr (SCALE_MID) {
+    float mx = 0.f;
+    for (int t = t_begin + tid; t < t_end; t += 256) mx = fmaxf(mx, ep[t]);
+    mx = block_max(mx, red);
+    if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
+  }
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) zero(acc[i]);
+
+  const int th = w >> 1, jh = w & 1;  // forward role: token half, hidden half
+  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+    __syncthreads();  // previous tile's LDS reads are done
+    if (tid < TT) eta_s[tid] = (t0 + tid < t_end) ? ep[t0 + tid] * scale : 0.f;
+
+    // forward operands of this wave's 32 tokens, straight from global memory
+    const int trow = t0 + th * 32 + (lane & 31);
+    const bool tvalid = trow < t_end;
+    typename M::frag kf[KS], vf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
+      if (tvalid) {
+        kf[s] = FragIo<IoT, OpT>::load(Kp + (int64_t)trow * H + c);
+        vf[s] = FragIo<IoT, OpT>::load(Vp + (int64_t)trow * H + c);
+      } else {
+        kf[s] = zero_frag<OpT>();
+        vf[s] = zero_frag<OpT>();
+      }
+    }
+    // transposed copies for the token contractions: hidden-half 0 writes K^T, half 1 writes V^T
+    {
+      OpT* dst = jh == 0 ? Kt : Vt;
+      const int tcol = th * 32 + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
+#pragma unroll
+        for (int e = 0; e < M::KSUB; ++e)
+          dst[(c + e) * LDT + tcol] = frag_elem<OpT>(jh == 0 ? kf[s] : vf[s], e);
+      }
+    }
+    __syncthreads();  // eta_s, Kt, Vt visible
+
+    // forward products for (hidden rows jh*32.., tokens th*32..): A^T, Bm^T, D^T
+    {
+      f32x16 fa, fb, fd;
+      zero(fa);
+      zero(fb);
+      zero(fd);
+      const OpT* w0 = Wb + (0 * RB + jh * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
+      const OpT* w2 = Wb + (1 * RB + jh * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
+      const OpT* w1 = Wb + (2 * RB + jh * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        fa = M::mma(M::load(w0 + s * M::KSTEP), kf[s], fa);
+        fb = M::mma(M::load(w2 + s * M::KSTEP), kf[s], fb);
+        if constexpr (!LINATTN) fd = M::mma(M::load(w1 + s * M::KSTEP), vf[s], fd);
+      }
+      // epilogue: element (j, t) with j = jh*32 + acc_row, t = th*32 + lane&31
+      const int tl = th * 32 + (lane & 31);
+      const float e = eta_s[tl];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jh * 32 + acc_row(r, lane);
+        const float A = fa[r], Bm = fb[r];
+        const float sg = sigmoidf_(A);
+        const float sil = A * sg;
+        Mid[(0 * RB + j) * LDT + tl] = M::from_f32(e * sil * Bm);  // eta * H
+        if constexpr (!LINATTN) {
+          const float D = e * fd[r];
+          Mid[(1 * RB + j) * LDT + tl] = M::from_f32(D * Bm * (sg * (1.f + A * (1.f - sg))));  // X0
+          Mid[(2 * RB + j) * LDT + tl] = M::from_f32(D * sil);                                 // X2
+        }
+      }
+    }
+    __syncthreads();  // Mid visible
+
+    // token contractions: P1 += (eta H)^T V, P0 += X0^T K, P2 += X2^T K (rows j, cols c)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int q = w + NWAVE * i;
+      if (q < NQ) {
+        const int mat = q / (2 * CB), jhq = (q / CB) % 2, cb = q % CB;
+        // mat index: 0 -> P1 (mid 0 with V^T), 1 -> P0 (mid 1 with K^T), 2 -> P2 (mid 2 with K^T)
+        const OpT* am = Mid + (mat * RB + jhq * 32) * LDT;
+        const OpT* bm = (mat == 0 ? Vt : Kt) + cb * 32 * LDT;
+        mma_tile<OpT, TT>(acc[i], am, LDT, bm, LDT, lane);
+      }
+    }
+  }
+
+  // --- write partial sums: rows j, cols c; out matrices ordered (P0, P1, P2) ---------------
+  const float inv = 1.f / scale;
+  float* ob = a.out + seg * a.out_y_stride + pair * a.out_pair_stride;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int q = w + NWAVE * i;
+    if (q < NQ) {
+      const int mat = q / (2 * CB), jhq = (q / CB) % 2, cb = q % CB;
+      const int omat = LINATTN ? 0 : (mat == 0 ? 1 : (mat == 1 ? 0 : 2));
+      float* o = ob + omat * a.out_mat_stride + ((int64_t)jb * RB + jhq * 32) * H + cb * 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[acc_row(r, lane) * H + acc_col(lane)] = acc[i][r] * inv;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+struct ApplyArgs {
+  const void* Q;            // [pair][Nq][H]
+  int64_t tok_pair_stride;
+  int t_base;               // first query token of the launch (a chunk boundary)
+  int t_limit;              // one past the last query token of the launch
+  int tiles_per_chunk;      // grid.x = chunks * tiles_per_chunk; tiles never straddle chunks
+  const void* W0T;          // [rh][H] per pair
+  const void* W2T;
+  int64_t w_pair_stride;
+  const void* W1T;          // [H][rh] per pair, optionally per chunk
+  int64_t w1t_pair_stride;
+  int64_t w1t_chunk_stride; // elements between chunks' W1T (0: one W1T for all tokens)
+  int chunk;                // query tokens per chunk (selects the W1T of a query tile)
+  int rh;
+  void* O;                  // [pair][Nq][H]
+};
+
+template <class OpT, int H>
+constexpr int apply_lds_bytes() {
+  constexpr int P = Pad<OpT>::v;
+  return (TT * (H + P) + 2 * RB * (H + P) + H * (RB + P) + TT * (RB + P)) * (int)sizeof(OpT);
+}
+
+// grid: x = (chunk, 64-token tile within the chunk), y = pair. block: 256 threads.
+template <class IoT, class OpT, int H>
+__global__ void __launch_bounds__(256) apply_kernel(ApplyArgs a) {
+  typedef Mfma<OpT> M;
+  constexpr int P = Pad<OpT>::v;
+  constexpr int LDQ = H + P, LDH = RB + P;
+  constexpr int CB = H / 32;
+  constexpr int NO = 2 * CB;                      // output tiles (2 token halves x CB)
+  constexpr int NT = (NO + NWAVE - 1) / NWAVE;
+  extern __shared__ __align__(16) unsigned char smem[];
+  OpT* Qs = reinterpret_cast<OpT*>(smem);  // [TT][LDQ]
+  OpT* W0s = Qs + TT * LDQ;                // [RB][LDQ]
+  OpT* W2s = W0s + RB * LDQ;               // [RB][LDQ]
+  OpT* W1s = W2s + RB * LDQ;               // [H][LDH]
+  OpT* Hs = W1s + H * LDH;                 // [TT][LDH]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int pair = blockIdx.y;
+  const int chunk_idx = blockIdx.x / a.tiles_per_chunk;
+  const int t0 = a.t_base + chunk_idx * a.chunk + (blockIdx.x % a.tiles_per_chunk) * TT;
+  const int t_lim = min(a.t_base + (chunk_idx + 1) * a.chunk, a.t_limit);
+  if (t0 >= t_lim) return;
+  const IoT* Qp = reinterpret_cast<const IoT*>(a.Q) + pair * a.tok_pair_stride;
+  const OpT* w0g = reinterpret_cast<const OpT*>(a.W0T) + pair * a.w_pair_stride;
+  const OpT* w2g = reinterpret_cast<const OpT*>(a.W2T) + pair * a.w_pair_stride;
+  const OpT* w1g = reinterpret_cast<const OpT*>(a.W1T) + pair * a.w1t_pair_stride +
+                   (int64_t)chunk_idx * a.w1t_chunk_stride;
+
+  // stage the query tile (converted to the operand type); rows beyond the limit are zero
+  {
+    constexpr int VE = Io<IoT>::VEC;
+    for (int i = tid; i < TT * H / VE; i += 256) {
+      const int row = i / (H / VE), c = (i % (H / VE)) * VE;
+      OpT tmp[VE];
+      if (t0 + row < t_lim) {
+        Io<IoT>::template load_cvt<OpT>(Qp + (int64_t)(t0 + row) * H + c, tmp);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) tmp[e] = M::from_f32(0.f);
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) Qs[row * LDQ + c + e] = tmp[e];
+    }
+  }
+  f32x16 acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) zero(acc[i]);
+
+  const int th = w >> 1, jh = w & 1;
+  constexpr int VW = 16 / sizeof(OpT);
+  for (int j0 = 0; j0 < a.rh; j0 += RB) {
+    __syncthreads();
+    for (int i = tid; i < RB * H / VW; i += 256) {
+      const int row = i / (H / VW), c = (i % (H / VW)) * VW;
+      *reinterpret_cast<u32x4*>(W0s + row * LDQ + c) =
+          *reinterpret_cast<const u32x4*>(w0g + (int64_t)(j0 + row) * H + c);
+      *reinterpret_cast<u32x4*>(W2s + row * LDQ + c) =
+          *reinterpret_cast<const u32x4*>(w2g + (int64_t)(j0 + row) * H + c);
+    }
+    for (int i = tid; i < H * RB / VW; i += 256) {
+      const int row = i / (RB / VW), c = (i % (RB / VW)) * VW;
+      *reinterpret_cast<u32x4*>(W1s + row * LDH + c) =
+          *reinterpret_cast<const u32x4*>(w1g + (int64_t)row * a.rh + j0 + c);
+    }
+    __syncthreads();
+    // hidden activations for tokens th*32.., hidden units jh*32..
+    {
+      f32x16 fa, fb;
+      zero(fa);
+      zero(fb);
+      mma_tile<OpT, H>(fa, Qs + th * 32 * LDQ, LDQ, W0s + jh * 32 * LDQ, LDQ, lane);
+      mma_tile<OpT, H>(fb, Qs + th * 32 * LDQ, LDQ, W2s + jh * 32 * LDQ, LDQ, lane);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float A = fa[r];
+        const float hv = A * sigmoidf_(A) * fb[r];
+        Hs[(th * 32 + acc_row(r, lane)) * LDH + jh * 32 + acc_col(lane)] = M::from_f32(hv);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int q = w + NWAVE * i;
+      if (q < NO) {
+        const int tq = q % 2, cb = q / 2;
+        mma_tile<OpT, RB>(acc[i], Hs + tq * 32 * LDH, LDH, W1s + cb * 32 * LDH, LDH, lane);
+      }
+    }
+  }
+  IoT* Op = reinterpret_cast<IoT*>(a.O) + pair * a.tok_pair_stride;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int q = w + NWAVE * i;
+    if (q < NO) {
+      const int tq = q % 2, cb = q / 2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + tq * 32 + acc_row(r, lane);
+        if (t < t_lim) Io<IoT>::store(Op + (int64_t)t * H + cb * 32 + acc_col(lane), acc[i][r]);
+      }
+    }
+  }
+}
+
+}  // namespace ttt

@@ -1,0 +1,34 @@
+// host.hpp -- host-side helpers shared by the entry points (validation, workspace planning).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+#include "../../include/ttt_lact.h"
+
+namespace ttt {
+
+#define TTT_HIP(expr)                          \
+  do {                                         \
+    hipError_t _e = (expr);                    \
+    if (_e != hipSuccess) return TTT_ERR_HIP;  \
+  } while (0)
+
+// Sub-allocations of the caller's workspace, each 256-byte aligned.
+struct WorkspacePlan {
+  size_t total = 0;
+  size_t add(size_t bytes) {
+    const size_t off = total;
+    total += (bytes + 255) & ~size_t(255);
+    return off;
+  }
+};
+
+// Raise a kernel's dynamic-LDS limit once per instantiation.
+template <class F>
+inline hipError_t allow_lds(F* kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+}  // namespace ttt

@@ -1,0 +1,433 @@
+// lact.hip -- the chunked LaCT fast-weight layer on gfx950 (ttt_lact_forward).
+//
+// Per (sequence, head) pair and chunk (sources: KV-binding summary page, "Prerequisites ->
+// LaCT"; "Test-Time Training Done Right" reading notes, sections 2.1-2.3; "In-Place
+// Test-Time Training" notes, section 3.1):
+//   apply: O_c = (silu(Q_c W0) * (Q_c W2)) W1
+//   write: G = gradients of -sum eta <f(k), v> at the chunk-start weights (grad_kernel),
+//          U = G, or M = momentum*M + G and U = M; optionally U = NS5(U); W -= U;
+//          optionally each output column renormalised over its inputs to its initial norm.
+// Launch sequence per chunk: [apply] -> grad -> update -> [apply], all on the caller's stream.
+//
+// State layout in the workspace (float32, per pair): W0T [rh][h], W1 [rh][h], W2T [rh][h];
+// the same for the momentum buffers. Row j of W0T / W2T is input-weight column j of W0 / W2,
+// so the renormalisation of W0 / W2 is a row norm here and that of W1 a column norm.
+#include "fastweight.hpp"
+#include "host.hpp"
+
+namespace ttt {
+
+constexpr float NS_A = 3.4445f, NS_B = -4.7750f, NS_C = 2.0315f;  // notes section 2.2
+constexpr int NS_STEPS = 5;
+
+struct LactState {
+  float* W;        // [P][3][rh*h]
+  float* M;        // [P][3][rh*h]
+  float* nu;       // [P][3][NU] renorm targets
+  void* sh;        // operand shadows: [P][4][rh*h] (W0T, W2T, W1, W1T)
+  float* part;     // partial sums [S][P][3][rh*h]
+  float* ns;       // NS5 scratch [P][3][NSZ]
+  int P, h, rh, NU;
+  int64_t NSZ;
+};
+
+// ---------------------------------------------------------------------------------------
+// init: load the initial state (transposing W0, W2), momentum, renorm targets and shadows.
+// grid (3, P), block 256.
+template <class OpT>
+__global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float* W0, const float* W1,
+                                                       const float* W2, const float* M_in, int H,
+                                                       int64_t w_batch_stride) {
+  const int mat = blockIdx.x, pair = blockIdx.y;
+  const int h = s.h, rh = s.rh;
+  const int64_t n = (int64_t)rh * h;
+  const int b = pair / H, head = pair % H;
+  const float* src = (mat == 0 ? W0 : mat == 1 ? W1 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
+  float* W = s.W + ((int64_t)pair * 3 + mat) * n;
+  float* M = s.M + ((int64_t)pair * 3 + mat) * n;
+  const float* msrc = M_in ? M_in + ((int64_t)pair * 3 + mat) * n : nullptr;
+  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+    const int j = (int)(e / h), c = (int)(e % h);  // state element [j][c]
+    // row-form source: W0/W2 are [h][rh] (element [c][j]); W1 is [rh][h] (element [j][c])
+    const int64_t si = (mat == 1) ? e : (int64_t)c * rh + j;
+    W[e] = src[si];
+    M[e] = msrc ? msrc[si] : 0.f;
+  }
+  __syncthreads();
+  float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
+  if (mat == 1) {
+    for (int c = threadIdx.x; c < h; c += blockDim.x) {
+      float acc = 0.f;
+      for (int j = 0; j < rh; ++j) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
+      nu[c] = sqrtf(acc);
+    }
+  } else {
+    for (int j = threadIdx.x; j < rh; j += blockDim.x) {
+      float acc = 0.f;
+      for (int c = 0; c < h; ++c) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
+      nu[j] = sqrtf(acc);
+    }
+  }
+  OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
+  OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
+  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+    dst[e] = Mfma<OpT>::from_f32(W[e]);
+    if (mat == 1) {
+      const int j = (int)(e / h), c = (int)(e % h);
+      sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(W[e]);
+    }
+  }
+}
+
+// finalize: state and momentum back to the row form of the API. grid (3, P), block 256.
+__global__ void __launch_bounds__(256) lact_final_kernel(LactState s, float* W0o, float* W1o, float* W2o,
+                                                        float* Mo) {
+  const int mat = blockIdx.x, pair = blockIdx.y;
+  const int h = s.h, rh = s.rh;
+  const int64_t n = (int64_t)rh * h;
+  const float* W = s.W + ((int64_t)pair * 3 + mat) * n;
+  const float* M = s.M + ((int64_t)pair * 3 + mat) * n;
+  float* wo = (mat == 0 ? W0o : mat == 1 ? W1o : W2o);
+  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+    const int j = (int)(e / h), c = (int)(e % h);
+    const int64_t di = (mat == 1) ? e : (int64_t)c * rh + j;
+    if (wo) wo[(int64_t)pair * n + di] = W[e];
+    if (Mo) Mo[((int64_t)pair * 3 + mat) * n + di] = M[e];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// update: one workgroup per (matrix, pair). block 512 (8 waves).
+//   G = -(sum of partials, fixed order); momentum; Newton-Schulz-5 with split-bf16 operands;
+//   W -= U; input-dim renormalisation; operand shadows.
+// Newton-Schulz on the stored [rh][h] matrix Y = X^T (X = [h][rh], the wide orientation):
+//   X = U/(||U||_F + eps); 5 x { A = X X^T; B = b A + c A A; X = a X + B X }.
+struct UpdateArgs {
+  LactState s;
+  int S;               // partial segments
+  uint32_t mask;
+  int muon, weight_norm;
+  float momentum, eps_norm, eps_ns;
+};
+
+template <class OpT>
+__global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
+  const LactState& s = u.s;
+  const int mat = blockIdx.x, pair = blockIdx.y;
+  const uint32_t bit = mat == 0 ? 1u : mat == 1 ? 2u : 4u;
+  if (!(u.mask & bit)) return;
+  __shared__ float red[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  const int h = s.h, rh = s.rh;
+  const int64_t n = (int64_t)rh * h;
+  float* W = s.W + ((int64_t)pair * 3 + mat) * n;
+  float* M = s.M + ((int64_t)pair * 3 + mat) * n;
+  float* ns = s.ns + ((int64_t)pair * 3 + mat) * s.NSZ;
+  float* X[2] = {ns, ns + n};
+  float* Y[2] = {ns + 2 * n, ns + 3 * n};
+  float* A = ns + 4 * n;
+  float* Bq = A + (int64_t)h * h;
+  float* U = Y[0];  // the write, in the state layout
+
+  // gradient (sum over segments in order) and momentum
+  const int64_t seg_stride = (int64_t)s.P * 3 * n;
+  const float* part = s.part + ((int64_t)pair * 3 + mat) * n;
+  float ss = 0.f;
+  for (int64_t e = tid; e < n; e += blockDim.x) {
+    float g = 0.f;
+    for (int k = 0; k < u.S; ++k) g += part[k * seg_stride + e];
+    g = -g;
+    float v = g;
+    if (u.momentum != 0.f) {
+      v = u.momentum * M[e] + g;
+      M[e] = v;
+    }
+    U[e] = v;
+    ss += v * v;
+  }
+  if (u.muon) {
+    const float nrm = sqrtf(block_sum(ss, red));
+    const float inv = 1.f / (nrm + u.eps_ns);
+    __syncthreads();
+    for (int64_t e = tid; e < n; e += blockDim.x) {
+      const int j = (int)(e / h), c = (int)(e % h);
+      const float v = U[e] * inv;
+      U[e] = v;
+      X[0][(int64_t)c * rh + j] = v;
+    }
+    __syncthreads();
+    int cur = 0;
+    const int hb = h / 32, rb = rh / 32;
+    for (int it = 0; it < NS_STEPS; ++it) {
+      const float* Xc = X[cur];
+      const float* Yc = Y[cur];
+      for (int t = w; t < hb * hb; t += nw) {  // A = X X^T
+        const int ib = t / hb, kb = t % hb;
+        f32x16 acc;
+        zero(acc);
+        mma_tile_split(acc, Xc + (int64_t)ib * 32 * rh, rh, Xc + (int64_t)kb * 32 * rh, rh, rh, lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) A[(ib * 32 + acc_row(r, lane)) * h + kb * 32 + acc_col(lane)] = acc[r];
+      }
+      __syncthreads();
+      for (int t = w; t < hb * hb; t += nw) {  // B = b A + c A A
+        const int ib = t / hb, kb = t % hb;
+        f32x16 acc;
+        zero(acc);
+        mma_tile_split(acc, A + ib * 32 * h, h, A + kb * 32 * h, h, h, lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = ib * 32 + acc_row(r, lane), k = kb * 32 + acc_col(lane);
+          Bq[i * h + k] = NS_B * A[i * h + k] + NS_C * acc[r];
+        }
+      }
+      __syncthreads();
+      float* Xn = X[cur ^ 1];
+      float* Yn = Y[cur ^ 1];
+      for (int t = w; t < hb * rb; t += nw) {  // X = a X + B X
+        const int ib = t / rb, jb = t % rb;
+        f32x16 acc;
+        zero(acc);
+        mma_tile_split(acc, Bq + ib * 32 * h, h, Yc + (int64_t)jb * 32 * h, h, h, lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = ib * 32 + acc_row(r, lane), j = jb * 32 + acc_col(lane);
+          const float v = NS_A * Xc[(int64_t)i * rh + j] + acc[r];
+          Xn[(int64_t)i * rh + j] = v;
+          Yn[(int64_t)j * h + i] = v;
+        }
+      }
+      __syncthreads();
+      cur ^= 1;
+    }
+    U = Y[cur];
+  }
+  __syncthreads();
+  // subtract, renormalise, write state and shadows
+  for (int64_t e = tid; e < n; e += blockDim.x) W[e] -= U[e];
+  __syncthreads();
+  const float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
+  if (u.weight_norm) {
+    if (mat == 1) {  // W1 [rh][h]: column c over the rh inputs
+      for (int c = tid; c < h; c += blockDim.x) {
+        float acc = 0.f;
+        for (int j = 0; j < rh; ++j) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
+        const float f = nu[c] / (sqrtf(acc) + u.eps_norm);
+        for (int j = 0; j < rh; ++j) W[(int64_t)j * h + c] *= f;
+      }
+    } else {  // W0T / W2T: row j over the h inputs
+      for (int j = w; j < rh; j += nw) {
+        float acc = 0.f;
+        for (int c = lane; c < h; c += 64) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
+        acc = wave_sum(acc);
+        const float f = nu[j] / (sqrtf(acc) + u.eps_norm);
+        for (int c = lane; c < h; c += 64) W[(int64_t)j * h + c] *= f;
+      }
+    }
+  }
+  __syncthreads();
+  OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
+  OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
+  for (int64_t e = tid; e < n; e += blockDim.x) {
+    const float v = W[e];
+    dst[e] = Mfma<OpT>::from_f32(v);
+    if (mat == 1) {
+      const int j = (int)(e / h), c = (int)(e % h);
+      sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <class IoT, class OpT, int H>
+static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, const void* Q,
+                           const void* K, const void* V, const float* eta, const float* W0,
+                           const float* W1, const float* W2, const float* M_in, void* O, float* W0o,
+                           float* W1o, float* W2o, float* Mo, hipStream_t st) {
+  constexpr bool SCALE = sizeof(OpT) == 2;
+  auto gk = grad_kernel<IoT, OpT, H, false, SCALE>;
+  auto ak = apply_kernel<IoT, OpT, H>;
+  constexpr int glds = grad_lds_bytes<OpT, H, false>();
+  constexpr int alds = apply_lds_bytes<OpT, H>();
+  static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
+  static const hipError_t lds_ok = [&] {
+    hipError_t e = allow_lds(gk, glds);
+    return e != hipSuccess ? e : allow_lds(ak, alds);
+  }();
+  TTT_HIP(lds_ok);
+
+  const int P = s.P, rh = s.rh;
+  const int64_t n = (int64_t)rh * H;
+  const int nch = p.Nk / p.chunk_kv;
+  hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, M_in, p.H,
+                     p.w_batch_stride);
+  TTT_HIP(hipGetLastError());
+
+  const OpT* sh = reinterpret_cast<const OpT*>(s.sh);
+  ApplyArgs aa{};
+  aa.Q = Q;
+  aa.tok_pair_stride = (int64_t)p.Nq * H;
+  aa.W0T = sh;
+  aa.W2T = sh + n;
+  aa.w_pair_stride = 4 * n;
+  aa.W1T = sh + 3 * n;
+  aa.w1t_pair_stride = 4 * n;
+  aa.w1t_chunk_stride = 0;
+  aa.chunk = p.chunk_q;
+  aa.tiles_per_chunk = (p.chunk_q + TT - 1) / TT;
+  aa.rh = rh;
+  aa.O = O;
+
+  GradArgs ga{};
+  ga.K = K;
+  ga.V = V;
+  ga.eta = eta;
+  ga.tok_pair_stride = (int64_t)p.Nk * H;
+  ga.eta_pair_stride = p.Nk;
+  const int ntile = (p.chunk_kv + TT - 1) / TT;
+  const int tiles_per_seg = (ntile + S - 1) / S;
+  ga.seg_len = tiles_per_seg * TT;
+  ga.W0T = sh;
+  ga.W2T = sh + n;
+  ga.W1 = sh + 2 * n;
+  ga.w_pair_stride = 4 * n;
+  ga.rh = rh;
+  ga.out = s.part;
+  ga.out_y_stride = (int64_t)P * 3 * n;
+  ga.out_pair_stride = 3 * n;
+  ga.out_mat_stride = n;
+
+  UpdateArgs ua{};
+  ua.s = s;
+  ua.S = S;
+  ua.mask = p.update_mask;
+  ua.muon = p.muon;
+  ua.weight_norm = p.weight_norm;
+  ua.momentum = p.momentum;
+  ua.eps_norm = p.eps_norm;
+  ua.eps_ns = p.eps_ns;
+
+  const dim3 agrid((p.chunk_q + TT - 1) / TT, P);
+  for (int c = 0; c < nch; ++c) {
+    aa.t_base = c * p.chunk_q;
+    aa.t_limit = (c + 1) * p.chunk_q;
+    if (p.order == TTT_APPLY_THEN_UPDATE) {
+      hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
+      TTT_HIP(hipGetLastError());
+    }
+    ga.t_base = c * p.chunk_kv;
+    ga.t_limit = (c + 1) * p.chunk_kv;
+    hipLaunchKernelGGL(gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga);
+    TTT_HIP(hipGetLastError());
+    hipLaunchKernelGGL(lact_update_kernel<OpT>, dim3(3, P), dim3(512), 0, st, ua);
+    TTT_HIP(hipGetLastError());
+    if (p.order == TTT_UPDATE_THEN_APPLY) {
+      hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
+      TTT_HIP(hipGetLastError());
+    }
+  }
+  if (W0o || W1o || W2o || Mo) {
+    hipLaunchKernelGGL(lact_final_kernel, dim3(3, P), dim3(256), 0, st, s, W0o, W1o, W2o, Mo);
+    TTT_HIP(hipGetLastError());
+  }
+  return TTT_OK;
+}
+
+}  // namespace ttt
+
+using namespace ttt;
+
+extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, const void* K,
+                                       const void* V, const float* eta, const float* W0,
+                                       const float* W1, const float* W2, const float* M_in, void* O,
+                                       float* W0_out, float* W1_out, float* W2_out, float* M_out,
+                                       void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!p || !workspace_bytes) return TTT_ERR_ARG;
+  const ttt_lact_params& q = *p;
+  if (q.B < 0 || q.H < 0 || q.Nq < 0 || q.Nk < 0 || q.h <= 0 || q.r <= 0 || q.chunk_q <= 0 ||
+      q.chunk_kv <= 0)
+    return TTT_ERR_ARG;
+  if (q.order != TTT_APPLY_THEN_UPDATE && q.order != TTT_UPDATE_THEN_APPLY) return TTT_ERR_ARG;
+  if (q.dtype != TTT_FP32 && q.dtype != TTT_BF16) return TTT_ERR_ARG;
+  if (q.update_mask & ~7u) return TTT_ERR_ARG;
+  if (q.w_batch_stride < 0) return TTT_ERR_ARG;
+  if (q.Nq % q.chunk_q || q.Nk % q.chunk_kv) return TTT_ERR_SHAPE;
+  if (q.Nq / q.chunk_q != q.Nk / q.chunk_kv) return TTT_ERR_SHAPE;
+  const int64_t rh64 = (int64_t)q.r * q.h;
+  if (q.h % 32 || rh64 % 64 || rh64 > 1024) return TTT_ERR_SHAPE;
+  if (q.w_batch_stride != 0 && q.w_batch_stride != (int64_t)q.H * rh64 * q.h) return TTT_ERR_SHAPE;
+  const bool bf16 = q.dtype == TTT_BF16;
+  if (bf16 ? (q.h > 192) : (q.h > 64)) return TTT_ERR_UNSUPPORTED;
+  const int P = q.B * q.H, h = q.h, rh = (int)rh64;
+  const int64_t n = rh64 * h;
+  const int nch = q.chunk_kv ? q.Nk / q.chunk_kv : 0;
+  const bool have_tokens = P > 0 && nch > 0;
+  if (P > 0) {
+    if (!W0 || !W1 || !W2) return TTT_ERR_ARG;
+    if (have_tokens && (!Q || !K || !V || !eta || !O)) return TTT_ERR_ARG;
+  }
+  // segments of the token contraction: enough workgroups to cover the chip twice
+  const int ntile = (q.chunk_kv + TT - 1) / TT;
+  int S = (512 + (rh / RB) * std::max(P, 1) - 1) / ((rh / RB) * std::max(P, 1));
+  S = std::max(1, std::min(S, ntile));
+  const size_t opsz = bf16 ? 2 : 4;
+  WorkspacePlan plan;
+  const size_t oW = plan.add((size_t)P * 3 * n * 4);
+  const size_t oM = plan.add((size_t)P * 3 * n * 4);
+  const int NU = std::max(rh, h);
+  const size_t oNu = plan.add((size_t)P * 3 * NU * 4);
+  const size_t oSh = plan.add((size_t)P * 4 * n * opsz);
+  const size_t oPart = plan.add((size_t)S * P * 3 * n * 4);
+  const int64_t NSZ = 4 * n + 2 * (int64_t)h * h;
+  const size_t oNs = plan.add((size_t)P * 3 * NSZ * 4);
+  if (!workspace) {
+    *workspace_bytes = plan.total;
+    return TTT_OK;
+  }
+  if (*workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TTT_ERR_WORKSPACE;
+  if (P == 0) return TTT_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  LactState s;
+  s.W = reinterpret_cast<float*>(ws + oW);
+  s.M = reinterpret_cast<float*>(ws + oM);
+  s.nu = reinterpret_cast<float*>(ws + oNu);
+  s.sh = ws + oSh;
+  s.part = reinterpret_cast<float*>(ws + oPart);
+  s.ns = reinterpret_cast<float*>(ws + oNs);
+  s.P = P;
+  s.h = h;
+  s.rh = rh;
+  s.NU = NU;
+  s.NSZ = NSZ;
+  ttt_lact_params qq = q;
+  if (!have_tokens) {  // nothing to apply: the final state is the initial state
+    qq.Nq = qq.Nk = 0;
+  }
+#define TTT_LACT_CASE(IOT, OPT, HH)                                                                  \
+  case HH:                                                                                         \
+    return lact_run<IOT, OPT, HH>(qq, s, S, Q, K, V, eta, W0, W1, W2, M_in, O, W0_out, W1_out, W2_out, \
+                                  M_out, st);
+  try {
+    if (bf16) {
+      switch (h) {
+        TTT_LACT_CASE(bf16_t, _Float16, 32)
+        TTT_LACT_CASE(bf16_t, _Float16, 64)
+        TTT_LACT_CASE(bf16_t, _Float16, 96)
+        TTT_LACT_CASE(bf16_t, _Float16, 128)
+        TTT_LACT_CASE(bf16_t, _Float16, 160)
+        TTT_LACT_CASE(bf16_t, _Float16, 192)
+        default: return TTT_ERR_UNSUPPORTED;
+      }
+    } else {
+      switch (h) {
+        TTT_LACT_CASE(float, float, 32)
+        TTT_LACT_CASE(float, float, 64)
+        default: return TTT_ERR_UNSUPPORTED;
+      }
+    }
+  } catch (...) {
+    return TTT_ERR_HIP;
+  }
+#undef TTT_LACT_CASE
+}

@@ -1,0 +1,196 @@
+// linattn.hip -- the last-layer-only linear-attention form on gfx950 (ttt_linattn_forward).
+//
+// With only W1 written and no renormalisation, the fast weight's kernel
+// phi(x) = silu(x W0) * (x W2) is static and the state update is associative (KV-binding
+// summary page, "Prerequisites -> Linear attention" and Theorem 5.2 under "Method step
+// details"; press article, section 4). Per pair:
+//   dS_c = phi(K_c)^T diag(eta_c) V_c                    (grad_kernel, linear-attention mode)
+//   S_c  = W1 + sum_{j<c} dS_j   (apply-then-update)  or  sum_{j<=c} (update-then-apply)
+//   O_c  = phi(Q_c) S_c                                   (apply_kernel with per-chunk S_c)
+// The chunk prefix is an exclusive (or inclusive) scan over the chunks of each pair.
+#include "fastweight.hpp"
+#include "host.hpp"
+
+namespace ttt {
+
+// Operand shadows W0T, W2T [rh][h] per pair from the row-form W0, W2 [h][rh].
+template <class OpT>
+__global__ void __launch_bounds__(256) linattn_prep_kernel(const float* W0, const float* W2, OpT* sh, int H,
+                                                          int h, int rh, int64_t w_batch_stride) {
+  const int mat = blockIdx.x, pair = blockIdx.y;
+  const int b = pair / H, head = pair % H;
+  const int64_t n = (int64_t)rh * h;
+  const float* src = (mat == 0 ? W0 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
+  OpT* dst = sh + ((int64_t)pair * 2 + mat) * n;
+  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+    const int j = (int)(e / h), c = (int)(e % h);
+    dst[e] = Mfma<OpT>::from_f32(src[(int64_t)c * rh + j]);
+  }
+}
+
+// Chunk prefix scan, one thread per state element [j][c]: writes S_c^T [h][rh] per chunk as
+// an operand shadow and optionally the final state. grid (ceil(rh*h/256), P), block 256.
+template <class OpT>
+__global__ void __launch_bounds__(256) linattn_scan_kernel(const float* W1, const float* dS, OpT* St, float* S_out,
+                                                          int H, int h, int rh, int nch, int inclusive,
+                                                          int64_t w_batch_stride) {
+  const int pair = blockIdx.y;
+  const int64_t n = (int64_t)rh * h;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const int b = pair / H, head = pair % H;
+  const int j = (int)(e / h), c = (int)(e % h);
+  float s = W1[(int64_t)b * w_batch_stride + (int64_t)head * n + e];
+  const float* d = dS + (int64_t)pair * nch * n + e;
+  OpT* o = St + (int64_t)pair * nch * n + (int64_t)c * rh + j;
+  for (int k = 0; k < nch; ++k) {
+    if (inclusive) s += d[k * n];
+    o[k * n] = Mfma<OpT>::from_f32(s);
+    if (!inclusive) s += d[k * n];
+  }
+  if (S_out) S_out[(int64_t)pair * n + e] = s;
+}
+
+template <class IoT, class OpT, int H>
+static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh, size_t odS, size_t oSt,
+                              const void* Q, const void* K, const void* V, const float* eta,
+                              const float* W0, const float* W2, const float* W1, void* O, float* S_out,
+                              hipStream_t st) {
+  auto gk = grad_kernel<IoT, OpT, H, true, false>;
+  auto ak = apply_kernel<IoT, OpT, H>;
+  constexpr int glds = grad_lds_bytes<OpT, H, true>();
+  constexpr int alds = apply_lds_bytes<OpT, H>();
+  static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
+  static const hipError_t lds_ok = [&] {
+    hipError_t e = allow_lds(gk, glds);
+    return e != hipSuccess ? e : allow_lds(ak, alds);
+  }();
+  TTT_HIP(lds_ok);
+  const int P = p.B * p.H, rh = p.r * H, nch = p.N / p.chunk;
+  const int64_t n = (int64_t)rh * H;
+  OpT* sh = reinterpret_cast<OpT*>(ws + oSh);
+  float* dS = reinterpret_cast<float*>(ws + odS);
+  OpT* St = reinterpret_cast<OpT*>(ws + oSt);
+
+  hipLaunchKernelGGL(linattn_prep_kernel<OpT>, dim3(2, P), dim3(256), 0, st, W0, W2, sh, p.H, H, rh,
+                     p.w_batch_stride);
+  TTT_HIP(hipGetLastError());
+  GradArgs ga{};
+  ga.K = K;
+  ga.V = V;
+  ga.eta = eta;
+  ga.tok_pair_stride = (int64_t)p.N * H;
+  ga.eta_pair_stride = p.N;
+  ga.t_base = 0;
+  ga.seg_len = p.chunk;
+  ga.t_limit = p.N;
+  ga.W0T = sh;
+  ga.W2T = sh + n;
+  ga.W1 = nullptr;
+  ga.w_pair_stride = 2 * n;
+  ga.rh = rh;
+  ga.out = dS;
+  ga.out_y_stride = n;
+  ga.out_pair_stride = (int64_t)nch * n;
+  ga.out_mat_stride = 0;
+  hipLaunchKernelGGL(gk, dim3(rh / RB, nch, P), dim3(256), glds, st, ga);
+  TTT_HIP(hipGetLastError());
+  hipLaunchKernelGGL(linattn_scan_kernel<OpT>, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
+                     St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0,
+                     p.w_batch_stride);
+  TTT_HIP(hipGetLastError());
+  ApplyArgs aa{};
+  aa.Q = Q;
+  aa.tok_pair_stride = (int64_t)p.N * H;
+  aa.t_base = 0;
+  aa.t_limit = p.N;
+  aa.tiles_per_chunk = (p.chunk + TT - 1) / TT;
+  aa.W0T = sh;
+  aa.W2T = sh + n;
+  aa.w_pair_stride = 2 * n;
+  aa.W1T = St;
+  aa.w1t_pair_stride = (int64_t)nch * n;
+  aa.w1t_chunk_stride = n;
+  aa.chunk = p.chunk;
+  aa.rh = rh;
+  aa.O = O;
+  hipLaunchKernelGGL(ak, dim3(nch * aa.tiles_per_chunk, P), dim3(256), alds, st, aa);
+  TTT_HIP(hipGetLastError());
+  return TTT_OK;
+}
+
+}  // namespace ttt
+
+using namespace ttt;
+
+extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const void* Q, const void* K,
+                                          const void* V, const float* eta, const float* W0,
+                                          const float* W2, const float* W1, void* O, float* S_out,
+                                          void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!p || !workspace_bytes) return TTT_ERR_ARG;
+  const ttt_linattn_params& q = *p;
+  if (q.B < 0 || q.H < 0 || q.N < 0 || q.h <= 0 || q.r <= 0 || q.chunk <= 0) return TTT_ERR_ARG;
+  if (q.order != TTT_APPLY_THEN_UPDATE && q.order != TTT_UPDATE_THEN_APPLY) return TTT_ERR_ARG;
+  if (q.dtype != TTT_FP32 && q.dtype != TTT_BF16) return TTT_ERR_ARG;
+  if (q.w_batch_stride < 0) return TTT_ERR_ARG;
+  if (q.N % q.chunk) return TTT_ERR_SHAPE;
+  const int64_t rh64 = (int64_t)q.r * q.h;
+  if (q.h % 32 || rh64 % 64 || rh64 > 1024) return TTT_ERR_SHAPE;
+  if (q.w_batch_stride != 0 && q.w_batch_stride != (int64_t)q.H * rh64 * q.h) return TTT_ERR_SHAPE;
+  const bool bf16 = q.dtype == TTT_BF16;
+  if (bf16 ? (q.h > 256) : (q.h > 128)) return TTT_ERR_UNSUPPORTED;
+  const int P = q.B * q.H, nch = q.N / q.chunk;
+  if (P > 0 && (!W0 || !W1 || !W2)) return TTT_ERR_ARG;
+  if (P > 0 && nch > 0 && (!Q || !K || !V || !eta || !O)) return TTT_ERR_ARG;
+  const int64_t n = rh64 * q.h;
+  const size_t opsz = bf16 ? 2 : 4;
+  WorkspacePlan plan;
+  const size_t oSh = plan.add((size_t)P * 2 * n * opsz);
+  const size_t odS = plan.add((size_t)P * nch * n * 4);
+  const size_t oSt = plan.add((size_t)P * nch * n * opsz);
+  if (!workspace) {
+    *workspace_bytes = plan.total;
+    return TTT_OK;
+  }
+  if (*workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TTT_ERR_WORKSPACE;
+  if (P == 0) return TTT_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (nch == 0) {  // empty sequences: the final state is W1
+    if (S_out) {
+      for (int b = 0; b < q.B; ++b)
+        TTT_HIP(hipMemcpyAsync(S_out + (int64_t)b * q.H * n, W1 + (int64_t)b * q.w_batch_stride,
+                               (size_t)q.H * n * 4, hipMemcpyDeviceToDevice, st));
+    }
+    return TTT_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+#define TTT_LIN_CASE(IOT, OPT, HH) \
+  case HH:                         \
+    return linattn_run<IOT, OPT, HH>(q, ws, oSh, odS, oSt, Q, K, V, eta, W0, W2, W1, O, S_out, st);
+  try {
+    if (bf16) {
+      switch (q.h) {
+        TTT_LIN_CASE(bf16_t, __bf16, 32)
+        TTT_LIN_CASE(bf16_t, __bf16, 64)
+        TTT_LIN_CASE(bf16_t, __bf16, 96)
+        TTT_LIN_CASE(bf16_t, __bf16, 128)
+        TTT_LIN_CASE(bf16_t, __bf16, 160)
+        TTT_LIN_CASE(bf16_t, __bf16, 192)
+        TTT_LIN_CASE(bf16_t, __bf16, 224)
+        TTT_LIN_CASE(bf16_t, __bf16, 256)
+        default: return TTT_ERR_UNSUPPORTED;
+      }
+    } else {
+      switch (q.h) {
+        TTT_LIN_CASE(float, float, 32)
+        TTT_LIN_CASE(float, float, 64)
+        TTT_LIN_CASE(float, float, 96)
+        TTT_LIN_CASE(float, float, 128)
+        default: return TTT_ERR_UNSUPPORTED;
+      }
+    }
+  } catch (...) {
+    return TTT_ERR_HIP;
+  }
+#undef TTT_LIN_CASE
+}

@@ -1,0 +1,108 @@
+"""GPU parity of ttt_linattn_forward against the CPU oracle, plus the properties the pages
+state: the recurrent last-layer-only layer equals the scan form, and gradient ascent is a
+sign flip of the values."""
+import numpy as np
+import pytest
+
+from tests._helpers import BF16_TOL, FP32_TOL, announce, dev, host, lact_on_gpu
+from workloads import BF16, CONFIGS, FP32, LactProblem, UPD_W1, make_lact_inputs, max_abs_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _lin_gpu(lib, p, x, V=None, eta=None):
+    import torch
+    io = torch.bfloat16 if p.dtype == BF16 else torch.float32
+    return lib.linattn_forward(dev(x["Q"], io), dev(x["K"], io), dev(x["V"] if V is None else V, io),
+                               dev(x["eta"] if eta is None else eta, torch.float32),
+                               dev(x["W0"], torch.float32), dev(x["W2"], torch.float32),
+                               dev(x["W1"], torch.float32), chunk=p.chunk_kv, order=p.order)
+
+
+def _lin_ref(p, x, pairs=None, V=None):
+    from oracle import linattn as LA
+    return LA.linattn_forward(x["Q"], x["K"], x["V"] if V is None else V, x["eta"], x["W0"], x["W1"], x["W2"],
+                              chunk=p.chunk_kv, order=p.order, pairs=pairs)
+
+
+CASES = [
+    ("bf16 AU h64", dict(h=64, N=1024, chunk=256), 1),
+    ("bf16 UA h64", dict(h=64, N=1024, chunk=256, order=1), 2),
+    ("bf16 ragged tile chunk 96 h32", dict(h=32, N=480, chunk=96), 3),
+    ("bf16 single chunk h128", dict(h=128, N=512, chunk=512), 4),
+    ("bf16 h192 r2", dict(h=192, N=512, chunk=128), 5),
+    ("bf16 h256 r1", dict(h=256, r=1, N=256, chunk=128), 6),
+    ("fp32 AU h64", dict(h=64, N=512, chunk=128, dtype=FP32), 7),
+    ("fp32 UA h128 r1", dict(h=128, r=1, N=256, chunk=64, dtype=FP32, order=1), 8),
+]
+
+
+@pytest.mark.parametrize("label,kw,seed", CASES, ids=[c[0] for c in CASES])
+def test_small_cases(lib, label, kw, seed):
+    kw = dict(kw)
+    N, chunk = kw.pop("N"), kw.pop("chunk")
+    base = dict(B=2, H=2, h=64, r=2, Nq=N, Nk=N, chunk_q=chunk, chunk_kv=chunk, dtype=BF16,
+                update_mask=UPD_W1, weight_norm=False)
+    base.update(kw)
+    p = LactProblem(**base)
+    announce(f"linattn {label}")
+    for variant, xs in (("plain", dict()), ("eta x100", dict(eta_scale=1.0)), ("W1=0", dict(w1_zero=True))):
+        x = make_lact_inputs(p, 200 + seed, **xs)
+        O, S = _lin_gpu(lib, p, x)
+        ref = _lin_ref(p, x)
+        eo, es = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(S), ref["S"])
+        print(f"{label} [{variant}] O={eo:.2e} S={es:.2e}", flush=True)
+        tol = BF16_TOL if p.dtype == BF16 else FP32_TOL
+        assert eo <= tol and es <= tol, (variant, eo, es)
+
+
+def test_config1_full_size(lib):
+    p = CONFIGS[1]
+    announce("linattn config1 full size B4 H8 h64 r2 N8192 chunk512")
+    x = make_lact_inputs(p, 1)
+    O, S = _lin_gpu(lib, p, x)
+    pairs = [(0, 0), (1, 3), (2, 6), (3, 7)]
+    ref = _lin_ref(p, x, pairs=pairs)
+    sel = lambda a: np.stack([a[b, h] for b, h in pairs])
+    eo, es = max_abs_rel(sel(host(O)), sel(ref["O"])), max_abs_rel(sel(host(S)), sel(ref["S"]))
+    print(f"config1 O={eo:.2e} S={es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+def test_recurrent_layer_equals_scan_on_gpu(lib):
+    """Theorem 5.2 on the device: the LaCT layer writing only W1, without renormalisation,
+    momentum or Muon, gives the scan form's outputs."""
+    for order in (0, 1):
+        p = LactProblem(B=2, H=2, h=64, r=2, Nq=1024, Nk=1024, chunk_q=256, chunk_kv=256, dtype=BF16,
+                        update_mask=UPD_W1, weight_norm=False, order=order)
+        announce(f"linattn vs recurrent layer order={order}")
+        x = make_lact_inputs(p, 300 + order, eta_scale=1.0)
+        Ol, _ = _lin_gpu(lib, p, x)
+        Or = lact_on_gpu(lib, p, x)[0]
+        err = max_abs_rel(host(Ol), host(Or))
+        print(f"order {order}: scan vs recurrent {err:.2e}")
+        assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", [FP32, BF16])
+def test_gradient_ascent_is_a_value_sign_flip(lib, dtype):
+    """The state increment is linear in V, so writing with -V (gradient ascent) flips the sign
+    of O - phi(Q) W1: O(V) + O(-V) = 2 O(eta = 0). In fp32 mode the update parts are compared
+    directly; in bf16 mode (outputs rounded to bf16) against the output scale."""
+    p = LactProblem(B=1, H=2, h=64, r=2, Nq=1024, Nk=1024, chunk_q=256, chunk_kv=256, dtype=dtype,
+                    update_mask=UPD_W1, weight_norm=False)
+    announce(f"linattn ascent sign flip dtype={dtype}")
+    x = make_lact_inputs(p, 400, eta_scale=1.0)
+    Op, _ = _lin_gpu(lib, p, x)
+    On, _ = _lin_gpu(lib, p, x, V=-x["V"])
+    O0, _ = _lin_gpu(lib, p, x, eta=np.zeros_like(x["eta"]))
+    op, on, o0 = host(Op).astype(np.float64), host(On).astype(np.float64), host(O0).astype(np.float64)
+    if dtype == FP32:
+        err = max_abs_rel(op - o0, -(on - o0))
+        tol = FP32_TOL
+    else:
+        err = float(np.max(np.abs(op + on - 2 * o0)) / np.max(np.abs(2 * o0)))
+        tol = BF16_TOL
+    print(f"ascent flip ({dtype}) {err:.2e}")
+    assert err <= tol
+    assert max_abs_rel(op, o0) > 0.05  # the writes are visible
