@@ -1,0 +1,73 @@
+"""Algorithmic FLOP and byte counts of the three forms (host-side bookkeeping for the
+benchmark's roofline figures).
+
+FLOPs count multiply-adds of the matrix products only (2 per MAC), as the LaCT paper's
+FLOP model does ("Test-Time Training Done Right" notes, section 2.5: update + apply over n
+tokens is 9 matmuls = 18 n r d^2 / n_h = 6 n S with state S = 3 r d^2 / n_h per layer).
+Newton-Schulz products are counted on top because the method computes them; elementwise
+work (silu, norms, scans) is not counted.
+"""
+from __future__ import annotations
+
+
+def state_elements(d: int, n_h: int, r: float) -> float:
+    """Fast-weight elements per layer: three matrices of h x rh per head, S = 3 r d^2 / n_h."""
+    return 3.0 * r * d * d / n_h
+
+
+def swiglu_matmul_flops(tokens: int, d: int, n_h: int, r: float) -> float:
+    """Update + apply over `tokens` tokens: 9 products of 2 * tokens * h * rh each per head."""
+    h = d // n_h
+    return 9 * 2.0 * tokens * h * (r * h) * n_h
+
+
+def ns5_flops(m: int, n: int, steps: int = 5) -> float:
+    """Newton-Schulz on an m x n matrix (m <= n): per step X X^T (2 m^2 n), A A (2 m^3),
+    B X (2 m^2 n)."""
+    m, n = min(m, n), max(m, n)
+    return steps * (4.0 * m * m * n + 2.0 * m ** 3)
+
+
+def lact_flops(B, H, Nq, Nk, h, r, chunk_q, chunk_kv, update_mask=7, muon=False) -> float:
+    rh = r * h
+    n_ch = Nk // chunk_kv
+    pairs = B * H
+    apply = 3 * 2.0 * Nq * h * rh
+    n_upd = bin(update_mask & 7).count("1")
+    if update_mask == 7:
+        grads = 6 * 2.0 * Nk * h * rh          # A, Bm, D and the three token contractions
+    elif update_mask == 2:
+        grads = 3 * 2.0 * Nk * h * rh          # A, Bm and H^T V
+    else:
+        grads = 6 * 2.0 * Nk * h * rh
+    ns = n_ch * n_upd * ns5_flops(h, rh) if muon else 0.0
+    return pairs * (apply + grads + ns)
+
+
+def lact_bytes(B, H, Nq, Nk, h, r, io_bytes=2) -> float:
+    """Compulsory HBM traffic: Q, K, V, O once, eta once, initial and final fp32 state."""
+    pairs = B * H
+    rh = r * h
+    return pairs * ((2 * Nq + 2 * Nk) * h * io_bytes + 4 * Nk + 2 * 3 * h * rh * 4)
+
+
+def linattn_flops(B, H, N, h, r) -> float:
+    """phi(K) (2 products), dS (1), phi(Q) (2), phi(Q) S (1): 6 products of 2 N h rh."""
+    return B * H * 6 * 2.0 * N * h * (r * h)
+
+
+def linattn_bytes(B, H, N, h, r, io_bytes=2) -> float:
+    """Q, K, V read and O written once, eta once, W0/W1/W2 read once per head (fp32) and the
+    final state written (fp32)."""
+    rh = r * h
+    return B * H * (4 * N * h * io_bytes + 4 * N + 4 * h * rh * 4)
+
+
+def inplace_flops(B, N, d_model, d_hidden) -> float:
+    """Z (2 products), apply (1), update (1): 4 products of 2 N d_model d_hidden."""
+    return B * 4 * 2.0 * N * d_model * d_hidden
+
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 / fp16 MFMA (AMD public figure)
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0

@@ -125,6 +125,32 @@ __device__ __forceinline__ void mma_tile_split(f32x16& acc, const float* a, int 
   }
 }
 
+// K-major operand fragment from LDS with the gfx950 transpose read (ds_read_b64_tr_b16).
+// The tile is row-major with K along rows: element (k, n) at base[k * ld + n] (16-bit type T).
+// Lane l receives n = l & 31 and k = k0 + 8*(l >> 5) + 0..7, i.e. the same fragment that
+// Mfma<T>::load gives for an n-major tile. Each 16-lane group addresses a 4 x 16 block
+// (lane s of the group: row s / 4, 4-element chunk s % 4) and lane i of the group receives
+// column i of the block, rows 0..3; two reads cover the 8 k values. `ld` must keep every
+// 4-element chunk 8-byte aligned.
+template <class T>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag_tr(const T* base, int ld, int k0, int lane) {
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4;
+  const int g = lane >> 4, s = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (s >> 2);
+  const int col = 16 * (g & 1) + 4 * (s & 3);
+  const T* p0 = base + row * ld + col;
+  const T* p1 = p0 + 4 * ld;
+  v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4*)((__attribute__((address_space(3))) T*)(p0)));
+  v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4*)((__attribute__((address_space(3))) T*)(p1)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(typename Mfma<T>::frag, v);
+}
+
 // Row / column of accumulator element r for lane l (see the header comment).
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }

@@ -31,40 +31,6 @@ constexpr int NWAVE = 4; // waves per workgroup (256 threads)
 
 template <class T> struct Pad { static constexpr int v = 16 / sizeof(T); };  // 16-byte row pad
 
-// Load one K-step fragment of a token row from global memory, converting to the operand type.
-template <class IoT, class OpT> struct FragIo;
-template <class OpT> struct FragIo<bf16_t, OpT> {
-  __device__ __forceinline__ static typename Mfma<OpT>::frag load(const bf16_t* p) {
-    u16x8 v = *reinterpret_cast<const u16x8*>(p);
-    typename Mfma<OpT>::frag f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = Mfma<OpT>::from_f32(bf16_to_f32(v[e]));
-    return f;
-  }
-};
-template <> struct FragIo<float, float> {
-  __device__ __forceinline__ static float load(const float* p) { return *p; }
-};
-
-template <class OpT> __device__ __forceinline__ typename Mfma<OpT>::frag zero_frag() {
-  typename Mfma<OpT>::frag f;
-  if constexpr (Mfma<OpT>::KSUB == 1) {
-    f = 0.f;
-  } else {
-#pragma unroll
-    for (int e = 0; e < Mfma<OpT>::KSUB; ++e) f[e] = Mfma<OpT>::from_f32(0.f);
-  }
-  return f;
-}
-
-template <class OpT> __device__ __forceinline__ OpT frag_elem(const typename Mfma<OpT>::frag& f, int e) {
-  if constexpr (Mfma<OpT>::KSUB == 1) {
-    return f;
-  } else {
-    return f[e];
-  }
-}
-
 struct GradArgs {
   const void* K;          // [pair][N][H] I/O type
   const void* V;
@@ -85,23 +51,83 @@ struct GradArgs {
   int64_t out_mat_stride; // between P0 / P1 / P2 (= rh*H)
 };
 
+// K-major fragment: element (k, n) at base[k * ld + n]; lane l receives n = l & 31 and the
+// k values of its K step (16-bit: LDS transpose read; fp32: one strided element).
+template <class T>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag_kmajor(const T* base, int ld, int k0, int lane) {
+  if constexpr (sizeof(T) == 2) {
+    return load_frag_tr<T>(base, ld, k0, lane);
+  } else {
+    return base[(k0 + (lane >> 5)) * ld + (lane & 31)];
+  }
+}
+
+// Staging of a 64-token tile of K and V: each thread moves NCH 16-byte chunks per tensor from
+// global memory (rows beyond the segment are zero) through registers into row-major LDS
+// [t][c], converting to the operand type on the way.
+template <class IoT, class OpT, int H>
+struct TileStage {
+  static constexpr int VE = Io<IoT>::VEC;                 // elements per 16-byte chunk
+  static constexpr int NCH = TT * H / VE / 256;           // chunks per thread per tensor
+  static_assert(TT * H % (VE * 256) == 0, "staging map");
+  u32x4 k[NCH], v[NCH];
+  __device__ __forceinline__ void load(const IoT* Kp, const IoT* Vp, int t0, int t_end, int tid) {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int ch = tid + 256 * q;
+      const int row = ch / (H / VE), col = (ch % (H / VE)) * VE;
+      if (t0 + row < t_end) {
+        k[q] = *reinterpret_cast<const u32x4*>(Kp + (int64_t)(t0 + row) * H + col);
+        v[q] = *reinterpret_cast<const u32x4*>(Vp + (int64_t)(t0 + row) * H + col);
+      } else {
+        k[q] = u32x4{0u, 0u, 0u, 0u};
+        v[q] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ static void put(const u32x4& raw, OpT* dst) {
+    if constexpr (sizeof(IoT) == 2) {  // 8 bf16 -> 8 operand elements (16 bytes for fp16)
+      const u16x8 b = __builtin_bit_cast(u16x8, raw);
+      typename Mfma<OpT>::frag f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = Mfma<OpT>::from_f32(bf16_to_f32(b[e]));
+      *reinterpret_cast<typename Mfma<OpT>::frag*>(dst) = f;
+    } else {                           // 4 fp32
+      *reinterpret_cast<u32x4*>(dst) = raw;
+    }
+  }
+  __device__ __forceinline__ void store(OpT* Ks, OpT* Vs, int ld, int tid) const {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int ch = tid + 256 * q;
+      const int row = ch / (H / VE), col = (ch % (H / VE)) * VE;
+      put(k[q], Ks + row * ld + col);
+      put(v[q], Vs + row * ld + col);
+    }
+  }
+};
+
 // LDS bytes of grad_kernel<OpT, H, LINATTN>.
 template <class OpT, int H, bool LINATTN>
 constexpr int grad_lds_bytes() {
   constexpr int P = Pad<OpT>::v;
   constexpr int nW = LINATTN ? 2 : 3;
   constexpr int nMid = LINATTN ? 1 : 3;
-  return (nW * RB * (H + P) + 2 * H * (TT + P) + nMid * RB * (TT + P)) * (int)sizeof(OpT) +
-         TT * 4 + 16 * 4;
+  return (nW * RB * (H + P) + 2 * TT * (H + P) + nMid * RB * (TT + P)) * (int)sizeof(OpT) + TT * 4 + 16 * 4;
 }
 
-// grid: x = hidden block (rh/64), y = token segment, z = pair. block: 256 threads.
+// grid: x = hidden block (rh/64), y = token segment, z = pair. block: 256 threads (4 waves).
+// Per 64-token tile: K and V are staged row-major in LDS (the next tile is prefetched into
+// registers meanwhile); wave (th, jh) forms A^T, Bm^T, D^T for hidden rows jh*32.. and tokens
+// th*32.. (operands: fast-weight rows and token rows, both K-contiguous), the SwiGLU / silu'
+// epilogue writes eta*H, X0, X2 as [j][t] tiles, and the token contractions read K and V
+// K-major through the LDS transpose read.
 template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID>
 __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   typedef Mfma<OpT> M;
   constexpr int P = Pad<OpT>::v;
-  constexpr int LDW = H + P;        // W block row stride
-  constexpr int LDT = TT + P;       // transposed token-tile / mid row stride
+  constexpr int LDW = H + P;        // W block / token tile row stride
+  constexpr int LDT = TT + P;       // mid row stride
   constexpr int nW = LINATTN ? 2 : 3;
   constexpr int nMid = LINATTN ? 1 : 3;
   constexpr int NMAT = LINATTN ? 1 : 3;
@@ -112,9 +138,9 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
 
   extern __shared__ __align__(16) unsigned char smem[];
   OpT* Wb = reinterpret_cast<OpT*>(smem);                    // [nW][RB][LDW]
-  OpT* Kt = Wb + nW * RB * LDW;                              // [H][LDT]
-  OpT* Vt = Kt + H * LDT;                                    // [H][LDT]
-  OpT* Mid = Vt + H * LDT;                                   // [nMid][RB][LDT]
+  OpT* Ks = Wb + nW * RB * LDW;                              // [TT][LDW]
+  OpT* Vs = Ks + TT * LDW;                                   // [TT][LDW]
+  OpT* Mid = Vs + TT * LDW;                                  // [nMid][RB][LDT]
   float* eta_s = reinterpret_cast<float*>(Mid + nMid * RB * LDT);  // [TT]
   float* red = eta_s + TT;                                   // [16]
 
@@ -126,6 +152,9 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   const IoT* Kp = reinterpret_cast<const IoT*>(a.K) + pair * a.tok_pair_stride;
   const IoT* Vp = reinterpret_cast<const IoT*>(a.V) + pair * a.tok_pair_stride;
   const float* ep = a.eta + pair * a.eta_pair_stride;
+
+  TileStage<IoT, OpT, H> stage;
+  stage.load(Kp, Vp, t_begin, t_end, tid);
 
   // --- stage this hidden block of the fast weights ---------------------------------------
   {
@@ -158,36 +187,10 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   const int th = w >> 1, jh = w & 1;  // forward role: token half, hidden half
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     __syncthreads();  // previous tile's LDS reads are done
+    stage.store(Ks, Vs, LDW, tid);
     if (tid < TT) eta_s[tid] = (t0 + tid < t_end) ? ep[t0 + tid] * scale : 0.f;
-
-    // forward operands of this wave's 32 tokens, straight from global memory
-    const int trow = t0 + th * 32 + (lane & 31);
-    const bool tvalid = trow < t_end;
-    typename M::frag kf[KS], vf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
-      if (tvalid) {
-        kf[s] = FragIo<IoT, OpT>::load(Kp + (int64_t)trow * H + c);
-        vf[s] = FragIo<IoT, OpT>::load(Vp + (int64_t)trow * H + c);
-      } else {
-        kf[s] = zero_frag<OpT>();
-        vf[s] = zero_frag<OpT>();
-      }
-    }
-    // transposed copies for the token contractions: hidden-half 0 writes K^T, half 1 writes V^T
-    {
-      OpT* dst = jh == 0 ? Kt : Vt;
-      const int tcol = th * 32 + (lane & 31);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
-#pragma unroll
-        for (int e = 0; e < M::KSUB; ++e)
-          dst[(c + e) * LDT + tcol] = frag_elem<OpT>(jh == 0 ? kf[s] : vf[s], e);
-      }
-    }
-    __syncthreads();  // eta_s, Kt, Vt visible
+    __syncthreads();
+    if (t0 + TT < t_end) stage.load(Kp, Vp, t0 + TT, t_end, tid);  // in flight during the MFMAs
 
     // forward products for (hidden rows jh*32.., tokens th*32..): A^T, Bm^T, D^T
     {
@@ -198,11 +201,14 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
       const OpT* w0 = Wb + (0 * RB + jh * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
       const OpT* w2 = Wb + (1 * RB + jh * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
       const OpT* w1 = Wb + (2 * RB + jh * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
+      const OpT* kr = Ks + (th * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
+      const OpT* vr = Vs + (th * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        fa = M::mma(M::load(w0 + s * M::KSTEP), kf[s], fa);
-        fb = M::mma(M::load(w2 + s * M::KSTEP), kf[s], fb);
-        if constexpr (!LINATTN) fd = M::mma(M::load(w1 + s * M::KSTEP), vf[s], fd);
+        const auto kf = M::load(kr + s * M::KSTEP);
+        fa = M::mma(M::load(w0 + s * M::KSTEP), kf, fa);
+        fb = M::mma(M::load(w2 + s * M::KSTEP), kf, fb);
+        if constexpr (!LINATTN) fd = M::mma(M::load(w1 + s * M::KSTEP), M::load(vr + s * M::KSTEP), fd);
       }
       // epilogue: element (j, t) with j = jh*32 + acc_row, t = th*32 + lane&31
       const int tl = th * 32 + (lane & 31);
@@ -229,10 +235,11 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
       const int q = w + NWAVE * i;
       if (q < NQ) {
         const int mat = q / (2 * CB), jhq = (q / CB) % 2, cb = q % CB;
-        // mat index: 0 -> P1 (mid 0 with V^T), 1 -> P0 (mid 1 with K^T), 2 -> P2 (mid 2 with K^T)
-        const OpT* am = Mid + (mat * RB + jhq * 32) * LDT;
-        const OpT* bm = (mat == 0 ? Vt : Kt) + cb * 32 * LDT;
-        mma_tile<OpT, TT>(acc[i], am, LDT, bm, LDT, lane);
+        const OpT* am = Mid + (mat * RB + jhq * 32 + (lane & 31)) * LDT + (lane >> 5) * M::KSUB;
+        const OpT* bt = (mat == 0 ? Vs : Ks) + cb * 32;
+#pragma unroll
+        for (int k = 0; k < TT; k += M::KSTEP)
+          acc[i] = M::mma(M::load(am + k), load_frag_kmajor<OpT>(bt, LDW, k, lane), acc[i]);
       }
     }
   }

@@ -14,104 +14,83 @@
 // so the renormalisation of W0 / W2 is a row norm here and that of W1 a column norm.
 #include "fastweight.hpp"
 #include "host.hpp"
+#include "update.hpp"
 
 namespace ttt {
 
-constexpr float NS_A = 3.4445f, NS_B = -4.7750f, NS_C = 2.0315f;  // notes section 2.2
-constexpr int NS_STEPS = 5;
-
-struct LactState {
-  float* W;        // [P][3][rh*h]
-  float* M;        // [P][3][rh*h]
-  float* nu;       // [P][3][NU] renorm targets
-  void* sh;        // operand shadows: [P][4][rh*h] (W0T, W2T, W1, W1T)
-  float* part;     // partial sums [S][P][3][rh*h]
-  float* ns;       // NS5 scratch [P][3][NSZ]
-  int P, h, rh, NU;
-  int64_t NSZ;
-};
-
 // ---------------------------------------------------------------------------------------
-// init: load the initial state (transposing W0, W2), momentum, renorm targets and shadows.
-// grid (3, P), block 256.
+// init: the initial state (W0, W2 transposed into rows of hidden units), momentum and operand
+// shadows, one thread per state element. grid (ceil(n/256), 3, P), block 256.
 template <class OpT>
 __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float* W0, const float* W1,
                                                        const float* W2, const float* M_in, int H,
                                                        int64_t w_batch_stride) {
+  const int mat = blockIdx.y, pair = blockIdx.z;
+  const int h = s.h, rh = s.rh;
+  const int64_t n = (int64_t)rh * h;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int b = pair / H, head = pair % H;
+  const float* src = (mat == 0 ? W0 : mat == 1 ? W1 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
+  const int j = (int)(e / h), c = (int)(e % h);  // state element [j][c]
+  // row-form source: W0/W2 are [h][rh] (element [c][j]); W1 is [rh][h] (element [j][c])
+  const int64_t si = (mat == 1) ? e : (int64_t)c * rh + j;
+  const float v = src[si];
+  s.W[((int64_t)pair * 3 + mat) * n + e] = v;
+  s.M[((int64_t)pair * 3 + mat) * n + e] = M_in ? M_in[((int64_t)pair * 3 + mat) * n + si] : 0.f;
+  OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
+  sh[(mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + e] = Mfma<OpT>::from_f32(v);
+  if (mat == 1) sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(v);
+}
+
+// renorm targets (column norms of the initial row-form weights over their input axis) and the
+// barrier counters / error word. grid (3, P), block 256.
+__global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const float* W0, const float* W1,
+                                                        const float* W2, int H, int64_t w_batch_stride) {
   const int mat = blockIdx.x, pair = blockIdx.y;
   const int h = s.h, rh = s.rh;
   const int64_t n = (int64_t)rh * h;
   const int b = pair / H, head = pair % H;
   const float* src = (mat == 0 ? W0 : mat == 1 ? W1 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
-  float* W = s.W + ((int64_t)pair * 3 + mat) * n;
-  float* M = s.M + ((int64_t)pair * 3 + mat) * n;
-  const float* msrc = M_in ? M_in + ((int64_t)pair * 3 + mat) * n : nullptr;
-  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
-    const int j = (int)(e / h), c = (int)(e % h);  // state element [j][c]
-    // row-form source: W0/W2 are [h][rh] (element [c][j]); W1 is [rh][h] (element [j][c])
-    const int64_t si = (mat == 1) ? e : (int64_t)c * rh + j;
-    W[e] = src[si];
-    M[e] = msrc ? msrc[si] : 0.f;
-  }
-  __syncthreads();
   float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
-  if (mat == 1) {
-    for (int c = threadIdx.x; c < h; c += blockDim.x) {
-      float acc = 0.f;
-      for (int j = 0; j < rh; ++j) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
-      nu[c] = sqrtf(acc);
-    }
-  } else {
-    for (int j = threadIdx.x; j < rh; j += blockDim.x) {
-      float acc = 0.f;
-      for (int c = 0; c < h; ++c) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
-      nu[j] = sqrtf(acc);
-    }
+  const int cols = mat == 1 ? h : rh, rows = mat == 1 ? rh : h;  // row-form [rows][cols]
+  for (int j = threadIdx.x; j < cols; j += 256) {
+    float acc = 0.f;
+    for (int r = 0; r < rows; ++r) acc += src[(int64_t)r * cols + j] * src[(int64_t)r * cols + j];
+    nu[j] = sqrtf(acc);
   }
-  OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
-  OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
-  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
-    dst[e] = Mfma<OpT>::from_f32(W[e]);
-    if (mat == 1) {
-      const int j = (int)(e / h), c = (int)(e % h);
-      sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(W[e]);
-    }
-  }
+  unsigned* cnt = s.sync + ((int64_t)pair * 3 + mat) * SYNC_LINE;
+  if (threadIdx.x < SYNC_LINE) cnt[threadIdx.x] = 0u;
+  if (mat == 0 && pair == 0 && threadIdx.x == 0) s.sync[(int64_t)s.P * 3 * SYNC_LINE] = 0u;
 }
 
-// finalize: state and momentum back to the row form of the API. grid (3, P), block 256.
+// finalize: state and momentum back to the API's row form, one thread per output element;
+// a raised error word (barrier timeout or XCD mismatch) poisons the outputs with NaN.
+// grid (ceil(n/256), 3, P), block 256.
+template <class IoT>
 __global__ void __launch_bounds__(256) lact_final_kernel(LactState s, float* W0o, float* W1o, float* W2o,
-                                                        float* Mo) {
-  const int mat = blockIdx.x, pair = blockIdx.y;
+                                                        float* Mo, IoT* O, int64_t o_pair_stride) {
+  const int mat = blockIdx.y, pair = blockIdx.z;
   const int h = s.h, rh = s.rh;
   const int64_t n = (int64_t)rh * h;
-  const float* W = s.W + ((int64_t)pair * 3 + mat) * n;
-  const float* M = s.M + ((int64_t)pair * 3 + mat) * n;
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (d >= n) return;
+  const bool bad = s.sync[(int64_t)s.P * 3 * SYNC_LINE] != 0u;
+  // row-form element d: W1 [rh][h] is the state layout; W0/W2 [h][rh] element [c][j]
+  const int64_t e = (mat == 1) ? d : (int64_t)(d % rh) * h + d / rh;
+  const float nan = __builtin_nanf("");
   float* wo = (mat == 0 ? W0o : mat == 1 ? W1o : W2o);
-  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
-    const int j = (int)(e / h), c = (int)(e % h);
-    const int64_t di = (mat == 1) ? e : (int64_t)c * rh + j;
-    if (wo) wo[(int64_t)pair * n + di] = W[e];
-    if (Mo) Mo[((int64_t)pair * 3 + mat) * n + di] = M[e];
-  }
+  if (wo) wo[(int64_t)pair * n + d] = bad ? nan : s.W[((int64_t)pair * 3 + mat) * n + e];
+  if (Mo) Mo[((int64_t)pair * 3 + mat) * n + d] = bad ? nan : s.M[((int64_t)pair * 3 + mat) * n + e];
+  if (bad && O && mat == 0 && d == 0) Io<IoT>::store(O + pair * o_pair_stride, nan);
 }
 
 // ---------------------------------------------------------------------------------------
-// update: one workgroup per (matrix, pair). block 512 (8 waves).
-//   G = -(sum of partials, fixed order); momentum; Newton-Schulz-5 with split-bf16 operands;
-//   W -= U; input-dim renormalisation; operand shadows.
-// Newton-Schulz on the stored [rh][h] matrix Y = X^T (X = [h][rh], the wide orientation):
-//   X = U/(||U||_F + eps); 5 x { A = X X^T; B = b A + c A A; X = a X + B X }.
-struct UpdateArgs {
-  LactState s;
-  int S;               // partial segments
-  uint32_t mask;
-  int muon, weight_norm;
-  float momentum, eps_norm, eps_ns;
-};
-
+// Fallback update for head dims whose h x h Gram matrix does not fit in LDS next to the X
+// columns: one workgroup per (matrix, pair), operands read from an L2-resident global scratch.
+// Same steps as lact_update_kernel (update.hpp). block 512 (8 waves).
 template <class OpT>
-__global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
+__global__ void __launch_bounds__(512) lact_update_global_kernel(UpdateArgs u) {
   const LactState& s = u.s;
   const int mat = blockIdx.x, pair = blockIdx.y;
   const uint32_t bit = mat == 0 ? 1u : mat == 1 ? 2u : 4u;
@@ -259,8 +238,10 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const int P = s.P, rh = s.rh;
   const int64_t n = (int64_t)rh * H;
   const int nch = p.Nk / p.chunk_kv;
-  hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, M_in, p.H,
-                     p.w_batch_stride);
+  hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0, W1,
+                     W2, M_in, p.H, p.w_batch_stride);
+  TTT_HIP(hipGetLastError());
+  hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
   TTT_HIP(hipGetLastError());
 
   const OpT* sh = reinterpret_cast<const OpT*>(s.sh);
@@ -307,6 +288,34 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   ua.eps_norm = p.eps_norm;
   ua.eps_ns = p.eps_ns;
 
+  // update path: LDS-resident kernel for the (h, rh) shapes it is built for, else the fallback
+  const void* uk = nullptr;
+  int ug = 1, ulds = 0;
+#define TTT_UPD(HH, RR)                                                                     \
+  if (H == HH && rh == RR) {                                                                \
+    constexpr int g2 = update_lds_bytes<HH, RR, 1>() > 150 * 1024 ? 2 : 1;                  \
+    uk = reinterpret_cast<const void*>(lact_update_kernel<OpT, HH, RR, g2>);                 \
+    ug = g2;                                                                                \
+    ulds = update_lds_bytes<HH, RR, g2>();                                                  \
+  }
+  if constexpr (H == 32) { TTT_UPD(32, 64) TTT_UPD(32, 128) }
+  if constexpr (H == 64) { TTT_UPD(64, 128) TTT_UPD(64, 256) }
+  if constexpr (H == 96) { TTT_UPD(96, 192) TTT_UPD(96, 384) }
+  if constexpr (H == 128) { TTT_UPD(128, 256) }
+#undef TTT_UPD
+  if (uk) {
+    TTT_HIP(hipFuncSetAttribute(uk, hipFuncAttributeMaxDynamicSharedMemorySize, ulds));
+  }
+  const int M = 3 * P;
+  const unsigned ugrid = ug == 2 ? 16u * (unsigned)((M + 7) / 8) : (unsigned)M;
+  if (uk && ug == 2) {  // the two parts of a matrix wait for each other: all must be resident
+    int dev = 0, ncu = 0, per_cu = 0;
+    TTT_HIP(hipGetDevice(&dev));
+    TTT_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    TTT_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, uk, 512, ulds));
+    if ((long)per_cu * ncu < (long)ugrid) uk = nullptr;  // too many matrices at once: fallback
+  }
+
   const dim3 agrid((p.chunk_q + TT - 1) / TT, P);
   for (int c = 0; c < nch; ++c) {
     aa.t_base = c * p.chunk_q;
@@ -319,17 +328,27 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     ga.t_limit = (c + 1) * p.chunk_kv;
     hipLaunchKernelGGL(gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga);
     TTT_HIP(hipGetLastError());
-    hipLaunchKernelGGL(lact_update_kernel<OpT>, dim3(3, P), dim3(512), 0, st, ua);
-    TTT_HIP(hipGetLastError());
+    ua.chunk = c;
+    if (uk) {
+      if (ug == 2) {
+        void* args[] = {&ua};
+        TTT_HIP(hipLaunchCooperativeKernel(uk, dim3(ugrid), dim3(512), args, (unsigned)ulds, st));
+      } else {
+        void* args[] = {&ua};
+        TTT_HIP(hipLaunchKernel(uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
+      }
+    } else {
+      hipLaunchKernelGGL(lact_update_global_kernel<OpT>, dim3(3, P), dim3(512), 0, st, ua);
+      TTT_HIP(hipGetLastError());
+    }
     if (p.order == TTT_UPDATE_THEN_APPLY) {
       hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
       TTT_HIP(hipGetLastError());
     }
   }
-  if (W0o || W1o || W2o || Mo) {
-    hipLaunchKernelGGL(lact_final_kernel, dim3(3, P), dim3(256), 0, st, s, W0o, W1o, W2o, Mo);
-    TTT_HIP(hipGetLastError());
-  }
+  hipLaunchKernelGGL(lact_final_kernel<IoT>, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0o,
+                     W1o, W2o, Mo, reinterpret_cast<IoT*>(O), (int64_t)p.Nq * H);
+  TTT_HIP(hipGetLastError());
   return TTT_OK;
 }
 
@@ -380,6 +399,8 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   const size_t oPart = plan.add((size_t)S * P * 3 * n * 4);
   const int64_t NSZ = 4 * n + 2 * (int64_t)h * h;
   const size_t oNs = plan.add((size_t)P * 3 * NSZ * 4);
+  const size_t oXb = plan.add((size_t)P * 3 * 4 * h * h * 4);
+  const size_t oSync = plan.add(((size_t)P * 3 + 1) * SYNC_LINE * 4);
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -395,6 +416,8 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   s.sh = ws + oSh;
   s.part = reinterpret_cast<float*>(ws + oPart);
   s.ns = reinterpret_cast<float*>(ws + oNs);
+  s.xbuf = reinterpret_cast<float*>(ws + oXb);
+  s.sync = reinterpret_cast<unsigned*>(ws + oSync);
   s.P = P;
   s.h = h;
   s.rh = rh;
