@@ -19,8 +19,9 @@
  * - "I/O dtype" (TTT_BF16 or TTT_FP32) is the element type of the token tensors (Q, K, V, O,
  *   H, Vbar) and of the In-Place slow weights. Fast-weight state, momentum and step sizes are
  *   always float32. Accumulation is always float32.
- * - Ownership: the caller owns every buffer. The library never allocates, frees or
- *   synchronises; it keeps no mutable global state and is re-entrant for calls with distinct
+ * - Ownership: the caller owns every buffer. The entry points never allocate, free or
+ *   synchronise device memory; apart from the optional timing recorder (ttt_timing_*) the
+ *   library keeps no mutable global state and is re-entrant for calls with distinct
  *   workspaces. Inputs are read only. Outputs are fully overwritten and must not alias inputs.
  * - Workspace: pass workspace == NULL to query; the required size in bytes is written to
  *   *workspace_bytes, TTT_OK is returned and nothing is launched. Otherwise *workspace_bytes
@@ -108,8 +109,9 @@ typedef int32_t ttt_status;
  *   W0_out, W2_out [B, H, h, rh], W1_out [B, H, rh, h] float32, nullable: final fast weights
  *   M_out   [B, H, 3, h*rh] float32, nullable: final momentum
  * Shape rules: Nq/chunk_q == Nk/chunk_kv (number of chunks); a ragged last chunk is rejected
- * (TTT_ERR_SHAPE); h a multiple of 32 with 32 <= h <= 256; r >= 1 with r*h a multiple of 64
- * and r*h <= 1024.
+ * (TTT_ERR_SHAPE); h a multiple of 32 and r >= 1 with r*h a multiple of 64, r*h <= 1024;
+ * this build implements h <= 192 in TTT_BF16 mode and h <= 64 in TTT_FP32 mode
+ * (TTT_ERR_UNSUPPORTED otherwise).
  * Precision: in TTT_BF16 mode the per-chunk products use fp16 MFMA operands (bf16 inputs
  * convert exactly) and Newton-Schulz uses split-bf16 operands; fp32 state throughout. In
  * TTT_FP32 mode all operands are fp32.
@@ -196,6 +198,26 @@ ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p,
                                     const float* W_down, const void* Vbar,
                                     void* O, float* W_down_out,
                                     void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel timing (instrumentation; off by default)
+ *
+ * For callers that need per-kernel durations (the benchmark's roofline figures). While
+ * enabled, every kernel launched by the entry points above is bracketed by two HIP events
+ * recorded on the stream it is launched on, grouped by kernel class. ttt_timing_collect waits
+ * for the recorded events, writes one entry per class that ran (name: static string,
+ * launches, summed milliseconds) and clears the record. The recorder is process-wide state
+ * owned by the library; it is not meant for concurrent use from several host threads.
+ * Returns TTT_ERR_HIP if an event cannot be created or read.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  const char* name;
+  int32_t launches;
+  float total_ms;
+} ttt_kernel_time;
+
+ttt_status ttt_timing_enable(int32_t on);
+ttt_status ttt_timing_collect(ttt_kernel_time* out, int32_t capacity, int32_t* count);
 
 /* Human-readable name of a status code (static string). */
 const char* ttt_status_string(ttt_status s);

@@ -25,7 +25,12 @@ APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
 FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
 
-EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_inplace_down_forward", "ttt_status_string")
+EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_inplace_down_forward", "ttt_status_string",
+            "ttt_timing_enable", "ttt_timing_collect")
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_float)]
 
 
 class LactParams(ctypes.Structure):
@@ -78,12 +83,34 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ttt_inplace_down_forward.restype = ctypes.c_int32
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
     lib.ttt_status_string.restype = ctypes.c_char_p
+    lib.ttt_timing_enable.argtypes = [ctypes.c_int32]
+    lib.ttt_timing_enable.restype = ctypes.c_int32
+    lib.ttt_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.ttt_timing_collect.restype = ctypes.c_int32
     _lib = lib
     return lib
 
 
 def status_string(s: int) -> str:
     return load().ttt_status_string(s).decode()
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every kernel launched by the entry points with HIP events (per kernel class)."""
+    st = load().ttt_timing_enable(int(bool(on)))
+    if st != TTT_OK:
+        raise TTTError("ttt_timing_enable", st)
+
+
+def timing_collect() -> dict:
+    """Wait for the recorded events; return {kernel class: (launches, total ms)} and clear."""
+    lib = load()
+    buf = (KernelTime * 32)()
+    n = ctypes.c_int32(0)
+    st = lib.ttt_timing_collect(buf, 32, ctypes.byref(n))
+    if st != TTT_OK:
+        raise TTTError("ttt_timing_collect", st)
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, 32))}
 
 
 # ----------------------------------------------------------------------------------------

@@ -71,3 +71,44 @@ def inplace_flops(B, N, d_model, d_hidden) -> float:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 / fp16 MFMA (AMD public figure)
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+
+def kernel_source_hash(root: str) -> str:
+    """sha1 over the kernel sources and the C header (identifies the build a profile was taken on)."""
+    import glob
+    import hashlib
+    import os
+    h = hashlib.sha1()
+    files = sorted(glob.glob(os.path.join(root, "linear_attention_lact_amd", "csrc", "*")))
+    files.append(os.path.join(root, "include", "ttt_lact.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(root: str, kernel_class: str):
+    """HBM bytes per launch (read + write) of a kernel class from the committed counter profile,
+    or None when there is none for this class or the kernel sources changed since it was taken."""
+    import glob
+    import os
+    symbol = {"lact_update": "lact_update_kernel", "lact_grad": "grad_kernel", "lact_apply": "apply_kernel"}
+    sym = symbol.get(kernel_class)
+    if sym is None:
+        return None
+    cur = kernel_source_hash(root)
+    for path in glob.glob(os.path.join(root, "profiles", "*_hbm_counters.txt")):
+        lines = open(path).read().splitlines()
+        tag = [l for l in lines if l.startswith("# kernel sources sha1:")]
+        if not tag or tag[0].split(":", 1)[1].strip() != cur:
+            continue
+        for l in lines:
+            if l.startswith("#") or sym not in l:
+                continue
+            parts = l.split()
+            try:
+                return (float(parts[3]) + float(parts[4])) * 1e6
+            except (ValueError, IndexError):
+                return None
+    return None

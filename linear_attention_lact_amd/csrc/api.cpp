@@ -1,5 +1,9 @@
-// api.cpp -- status strings of the C ABI.
+// api.cpp -- status strings and the optional kernel-timing recorder of the C ABI.
+#include <hip/hip_runtime.h>
+#include <mutex>
+#include <vector>
 #include "../../include/ttt_lact.h"
+#include "timing.hpp"
 
 extern "C" const char* ttt_status_string(ttt_status s) {
   switch (s) {
@@ -11,4 +15,76 @@ extern "C" const char* ttt_status_string(ttt_status s) {
     case TTT_ERR_HIP: return "HIP launch failure";
     default: return "unknown status";
   }
+}
+
+namespace ttt {
+namespace {
+const char* kClassNames[K_NUM_CLASSES] = {
+    "lact_init", "lact_grad", "lact_update", "lact_apply", "lact_final",
+    "linattn_prep", "linattn_delta", "linattn_scan", "linattn_apply", "linattn_fused",
+    "inplace_prep", "inplace_z", "inplace_apply", "inplace_update"};
+struct Rec { int cls; hipEvent_t a, b; };
+std::mutex mu;
+bool on = false;
+std::vector<Rec> recs;
+std::vector<hipEvent_t> pool;  // events not in use
+}  // namespace
+
+bool timing_on() { return on; }
+
+hipEvent_t timing_event() {
+  std::lock_guard<std::mutex> g(mu);
+  if (!pool.empty()) {
+    hipEvent_t e = pool.back();
+    pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void timing_record(int cls, hipEvent_t a, hipEvent_t b) {
+  std::lock_guard<std::mutex> g(mu);
+  recs.push_back({cls, a, b});
+}
+}  // namespace ttt
+
+extern "C" ttt_status ttt_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> g(ttt::mu);
+  ttt::on = enable != 0;
+  return TTT_OK;
+}
+
+extern "C" ttt_status ttt_timing_collect(ttt_kernel_time* out, int32_t capacity, int32_t* count) {
+  using namespace ttt;
+  std::vector<Rec> rs;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    rs.swap(recs);
+  }
+  int launches[K_NUM_CLASSES] = {0};
+  float ms[K_NUM_CLASSES] = {0.f};
+  ttt_status st = TTT_OK;
+  for (const Rec& r : rs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) st = TTT_ERR_HIP;
+    launches[r.cls] += 1;
+    ms[r.cls] += t;
+  }
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (const Rec& r : rs) {
+      pool.push_back(r.a);
+      pool.push_back(r.b);
+    }
+  }
+  int n = 0;
+  for (int c = 0; c < K_NUM_CLASSES; ++c) {
+    if (!launches[c]) continue;
+    if (out && n < capacity) out[n] = ttt_kernel_time{kClassNames[c], launches[c], ms[c]};
+    ++n;
+  }
+  if (count) *count = n;
+  return st;
 }

@@ -10,6 +10,7 @@
 // (for the update, contracting over tokens); Vbar is transposed once per sequence.
 #include "common.hpp"
 #include "host.hpp"
+#include "timing.hpp"
 
 namespace ttt {
 
@@ -226,11 +227,14 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
     TTT_HIP(hipMemcpyAsync(Wf, W_down + (int64_t)b * q.wdown_batch_stride, (size_t)nW * 4,
                            hipMemcpyDeviceToDevice, st));
     if (nch == 0) continue;
-    hipLaunchKernelGGL(to_bf16_kernel, dim3(2048), dim3(256), 0, st, Wf, Wsh, nW);
-    TTT_HIP(hipGetLastError());
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(q.d_model / 64, q.N / 64), dim3(256), 0, st,
-                       Vb + (int64_t)b * q.N * q.d_model, Vt, q.N, q.d_model);
-    TTT_HIP(hipGetLastError());
+    {
+      LaunchTimer lt(K_INP_PREP, st);
+      hipLaunchKernelGGL(to_bf16_kernel, dim3(2048), dim3(256), 0, st, Wf, Wsh, nW);
+      TTT_HIP(hipGetLastError());
+      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(q.d_model / 64, q.N / 64), dim3(256), 0, st,
+                         Vb + (int64_t)b * q.N * q.d_model, Vt, q.N, q.d_model);
+      TTT_HIP(hipGetLastError());
+    }
     for (int i = 0; i < nch; ++i) {
       const int64_t t0 = (int64_t)i * q.chunk;
       Args z{};
@@ -246,9 +250,12 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       z.ldc = q.d_hidden;
       z.Ct = Zt;
       z.ldct = q.chunk;
-      hipLaunchKernelGGL(gemm_tn_kernel<EPI_SWIGLU>, dim3(q.d_hidden / BN, q.chunk / BM), dim3(256),
-                         lds_bytes<EPI_SWIGLU>(), st, z);
-      TTT_HIP(hipGetLastError());
+      {
+        LaunchTimer lt(K_INP_Z, st);
+        hipLaunchKernelGGL(gemm_tn_kernel<EPI_SWIGLU>, dim3(q.d_hidden / BN, q.chunk / BM), dim3(256),
+                           lds_bytes<EPI_SWIGLU>(), st, z);
+        TTT_HIP(hipGetLastError());
+      }
       Args a{};
       a.A = Z;
       a.lda = q.d_hidden;
@@ -259,9 +266,12 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       a.K = q.d_hidden;
       a.C = Ob + ((int64_t)b * q.N + t0) * q.d_model;
       a.ldc = q.d_model;
-      hipLaunchKernelGGL(gemm_tn_kernel<EPI_STORE>, dim3(q.d_model / BN, q.chunk / BM), dim3(256),
-                         lds_bytes<EPI_STORE>(), st, a);
-      TTT_HIP(hipGetLastError());
+      {
+        LaunchTimer lt(K_INP_APPLY, st);
+        hipLaunchKernelGGL(gemm_tn_kernel<EPI_STORE>, dim3(q.d_model / BN, q.chunk / BM), dim3(256),
+                           lds_bytes<EPI_STORE>(), st, a);
+        TTT_HIP(hipGetLastError());
+      }
       Args u{};
       u.A = Vt + t0;
       u.lda = q.N;
@@ -274,9 +284,12 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       u.Wsh = Wsh;
       u.ldw = q.d_hidden;
       u.alpha = q.eta;
-      hipLaunchKernelGGL(gemm_tn_kernel<EPI_RMW>, dim3(q.d_hidden / BN, q.d_model / BM), dim3(256),
-                         lds_bytes<EPI_RMW>(), st, u);
-      TTT_HIP(hipGetLastError());
+      {
+        LaunchTimer lt(K_INP_UPDATE, st);
+        hipLaunchKernelGGL(gemm_tn_kernel<EPI_RMW>, dim3(q.d_hidden / BN, q.d_model / BM), dim3(256),
+                           lds_bytes<EPI_RMW>(), st, u);
+        TTT_HIP(hipGetLastError());
+      }
     }
   }
   return TTT_OK;

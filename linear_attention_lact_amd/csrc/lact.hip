@@ -14,6 +14,7 @@
 // so the renormalisation of W0 / W2 is a row norm here and that of W1 a column norm.
 #include "fastweight.hpp"
 #include "host.hpp"
+#include "timing.hpp"
 #include "update.hpp"
 
 namespace ttt {
@@ -238,11 +239,14 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const int P = s.P, rh = s.rh;
   const int64_t n = (int64_t)rh * H;
   const int nch = p.Nk / p.chunk_kv;
-  hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0, W1,
-                     W2, M_in, p.H, p.w_batch_stride);
-  TTT_HIP(hipGetLastError());
-  hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
-  TTT_HIP(hipGetLastError());
+  {
+    LaunchTimer lt(K_LACT_INIT, st);
+    hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0,
+                       W1, W2, M_in, p.H, p.w_batch_stride);
+    TTT_HIP(hipGetLastError());
+    hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
+    TTT_HIP(hipGetLastError());
+  }
 
   const OpT* sh = reinterpret_cast<const OpT*>(s.sh);
   ApplyArgs aa{};
@@ -321,31 +325,37 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     aa.t_base = c * p.chunk_q;
     aa.t_limit = (c + 1) * p.chunk_q;
     if (p.order == TTT_APPLY_THEN_UPDATE) {
+      LaunchTimer lt(K_LACT_APPLY, st);
       hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
       TTT_HIP(hipGetLastError());
     }
     ga.t_base = c * p.chunk_kv;
     ga.t_limit = (c + 1) * p.chunk_kv;
-    hipLaunchKernelGGL(gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga);
-    TTT_HIP(hipGetLastError());
-    ua.chunk = c;
-    if (uk) {
-      if (ug == 2) {
-        void* args[] = {&ua};
-        TTT_HIP(hipLaunchCooperativeKernel(uk, dim3(ugrid), dim3(512), args, (unsigned)ulds, st));
-      } else {
-        void* args[] = {&ua};
-        TTT_HIP(hipLaunchKernel(uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
-      }
-    } else {
-      hipLaunchKernelGGL(lact_update_global_kernel<OpT>, dim3(3, P), dim3(512), 0, st, ua);
+    {
+      LaunchTimer lt(K_LACT_GRAD, st);
+      hipLaunchKernelGGL(gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga);
       TTT_HIP(hipGetLastError());
     }
+    ua.chunk = c;
+    {
+      LaunchTimer lt(K_LACT_UPDATE, st);
+      void* args[] = {&ua};
+      if (uk && ug == 2) {
+        TTT_HIP(hipLaunchCooperativeKernel(uk, dim3(ugrid), dim3(512), args, (unsigned)ulds, st));
+      } else if (uk) {
+        TTT_HIP(hipLaunchKernel(uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
+      } else {
+        hipLaunchKernelGGL(lact_update_global_kernel<OpT>, dim3(3, P), dim3(512), 0, st, ua);
+        TTT_HIP(hipGetLastError());
+      }
+    }
     if (p.order == TTT_UPDATE_THEN_APPLY) {
+      LaunchTimer lt(K_LACT_APPLY, st);
       hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
       TTT_HIP(hipGetLastError());
     }
   }
+  LaunchTimer lt_fin(K_LACT_FINAL, st);
   hipLaunchKernelGGL(lact_final_kernel<IoT>, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0o,
                      W1o, W2o, Mo, reinterpret_cast<IoT*>(O), (int64_t)p.Nq * H);
   TTT_HIP(hipGetLastError());

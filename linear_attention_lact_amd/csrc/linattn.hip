@@ -10,6 +10,7 @@
 // The chunk prefix is an exclusive (or inclusive) scan over the chunks of each pair.
 #include "fastweight.hpp"
 #include "host.hpp"
+#include "timing.hpp"
 
 namespace ttt {
 
@@ -72,9 +73,12 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   float* dS = reinterpret_cast<float*>(ws + odS);
   OpT* St = reinterpret_cast<OpT*>(ws + oSt);
 
-  hipLaunchKernelGGL(linattn_prep_kernel<OpT>, dim3(2, P), dim3(256), 0, st, W0, W2, sh, p.H, H, rh,
-                     p.w_batch_stride);
-  TTT_HIP(hipGetLastError());
+  {
+    LaunchTimer lt(K_LIN_PREP, st);
+    hipLaunchKernelGGL(linattn_prep_kernel<OpT>, dim3(2, P), dim3(256), 0, st, W0, W2, sh, p.H, H, rh,
+                       p.w_batch_stride);
+    TTT_HIP(hipGetLastError());
+  }
   GradArgs ga{};
   ga.K = K;
   ga.V = V;
@@ -93,12 +97,17 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   ga.out_y_stride = n;
   ga.out_pair_stride = (int64_t)nch * n;
   ga.out_mat_stride = 0;
-  hipLaunchKernelGGL(gk, dim3(rh / RB, nch, P), dim3(256), glds, st, ga);
-  TTT_HIP(hipGetLastError());
-  hipLaunchKernelGGL(linattn_scan_kernel<OpT>, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
-                     St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0,
-                     p.w_batch_stride);
-  TTT_HIP(hipGetLastError());
+  {
+    LaunchTimer lt(K_LIN_DELTA, st);
+    hipLaunchKernelGGL(gk, dim3(rh / RB, nch, P), dim3(256), glds, st, ga);
+    TTT_HIP(hipGetLastError());
+  }
+  {
+    LaunchTimer lt(K_LIN_SCAN, st);
+    hipLaunchKernelGGL(linattn_scan_kernel<OpT>, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
+                       St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.w_batch_stride);
+    TTT_HIP(hipGetLastError());
+  }
   ApplyArgs aa{};
   aa.Q = Q;
   aa.tok_pair_stride = (int64_t)p.N * H;
@@ -114,8 +123,11 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   aa.chunk = p.chunk;
   aa.rh = rh;
   aa.O = O;
-  hipLaunchKernelGGL(ak, dim3(nch * aa.tiles_per_chunk, P), dim3(256), alds, st, aa);
-  TTT_HIP(hipGetLastError());
+  {
+    LaunchTimer lt(K_LIN_APPLY, st);
+    hipLaunchKernelGGL(ak, dim3(nch * aa.tiles_per_chunk, P), dim3(256), alds, st, aa);
+    TTT_HIP(hipGetLastError());
+  }
   return TTT_OK;
 }
 
