@@ -151,6 +151,47 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag_tr(const T* base, in
   return __builtin_bit_cast(typename Mfma<T>::frag, v);
 }
 
+// Operand fragments that continue from an accumulator tile C[t][j] (32 x 32, fp32, lane layout
+// above) into a product contracting over t. Element r of lane l holds t = 8*(r/4) + 4*(l>>5) + r%4,
+// so with 16-bit operands K step q (q = 0, 1) takes elements r = 8q .. 8q+7 of every lane: lane
+// half g then supplies t = 16q + {4g..4g+3, 8+4g..8+4g+3}. The partner operand must present the
+// same t permutation: acc_kfrag_tr reads rows of a row-major (t-major) LDS tile accordingly.
+template <class T>
+__device__ __forceinline__ typename Mfma<T>::frag acc_to_afrag(const f32x16& c, int q) {
+  typename Mfma<T>::frag f;
+  if constexpr (Mfma<T>::KSUB == 1) {
+    f = c[q];  // fp32: one element per K step of 2, step index q = r
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = Mfma<T>::from_f32(c[8 * q + e]);
+  }
+  return f;
+}
+
+// Partner of acc_to_afrag: element (t, n) at base[t * ld + n] with t relative to the
+// accumulator tile's first row; lane l receives n = l & 31 and the permuted t set of K step q.
+template <class T>
+__device__ __forceinline__ typename Mfma<T>::frag acc_kfrag_tr(const T* base, int ld, int q, int lane) {
+  if constexpr (Mfma<T>::KSUB == 1) {
+    // fp32 K step q = r: lane half g supplies t = 8*(r/4) + 4*g + r%4
+    const int t = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+    return base[t * ld + (lane & 31)];
+  } else {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4;
+    const int g = lane >> 4, s = lane & 15;
+    const int row = 16 * q + 4 * (g >> 1) + (s >> 2);
+    const int col = 16 * (g & 1) + 4 * (s & 3);
+    const T* p0 = base + row * ld + col;
+    const T* p1 = p0 + 8 * ld;
+    v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)((__attribute__((address_space(3))) T*)(p0)));
+    v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)((__attribute__((address_space(3))) T*)(p1)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    v8i16 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(typename Mfma<T>::frag, v);
+  }
+}
+
 // Row / column of accumulator element r for lane l (see the header comment).
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }

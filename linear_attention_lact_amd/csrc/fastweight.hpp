@@ -261,6 +261,181 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Register-direct variant for h <= 128 (same arguments and outputs as grad_kernel).
+// Wave w owns hidden rows jh*32.. (jh = w & 1) of the workgroup's block and token half th = w >> 1
+// of every 64-token tile. Its slices of W0^T, W2^T, W1 stay in registers as MFMA B fragments
+// for the whole segment. The forward products are formed as C[t][j] (K and V rows as the A
+// operand, from the row-major LDS tile); the epilogue values eta*H, X0, X2 then serve directly
+// as A fragments of the token contractions (acc_to_afrag), whose partner K / V fragments come from
+// the same LDS tile through the permuted transpose read (acc_kfrag_tr). The two token halves are
+// summed in LDS at the end (fixed order). Block mapping: the hidden blocks of one
+// (pair, segment) are workgroups w, w+8, ..., i.e. on one XCD, so its K / V tiles are fetched from
+// HBM once per XCD.
+// grid: x = rh/64 * 8 * ceil(P * nseg / 8); block 256.
+template <class OpT, int H, bool LINATTN>
+constexpr int grad_rd_lds_bytes() {
+  constexpr int P = Pad<OpT>::v;
+  constexpr int tiles = 2 * TT * (H + P) * (int)sizeof(OpT) + TT * 4 + 16 * 4;
+  constexpr int comb = 2 * (LINATTN ? 1 : 3) * (H / 32) * 16 * 64 * 4;
+  return tiles > comb ? tiles : comb;
+}
+
+template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID>
+__global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int npairs) {
+  static_assert(H <= 128, "register budget");
+  typedef Mfma<OpT> M;
+  constexpr int P = Pad<OpT>::v;
+  constexpr int LDK = H + P;
+  constexpr int CB = H / 32;
+  constexpr int KS = H / M::KSTEP;          // forward K steps over h
+  constexpr int QS = 32 / M::KSTEP;         // contraction K steps over a 32-token half
+  constexpr int NMAT = LINATTN ? 1 : 3;
+  constexpr int NWM = LINATTN ? 2 : 3;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  OpT* Ks = reinterpret_cast<OpT*>(smem);   // [TT][LDK]
+  OpT* Vs = Ks + TT * LDK;                  // [TT][LDK]
+  float* eta_s = reinterpret_cast<float*>(Vs + TT * LDK);
+  float* red = eta_s + TT;
+  float* comb = reinterpret_cast<float*>(smem);  // reused after the token loop
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int njb = a.rh / RB;
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int jb = slot % njb;
+  const int group = xcd + 8 * (slot / njb);
+  if (group >= npairs * nseg) return;
+  const int pair = group / nseg, seg = group % nseg;
+  const int t_begin = a.t_base + seg * a.seg_len;
+  const int t_end = min(t_begin + a.seg_len, a.t_limit);
+  const int jh = w & 1, th = w >> 1;
+
+  const IoT* Kp = reinterpret_cast<const IoT*>(a.K) + pair * a.tok_pair_stride;
+  const IoT* Vp = reinterpret_cast<const IoT*>(a.V) + pair * a.tok_pair_stride;
+  const float* ep = a.eta + pair * a.eta_pair_stride;
+
+  TileStage<IoT, OpT, H> stage;
+  stage.load(Kp, Vp, t_begin, t_end, tid);
+
+  // fast-weight slices as B fragments: lane (n = j, k = c) of rows jb*64 + jh*32 + (lane & 31)
+  typename M::frag wf[NWM][KS];
+  {
+    const OpT* src[3] = {reinterpret_cast<const OpT*>(a.W0T), reinterpret_cast<const OpT*>(a.W2T),
+                         reinterpret_cast<const OpT*>(a.W1)};
+#pragma unroll
+    for (int m = 0; m < NWM; ++m) {
+      const OpT* row = src[m] + pair * a.w_pair_stride + (int64_t)(jb * RB + jh * 32 + (lane & 31)) * H +
+                       (lane >> 5) * M::KSUB;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) wf[m][s] = M::load(row + s * M::KSTEP);
+    }
+  }
+
+  float scale = 1.f;
+  if constexpr (SCALE_MID) {
+    float mx = 0.f;
+    for (int t = t_begin + tid; t < t_end; t += 256) mx = fmaxf(mx, ep[t]);
+    mx = block_max(mx, red);
+    if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
+  }
+
+  f32x16 acc[NMAT][CB];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int c = 0; c < CB; ++c) zero(acc[m][c]);
+
+  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+    __syncthreads();
+    stage.store(Ks, Vs, LDK, tid);
+    if (tid < TT) eta_s[tid] = (t0 + tid < t_end) ? ep[t0 + tid] * scale : 0.f;
+    __syncthreads();
+    if (t0 + TT < t_end) stage.load(Kp, Vp, t0 + TT, t_end, tid);
+
+    // forward: C[t][j] for tokens th*32.., hidden jh*32..
+    f32x16 fa, fb, fd;
+    zero(fa);
+    zero(fb);
+    zero(fd);
+    {
+      const OpT* kr = Ks + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
+      const OpT* vr = Vs + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const auto kf = M::load(kr + s * M::KSTEP);
+        fa = M::mma(kf, wf[0][s], fa);
+        fb = M::mma(kf, wf[1][s], fb);
+        if constexpr (!LINATTN) fd = M::mma(M::load(vr + s * M::KSTEP), wf[2][s], fd);
+      }
+    }
+    // epilogue in registers: fa <- eta*H, fb <- X0, fd <- X2 (element r: t = th*32 + acc_row)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = eta_s[th * 32 + acc_row(r, lane)];
+      const float A = fa[r], Bm = fb[r];
+      const float sg = sigmoidf_(A);
+      const float sil = A * sg;
+      fa[r] = e * sil * Bm;
+      if constexpr (!LINATTN) {
+        const float D = e * fd[r];
+        fb[r] = D * Bm * (sg * (1.f + A * (1.f - sg)));
+        fd[r] = D * sil;
+      }
+    }
+    // token contractions over this wave's 32 tokens
+    const OpT* kb = Ks + th * 32 * LDK;
+    const OpT* vb = Vs + th * 32 * LDK;
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const auto ah = acc_to_afrag<OpT>(fa, q);
+      typename M::frag a0, a2;
+      if constexpr (!LINATTN) {
+        a0 = acc_to_afrag<OpT>(fb, q);
+        a2 = acc_to_afrag<OpT>(fd, q);
+      }
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        acc[0][c] = M::mma(ah, acc_kfrag_tr<OpT>(vb + c * 32, LDK, q, lane), acc[0][c]);
+        if constexpr (!LINATTN) {
+          const auto bk = acc_kfrag_tr<OpT>(kb + c * 32, LDK, q, lane);
+          acc[1][c] = M::mma(a0, bk, acc[1][c]);
+          acc[2][c] = M::mma(a2, bk, acc[2][c]);
+        }
+      }
+    }
+  }
+
+  // sum the token halves in LDS (wave (jh, 1) hands its tiles to wave (jh, 0)), then store
+  __syncthreads();
+  float* cb_ = comb + (size_t)jh * NMAT * CB * 16 * 64;
+  if (th == 1) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cb_[((m * CB + c) * 16 + r) * 64 + lane] = acc[m][c][r];
+  }
+  __syncthreads();
+  if (th == 0) {
+    const float inv = 1.f / scale;
+    float* ob = a.out + seg * a.out_y_stride + pair * a.out_pair_stride;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      // acc[0] = P1 (eta H with V), acc[1] = P0 (X0 with K), acc[2] = P2 (X2 with K)
+      const int omat = LINATTN ? 0 : (m == 0 ? 1 : (m == 1 ? 0 : 2));
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        float* o = ob + omat * a.out_mat_stride + ((int64_t)jb * RB + jh * 32) * H + c * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o[acc_row(r, lane) * H + acc_col(lane)] = (acc[m][c][r] + cb_[((m * CB + c) * 16 + r) * 64 + lane]) * inv;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 struct ApplyArgs {
   const void* Q;            // [pair][Nq][H]
   int64_t tok_pair_stride;
@@ -276,6 +451,8 @@ struct ApplyArgs {
   int chunk;                // query tokens per chunk (selects the W1T of a query tile)
   int rh;
   void* O;                  // [pair][Nq][H]
+  int npairs;               // pairs in the launch
+  int ntiles;               // query tiles per pair in the launch (chunks * tiles_per_chunk)
 };
 
 template <class OpT, int H>
@@ -284,7 +461,8 @@ constexpr int apply_lds_bytes() {
   return (TT * (H + P) + 2 * RB * (H + P) + H * (RB + P) + TT * (RB + P)) * (int)sizeof(OpT);
 }
 
-// grid: x = (chunk, 64-token tile within the chunk), y = pair. block: 256 threads.
+// grid: x = 8 * ceil(npairs / 8) * ntiles; all tiles of a pair run on one XCD (workgroups
+// w, w+8, ...), so its fast-weight shadows stay in that XCD's L2. block: 256 threads.
 template <class IoT, class OpT, int H>
 __global__ void __launch_bounds__(256) apply_kernel(ApplyArgs a) {
   typedef Mfma<OpT> M;
@@ -301,9 +479,12 @@ __global__ void __launch_bounds__(256) apply_kernel(ApplyArgs a) {
   OpT* Hs = W1s + H * LDH;                 // [TT][LDH]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int pair = blockIdx.y;
-  const int chunk_idx = blockIdx.x / a.tiles_per_chunk;
-  const int t0 = a.t_base + chunk_idx * a.chunk + (blockIdx.x % a.tiles_per_chunk) * TT;
+  const int bid = blockIdx.x, slot = bid >> 3;
+  const int pair = (bid & 7) + 8 * (slot / a.ntiles);
+  const int tile = slot % a.ntiles;
+  if (pair >= a.npairs) return;
+  const int chunk_idx = tile / a.tiles_per_chunk;
+  const int t0 = a.t_base + chunk_idx * a.chunk + (tile % a.tiles_per_chunk) * TT;
   const int t_lim = min(a.t_base + (chunk_idx + 1) * a.chunk, a.t_limit);
   if (t0 >= t_lim) return;
   const IoT* Qp = reinterpret_cast<const IoT*>(a.Q) + pair * a.tok_pair_stride;

@@ -225,13 +225,15 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
                            const float* W1, const float* W2, const float* M_in, void* O, float* W0o,
                            float* W1o, float* W2o, float* Mo, hipStream_t st) {
   constexpr bool SCALE = sizeof(OpT) == 2;
+  constexpr bool RD = H <= 128;  // register-direct gradient kernel
   auto gk = grad_kernel<IoT, OpT, H, false, SCALE>;
+  auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE>;
   auto ak = apply_kernel<IoT, OpT, H>;
-  constexpr int glds = grad_lds_bytes<OpT, H, false>();
+  constexpr int glds = RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false>() : grad_lds_bytes<OpT, H, false>();
   constexpr int alds = apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
-    hipError_t e = allow_lds(gk, glds);
+    hipError_t e = RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
     return e != hipSuccess ? e : allow_lds(ak, alds);
   }();
   TTT_HIP(lds_ok);
@@ -262,6 +264,8 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   aa.tiles_per_chunk = (p.chunk_q + TT - 1) / TT;
   aa.rh = rh;
   aa.O = O;
+  aa.npairs = P;
+  aa.ntiles = aa.tiles_per_chunk;
 
   GradArgs ga{};
   ga.K = K;
@@ -320,7 +324,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     if ((long)per_cu * ncu < (long)ugrid) uk = nullptr;  // too many matrices at once: fallback
   }
 
-  const dim3 agrid((p.chunk_q + TT - 1) / TT, P);
+  const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
   for (int c = 0; c < nch; ++c) {
     aa.t_base = c * p.chunk_q;
     aa.t_limit = (c + 1) * p.chunk_q;
@@ -333,7 +337,12 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     ga.t_limit = (c + 1) * p.chunk_kv;
     {
       LaunchTimer lt(K_LACT_GRAD, st);
-      hipLaunchKernelGGL(gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga);
+      if constexpr (RD) {
+        const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
+        hipLaunchKernelGGL(gkr, dim3(grid), dim3(256), glds, st, ga, S, P);
+      } else {
+        hipLaunchKernelGGL(gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga);
+      }
       TTT_HIP(hipGetLastError());
     }
     ua.chunk = c;
@@ -397,7 +406,8 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   }
   // segments of the token contraction: enough workgroups to cover the chip twice
   const int ntile = (q.chunk_kv + TT - 1) / TT;
-  int S = (512 + (rh / RB) * std::max(P, 1) - 1) / ((rh / RB) * std::max(P, 1));
+  const int wg_target = (bf16 ? q.h <= 128 : true) ? 256 : 512;  // register-direct kernel: 1 per CU
+  int S = (wg_target + (rh / RB) * std::max(P, 1) - 1) / ((rh / RB) * std::max(P, 1));
   S = std::max(1, std::min(S, ntile));
   const size_t opsz = bf16 ? 2 : 4;
   WorkspacePlan plan;

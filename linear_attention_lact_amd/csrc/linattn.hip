@@ -57,13 +57,15 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
                               const void* Q, const void* K, const void* V, const float* eta,
                               const float* W0, const float* W2, const float* W1, void* O, float* S_out,
                               hipStream_t st) {
+  constexpr bool RD = H <= 128;  // register-direct chunk-aggregate kernel
   auto gk = grad_kernel<IoT, OpT, H, true, false>;
+  auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), true, false>;
   auto ak = apply_kernel<IoT, OpT, H>;
-  constexpr int glds = grad_lds_bytes<OpT, H, true>();
+  constexpr int glds = RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), true>() : grad_lds_bytes<OpT, H, true>();
   constexpr int alds = apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
-    hipError_t e = allow_lds(gk, glds);
+    hipError_t e = RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
     return e != hipSuccess ? e : allow_lds(ak, alds);
   }();
   TTT_HIP(lds_ok);
@@ -99,7 +101,12 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   ga.out_mat_stride = 0;
   {
     LaunchTimer lt(K_LIN_DELTA, st);
-    hipLaunchKernelGGL(gk, dim3(rh / RB, nch, P), dim3(256), glds, st, ga);
+    if constexpr (RD) {
+      const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * nch + 7) / 8);
+      hipLaunchKernelGGL(gkr, dim3(grid), dim3(256), glds, st, ga, nch, P);
+    } else {
+      hipLaunchKernelGGL(gk, dim3(rh / RB, nch, P), dim3(256), glds, st, ga);
+    }
     TTT_HIP(hipGetLastError());
   }
   {
@@ -123,9 +130,11 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   aa.chunk = p.chunk;
   aa.rh = rh;
   aa.O = O;
+  aa.npairs = P;
+  aa.ntiles = nch * aa.tiles_per_chunk;
   {
     LaunchTimer lt(K_LIN_APPLY, st);
-    hipLaunchKernelGGL(ak, dim3(nch * aa.tiles_per_chunk, P), dim3(256), alds, st, aa);
+    hipLaunchKernelGGL(ak, dim3(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles), dim3(256), alds, st, aa);
     TTT_HIP(hipGetLastError());
   }
   return TTT_OK;
