@@ -21,6 +21,8 @@
 // apply_kernel: O = (silu(Q W0) * (Q W2)) W1 for a tile of 64 query tokens, streaming the
 // hidden dimension in blocks of 64.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ttt {
@@ -262,42 +264,57 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Register-direct variant for h <= 128 (same arguments and outputs as grad_kernel).
-// Wave w owns hidden rows jh*32.. (jh = w & 1) of the workgroup's block and token half th = w >> 1
-// of every 64-token tile. Its slices of W0^T, W2^T, W1 stay in registers as MFMA B fragments
-// for the whole segment. The forward products are formed as C[t][j] (K and V rows as the A
-// operand, from the row-major LDS tile); the epilogue values eta*H, X0, X2 then serve directly
-// as A fragments of the token contractions (acc_to_afrag), whose partner K / V fragments come from
-// the same LDS tile through the permuted transpose read (acc_kfrag_tr). The two token halves are
-// summed in LDS at the end (fixed order). Block mapping: the hidden blocks of one
-// (pair, segment) are workgroups w, w+8, ..., i.e. on one XCD, so its K / V tiles are fetched from
-// HBM once per XCD.
+// Wave w = jh + 2 th forms the forward products of hidden rows jh*32.. (of the workgroup's 64)
+// and token half th of every 64-token tile. Its slices of W0^T, W2^T, W1 stay in registers as
+// MFMA B fragments for the whole segment. The forward products are formed as C[t][j] (K and V
+// rows as the A operand, from the row-major LDS tile), so the epilogue values eta*H, X0, X2
+// serve directly as A fragments of the token contractions (acc_to_afrag). For the contractions
+// the wave takes column half th of the h outputs over all 64 tokens: its own A fragments come
+// from registers, its partner's (same jh, other token half) through a small LDS exchange, and
+// the K / V fragments from the LDS tile through the permuted transpose read (acc_kfrag_tr).
+// Every output element is thus summed by one wave in a fixed order.
+// Software pipeline: K, V and eta tiles are double-buffered in LDS and the tile after next is
+// prefetched into registers; the forward MFMAs of tile i+1 are interleaved with the (VALU)
+// epilogue of tile i, so matrix cores and vector ALU overlap within the single wave per SIMD
+// that the register budget allows.
+// Block mapping: the hidden blocks of one (pair, segment) are workgroups w, w+8, ..., i.e. on
+// one XCD, so its K / V tiles are fetched from HBM once per XCD.
 // grid: x = rh/64 * 8 * ceil(P * nseg / 8); block 256.
 template <class OpT, int H, bool LINATTN>
 constexpr int grad_rd_lds_bytes() {
   constexpr int P = Pad<OpT>::v;
-  constexpr int tiles = 2 * TT * (H + P) * (int)sizeof(OpT) + TT * 4 + 16 * 4;
-  constexpr int comb = 2 * (LINATTN ? 1 : 3) * (H / 32) * 16 * 64 * 4;
-  return tiles > comb ? tiles : comb;
+  constexpr int NMAT = LINATTN ? 1 : 3;
+  constexpr int QS = 32 / Mfma<OpT>::KSTEP;
+  constexpr int FRAG = (int)sizeof(typename Mfma<OpT>::frag);
+  return 4 * TT * (H + P) * (int)sizeof(OpT) + (2 * TT + 16) * 4 + NWAVE * NMAT * QS * 64 * FRAG;
+}
+
+// sigmoid through the hardware exp2 and reciprocal (about 1 ulp each; the results feed 16-bit
+// MFMA operands). Saturates to 0 / 1 for large |a|.
+__device__ __forceinline__ float sigmoid_fast(float a) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
 }
 
 template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID>
 __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int npairs) {
   static_assert(H <= 128, "register budget");
   typedef Mfma<OpT> M;
+  typedef typename M::frag frag;
   constexpr int P = Pad<OpT>::v;
   constexpr int LDK = H + P;
+  constexpr int TILE = TT * LDK;            // elements of one staged tensor tile
   constexpr int CB = H / 32;
+  constexpr int CH = (CB + 1) / 2;          // output column blocks per wave
   constexpr int KS = H / M::KSTEP;          // forward K steps over h
   constexpr int QS = 32 / M::KSTEP;         // contraction K steps over a 32-token half
   constexpr int NMAT = LINATTN ? 1 : 3;
   constexpr int NWM = LINATTN ? 2 : 3;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  OpT* Ks = reinterpret_cast<OpT*>(smem);   // [TT][LDK]
-  OpT* Vs = Ks + TT * LDK;                  // [TT][LDK]
-  float* eta_s = reinterpret_cast<float*>(Vs + TT * LDK);
-  float* red = eta_s + TT;
-  float* comb = reinterpret_cast<float*>(smem);  // reused after the token loop
+  OpT* tiles = reinterpret_cast<OpT*>(smem);                  // [2 buffers][K, V][TT][LDK]
+  float* eta_s = reinterpret_cast<float*>(tiles + 4 * TILE);  // [2 buffers][TT]
+  float* red = eta_s + 2 * TT;                                // [16]
+  frag* xch = reinterpret_cast<frag*>(red + 16);              // [NWAVE][NMAT][QS][64]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int njb = a.rh / RB;
@@ -308,17 +325,25 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
   const int pair = group / nseg, seg = group % nseg;
   const int t_begin = a.t_base + seg * a.seg_len;
   const int t_end = min(t_begin + a.seg_len, a.t_limit);
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + TT - 1) / TT : 0;
   const int jh = w & 1, th = w >> 1;
+  const int cb0 = th * CH;                  // first output column block of this wave
 
   const IoT* Kp = reinterpret_cast<const IoT*>(a.K) + pair * a.tok_pair_stride;
   const IoT* Vp = reinterpret_cast<const IoT*>(a.V) + pair * a.tok_pair_stride;
   const float* ep = a.eta + pair * a.eta_pair_stride;
 
   TileStage<IoT, OpT, H> stage;
-  stage.load(Kp, Vp, t_begin, t_end, tid);
+  float ev = 0.f;
+  auto fetch = [&](int i) {
+    const int t0 = t_begin + i * TT;
+    stage.load(Kp, Vp, t0, t_end, tid);
+    if (tid < TT) ev = (t0 + tid < t_end) ? ep[t0 + tid] : 0.f;
+  };
+  if (ntiles > 0) fetch(0);
 
   // fast-weight slices as B fragments: lane (n = j, k = c) of rows jb*64 + jh*32 + (lane & 31)
-  typename M::frag wf[NWM][KS];
+  frag wf[NWM][KS];
   {
     const OpT* src[3] = {reinterpret_cast<const OpT*>(a.W0T), reinterpret_cast<const OpT*>(a.W2T),
                          reinterpret_cast<const OpT*>(a.W1)};
@@ -338,98 +363,128 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
     mx = block_max(mx, red);
     if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
   }
+  auto put = [&](int i) {
+    OpT* b = tiles + (i & 1) * 2 * TILE;
+    stage.store(b, b + TILE, LDK, tid);
+    if (tid < TT) eta_s[(i & 1) * TT + tid] = ev * scale;
+  };
 
-  f32x16 acc[NMAT][CB];
+  f32x16 acc[NMAT][CH];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int c = 0; c < CB; ++c) zero(acc[m][c]);
+    for (int c = 0; c < CH; ++c) zero(acc[m][c]);
 
-  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
-    __syncthreads();
-    stage.store(Ks, Vs, LDK, tid);
-    if (tid < TT) eta_s[tid] = (t0 + tid < t_end) ? ep[t0 + tid] * scale : 0.f;
-    __syncthreads();
-    if (t0 + TT < t_end) stage.load(Kp, Vp, t0 + TT, t_end, tid);
-
-    // forward: C[t][j] for tokens th*32.., hidden jh*32..
-    f32x16 fa, fb, fd;
-    zero(fa);
-    zero(fb);
-    zero(fd);
-    {
-      const OpT* kr = Ks + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
-      const OpT* vr = Vs + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
+  // forward of the tile in buffer `b` (tokens th*32.., hidden jh*32..) into F, with the epilogue
+  // of the previous tile's Fp (eta from ebuf) interleaved when EPI is set:
+  // Fp[0] <- eta*H, Fp[1] <- X0, Fp[2] <- X2
+  auto fwd_epi = [&](const OpT* b, f32x16 (&F)[3], f32x16 (&Fp)[3], const float* ebuf, auto EPI) {
+    constexpr bool DO_EPI = decltype(EPI)::value;
+    const OpT* kr = b + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
+    const OpT* vr = kr + TILE;
+    const float* er = ebuf + th * 32 + 4 * (lane >> 5);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const auto kf = M::load(kr + s * M::KSTEP);
-        fa = M::mma(kf, wf[0][s], fa);
-        fb = M::mma(kf, wf[1][s], fb);
-        if constexpr (!LINATTN) fd = M::mma(M::load(vr + s * M::KSTEP), wf[2][s], fd);
-      }
-    }
-    // epilogue in registers: fa <- eta*H, fb <- X0, fd <- X2 (element r: t = th*32 + acc_row)
+    for (int m = 0; m < 3; ++m) zero(F[m]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = eta_s[th * 32 + acc_row(r, lane)];
-      const float A = fa[r], Bm = fb[r];
-      const float sg = sigmoidf_(A);
-      const float sil = A * sg;
-      fa[r] = e * sil * Bm;
-      if constexpr (!LINATTN) {
-        const float D = e * fd[r];
-        fb[r] = D * Bm * (sg * (1.f + A * (1.f - sg)));
-        fd[r] = D * sil;
-      }
-    }
-    // token contractions over this wave's 32 tokens
-    const OpT* kb = Ks + th * 32 * LDK;
-    const OpT* vb = Vs + th * 32 * LDK;
+    for (int s = 0; s < KS; ++s) {
+      const auto kf = M::load(kr + s * M::KSTEP);
+      F[0] = M::mma(kf, wf[0][s], F[0]);
+      F[1] = M::mma(kf, wf[1][s], F[1]);
+      if constexpr (!LINATTN) F[2] = M::mma(M::load(vr + s * M::KSTEP), wf[2][s], F[2]);
+      if constexpr (DO_EPI) {
 #pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const auto ah = acc_to_afrag<OpT>(fa, q);
-      typename M::frag a0, a2;
-      if constexpr (!LINATTN) {
-        a0 = acc_to_afrag<OpT>(fb, q);
-        a2 = acc_to_afrag<OpT>(fd, q);
-      }
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        acc[0][c] = M::mma(ah, acc_kfrag_tr<OpT>(vb + c * 32, LDK, q, lane), acc[0][c]);
-        if constexpr (!LINATTN) {
-          const auto bk = acc_kfrag_tr<OpT>(kb + c * 32, LDK, q, lane);
-          acc[1][c] = M::mma(a0, bk, acc[1][c]);
-          acc[2][c] = M::mma(a2, bk, acc[2][c]);
+        for (int r = 16 * s / KS; r < 16 * (s + 1) / KS; ++r) {
+          const float e = er[8 * (r >> 2) + (r & 3)];
+          const float A = Fp[0][r], Bm = Fp[1][r];
+          const float sg = sigmoid_fast(A);
+          const float sil = A * sg;
+          const float eB = e * Bm;
+          Fp[0][r] = sil * eB;
+          if constexpr (!LINATTN) {
+            const float Dr = Fp[2][r];
+            Fp[1][r] = (eB * Dr) * (sg * fmaf(A, 1.f - sg, 1.f));
+            Fp[2][r] = (e * sil) * Dr;
+          }
         }
       }
     }
-  }
-
-  // sum the token halves in LDS (wave (jh, 1) hands its tiles to wave (jh, 0)), then store
-  __syncthreads();
-  float* cb_ = comb + (size_t)jh * NMAT * CB * 16 * 64;
-  if (th == 1) {
+  };
+  // token contractions of the tile in buffer `b`: own token half from registers, then the
+  // partner's half from the exchange area; output columns (cb0 + cc) * 32..
+  auto contract = [&](const OpT* b, const f32x16 (&F)[3]) {
+    frag own[NMAT][QS];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
+      for (int q = 0; q < QS; ++q) {
+        own[m][q] = acc_to_afrag<OpT>(F[m], q);
+        xch[((w * NMAT + m) * QS + q) * 64 + lane] = own[m][q];
+      }
+    __syncthreads();  // partner fragments published
+    const frag* pf = xch + (size_t)(w ^ 2) * NMAT * QS * 64 + lane;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cb_[((m * CB + c) * 16 + r) * 64 + lane] = acc[m][c][r];
+    for (int half = 0; half < 2; ++half) {
+      const OpT* kb = b + (half == 0 ? th : 1 - th) * 32 * LDK;
+      const OpT* vb = kb + TILE;
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        frag am[NMAT];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) am[m] = half == 0 ? own[m][q] : pf[(m * QS + q) * 64];
+#pragma unroll
+        for (int cc = 0; cc < CH; ++cc) {
+          const int c = cb0 + cc;
+          if (CB % 2 == 0 || c < CB) {
+            // am[0] = eta H (with V) -> P1; am[1] = X0 (with K) -> P0; am[2] = X2 (with K) -> P2
+            acc[0][cc] = M::mma(am[0], acc_kfrag_tr<OpT>(vb + c * 32, LDK, q, lane), acc[0][cc]);
+            if constexpr (!LINATTN) {
+              const auto bk = acc_kfrag_tr<OpT>(kb + c * 32, LDK, q, lane);
+              acc[1][cc] = M::mma(am[1], bk, acc[1][cc]);
+              acc[2][cc] = M::mma(am[2], bk, acc[2][cc]);
+            }
+          }
+        }
+      }
+    }
+  };
+  // one pipeline step: publish tile i+1, prefetch tile i+2, forward(i+1) || epilogue(i),
+  // contractions(i). At the last tile the forward reruns on the other buffer's stale (or unset)
+  // contents and its result is discarded, which keeps the step free of branches.
+  auto step = [&](int i, f32x16 (&Fc)[3], f32x16 (&Fn)[3]) {
+    __syncthreads();  // every wave is done with buffer (i+1)&1 and the exchange area
+    if (i + 1 < ntiles) {
+      put(i + 1);
+      if (i + 2 < ntiles) fetch(i + 2);
+    }
+    __syncthreads();  // tile i+1 published
+    fwd_epi(tiles + ((i + 1) & 1) * 2 * TILE, Fn, Fc, eta_s + (i & 1) * TT, std::true_type{});
+    contract(tiles + (i & 1) * 2 * TILE, Fc);
+  };
+
+  if (ntiles > 0) {
+    f32x16 F0[3], F1[3];
+    put(0);
+    if (ntiles > 1) fetch(1);
+    __syncthreads();
+    fwd_epi(tiles, F0, F1, eta_s, std::false_type{});
+    for (int i = 0; i < ntiles; i += 2) {
+      step(i, F0, F1);
+      if (i + 1 < ntiles) step(i + 1, F1, F0);
+    }
   }
-  __syncthreads();
-  if (th == 0) {
-    const float inv = 1.f / scale;
-    float* ob = a.out + seg * a.out_y_stride + pair * a.out_pair_stride;
+
+  const float inv = 1.f / scale;
+  float* ob = a.out + seg * a.out_y_stride + pair * a.out_pair_stride;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      // acc[0] = P1 (eta H with V), acc[1] = P0 (X0 with K), acc[2] = P2 (X2 with K)
-      const int omat = LINATTN ? 0 : (m == 0 ? 1 : (m == 1 ? 0 : 2));
+  for (int m = 0; m < NMAT; ++m) {
+    const int omat = LINATTN ? 0 : (m == 0 ? 1 : (m == 1 ? 0 : 2));
 #pragma unroll
-      for (int c = 0; c < CB; ++c) {
+    for (int cc = 0; cc < CH; ++cc) {
+      const int c = cb0 + cc;
+      if (CB % 2 == 0 || c < CB) {
         float* o = ob + omat * a.out_mat_stride + ((int64_t)jb * RB + jh * 32) * H + c * 32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          o[acc_row(r, lane) * H + acc_col(lane)] = (acc[m][c][r] + cb_[((m * CB + c) * 16 + r) * 64 + lane]) * inv;
+        for (int r = 0; r < 16; ++r) o[acc_row(r, lane) * H + acc_col(lane)] = acc[m][cc][r] * inv;
       }
     }
   }

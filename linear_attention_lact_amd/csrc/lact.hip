@@ -44,8 +44,8 @@ __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float
   if (mat == 1) sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(v);
 }
 
-// renorm targets (column norms of the initial row-form weights over their input axis) and the
-// barrier counters / error word. grid (3, P), block 256.
+// renorm targets (column norms of the initial row-form weights over their input axis).
+// grid (3, P), block 256; the row loop is unrolled so that eight loads are in flight.
 __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const float* W0, const float* W1,
                                                         const float* W2, int H, int64_t w_batch_stride) {
   const int mat = blockIdx.x, pair = blockIdx.y;
@@ -57,33 +57,26 @@ __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const floa
   const int cols = mat == 1 ? h : rh, rows = mat == 1 ? rh : h;  // row-form [rows][cols]
   for (int j = threadIdx.x; j < cols; j += 256) {
     float acc = 0.f;
+#pragma unroll 8
     for (int r = 0; r < rows; ++r) acc += src[(int64_t)r * cols + j] * src[(int64_t)r * cols + j];
     nu[j] = sqrtf(acc);
   }
-  unsigned* cnt = s.sync + ((int64_t)pair * 3 + mat) * SYNC_LINE;
-  if (threadIdx.x < SYNC_LINE) cnt[threadIdx.x] = 0u;
-  if (mat == 0 && pair == 0 && threadIdx.x == 0) s.sync[(int64_t)s.P * 3 * SYNC_LINE] = 0u;
 }
 
-// finalize: state and momentum back to the API's row form, one thread per output element;
-// a raised error word (barrier timeout or XCD mismatch) poisons the outputs with NaN.
+// finalize: state and momentum back to the API's row form, one thread per output element.
 // grid (ceil(n/256), 3, P), block 256.
-template <class IoT>
 __global__ void __launch_bounds__(256) lact_final_kernel(LactState s, float* W0o, float* W1o, float* W2o,
-                                                        float* Mo, IoT* O, int64_t o_pair_stride) {
+                                                        float* Mo) {
   const int mat = blockIdx.y, pair = blockIdx.z;
   const int h = s.h, rh = s.rh;
   const int64_t n = (int64_t)rh * h;
   const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (d >= n) return;
-  const bool bad = s.sync[(int64_t)s.P * 3 * SYNC_LINE] != 0u;
   // row-form element d: W1 [rh][h] is the state layout; W0/W2 [h][rh] element [c][j]
   const int64_t e = (mat == 1) ? d : (int64_t)(d % rh) * h + d / rh;
-  const float nan = __builtin_nanf("");
   float* wo = (mat == 0 ? W0o : mat == 1 ? W1o : W2o);
-  if (wo) wo[(int64_t)pair * n + d] = bad ? nan : s.W[((int64_t)pair * 3 + mat) * n + e];
-  if (Mo) Mo[((int64_t)pair * 3 + mat) * n + d] = bad ? nan : s.M[((int64_t)pair * 3 + mat) * n + e];
-  if (bad && O && mat == 0 && d == 0) Io<IoT>::store(O + pair * o_pair_stride, nan);
+  if (wo) wo[(int64_t)pair * n + d] = s.W[((int64_t)pair * 3 + mat) * n + e];
+  if (Mo) Mo[((int64_t)pair * 3 + mat) * n + d] = s.M[((int64_t)pair * 3 + mat) * n + e];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -298,31 +291,28 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
 
   // update path: LDS-resident kernel for the (h, rh) shapes it is built for, else the fallback
   const void* uk = nullptr;
-  int ug = 1, ulds = 0;
-#define TTT_UPD(HH, RR)                                                                     \
-  if (H == HH && rh == RR) {                                                                \
-    constexpr int g2 = update_lds_bytes<HH, RR, 1>() > 150 * 1024 ? 2 : 1;                  \
-    uk = reinterpret_cast<const void*>(lact_update_kernel<OpT, HH, RR, g2>);                 \
-    ug = g2;                                                                                \
-    ulds = update_lds_bytes<HH, RR, g2>();                                                  \
+  int ulds = 0;
+#define TTT_UPD(HH, RR)                                                  \
+  if (H == HH && rh == RR) {                                             \
+    uk = reinterpret_cast<const void*>(lact_update_kernel<OpT, HH, RR>); \
+    ulds = update_lds_bytes<HH, RR>();                                   \
   }
-  if constexpr (H == 32) { TTT_UPD(32, 64) TTT_UPD(32, 128) }
-  if constexpr (H == 64) { TTT_UPD(64, 128) TTT_UPD(64, 256) }
-  if constexpr (H == 96) { TTT_UPD(96, 192) TTT_UPD(96, 384) }
-  if constexpr (H == 128) { TTT_UPD(128, 256) }
+  // With Muon the LDS kernel evaluates Newton-Schulz through the h x h Gram matrix, whose
+  // rounding grows with the conditioning of the write (weak directions are amplified by up to
+  // 3.4445^5). It is used for 16-bit I/O when a chunk has at least h tokens (the write can have
+  // full rank); fp32 I/O and shorter chunks keep the five explicit X rounds (fallback kernel).
+  const bool gram_ok = !p.muon || (sizeof(OpT) == 2 && p.chunk_kv >= H);
+  if (gram_ok) {
+    if constexpr (H == 32) { TTT_UPD(32, 64) TTT_UPD(32, 128) }
+    if constexpr (H == 64) { TTT_UPD(64, 128) TTT_UPD(64, 256) }
+    if constexpr (H == 96) { TTT_UPD(96, 192) TTT_UPD(96, 384) }
+    if constexpr (H == 128) { TTT_UPD(128, 256) }
+  }
 #undef TTT_UPD
   if (uk) {
     TTT_HIP(hipFuncSetAttribute(uk, hipFuncAttributeMaxDynamicSharedMemorySize, ulds));
   }
-  const int M = 3 * P;
-  const unsigned ugrid = ug == 2 ? 16u * (unsigned)((M + 7) / 8) : (unsigned)M;
-  if (uk && ug == 2) {  // the two parts of a matrix wait for each other: all must be resident
-    int dev = 0, ncu = 0, per_cu = 0;
-    TTT_HIP(hipGetDevice(&dev));
-    TTT_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-    TTT_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, uk, 512, ulds));
-    if ((long)per_cu * ncu < (long)ugrid) uk = nullptr;  // too many matrices at once: fallback
-  }
+  const unsigned ugrid = (unsigned)(3 * P);
 
   const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
   for (int c = 0; c < nch; ++c) {
@@ -345,13 +335,10 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
       }
       TTT_HIP(hipGetLastError());
     }
-    ua.chunk = c;
     {
       LaunchTimer lt(K_LACT_UPDATE, st);
       void* args[] = {&ua};
-      if (uk && ug == 2) {
-        TTT_HIP(hipLaunchCooperativeKernel(uk, dim3(ugrid), dim3(512), args, (unsigned)ulds, st));
-      } else if (uk) {
+      if (uk) {
         TTT_HIP(hipLaunchKernel(uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
       } else {
         hipLaunchKernelGGL(lact_update_global_kernel<OpT>, dim3(3, P), dim3(512), 0, st, ua);
@@ -365,8 +352,8 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     }
   }
   LaunchTimer lt_fin(K_LACT_FINAL, st);
-  hipLaunchKernelGGL(lact_final_kernel<IoT>, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0o,
-                     W1o, W2o, Mo, reinterpret_cast<IoT*>(O), (int64_t)p.Nq * H);
+  hipLaunchKernelGGL(lact_final_kernel, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0o, W1o,
+                     W2o, Mo);
   TTT_HIP(hipGetLastError());
   return TTT_OK;
 }
@@ -417,10 +404,9 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   const size_t oNu = plan.add((size_t)P * 3 * NU * 4);
   const size_t oSh = plan.add((size_t)P * 4 * n * opsz);
   const size_t oPart = plan.add((size_t)S * P * 3 * n * 4);
+  const size_t oU = plan.add((size_t)P * 3 * n * 4);
   const int64_t NSZ = 4 * n + 2 * (int64_t)h * h;
   const size_t oNs = plan.add((size_t)P * 3 * NSZ * 4);
-  const size_t oXb = plan.add((size_t)P * 3 * 4 * h * h * 4);
-  const size_t oSync = plan.add(((size_t)P * 3 + 1) * SYNC_LINE * 4);
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -435,9 +421,8 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   s.nu = reinterpret_cast<float*>(ws + oNu);
   s.sh = ws + oSh;
   s.part = reinterpret_cast<float*>(ws + oPart);
+  s.U = reinterpret_cast<float*>(ws + oU);
   s.ns = reinterpret_cast<float*>(ws + oNs);
-  s.xbuf = reinterpret_cast<float*>(ws + oXb);
-  s.sync = reinterpret_cast<unsigned*>(ws + oSync);
   s.P = P;
   s.h = h;
   s.rh = rh;

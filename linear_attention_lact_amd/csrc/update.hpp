@@ -1,24 +1,25 @@
-// update.hpp -- batched per-matrix write of the LaCT fast weights (gfx950).
+// update.hpp -- per-chunk write of the LaCT fast weights (gfx950).
 //
-// One launch per chunk covers every (pair, matrix) of the call. For each matrix in the
-// update mask ("Test-Time Training Done Right" notes, section 2.2):
+// One launch per chunk covers every (pair, matrix) of the call, one workgroup per matrix. For
+// each matrix in the update mask ("Test-Time Training Done Right" notes, section 2.2):
 //   G = -(sum of the token-segment partial products, in segment order)
 //   U = G, or M = momentum * M + G and U = M         (heavy-ball momentum fed to the operator)
-//   U = NS5(U) if Muon: X = U / (||U||_F + eps), five rounds of
-//       A = X X^T, B = b A + c A A, X = a X + B X, on the wide orientation X (h x rh)
+//   U = NS5(U) if Muon: X = U / (||U||_F + eps) on the wide orientation X (h x rh), five rounds
+//       of A = X X^T, B = b A + c A A, X = a X + B X
 //   W = W - U, then each output column renormalised over its inputs to its initial norm
 //   fp16/bf16/fp32 operand shadows of the new W for the next chunk's products.
-// Newton-Schulz runs in split-bf16 (x = hi + lo, three MFMA products per multiply) because the
-// iteration amplifies rounding in weak singular directions by up to 3.4445^5; fp32 state.
 //
-// Work split: the wide X is split by columns into G parts (G = 2 for rh = 256), one
-// workgroup each, both on the same XCD. Each workgroup keeps its X columns and the full h x h
-// Gram / polynomial matrix in LDS (fp32) and forms bf16 hi/lo fragments on the fly. Per round
-// the partial Gram matrices are exchanged through L2 (xcd_sync.hpp); A^2 is formed redundantly
-// by both workgroups so that one exchange per round suffices.
+// Newton-Schulz is evaluated through the h x h Gram matrix instead of the h x rh iterate. Every
+// round multiplies X on the left by P_k = a I + b A_k + c A_k^2 with A_k = X_k X_k^T, so
+//   X_5 = Q X_0 with Q = P_4 P_3 P_2 P_1 P_0,  A_{k+1} = P_k A_k P_k
+// (P_k is a polynomial in A_k; all of them commute). The result equals the five X rounds up to
+// rounding order, while the rounds touch only h x h matrices: X_0 enters twice (A_0 and the
+// final Q X_0), streamed from L2 in 64-row chunks, so one workgroup holds a whole matrix and no
+// workgroups need to exchange data. Products run in split-bf16 (x = hi + lo, three MFMA products
+// per multiply) because the iteration amplifies rounding in weak singular directions by up to
+// 3.4445^5; fp32 state, fp32 matrix masters in registers.
 #pragma once
 #include "common.hpp"
-#include "xcd_sync.hpp"
 
 namespace ttt {
 
@@ -31,9 +32,8 @@ struct LactState {
   float* nu;       // [P][3][NU] renorm targets (W0T/W2T: per row j; W1: per column c)
   void* sh;        // operand shadows [P][4][rh*h] (W0T, W2T, W1, W1T)
   float* part;     // token-segment partial products [S][P][3][rh*h]
+  float* U;        // the write before Newton-Schulz [P][3][rh*h] (scratch)
   float* ns;       // global NS5 scratch [P][3][NSZ] (large-h path)
-  float* xbuf;     // exchange buffers [P*3][2 parity][2 parts][h*h]
-  unsigned* sync;  // [P*3][SYNC_LINE] barrier counters, then error word at sync[P*3*SYNC_LINE]
   int P, h, rh, NU;
   int64_t NSZ;
 };
@@ -44,7 +44,6 @@ struct UpdateArgs {
   uint32_t mask;
   int muon, weight_norm;
   float momentum, eps_norm, eps_ns;
-  int chunk;           // chunk index (barrier targets continue across launches)
 };
 
 typedef __bf16 bf16;
@@ -55,339 +54,449 @@ __device__ __forceinline__ void split_store(bf16* hi, bf16* lo, float v) {
   *lo = static_cast<bf16>(v - static_cast<float>(h));
 }
 
-// Split-bf16 products for a 32 x 64 output block (two 32 x 32 tiles sharing the A rows):
-//   c_t += (Ah + Al)[32 x K] * (Bh + Bl)^T, dropping the lo*lo term.
-// A rows are K-contiguous (lda). B is either n-major (rows n, K-contiguous; TR = false) or
-// K-major (rows k, n-contiguous; TR = true, read with the LDS transpose read). `two` = false
-// computes only the first tile.
-template <int K, bool TR>
-__device__ __forceinline__ void mma_split_2t(f32x16& c0, f32x16& c1, const bf16* Ah, const bf16* Al, int lda,
-                                             const bf16* Bh, const bf16* Bl, int ldb, bool two, int lane) {
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// hi / lo bf16 pair of four consecutive values (x = hi + lo to ~2^-16 relative), 8-byte stores
+__device__ __forceinline__ void split_store4(bf16* hi, bf16* lo, f32x4 v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h[q] = static_cast<bf16>(v[q]);
+    l[q] = static_cast<bf16>(v[q] - static_cast<float>(h[q]));
+  }
+  *reinterpret_cast<bf16x4*>(hi) = h;
+  *reinterpret_cast<bf16x4*>(lo) = l;
+}
+
+template <class T>
+__device__ __forceinline__ void store4(T* p, f32x4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(p) = v;
+  } else {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = Mfma<T>::from_f32(v[q]);
+    *reinterpret_cast<t4*>(p) = o;
+  }
+}
+
+// Split-bf16 product of Q consecutive 32 x 32 output blocks that share their A rows:
+//   c[q] += (Ah + Al)[32 x K] (Bh + Bl)[block q]^T, the lo*lo term dropped.
+// TA / TB: operand stored K-major (element (k, m) at base[k * ld + m], LDS transpose read);
+// otherwise row-major with K contiguous (element (m, k) at base[m * ld + k]).
+// B block q starts at Bh + q * 32 (TB) or Bh + q * 32 * ldb. The hi*hi and the cross products
+// accumulate in separate registers and are added at the end.
+template <int K, int Q, bool TA, bool TB>
+__device__ __forceinline__ void mma_split(f32x16 (&c)[Q], const bf16* Ah, const bf16* Al, int lda,
+                                          const bf16* Bh, const bf16* Bl, int ldb, int lane) {
   typedef Mfma<bf16> M;
-  const int ao = (lane & 31) * lda + (lane >> 5) * 8;
-  const int bo = (lane & 31) * ldb + (lane >> 5) * 8;
+  const int ro = lane & 31, ko = (lane >> 5) * 8;
+  f32x16 d[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) zero(d[q]);
 #pragma unroll 1
   for (int k = 0; k < K; k += 16) {
-    const bf16x8 ah = M::load(Ah + ao + k), al = M::load(Al + ao + k);
-    bf16x8 b0h, b0l, b1h, b1l;
-    if constexpr (TR) {
-      b0h = load_frag_tr<bf16>(Bh, ldb, k, lane);
-      b0l = load_frag_tr<bf16>(Bl, ldb, k, lane);
+    bf16x8 ah, al;
+    if constexpr (TA) {
+      ah = load_frag_tr<bf16>(Ah, lda, k, lane);
+      al = load_frag_tr<bf16>(Al, lda, k, lane);
     } else {
-      b0h = M::load(Bh + bo + k);
-      b0l = M::load(Bl + bo + k);
+      ah = M::load(Ah + ro * lda + ko + k);
+      al = M::load(Al + ro * lda + ko + k);
     }
-    c0 = M::mma(ah, b0h, c0);
-    c0 = M::mma(ah, b0l, c0);
-    c0 = M::mma(al, b0h, c0);
-    if (two) {
-      if constexpr (TR) {
-        b1h = load_frag_tr<bf16>(Bh + 32, ldb, k, lane);
-        b1l = load_frag_tr<bf16>(Bl + 32, ldb, k, lane);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      bf16x8 bh, bl;
+      if constexpr (TB) {
+        bh = load_frag_tr<bf16>(Bh + q * 32, ldb, k, lane);
+        bl = load_frag_tr<bf16>(Bl + q * 32, ldb, k, lane);
       } else {
-        b1h = M::load(Bh + 32 * ldb + bo + k);
-        b1l = M::load(Bl + 32 * ldb + bo + k);
+        bh = M::load(Bh + (q * 32 + ro) * ldb + ko + k);
+        bl = M::load(Bl + (q * 32 + ro) * ldb + ko + k);
       }
-      c1 = M::mma(ah, b1h, c1);
-      c1 = M::mma(ah, b1l, c1);
-      c1 = M::mma(al, b1h, c1);
+      c[q] = M::mma(ah, bh, c[q]);
+      d[q] = M::mma(ah, bl, d[q]);
+      d[q] = M::mma(al, bh, d[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) c[q] += d[q];
+}
+
+// Blocks t = Q*w + q (q < Q) of an NB-block output grid with BPR blocks per row: block t is
+// (t / BPR, t % BPR), its A operand the 32-block t / BPR, its B operand the 32-block t % BPR.
+// A wave's blocks share their A operand when BPR % Q == 0; otherwise each is formed alone.
+template <int K, int Q, int BPR, int NB, bool TA, bool TB>
+__device__ __forceinline__ void mma_blocks(f32x16 (&c)[Q], int w, const bf16* Ah, const bf16* Al, int lda,
+                                           const bf16* Bh, const bf16* Bl, int ldb, int lane) {
+  auto aoff = [&](int b) { return TA ? b * 32 : b * 32 * lda; };
+  auto boff = [&](int b) { return TB ? b * 32 : b * 32 * ldb; };
+  if constexpr (BPR % Q == 0) {
+    const int t0 = Q * w;
+    if (t0 < NB)
+      mma_split<K, Q, TA, TB>(c, Ah + aoff(t0 / BPR), Al + aoff(t0 / BPR), lda, Bh + boff(t0 % BPR),
+                              Bl + boff(t0 % BPR), ldb, lane);
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int t = Q * w + q;
+      if (t < NB) {
+        f32x16 one[1] = {c[q]};
+        mma_split<K, 1, TA, TB>(one, Ah + aoff(t / BPR), Al + aoff(t / BPR), lda, Bh + boff(t % BPR),
+                                Bl + boff(t % BPR), ldb, lane);
+        c[q] = one[0];
+      }
     }
   }
 }
 
-template <int H, int RH, int G>
+// Row stride (16-bit elements) of a chunk read with the LDS transpose read: rows 0..3 of a
+// 16-lane group then fall into disjoint 16-bank windows.
+constexpr int gram_ld(int h) {
+  int l = h + 4;
+  while ((l / 2) % 32 != 16) l += 4;
+  return l;
+}
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int H, int RH>
 struct UpdLayout {
-  static constexpr int RHG = RH / G;          // X columns (state rows) per workgroup
-  static constexpr int LDX = RHG + 8;         // bf16 row stride of X hi / lo  [H][LDX]
-  static constexpr int LDA = H + 8;           // bf16 row stride of A hi / lo  [H][LDA]
-  static constexpr int LDW = RHG + 4;         // fp32 row stride of the new W  [H][LDW]
-  static constexpr int XB = 2 * H * LDX * 2;  // bytes of X hi + lo
-  static constexpr int AB = 2 * H * LDA * 2;
-  static constexpr int WB = H * LDW * 4;
-  static constexpr int RB = AB > WB ? AB : WB; // A hi/lo and the new W share one region
-  static constexpr int bytes = XB + RB + (2 * H + 32) * 4;
+  static constexpr int JC = 64;                // state rows per streamed chunk of X^T
+  static constexpr int NCH = RH / JC;
+  static constexpr int LDA = H + 8;            // h x h matrices: bf16 hi / lo [H][LDA]
+  static constexpr int SLOT = 2 * H * LDA * 2;
+  static constexpr int LDG = gram_ld(H);       // X^T chunk for the Gram product (transpose reads)
+  static constexpr int LDF = H + 8;            // X^T chunk for the final product (row reads)
+  static constexpr int CHG = 2 * JC * LDG * 2;
+  static constexpr int CHF = 2 * JC * LDF * 2;
+  static constexpr int LDW = H + 4;            // fp32 staging of the new state [RH][LDW]
+  static constexpr int WB = RH * LDW * 4;
+  static constexpr int R = cmax(cmax(2 * SLOT, 2 * CHG), cmax(SLOT + 2 * CHF, WB));
+  static constexpr int NF = RH > H ? RH : H;
+  static constexpr int bytes = R + (2 * NF + 512 + 32) * 4;
+  static constexpr int HB = H / 32;
+  static constexpr int NBA = HB * HB, QA = (NBA + 7) / 8;   // h x h blocks per wave
+  static constexpr int NBF = HB * (JC / 32);                // final-product blocks per chunk
+  static_assert(RH % JC == 0 && H % 32 == 0 && NBF <= 8, "shape");
 };
 
-template <int H, int RH, int G>
-constexpr int update_lds_bytes() { return UpdLayout<H, RH, G>::bytes; }
+template <int H, int RH>
+constexpr int update_lds_bytes() { return UpdLayout<H, RH>::bytes; }
 
-// grid: G * 8 * ceil(M / 8) workgroups for M = 3 * P matrices (G == 2: the parts of a matrix
-// are workgroups w and w + 8, i.e. on one XCD); block 512 threads (8 waves).
-template <class OpT, int H, int RH, int G>
+// grid: 3 * P workgroups (one per matrix); block 512 threads (8 waves).
+// h x h block t = QA*w + q of wave w: rows c = (t / HB)*32 + acc_row, columns
+// c' = (t % HB)*32 + acc_col. Every product is stored through its transposed block (the 4
+// consecutive accumulator rows of a lane become one 8-byte run), so slot contents are the
+// transposes of the masters; each product reads them in the orientation that gives the exact
+// (not symmetry-assumed) result wherever a matrix is symmetric only up to rounding: Q's
+// dynamic range (up to 3.4445^5 in weak directions) amplifies any such asymmetry.
+template <class OpT, int H, int RH>
 __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
-  static_assert(G == 1 || G == 2, "parts");
-  typedef UpdLayout<H, RH, G> L;
-  constexpr int RHG = L::RHG, LDX = L::LDX, LDA = L::LDA, LDW = L::LDW;
-  constexpr int HB = H / 32, CB = RHG / 32;
-  constexpr int NWV = 8;
+  typedef UpdLayout<H, RH> L;
+  constexpr int JC = L::JC, NCH = L::NCH, LDA = L::LDA, LDG = L::LDG, LDF = L::LDF, LDW = L::LDW;
+  constexpr int HB = L::HB, NBA = L::NBA, QA = L::QA, NBF = L::NBF;
+  constexpr int NE4 = RH * H / 4;              // float4 groups of the matrix
+  constexpr int NG = (NE4 + 511) / 512;
+  constexpr int CG4 = JC * H / 4 / 512 > 0 ? JC * H / 4 / 512 : 1;   // float4 groups per chunk per thread
+  static_assert(JC * H / 4 <= 512 * CG4, "chunk map");
   const LactState& s = u.s;
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16* Xh = reinterpret_cast<bf16*>(smem);                 // [H][LDX]  X columns of this part
-  bf16* Xl = Xh + H * LDX;
-  bf16* Ah = reinterpret_cast<bf16*>(smem + L::XB);         // [H][LDA]  Gram / polynomial matrix
-  bf16* Al = Ah + H * LDA;
-  float* Wn = reinterpret_cast<float*>(smem + L::XB);       // [H][LDW]  new W (after Newton-Schulz)
-  float* cn = reinterpret_cast<float*>(smem + L::XB + L::RB);  // [2H]
-  float* red = cn + 2 * H;                                  // [32]
+  bf16* S1h = reinterpret_cast<bf16*>(smem);                 // slot 1 [H][LDA] hi, then lo
+  bf16* S1l = S1h + H * LDA;
+  bf16* S2h = reinterpret_cast<bf16*>(smem + L::SLOT);       // slot 2
+  bf16* S2l = S2h + H * LDA;
+  float* Wn = reinterpret_cast<float*>(smem);                // [RH][LDW] (after the products)
+  float* fac = reinterpret_cast<float*>(smem + L::R);        // [2 NF]
+  float* cpart = fac + 2 * L::NF;                            // [512]
+  float* red = cpart + 512;                                  // [32]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wg = blockIdx.x;
-  const int part = G == 2 ? ((wg >> 3) & 1) : 0;
-  const int mi = G == 2 ? ((wg & 7) + 8 * (wg >> 4)) : wg;
-  const int M = 3 * s.P;
-  if (mi >= M) return;
+  const int mi = blockIdx.x;
+  if (mi >= 3 * s.P) return;
   const int pair = mi / 3, mat = mi % 3;
   const uint32_t bit = mat == 0 ? 1u : mat == 1 ? 2u : 4u;
   if (!(u.mask & bit)) return;
-  unsigned* err = s.sync + (size_t)M * SYNC_LINE;
-  unsigned* cnt = s.sync + (size_t)mi * SYNC_LINE;
-  if (G == 2 && tid == 0 && hw_xcc_id() != (unsigned)(wg & 7))
-    __hip_atomic_fetch_add(err, 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int nb = G == 2 ? (u.muon ? 1 + NS_STEPS : 0) + (mat == 1 && u.weight_norm ? 1 : 0) : 0;
-  int bi = u.chunk * nb;  // barriers completed by this matrix before this launch
-  float* xb = s.xbuf + (size_t)mi * 4 * H * H;
-  auto xslot = [&](int parity, int p) { return xb + ((size_t)parity * 2 + p) * H * H; };
-
   const int64_t n = (int64_t)RH * H;
-  const int j0 = part * RHG;
   float* W = s.W + ((int64_t)pair * 3 + mat) * n;
   float* Mm = s.M + ((int64_t)pair * 3 + mat) * n;
+  const float* part0 = s.part + ((int64_t)pair * 3 + mat) * n;
   const float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
+  const bool mom = u.momentum != 0.f;
+  // U goes to a buffer of its own that this launch has not read before: the chunk loads below
+  // must not hit lines of M or of the partials that the per-CU L1 still holds from step 1
+  float* Ud = s.U + ((int64_t)pair * 3 + mat) * n;
 
   // ---- 1. gradient from the segment partials (in segment order), momentum -------------------
-  // U is staged transposed in the (still unused) fp32 W region: Wn[c][jl] = U[j0 + jl][c]
+  float ss = 0.f;
   {
     const int64_t seg_stride = (int64_t)s.P * 3 * n;
-    const float* pp = s.part + ((int64_t)pair * 3 + mat) * n;
-    float ss = 0.f;
-    // float4 groups of 4 consecutive c; all segment loads of a group issued together
-#pragma unroll 2
-    for (int e4 = tid; e4 < RHG * H / 4; e4 += 512) {
-      const int jl = (4 * e4) / H, c = (4 * e4) % H;
-      const int64_t idx = (int64_t)(j0 + jl) * H + c;
-      f32x4 g = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < u.S; ++k) g += *reinterpret_cast<const f32x4*>(pp + k * seg_stride + idx);
-      g = -g;
-      f32x4 v = g;
-      if (u.momentum != 0.f) {
-        v = u.momentum * *reinterpret_cast<const f32x4*>(Mm + idx) + g;
-        *reinterpret_cast<f32x4*>(Mm + idx) = v;
+    constexpr int NB8 = NG < 8 ? NG : 8;
+#pragma unroll 1
+    for (int b0 = 0; b0 < NG; b0 += NB8) {
+      f32x4 g[NB8], mv[NB8];
+#pragma unroll
+      for (int i = 0; i < NB8; ++i) {
+        g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mv[i] = g[i];
+        const int e4 = tid + 512 * (b0 + i);
+        if (mom && e4 < NE4) mv[i] = *reinterpret_cast<const f32x4*>(Mm + 4 * e4);
+      }
+      for (int k = 0; k < u.S; ++k) {
+#pragma unroll
+        for (int i = 0; i < NB8; ++i) {
+          const int e4 = tid + 512 * (b0 + i);
+          if (e4 < NE4) g[i] += *reinterpret_cast<const f32x4*>(part0 + k * seg_stride + 4 * e4);
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        Wn[(c + q) * LDW + jl] = v[q];
-        ss += v[q] * v[q];
+      for (int i = 0; i < NB8; ++i) {
+        const int e4 = tid + 512 * (b0 + i);
+        if (e4 >= NE4) continue;
+        f32x4 v = -g[i];
+        if (mom) {
+          v = u.momentum * mv[i] + v;
+          *reinterpret_cast<f32x4*>(Mm + 4 * e4) = v;
+        }
+        *reinterpret_cast<f32x4*>(Ud + 4 * e4) = v;
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
       }
     }
-    float inv = 1.f;
-    if (u.muon) {
-      float tot = block_sum(ss, red);
-      if constexpr (G == 2) {
-        float* mine = xslot(bi & 1, part);
-        if (tid == 0) mine[0] = tot;
-        xcd_barrier(cnt, G * (++bi), err);
-        const float* m0 = xslot((bi - 1) & 1, 0);
-        const float* m1 = xslot((bi - 1) & 1, 1);
-        tot = xcd_load(m0) + xcd_load(m1);
-      }
-      inv = 1.f / (sqrtf(tot) + u.eps_ns);
-    }
-    __syncthreads();
-    // X[c][jl] = U[j0 + jl][c] * inv, as hi / lo
-    for (int e = tid; e < H * RHG; e += 512) {
-      const int c = e / RHG, jl = e % RHG;
-      split_store(Xh + c * LDX + jl, Xl + c * LDX + jl, Wn[c * LDW + jl] * inv);
-    }
-    __syncthreads();
   }
+  float inv = 1.f;
+  if (u.muon) inv = 1.f / (sqrtf(block_sum(ss, red)) + u.eps_ns);
+  __syncthreads();
 
-  // ---- 2. Newton-Schulz-5 ------------------------------------------------------------------
+  // chunk staging: rows ch*JC .. of U (state rows j, h columns) scaled by inv, as X^T hi / lo
+  f32x4 cv[CG4];
+  auto chunk_load = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < CG4; ++i) {
+      const int e4 = tid + 512 * i;
+      cv[i] = e4 < JC * H / 4 ? *reinterpret_cast<const f32x4*>(Ud + (int64_t)ch * JC * H + 4 * e4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto chunk_store = [&](bf16* bh, bf16* bl, int ld) {
+#pragma unroll
+    for (int i = 0; i < CG4; ++i) {
+      const int e4 = tid + 512 * i;
+      if (e4 < JC * H / 4) {
+        const int row = (4 * e4) / H, c = (4 * e4) % H;
+        split_store4(bh + row * ld + c, bl + row * ld + c, cv[i] * inv);
+      }
+    }
+  };
+  auto put_sym = [&](const f32x16 (&v)[QA], bf16* dh, bf16* dl) {
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int t = QA * w + q;
+      if (t < NBA) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c = (t / HB) * 32 + 8 * g4 + 4 * (lane >> 5), c2 = (t % HB) * 32 + (lane & 31);
+          split_store4(dh + c2 * LDA + c, dl + c2 * LDA + c,
+                       f32x4{v[q][4 * g4], v[q][4 * g4 + 1], v[q][4 * g4 + 2], v[q][4 * g4 + 3]});
+        }
+      }
+    }
+  };
+  auto zero_q = [&](f32x16 (&v)[QA]) {
+#pragma unroll
+    for (int q = 0; q < QA; ++q) zero(v[q]);
+  };
+
+  // ---- 2. Newton-Schulz-5 through the Gram matrix ----------------------------------------------
   if (u.muon) {
-    constexpr int PB_A = HB * ((HB + 1) / 2);   // 32 x 64 units of an H x H product
-    constexpr int PB_X = HB * ((CB + 1) / 2);   // 32 x 64 units of the H x RHG product
-    for (int it = 0; it < NS_STEPS; ++it) {
-      // (a) Gram partial over this part's columns (one 32 x 64 unit per wave at most)
-      static_assert(PB_A <= NWV, "Gram units per wave");
-      {
-        const int t = w < PB_A ? w : 0;
-        const bool active = w < PB_A;
-        const int ib = t / ((HB + 1) / 2), kb = 2 * (t % ((HB + 1) / 2));
-        const bool two = active && kb + 1 < HB;
-        f32x16 c0, c1;
-        zero(c0);
-        zero(c1);
-        if (active)
-          mma_split_2t<RHG, false>(c0, c1, Xh + ib * 32 * LDX, Xl + ib * 32 * LDX, LDX, Xh + kb * 32 * LDX,
-                                   Xl + kb * 32 * LDX, LDX, two, lane);
-        if constexpr (G == 1) {
-          if (active) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = ib * 32 + acc_row(r, lane), k = kb * 32 + acc_col(lane);
-              split_store(Ah + i * LDA + k, Al + i * LDA + k, c0[r]);
-              if (two) split_store(Ah + i * LDA + k + 32, Al + i * LDA + k + 32, c1[r]);
-            }
-          }
-        } else {
-          // own partial to L2; after the barrier add the partner's at the same positions
-          // (IEEE addition commutes, so both parts form bitwise the same A)
-          float* mine = xslot(bi & 1, part);
-          if (active) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = ib * 32 + acc_row(r, lane), k = kb * 32 + acc_col(lane);
-              mine[i * H + k] = c0[r];
-              if (two) mine[i * H + k + 32] = c1[r];
-            }
-          }
-          xcd_barrier(cnt, G * (++bi), err);
-          const float* other = xslot((bi - 1) & 1, part ^ 1);
-          if (active) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = ib * 32 + acc_row(r, lane), k = kb * 32 + acc_col(lane);
-              c0[r] += xcd_load(other + i * H + k);
-              if (two) c1[r] += xcd_load(other + i * H + k + 32);
-            }
-          }
-          if (active)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = ib * 32 + acc_row(r, lane), k = kb * 32 + acc_col(lane);
-            split_store(Ah + i * LDA + k, Al + i * LDA + k, c0[r]);
-            if (two) split_store(Ah + i * LDA + k + 32, Al + i * LDA + k + 32, c1[r]);
-          }
-        }
-      }
+    f32x16 am[QA], pm[QA], qm[QA], t[QA];
+    // (a) A_0 = X_0 X_0^T, X_0^T streamed in chunks of JC state rows (double-buffered)
+    zero_q(am);
+    {
+      auto gb = [&](int i) { return reinterpret_cast<bf16*>(smem + (i & 1) * L::CHG); };
+      chunk_load(0);
+      chunk_store(gb(0), gb(0) + JC * LDG, LDG);
+      if (NCH > 1) chunk_load(1);
       __syncthreads();
-      // (b) B = b A + c A A   (A symmetric: its rows serve as the n-major B operand)
-      {
-        constexpr int NQ = (PB_A + NWV - 1) / NWV;
-        f32x16 q0[NQ], q1[NQ];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int t = w + q * NWV;
-          zero(q0[q]);
-          zero(q1[q]);
-          if (t < PB_A) {
-            const int ib = t / ((HB + 1) / 2), kb = 2 * (t % ((HB + 1) / 2));
-            mma_split_2t<H, false>(q0[q], q1[q], Ah + ib * 32 * LDA, Al + ib * 32 * LDA, LDA, Ah + kb * 32 * LDA,
-                                   Al + kb * 32 * LDA, LDA, kb + 1 < HB, lane);
-          }
+#pragma unroll 1
+      for (int ch = 0; ch < NCH; ++ch) {
+        if (ch + 1 < NCH) {
+          bf16* nb = gb(ch + 1);
+          chunk_store(nb, nb + JC * LDG, LDG);
+          if (ch + 2 < NCH) chunk_load(ch + 2);
         }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int t = w + q * NWV;
-          if (t < PB_A) {
-            const int ib = t / ((HB + 1) / 2), kb = 2 * (t % ((HB + 1) / 2));
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = ib * 32 + acc_row(r, lane), k = kb * 32 + acc_col(lane);
-              const int o = i * LDA + k;
-              split_store(Ah + o, Al + o, NS_B * (static_cast<float>(Ah[o]) + static_cast<float>(Al[o])) + NS_C * q0[q][r]);
-              if (kb + 1 < HB)
-                split_store(Ah + o + 32, Al + o + 32,
-                            NS_B * (static_cast<float>(Ah[o + 32]) + static_cast<float>(Al[o + 32])) + NS_C * q1[q][r]);
-            }
-          }
-        }
-        __syncthreads();
-      }
-      // (c) X = a X + B X over this part's columns (X read K-major with the transpose read)
-      {
-        constexpr int NQ = (PB_X + NWV - 1) / NWV;
-        f32x16 q0[NQ], q1[NQ];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int t = w + q * NWV;
-          zero(q0[q]);
-          zero(q1[q]);
-          if (t < PB_X) {
-            const int ib = t / ((CB + 1) / 2), jb = 2 * (t % ((CB + 1) / 2));
-            mma_split_2t<H, true>(q0[q], q1[q], Ah + ib * 32 * LDA, Al + ib * 32 * LDA, LDA, Xh + jb * 32,
-                                  Xl + jb * 32, LDX, jb + 1 < CB, lane);
-          }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int t = w + q * NWV;
-          if (t < PB_X) {
-            const int ib = t / ((CB + 1) / 2), jb = 2 * (t % ((CB + 1) / 2));
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int o = (ib * 32 + acc_row(r, lane)) * LDX + jb * 32 + acc_col(lane);
-              split_store(Xh + o, Xl + o, NS_A * (static_cast<float>(Xh[o]) + static_cast<float>(Xl[o])) + q0[q][r]);
-              if (jb + 1 < CB)
-                split_store(Xh + o + 32, Xl + o + 32,
-                            NS_A * (static_cast<float>(Xh[o + 32]) + static_cast<float>(Xl[o + 32])) + q1[q][r]);
-            }
-          }
-        }
+        bf16* cb = gb(ch);
+        mma_blocks<JC, QA, HB, NBA, true, true>(am, w, cb, cb + JC * LDG, LDG, cb, cb + JC * LDG, LDG, lane);
         __syncthreads();
       }
     }
+    put_sym(am, S1h, S1l);
+    __syncthreads();
+    // (b) five rounds on h x h matrices: slot 1 holds A_k (then P_k A_k, then Q_k), slot 2 P_k
+#pragma unroll 1
+    for (int k = 0; k < NS_STEPS; ++k) {
+      zero_q(t);
+      mma_blocks<H, QA, HB, NBA, false, false>(t, w, S1h, S1l, LDA, S1h, S1l, LDA, lane);  // A_k^2
+#pragma unroll
+      for (int q = 0; q < QA; ++q) {
+        const int tb = QA * w + q;
+        const bool diag = (tb / HB) == (tb % HB);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float id = (diag && acc_row(r, lane) == acc_col(lane)) ? NS_A : 0.f;
+          pm[q][r] = id + NS_B * am[q][r] + NS_C * t[q][r];
+        }
+      }
+      put_sym(pm, S2h, S2l);
+      __syncthreads();
+      if (k + 1 < NS_STEPS) {
+        // C = A^T P^T (slot 1 rows, slot 2 read K-major), stored transposed: slot 1 <- P A in
+        // its own orientation (P A is symmetric only up to rounding, which the rounds amplify)
+        zero_q(t);
+        mma_blocks<H, QA, HB, NBA, false, true>(t, w, S1h, S1l, LDA, S2h, S2l, LDA, lane);
+        __syncthreads();
+        put_sym(t, S1h, S1l);
+        __syncthreads();
+        zero_q(am);
+        mma_blocks<H, QA, HB, NBA, false, false>(am, w, S1h, S1l, LDA, S2h, S2l, LDA, lane);  // (P A) P
+        __syncthreads();
+      }
+      if (k == 0) {
+#pragma unroll
+        for (int q = 0; q < QA; ++q) qm[q] = pm[q];
+      } else {
+        put_sym(qm, S1h, S1l);
+        __syncthreads();
+        zero_q(qm);
+        mma_blocks<H, QA, HB, NBA, false, false>(qm, w, S2h, S2l, LDA, S1h, S1l, LDA, lane);  // P Q
+        __syncthreads();
+      }
+      if (k + 1 < NS_STEPS) {
+        put_sym(am, S1h, S1l);
+        __syncthreads();
+      }
+    }
+    put_sym(qm, S1h, S1l);  // Q in slot 1 for the final product
+    __syncthreads();
   }
 
-  // ---- 3. W = W - U, kept as Wn[c][jl] (fp32); renorm over the input axis -----------------------
-  // U = hi + lo (the split pair carries U to ~2^-16 relative, also without Muon)
-#pragma unroll 4
-  for (int e4 = tid; e4 < RHG * H / 4; e4 += 512) {
-    const int jl = (4 * e4) / H, c = (4 * e4) % H;
-    const f32x4 wv = *reinterpret_cast<const f32x4*>(W + (int64_t)(j0 + jl) * H + c);
+  // ---- 3. W - U per chunk, U = (Q X_0)^T with Muon: block C[c][j] = sum_m Q[c][m] X_0^T[j][m] ---
+  // wave w < NBF owns block (c-block w / (JC/32), j-block w % (JC/32)) of every chunk
+  constexpr int JBC = JC / 32;
+  const bool fact = w < NBF;
+  const int fcb = (w < NBF ? w : 0) / JBC, fjb = (w < NBF ? w : 0) % JBC;
+  auto fcoord = [&](int ch, int g4, int& j, int& c) {
+    c = fcb * 32 + 8 * g4 + 4 * (lane >> 5);
+    j = ch * JC + fjb * 32 + (lane & 31);
+  };
+  f32x16 wn[NCH];
+  {
+    auto fb = [&](int i) { return reinterpret_cast<bf16*>(smem + L::SLOT + (i & 1) * L::CHF); };
+    if (u.muon) {
+      chunk_load(0);
+      chunk_store(fb(0), fb(0) + JC * LDF, LDF);
+      if (NCH > 1) chunk_load(1);
+      __syncthreads();
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int o = (c + q) * LDX + jl;
-      Wn[(c + q) * LDW + jl] = wv[q] - (static_cast<float>(Xh[o]) + static_cast<float>(Xl[o]));
+    for (int ch = 0; ch < NCH; ++ch) {
+      f32x16 cx[1];
+      zero(cx[0]);
+      if (u.muon) {
+        if (ch + 1 < NCH) {
+          bf16* nb = fb(ch + 1);
+          chunk_store(nb, nb + JC * LDF, LDF);
+          if (ch + 2 < NCH) chunk_load(ch + 2);
+        }
+        bf16* cb = fb(ch);
+        // slot 1 holds Q^T: read K-major for Q's rows
+        mma_blocks<H, 1, JBC, NBF, true, false>(cx, w, S1h, S1l, LDA, cb, cb + JC * LDF, LDF, lane);
+      }
+      if (fact) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          int j, c;
+          fcoord(ch, g4, j, c);
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(W + (int64_t)j * H + c);
+          f32x4 uv;
+          if (u.muon)
+            uv = f32x4{cx[0][4 * g4], cx[0][4 * g4 + 1], cx[0][4 * g4 + 2], cx[0][4 * g4 + 3]};
+          else
+            uv = *reinterpret_cast<const f32x4*>(Ud + (int64_t)j * H + c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wn[ch][4 * g4 + i] = wv[i] - uv[i];
+        }
+      }
+      if (u.muon) __syncthreads();
     }
   }
   __syncthreads();
+  if (fact) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        int j, c;
+        fcoord(ch, g4, j, c);
+        *reinterpret_cast<f32x4*>(Wn + j * LDW + c) =
+            f32x4{wn[ch][4 * g4], wn[ch][4 * g4 + 1], wn[ch][4 * g4 + 2], wn[ch][4 * g4 + 3]};
+      }
+  }
+  __syncthreads();
+
+  // ---- 4. renorm over the input axis -----------------------------------------------------------
   if (u.weight_norm) {
-    if (mat == 1) {  // W1 [rh][h]: column c over all rh rows (both parts)
-      for (int c = w; c < H; c += NWV) {
+    if (mat == 1) {  // W1 [rh][h]: column c over all rh rows
+      constexpr int CG = 512 / H;
+      if (tid < CG * H) {
+        const int c = tid % H, grp = tid / H;
         float acc = 0.f;
-        for (int jl = lane; jl < RHG; jl += 64) acc += Wn[c * LDW + jl] * Wn[c * LDW + jl];
+        for (int j = grp; j < RH; j += CG) acc += Wn[j * LDW + c] * Wn[j * LDW + c];
+        cpart[grp * H + c] = acc;
+      }
+      __syncthreads();
+      if (tid < H) {
+        float tot = 0.f;
+        for (int g = 0; g < CG; ++g) tot += cpart[g * H + tid];
+        fac[L::NF + tid] = nu[tid] / (sqrtf(tot) + u.eps_norm);
+      }
+    } else {  // W0T / W2T: state row j over its h inputs
+      for (int j = w; j < RH; j += 8) {
+        float acc = 0.f;
+        for (int c = lane; c < H; c += 64) acc += Wn[j * LDW + c] * Wn[j * LDW + c];
         acc = wave_sum(acc);
-        if (lane == 0) cn[c] = acc;
-      }
-      if constexpr (G == 2) {
-        __syncthreads();
-        float* mine = xslot(bi & 1, part);
-        for (int c = tid; c < H; c += 512) mine[c] = cn[c];
-        xcd_barrier(cnt, G * (++bi), err);
-        const float* m0 = xslot((bi - 1) & 1, 0);
-        const float* m1 = xslot((bi - 1) & 1, 1);
-        for (int c = tid; c < H; c += 512) cn[c] = xcd_load(m0 + c) + xcd_load(m1 + c);
-      }
-      __syncthreads();
-      for (int c = tid; c < H; c += 512) cn[H + c] = nu[c] / (sqrtf(cn[c]) + u.eps_norm);
-      __syncthreads();
-      for (int e = tid; e < H * RHG; e += 512) Wn[(e / RHG) * LDW + e % RHG] *= cn[H + e / RHG];
-    } else {  // W0T / W2T: row j over its h inputs (column jl of Wn)
-      for (int jl = tid; jl < RHG; jl += 512) {
-        float acc = 0.f;
-        for (int c = 0; c < H; ++c) acc += Wn[c * LDW + jl] * Wn[c * LDW + jl];
-        const float f = nu[j0 + jl] / (sqrtf(acc) + u.eps_norm);
-        for (int c = 0; c < H; ++c) Wn[c * LDW + jl] *= f;
+        if (lane == 0) fac[L::NF + j] = nu[j] / (sqrtf(acc) + u.eps_norm);
       }
     }
     __syncthreads();
   }
-  // ---- 4. state and operand shadows -----------------------------------------------------------
+
+  // ---- 5. state and operand shadows -----------------------------------------------------------
   OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
   OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
-  for (int e = tid; e < RHG * H; e += 512) {
-    const int jl = e / H, c = e % H;
-    const float v = Wn[c * LDW + jl];
-    const int64_t idx = (int64_t)(j0 + jl) * H + c;
-    W[idx] = v;
-    dst[idx] = Mfma<OpT>::from_f32(v);
+  const float* f = fac + L::NF;
+#pragma unroll 4
+  for (int gi = 0; gi < NG; ++gi) {
+    const int e4 = tid + 512 * gi;
+    if (e4 >= NE4) continue;
+    const int e = 4 * e4, j = e / H, c = e % H;
+    f32x4 v = *reinterpret_cast<const f32x4*>(Wn + j * LDW + c);
+    if (u.weight_norm) {
+      if (mat == 1)
+        v *= *reinterpret_cast<const f32x4*>(f + c);
+      else
+        v *= f[j];
+    }
+    *reinterpret_cast<f32x4*>(W + e) = v;
+    store4(dst + e, v);
   }
-  if (mat == 1) {
-    for (int e = tid; e < RHG * H; e += 512) {
-      const int c = e / RHG, jl = e % RHG;
-      sh[3 * n + (int64_t)c * RH + j0 + jl] = Mfma<OpT>::from_f32(Wn[c * LDW + jl]);
+  if (mat == 1) {  // W1^T shadow [h][rh]: four consecutive state rows per thread
+    for (int e4 = tid; e4 < NE4; e4 += 512) {
+      const int c = (4 * e4) / RH, j = (4 * e4) % RH;
+      const float fc = u.weight_norm ? f[c] : 1.f;
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = Wn[(j + i) * LDW + c] * fc;
+      store4(sh + 3 * n + (int64_t)c * RH + j, v);
     }
   }
 }
