@@ -170,12 +170,11 @@ struct UpdLayout {
   static constexpr int LDF = H + 8;            // X^T chunk for the final product (row reads)
   static constexpr int CHG = 2 * JC * LDG * 2;
   static constexpr int CHF = 2 * JC * LDF * 2;
-  static constexpr int LDW = H + 4;            // fp32 staging of the new state [RH][LDW]
-  static constexpr int WB = RH * LDW * 4;
-  static constexpr int R = cmax(cmax(2 * SLOT, 2 * CHG), cmax(SLOT + 2 * CHF, WB));
-  static constexpr int NF = RH > H ? RH : H;
-  static constexpr int bytes = R + (2 * NF + 512 + 32) * 4;
-  static constexpr int HB = H / 32;
+  static constexpr int R = cmax(cmax(2 * SLOT, 2 * CHG), SLOT + 2 * CHF);
+  static constexpr int HB = H / 32, JBC = JC / 32;
+  static constexpr int NF = RH > H ? RH : H;              // renorm factors
+  static constexpr int NP = cmax(HB * RH, JBC * H);       // renorm partial sums
+  static constexpr int bytes = R + (NP + NF + 32) * 4;
   static constexpr int NBA = HB * HB, QA = (NBA + 7) / 8;   // h x h blocks per wave
   static constexpr int NBF = HB * (JC / 32);                // final-product blocks per chunk
   static_assert(RH % JC == 0 && H % 32 == 0 && NBF <= 8, "shape");
@@ -194,7 +193,7 @@ constexpr int update_lds_bytes() { return UpdLayout<H, RH>::bytes; }
 template <class OpT, int H, int RH>
 __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   typedef UpdLayout<H, RH> L;
-  constexpr int JC = L::JC, NCH = L::NCH, LDA = L::LDA, LDG = L::LDG, LDF = L::LDF, LDW = L::LDW;
+  constexpr int JC = L::JC, NCH = L::NCH, LDA = L::LDA, LDG = L::LDG, LDF = L::LDF;
   constexpr int HB = L::HB, NBA = L::NBA, QA = L::QA, NBF = L::NBF;
   constexpr int NE4 = RH * H / 4;              // float4 groups of the matrix
   constexpr int NG = (NE4 + 511) / 512;
@@ -206,10 +205,9 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   bf16* S1l = S1h + H * LDA;
   bf16* S2h = reinterpret_cast<bf16*>(smem + L::SLOT);       // slot 2
   bf16* S2l = S2h + H * LDA;
-  float* Wn = reinterpret_cast<float*>(smem);                // [RH][LDW] (after the products)
-  float* fac = reinterpret_cast<float*>(smem + L::R);        // [2 NF]
-  float* cpart = fac + 2 * L::NF;                            // [512]
-  float* red = cpart + 512;                                  // [32]
+  float* npart = reinterpret_cast<float*>(smem + L::R);      // [NP] renorm partial sums
+  float* fac = npart + L::NP;                                // [NF] renorm factors
+  float* red = fac + L::NF;                                  // [32]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int mi = blockIdx.x;
@@ -223,9 +221,7 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   const float* part0 = s.part + ((int64_t)pair * 3 + mat) * n;
   const float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
   const bool mom = u.momentum != 0.f;
-  // U goes to a buffer of its own that this launch has not read before: the chunk loads below
-  // must not hit lines of M or of the partials that the per-CU L1 still holds from step 1
-  float* Ud = s.U + ((int64_t)pair * 3 + mat) * n;
+  float* Ud = mom ? Mm : s.U + ((int64_t)pair * 3 + mat) * n;  // U after step 1
 
   // ---- 1. gradient from the segment partials (in segment order), momentum -------------------
   float ss = 0.f;
@@ -254,10 +250,7 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
         const int e4 = tid + 512 * (b0 + i);
         if (e4 >= NE4) continue;
         f32x4 v = -g[i];
-        if (mom) {
-          v = u.momentum * mv[i] + v;
-          *reinterpret_cast<f32x4*>(Mm + 4 * e4) = v;
-        }
+        if (mom) v = u.momentum * mv[i] + v;
         *reinterpret_cast<f32x4*>(Ud + 4 * e4) = v;
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
       }
@@ -380,8 +373,9 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   }
 
   // ---- 3. W - U per chunk, U = (Q X_0)^T with Muon: block C[c][j] = sum_m Q[c][m] X_0^T[j][m] ---
-  // wave w < NBF owns block (c-block w / (JC/32), j-block w % (JC/32)) of every chunk
-  constexpr int JBC = JC / 32;
+  // wave w < NBF owns block (c-block w / (JC/32), j-block w % (JC/32)) of every chunk and keeps
+  // the new state of those blocks in registers through the renorm and the writes
+  constexpr int JBC = L::JBC;
   const bool fact = w < NBF;
   const int fcb = (w < NBF ? w : 0) / JBC, fjb = (w < NBF ? w : 0) % JBC;
   auto fcoord = [&](int ch, int g4, int& j, int& c) {
@@ -389,6 +383,18 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
     j = ch * JC + fjb * 32 + (lane & 31);
   };
   f32x16 wn[NCH];
+  if (fact) {  // all of this wave's W entries in flight at once
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        int j, c;
+        fcoord(ch, g4, j, c);
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(W + (int64_t)j * H + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wn[ch][4 * g4 + i] = wv[i];
+      }
+  }
   {
     auto fb = [&](int i) { return reinterpret_cast<bf16*>(smem + L::SLOT + (i & 1) * L::CHF); };
     if (u.muon) {
@@ -416,88 +422,89 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
         for (int g4 = 0; g4 < 4; ++g4) {
           int j, c;
           fcoord(ch, g4, j, c);
-          const f32x4 wv = *reinterpret_cast<const f32x4*>(W + (int64_t)j * H + c);
           f32x4 uv;
           if (u.muon)
             uv = f32x4{cx[0][4 * g4], cx[0][4 * g4 + 1], cx[0][4 * g4 + 2], cx[0][4 * g4 + 3]};
           else
             uv = *reinterpret_cast<const f32x4*>(Ud + (int64_t)j * H + c);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wn[ch][4 * g4 + i] = wv[i] - uv[i];
+          for (int i = 0; i < 4; ++i) wn[ch][4 * g4 + i] -= uv[i];
         }
       }
       if (u.muon) __syncthreads();
     }
   }
-  __syncthreads();
+
+  // ---- 4. renorm over the input axis (partial sums of squares from the register blocks) --------
+  if (u.weight_norm) {
+    if (mat == 1) {  // W1 [rh][h]: column c over all rh rows; lanes of a half hold 32 rows j
+      if (fact) {
+        float cs[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float a = 0.f;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) a += wn[ch][r] * wn[ch][r];
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) a += __shfl_xor(a, off, 64);
+          cs[r] = a;
+        }
+        if ((lane & 31) == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) npart[fjb * H + fcb * 32 + acc_row(r, lane)] = cs[r];
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < H; c += 512) {
+        float tot = 0.f;
+        for (int jb = 0; jb < JBC; ++jb) tot += npart[jb * H + c];
+        fac[c] = nu[c] / (sqrtf(tot) + u.eps_norm);
+      }
+    } else {  // W0T / W2T: state row j over its h inputs; a lane holds 16 of a block's 32 columns
+      if (fact) {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+          float a = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a += wn[ch][r] * wn[ch][r];
+          a += __shfl_xor(a, 32, 64);
+          if (lane < 32) npart[fcb * RH + ch * JC + fjb * 32 + lane] = a;
+        }
+      }
+      __syncthreads();
+      for (int j = tid; j < RH; j += 512) {
+        float tot = 0.f;
+        for (int cb = 0; cb < HB; ++cb) tot += npart[cb * RH + j];
+        fac[j] = nu[j] / (sqrtf(tot) + u.eps_norm);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- 5. state and operand shadows from the register blocks ----------------------------------
   if (fact) {
+    OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
+    OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         int j, c;
         fcoord(ch, g4, j, c);
-        *reinterpret_cast<f32x4*>(Wn + j * LDW + c) =
-            f32x4{wn[ch][4 * g4], wn[ch][4 * g4 + 1], wn[ch][4 * g4 + 2], wn[ch][4 * g4 + 3]};
-      }
-  }
-  __syncthreads();
-
-  // ---- 4. renorm over the input axis -----------------------------------------------------------
-  if (u.weight_norm) {
-    if (mat == 1) {  // W1 [rh][h]: column c over all rh rows
-      constexpr int CG = 512 / H;
-      if (tid < CG * H) {
-        const int c = tid % H, grp = tid / H;
-        float acc = 0.f;
-        for (int j = grp; j < RH; j += CG) acc += Wn[j * LDW + c] * Wn[j * LDW + c];
-        cpart[grp * H + c] = acc;
-      }
-      __syncthreads();
-      if (tid < H) {
-        float tot = 0.f;
-        for (int g = 0; g < CG; ++g) tot += cpart[g * H + tid];
-        fac[L::NF + tid] = nu[tid] / (sqrtf(tot) + u.eps_norm);
-      }
-    } else {  // W0T / W2T: state row j over its h inputs
-      for (int j = w; j < RH; j += 8) {
-        float acc = 0.f;
-        for (int c = lane; c < H; c += 64) acc += Wn[j * LDW + c] * Wn[j * LDW + c];
-        acc = wave_sum(acc);
-        if (lane == 0) fac[L::NF + j] = nu[j] / (sqrtf(acc) + u.eps_norm);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- 5. state and operand shadows -----------------------------------------------------------
-  OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
-  OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
-  const float* f = fac + L::NF;
-#pragma unroll 4
-  for (int gi = 0; gi < NG; ++gi) {
-    const int e4 = tid + 512 * gi;
-    if (e4 >= NE4) continue;
-    const int e = 4 * e4, j = e / H, c = e % H;
-    f32x4 v = *reinterpret_cast<const f32x4*>(Wn + j * LDW + c);
-    if (u.weight_norm) {
-      if (mat == 1)
-        v *= *reinterpret_cast<const f32x4*>(f + c);
-      else
-        v *= f[j];
-    }
-    *reinterpret_cast<f32x4*>(W + e) = v;
-    store4(dst + e, v);
-  }
-  if (mat == 1) {  // W1^T shadow [h][rh]: four consecutive state rows per thread
-    for (int e4 = tid; e4 < NE4; e4 += 512) {
-      const int c = (4 * e4) / RH, j = (4 * e4) % RH;
-      const float fc = u.weight_norm ? f[c] : 1.f;
-      f32x4 v;
+        f32x4 v = f32x4{wn[ch][4 * g4], wn[ch][4 * g4 + 1], wn[ch][4 * g4 + 2], wn[ch][4 * g4 + 3]};
+        if (u.weight_norm) {
+          if (mat == 1)
+            v *= *reinterpret_cast<const f32x4*>(fac + c);
+          else
+            v *= fac[j];
+        }
+        *reinterpret_cast<f32x4*>(W + (int64_t)j * H + c) = v;
+        store4(dst + (int64_t)j * H + c, v);
+        if (mat == 1) {  // W1^T shadow [h][rh]: 32 lanes write 32 consecutive j of a row c
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = Wn[(j + i) * LDW + c] * fc;
-      store4(sh + 3 * n + (int64_t)c * RH + j, v);
-    }
+          for (int i = 0; i < 4; ++i) sh[3 * n + (int64_t)(c + i) * RH + j] = Mfma<OpT>::from_f32(v[i]);
+        }
+      }
   }
 }
 
