@@ -508,6 +508,9 @@ struct ApplyArgs {
   void* O;                  // [pair][Nq][H]
   int npairs;               // pairs in the launch
   int ntiles;               // query tiles per pair in the launch (chunks * tiles_per_chunk)
+  const void* W1;           // [rh][H] per pair (rows j), optionally per chunk (apply_rd_kernel)
+  int64_t w1_pair_stride;
+  int64_t w1_chunk_stride;
 };
 
 template <class OpT, int H>
@@ -621,6 +624,179 @@ __global__ void __launch_bounds__(256) apply_kernel(ApplyArgs a) {
         if (t < t_lim) Io<IoT>::store(Op + (int64_t)t * H + cb * 32 + acc_col(lane), acc[i][r]);
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Register-direct apply for h <= 128: a workgroup of 8 waves takes AT = 256 query tokens of one
+// pair, wave w the 32 tokens t0 + 32 w .. Its query rows stay in registers as MFMA B fragments
+// for the whole launch; the fast weights stream through LDS in blocks of 32 hidden units
+// (W0^T, W2^T and W1 rows, double-buffered, shared by the 8 waves). Per block the wave forms
+// C0[j][t] = W0^T Q^T and C2[j][t] = W2^T Q^T (hidden rows as the A operand), the SwiGLU values
+// h = silu(C0) * C2 become the A fragments of O[t][c] += sum_j h[t][j] W1[j][c] directly
+// (acc_to_afrag), and W1's rows are read K-major through the permuted transpose read
+// (acc_kfrag_tr). No activation tile goes through LDS.
+// grid: x = 8 * ceil(npairs / 8) * ntiles (all tiles of a pair on one XCD); block 512.
+constexpr int AT = 256;
+
+template <class OpT>
+constexpr int tr_ld(int cols) {  // row stride for transpose reads of 16-bit rows without bank conflicts
+  if (sizeof(OpT) != 2) return cols + 4;
+  int l = cols + 4;
+  while ((l / 2) % 32 != 16) l += 4;
+  return l;
+}
+
+template <class OpT, int H>
+struct ApplyRdLayout {
+  static constexpr int LDW = H + Pad<OpT>::v;       // W0^T / W2^T block rows
+  static constexpr int LD1 = tr_ld<OpT>(H);        // W1 block rows (transpose reads)
+  static constexpr int BUF = (2 * 32 * LDW + 32 * LD1) * (int)sizeof(OpT);
+  static constexpr int bytes = 2 * BUF;
+};
+
+template <class OpT, int H>
+constexpr int apply_rd_lds_bytes() { return ApplyRdLayout<OpT, H>::bytes; }
+
+template <class IoT, class OpT, int H>
+__global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
+  static_assert(H <= 128, "register budget");
+  typedef Mfma<OpT> M;
+  typedef typename M::frag frag;
+  typedef ApplyRdLayout<OpT, H> L;
+  constexpr int LDW = L::LDW, LD1 = L::LD1;
+  constexpr int KS = H / M::KSTEP;          // K steps over h
+  constexpr int QS = 32 / M::KSTEP;         // K steps over a 32-unit hidden block
+  constexpr int CB = H / 32;
+  constexpr int VW = 16 / (int)sizeof(OpT); // elements per 16-byte chunk
+  constexpr int NCHK = 3 * 32 * H / VW;     // 16-byte chunks of one staged block
+  constexpr int CPT = (NCHK + 511) / 512;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bid = blockIdx.x, slot = bid >> 3;
+  const int pair = (bid & 7) + 8 * (slot / a.ntiles);
+  const int tile = slot % a.ntiles;
+  if (pair >= a.npairs) return;
+  const int chunk_idx = tile / a.tiles_per_chunk;
+  const int t0 = a.t_base + chunk_idx * a.chunk + (tile % a.tiles_per_chunk) * AT;
+  const int t_lim = min(a.t_base + (chunk_idx + 1) * a.chunk, a.t_limit);
+  if (t0 >= t_lim) return;
+  const int tw = t0 + 32 * w;               // this wave's first token
+
+  const IoT* Qp = reinterpret_cast<const IoT*>(a.Q) + pair * a.tok_pair_stride;
+  const OpT* w0g = reinterpret_cast<const OpT*>(a.W0T) + pair * a.w_pair_stride;
+  const OpT* w2g = reinterpret_cast<const OpT*>(a.W2T) + pair * a.w_pair_stride;
+  const OpT* w1g = reinterpret_cast<const OpT*>(a.W1) + pair * a.w1_pair_stride +
+                   (int64_t)chunk_idx * a.w1_chunk_stride;
+
+  // staged block jb: rows jb*32 .. of W0^T, W2^T, W1 (16-byte chunks, plain copies)
+  u32x4 sv[CPT];
+  auto bufp = [&](int i) { return reinterpret_cast<OpT*>(smem + (i & 1) * L::BUF); };
+  auto load_blk = [&](int jb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + 512 * i;
+      if (NCHK % 512 == 0 || ch < NCHK) {
+        const int m = ch / (32 * H / VW), r = (ch / (H / VW)) % 32, c = (ch % (H / VW)) * VW;
+        const OpT* src = (m == 0 ? w0g : m == 1 ? w2g : w1g) + (int64_t)(jb * 32 + r) * H + c;
+        sv[i] = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+  };
+  auto store_blk = [&](OpT* b) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + 512 * i;
+      if (NCHK % 512 == 0 || ch < NCHK) {
+        const int m = ch / (32 * H / VW), r = (ch / (H / VW)) % 32, c = (ch % (H / VW)) * VW;
+        OpT* dst = m < 2 ? b + m * 32 * LDW + r * LDW + c : b + 2 * 32 * LDW + r * LD1 + c;
+        *reinterpret_cast<u32x4*>(dst) = sv[i];
+      }
+    }
+  };
+
+  const int njb = a.rh / 32;
+  load_blk(0);
+
+  // query rows as B fragments: lane (n = token lane & 31, k = c); rows past the limit are zero
+  frag qf[KS];
+  {
+    const int t = tw + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      OpT tmp[M::KSUB];
+      const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
+      if (t < t_lim) {
+        if constexpr (M::KSUB == 8) {
+          Io<IoT>::template load_cvt<OpT>(Qp + (int64_t)t * H + c, tmp);
+        } else {
+          static_assert(std::is_same<IoT, float>::value, "fp32 operands come with fp32 I/O");
+          tmp[0] = Qp[(int64_t)t * H + c];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < M::KSUB; ++e) tmp[e] = M::from_f32(0.f);
+      }
+      if constexpr (M::KSUB == 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[s][e] = tmp[e];
+      } else {
+        qf[s] = tmp[0];
+      }
+    }
+  }
+
+  store_blk(bufp(0));
+  if (njb > 1) load_blk(1);
+  __syncthreads();
+
+  f32x16 o[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) zero(o[cb]);
+
+  for (int jb = 0; jb < njb; ++jb) {
+    if (jb + 1 < njb) {
+      store_blk(bufp(jb + 1));
+      if (jb + 2 < njb) load_blk(jb + 2);
+    }
+    const OpT* b = bufp(jb);
+    if (tw < t_lim) {
+      f32x16 c0, c2;
+      zero(c0);
+      zero(c2);
+      const OpT* r0 = b + (lane & 31) * LDW + (lane >> 5) * M::KSUB;
+      const OpT* r2 = r0 + 32 * LDW;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        c0 = M::mma(M::load(r0 + s * M::KSTEP), qf[s], c0);
+        c2 = M::mma(M::load(r2 + s * M::KSTEP), qf[s], c2);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float A = c0[r];
+        c0[r] = A * sigmoid_fast(A) * c2[r];
+      }
+      const OpT* w1s = b + 2 * 32 * LDW;
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        const frag hf = acc_to_afrag<OpT>(c0, q);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb] = M::mma(hf, acc_kfrag_tr<OpT>(w1s + cb * 32, LD1, q, lane), o[cb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (tw < t_lim) {
+    IoT* Op = reinterpret_cast<IoT*>(a.O) + pair * a.tok_pair_stride;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = tw + acc_row(r, lane);
+        if (t < t_lim) Io<IoT>::store(Op + (int64_t)t * H + cb * 32 + acc_col(lane), o[cb][r]);
+      }
   }
 }
 

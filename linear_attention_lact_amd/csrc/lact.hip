@@ -222,12 +222,13 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   auto gk = grad_kernel<IoT, OpT, H, false, SCALE>;
   auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE>;
   auto ak = apply_kernel<IoT, OpT, H>;
+  auto akr = apply_rd_kernel<IoT, OpT, (RD ? H : 128)>;
   constexpr int glds = RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false>() : grad_lds_bytes<OpT, H, false>();
-  constexpr int alds = apply_lds_bytes<OpT, H>();
+  constexpr int alds = RD ? apply_rd_lds_bytes<OpT, (RD ? H : 128)>() : apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
     hipError_t e = RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
-    return e != hipSuccess ? e : allow_lds(ak, alds);
+    return e != hipSuccess ? e : (RD ? allow_lds(akr, alds) : allow_lds(ak, alds));
   }();
   TTT_HIP(lds_ok);
 
@@ -254,7 +255,10 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   aa.w1t_pair_stride = 4 * n;
   aa.w1t_chunk_stride = 0;
   aa.chunk = p.chunk_q;
-  aa.tiles_per_chunk = (p.chunk_q + TT - 1) / TT;
+  aa.tiles_per_chunk = RD ? (p.chunk_q + AT - 1) / AT : (p.chunk_q + TT - 1) / TT;
+  aa.W1 = sh + 2 * n;
+  aa.w1_pair_stride = 4 * n;
+  aa.w1_chunk_stride = 0;
   aa.rh = rh;
   aa.O = O;
   aa.npairs = P;
@@ -315,13 +319,21 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const unsigned ugrid = (unsigned)(3 * P);
 
   const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
+  auto apply = [&]() -> ttt_status {
+    LaunchTimer lt(K_LACT_APPLY, st);
+    if constexpr (RD)
+      hipLaunchKernelGGL(akr, agrid, dim3(512), alds, st, aa);
+    else
+      hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
+    TTT_HIP(hipGetLastError());
+    return TTT_OK;
+  };
   for (int c = 0; c < nch; ++c) {
     aa.t_base = c * p.chunk_q;
     aa.t_limit = (c + 1) * p.chunk_q;
     if (p.order == TTT_APPLY_THEN_UPDATE) {
-      LaunchTimer lt(K_LACT_APPLY, st);
-      hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
-      TTT_HIP(hipGetLastError());
+      const ttt_status e = apply();
+      if (e != TTT_OK) return e;
     }
     ga.t_base = c * p.chunk_kv;
     ga.t_limit = (c + 1) * p.chunk_kv;
@@ -346,9 +358,8 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
       }
     }
     if (p.order == TTT_UPDATE_THEN_APPLY) {
-      LaunchTimer lt(K_LACT_APPLY, st);
-      hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
-      TTT_HIP(hipGetLastError());
+      const ttt_status e = apply();
+      if (e != TTT_OK) return e;
     }
   }
   LaunchTimer lt_fin(K_LACT_FINAL, st);

@@ -29,9 +29,10 @@ __global__ void __launch_bounds__(256) linattn_prep_kernel(const float* W0, cons
   }
 }
 
-// Chunk prefix scan, one thread per state element [j][c]: writes S_c^T [h][rh] per chunk as
-// an operand shadow and optionally the final state. grid (ceil(rh*h/256), P), block 256.
-template <class OpT>
+// Chunk prefix scan, one thread per state element [j][c]: writes S_c per chunk as an operand
+// shadow, [rh][h] (ROWS) or transposed [h][rh], and optionally the final state.
+// grid (ceil(rh*h/256), P), block 256.
+template <class OpT, bool ROWS>
 __global__ void __launch_bounds__(256) linattn_scan_kernel(const float* W1, const float* dS, OpT* St, float* S_out,
                                                           int H, int h, int rh, int nch, int inclusive,
                                                           int64_t w_batch_stride) {
@@ -43,7 +44,7 @@ __global__ void __launch_bounds__(256) linattn_scan_kernel(const float* W1, cons
   const int j = (int)(e / h), c = (int)(e % h);
   float s = W1[(int64_t)b * w_batch_stride + (int64_t)head * n + e];
   const float* d = dS + (int64_t)pair * nch * n + e;
-  OpT* o = St + (int64_t)pair * nch * n + (int64_t)c * rh + j;
+  OpT* o = St + (int64_t)pair * nch * n + (ROWS ? e : (int64_t)c * rh + j);
   for (int k = 0; k < nch; ++k) {
     if (inclusive) s += d[k * n];
     o[k * n] = Mfma<OpT>::from_f32(s);
@@ -61,12 +62,13 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   auto gk = grad_kernel<IoT, OpT, H, true, false>;
   auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), true, false>;
   auto ak = apply_kernel<IoT, OpT, H>;
+  auto akr = apply_rd_kernel<IoT, OpT, (RD ? H : 128)>;
   constexpr int glds = RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), true>() : grad_lds_bytes<OpT, H, true>();
-  constexpr int alds = apply_lds_bytes<OpT, H>();
+  constexpr int alds = RD ? apply_rd_lds_bytes<OpT, (RD ? H : 128)>() : apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
     hipError_t e = RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
-    return e != hipSuccess ? e : allow_lds(ak, alds);
+    return e != hipSuccess ? e : (RD ? allow_lds(akr, alds) : allow_lds(ak, alds));
   }();
   TTT_HIP(lds_ok);
   const int P = p.B * p.H, rh = p.r * H, nch = p.N / p.chunk;
@@ -111,7 +113,8 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   }
   {
     LaunchTimer lt(K_LIN_SCAN, st);
-    hipLaunchKernelGGL(linattn_scan_kernel<OpT>, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
+    auto sk = linattn_scan_kernel<OpT, RD>;
+    hipLaunchKernelGGL(sk, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
                        St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.w_batch_stride);
     TTT_HIP(hipGetLastError());
   }
@@ -120,13 +123,16 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   aa.tok_pair_stride = (int64_t)p.N * H;
   aa.t_base = 0;
   aa.t_limit = p.N;
-  aa.tiles_per_chunk = (p.chunk + TT - 1) / TT;
+  aa.tiles_per_chunk = RD ? (p.chunk + AT - 1) / AT : (p.chunk + TT - 1) / TT;
   aa.W0T = sh;
   aa.W2T = sh + n;
   aa.w_pair_stride = 2 * n;
   aa.W1T = St;
   aa.w1t_pair_stride = (int64_t)nch * n;
   aa.w1t_chunk_stride = n;
+  aa.W1 = St;
+  aa.w1_pair_stride = (int64_t)nch * n;
+  aa.w1_chunk_stride = n;
   aa.chunk = p.chunk;
   aa.rh = rh;
   aa.O = O;
@@ -134,7 +140,11 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   aa.ntiles = nch * aa.tiles_per_chunk;
   {
     LaunchTimer lt(K_LIN_APPLY, st);
-    hipLaunchKernelGGL(ak, dim3(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles), dim3(256), alds, st, aa);
+    const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
+    if constexpr (RD)
+      hipLaunchKernelGGL(akr, agrid, dim3(512), alds, st, aa);
+    else
+      hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
     TTT_HIP(hipGetLastError());
   }
   return TTT_OK;

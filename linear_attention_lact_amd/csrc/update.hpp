@@ -95,7 +95,7 @@ __device__ __forceinline__ void mma_split(f32x16 (&c)[Q], const bf16* Ah, const 
   f32x16 d[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) zero(d[q]);
-#pragma unroll 1
+#pragma unroll 8
   for (int k = 0; k < K; k += 16) {
     bf16x8 ah, al;
     if constexpr (TA) {
