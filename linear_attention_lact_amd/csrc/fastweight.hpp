@@ -630,14 +630,16 @@ __global__ void __launch_bounds__(256) apply_kernel(ApplyArgs a) {
 // ------------------------------------------------------------------------------------------
 // Register-direct apply for h <= 128: a workgroup of 8 waves takes AT = 256 query tokens of one
 // pair, wave w the 32 tokens t0 + 32 w .. Its query rows stay in registers as MFMA B fragments
-// for the whole launch; the fast weights stream through LDS in blocks of 32 hidden units
-// (W0^T, W2^T and W1 rows, double-buffered, shared by the 8 waves). Per block the wave forms
-// C0[j][t] = W0^T Q^T and C2[j][t] = W2^T Q^T (hidden rows as the A operand), the SwiGLU values
-// h = silu(C0) * C2 become the A fragments of O[t][c] += sum_j h[t][j] W1[j][c] directly
-// (acc_to_afrag), and W1's rows are read K-major through the permuted transpose read
+// for the whole launch; the fast weights stream through LDS in blocks of AJ = 64 hidden units
+// (W0^T, W2^T and W1 rows, double-buffered in LDS, each block requested two blocks ahead
+// through two alternating register sets, shared by the 8 waves). Per 32-unit half of a block
+// the wave forms C0[j][t] = W0^T Q^T and C2[j][t] = W2^T Q^T (hidden rows as the A operand);
+// the SwiGLU values h = silu(C0) * C2 become the A fragments of O[t][c] += sum_j h[t][j] W1[j][c]
+// directly (acc_to_afrag), and W1's rows are read K-major through the permuted transpose read
 // (acc_kfrag_tr). No activation tile goes through LDS.
 // grid: x = 8 * ceil(npairs / 8) * ntiles (all tiles of a pair on one XCD); block 512.
 constexpr int AT = 256;
+constexpr int AJ = 64;
 
 template <class OpT>
 constexpr int tr_ld(int cols) {  // row stride for transpose reads of 16-bit rows without bank conflicts
@@ -651,7 +653,7 @@ template <class OpT, int H>
 struct ApplyRdLayout {
   static constexpr int LDW = H + Pad<OpT>::v;       // W0^T / W2^T block rows
   static constexpr int LD1 = tr_ld<OpT>(H);        // W1 block rows (transpose reads)
-  static constexpr int BUF = (2 * 32 * LDW + 32 * LD1) * (int)sizeof(OpT);
+  static constexpr int BUF = (2 * AJ * LDW + AJ * LD1) * (int)sizeof(OpT);
   static constexpr int bytes = 2 * BUF;
 };
 
@@ -666,10 +668,10 @@ __global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
   typedef ApplyRdLayout<OpT, H> L;
   constexpr int LDW = L::LDW, LD1 = L::LD1;
   constexpr int KS = H / M::KSTEP;          // K steps over h
-  constexpr int QS = 32 / M::KSTEP;         // K steps over a 32-unit hidden block
+  constexpr int QS = 32 / M::KSTEP;         // K steps over a 32-unit hidden half block
   constexpr int CB = H / 32;
   constexpr int VW = 16 / (int)sizeof(OpT); // elements per 16-byte chunk
-  constexpr int NCHK = 3 * 32 * H / VW;     // 16-byte chunks of one staged block
+  constexpr int NCHK = 3 * AJ * H / VW;     // 16-byte chunks of one staged block
   constexpr int CPT = (NCHK + 511) / 512;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -689,35 +691,37 @@ __global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
   const OpT* w2g = reinterpret_cast<const OpT*>(a.W2T) + pair * a.w_pair_stride;
   const OpT* w1g = reinterpret_cast<const OpT*>(a.W1) + pair * a.w1_pair_stride +
                    (int64_t)chunk_idx * a.w1_chunk_stride;
+  const int njb = a.rh / AJ;
 
-  // staged block jb: rows jb*32 .. of W0^T, W2^T, W1 (16-byte chunks, plain copies)
-  u32x4 sv[CPT];
+  // staged block jb: rows jb*AJ .. of W0^T, W2^T, W1 (16-byte chunks, plain copies)
+  u32x4 sva[CPT], svb[CPT];
   auto bufp = [&](int i) { return reinterpret_cast<OpT*>(smem + (i & 1) * L::BUF); };
-  auto load_blk = [&](int jb) {
+  auto load_blk = [&](int jb, u32x4 (&sv)[CPT]) {
+    if (jb >= njb) return;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + 512 * i;
       if (NCHK % 512 == 0 || ch < NCHK) {
-        const int m = ch / (32 * H / VW), r = (ch / (H / VW)) % 32, c = (ch % (H / VW)) * VW;
-        const OpT* src = (m == 0 ? w0g : m == 1 ? w2g : w1g) + (int64_t)(jb * 32 + r) * H + c;
+        const int m = ch / (AJ * H / VW), r = (ch / (H / VW)) % AJ, c = (ch % (H / VW)) * VW;
+        const OpT* src = (m == 0 ? w0g : m == 1 ? w2g : w1g) + (int64_t)(jb * AJ + r) * H + c;
         sv[i] = *reinterpret_cast<const u32x4*>(src);
       }
     }
   };
-  auto store_blk = [&](OpT* b) {
+  auto store_blk = [&](OpT* b, const u32x4 (&sv)[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + 512 * i;
       if (NCHK % 512 == 0 || ch < NCHK) {
-        const int m = ch / (32 * H / VW), r = (ch / (H / VW)) % 32, c = (ch % (H / VW)) * VW;
-        OpT* dst = m < 2 ? b + m * 32 * LDW + r * LDW + c : b + 2 * 32 * LDW + r * LD1 + c;
+        const int m = ch / (AJ * H / VW), r = (ch / (H / VW)) % AJ, c = (ch % (H / VW)) * VW;
+        OpT* dst = m < 2 ? b + m * AJ * LDW + r * LDW + c : b + 2 * AJ * LDW + r * LD1 + c;
         *reinterpret_cast<u32x4*>(dst) = sv[i];
       }
     }
   };
 
-  const int njb = a.rh / 32;
-  load_blk(0);
+  load_blk(0, sva);
+  load_blk(1, svb);
 
   // query rows as B fragments: lane (n = token lane & 31, k = c); rows past the limit are zero
   frag qf[KS];
@@ -747,45 +751,52 @@ __global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
     }
   }
 
-  store_blk(bufp(0));
-  if (njb > 1) load_blk(1);
+  store_blk(bufp(0), sva);
+  load_blk(2, sva);
   __syncthreads();
 
   f32x16 o[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) zero(o[cb]);
 
-  for (int jb = 0; jb < njb; ++jb) {
-    if (jb + 1 < njb) {
-      store_blk(bufp(jb + 1));
-      if (jb + 2 < njb) load_blk(jb + 2);
-    }
+  // block jb: publish block jb+1 (requested two blocks ago), request block jb+3, compute jb
+  auto step = [&](int jb, u32x4 (&nxt)[CPT]) {
+    if (jb + 1 < njb) store_blk(bufp(jb + 1), nxt);
+    load_blk(jb + 3, nxt);
     const OpT* b = bufp(jb);
     if (tw < t_lim) {
-      f32x16 c0, c2;
-      zero(c0);
-      zero(c2);
-      const OpT* r0 = b + (lane & 31) * LDW + (lane >> 5) * M::KSUB;
-      const OpT* r2 = r0 + 32 * LDW;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        c0 = M::mma(M::load(r0 + s * M::KSTEP), qf[s], c0);
-        c2 = M::mma(M::load(r2 + s * M::KSTEP), qf[s], c2);
-      }
+      for (int hb = 0; hb < AJ / 32; ++hb) {
+        f32x16 c0, c2;
+        zero(c0);
+        zero(c2);
+        const OpT* r0 = b + (hb * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
+        const OpT* r2 = r0 + AJ * LDW;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float A = c0[r];
-        c0[r] = A * sigmoid_fast(A) * c2[r];
-      }
-      const OpT* w1s = b + 2 * 32 * LDW;
+        for (int s = 0; s < KS; ++s) {
+          c0 = M::mma(M::load(r0 + s * M::KSTEP), qf[s], c0);
+          c2 = M::mma(M::load(r2 + s * M::KSTEP), qf[s], c2);
+        }
 #pragma unroll
-      for (int q = 0; q < QS; ++q) {
-        const frag hf = acc_to_afrag<OpT>(c0, q);
+        for (int r = 0; r < 16; ++r) {
+          const float A = c0[r];
+          c0[r] = A * sigmoid_fast(A) * c2[r];
+        }
+        const OpT* w1s = b + 2 * AJ * LDW + hb * 32 * LD1;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) o[cb] = M::mma(hf, acc_kfrag_tr<OpT>(w1s + cb * 32, LD1, q, lane), o[cb]);
+        for (int q = 0; q < QS; ++q) {
+          const frag hf = acc_to_afrag<OpT>(c0, q);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            o[cb] = M::mma(hf, acc_kfrag_tr<OpT>(w1s + cb * 32, LD1, q, lane), o[cb]);
+        }
       }
     }
     __syncthreads();
+  };
+  for (int jb = 0; jb < njb; jb += 2) {
+    step(jb, svb);
+    if (jb + 1 < njb) step(jb + 1, sva);
   }
 
   if (tw < t_lim) {

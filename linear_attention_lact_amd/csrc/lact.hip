@@ -222,13 +222,15 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   auto gk = grad_kernel<IoT, OpT, H, false, SCALE>;
   auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE>;
   auto ak = apply_kernel<IoT, OpT, H>;
-  auto akr = apply_rd_kernel<IoT, OpT, (RD ? H : 128)>;
+  // register-direct apply where its double-buffered weight blocks fit in LDS
+  constexpr bool ARD = H <= 128 && apply_rd_lds_bytes<OpT, (H <= 128 ? H : 128)>() <= 160 * 1024;
+  auto akr = apply_rd_kernel<IoT, OpT, (ARD ? H : 64)>;
   constexpr int glds = RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false>() : grad_lds_bytes<OpT, H, false>();
-  constexpr int alds = RD ? apply_rd_lds_bytes<OpT, (RD ? H : 128)>() : apply_lds_bytes<OpT, H>();
+  constexpr int alds = ARD ? apply_rd_lds_bytes<OpT, (ARD ? H : 64)>() : apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
     hipError_t e = RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
-    return e != hipSuccess ? e : (RD ? allow_lds(akr, alds) : allow_lds(ak, alds));
+    return e != hipSuccess ? e : (ARD ? allow_lds(akr, alds) : allow_lds(ak, alds));
   }();
   TTT_HIP(lds_ok);
 
@@ -255,7 +257,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   aa.w1t_pair_stride = 4 * n;
   aa.w1t_chunk_stride = 0;
   aa.chunk = p.chunk_q;
-  aa.tiles_per_chunk = RD ? (p.chunk_q + AT - 1) / AT : (p.chunk_q + TT - 1) / TT;
+  aa.tiles_per_chunk = ARD ? (p.chunk_q + AT - 1) / AT : (p.chunk_q + TT - 1) / TT;
   aa.W1 = sh + 2 * n;
   aa.w1_pair_stride = 4 * n;
   aa.w1_chunk_stride = 0;
@@ -321,7 +323,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
   auto apply = [&]() -> ttt_status {
     LaunchTimer lt(K_LACT_APPLY, st);
-    if constexpr (RD)
+    if constexpr (ARD)
       hipLaunchKernelGGL(akr, agrid, dim3(512), alds, st, aa);
     else
       hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);

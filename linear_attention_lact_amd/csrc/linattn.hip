@@ -62,13 +62,15 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   auto gk = grad_kernel<IoT, OpT, H, true, false>;
   auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), true, false>;
   auto ak = apply_kernel<IoT, OpT, H>;
-  auto akr = apply_rd_kernel<IoT, OpT, (RD ? H : 128)>;
+  // register-direct apply where its double-buffered weight blocks fit in LDS
+  constexpr bool ARD = H <= 128 && apply_rd_lds_bytes<OpT, (H <= 128 ? H : 128)>() <= 160 * 1024;
+  auto akr = apply_rd_kernel<IoT, OpT, (ARD ? H : 64)>;
   constexpr int glds = RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), true>() : grad_lds_bytes<OpT, H, true>();
-  constexpr int alds = RD ? apply_rd_lds_bytes<OpT, (RD ? H : 128)>() : apply_lds_bytes<OpT, H>();
+  constexpr int alds = ARD ? apply_rd_lds_bytes<OpT, (ARD ? H : 64)>() : apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
     hipError_t e = RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
-    return e != hipSuccess ? e : (RD ? allow_lds(akr, alds) : allow_lds(ak, alds));
+    return e != hipSuccess ? e : (ARD ? allow_lds(akr, alds) : allow_lds(ak, alds));
   }();
   TTT_HIP(lds_ok);
   const int P = p.B * p.H, rh = p.r * H, nch = p.N / p.chunk;
@@ -113,7 +115,7 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   }
   {
     LaunchTimer lt(K_LIN_SCAN, st);
-    auto sk = linattn_scan_kernel<OpT, RD>;
+    auto sk = linattn_scan_kernel<OpT, ARD>;
     hipLaunchKernelGGL(sk, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
                        St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.w_batch_stride);
     TTT_HIP(hipGetLastError());
@@ -123,7 +125,7 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   aa.tok_pair_stride = (int64_t)p.N * H;
   aa.t_base = 0;
   aa.t_limit = p.N;
-  aa.tiles_per_chunk = RD ? (p.chunk + AT - 1) / AT : (p.chunk + TT - 1) / TT;
+  aa.tiles_per_chunk = ARD ? (p.chunk + AT - 1) / AT : (p.chunk + TT - 1) / TT;
   aa.W0T = sh;
   aa.W2T = sh + n;
   aa.w_pair_stride = 2 * n;
@@ -141,7 +143,7 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   {
     LaunchTimer lt(K_LIN_APPLY, st);
     const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
-    if constexpr (RD)
+    if constexpr (ARD)
       hipLaunchKernelGGL(akr, agrid, dim3(512), alds, st, aa);
     else
       hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
