@@ -138,6 +138,11 @@ def kernel_breakdown(ttt, step, steps):
             for k, (n, ms) in rec.items()}
 
 
+# profiles/<stem>_*.txt: the committed rocprofv3 summaries of each workload
+PROFILE_STEMS = {1: "linattn_scan_b4h8_h64_seq8192_chunk512", 2: "lact_lm_layer_b4h8_h128_seq32768_chunk2048",
+                 3: "lact_nvs_b1h4_h192_ctx196608_q4096", 4: "inplace_down_d4096_dh14336_seq32768_chunk1024"}
+
+
 def roofline(kern, work, bound, peak, unit):
     """Roofline of the class with the largest total time: work[class] = algorithmic FLOPs (or
     bytes) per launch."""
@@ -239,7 +244,7 @@ def main():
     ms = time_steps(step, args.steps, args.warmup, stream)
     kern = kernel_breakdown(ttt, step, args.steps)
     roof = roofline(kern, work, bound, peak, unit)
-    roof["traffic"] = acc.profiled_traffic(ROOT, roof["kernel"])
+    roof["traffic"] = acc.profiled_traffic(ROOT, roof["kernel"], PROFILE_STEMS[k])
     out = {
         "metric": metric,
         "value": round(tokens / (ms * 1e-3), 1),

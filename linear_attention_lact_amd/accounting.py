@@ -88,17 +88,20 @@ def kernel_source_hash(root: str) -> str:
     return h.hexdigest()
 
 
-def profiled_traffic(root: str, kernel_class: str):
-    """HBM bytes per launch (read + write) of a kernel class from the committed counter profile,
-    or None when there is none for this class or the kernel sources changed since it was taken."""
+def profiled_traffic(root: str, kernel_class: str, stem: str):
+    """HBM bytes per launch (read + write) of a kernel class from the committed counter profile
+    profiles/<stem>_hbm_counters.txt, or None when there is none for this class or the kernel
+    sources changed since it was taken."""
     import glob
     import os
-    symbol = {"lact_update": "lact_update_kernel", "lact_grad": "grad_kernel", "lact_apply": "apply_kernel"}
+    symbol = {"lact_update": "lact_update_kernel", "lact_grad": "grad_rd_kernel", "lact_apply": "apply_rd_kernel",
+              "linattn_delta": "grad_rd_kernel", "linattn_apply": "apply_rd_kernel",
+              "linattn_scan": "linattn_scan_kernel"}
     sym = symbol.get(kernel_class)
     if sym is None:
         return None
     cur = kernel_source_hash(root)
-    for path in glob.glob(os.path.join(root, "profiles", "*_hbm_counters.txt")):
+    for path in glob.glob(os.path.join(root, "profiles", stem + "_hbm_counters.txt")):
         lines = open(path).read().splitlines()
         tag = [l for l in lines if l.startswith("# kernel sources sha1:")]
         if not tag or tag[0].split(":", 1)[1].strip() != cur:

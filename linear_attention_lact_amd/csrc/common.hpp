@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ttt {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -206,13 +208,34 @@ __device__ __forceinline__ void zero(f32x16& a) {
 // ------------------------------------------------------------------------------------------
 template <class IoT> struct Io;
 
+// 8 bf16 (one 16-byte chunk) to 8 fp16: each 32-bit word holds two bf16, which become fp32 by
+// placing them in the high half; v_cvt_pkrtz then packs the pair. Every bf16 value inside the
+// fp16 range has at most 8 significant bits, so the round-toward-zero pack is exact there.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(u32x4 raw) {
+  typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, raw[i] << 16);
+    const float hi = __builtin_bit_cast(float, raw[i] & 0xffff0000u);
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return __builtin_bit_cast(f16x8, o);
+}
+
 template <> struct Io<bf16_t> {
   static constexpr int VEC = 8;  // elements per 16-byte load
   template <class T>
   __device__ __forceinline__ static void load_cvt(const bf16_t* p, T* out) {
-    u16x8 v = *reinterpret_cast<const u16x8*>(p);
+    if constexpr (std::is_same<T, _Float16>::value) {
+      const f16x8 h = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(p));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = Mfma<T>::from_f32(bf16_to_f32(v[e]));
+      for (int e = 0; e < 8; ++e) out[e] = h[e];
+    } else {
+      u16x8 v = *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = Mfma<T>::from_f32(bf16_to_f32(v[e]));
+    }
   }
   __device__ __forceinline__ static void store(bf16_t* p, float x) { p->bits = f32_to_bf16(x); }
 };

@@ -88,7 +88,9 @@ struct TileStage {
     }
   }
   __device__ __forceinline__ static void put(const u32x4& raw, OpT* dst) {
-    if constexpr (sizeof(IoT) == 2) {  // 8 bf16 -> 8 operand elements (16 bytes for fp16)
+    if constexpr (sizeof(IoT) == 2 && std::is_same<OpT, _Float16>::value) {  // 8 bf16 -> 8 fp16
+      *reinterpret_cast<f16x8*>(dst) = bf16x8_to_f16x8(raw);
+    } else if constexpr (sizeof(IoT) == 2) {
       const u16x8 b = __builtin_bit_cast(u16x8, raw);
       typename Mfma<OpT>::frag f;
 #pragma unroll
