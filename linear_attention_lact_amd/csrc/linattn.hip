@@ -9,6 +9,7 @@
 //   O_c  = phi(Q_c) S_c                                   (apply_kernel with per-chunk S_c)
 // The chunk prefix is an exclusive (or inclusive) scan over the chunks of each pair.
 #include "fastweight.hpp"
+#include "linattn_fused.hpp"
 #include "host.hpp"
 #include "timing.hpp"
 
@@ -152,6 +153,48 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
   return TTT_OK;
 }
 
+// Single-pass path (linattn_fused.hpp) for rh <= 128.
+template <class IoT, class OpT, int H, int RH>
+static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_t oAgg, size_t oIncl, size_t oFl,
+                                    size_t oTk, const void* Q, const void* K, const void* V, const float* eta,
+                                    const float* W0, const float* W2, const float* W1, void* O, float* S_out,
+                                    hipStream_t st) {
+  auto fk = linattn_fused_kernel<IoT, OpT, H, RH>;
+  constexpr int lds = linattn_fused_lds_bytes<OpT, H, RH>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t lds_ok = allow_lds(fk, lds);
+  TTT_HIP(lds_ok);
+  const int P = p.B * p.H, nch = p.N / p.chunk;
+  FusedArgs fa{};
+  fa.Q = Q;
+  fa.K = K;
+  fa.V = V;
+  fa.eta = eta;
+  fa.W0 = W0;
+  fa.W2 = W2;
+  fa.W1 = W1;
+  fa.O = O;
+  fa.S_out = S_out;
+  fa.agg = reinterpret_cast<float*>(ws + oAgg);
+  fa.incl = reinterpret_cast<float*>(ws + oIncl);
+  fa.flags = reinterpret_cast<unsigned*>(ws + oFl);
+  fa.tickets = reinterpret_cast<unsigned*>(ws + oTk);
+  fa.P = P;
+  fa.heads = p.H;
+  fa.N = p.N;
+  fa.chunk = p.chunk;
+  fa.nch = nch;
+  fa.inclusive = p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0;
+  fa.w_batch_stride = p.w_batch_stride;
+  LaunchTimer lt(K_LIN_FUSED, st);
+  hipLaunchKernelGGL(linattn_fused_reset, dim3(1), dim3(256), 0, st, fa.tickets, fa.flags, P * nch);
+  TTT_HIP(hipGetLastError());
+  const unsigned grid = 8u * (unsigned)((P + 7) / 8) * (unsigned)nch;
+  hipLaunchKernelGGL(fk, dim3(grid), dim3(FusedLayout<OpT, H, RH>::NT), lds, st, fa);
+  TTT_HIP(hipGetLastError());
+  return TTT_OK;
+}
+
 }  // namespace ttt
 
 using namespace ttt;
@@ -177,10 +220,21 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   if (P > 0 && nch > 0 && (!Q || !K || !V || !eta || !O)) return TTT_ERR_ARG;
   const int64_t n = rh64 * q.h;
   const size_t opsz = bf16 ? 2 : 4;
+  // single pass for bf16 I/O and (h, rh) in {(32, 64), (32, 128), (64, 128)}
+  const bool fused = bf16 && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
+                     (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31;  // buffer offsets are 32-bit
   WorkspacePlan plan;
-  const size_t oSh = plan.add((size_t)P * 2 * n * opsz);
-  const size_t odS = plan.add((size_t)P * nch * n * 4);
-  const size_t oSt = plan.add((size_t)P * nch * n * opsz);
+  size_t oSh = 0, odS = 0, oSt = 0, oAgg = 0, oIncl = 0, oFl = 0, oTk = 0;
+  if (fused) {
+    oAgg = plan.add((size_t)P * nch * n * 4);
+    oIncl = plan.add((size_t)P * nch * n * 4);
+    oFl = plan.add((size_t)P * nch * 4);
+    oTk = plan.add(16 * 4);
+  } else {
+    oSh = plan.add((size_t)P * 2 * n * opsz);
+    odS = plan.add((size_t)P * nch * n * 4);
+    oSt = plan.add((size_t)P * nch * n * opsz);
+  }
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -197,6 +251,20 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
     return TTT_OK;
   }
   char* ws = static_cast<char*>(workspace);
+  if (fused) {
+    try {
+#define TTT_FUSED(IOT, OPT, HH, RR) \
+  if (q.h == HH && rh64 == RR)      \
+    return linattn_fused_run<IOT, OPT, HH, RR>(q, ws, oAgg, oIncl, oFl, oTk, Q, K, V, eta, W0, W2, W1, O, S_out, st);
+      TTT_FUSED(bf16_t, _Float16, 32, 64)
+      TTT_FUSED(bf16_t, _Float16, 32, 128)
+      TTT_FUSED(bf16_t, _Float16, 64, 128)
+#undef TTT_FUSED
+    } catch (...) {
+      return TTT_ERR_HIP;
+    }
+    return TTT_ERR_UNSUPPORTED;
+  }
 #define TTT_LIN_CASE(IOT, OPT, HH) \
   case HH:                         \
     return linattn_run<IOT, OPT, HH>(q, ws, oSh, odS, oSt, Q, K, V, eta, W0, W2, W1, O, S_out, st);
