@@ -144,10 +144,17 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   float* aggp = a.agg + (int64_t)pair * a.nch * n;
   float* inclp = a.incl + (int64_t)pair * a.nch * n;
 
-  // ---- token-tile staging (K and V; Q reuses the K half), rows past the chunk end are zero ----
-  u32x4 sk[CPT], sv[CPT];
-  float ev = 0.f;
-  auto fetch = [&](int t0) {
+  // ---- token-tile staging of K, V, eta (rows past the chunk end are zero); two register sets
+  // alternate, so a tile is requested two tiles before it is stored to LDS ----
+  struct Staged {
+    u32x4 k[CPT], v[CPT];
+    float e;
+  };
+  Staged sa, sb;
+  auto fetch = [&](int t0, Staged& sg) {
+    u32x4* sk = sg.k;
+    u32x4* sv = sg.v;
+    if (t0 >= cend) return;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c16 = tid + NT * i;
@@ -156,9 +163,11 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
       sk[i] = in ? *reinterpret_cast<const u32x4*>(Kp + (int64_t)(t0 + row) * H + col) : u32x4{0u, 0u, 0u, 0u};
       sv[i] = in ? *reinterpret_cast<const u32x4*>(Vp + (int64_t)(t0 + row) * H + col) : u32x4{0u, 0u, 0u, 0u};
     }
-    if (tid < TT) ev = (t0 + tid < cend) ? ep[t0 + tid] : 0.f;
+    if (tid < TT) sg.e = (t0 + tid < cend) ? ep[t0 + tid] : 0.f;
   };
-  auto put = [&](int buf) {
+  auto put = [&](int buf, const Staged& sg) {
+    const u32x4* sk = sg.k;
+    const u32x4* sv = sg.v;
     OpT* kb = tiles + buf * 2 * TILE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -169,11 +178,12 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
         TileStage<IoT, OpT, H>::put(sv[i], kb + TILE + row * LDK + col);
       }
     }
-    if (tid < TT) eta_s[buf * TT + tid] = ev;
+    if (tid < TT) eta_s[buf * TT + tid] = sg.e;
   };
 
   const int ntile = (a.chunk + TT - 1) / TT;
-  fetch(cbase);
+  fetch(cbase, sa);
+  fetch(cbase + TT, sb);
 
   // ---- fast-weight fragments of hidden rows jb*32 + (lane & 31): MFMA B operands in phase A,
   // A operands in phase C (same lane layout); W0^T / W2^T also go to LDS for phase C ----
@@ -203,10 +213,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   f32x16 acc[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) zero(acc[c]);
-  for (int i = 0; i < ntile; ++i) {
+  auto tile_step = [&](int i, Staged& sg) {
     __syncthreads();  // the buffer written next is no longer read
-    put(i & 1);
-    if (i + 1 < ntile) fetch(cbase + (i + 1) * TT);
+    put(i & 1, sg);
+    fetch(cbase + (i + 2) * TT, sg);
     __syncthreads();
     const OpT* kb = tiles + (i & 1) * 2 * TILE;
     const OpT* vb = kb + TILE;
@@ -233,6 +243,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 #pragma unroll
       for (int c = 0; c < CB; ++c) acc[c] = M::mma(af, acc_kfrag_tr<OpT>(vh + c * 32, LDK, q, lane), acc[c]);
     }
+  };
+  for (int i = 0; i < ntile; i += 2) {
+    tile_step(i, sa);
+    if (i + 1 < ntile) tile_step(i + 1, sb);
   }
   // token halves: wave (jb, 1) hands its sums to wave (jb, 0); publish the aggregate
   __syncthreads();
@@ -254,6 +268,19 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   drain_stores();
   __syncthreads();
   if (tid == 0) __hip_atomic_store(fl + ch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // the first query pass's rows are requested now and arrive during the lookback
+  static_assert(std::is_same<IoT, bf16_t>::value && std::is_same<OpT, _Float16>::value, "bf16 I/O");
+  u32x4 qa[KS], qb[KS];
+  auto load_q = [&](int t0, u32x4 (&qr)[KS]) {
+    const int t = t0 + 32 * w + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
+      qr[s] = (t0 < cend && t < cend) ? *reinterpret_cast<const u32x4*>(Qp + (int64_t)t * H + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  load_q(cbase, qa);
 
   // ---- B. decoupled lookback ----
   if (tid == 0) {
@@ -326,29 +353,13 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 
   // ---- C. O = phi(Q) S for the chunk's query tokens, wave w: 32 tokens per pass ----
   const float poison = bad ? __builtin_nanf("") : 0.f;
-  for (int t0 = cbase; t0 < cend; t0 += NW * 32) {
+  auto pass = [&](int t0, const u32x4 (&qcur)[KS], u32x4 (&qnext)[KS]) {
+    load_q(t0 + NW * 32, qnext);
     const int tw = t0 + 32 * w;
     if (tw < cend) {
       frag qf[KS];
-      const int t = tw + (lane & 31);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
-        if constexpr (M::KSUB == 8) {
-          OpT tmp[8];
-          if (t < cend) {
-            Io<IoT>::template load_cvt<OpT>(Qp + (int64_t)t * H + c, tmp);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = M::from_f32(0.f);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qf[s][e] = tmp[e];
-        } else {
-          static_assert(std::is_same<IoT, float>::value, "fp32 operands come with fp32 I/O");
-          qf[s] = t < cend ? Qp[(int64_t)t * H + c] : 0.f;
-        }
-      }
+      for (int s = 0; s < KS; ++s) qf[s] = bf16x8_to_f16x8(qcur[s]);
       f32x16 o[CB];
 #pragma unroll
       for (int c = 0; c < CB; ++c) zero(o[c]);
@@ -403,6 +414,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
           }
       }
     }
+  };
+  for (int t0 = cbase; t0 < cend; t0 += 2 * NW * 32) {
+    pass(t0, qa, qb);
+    if (t0 + NW * 32 < cend) pass(t0 + NW * 32, qb, qa);
   }
 }
 
