@@ -260,23 +260,30 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   if (u.muon) inv = 1.f / (sqrtf(block_sum(ss, red)) + u.eps_ns);
   __syncthreads();
 
-  // chunk staging: rows ch*JC .. of U (state rows j, h columns) scaled by inv, as X^T hi / lo
-  f32x4 cv[CG4];
-  auto chunk_load = [&](int ch) {
+  // chunk staging: rows ch*JC .. of U (state rows j, h columns) scaled by inv, as X^T hi / lo.
+  // All chunks of the matrix are requested at once (they come from L2: step 1 just wrote them).
+  f32x4 cv[NCH][CG4];
+  auto chunk_load_all = [&]() {
 #pragma unroll
-    for (int i = 0; i < CG4; ++i) {
-      const int e4 = tid + 512 * i;
-      cv[i] = e4 < JC * H / 4 ? *reinterpret_cast<const f32x4*>(Ud + (int64_t)ch * JC * H + 4 * e4)
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int i = 0; i < CG4; ++i) {
+        const int e4 = tid + 512 * i;
+        cv[ch][i] = e4 < JC * H / 4 ? *reinterpret_cast<const f32x4*>(Ud + (int64_t)ch * JC * H + 4 * e4)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
   };
-  auto chunk_store = [&](bf16* bh, bf16* bl, int ld) {
+  auto chunk_store = [&](int ch, bf16* bh, bf16* bl, int ld) {
 #pragma unroll
-    for (int i = 0; i < CG4; ++i) {
-      const int e4 = tid + 512 * i;
-      if (e4 < JC * H / 4) {
-        const int row = (4 * e4) / H, c = (4 * e4) % H;
-        split_store4(bh + row * ld + c, bl + row * ld + c, cv[i] * inv);
+    for (int c4 = 0; c4 < NCH; ++c4) {
+      if (c4 != ch) continue;
+#pragma unroll
+      for (int i = 0; i < CG4; ++i) {
+        const int e4 = tid + 512 * i;
+        if (e4 < JC * H / 4) {
+          const int row = (4 * e4) / H, c = (4 * e4) % H;
+          split_store4(bh + row * ld + c, bl + row * ld + c, cv[c4][i] * inv);
+        }
       }
     }
   };
@@ -294,6 +301,23 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
       }
     }
   };
+  // the same blocks stored in their own orientation (element [c][c'] at row c): 2-byte stores,
+  // used once for Q, which the final product reads by rows
+  auto put_direct = [&](const f32x16 (&v)[QA], bf16* dh, bf16* dl) {
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int t = QA * w + q;
+      if (t < NBA) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = (t / HB) * 32 + acc_row(r, lane), c2 = (t % HB) * 32 + acc_col(lane);
+          const bf16 hi = static_cast<bf16>(v[q][r]);
+          dh[c * LDA + c2] = hi;
+          dl[c * LDA + c2] = static_cast<bf16>(v[q][r] - static_cast<float>(hi));
+        }
+      }
+    }
+  };
   auto zero_q = [&](f32x16 (&v)[QA]) {
 #pragma unroll
     for (int q = 0; q < QA; ++q) zero(v[q]);
@@ -306,16 +330,14 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
     zero_q(am);
     {
       auto gb = [&](int i) { return reinterpret_cast<bf16*>(smem + (i & 1) * L::CHG); };
-      chunk_load(0);
-      chunk_store(gb(0), gb(0) + JC * LDG, LDG);
-      if (NCH > 1) chunk_load(1);
+      chunk_load_all();
+      chunk_store(0, gb(0), gb(0) + JC * LDG, LDG);
       __syncthreads();
-#pragma unroll 1
+#pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         if (ch + 1 < NCH) {
           bf16* nb = gb(ch + 1);
-          chunk_store(nb, nb + JC * LDG, LDG);
-          if (ch + 2 < NCH) chunk_load(ch + 2);
+          chunk_store(ch + 1, nb, nb + JC * LDG, LDG);
         }
         bf16* cb = gb(ch);
         mma_blocks<JC, QA, HB, NBA, true, true>(am, w, cb, cb + JC * LDG, LDG, cb, cb + JC * LDG, LDG, lane);
@@ -368,7 +390,7 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
         __syncthreads();
       }
     }
-    put_sym(qm, S1h, S1l);  // Q in slot 1 for the final product
+    put_direct(qm, S1h, S1l);  // Q in slot 1, row-major, for the final product
     __syncthreads();
   }
 
@@ -398,9 +420,8 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   {
     auto fb = [&](int i) { return reinterpret_cast<bf16*>(smem + L::SLOT + (i & 1) * L::CHF); };
     if (u.muon) {
-      chunk_load(0);
-      chunk_store(fb(0), fb(0) + JC * LDF, LDF);
-      if (NCH > 1) chunk_load(1);
+      chunk_load_all();
+      chunk_store(0, fb(0), fb(0) + JC * LDF, LDF);
       __syncthreads();
     }
 #pragma unroll
@@ -410,12 +431,10 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
       if (u.muon) {
         if (ch + 1 < NCH) {
           bf16* nb = fb(ch + 1);
-          chunk_store(nb, nb + JC * LDF, LDF);
-          if (ch + 2 < NCH) chunk_load(ch + 2);
+          chunk_store(ch + 1, nb, nb + JC * LDF, LDF);
         }
         bf16* cb = fb(ch);
-        // slot 1 holds Q^T: read K-major for Q's rows
-        mma_blocks<H, 1, JBC, NBF, true, false>(cx, w, S1h, S1l, LDA, cb, cb + JC * LDF, LDF, lane);
+        mma_blocks<H, 1, JBC, NBF, false, false>(cx, w, S1h, S1l, LDA, cb, cb + JC * LDF, LDF, lane);
       }
       if (fact) {
 #pragma unroll
