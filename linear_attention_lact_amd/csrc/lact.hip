@@ -16,6 +16,7 @@
 #include "host.hpp"
 #include "timing.hpp"
 #include "update.hpp"
+#include "update_tiled.hpp"
 
 namespace ttt {
 
@@ -77,138 +78,6 @@ __global__ void __launch_bounds__(256) lact_final_kernel(LactState s, float* W0o
   float* wo = (mat == 0 ? W0o : mat == 1 ? W1o : W2o);
   if (wo) wo[(int64_t)pair * n + d] = s.W[((int64_t)pair * 3 + mat) * n + e];
   if (Mo) Mo[((int64_t)pair * 3 + mat) * n + d] = s.M[((int64_t)pair * 3 + mat) * n + e];
-}
-
-// ---------------------------------------------------------------------------------------
-// Fallback update for head dims whose h x h Gram matrix does not fit in LDS next to the X
-// columns: one workgroup per (matrix, pair), operands read from an L2-resident global scratch.
-// Same steps as lact_update_kernel (update.hpp). block 512 (8 waves).
-template <class OpT>
-__global__ void __launch_bounds__(512) lact_update_global_kernel(UpdateArgs u) {
-  const LactState& s = u.s;
-  const int mat = blockIdx.x, pair = blockIdx.y;
-  const uint32_t bit = mat == 0 ? 1u : mat == 1 ? 2u : 4u;
-  if (!(u.mask & bit)) return;
-  __shared__ float red[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
-  const int h = s.h, rh = s.rh;
-  const int64_t n = (int64_t)rh * h;
-  float* W = s.W + ((int64_t)pair * 3 + mat) * n;
-  float* M = s.M + ((int64_t)pair * 3 + mat) * n;
-  float* ns = s.ns + ((int64_t)pair * 3 + mat) * s.NSZ;
-  float* X[2] = {ns, ns + n};
-  float* Y[2] = {ns + 2 * n, ns + 3 * n};
-  float* A = ns + 4 * n;
-  float* Bq = A + (int64_t)h * h;
-  float* U = Y[0];  // the write, in the state layout
-
-  // gradient (sum over segments in order) and momentum
-  const int64_t seg_stride = (int64_t)s.P * 3 * n;
-  const float* part = s.part + ((int64_t)pair * 3 + mat) * n;
-  float ss = 0.f;
-  for (int64_t e = tid; e < n; e += blockDim.x) {
-    float g = 0.f;
-    for (int k = 0; k < u.S; ++k) g += part[k * seg_stride + e];
-    g = -g;
-    float v = g;
-    if (u.momentum != 0.f) {
-      v = u.momentum * M[e] + g;
-      M[e] = v;
-    }
-    U[e] = v;
-    ss += v * v;
-  }
-  if (u.muon) {
-    const float nrm = sqrtf(block_sum(ss, red));
-    const float inv = 1.f / (nrm + u.eps_ns);
-    __syncthreads();
-    for (int64_t e = tid; e < n; e += blockDim.x) {
-      const int j = (int)(e / h), c = (int)(e % h);
-      const float v = U[e] * inv;
-      U[e] = v;
-      X[0][(int64_t)c * rh + j] = v;
-    }
-    __syncthreads();
-    int cur = 0;
-    const int hb = h / 32, rb = rh / 32;
-    for (int it = 0; it < NS_STEPS; ++it) {
-      const float* Xc = X[cur];
-      const float* Yc = Y[cur];
-      for (int t = w; t < hb * hb; t += nw) {  // A = X X^T
-        const int ib = t / hb, kb = t % hb;
-        f32x16 acc;
-        zero(acc);
-        mma_tile_split(acc, Xc + (int64_t)ib * 32 * rh, rh, Xc + (int64_t)kb * 32 * rh, rh, rh, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) A[(ib * 32 + acc_row(r, lane)) * h + kb * 32 + acc_col(lane)] = acc[r];
-      }
-      __syncthreads();
-      for (int t = w; t < hb * hb; t += nw) {  // B = b A + c A A
-        const int ib = t / hb, kb = t % hb;
-        f32x16 acc;
-        zero(acc);
-        mma_tile_split(acc, A + ib * 32 * h, h, A + kb * 32 * h, h, h, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = ib * 32 + acc_row(r, lane), k = kb * 32 + acc_col(lane);
-          Bq[i * h + k] = NS_B * A[i * h + k] + NS_C * acc[r];
-        }
-      }
-      __syncthreads();
-      float* Xn = X[cur ^ 1];
-      float* Yn = Y[cur ^ 1];
-      for (int t = w; t < hb * rb; t += nw) {  // X = a X + B X
-        const int ib = t / rb, jb = t % rb;
-        f32x16 acc;
-        zero(acc);
-        mma_tile_split(acc, Bq + ib * 32 * h, h, Yc + (int64_t)jb * 32 * h, h, h, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = ib * 32 + acc_row(r, lane), j = jb * 32 + acc_col(lane);
-          const float v = NS_A * Xc[(int64_t)i * rh + j] + acc[r];
-          Xn[(int64_t)i * rh + j] = v;
-          Yn[(int64_t)j * h + i] = v;
-        }
-      }
-      __syncthreads();
-      cur ^= 1;
-    }
-    U = Y[cur];
-  }
-  __syncthreads();
-  // subtract, renormalise, write state and shadows
-  for (int64_t e = tid; e < n; e += blockDim.x) W[e] -= U[e];
-  __syncthreads();
-  const float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
-  if (u.weight_norm) {
-    if (mat == 1) {  // W1 [rh][h]: column c over the rh inputs
-      for (int c = tid; c < h; c += blockDim.x) {
-        float acc = 0.f;
-        for (int j = 0; j < rh; ++j) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
-        const float f = nu[c] / (sqrtf(acc) + u.eps_norm);
-        for (int j = 0; j < rh; ++j) W[(int64_t)j * h + c] *= f;
-      }
-    } else {  // W0T / W2T: row j over the h inputs
-      for (int j = w; j < rh; j += nw) {
-        float acc = 0.f;
-        for (int c = lane; c < h; c += 64) acc += W[(int64_t)j * h + c] * W[(int64_t)j * h + c];
-        acc = wave_sum(acc);
-        const float f = nu[j] / (sqrtf(acc) + u.eps_norm);
-        for (int c = lane; c < h; c += 64) W[(int64_t)j * h + c] *= f;
-      }
-    }
-  }
-  __syncthreads();
-  OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
-  OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
-  for (int64_t e = tid; e < n; e += blockDim.x) {
-    const float v = W[e];
-    dst[e] = Mfma<OpT>::from_f32(v);
-    if (mat == 1) {
-      const int j = (int)(e / h), c = (int)(e % h);
-      sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(v);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -295,7 +164,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   ua.eps_norm = p.eps_norm;
   ua.eps_ns = p.eps_ns;
 
-  // update path: LDS-resident kernel for the (h, rh) shapes it is built for, else the fallback
+  // update path: LDS-resident kernel for the (h, rh) shapes it is built for, else the tiled launches
   const void* uk = nullptr;
   int ulds = 0;
 #define TTT_UPD(HH, RR)                                                  \
@@ -306,7 +175,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   // With Muon the LDS kernel evaluates Newton-Schulz through the h x h Gram matrix, whose
   // rounding grows with the conditioning of the write (weak directions are amplified by up to
   // 3.4445^5). It is used for 16-bit I/O when a chunk has at least h tokens (the write can have
-  // full rank); fp32 I/O and shorter chunks keep the five explicit X rounds (fallback kernel).
+  // full rank); fp32 I/O and shorter chunks keep the five explicit X rounds (tiled launches).
   const bool gram_ok = !p.muon || (sizeof(OpT) == 2 && p.chunk_kv >= H);
   if (gram_ok) {
     if constexpr (H == 32) { TTT_UPD(32, 64) TTT_UPD(32, 128) }
@@ -355,8 +224,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
       if (uk) {
         TTT_HIP(hipLaunchKernel(uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
       } else {
-        hipLaunchKernelGGL(lact_update_global_kernel<OpT>, dim3(3, P), dim3(512), 0, st, ua);
-        TTT_HIP(hipGetLastError());
+        TTT_HIP(tu_run<OpT>(ua, st));
       }
     }
     if (p.order == TTT_UPDATE_THEN_APPLY) {
@@ -418,7 +286,7 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   const size_t oSh = plan.add((size_t)P * 4 * n * opsz);
   const size_t oPart = plan.add((size_t)S * P * 3 * n * 4);
   const size_t oU = plan.add((size_t)P * 3 * n * 4);
-  const int64_t NSZ = 4 * n + 2 * (int64_t)h * h;
+  const int64_t NSZ = 4 * n + 2 * (int64_t)h * h + TU_SS;
   const size_t oNs = plan.add((size_t)P * 3 * NSZ * 4);
   if (!workspace) {
     *workspace_bytes = plan.total;
