@@ -221,6 +221,8 @@ def main():
             work = {"lact_grad": P * 6 * 2.0 * p.chunk_kv * p.h * rh,
                     "lact_apply": P * 3 * 2.0 * p.chunk_q * p.h * rh,
                     "lact_update": P * n_upd * acc.ns5_flops(p.h, rh) if p.muon else 0.0}
+            # apply-then-update order: the update and the same chunk's apply share one launch
+            work["lact_update_apply"] = work["lact_update"] + work["lact_apply"]
             bound, peak, unit = "mfma", acc.PEAK_BF16_TFLOPS, "TFLOP/s"
             metric = ("TTT-layer tokens/sec at h=128, chunk 2048 bf16; % of bf16 MFMA peak" if k == 2 else
                       "TTT-layer tokens/sec, view-synthesis shape (h=192, 196608 context + 4096 query), bf16")

@@ -96,7 +96,8 @@ def profiled_traffic(root: str, kernel_class: str, stem: str):
     import os
     symbol = {"lact_update": "lact_update_kernel", "lact_grad": "grad_rd_kernel", "lact_apply": "apply_rd_kernel",
               "linattn_delta": "grad_rd_kernel", "linattn_apply": "apply_rd_kernel",
-              "linattn_scan": "linattn_scan_kernel"}
+              "linattn_scan": "linattn_scan_kernel", "lact_update_apply": "lact_update_apply_kernel",
+              "linattn_fused": "linattn_fused_kernel"}
     sym = symbol.get(kernel_class)
     if sym is None:
         return None

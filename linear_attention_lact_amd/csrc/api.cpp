@@ -22,7 +22,7 @@ namespace {
 const char* kClassNames[K_NUM_CLASSES] = {
     "lact_init", "lact_grad", "lact_update", "lact_apply", "lact_final",
     "linattn_prep", "linattn_delta", "linattn_scan", "linattn_apply", "linattn_fused",
-    "inplace_prep", "inplace_z", "inplace_apply", "inplace_update"};
+    "inplace_prep", "inplace_z", "inplace_apply", "inplace_update", "lact_update_apply"};
 struct Rec { int cls; hipEvent_t a, b; };
 std::mutex mu;
 bool on = false;

@@ -663,7 +663,7 @@ template <class OpT, int H>
 constexpr int apply_rd_lds_bytes() { return ApplyRdLayout<OpT, H>::bytes; }
 
 template <class IoT, class OpT, int H>
-__global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
+__device__ __forceinline__ void apply_rd_body(const ApplyArgs& a, int bid, unsigned char* smem) {
   static_assert(H <= 128, "register budget");
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
@@ -675,10 +675,8 @@ __global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
   constexpr int VW = 16 / (int)sizeof(OpT); // elements per 16-byte chunk
   constexpr int NCHK = 3 * AJ * H / VW;     // 16-byte chunks of one staged block
   constexpr int CPT = (NCHK + 511) / 512;
-  extern __shared__ __align__(16) unsigned char smem[];
-
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bid = blockIdx.x, slot = bid >> 3;
+  const int slot = bid >> 3;
   const int pair = (bid & 7) + 8 * (slot / a.ntiles);
   const int tile = slot % a.ntiles;
   if (pair >= a.npairs) return;
@@ -811,6 +809,13 @@ __global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
         if (t < t_lim) Io<IoT>::store(Op + (int64_t)t * H + cb * 32 + acc_col(lane), o[cb][r]);
       }
   }
+}
+
+// workgroup bid: pair (bid & 7) + 8 * (slot / ntiles), 256-token tile slot % ntiles (slot = bid >> 3)
+template <class IoT, class OpT, int H>
+__global__ void __launch_bounds__(512) apply_rd_kernel(ApplyArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  apply_rd_body<IoT, OpT, H>(a, blockIdx.x, smem);
 }
 
 }  // namespace ttt

@@ -40,9 +40,25 @@ __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float
   const float v = src[si];
   s.W[((int64_t)pair * 3 + mat) * n + e] = v;
   s.M[((int64_t)pair * 3 + mat) * n + e] = M_in ? M_in[((int64_t)pair * 3 + mat) * n + si] : 0.f;
-  OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
-  sh[(mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + e] = Mfma<OpT>::from_f32(v);
-  if (mat == 1) sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(v);
+  // both shadow buffers: a matrix outside the update mask keeps its initial shadow in each
+  for (int buf = 0; buf < 2; ++buf) {
+    OpT* sh = reinterpret_cast<OpT*>(s.sh) + ((int64_t)buf * s.P + pair) * 4 * n;
+    sh[(mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + e] = Mfma<OpT>::from_f32(v);
+    if (mat == 1) sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(v);
+  }
+}
+
+// The weight update of chunk c and the apply of the same chunk (apply-then-update order) in
+// one launch: the first nupd workgroups run the update (one matrix each, writing the other
+// shadow buffer), the rest the apply (reading the shadows the chunk's gradient used). The
+// update occupies one CU per matrix; the apply's workgroups fill the remaining CUs meanwhile.
+template <class IoT, class OpT, int H, int RH>
+__global__ void __launch_bounds__(512) lact_update_apply_kernel(UpdateArgs u, ApplyArgs a, int nupd) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x < nupd)
+    lact_update_body<OpT, H, RH>(u, blockIdx.x, smem);
+  else
+    apply_rd_body<IoT, OpT, H>(a, blockIdx.x - nupd, smem);
 }
 
 // renorm targets (column norms of the initial row-form weights over their input axis).
@@ -115,7 +131,10 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     TTT_HIP(hipGetLastError());
   }
 
+  // operand shadows, double-buffered: chunk c's gradient and apply read buffer c & 1 while its
+  // update writes buffer (c + 1) & 1
   const OpT* sh = reinterpret_cast<const OpT*>(s.sh);
+  const int64_t shb = (int64_t)P * 4 * n;
   ApplyArgs aa{};
   aa.Q = Q;
   aa.tok_pair_stride = (int64_t)p.Nq * H;
@@ -167,10 +186,12 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   // update path: LDS-resident kernel for the (h, rh) shapes it is built for, else the tiled launches
   const void* uk = nullptr;
   int ulds = 0;
-#define TTT_UPD(HH, RR)                                                  \
-  if (H == HH && rh == RR) {                                             \
-    uk = reinterpret_cast<const void*>(lact_update_kernel<OpT, HH, RR>); \
-    ulds = update_lds_bytes<HH, RR>();                                   \
+  const void* uak = nullptr;  // update + apply in one launch
+#define TTT_UPD(HH, RR)                                                                         \
+  if (H == HH && rh == RR) {                                                                    \
+    uk = reinterpret_cast<const void*>(lact_update_kernel<OpT, HH, RR>);                        \
+    ulds = update_lds_bytes<HH, RR>();                                                          \
+    if constexpr (ARD) uak = reinterpret_cast<const void*>(lact_update_apply_kernel<IoT, OpT, HH, RR>); \
   }
   // With Muon the LDS kernel evaluates Newton-Schulz through the h x h Gram matrix, whose
   // rounding grows with the conditioning of the write (weak directions are amplified by up to
@@ -187,7 +208,13 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   if (uk) {
     TTT_HIP(hipFuncSetAttribute(uk, hipFuncAttributeMaxDynamicSharedMemorySize, ulds));
   }
+  const bool fuse_ua = uak && p.order == TTT_APPLY_THEN_UPDATE;
+  const int ualds = std::max(ulds, alds);
+  if (fuse_ua) {
+    TTT_HIP(hipFuncSetAttribute(uak, hipFuncAttributeMaxDynamicSharedMemorySize, ualds));
+  }
   const unsigned ugrid = (unsigned)(3 * P);
+  const int nupd = 8 * ((3 * P + 7) / 8);  // keeps the apply's workgroup -> XCD mapping
 
   const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
   auto apply = [&]() -> ttt_status {
@@ -199,10 +226,23 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     TTT_HIP(hipGetLastError());
     return TTT_OK;
   };
+  auto set_apply_weights = [&](const OpT* b) {
+    aa.W0T = b;
+    aa.W2T = b + n;
+    aa.W1 = b + 2 * n;
+    aa.W1T = b + 3 * n;
+  };
   for (int c = 0; c < nch; ++c) {
+    const OpT* rd = sh + (c & 1) * shb;
+    const OpT* wr = sh + ((c + 1) & 1) * shb;
+    set_apply_weights(rd);
+    ga.W0T = rd;
+    ga.W2T = rd + n;
+    ga.W1 = rd + 2 * n;
+    ua.s.sh = const_cast<OpT*>(wr);
     aa.t_base = c * p.chunk_q;
     aa.t_limit = (c + 1) * p.chunk_q;
-    if (p.order == TTT_APPLY_THEN_UPDATE) {
+    if (p.order == TTT_APPLY_THEN_UPDATE && !fuse_ua) {
       const ttt_status e = apply();
       if (e != TTT_OK) return e;
     }
@@ -218,6 +258,13 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
       }
       TTT_HIP(hipGetLastError());
     }
+    if (fuse_ua) {
+      LaunchTimer lt(K_LACT_UPD_APPLY, st);
+      int nu = nupd;
+      void* args[] = {&ua, &aa, &nu};
+      TTT_HIP(hipLaunchKernel(uak, dim3((unsigned)nupd + agrid.x), dim3(512), args, (size_t)ualds, st));
+      continue;
+    }
     {
       LaunchTimer lt(K_LACT_UPDATE, st);
       void* args[] = {&ua};
@@ -228,6 +275,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
       }
     }
     if (p.order == TTT_UPDATE_THEN_APPLY) {
+      set_apply_weights(wr);
       const ttt_status e = apply();
       if (e != TTT_OK) return e;
     }
@@ -283,7 +331,7 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   const size_t oM = plan.add((size_t)P * 3 * n * 4);
   const int NU = std::max(rh, h);
   const size_t oNu = plan.add((size_t)P * 3 * NU * 4);
-  const size_t oSh = plan.add((size_t)P * 4 * n * opsz);
+  const size_t oSh = plan.add((size_t)2 * P * 4 * n * opsz);
   const size_t oPart = plan.add((size_t)S * P * 3 * n * 4);
   const size_t oU = plan.add((size_t)P * 3 * n * 4);
   const int64_t NSZ = 4 * n + 2 * (int64_t)h * h + TU_SS;

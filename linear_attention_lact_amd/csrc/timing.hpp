@@ -8,6 +8,7 @@ enum KernelClass {
   K_LACT_INIT = 0, K_LACT_GRAD, K_LACT_UPDATE, K_LACT_APPLY, K_LACT_FINAL,
   K_LIN_PREP, K_LIN_DELTA, K_LIN_SCAN, K_LIN_APPLY, K_LIN_FUSED,
   K_INP_PREP, K_INP_Z, K_INP_APPLY, K_INP_UPDATE,
+  K_LACT_UPD_APPLY,  // weight update and the chunk's apply in one launch
   K_NUM_CLASSES
 };
 

@@ -191,7 +191,7 @@ constexpr int update_lds_bytes() { return UpdLayout<H, RH>::bytes; }
 // (not symmetry-assumed) result wherever a matrix is symmetric only up to rounding: Q's
 // dynamic range (up to 3.4445^5 in weak directions) amplifies any such asymmetry.
 template <class OpT, int H, int RH>
-__global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
+__device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, unsigned char* smem) {
   typedef UpdLayout<H, RH> L;
   constexpr int JC = L::JC, NCH = L::NCH, LDA = L::LDA, LDG = L::LDG, LDF = L::LDF;
   constexpr int HB = L::HB, NBA = L::NBA, QA = L::QA, NBF = L::NBF;
@@ -200,7 +200,6 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   constexpr int CG4 = JC * H / 4 / 512 > 0 ? JC * H / 4 / 512 : 1;   // float4 groups per chunk per thread
   static_assert(JC * H / 4 <= 512 * CG4, "chunk map");
   const LactState& s = u.s;
-  extern __shared__ __align__(16) unsigned char smem[];
   bf16* S1h = reinterpret_cast<bf16*>(smem);                 // slot 1 [H][LDA] hi, then lo
   bf16* S1l = S1h + H * LDA;
   bf16* S2h = reinterpret_cast<bf16*>(smem + L::SLOT);       // slot 2
@@ -210,7 +209,6 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
   float* red = fac + L::NF;                                  // [32]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int mi = blockIdx.x;
   if (mi >= 3 * s.P) return;
   const int pair = mi / 3, mat = mi % 3;
   const uint32_t bit = mat == 0 ? 1u : mat == 1 ? 2u : 4u;
@@ -525,6 +523,13 @@ __global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
         }
       }
   }
+}
+
+// workgroup mi handles matrix mi % 3 of pair mi / 3
+template <class OpT, int H, int RH>
+__global__ void __launch_bounds__(512) lact_update_kernel(UpdateArgs u) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  lact_update_body<OpT, H, RH>(u, blockIdx.x, smem);
 }
 
 }  // namespace ttt
