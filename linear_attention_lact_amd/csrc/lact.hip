@@ -21,30 +21,54 @@
 namespace ttt {
 
 // ---------------------------------------------------------------------------------------
-// init: the initial state (W0, W2 transposed into rows of hidden units), momentum and operand
-// shadows, one thread per state element. grid (ceil(n/256), 3, P), block 256.
+// init: the initial state (W0, W2 transposed into rows of hidden units), momentum and both
+// operand shadow buffers (a matrix outside the update mask keeps its initial shadow in each).
+// grid (rh/32 * h/32, 3, P), block 256: one 32 x 32 tile of the state (rows j, columns c);
+// W0/W2 and their momentum arrive in row form [h][rh] and are transposed through LDS.
 template <class OpT>
 __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float* W0, const float* W1,
                                                        const float* W2, const float* M_in, int H,
                                                        int64_t w_batch_stride) {
+  __shared__ float tw[32][33], tm[32][33];
   const int mat = blockIdx.y, pair = blockIdx.z;
-  const int h = s.h, rh = s.rh;
+  const int h = s.h, rh = s.rh, hb = h / 32;
   const int64_t n = (int64_t)rh * h;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n) return;
+  const int j0 = (blockIdx.x / hb) * 32, c0 = (blockIdx.x % hb) * 32;
   const int b = pair / H, head = pair % H;
   const float* src = (mat == 0 ? W0 : mat == 1 ? W1 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
-  const int j = (int)(e / h), c = (int)(e % h);  // state element [j][c]
-  // row-form source: W0/W2 are [h][rh] (element [c][j]); W1 is [rh][h] (element [j][c])
-  const int64_t si = (mat == 1) ? e : (int64_t)c * rh + j;
-  const float v = src[si];
-  s.W[((int64_t)pair * 3 + mat) * n + e] = v;
-  s.M[((int64_t)pair * 3 + mat) * n + e] = M_in ? M_in[((int64_t)pair * 3 + mat) * n + si] : 0.f;
-  // both shadow buffers: a matrix outside the update mask keeps its initial shadow in each
+  const float* msrc = M_in ? M_in + ((int64_t)pair * 3 + mat) * n : nullptr;
+  const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+  // row-form tile rows: state rows j (W1) or input columns c (W0, W2)
+  const int64_t so = mat == 1 ? (int64_t)(j0 + r) * h + c0 + c4 : (int64_t)(c0 + r) * rh + j0 + c4;
+  const f32x4 v = *reinterpret_cast<const f32x4*>(src + so);
+  const f32x4 m = msrc ? *reinterpret_cast<const f32x4*>(msrc + so) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    tw[r][c4 + q] = v[q];
+    tm[r][c4 + q] = m[q];
+  }
+  __syncthreads();
+  f32x4 sv = v, sm = m;  // state row j0 + r, columns c0 + c4..
+  if (mat != 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sv[q] = tw[c4 + q][r];
+      sm[q] = tm[c4 + q][r];
+    }
+  }
+  const int64_t e = (int64_t)(j0 + r) * h + c0 + c4;
+  *reinterpret_cast<f32x4*>(s.W + ((int64_t)pair * 3 + mat) * n + e) = sv;
+  *reinterpret_cast<f32x4*>(s.M + ((int64_t)pair * 3 + mat) * n + e) = sm;
   for (int buf = 0; buf < 2; ++buf) {
     OpT* sh = reinterpret_cast<OpT*>(s.sh) + ((int64_t)buf * s.P + pair) * 4 * n;
-    sh[(mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + e] = Mfma<OpT>::from_f32(v);
-    if (mat == 1) sh[3 * n + (int64_t)c * rh + j] = Mfma<OpT>::from_f32(v);
+    OpT* d = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + e;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = Mfma<OpT>::from_f32(sv[q]);
+    if (mat == 1) {  // W1^T [h][rh]: row c0 + r, columns j0 + c4..
+      OpT* dt = sh + 3 * n + (int64_t)(c0 + r) * rh + j0 + c4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dt[q] = Mfma<OpT>::from_f32(tw[c4 + q][r]);
+    }
   }
 }
 
@@ -80,20 +104,37 @@ __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const floa
   }
 }
 
-// finalize: state and momentum back to the API's row form, one thread per output element.
-// grid (ceil(n/256), 3, P), block 256.
+// finalize: state and momentum back to the API's row form (W0/W2 transposed through LDS).
+// grid (rh/32 * h/32, 3, P), block 256: one 32 x 32 state tile.
 __global__ void __launch_bounds__(256) lact_final_kernel(LactState s, float* W0o, float* W1o, float* W2o,
                                                         float* Mo) {
+  __shared__ float tw[32][33], tm[32][33];
   const int mat = blockIdx.y, pair = blockIdx.z;
-  const int h = s.h, rh = s.rh;
+  const int h = s.h, rh = s.rh, hb = h / 32;
   const int64_t n = (int64_t)rh * h;
-  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (d >= n) return;
-  // row-form element d: W1 [rh][h] is the state layout; W0/W2 [h][rh] element [c][j]
-  const int64_t e = (mat == 1) ? d : (int64_t)(d % rh) * h + d / rh;
+  const int j0 = (blockIdx.x / hb) * 32, c0 = (blockIdx.x % hb) * 32;
+  const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+  const int64_t e = (int64_t)(j0 + r) * h + c0 + c4;
+  f32x4 v = *reinterpret_cast<const f32x4*>(s.W + ((int64_t)pair * 3 + mat) * n + e);
+  f32x4 m = *reinterpret_cast<const f32x4*>(s.M + ((int64_t)pair * 3 + mat) * n + e);
+  int64_t d = e;  // row-form offset of this thread's four outputs
+  if (mat != 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tw[r][c4 + q] = v[q];
+      tm[r][c4 + q] = m[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = tw[c4 + q][r];
+      m[q] = tm[c4 + q][r];
+    }
+    d = (int64_t)(c0 + r) * rh + j0 + c4;
+  }
   float* wo = (mat == 0 ? W0o : mat == 1 ? W1o : W2o);
-  if (wo) wo[(int64_t)pair * n + d] = s.W[((int64_t)pair * 3 + mat) * n + e];
-  if (Mo) Mo[((int64_t)pair * 3 + mat) * n + d] = s.M[((int64_t)pair * 3 + mat) * n + e];
+  if (wo) *reinterpret_cast<f32x4*>(wo + (int64_t)pair * n + d) = v;
+  if (Mo) *reinterpret_cast<f32x4*>(Mo + ((int64_t)pair * 3 + mat) * n + d) = m;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -124,8 +165,8 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const int nch = p.Nk / p.chunk_kv;
   {
     LaunchTimer lt(K_LACT_INIT, st);
-    hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0,
-                       W1, W2, M_in, p.H, p.w_batch_stride);
+    hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3((unsigned)(n / 1024), 3, P), dim3(256), 0, st, s, W0, W1,
+                       W2, M_in, p.H, p.w_batch_stride);
     TTT_HIP(hipGetLastError());
     hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
     TTT_HIP(hipGetLastError());
@@ -281,8 +322,8 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     }
   }
   LaunchTimer lt_fin(K_LACT_FINAL, st);
-  hipLaunchKernelGGL(lact_final_kernel, dim3((unsigned)((n + 255) / 256), 3, P), dim3(256), 0, st, s, W0o, W1o,
-                     W2o, Mo);
+  hipLaunchKernelGGL(lact_final_kernel, dim3((unsigned)(n / 1024), 3, P), dim3(256), 0, st, s, W0o, W1o, W2o,
+                     Mo);
   TTT_HIP(hipGetLastError());
   return TTT_OK;
 }
