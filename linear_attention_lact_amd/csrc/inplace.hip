@@ -8,6 +8,8 @@
 // All three are "TN" products C[M x N] = A[M x K] B[N x K]^T with K-contiguous operands:
 // Z is written both token-major (for the apply, contracting over d_hidden) and hidden-major
 // (for the update, contracting over tokens); Vbar is transposed once per sequence.
+#include <mutex>
+
 #include "common.hpp"
 #include "host.hpp"
 #include "timing.hpp"
@@ -148,6 +150,225 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(Args g) {
 }
 }  // namespace gemm
 
+// ---------------------------------------------------------------------------------------------
+// Large-tile TN GEMM for shapes divisible by its tile: 256 x 256 outputs per workgroup (SwiGLU:
+// 256 tokens x 128 hidden units for each of the two B operands), K in blocks of 64, 8 waves
+// (2 per SIMD, so one wave's LDS reads overlap the other's MFMAs), each a 128 x 64 block of
+// 4 x 2 MFMA 32x32x16 tiles. Operand tiles go global -> LDS directly (16-byte lane-contiguous
+// DMA loads, no register staging), double-buffered: the loads of block k + 2 are issued once
+// every wave is done with block k. LDS rows are 128 bytes (64 bf16); the 16-byte K chunk c of
+// row r sits at position c ^ (r % 8) ^ ((r / 8) % 2), so the rows an MFMA operand read touches
+// together fall into distinct bank groups. An optional K split writes fp32 partials that a
+// second kernel adds in split order.
+namespace gemm2 {
+using gemm::Args;
+using gemm::EPI_SWIGLU;
+using gemm::EPI_STORE;
+using gemm::EPI_RMW;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int ROWB = BK * 2;                    // bytes per staged row
+constexpr int STAGE = (BM + BN) * ROWB;         // 64 KB: A rows, then B rows
+constexpr int LDS = 2 * STAGE;
+constexpr int THREADS = 512;
+constexpr int EPI_PARTIAL = 3;                  // fp32 partial of one K split
+
+template <int EPI>
+constexpr int tile_n() { return EPI == EPI_SWIGLU ? BN / 2 : BN; }
+
+__device__ __forceinline__ int chunk_pos(int c, int row) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
+
+// grid: ksplit * (M / BM) * (N / tile_n) workgroups of 512 threads; split fastest, then N tile.
+// Wave w: rows (w & 1) * 128.. of the A tile; B rows (w >> 1) * 64.. (SwiGLU: gate rows
+// (w >> 1) * 32.. and the same up rows, so each wave holds both factors of its outputs).
+template <int EPI>
+__global__ void __launch_bounds__(512) gemm_big_kernel(Args g, int ksplit, float* part) {
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr int TN = tile_n<EPI>();
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int ntn = g.N / TN;
+  int bid = blockIdx.x;
+  const int ks = bid % ksplit;
+  bid /= ksplit;
+  const int m0 = (bid / ntn) * BM, n0 = (bid % ntn) * TN;
+  const int kper = g.K / ksplit, kbeg = ks * kper, nkb = kper / BK;
+
+  // staging: instruction j of wave w fills rows 32w + 8j .. +8 of each operand tile; lane l
+  // takes row + l/8 and LDS chunk l%8
+  const int lr = lane >> 3;
+  const __bf16* asrc[4];
+  const __bf16* bsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * w + 8 * j + lr;
+    const int ch = chunk_pos(lane & 7, row);
+    asrc[j] = g.A + (int64_t)(m0 + row) * g.lda + kbeg + ch * 8;
+    // B tile rows: SwiGLU rows 0..127 gate, 128..255 up (same hidden units n0..n0+127)
+    bsrc[j] = SW ? (row < 128 ? g.B0 : g.B1) + (int64_t)(n0 + (row & 127)) * g.ldb + kbeg + ch * 8
+                 : g.B0 + (int64_t)(n0 + row) * g.ldb + kbeg + ch * 8;
+  }
+  auto issue = [&](int kb, int stage) {
+    unsigned char* sa = smem + stage * STAGE + (32 * w) * ROWB;
+    unsigned char* sb = smem + stage * STAGE + (BM + 32 * w) * ROWB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds(asrc[j] + kb * BK, sa + 8 * j * ROWB, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc[j] + kb * BK, sb + 8 * j * ROWB, 16, 0, 0);
+    }
+  };
+
+  // operand reads: A rows wm*128 + 32i + lane%32, B rows (per j) from brow_of; K chunk 2s + lane/32
+  const int arow = wm * 128 + (lane & 31);
+  auto brow_of = [&](int j) {
+    return BM + (SW ? j * 128 + wn * 32 : wn * 64 + 32 * j) + (lane & 31);
+  };
+  int coff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) coff[s] = chunk_pos(2 * s + (lane >> 5), lane & 31) * 16;  // same for all rows used
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) zero(acc[i][j]);
+
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  for (int kb = 0; kb < nkb; ++kb) {
+    // block kb landed (this wave's 8 loads of block kb + 1 may still be in flight), then every
+    // wave's part of it. Plain s_barrier: __syncthreads would also wait for block kb + 1.
+    if (kb + 1 < nkb)
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const unsigned char* st = smem + (kb & 1) * STAGE;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + (arow + 32 * i) * ROWB + coff[s]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + brow_of(j) * ROWB + coff[s]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave is done with this stage
+    if (kb + 2 < nkb) issue(kb + 2, kb & 1);
+  }
+
+  if constexpr (EPI == EPI_RMW) {
+    // W += alpha * acc through LDS in four passes of 64 rows, so that the fp32 state is read and
+    // written in whole 16-byte runs per lane (1 KB per row) with eight loads in flight per thread
+    constexpr int LDE = BN + 4;                 // padded fp32 row
+    float* ep = reinterpret_cast<float*>(smem);
+    const int tid = threadIdx.x;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      if (wm == (pass >> 1)) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * (pass & 1) + ii;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              ep[(32 * ii + acc_row(r, lane)) * LDE + wn * 64 + 32 * j + acc_col(lane)] = acc[i][j][r];
+        }
+      }
+      __syncthreads();
+      f32x4 wv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int f = tid + THREADS * q, row = f >> 6, c4 = (f & 63) * 4;
+        wv[q] = *reinterpret_cast<const f32x4*>(g.Wf + (int64_t)(m0 + 64 * pass + row) * g.ldw + n0 + c4);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int f = tid + THREADS * q, row = f >> 6, c4 = (f & 63) * 4;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(ep + row * LDE + c4);
+        const f32x4 v = wv[q] + g.alpha * a;
+        const int64_t idx = (int64_t)(m0 + 64 * pass + row) * g.ldw + n0 + c4;
+        *reinterpret_cast<f32x4*>(g.Wf + idx) = v;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 s4 = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                           static_cast<__bf16>(v[3])};
+        *reinterpret_cast<bf16x4*>(g.Wsh + idx) = s4;
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // epilogues: tile (i, j) element r at row m0 + wm*128 + 32i + acc_row, column n + acc_col
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mb = m0 + wm * 128 + 32 * i;
+    if constexpr (SW) {
+      const int n = n0 + wn * 32 + acc_col(lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __bf16 zv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e;
+          const float gt = acc[i][0][r], up = acc[i][1][r];
+          zv[e] = static_cast<__bf16>(gt * sigmoidf_(gt) * up);
+          g.C[(int64_t)(mb + acc_row(r, lane)) * g.ldc + n] = zv[e];
+        }
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 v4 = {zv[0], zv[1], zv[2], zv[3]};
+        *reinterpret_cast<bf16x4*>(g.Ct + (int64_t)n * g.ldct + mb + acc_row(4 * q, lane)) = v4;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + 32 * j + acc_col(lane);
+        if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            g.C[(int64_t)(mb + acc_row(r, lane)) * g.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
+        } else if constexpr (EPI == EPI_PARTIAL) {
+          float* pp = part + (int64_t)ks * g.M * g.N;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pp[(int64_t)(mb + acc_row(r, lane)) * g.N + n] = acc[i][j][r];
+        }
+      }
+    }
+  }
+}
+
+// C[m][n] = bf16(sum over splits of part[s][m][n]), splits in order. grid-stride over float4.
+__global__ void __launch_bounds__(256) ksplit_sum_kernel(const float* part, int ksplit, int M, int N,
+                                                         __bf16* C, int64_t ldc) {
+  const int64_t mn = (int64_t)M * N;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += (int64_t)gridDim.x * 1024) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+    for (int s = 1; s < ksplit; ++s) v += *reinterpret_cast<const f32x4*>(part + s * mn + i);
+    const int64_t m = i / N, n = i % N;
+    __bf16* d = C + m * ldc + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = static_cast<__bf16>(v[e]);
+  }
+}
+
+template <int EPI>
+inline bool fits(const Args& g) {
+  return g.M % BM == 0 && g.N % tile_n<EPI>() == 0 && g.K % BK == 0 && g.K >= BK;
+}
+// splits of K that bring the grid to about one workgroup per CU, each at least 8 K blocks
+inline int choose_ksplit(const Args& g, int tiles) {
+  int best = 1;
+  for (int s = 2; s <= 16; ++s) {
+    if (tiles * (s - 1) >= 256) break;
+    if ((g.K / BK) % s == 0 && g.K / BK / s >= 8) best = s;
+  }
+  return best;
+}
+}  // namespace gemm2
+
 // fp32 -> bf16 shadow copy. grid-stride, 4 elements per thread step.
 __global__ void __launch_bounds__(256) to_bf16_kernel(const float* src, __bf16* dst, int64_t n) {
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * blockDim.x * 4) {
@@ -172,6 +393,58 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(const __bf16* src, 
   }
 }
 
+// Helper stream and events of the In-Place path, one set per device, created on first use and
+// kept for the life of the process. The stream has the default priority.
+struct InplaceStreams {
+  hipStream_t zs = nullptr;
+  hipEvent_t start = nullptr, zdone[2] = {nullptr, nullptr}, zfree[2] = {nullptr, nullptr};
+};
+static hipError_t inplace_streams(InplaceStreams** out) {
+  static std::mutex mu;
+  static InplaceStreams sets[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  InplaceStreams& s = sets[dev];
+  if (!s.zs) {
+    InplaceStreams t;
+    e = hipStreamCreateWithFlags(&t.zs, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t.start, hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      e = hipEventCreateWithFlags(&t.zdone[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&t.zfree[i], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) return e;
+    s = t;
+  }
+  *out = &s;
+  return hipSuccess;
+}
+
+// One TN GEMM: the large-tile kernel where the shape fits its tile, else the 128 x 128 kernel.
+// EPI_STORE with ksplit > 1 goes through fp32 partials in `part` and the split sum.
+template <int EPI>
+static hipError_t run_gemm(const gemm::Args& g, int ksplit, float* part, hipStream_t st) {
+  if (gemm2::fits<EPI>(g)) {
+    const unsigned tiles = (unsigned)((g.M / gemm2::BM) * (g.N / gemm2::tile_n<EPI>()));
+    if (EPI == gemm::EPI_STORE && ksplit > 1) {
+      hipLaunchKernelGGL(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, dim3(tiles * ksplit), dim3(gemm2::THREADS),
+                         gemm2::LDS, st, g, ksplit, part);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(gemm2::ksplit_sum_kernel, dim3(1024), dim3(256), 0, st, part, ksplit, g.M, g.N, g.C, g.ldc);
+    } else {
+      hipLaunchKernelGGL(gemm2::gemm_big_kernel<EPI>, dim3(tiles), dim3(gemm2::THREADS), gemm2::LDS, st, g, 1, part);
+    }
+  } else {
+    const dim3 grid((unsigned)(g.N / gemm::BN), (unsigned)(g.M / gemm::BM));
+    hipLaunchKernelGGL(gemm::gemm_tn_kernel<EPI>, grid, dim3(256), gemm::lds_bytes<EPI>(), st, g);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace ttt
 
 using namespace ttt;
@@ -194,12 +467,23 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
   if (q.wdown_batch_stride != 0 && q.wdown_batch_stride != nW) return TTT_ERR_SHAPE;
   if (q.B > 0 && !W_down) return TTT_ERR_ARG;
   if (q.B > 0 && q.N > 0 && (!Hs || !W_gate || !W_up || !Vbar || !O)) return TTT_ERR_ARG;
+  // GEMM shapes of one chunk: Z [C x d_H] (K d), apply [C x d] (K d_H), update [d x d_H] (K C)
+  gemm::Args za{}, aa{}, ua{};
+  za.M = q.chunk, za.N = q.d_hidden, za.K = q.d_model;
+  aa.M = q.chunk, aa.N = q.d_model, aa.K = q.d_hidden;
+  ua.M = q.d_model, ua.N = q.d_hidden, ua.K = q.chunk;
+  const int ks_apply =
+      gemm2::fits<EPI_STORE>(aa)
+          ? gemm2::choose_ksplit(aa, (aa.M / gemm2::BM) * (aa.N / gemm2::tile_n<EPI_STORE>()))
+          : 1;
   WorkspacePlan plan;
   const size_t oWf = plan.add(W_down_out ? 0 : (size_t)nW * 4);
+  const size_t oPart = plan.add(ks_apply > 1 ? (size_t)ks_apply * q.chunk * q.d_model * 4 : 0);
   const size_t oSh = plan.add((size_t)nW * 2);
   const size_t oVt = plan.add((size_t)q.d_model * q.N * 2);
-  const size_t oZ = plan.add((size_t)q.chunk * q.d_hidden * 2);
-  const size_t oZt = plan.add((size_t)q.chunk * q.d_hidden * 2);
+  // Z and Z^T double-buffered: chunk i + 1's Z is produced while chunk i is applied and written
+  const size_t oZ = plan.add((size_t)2 * q.chunk * q.d_hidden * 2);
+  const size_t oZt = plan.add((size_t)2 * q.chunk * q.d_hidden * 2);
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -209,19 +493,34 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
   char* ws = static_cast<char*>(workspace);
   __bf16* Wsh = reinterpret_cast<__bf16*>(ws + oSh);
   __bf16* Vt = reinterpret_cast<__bf16*>(ws + oVt);
-  __bf16* Z = reinterpret_cast<__bf16*>(ws + oZ);
-  __bf16* Zt = reinterpret_cast<__bf16*>(ws + oZt);
+  __bf16* Zb[2] = {reinterpret_cast<__bf16*>(ws + oZ), reinterpret_cast<__bf16*>(ws + oZ) + (int64_t)q.chunk * q.d_hidden};
+  __bf16* Ztb[2] = {reinterpret_cast<__bf16*>(ws + oZt),
+                    reinterpret_cast<__bf16*>(ws + oZt) + (int64_t)q.chunk * q.d_hidden};
   static const hipError_t lds_ok = [] {
     hipError_t e = allow_lds(gemm_tn_kernel<EPI_SWIGLU>, lds_bytes<EPI_SWIGLU>());
     if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_STORE>, lds_bytes<EPI_STORE>());
     if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_RMW>, lds_bytes<EPI_RMW>());
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_RMW>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, gemm2::LDS);
     return e;
   }();
+  float* part = reinterpret_cast<float*>(ws + oPart);
   TTT_HIP(lds_ok);
   const __bf16* Hb = static_cast<const __bf16*>(Hs);
   const __bf16* Vb = static_cast<const __bf16*>(Vbar);
   __bf16* Ob = static_cast<__bf16*>(O);
   const int nch = q.N / q.chunk;
+  // Z depends only on the inputs and W_gate / W_up, so it runs on a helper stream: Z of chunk i
+  // into buffer i % 2 after the chunk that last read that buffer was written (event zfree), and
+  // the caller's stream waits for it (event zdone) before the chunk's apply.
+  InplaceStreams* hs = nullptr;
+  TTT_HIP(inplace_streams(&hs));
+  hipStream_t zs = hs->zs;
+  TTT_HIP(hipEventRecord(hs->start, st));
+  TTT_HIP(hipStreamWaitEvent(zs, hs->start, 0));
+  bool freed[2] = {false, false};
   for (int b = 0; b < q.B; ++b) {
     float* Wf = W_down_out ? W_down_out + (int64_t)b * nW : reinterpret_cast<float*>(ws + oWf);
     TTT_HIP(hipMemcpyAsync(Wf, W_down + (int64_t)b * q.wdown_batch_stride, (size_t)nW * 4,
@@ -237,6 +536,9 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
     }
     for (int i = 0; i < nch; ++i) {
       const int64_t t0 = (int64_t)i * q.chunk;
+      const int zb = i & 1;
+      __bf16* Z = Zb[zb];
+      __bf16* Zt = Ztb[zb];
       Args z{};
       z.A = Hb + ((int64_t)b * q.N + t0) * q.d_model;
       z.lda = q.d_model;
@@ -250,12 +552,13 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       z.ldc = q.d_hidden;
       z.Ct = Zt;
       z.ldct = q.chunk;
+      if (freed[zb]) TTT_HIP(hipStreamWaitEvent(zs, hs->zfree[zb], 0));
       {
-        LaunchTimer lt(K_INP_Z, st);
-        hipLaunchKernelGGL(gemm_tn_kernel<EPI_SWIGLU>, dim3(q.d_hidden / BN, q.chunk / BM), dim3(256),
-                           lds_bytes<EPI_SWIGLU>(), st, z);
-        TTT_HIP(hipGetLastError());
+        LaunchTimer lt(K_INP_Z, zs);
+        TTT_HIP(run_gemm<EPI_SWIGLU>(z, 1, part, zs));
       }
+      TTT_HIP(hipEventRecord(hs->zdone[zb], zs));
+      TTT_HIP(hipStreamWaitEvent(st, hs->zdone[zb], 0));
       Args a{};
       a.A = Z;
       a.lda = q.d_hidden;
@@ -268,9 +571,7 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       a.ldc = q.d_model;
       {
         LaunchTimer lt(K_INP_APPLY, st);
-        hipLaunchKernelGGL(gemm_tn_kernel<EPI_STORE>, dim3(q.d_model / BN, q.chunk / BM), dim3(256),
-                           lds_bytes<EPI_STORE>(), st, a);
-        TTT_HIP(hipGetLastError());
+        TTT_HIP(run_gemm<EPI_STORE>(a, ks_apply, part, st));
       }
       Args u{};
       u.A = Vt + t0;
@@ -286,10 +587,10 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       u.alpha = q.eta;
       {
         LaunchTimer lt(K_INP_UPDATE, st);
-        hipLaunchKernelGGL(gemm_tn_kernel<EPI_RMW>, dim3(q.d_hidden / BN, q.d_model / BM), dim3(256),
-                           lds_bytes<EPI_RMW>(), st, u);
-        TTT_HIP(hipGetLastError());
+        TTT_HIP(run_gemm<EPI_RMW>(u, 1, part, st));
       }
+      TTT_HIP(hipEventRecord(hs->zfree[zb], st));
+      freed[zb] = true;
     }
   }
   return TTT_OK;
