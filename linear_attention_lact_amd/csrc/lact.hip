@@ -361,11 +361,24 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
     if (!W0 || !W1 || !W2) return TTT_ERR_ARG;
     if (have_tokens && (!Q || !K || !V || !eta || !O)) return TTT_ERR_ARG;
   }
-  // segments of the token contraction: enough workgroups to cover the chip twice
+  // segments of the token contraction. The gradient kernels hold one workgroup per CU, so the
+  // grid runs in rounds of 256: take the fewest segments whose grid fills its rounds to >= 97 %
+  // (else the best filling up to 64 segments); a grid that already covers the chip keeps one.
   const int ntile = (q.chunk_kv + TT - 1) / TT;
-  const int wg_target = (bf16 ? q.h <= 128 : true) ? 256 : 512;  // register-direct kernel: 1 per CU
-  int S = (wg_target + (rh / RB) * std::max(P, 1) - 1) / ((rh / RB) * std::max(P, 1));
-  S = std::max(1, std::min(S, ntile));
+  const int per_seg = (rh / RB) * std::max(P, 1);
+  int S = 1;
+  if (per_seg < 256) {
+    double best = 0.0;
+    for (int s = 1; s <= std::min(ntile, 64); ++s) {
+      const int64_t tot = (int64_t)per_seg * s, rounds = (tot + 255) / 256;
+      const double fill = (double)tot / (double)(256 * rounds);
+      if (fill > best + 1e-9) {
+        best = fill;
+        S = s;
+      }
+      if (fill >= 0.97) break;
+    }
+  }
   const size_t opsz = bf16 ? 2 : 4;
   WorkspacePlan plan;
   const size_t oW = plan.add((size_t)P * 3 * n * 4);
