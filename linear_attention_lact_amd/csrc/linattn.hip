@@ -186,10 +186,17 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
   fa.nch = nch;
   fa.inclusive = p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0;
   fa.w_batch_stride = p.w_batch_stride;
+  // chunks per workgroup: the workgroups hold one CU each (LDS), so groups of G chunks bring the
+  // grid down to one round of 256 where the chunk splits into whole query passes
+  constexpr int PASS = FusedLayout<OpT, H, RH>::NW * 32;
+  int G = 1;
+  while (G < 8 && (int64_t)8 * ((P + 7) / 8) * (nch / G) > 256 && nch % (2 * G) == 0 && p.chunk % PASS == 0)
+    G *= 2;
+  fa.group = G;
   LaunchTimer lt(K_LIN_FUSED, st);
   hipLaunchKernelGGL(linattn_fused_reset, dim3(1), dim3(256), 0, st, fa.tickets, fa.flags, P * nch);
   TTT_HIP(hipGetLastError());
-  const unsigned grid = 8u * (unsigned)((P + 7) / 8) * (unsigned)nch;
+  const unsigned grid = 8u * (unsigned)((P + 7) / 8) * (unsigned)(nch / G);
   hipLaunchKernelGGL(fk, dim3(grid), dim3(FusedLayout<OpT, H, RH>::NT), lds, st, fa);
   TTT_HIP(hipGetLastError());
   return TTT_OK;

@@ -5,7 +5,9 @@
 // Linear attention" and Theorem 5.2 under "Method step details"; press article, section 4):
 //   dS_c = phi(K_c)^T diag(eta_c) V_c,   S_c = W1 + sum_{j<c} dS_j (apply-then-update; j <= c for
 //   update-then-apply),   O_c = phi(Q_c) S_c.
-// One launch, one workgroup per (pair, chunk c):
+// One launch, one workgroup per (pair, group of G consecutive chunks); a group behaves as one
+// chunk of G*chunk tokens for the scan (its aggregate is the sum of its chunks' aggregates, added
+// in chunk order) while each chunk's queries still read their own state:
 //   A. the chunk aggregate dS_c from K_c, V_c, eta_c (hidden-row ownership: wave (jb, th) holds
 //      W0^T / W2^T rows jb*32.. as MFMA fragments and sums its token half; halves combined in a
 //      fixed order), published to L2 with a flag;
@@ -44,6 +46,7 @@ struct FusedArgs {
   unsigned* flags;          // [pair][nch]: 1 aggregate published, 2 inclusive prefix published
   unsigned* tickets;        // [8] per-XCD work counters, then the error word at [8]
   int P, heads, N, chunk, nch, inclusive;
+  int group;                // chunks per workgroup G (nch % G == 0; G > 1 needs chunk % (NW*32) == 0)
   int64_t w_batch_stride;
 };
 
@@ -91,7 +94,7 @@ struct FusedLayout {
 template <class OpT, int H, int RH>
 constexpr int linattn_fused_lds_bytes() { return FusedLayout<OpT, H, RH>::bytes; }
 
-// grid: 8 * ceil(P / 8) * nch workgroups; block NT = 128 * RH / 32 threads.
+// grid: 8 * ceil(P / 8) * (nch / G) workgroups; block NT = 128 * RH / 32 threads.
 template <class IoT, class OpT, int H, int RH>
 __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArgs a) {
   typedef Mfma<OpT> M;
@@ -128,10 +131,11 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   }
   __syncthreads();
   const int ticket = ctl[0], xcd = ctl[1];
-  const int pair = xcd + 8 * (ticket / a.nch), ch = ticket % a.nch;
+  const int G = a.group, ngr = a.nch / G;
+  const int pair = xcd + 8 * (ticket / ngr), ch = ticket % ngr;  // ch: the group's index
   if (pair >= a.P) return;
   const int64_t n = (int64_t)RH * H;
-  const int cbase = ch * a.chunk, cend = cbase + a.chunk;
+  const int cbase = ch * G * a.chunk, cend = cbase + G * a.chunk;  // the group's tokens
   const int b = pair / a.heads, head = pair % a.heads;
   const float* W0p = a.W0 + (int64_t)b * a.w_batch_stride + (int64_t)head * n;  // [h][rh]
   const float* W2p = a.W2 + (int64_t)b * a.w_batch_stride + (int64_t)head * n;
@@ -144,13 +148,14 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   float* aggp = a.agg + (int64_t)pair * a.nch * n;
   float* inclp = a.incl + (int64_t)pair * a.nch * n;
 
-  // ---- token-tile staging of K, V, eta (rows past the chunk end are zero); two register sets
-  // alternate, so a tile is requested two tiles before it is stored to LDS ----
+  // ---- token-tile staging of K, V, eta (rows past the chunk end are zero); NPF register sets
+  // rotate, so a tile is requested NPF tiles before it is stored to LDS ----
   struct Staged {
     u32x4 k[CPT], v[CPT];
     float e;
   };
-  Staged sa, sb;
+  constexpr int NPF = 4;
+  Staged sg4[NPF];
   auto fetch = [&](int t0, Staged& sg) {
     u32x4* sk = sg.k;
     u32x4* sv = sg.v;
@@ -181,9 +186,9 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
     if (tid < TT) eta_s[buf * TT + tid] = sg.e;
   };
 
-  const int ntile = (a.chunk + TT - 1) / TT;
-  fetch(cbase, sa);
-  fetch(cbase + TT, sb);
+  const int ntile = (G * a.chunk + TT - 1) / TT;
+#pragma unroll
+  for (int k = 0; k < NPF; ++k) fetch(cbase + k * TT, sg4[k]);
 
   // ---- fast-weight fragments of hidden rows jb*32 + (lane & 31): MFMA B operands in phase A,
   // A operands in phase C (same lane layout); W0^T / W2^T also go to LDS for phase C ----
@@ -216,7 +221,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   auto tile_step = [&](int i, Staged& sg) {
     __syncthreads();  // the buffer written next is no longer read
     put(i & 1, sg);
-    fetch(cbase + (i + 2) * TT, sg);
+    fetch(cbase + (i + NPF) * TT, sg);
     __syncthreads();
     const OpT* kb = tiles + (i & 1) * 2 * TILE;
     const OpT* vb = kb + TILE;
@@ -244,26 +249,56 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
       for (int c = 0; c < CB; ++c) acc[c] = M::mma(af, acc_kfrag_tr<OpT>(vh + c * 32, LDK, q, lane), acc[c]);
     }
   };
-  for (int i = 0; i < ntile; i += 2) {
-    tile_step(i, sa);
-    if (i + 1 < ntile) tile_step(i + 1, sb);
-  }
-  // token halves: wave (jb, 1) hands its sums to wave (jb, 0); publish the aggregate
-  __syncthreads();
-  if (th == 1) {
+  // token halves: wave (jb, 1) hands its sums to wave (jb, 0), which adds them in a fixed order.
+  // Chunk i of the group: aggregate to slot ch*G + i for i < G-1; the group's sum (the chunks'
+  // aggregates added in order) to slot ch*G + G-1. The combine area overlays the token tiles, whose
+  // buffers are both free between the chunk's last step and the next step's store.
+  f32x16 tot[CB];
+  auto combine = [&](int i) {
+    __syncthreads();
+    if (th == 1) {
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
+      for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) comb[((jb * CB + c) * 16 + r) * 64 + lane] = acc[c][r];
+        for (int r = 0; r < 16; ++r) comb[((jb * CB + c) * 16 + r) * 64 + lane] = acc[c][r];
+    }
+    __syncthreads();
+    if (th == 0) {
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = acc[c][r] + comb[((jb * CB + c) * 16 + r) * 64 + lane];
+          tot[c][r] = i == 0 ? v : tot[c][r] + v;
+          acc[c][r] = v;
+        }
+      if (i < G - 1) {
+        float* ag = aggp + ((int64_t)ch * G + i) * n + (int64_t)jb * 32 * H;
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ag[acc_row(r, lane) * H + c * 32 + acc_col(lane)] = acc[c][r];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) zero(acc[c]);
+  };
+  const int tpc = a.chunk / TT;  // tiles per chunk (G > 1: whole tiles)
+  for (int i = 0; i < ntile; i += NPF) {
+#pragma unroll
+    for (int k = 0; k < NPF; ++k)
+      if (i + k < ntile) {
+        tile_step(i + k, sg4[k]);
+        if (G > 1 && (i + k + 1) % tpc == 0 && i + k + 1 < ntile) combine((i + k) / tpc);
+      }
   }
-  __syncthreads();
+  combine(G - 1);
   if (th == 0) {
-    float* ag = aggp + (int64_t)ch * n + (int64_t)jb * 32 * H;
+    float* ag = aggp + ((int64_t)ch * G + G - 1) * n + (int64_t)jb * 32 * H;
 #pragma unroll
     for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ag[acc_row(r, lane) * H + c * 32 + acc_col(lane)] = acc[c][r] + comb[((jb * CB + c) * 16 + r) * 64 + lane];
+      for (int r = 0; r < 16; ++r) ag[acc_row(r, lane) * H + c * 32 + acc_col(lane)] = tot[c][r];
   }
   drain_stores();
   __syncthreads();
@@ -282,36 +317,46 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   };
   load_q(cbase, qa);
 
-  // ---- B. decoupled lookback ----
-  if (tid == 0) {
+  // ---- B. decoupled lookback: wave 0 reads the flags of up to 64 predecessors at once (lane l:
+  // chunk base - l); the nearest inclusive prefix ends the walk, a zero flag (aggregate not yet
+  // published) is polled again, within a bounded number of polls ----
+  if (w == 0) {
     int stop = -1, bad = 0;
-    for (int j = ch - 1; j >= 0; --j) {
-      unsigned f;
-      long spins = 0;
-      while ((f = flag_load(fl + j)) == 0u) {
-        if (++spins > FUSED_SPIN_LIMIT) break;
+    long spins = 0;
+    for (int base = ch - 1; base >= 0;) {
+      const int j = base - lane;
+      const unsigned f = j >= 0 ? flag_load(fl + j) : 1u;
+      const unsigned long long inc = __ballot(f == 2u), zero = __ballot(f == 0u);
+      const int first2 = inc ? __builtin_ctzll(inc) : 64;               // nearest inclusive prefix
+      const unsigned long long below = first2 >= 64 ? ~0ull : ((1ull << first2) - 1ull);
+      if (zero & below) {                                              // an aggregate still missing
+        if (++spins > FUSED_SPIN_LIMIT) {
+          bad = 1;
+          break;
+        }
+        continue;
       }
-      if (f == 0u) {
-        bad = 1;
-        __hip_atomic_fetch_add(a.tickets + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (first2 < 64) {
+        stop = base - first2;
         break;
       }
-      if (f == 2u) {
-        stop = j;
-        break;
-      }
+      base -= 64;
     }
-    ctl[1] = stop;
-    ctl[2] = bad;
+    if (lane == 0) {
+      if (bad) __hip_atomic_fetch_add(a.tickets + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ctl[1] = stop;
+      ctl[2] = bad;
+    }
   }
   __syncthreads();
   const int stop = ctl[1];
   const bool bad = ctl[2] != 0;
+  const __amdgpu_buffer_rsrc_t ra = dev_rsrc(aggp, (int)(a.nch * n * 4));
+  const __amdgpu_buffer_rsrc_t ri = dev_rsrc(inclp, (int)(a.nch * n * 4));
+  f32x4 run[SPT], ginc[SPT];  // state before the group's current chunk; the group's inclusive prefix
   {
     // prefix = (inclusive prefix at `stop`, or W1) + aggregates stop+1 .. ch-1, left to right;
-    // loads of four aggregates are in flight together
-    const __amdgpu_buffer_rsrc_t ra = dev_rsrc(aggp, (int)(a.nch * n * 4));
-    const __amdgpu_buffer_rsrc_t ri = dev_rsrc(inclp, (int)(a.nch * n * 4));
+    // loads of eight aggregates are in flight together
     f32x4 s[SPT];
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
@@ -319,17 +364,18 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
       if (NS4 % NT != 0 && e >= 4 * NS4) continue;
       s[i] = stop >= 0 ? dev_load4(ri, (int)((stop * n + e) * 4)) : *reinterpret_cast<const f32x4*>(W1p + e);
     }
-    for (int j0 = stop + 1; j0 < ch; j0 += 4) {
-      f32x4 t[4][SPT];
+    for (int j0 = stop + 1; j0 < ch; j0 += 8) {
+      f32x4 t[8][SPT];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
           const int e = 4 * (tid + NT * i);
-          t[jj][i] = (j0 + jj < ch) ? dev_load4(ra, (int)(((j0 + jj) * n + e) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+          t[jj][i] = (j0 + jj < ch) ? dev_load4(ra, (int)((((j0 + jj) * G + G - 1) * n + e) * 4))
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 8; ++jj)
         if (j0 + jj < ch)
 #pragma unroll
           for (int i = 0; i < SPT; ++i) s[i] += t[jj][i];
@@ -338,13 +384,11 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
     for (int i = 0; i < SPT; ++i) {
       const int e = 4 * (tid + NT * i);
       if (NS4 % NT != 0 && e >= 4 * NS4) continue;
-      const f32x4 inc = s[i] + dev_load4(ra, (int)((ch * n + e) * 4));
+      const f32x4 inc = s[i] + dev_load4(ra, (int)(((ch * G + G - 1) * n + e) * 4));
       *reinterpret_cast<f32x4*>(inclp + (int64_t)ch * n + e) = inc;
-      if (ch == a.nch - 1 && a.S_out) *reinterpret_cast<f32x4*>(a.S_out + (int64_t)pair * n + e) = inc;
-      const f32x4 sc = a.inclusive ? inc : s[i];  // the state this chunk's queries read
-      const int j = e / H, c = e % H;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) Ss[j * LD1 + c + q] = M::from_f32(sc[q]);
+      if (ch == ngr - 1 && a.S_out) *reinterpret_cast<f32x4*>(a.S_out + (int64_t)pair * n + e) = inc;
+      run[i] = s[i];
+      ginc[i] = inc;
     }
   }
   drain_stores();
@@ -353,10 +397,11 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 
   // ---- C. O = phi(Q) S for the chunk's query tokens, wave w: 32 tokens per pass ----
   const float poison = bad ? __builtin_nanf("") : 0.f;
+  int oend = cend;  // end of the chunk whose outputs are written
   auto pass = [&](int t0, const u32x4 (&qcur)[KS], u32x4 (&qnext)[KS]) {
     load_q(t0 + NW * 32, qnext);
     const int tw = t0 + 32 * w;
-    if (tw < cend) {
+    if (tw < oend) {
       frag qf[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = bf16x8_to_f16x8(qcur[s]);
@@ -399,7 +444,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 #pragma unroll
         for (int i = lane; i < 32 * H / 8; i += 64) {
           const int row = i / (H / 8), col = (i % (H / 8)) * 8;
-          if (tw + row < cend)
+          if (tw + row < oend)
             *reinterpret_cast<u32x4*>(Op + (int64_t)(tw + row) * H + col) =
                 *reinterpret_cast<const u32x4*>(os + row * (H + 8) + col);
         }
@@ -410,14 +455,36 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int tt = tw + acc_row(r, lane);
-            if (tt < cend) Io<IoT>::store(Op + (int64_t)tt * H + c * 32 + acc_col(lane), o[c][r] + poison);
+            if (tt < oend) Io<IoT>::store(Op + (int64_t)tt * H + c * 32 + acc_col(lane), o[c][r] + poison);
           }
       }
     }
   };
-  for (int t0 = cbase; t0 < cend; t0 += 2 * NW * 32) {
-    pass(t0, qa, qb);
-    if (t0 + NW * 32 < cend) pass(t0 + NW * 32, qb, qa);
+  // chunk i of the group reads S = run (+ its own aggregate when inclusive); run then advances by
+  // the chunk's aggregate (the last chunk's inclusive state is the group's inclusive prefix)
+  int np = 0;  // passes so far: even passes read qa and prefetch into qb, odd ones the reverse
+  for (int i = 0; i < G; ++i) {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int e = 4 * (tid + NT * k);
+      if (NS4 % NT != 0 && e >= 4 * NS4) continue;
+      const f32x4 nxt = i == G - 1 ? ginc[k] : run[k] + dev_load4(ra, (int)(((ch * G + i) * n + e) * 4));
+      const f32x4 sc = a.inclusive ? nxt : run[k];
+      const int j = e / H, c = e % H;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Ss[j * LD1 + c + q] = M::from_f32(sc[q]);
+      run[k] = nxt;
+    }
+    __syncthreads();  // S of chunk i in LDS
+    const int c0 = cbase + i * a.chunk;
+    oend = c0 + a.chunk;
+    for (int t0 = c0; t0 < oend; t0 += NW * 32, ++np) {
+      if (np & 1)
+        pass(t0, qb, qa);
+      else
+        pass(t0, qa, qb);
+    }
+    __syncthreads();  // every wave is done with S before the next chunk's is stored
   }
 }
 

@@ -69,6 +69,23 @@ def test_config1_full_size(lib):
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
+@pytest.mark.parametrize("order", [0, 1])
+def test_grouped_chunks_many_pairs(lib, order):
+    """64 sequence-head pairs x 16 chunks: the single-pass kernel handles four chunks per
+    workgroup (one round of workgroups); both orders, sampled pairs against the oracle."""
+    p = LactProblem(B=8, H=8, h=64, r=2, Nq=4096, Nk=4096, chunk_q=256, chunk_kv=256, dtype=BF16,
+                    update_mask=UPD_W1, weight_norm=False, order=order)
+    announce(f"linattn grouped chunks B8 H8 N4096 chunk256 order={order}")
+    x = make_lact_inputs(p, 400 + order)
+    O, S = _lin_gpu(lib, p, x)
+    pairs = [(0, 0), (3, 5), (7, 7)]
+    ref = _lin_ref(p, x, pairs=pairs)
+    sel = lambda a: np.stack([a[b, h] for b, h in pairs])
+    eo, es = max_abs_rel(sel(host(O)), sel(ref["O"])), max_abs_rel(sel(host(S)), sel(ref["S"]))
+    print(f"grouped order={order} O={eo:.2e} S={es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
 def test_recurrent_layer_equals_scan_on_gpu(lib):
     """Theorem 5.2 on the device: the LaCT layer writing only W1, without renormalisation,
     momentum or Muon, gives the scan form's outputs."""
