@@ -100,6 +100,16 @@ struct TileStage {
       *reinterpret_cast<u32x4*>(dst) = raw;
     }
   }
+  template <class TL>
+  __device__ __forceinline__ void store_at(OpT* Ks, OpT* Vs, int tid) const {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int ch = tid + 256 * q;
+      const int row = ch / (H / VE), col = (ch % (H / VE)) * VE;
+      put(k[q], Ks + TL::at(row, col));
+      put(v[q], Vs + TL::at(row, col));
+    }
+  }
   __device__ __forceinline__ void store(OpT* Ks, OpT* Vs, int ld, int tid) const {
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
@@ -110,6 +120,45 @@ struct TileStage {
     }
   }
 };
+
+// Token-tile layout of the register-direct kernels. With 16-bit operands and h = 128 the rows
+// carry no padding and the 16-byte chunk c of row r sits at position c ^ (4 (r % 4) + (r / 4) % 2):
+// the MFMA row reads (8 consecutive rows of one chunk), the transpose reads (4 rows x 32
+// columns) and the 16-byte staging writes then each touch distinct LDS banks. Other shapes pad
+// the rows by 16 bytes.
+template <class OpT, int H>
+struct TileLayout {
+  static constexpr bool SWZ = sizeof(OpT) == 2 && H == 128;
+  static constexpr int LD = SWZ ? H : H + Pad<OpT>::v;
+  __device__ __forceinline__ static int at(int r, int c) {
+    if constexpr (SWZ)
+      return r * LD + (((c >> 3) ^ (4 * (r & 3) + ((r >> 2) & 1))) << 3) + (c & 7);
+    else
+      return r * LD + c;
+  }
+};
+
+// Transpose-read operand (see acc_kfrag_tr) from a tile in TileLayout: rows row0.. (tokens),
+// columns col0.. .
+template <class TL, class T>
+__device__ __forceinline__ typename Mfma<T>::frag tile_kfrag_tr(const T* tile, int row0, int col0, int q, int lane) {
+  if constexpr (!TL::SWZ) {
+    return acc_kfrag_tr<T>(tile + row0 * TL::LD + col0, TL::LD, q, lane);
+  } else {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4;
+    const int g = lane >> 4, s = lane & 15;
+    const int row = row0 + 16 * q + 4 * (g >> 1) + (s >> 2);
+    const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+    v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4*)((__attribute__((address_space(3))) T*)(tile + TL::at(row, col))));
+    v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4*)((__attribute__((address_space(3))) T*)(tile + TL::at(row + 8, col))));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    v8i16 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(typename Mfma<T>::frag, v);
+  }
+}
 
 // LDS bytes of grad_kernel<OpT, H, LINATTN>.
 template <class OpT, int H, bool LINATTN>
@@ -288,7 +337,8 @@ constexpr int grad_rd_lds_bytes() {
   constexpr int NMAT = LINATTN ? 1 : 3;
   constexpr int QS = 32 / Mfma<OpT>::KSTEP;
   constexpr int FRAG = (int)sizeof(typename Mfma<OpT>::frag);
-  return 4 * TT * (H + P) * (int)sizeof(OpT) + (2 * TT + 16) * 4 + NWAVE * NMAT * QS * 64 * FRAG;
+  (void)P;
+  return 4 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + (2 * TT + 16) * 4 + NWAVE * NMAT * QS * 64 * FRAG;
 }
 
 // sigmoid through the hardware exp2 and reciprocal (about 1 ulp each; the results feed 16-bit
@@ -303,7 +353,8 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
   constexpr int P = Pad<OpT>::v;
-  constexpr int LDK = H + P;
+  typedef TileLayout<OpT, H> TL;
+  constexpr int LDK = TL::LD;
   constexpr int TILE = TT * LDK;            // elements of one staged tensor tile
   constexpr int CB = H / 32;
   constexpr int CH = (CB + 1) / 2;          // output column blocks per wave
@@ -367,7 +418,7 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
   }
   auto put = [&](int i) {
     OpT* b = tiles + (i & 1) * 2 * TILE;
-    stage.store(b, b + TILE, LDK, tid);
+    stage.template store_at<TL>(b, b + TILE, tid);
     if (tid < TT) eta_s[(i & 1) * TT + tid] = ev * scale;
   };
 
@@ -382,17 +433,16 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
   // Fp[0] <- eta*H, Fp[1] <- X0, Fp[2] <- X2
   auto fwd_epi = [&](const OpT* b, f32x16 (&F)[3], f32x16 (&Fp)[3], const float* ebuf, auto EPI) {
     constexpr bool DO_EPI = decltype(EPI)::value;
-    const OpT* kr = b + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
-    const OpT* vr = kr + TILE;
+    const int kro = th * 32 + (lane & 31), kco = (lane >> 5) * M::KSUB;
     const float* er = ebuf + th * 32 + 4 * (lane >> 5);
 #pragma unroll
     for (int m = 0; m < 3; ++m) zero(F[m]);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const auto kf = M::load(kr + s * M::KSTEP);
+      const auto kf = M::load(b + TL::at(kro, kco + s * M::KSTEP));
       F[0] = M::mma(kf, wf[0][s], F[0]);
       F[1] = M::mma(kf, wf[1][s], F[1]);
-      if constexpr (!LINATTN) F[2] = M::mma(M::load(vr + s * M::KSTEP), wf[2][s], F[2]);
+      if constexpr (!LINATTN) F[2] = M::mma(M::load(b + TILE + TL::at(kro, kco + s * M::KSTEP)), wf[2][s], F[2]);
       if constexpr (DO_EPI) {
 #pragma unroll
         for (int r = 16 * s / KS; r < 16 * (s + 1) / KS; ++r) {
@@ -426,8 +476,7 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
     const frag* pf = xch + (size_t)(w ^ 2) * NMAT * QS * 64 + lane;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const OpT* kb = b + (half == 0 ? th : 1 - th) * 32 * LDK;
-      const OpT* vb = kb + TILE;
+      const int hrow = (half == 0 ? th : 1 - th) * 32;  // token rows of this half
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
         frag am[NMAT];
@@ -438,9 +487,9 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
           const int c = cb0 + cc;
           if (CB % 2 == 0 || c < CB) {
             // am[0] = eta H (with V) -> P1; am[1] = X0 (with K) -> P0; am[2] = X2 (with K) -> P2
-            acc[0][cc] = M::mma(am[0], acc_kfrag_tr<OpT>(vb + c * 32, LDK, q, lane), acc[0][cc]);
+            acc[0][cc] = M::mma(am[0], tile_kfrag_tr<TL>(b + TILE, hrow, c * 32, q, lane), acc[0][cc]);
             if constexpr (!LINATTN) {
-              const auto bk = acc_kfrag_tr<OpT>(kb + c * 32, LDK, q, lane);
+              const auto bk = tile_kfrag_tr<TL>(b, hrow, c * 32, q, lane);
               acc[1][cc] = M::mma(am[1], bk, acc[1][cc]);
               acc[2][cc] = M::mma(am[2], bk, acc[2][cc]);
             }
