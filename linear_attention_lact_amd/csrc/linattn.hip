@@ -193,9 +193,12 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
   while (G < 8 && (int64_t)8 * ((P + 7) / 8) * (nch / G) > 256 && nch % (2 * G) == 0 && p.chunk % PASS == 0)
     G *= 2;
   fa.group = G;
+  {
+    LaunchTimer lt(K_LIN_PREP, st);
+    hipLaunchKernelGGL(linattn_fused_reset, dim3(1), dim3(256), 0, st, fa.tickets, fa.flags, P * nch);
+    TTT_HIP(hipGetLastError());
+  }
   LaunchTimer lt(K_LIN_FUSED, st);
-  hipLaunchKernelGGL(linattn_fused_reset, dim3(1), dim3(256), 0, st, fa.tickets, fa.flags, P * nch);
-  TTT_HIP(hipGetLastError());
   const unsigned grid = 8u * (unsigned)((P + 7) / 8) * (unsigned)(nch / G);
   hipLaunchKernelGGL(fk, dim3(grid), dim3(FusedLayout<OpT, H, RH>::NT), lds, st, fa);
   TTT_HIP(hipGetLastError());
