@@ -225,7 +225,7 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
   float ss = 0.f;
   {
     const int64_t seg_stride = (int64_t)s.P * 3 * n;
-    constexpr int NB8 = NG < 8 ? NG : 8;
+    constexpr int NB8 = NG < 16 ? NG : 16;
 #pragma unroll 1
     for (int b0 = 0; b0 < NG; b0 += NB8) {
       f32x4 g[NB8], mv[NB8];
