@@ -109,7 +109,40 @@ __device__ __forceinline__ void tu_partial(TuLds& L, const float* a, int lda, co
   const int k0 = (w * nk / 4) * 16, k1 = ((w + 1) * nk / 4) * 16;
   f32x16 acc;
   zero(acc);
-  mma_tile_split(acc, a + k0, lda, b + k0, ldb, k1 - k0, lane);
+  // operands of up to four K steps requested together (they come from L2), then split and used
+  const float* ap = a + (lane & 31) * lda + (lane >> 5) * 8;
+  const float* bp = b + (lane & 31) * ldb + (lane >> 5) * 8;
+  for (int kb = k0; kb < k1; kb += 64) {
+    f32x4 av[4][2], bv[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = kb + 16 * j;
+      if (k < k1) {
+        av[j][0] = *reinterpret_cast<const f32x4*>(ap + k);
+        av[j][1] = *reinterpret_cast<const f32x4*>(ap + k + 4);
+        bv[j][0] = *reinterpret_cast<const f32x4*>(bp + k);
+        bv[j][1] = *reinterpret_cast<const f32x4*>(bp + k + 4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kb + 16 * j < k1) {
+        bf16x8 ah, al, bh, bl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = av[j][e >> 2][e & 3], y = bv[j][e >> 2][e & 3];
+          const __bf16 xh = static_cast<__bf16>(x), yh = static_cast<__bf16>(y);
+          ah[e] = xh;
+          al[e] = static_cast<__bf16>(x - static_cast<float>(xh));
+          bh[e] = yh;
+          bl[e] = static_cast<__bf16>(y - static_cast<float>(yh));
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) L.part[w][acc_row(r, lane)][acc_col(lane)] = acc[r];
   __syncthreads();
