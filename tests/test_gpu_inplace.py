@@ -21,6 +21,8 @@ def _gpu(lib, p, x):
     dict(B=2, N=512, d_model=256, d_hidden=512, chunk=128, eta=1e-3),
     dict(B=1, N=1024, d_model=512, d_hidden=768, chunk=256, eta=1e-2),
     dict(B=1, N=256, d_model=256, d_hidden=256, chunk=256, eta=1e-3),
+    # apply product 256 x 512 over K = 2048: the large-tile kernel with a four-way K split
+    dict(B=1, N=512, d_model=512, d_hidden=2048, chunk=256, eta=1e-3),
 ])
 def test_small_cases(lib, kw):
     from oracle import inplace as IP
