@@ -367,6 +367,102 @@ inline int choose_ksplit(const Args& g, int tiles) {
   }
   return best;
 }
+
+// W_down update with two workgroups per CU: 256 x 128 output tiles, 4 waves of 128 x 64, one LDS
+// stage of 48 KB (so two workgroups fit), K in blocks of 64. Each workgroup loads, waits and
+// computes in turn; the other workgroup on the CU fills the MFMA pipe meanwhile, and one
+// workgroup's fp32 read-modify-write epilogue overlaps the other's products.
+constexpr int PP_BN = 128;
+constexpr int PP_LDS = (BM + PP_BN) * ROWB;  // 48 KB
+
+__global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int ntn = g.N / PP_BN;
+  const int m0 = (blockIdx.x / ntn) * BM, n0 = (blockIdx.x % ntn) * PP_BN;
+  const int nkb = g.K / BK;
+  // staging: A rows 64w + 8j (j < 8), B rows 32w + 8j (j < 4); lane l: row + l/8, LDS chunk l%8
+  const int lr = lane >> 3;
+  auto issue = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 64 * w + 8 * j + lr;
+      __builtin_amdgcn_global_load_lds(g.A + (int64_t)(m0 + row) * g.lda + kb * BK + chunk_pos(lane & 7, row) * 8,
+                                       smem + (64 * w + 8 * j) * ROWB, 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 32 * w + 8 * j + lr;
+      __builtin_amdgcn_global_load_lds(g.B0 + (int64_t)(n0 + row) * g.ldb + kb * BK + chunk_pos(lane & 7, row) * 8,
+                                       smem + (BM + 32 * w + 8 * j) * ROWB, 16, 0, 0);
+    }
+  };
+  const int arow = wm * 128 + (lane & 31), brow = BM + wn * 64 + (lane & 31);
+  int coff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) coff[s] = chunk_pos(2 * s + (lane >> 5), lane & 31) * 16;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) zero(acc[i][j]);
+  for (int kb = 0; kb < nkb; ++kb) {
+    issue(kb);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(smem + (arow + 32 * i) * ROWB + coff[s]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(smem + (brow + 32 * j) * ROWB + coff[s]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the stage is reloaded next
+  }
+  // W += alpha * acc through LDS in four passes of 64 rows (16-byte runs of the fp32 state)
+  constexpr int LDE = PP_BN + 4;
+  float* ep = reinterpret_cast<float*>(smem);
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    if (wm == (pass >> 1)) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * (pass & 1) + ii;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            ep[(32 * ii + acc_row(r, lane)) * LDE + wn * 64 + 32 * j + acc_col(lane)] = acc[i][j][r];
+      }
+    }
+    __syncthreads();
+    f32x4 wv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int f = tid + 256 * q, row = f >> 5, c4 = (f & 31) * 4;
+      wv[q] = *reinterpret_cast<const f32x4*>(g.Wf + (int64_t)(m0 + 64 * pass + row) * g.ldw + n0 + c4);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int f = tid + 256 * q, row = f >> 5, c4 = (f & 31) * 4;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ep + row * LDE + c4);
+      const f32x4 v = wv[q] + g.alpha * a;
+      const int64_t idx = (int64_t)(m0 + 64 * pass + row) * g.ldw + n0 + c4;
+      *reinterpret_cast<f32x4*>(g.Wf + idx) = v;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 s4 = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                         static_cast<__bf16>(v[3])};
+      *reinterpret_cast<bf16x4*>(g.Wsh + idx) = s4;
+    }
+    __syncthreads();
+  }
+}
 }  // namespace gemm2
 
 // fp32 -> bf16 shadow copy. grid-stride, 4 elements per thread step.
@@ -427,6 +523,12 @@ static hipError_t inplace_streams(InplaceStreams** out) {
 // EPI_STORE with ksplit > 1 goes through fp32 partials in `part` and the split sum.
 template <int EPI>
 static hipError_t run_gemm(const gemm::Args& g, int ksplit, float* part, hipStream_t st) {
+  if (EPI == gemm::EPI_RMW && g.M % gemm2::BM == 0 && g.N % gemm2::PP_BN == 0 && g.K % gemm2::BK == 0 &&
+      g.K >= gemm2::BK) {
+    const unsigned tiles = (unsigned)((g.M / gemm2::BM) * (g.N / gemm2::PP_BN));
+    hipLaunchKernelGGL(gemm2::gemm_rmw_pp_kernel, dim3(tiles), dim3(256), gemm2::PP_LDS, st, g);
+    return hipGetLastError();
+  }
   if (gemm2::fits<EPI>(g)) {
     const unsigned tiles = (unsigned)((g.M / gemm2::BM) * (g.N / gemm2::tile_n<EPI>()));
     if (EPI == gemm::EPI_STORE && ksplit > 1) {
@@ -503,6 +605,7 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_RMW>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel, gemm2::PP_LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, gemm2::LDS);
     return e;
   }();
