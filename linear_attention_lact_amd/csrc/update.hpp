@@ -20,6 +20,7 @@
 // 3.4445^5; fp32 state, fp32 matrix masters in registers.
 #pragma once
 #include "common.hpp"
+#include "fastweight.hpp"
 
 namespace ttt {
 
@@ -56,14 +57,27 @@ __device__ __forceinline__ void split_store(bf16* hi, bf16* lo, float v) {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// hi / lo bf16 pair of four consecutive values (x = hi + lo to ~2^-16 relative), 8-byte stores
+// hi / lo bf16 pair of four consecutive values (x = hi + lo to ~2^-16 relative), 8-byte stores.
+// hi is the round-to-nearest bf16 pair; its fp32 values come from the bit pattern (a shift and a
+// mask) rather than a second conversion.
+__device__ __forceinline__ void split4(f32x4 v, bf16x4& h, bf16x4& l) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const bf16x2 hp = __builtin_convertvector(f32x2{v[2 * p], v[2 * p + 1]}, bf16x2);
+    const unsigned hb = __builtin_bit_cast(unsigned, hp);
+    const float h0 = __builtin_bit_cast(float, hb << 16), h1 = __builtin_bit_cast(float, hb & 0xffff0000u);
+    const bf16x2 lp = __builtin_convertvector(f32x2{v[2 * p] - h0, v[2 * p + 1] - h1}, bf16x2);
+    h[2 * p] = hp[0];
+    h[2 * p + 1] = hp[1];
+    l[2 * p] = lp[0];
+    l[2 * p + 1] = lp[1];
+  }
+}
 __device__ __forceinline__ void split_store4(bf16* hi, bf16* lo, f32x4 v) {
   bf16x4 h, l;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    h[q] = static_cast<bf16>(v[q]);
-    l[q] = static_cast<bf16>(v[q] - static_cast<float>(h[q]));
-  }
+  split4(v, h, l);
   *reinterpret_cast<bf16x4*>(hi) = h;
   *reinterpret_cast<bf16x4*>(lo) = l;
 }
@@ -151,37 +165,57 @@ __device__ __forceinline__ void mma_blocks(f32x16 (&c)[Q], int w, const bf16* Ah
   }
 }
 
-// Row stride (16-bit elements) of a chunk read with the LDS transpose read: rows 0..3 of a
-// 16-lane group then fall into disjoint 16-bank windows.
-constexpr int gram_ld(int h) {
-  int l = h + 4;
-  while ((l / 2) % 32 != 16) l += 4;
-  return l;
-}
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int H, int RH>
 struct UpdLayout {
-  static constexpr int JC = 64;                // state rows per streamed chunk of X^T
-  static constexpr int NCH = RH / JC;
   static constexpr int LDA = H + 8;            // h x h matrices: bf16 hi / lo [H][LDA]
   static constexpr int SLOT = 2 * H * LDA * 2;
-  static constexpr int LDG = gram_ld(H);       // X^T chunk for the Gram product (transpose reads)
-  static constexpr int LDF = H + 8;            // X^T chunk for the final product (row reads)
-  static constexpr int CHG = 2 * JC * LDG * 2;
-  static constexpr int CHF = 2 * JC * LDF * 2;
-  static constexpr int R = cmax(cmax(2 * SLOT, 2 * CHG), SLOT + 2 * CHF);
-  static constexpr int HB = H / 32, JBC = JC / 32;
-  static constexpr int NF = RH > H ? RH : H;              // renorm factors
-  static constexpr int NP = cmax(HB * RH, JBC * H);       // renorm partial sums
-  static constexpr int bytes = R + (NP + NF + 32) * 4;
+  typedef TileLayout<__bf16, H> GL;            // X_0^T (rows j, h columns) for the Gram product
+  static constexpr int GSZ = RH * GL::LD;      // elements of its hi (and of its lo) array
+  static constexpr int R = cmax(2 * SLOT, 2 * GSZ * 2);
+  static constexpr int HB = H / 32, NJ = RH / 32;
+  static constexpr int NJW = (NJ + 7) / 8;     // state-row blocks per wave in the final product
+  static constexpr int bytes = R + (8 * H + 32) * 4;      // + column-norm partials [8][H], [32]
   static constexpr int NBA = HB * HB, QA = (NBA + 7) / 8;   // h x h blocks per wave
-  static constexpr int NBF = HB * (JC / 32);                // final-product blocks per chunk
-  static_assert(RH % JC == 0 && H % 32 == 0 && NBF <= 8, "shape");
+  static_assert(H % 32 == 0 && RH % 32 == 0 && bytes <= 160 * 1024, "shape");
 };
 
 template <int H, int RH>
 constexpr int update_lds_bytes() { return UpdLayout<H, RH>::bytes; }
+
+// Gram product A_0 = X_0 X_0^T of wave w's blocks t = Q*w + q: block t is (t / HB, t % HB),
+// K runs over all RH state rows of X_0^T (transpose reads of the swizzled rows; both operands
+// take the same permuted K order), split-bf16 with the cross terms in separate registers.
+template <class GL, int RH, int Q, int HB, int NBA>
+__device__ __forceinline__ void gram_blocks(f32x16 (&c)[Q], int w, const bf16* Gh, const bf16* Gl, int lane) {
+  typedef Mfma<bf16> M;
+  f32x16 d[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) zero(d[q]);
+#pragma unroll 2
+  for (int hr = 0; hr < RH / 32; ++hr) {
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int t = Q * w + q;
+        if (t < NBA) {
+          const int ca = 32 * (t / HB), cb = 32 * (t % HB);
+          const bf16x8 ah = tile_kfrag_tr<GL>(Gh, 32 * hr, ca, q2, lane);
+          const bf16x8 al = tile_kfrag_tr<GL>(Gl, 32 * hr, ca, q2, lane);
+          const bf16x8 bh = tile_kfrag_tr<GL>(Gh, 32 * hr, cb, q2, lane);
+          const bf16x8 bl = tile_kfrag_tr<GL>(Gl, 32 * hr, cb, q2, lane);
+          c[q] = M::mma(ah, bh, c[q]);
+          d[q] = M::mma(ah, bl, d[q]);
+          d[q] = M::mma(al, bh, d[q]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) c[q] += d[q];
+}
 
 // grid: 3 * P workgroups (one per matrix); block 512 threads (8 waves).
 // h x h block t = QA*w + q of wave w: rows c = (t / HB)*32 + acc_row, columns
@@ -193,20 +227,19 @@ constexpr int update_lds_bytes() { return UpdLayout<H, RH>::bytes; }
 template <class OpT, int H, int RH>
 __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, unsigned char* smem) {
   typedef UpdLayout<H, RH> L;
-  constexpr int JC = L::JC, NCH = L::NCH, LDA = L::LDA, LDG = L::LDG, LDF = L::LDF;
-  constexpr int HB = L::HB, NBA = L::NBA, QA = L::QA, NBF = L::NBF;
+  typedef typename L::GL GL;
+  constexpr int LDA = L::LDA, HB = L::HB, NBA = L::NBA, QA = L::QA, NJ = L::NJ, NJW = L::NJW;
   constexpr int NE4 = RH * H / 4;              // float4 groups of the matrix
   constexpr int NG = (NE4 + 511) / 512;
-  constexpr int CG4 = JC * H / 4 / 512 > 0 ? JC * H / 4 / 512 : 1;   // float4 groups per chunk per thread
-  static_assert(JC * H / 4 <= 512 * CG4, "chunk map");
+  constexpr int NB8 = NG < 16 ? NG : 16;
+  constexpr bool KEEP = NG <= NB8;             // step 1 holds the whole matrix in registers
   const LactState& s = u.s;
   bf16* S1h = reinterpret_cast<bf16*>(smem);                 // slot 1 [H][LDA] hi, then lo
   bf16* S1l = S1h + H * LDA;
   bf16* S2h = reinterpret_cast<bf16*>(smem + L::SLOT);       // slot 2
   bf16* S2l = S2h + H * LDA;
-  float* npart = reinterpret_cast<float*>(smem + L::R);      // [NP] renorm partial sums
-  float* fac = npart + L::NP;                                // [NF] renorm factors
-  float* red = fac + L::NF;                                  // [32]
+  float* npart = reinterpret_cast<float*>(smem + L::R);      // [8][H] column-norm partials
+  float* red = npart + 8 * H;                                // [32]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (mi >= 3 * s.P) return;
@@ -223,9 +256,9 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
 
   // ---- 1. gradient from the segment partials (in segment order), momentum -------------------
   float ss = 0.f;
+  f32x4 keep[KEEP ? NG : 1];
   {
     const int64_t seg_stride = (int64_t)s.P * 3 * n;
-    constexpr int NB8 = NG < 16 ? NG : 16;
 #pragma unroll 1
     for (int b0 = 0; b0 < NG; b0 += NB8) {
       f32x4 g[NB8], mv[NB8];
@@ -246,9 +279,10 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
 #pragma unroll
       for (int i = 0; i < NB8; ++i) {
         const int e4 = tid + 512 * (b0 + i);
-        if (e4 >= NE4) continue;
         f32x4 v = -g[i];
         if (mom) v = u.momentum * mv[i] + v;
+        if constexpr (KEEP) keep[i] = v;
+        if (e4 >= NE4) continue;
         *reinterpret_cast<f32x4*>(Ud + 4 * e4) = v;
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
       }
@@ -258,33 +292,6 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
   if (u.muon) inv = 1.f / (sqrtf(block_sum(ss, red)) + u.eps_ns);
   __syncthreads();
 
-  // chunk staging: rows ch*JC .. of U (state rows j, h columns) scaled by inv, as X^T hi / lo.
-  // All chunks of the matrix are requested at once (they come from L2: step 1 just wrote them).
-  f32x4 cv[NCH][CG4];
-  auto chunk_load_all = [&]() {
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-      for (int i = 0; i < CG4; ++i) {
-        const int e4 = tid + 512 * i;
-        cv[ch][i] = e4 < JC * H / 4 ? *reinterpret_cast<const f32x4*>(Ud + (int64_t)ch * JC * H + 4 * e4)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-  };
-  auto chunk_store = [&](int ch, bf16* bh, bf16* bl, int ld) {
-#pragma unroll
-    for (int c4 = 0; c4 < NCH; ++c4) {
-      if (c4 != ch) continue;
-#pragma unroll
-      for (int i = 0; i < CG4; ++i) {
-        const int e4 = tid + 512 * i;
-        if (e4 < JC * H / 4) {
-          const int row = (4 * e4) / H, c = (4 * e4) % H;
-          split_store4(bh + row * ld + c, bl + row * ld + c, cv[c4][i] * inv);
-        }
-      }
-    }
-  };
   auto put_sym = [&](const f32x16 (&v)[QA], bf16* dh, bf16* dl) {
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
@@ -324,23 +331,28 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
   // ---- 2. Newton-Schulz-5 through the Gram matrix ----------------------------------------------
   if (u.muon) {
     f32x16 am[QA], pm[QA], qm[QA], t[QA];
-    // (a) A_0 = X_0 X_0^T, X_0^T streamed in chunks of JC state rows (double-buffered)
-    zero_q(am);
+    // (a) X_0^T = U^T / (||U||_F + eps) as split-bf16 rows j in LDS, then A_0 = X_0 X_0^T in one
+    //     pass over all RH rows
     {
-      auto gb = [&](int i) { return reinterpret_cast<bf16*>(smem + (i & 1) * L::CHG); };
-      chunk_load_all();
-      chunk_store(0, gb(0), gb(0) + JC * LDG, LDG);
-      __syncthreads();
+      bf16* Gh = reinterpret_cast<bf16*>(smem);
+      bf16* Gl = Gh + L::GSZ;
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        if (ch + 1 < NCH) {
-          bf16* nb = gb(ch + 1);
-          chunk_store(ch + 1, nb, nb + JC * LDG, LDG);
+      for (int i = 0; i < NG; ++i) {
+        const int e4 = tid + 512 * i;
+        if (NE4 % 512 == 0 || e4 < NE4) {
+          f32x4 v;
+          if constexpr (KEEP)
+            v = keep[i];
+          else
+            v = *reinterpret_cast<const f32x4*>(Ud + 4 * e4);  // this thread's own step-1 writes
+          const int j = (4 * e4) / H, c = (4 * e4) % H;
+          split_store4(Gh + GL::at(j, c), Gl + GL::at(j, c), v * inv);
         }
-        bf16* cb = gb(ch);
-        mma_blocks<JC, QA, HB, NBA, true, true>(am, w, cb, cb + JC * LDG, LDG, cb, cb + JC * LDG, LDG, lane);
-        __syncthreads();
       }
+      __syncthreads();
+      zero_q(am);
+      gram_blocks<GL, RH, QA, HB, NBA>(am, w, Gh, Gl, lane);
+      __syncthreads();
     }
     put_sym(am, S1h, S1l);
     __syncthreads();
@@ -392,137 +404,180 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
     __syncthreads();
   }
 
-  // ---- 3. W - U per chunk, U = (Q X_0)^T with Muon: block C[c][j] = sum_m Q[c][m] X_0^T[j][m] ---
-  // wave w < NBF owns block (c-block w / (JC/32), j-block w % (JC/32)) of every chunk and keeps
-  // the new state of those blocks in registers through the renorm and the writes
-  constexpr int JBC = L::JBC;
-  const bool fact = w < NBF;
-  const int fcb = (w < NBF ? w : 0) / JBC, fjb = (w < NBF ? w : 0) % JBC;
-  auto fcoord = [&](int ch, int g4, int& j, int& c) {
-    c = fcb * 32 + 8 * g4 + 4 * (lane >> 5);
-    j = ch * JC + fjb * 32 + (lane & 31);
-  };
-  f32x16 wn[NCH];
-  if (fact) {  // all of this wave's W entries in flight at once
+  // ---- 3-5. new state: wave w takes the state rows of blocks jb = w, w + 8, ... and keeps every
+  // h column of them in registers through W - U, the renorm and the writes. With Muon the write
+  // is U = (Q X_0)^T, each lane loading its X_0^T row j straight from the step-1 output as
+  // split-bf16 operand fragments (k = m = 16 s + 8 (lane / 32) + e), Q read by rows from slot 1.
+  // Block orientation per matrix, so that the renorm axis lies along the lane's own registers:
+  //   W0T / W2T (norm of row j over its h inputs): blocks C[c][j], a lane holds one j;
+  //   W1 (norm of column c over all rh rows): blocks C[j][c], a lane holds one c.
+  auto finish = [&](auto ROWS_J) {
+    constexpr bool RJ = decltype(ROWS_J)::value;  // accumulator rows are state rows j (W1)
+    constexpr int KS = H / 16;
+    f32x16 wn[NJW][HB];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
+    for (int x = 0; x < NJW; ++x) {
+      const int jb = w + 8 * x;
+      if (jb < NJ) {
+        const int jl = 32 * jb + (lane & 31);
+        if (u.muon) {
+          bf16x8 uh[KS], ul[KS];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        int j, c;
-        fcoord(ch, g4, j, c);
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(W + (int64_t)j * H + c);
+          for (int st = 0; st < KS; ++st) {
+            const float* src = Ud + (int64_t)jl * H + 16 * st + 8 * (lane >> 5);
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src) * inv;
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4) * inv;
+            bf16x4 h0, l0, h1, l1;
+            split4(v0, h0, l0);
+            split4(v1, h1, l1);
+            uh[st] = bf16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+            ul[st] = bf16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+          }
+          f32x16 dd[HB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wn[ch][4 * g4 + i] = wv[i];
-      }
-  }
-  {
-    auto fb = [&](int i) { return reinterpret_cast<bf16*>(smem + L::SLOT + (i & 1) * L::CHF); };
-    if (u.muon) {
-      chunk_load_all();
-      chunk_store(0, fb(0), fb(0) + JC * LDF, LDF);
-      __syncthreads();
-    }
+          for (int cb = 0; cb < HB; ++cb) {
+            zero(wn[x][cb]);
+            zero(dd[cb]);
+          }
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      f32x16 cx[1];
-      zero(cx[0]);
-      if (u.muon) {
-        if (ch + 1 < NCH) {
-          bf16* nb = fb(ch + 1);
-          chunk_store(ch + 1, nb, nb + JC * LDF, LDF);
+          for (int st = 0; st < KS; ++st) {
+#pragma unroll
+            for (int cb = 0; cb < HB; ++cb) {
+              const int qo = (32 * cb + (lane & 31)) * LDA + 16 * st + 8 * (lane >> 5);
+              const bf16x8 qh = Mfma<bf16>::load(S1h + qo), ql = Mfma<bf16>::load(S1l + qo);
+              if constexpr (RJ) {
+                wn[x][cb] = Mfma<bf16>::mma(uh[st], qh, wn[x][cb]);
+                dd[cb] = Mfma<bf16>::mma(uh[st], ql, dd[cb]);
+                dd[cb] = Mfma<bf16>::mma(ul[st], qh, dd[cb]);
+              } else {
+                wn[x][cb] = Mfma<bf16>::mma(qh, uh[st], wn[x][cb]);
+                dd[cb] = Mfma<bf16>::mma(qh, ul[st], dd[cb]);
+                dd[cb] = Mfma<bf16>::mma(ql, uh[st], dd[cb]);
+              }
+            }
+          }
+#pragma unroll
+          for (int cb = 0; cb < HB; ++cb) wn[x][cb] += dd[cb];
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < HB; ++cb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int ro = 8 * g4 + 4 * (lane >> 5);
+              if constexpr (RJ) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  wn[x][cb][4 * g4 + i] = Ud[(int64_t)(32 * jb + ro + i) * H + 32 * cb + (lane & 31)];
+              } else {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(Ud + (int64_t)jl * H + 32 * cb + ro);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wn[x][cb][4 * g4 + i] = v[i];
+              }
+            }
         }
-        bf16* cb = fb(ch);
-        mma_blocks<H, 1, JBC, NBF, false, false>(cx, w, S1h, S1l, LDA, cb, cb + JC * LDF, LDF, lane);
-      }
-      if (fact) {
+        // W - U
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          int j, c;
-          fcoord(ch, g4, j, c);
-          f32x4 uv;
-          if (u.muon)
-            uv = f32x4{cx[0][4 * g4], cx[0][4 * g4 + 1], cx[0][4 * g4 + 2], cx[0][4 * g4 + 3]};
-          else
-            uv = *reinterpret_cast<const f32x4*>(Ud + (int64_t)j * H + c);
+        for (int cb = 0; cb < HB; ++cb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wn[ch][4 * g4 + i] -= uv[i];
-        }
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int ro = 8 * g4 + 4 * (lane >> 5);
+            if constexpr (RJ) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                wn[x][cb][4 * g4 + i] = W[(int64_t)(32 * jb + ro + i) * H + 32 * cb + (lane & 31)] - wn[x][cb][4 * g4 + i];
+            } else {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(W + (int64_t)jl * H + 32 * cb + ro);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) wn[x][cb][4 * g4 + i] = v[i] - wn[x][cb][4 * g4 + i];
+            }
+          }
       }
-      if (u.muon) __syncthreads();
     }
-  }
 
-  // ---- 4. renorm over the input axis (partial sums of squares from the register blocks) --------
-  if (u.weight_norm) {
-    if (mat == 1) {  // W1 [rh][h]: column c over all rh rows; lanes of a half hold 32 rows j
-      if (fact) {
-        float cs[16];
+    // renorm over the input axis to the initial norms
+    float fr[NJW];      // W0T / W2T: factor of this lane's row j in block x
+    float fc[HB];       // W1: factor of this lane's column c in block cb
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+    for (int x = 0; x < NJW; ++x) fr[x] = 1.f;
+#pragma unroll
+    for (int cb = 0; cb < HB; ++cb) fc[cb] = 1.f;
+    if (u.weight_norm) {
+      if constexpr (RJ) {
+#pragma unroll
+        for (int cb = 0; cb < HB; ++cb) {
           float a = 0.f;
 #pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) a += wn[ch][r] * wn[ch][r];
+          for (int x = 0; x < NJW; ++x)
+            if (w + 8 * x < NJ) {
 #pragma unroll
-          for (int off = 1; off < 32; off <<= 1) a += __shfl_xor(a, off, 64);
-          cs[r] = a;
-        }
-        if ((lane & 31) == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) npart[fjb * H + fcb * 32 + acc_row(r, lane)] = cs[r];
-        }
-      }
-      __syncthreads();
-      for (int c = tid; c < H; c += 512) {
-        float tot = 0.f;
-        for (int jb = 0; jb < JBC; ++jb) tot += npart[jb * H + c];
-        fac[c] = nu[c] / (sqrtf(tot) + u.eps_norm);
-      }
-    } else {  // W0T / W2T: state row j over its h inputs; a lane holds 16 of a block's 32 columns
-      if (fact) {
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          float a = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) a += wn[ch][r] * wn[ch][r];
+              for (int r = 0; r < 16; ++r) a += wn[x][cb][r] * wn[x][cb][r];
+            }
           a += __shfl_xor(a, 32, 64);
-          if (lane < 32) npart[fcb * RH + ch * JC + fjb * 32 + lane] = a;
+          if (lane < 32) npart[w * H + 32 * cb + lane] = a;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int cb = 0; cb < HB; ++cb) {
+          const int c = 32 * cb + (lane & 31);
+          float tot = 0.f;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) tot += npart[v * H + c];
+          fc[cb] = nu[c] / (sqrtf(tot) + u.eps_norm);
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) {
+          const int jb = w + 8 * x;
+          if (jb < NJ) {
+            float a = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < HB; ++cb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) a += wn[x][cb][r] * wn[x][cb][r];
+            a += __shfl_xor(a, 32, 64);
+            fr[x] = nu[32 * jb + (lane & 31)] / (sqrtf(a) + u.eps_norm);
+          }
         }
       }
-      __syncthreads();
-      for (int j = tid; j < RH; j += 512) {
-        float tot = 0.f;
-        for (int cb = 0; cb < HB; ++cb) tot += npart[cb * RH + j];
-        fac[j] = nu[j] / (sqrtf(tot) + u.eps_norm);
-      }
     }
-    __syncthreads();
-  }
 
-  // ---- 5. state and operand shadows from the register blocks ----------------------------------
-  if (fact) {
+    // state and operand shadows
     OpT* sh = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n;
     OpT* dst = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n;
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
+    for (int x = 0; x < NJW; ++x) {
+      const int jb = w + 8 * x;
+      if (jb < NJ) {
+        const int jl = 32 * jb + (lane & 31);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        int j, c;
-        fcoord(ch, g4, j, c);
-        f32x4 v = f32x4{wn[ch][4 * g4], wn[ch][4 * g4 + 1], wn[ch][4 * g4 + 2], wn[ch][4 * g4 + 3]};
-        if (u.weight_norm) {
-          if (mat == 1)
-            v *= *reinterpret_cast<const f32x4*>(fac + c);
-          else
-            v *= fac[j];
-        }
-        *reinterpret_cast<f32x4*>(W + (int64_t)j * H + c) = v;
-        store4(dst + (int64_t)j * H + c, v);
-        if (mat == 1) {  // W1^T shadow [h][rh]: 32 lanes write 32 consecutive j of a row c
+        for (int cb = 0; cb < HB; ++cb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sh[3 * n + (int64_t)(c + i) * RH + j] = Mfma<OpT>::from_f32(v[i]);
-        }
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int ro = 8 * g4 + 4 * (lane >> 5);
+            f32x4 v = f32x4{wn[x][cb][4 * g4], wn[x][cb][4 * g4 + 1], wn[x][cb][4 * g4 + 2], wn[x][cb][4 * g4 + 3]};
+            if constexpr (RJ) {  // rows j0 .. j0 + 3 of column c
+              v *= fc[cb];
+              const int j0 = 32 * jb + ro, c = 32 * cb + (lane & 31);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                W[(int64_t)(j0 + i) * H + c] = v[i];
+                dst[(int64_t)(j0 + i) * H + c] = Mfma<OpT>::from_f32(v[i]);
+              }
+              store4(sh + 3 * n + (int64_t)c * RH + j0, v);  // W1^T shadow [h][rh]
+            } else {             // columns c0 .. c0 + 3 of row j
+              v *= fr[x];
+              const int c0 = 32 * cb + ro;
+              *reinterpret_cast<f32x4*>(W + (int64_t)jl * H + c0) = v;
+              store4(dst + (int64_t)jl * H + c0, v);
+            }
+          }
       }
-  }
+    }
+  };
+  if (mat == 1)
+    finish(std::true_type{});
+  else
+    finish(std::false_type{});
 }
 
 // workgroup mi handles matrix mi % 3 of pair mi / 3
