@@ -262,6 +262,10 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
+// Workgroup barrier that orders LDS accesses only: global memory operations of the waves may
+// still be in flight when it releases (__syncthreads would wait for them as well).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline float block_sum(float v, float* red /* >= 16 floats of LDS */) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;

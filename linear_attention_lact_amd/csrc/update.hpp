@@ -167,9 +167,19 @@ __device__ __forceinline__ void mma_blocks(f32x16 (&c)[Q], int w, const bf16* Ah
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Row stride (bf16 elements) of the h x h slots: the smallest 16-byte multiple >= h + 8 whose
+// 4-byte word count is 12 mod 32. Measured at h = 128 (304-byte rows): the row reads run as with
+// 272-byte rows and the transpose reads of the P A product lose their bank conflicts (1.5 us per
+// product instead of 2.2); 288-byte rows slow every product down.
+constexpr int slot_ld(int h) {
+  int l = h + 8;
+  while ((l / 2) % 32 != 12) l += 8;
+  return l;
+}
+
 template <int H, int RH>
 struct UpdLayout {
-  static constexpr int LDA = H + 8;            // h x h matrices: bf16 hi / lo [H][LDA]
+  static constexpr int LDA = slot_ld(H);       // h x h matrices: bf16 hi / lo [H][LDA]
   static constexpr int SLOT = 2 * H * LDA * 2;
   typedef TileLayout<__bf16, H> GL;            // X_0^T (rows j, h columns) for the Gram product
   static constexpr int GSZ = RH * GL::LD;      // elements of its hi (and of its lo) array
@@ -184,12 +194,14 @@ struct UpdLayout {
 template <int H, int RH>
 constexpr int update_lds_bytes() { return UpdLayout<H, RH>::bytes; }
 
-// Gram product A_0 = X_0 X_0^T of wave w's blocks t = Q*w + q: block t is (t / HB, t % HB),
-// K runs over all RH state rows of X_0^T (transpose reads of the swizzled rows; both operands
-// take the same permuted K order), split-bf16 with the cross terms in separate registers.
-template <class GL, int RH, int Q, int HB, int NBA>
-__device__ __forceinline__ void gram_blocks(f32x16 (&c)[Q], int w, const bf16* Gh, const bf16* Gl, int lane) {
+// Gram product A_0 = X_0 X_0^T for the Q consecutive 32 x 32 blocks of one block row starting at
+// block t0 = (t0 / HB, t0 % HB): K runs over all RH state rows of X_0^T (transpose reads of the
+// swizzled rows; both operands take the same permuted K order), split-bf16 with the cross terms
+// in separate registers.
+template <class GL, int RH, int Q, int HB>
+__device__ __forceinline__ void gram_row(f32x16 (&c)[Q], int t0, const bf16* Gh, const bf16* Gl, int lane) {
   typedef Mfma<bf16> M;
+  const int ca = 32 * (t0 / HB), cb0 = 32 * (t0 % HB);
   f32x16 d[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) zero(d[q]);
@@ -197,24 +209,38 @@ __device__ __forceinline__ void gram_blocks(f32x16 (&c)[Q], int w, const bf16* G
   for (int hr = 0; hr < RH / 32; ++hr) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
+      const bf16x8 ah = tile_kfrag_tr<GL>(Gh, 32 * hr, ca, q2, lane);
+      const bf16x8 al = tile_kfrag_tr<GL>(Gl, 32 * hr, ca, q2, lane);
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const int t = Q * w + q;
-        if (t < NBA) {
-          const int ca = 32 * (t / HB), cb = 32 * (t % HB);
-          const bf16x8 ah = tile_kfrag_tr<GL>(Gh, 32 * hr, ca, q2, lane);
-          const bf16x8 al = tile_kfrag_tr<GL>(Gl, 32 * hr, ca, q2, lane);
-          const bf16x8 bh = tile_kfrag_tr<GL>(Gh, 32 * hr, cb, q2, lane);
-          const bf16x8 bl = tile_kfrag_tr<GL>(Gl, 32 * hr, cb, q2, lane);
-          c[q] = M::mma(ah, bh, c[q]);
-          d[q] = M::mma(ah, bl, d[q]);
-          d[q] = M::mma(al, bh, d[q]);
-        }
+        const bf16x8 bh = tile_kfrag_tr<GL>(Gh, 32 * hr, cb0 + 32 * q, q2, lane);
+        const bf16x8 bl = tile_kfrag_tr<GL>(Gl, 32 * hr, cb0 + 32 * q, q2, lane);
+        c[q] = M::mma(ah, bh, c[q]);
+        d[q] = M::mma(ah, bl, d[q]);
+        d[q] = M::mma(al, bh, d[q]);
       }
     }
   }
 #pragma unroll
   for (int q = 0; q < Q; ++q) c[q] += d[q];
+}
+
+// wave w's blocks t = Q*w + q of the h x h Gram matrix (one block row when HB % Q == 0)
+template <class GL, int RH, int Q, int HB, int NBA>
+__device__ __forceinline__ void gram_blocks(f32x16 (&c)[Q], int w, const bf16* Gh, const bf16* Gl, int lane) {
+  if constexpr (HB % Q == 0) {
+    if (Q * w < NBA) gram_row<GL, RH, Q, HB>(c, Q * w, Gh, Gl, lane);
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int t = Q * w + q;
+      if (t < NBA) {
+        f32x16 one[1] = {c[q]};
+        gram_row<GL, RH, 1, HB>(one, t, Gh, Gl, lane);
+        c[q] = one[0];
+      }
+    }
+  }
 }
 
 // grid: 3 * P workgroups (one per matrix); block 512 threads (8 waves).
@@ -288,9 +314,21 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
       }
     }
   }
+  // The norm needs LDS only: its barriers leave the U stores in flight (they drain during the
+  // staging below, whose barrier waits for them; every later read of U follows that barrier).
   float inv = 1.f;
-  if (u.muon) inv = 1.f / (sqrtf(block_sum(ss, red)) + u.eps_ns);
-  __syncthreads();
+  if (u.muon) {
+    ss = wave_sum(ss);
+    lds_barrier();
+    if (lane == 0) red[w] = ss;
+    lds_barrier();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot += red[i];
+    inv = 1.f / (sqrtf(tot) + u.eps_ns);
+  } else {
+    __syncthreads();
+  }
 
   auto put_sym = [&](const f32x16 (&v)[QA], bf16* dh, bf16* dl) {
 #pragma unroll
