@@ -542,6 +542,203 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
 }
 
 // ------------------------------------------------------------------------------------------
+// grad_ws_kernel: the LaCT partial sums P0, P1, P2 of grad_rd_kernel (same block mapping, same
+// outputs) with the work of a workgroup split by role over 8 waves, so that every SIMD holds one
+// wave of each role and the register file takes two waves per SIMD:
+//   forward waves 0-3  (hidden half jh = w & 1, token half th = w >> 1 of a 64-token tile):
+//       A = K W0, Bm = K W2, D = V W1^T from register-resident fast-weight fragments, then the
+//       SwiGLU / silu' epilogue; the three intermediates go to LDS as contraction fragments;
+//   contraction waves 4-7 (hidden half jh = w & 1, output columns (w >> 2 & 1)-th half):
+//       P1 += (eta H)^T V, P0 += X0^T K, P2 += X2^T K over the tile, and the staging of the
+//       K / V tiles two steps ahead (global -> registers -> LDS, converted to the operand type).
+// One barrier per step: the forward of tile i+1 runs beside the contraction of tile i, so one
+// role's VALU work (the epilogue, the staging) overlaps the other role's MFMA work.
+template <class OpT, int H>
+constexpr int grad_ws_lds_bytes() {
+  return 3 * 2 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + (3 * TT + 16) * 4 + 2 * 4 * 3 * 2 * 64 * 16;
+}
+
+template <class IoT, class OpT, int H, bool SCALE_MID>
+__global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int npairs) {
+  static_assert(sizeof(OpT) == 2 && (H == 64 || H == 128), "16-bit operands, h = 64 or 128");
+  typedef Mfma<OpT> M;
+  typedef typename M::frag frag;
+  typedef TileLayout<OpT, H> TL;
+  constexpr int TILE = TT * TL::LD;         // elements of one staged tensor tile
+  constexpr int CB = H / 32;
+  constexpr int CH = CB / 2;                // output column blocks per contraction wave
+  constexpr int KS = H / M::KSTEP;          // forward K steps over h
+  constexpr int QS = 32 / M::KSTEP;         // contraction K steps over a 32-token half
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  OpT* tiles = reinterpret_cast<OpT*>(smem);                      // [3 buffers][K, V][TT][LD]
+  float* eta_s = reinterpret_cast<float*>(tiles + 3 * 2 * TILE);  // [3 buffers][TT]
+  float* red = eta_s + 3 * TT;                                    // [16]
+  frag* inter = reinterpret_cast<frag*>(red + 16);                // [2][4 forward waves][3][QS][64]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int njb = a.rh / RB;
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int jb = slot % njb;
+  const int group = xcd + 8 * (slot / njb);
+  if (group >= npairs * nseg) return;
+  const int pair = group / nseg, seg = group % nseg;
+  const int t_begin = a.t_base + seg * a.seg_len;
+  const int t_end = min(t_begin + a.seg_len, a.t_limit);
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + TT - 1) / TT : 0;
+  const int jh = w & 1;
+
+  const IoT* Kp = reinterpret_cast<const IoT*>(a.K) + pair * a.tok_pair_stride;
+  const IoT* Vp = reinterpret_cast<const IoT*>(a.V) + pair * a.tok_pair_stride;
+  const float* ep = a.eta + pair * a.eta_pair_stride;
+
+  float scale = 1.f;
+  if constexpr (SCALE_MID) {
+    float mx = 0.f;
+    for (int t = t_begin + tid; t < t_end; t += 512) mx = fmaxf(mx, ep[t]);
+    mx = block_max(mx, red);
+    if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
+  }
+
+  if (w < 4) {
+    // ---------------- forward waves ----------------
+    const int th = w >> 1;
+    frag wf[3][KS];
+    {
+      const OpT* src[3] = {reinterpret_cast<const OpT*>(a.W0T), reinterpret_cast<const OpT*>(a.W2T),
+                           reinterpret_cast<const OpT*>(a.W1)};
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const OpT* row = src[m] + pair * a.w_pair_stride + (int64_t)(jb * RB + jh * 32 + (lane & 31)) * H +
+                         (lane >> 5) * M::KSUB;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) wf[m][s] = M::load(row + s * M::KSTEP);
+      }
+    }
+    if (ntiles > 0) __syncthreads();  // tile 0 staged
+    int fb = 0;                       // buffer of tile i + 1
+    for (int i = -1; i < ntiles; ++i) {
+      if (i + 1 < ntiles) {
+        const OpT* b = tiles + fb * 2 * TILE;
+        const int kro = th * 32 + (lane & 31), kco = (lane >> 5) * M::KSUB;
+        f32x16 F[3];
+#pragma unroll
+        for (int m = 0; m < 3; ++m) zero(F[m]);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const auto kf = M::load(b + TL::at(kro, kco + s * M::KSTEP));
+          const auto vf = M::load(b + TILE + TL::at(kro, kco + s * M::KSTEP));
+          F[0] = M::mma(kf, wf[0][s], F[0]);
+          F[1] = M::mma(kf, wf[1][s], F[1]);
+          F[2] = M::mma(vf, wf[2][s], F[2]);
+        }
+        // epilogue: F[0] <- eta*H, F[1] <- X0, F[2] <- X2, as contraction fragments
+        const float* er = eta_s + fb * TT + th * 32 + 4 * (lane >> 5);
+        frag* dst = inter + (size_t)((((i + 1) & 1) * 4 + w) * 3) * QS * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+          frag o0, o1, o2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * q + e;
+            const float ev = er[8 * (r >> 2) + (r & 3)];
+            const float A = F[0][r], Bm = F[1][r], Dr = F[2][r];
+            const float sg = sigmoid_fast(A);
+            const float sil = A * sg;
+            const float eB = ev * Bm;
+            o0[e] = M::from_f32(sil * eB);
+            o1[e] = M::from_f32((eB * Dr) * (sg * fmaf(A, 1.f - sg, 1.f)));
+            o2[e] = M::from_f32((ev * sil) * Dr);
+          }
+          dst[(0 * QS + q) * 64] = o0;
+          dst[(1 * QS + q) * 64] = o1;
+          dst[(2 * QS + q) * 64] = o2;
+        }
+      }
+      fb = fb == 2 ? 0 : fb + 1;
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- contraction waves ----------------
+  const int ctid = tid - 256;
+  const int cpair = (w >> 1) & 1;           // output column blocks cpair * CH ..
+  TileStage<IoT, OpT, H> stage;
+  float ev = 0.f;
+  auto fetch = [&](int i) {
+    const int t0 = t_begin + i * TT;
+    stage.load(Kp, Vp, t0, t_end, ctid);
+    if (ctid < TT) ev = (t0 + ctid < t_end) ? ep[t0 + ctid] : 0.f;
+  };
+  auto put = [&](int buf) {
+    OpT* b = tiles + buf * 2 * TILE;
+    stage.template store_at<TL>(b, b + TILE, ctid);
+    if (ctid < TT) eta_s[buf * TT + ctid] = ev * scale;
+  };
+
+  f32x16 acc[3][CH];
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) zero(acc[m][c]);
+
+  if (ntiles > 0) {
+    fetch(0);
+    put(0);
+    if (ntiles > 1) fetch(1);
+    __syncthreads();  // tile 0 staged
+  }
+  int cb = 0;         // buffer of tile i (tile i + 2 goes to buffer cb + 2 mod 3)
+  for (int i = -1; i < ntiles; ++i) {
+    const int pb = cb == 0 ? 2 : cb - 1;    // buffer of tile i + 2 (= the buffer of tile i - 1)
+    if (i >= 0) {
+      const OpT* b = tiles + cb * 2 * TILE;
+      const frag* src = inter + (size_t)((i & 1) * 4 * 3) * QS * 64 + lane;
+#pragma unroll
+      for (int th2 = 0; th2 < 2; ++th2) {
+        const frag* fsrc = src + (size_t)((jh + 2 * th2) * 3) * QS * 64;
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+          frag am[3];
+#pragma unroll
+          for (int m = 0; m < 3; ++m) am[m] = fsrc[(m * QS + q) * 64];
+#pragma unroll
+          for (int cc = 0; cc < CH; ++cc) {
+            const int c = cpair * CH + cc;
+            // am[0] = eta H (with V) -> P1; am[1] = X0 (with K) -> P0; am[2] = X2 (with K) -> P2
+            acc[0][cc] = M::mma(am[0], tile_kfrag_tr<TL>(b + TILE, 32 * th2, c * 32, q, lane), acc[0][cc]);
+            const auto bk = tile_kfrag_tr<TL>(b, 32 * th2, c * 32, q, lane);
+            acc[1][cc] = M::mma(am[1], bk, acc[1][cc]);
+            acc[2][cc] = M::mma(am[2], bk, acc[2][cc]);
+          }
+        }
+      }
+    }
+    if (i + 2 < ntiles) {
+      put(i < 0 ? 1 : pb);
+      if (i + 3 < ntiles) fetch(i + 3);
+    }
+    if (i >= 0) cb = cb == 2 ? 0 : cb + 1;
+    __syncthreads();
+  }
+
+  const float inv = 1.f / scale;
+  float* ob = a.out + seg * a.out_y_stride + pair * a.out_pair_stride;
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const int omat = m == 0 ? 1 : (m == 1 ? 0 : 2);
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const int c = cpair * CH + cc;
+      float* o = ob + omat * a.out_mat_stride + ((int64_t)jb * RB + jh * 32) * H + c * 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[acc_row(r, lane) * H + acc_col(lane)] = acc[m][cc][r] * inv;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 struct ApplyArgs {
   const void* Q;            // [pair][Nq][H]
   int64_t tok_pair_stride;

@@ -145,17 +145,21 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
                            float* W1o, float* W2o, float* Mo, hipStream_t st) {
   constexpr bool SCALE = sizeof(OpT) == 2;
   constexpr bool RD = H <= 128;  // register-direct gradient kernel
+  constexpr bool WS = std::is_same<OpT, _Float16>::value && (H == 64 || H == 128);  // its role-split form
   auto gk = grad_kernel<IoT, OpT, H, false, SCALE>;
   auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE>;
+  auto gkw = grad_ws_kernel<typename std::conditional<WS, IoT, bf16_t>::type, _Float16, (WS ? H : 128), true>;
   auto ak = apply_kernel<IoT, OpT, H>;
   // register-direct apply where its double-buffered weight blocks fit in LDS
   constexpr bool ARD = H <= 128 && apply_rd_lds_bytes<OpT, (H <= 128 ? H : 128)>() <= 160 * 1024;
   auto akr = apply_rd_kernel<IoT, OpT, (ARD ? H : 64)>;
-  constexpr int glds = RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false>() : grad_lds_bytes<OpT, H, false>();
+  constexpr int glds = WS   ? grad_ws_lds_bytes<_Float16, (WS ? H : 128)>()
+                       : RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false>()
+                            : grad_lds_bytes<OpT, H, false>();
   constexpr int alds = ARD ? apply_rd_lds_bytes<OpT, (ARD ? H : 64)>() : apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
-    hipError_t e = RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
+    hipError_t e = WS ? allow_lds(gkw, glds) : RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
     return e != hipSuccess ? e : (ARD ? allow_lds(akr, alds) : allow_lds(ak, alds));
   }();
   TTT_HIP(lds_ok);
@@ -291,7 +295,10 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     ga.t_limit = (c + 1) * p.chunk_kv;
     {
       LaunchTimer lt(K_LACT_GRAD, st);
-      if constexpr (RD) {
+      if constexpr (WS) {
+        const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
+        hipLaunchKernelGGL(gkw, dim3(grid), dim3(512), glds, st, ga, S, P);
+      } else if constexpr (RD) {
         const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
         hipLaunchKernelGGL(gkr, dim3(grid), dim3(256), glds, st, ga, S, P);
       } else {
