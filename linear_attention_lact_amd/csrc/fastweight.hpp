@@ -51,6 +51,8 @@ struct GradArgs {
   int64_t out_y_stride;   // between grid.y segments
   int64_t out_pair_stride;
   int64_t out_mat_stride; // between P0 / P1 / P2 (= rh*H)
+  const float* eta_scale; // [pair][segment] power-of-two step-size scales of the region
+                          // (grad_ws_kernel; the other kernels derive them themselves)
 };
 
 // K-major fragment: element (k, n) at base[k * ld + n]; lane l receives n = l & 31 and the
@@ -547,23 +549,25 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
 // wave of each role and the register file takes two waves per SIMD:
 //   forward waves 0-3  (hidden half jh = w & 1, token half th = w >> 1 of a 64-token tile):
 //       A = K W0, Bm = K W2, D = V W1^T from register-resident fast-weight fragments, then the
-//       SwiGLU / silu' epilogue; the three intermediates go to LDS as contraction fragments;
-//   contraction waves 4-7 (hidden half jh = w & 1, output columns (w >> 2 & 1)-th half):
-//       P1 += (eta H)^T V, P0 += X0^T K, P2 += X2^T K over the tile, and the staging of the
-//       K / V tiles two steps ahead (global -> registers -> LDS, converted to the operand type).
-// One barrier per step: the forward of tile i+1 runs beside the contraction of tile i, so one
-// role's VALU work (the epilogue, the staging) overlaps the other role's MFMA work.
+//       SwiGLU / silu' epilogue with the (scaled) step sizes; the three intermediates go to LDS
+//       as contraction fragments;
+//   contraction waves 4-7 (hidden half jh = w & 1, output columns (w >> 1 & 1)-th half):
+//       the staging of the K / V tiles two steps ahead (global -> registers -> LDS, converted to
+//       fp16), then P1 += (eta H)^T V, P0 += X0^T K, P2 += X2^T K over the tile.
+// One barrier per step: the forward of tile i+1 runs beside the contraction of tile i, and each
+// role orders its work so that its VALU phase meets the other role's MFMA phase.
 template <class OpT, int H>
 constexpr int grad_ws_lds_bytes() {
-  return 3 * 2 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + (3 * TT + 16) * 4 + 2 * 4 * 3 * 2 * 64 * 16;
+  return 3 * 2 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + 3 * TT * 4 + 2 * 4 * 3 * 2 * 64 * 16;
 }
 
 template <class IoT, class OpT, int H, bool SCALE_MID>
 __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int npairs) {
-  static_assert(sizeof(OpT) == 2 && (H == 64 || H == 128), "16-bit operands, h = 64 or 128");
+  static_assert(std::is_same<OpT, _Float16>::value && (H == 64 || H == 128), "fp16 operands, h = 64 or 128");
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
   typedef TileLayout<OpT, H> TL;
+  typedef TileStage<IoT, OpT, H> Stage;
   constexpr int TILE = TT * TL::LD;         // elements of one staged tensor tile
   constexpr int CB = H / 32;
   constexpr int CH = CB / 2;                // output column blocks per contraction wave
@@ -572,9 +576,8 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
 
   extern __shared__ __align__(16) unsigned char smem[];
   OpT* tiles = reinterpret_cast<OpT*>(smem);                      // [3 buffers][K, V][TT][LD]
-  float* eta_s = reinterpret_cast<float*>(tiles + 3 * 2 * TILE);  // [3 buffers][TT]
-  float* red = eta_s + 3 * TT;                                    // [16]
-  frag* inter = reinterpret_cast<frag*>(red + 16);                // [2][4 forward waves][3][QS][64]
+  float* eta_s = reinterpret_cast<float*>(tiles + 3 * 2 * TILE);  // [3 buffers][TT] scaled step sizes
+  frag* inter = reinterpret_cast<frag*>(eta_s + 3 * TT);          // [2][4 forward waves][3][QS][64]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int njb = a.rh / RB;
@@ -592,29 +595,38 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
   const IoT* Vp = reinterpret_cast<const IoT*>(a.V) + pair * a.tok_pair_stride;
   const float* ep = a.eta + pair * a.eta_pair_stride;
 
-  float scale = 1.f;
-  if constexpr (SCALE_MID) {
-    float mx = 0.f;
-    for (int t = t_begin + tid; t < t_end; t += 512) mx = fmaxf(mx, ep[t]);
-    mx = block_max(mx, red);
-    if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
+  // requests first: fast weights (forward waves), tiles 0 and 1 and the segment's power-of-two
+  // eta scale (contraction waves, the only users of the scale)
+  const bool fwd = w < 4;
+  const int ctid = tid - 256;
+  frag wf[3][KS];
+  Stage st0, st1;                           // staging registers of even / odd tiles
+  float ev0 = 0.f, ev1 = 0.f;               // step size of token ctid of the staged tile
+  auto fetch = [&](int i, Stage& stg, float& ev) {
+    const int t0 = t_begin + i * TT;
+    stg.load(Kp, Vp, t0, t_end, ctid);
+    if (ctid < TT) ev = (t0 + ctid < t_end) ? ep[t0 + ctid] : 0.f;
+  };
+  if (fwd) {
+    const OpT* src[3] = {reinterpret_cast<const OpT*>(a.W0T), reinterpret_cast<const OpT*>(a.W2T),
+                         reinterpret_cast<const OpT*>(a.W1)};
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const OpT* row = src[m] + pair * a.w_pair_stride + (int64_t)(jb * RB + jh * 32 + (lane & 31)) * H +
+                       (lane >> 5) * M::KSUB;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) wf[m][s] = M::load(row + s * M::KSTEP);
+    }
+  } else if (ntiles > 0) {
+    fetch(0, st0, ev0);
+    if (ntiles > 1) fetch(1, st1, ev1);
   }
+  float scale = 1.f;
+  if constexpr (SCALE_MID) scale = a.eta_scale[pair * nseg + seg];
 
-  if (w < 4) {
+  if (fwd) {
     // ---------------- forward waves ----------------
     const int th = w >> 1;
-    frag wf[3][KS];
-    {
-      const OpT* src[3] = {reinterpret_cast<const OpT*>(a.W0T), reinterpret_cast<const OpT*>(a.W2T),
-                           reinterpret_cast<const OpT*>(a.W1)};
-#pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const OpT* row = src[m] + pair * a.w_pair_stride + (int64_t)(jb * RB + jh * 32 + (lane & 31)) * H +
-                         (lane >> 5) * M::KSUB;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) wf[m][s] = M::load(row + s * M::KSTEP);
-      }
-    }
     if (ntiles > 0) __syncthreads();  // tile 0 staged
     int fb = 0;                       // buffer of tile i + 1
     for (int i = -1; i < ntiles; ++i) {
@@ -647,7 +659,7 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
             const float sil = A * sg;
             const float eB = ev * Bm;
             o0[e] = M::from_f32(sil * eB);
-            o1[e] = M::from_f32((eB * Dr) * (sg * fmaf(A, 1.f - sg, 1.f)));
+            o1[e] = M::from_f32((eB * Dr) * fmaf(sil, 1.f - sg, sg));  // silu'(A) = sg + silu(A) (1 - sg)
             o2[e] = M::from_f32((ev * sil) * Dr);
           }
           dst[(0 * QS + q) * 64] = o0;
@@ -662,18 +674,10 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
   }
 
   // ---------------- contraction waves ----------------
-  const int ctid = tid - 256;
   const int cpair = (w >> 1) & 1;           // output column blocks cpair * CH ..
-  TileStage<IoT, OpT, H> stage;
-  float ev = 0.f;
-  auto fetch = [&](int i) {
-    const int t0 = t_begin + i * TT;
-    stage.load(Kp, Vp, t0, t_end, ctid);
-    if (ctid < TT) ev = (t0 + ctid < t_end) ? ep[t0 + ctid] : 0.f;
-  };
-  auto put = [&](int buf) {
+  auto put = [&](int buf, const Stage& stg, float ev) {
     OpT* b = tiles + buf * 2 * TILE;
-    stage.template store_at<TL>(b, b + TILE, ctid);
+    stg.template store_at<TL>(b, b + TILE, ctid);
     if (ctid < TT) eta_s[buf * TT + ctid] = ev * scale;
   };
 
@@ -684,14 +688,20 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
     for (int c = 0; c < CH; ++c) zero(acc[m][c]);
 
   if (ntiles > 0) {
-    fetch(0);
-    put(0);
-    if (ntiles > 1) fetch(1);
+    put(0, st0, ev0);
+    if (ntiles > 2) fetch(2, st0, ev0);
     __syncthreads();  // tile 0 staged
   }
   int cb = 0;         // buffer of tile i (tile i + 2 goes to buffer cb + 2 mod 3)
-  for (int i = -1; i < ntiles; ++i) {
+  // step i: staging of tile i + 2 first (VALU and LDS writes, while the forward waves run their
+  // MFMAs), then the contraction of tile i (while they run the epilogue). Tile t is staged from
+  // register set t & 1, requested two steps before it is stored.
+  auto step = [&](int i, Stage& stg, float& ev) {
     const int pb = cb == 0 ? 2 : cb - 1;    // buffer of tile i + 2 (= the buffer of tile i - 1)
+    if (i + 2 < ntiles) {
+      put(i < 0 ? 1 : pb, stg, ev);
+      if (i + 4 < ntiles) fetch(i + 4, stg, ev);
+    }
     if (i >= 0) {
       const OpT* b = tiles + cb * 2 * TILE;
       const frag* src = inter + (size_t)((i & 1) * 4 * 3) * QS * 64 + lane;
@@ -715,12 +725,12 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
         }
       }
     }
-    if (i + 2 < ntiles) {
-      put(i < 0 ? 1 : pb);
-      if (i + 3 < ntiles) fetch(i + 3);
-    }
     if (i >= 0) cb = cb == 2 ? 0 : cb + 1;
     __syncthreads();
+  };
+  for (int i = -1; i < ntiles; i += 2) {
+    step(i, st1, ev1);
+    if (i + 1 < ntiles) step(i + 1, st0, ev0);
   }
 
   const float inv = 1.f / scale;

@@ -104,6 +104,23 @@ __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const floa
   }
 }
 
+// power-of-two step-size scales of the gradient's token segments: for chunk c, pair p and
+// segment g, 2^-floor(log2(max eta)) over the segment's tokens (1 when the maximum is 0).
+// grid (P, nch), block 256; out [nch][P][S].
+__global__ void __launch_bounds__(256) lact_eta_scale_kernel(const float* eta, int64_t eta_pair_stride, int chunk,
+                                                            int seg_len, int S, float* out) {
+  __shared__ float red[16];
+  const int pair = blockIdx.x, c = blockIdx.y, P = gridDim.x;
+  const float* ep = eta + pair * eta_pair_stride;
+  for (int g = 0; g < S; ++g) {
+    const int t0 = c * chunk + g * seg_len, t1 = min(t0 + seg_len, (c + 1) * chunk);
+    float mx = 0.f;
+    for (int t = t0 + threadIdx.x; t < t1; t += 256) mx = fmaxf(mx, ep[t]);
+    mx = block_max(mx, red);
+    if (threadIdx.x == 0) out[((int64_t)c * P + pair) * S + g] = mx > 0.f ? exp2f(-floorf(log2f(mx))) : 1.f;
+  }
+}
+
 // finalize: state and momentum back to the API's row form (W0/W2 transposed through LDS).
 // grid (rh/32 * h/32, 3, P), block 256: one 32 x 32 state tile.
 __global__ void __launch_bounds__(256) lact_final_kernel(LactState s, float* W0o, float* W1o, float* W2o,
@@ -208,6 +225,12 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const int ntile = (p.chunk_kv + TT - 1) / TT;
   const int tiles_per_seg = (ntile + S - 1) / S;
   ga.seg_len = tiles_per_seg * TT;
+  if (WS && nch > 0) {  // the role-split gradient kernel reads its segments' step-size scales
+    LaunchTimer lt(K_LACT_INIT, st);
+    hipLaunchKernelGGL(lact_eta_scale_kernel, dim3((unsigned)P, (unsigned)nch), dim3(256), 0, st, eta,
+                       (int64_t)p.Nk, p.chunk_kv, ga.seg_len, S, s.esc);
+    TTT_HIP(hipGetLastError());
+  }
   ga.W0T = sh;
   ga.W2T = sh + n;
   ga.W1 = sh + 2 * n;
@@ -292,6 +315,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
       if (e != TTT_OK) return e;
     }
     ga.t_base = c * p.chunk_kv;
+    ga.eta_scale = s.esc + (int64_t)c * P * S;
     ga.t_limit = (c + 1) * p.chunk_kv;
     {
       LaunchTimer lt(K_LACT_GRAD, st);
@@ -397,6 +421,7 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   const size_t oU = plan.add((size_t)P * 3 * n * 4);
   const int64_t NSZ = 4 * n + 2 * (int64_t)h * h + TU_SS;
   const size_t oNs = plan.add((size_t)P * 3 * NSZ * 4);
+  const size_t oEsc = plan.add((size_t)nch * P * S * 4);
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -413,6 +438,7 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   s.part = reinterpret_cast<float*>(ws + oPart);
   s.U = reinterpret_cast<float*>(ws + oU);
   s.ns = reinterpret_cast<float*>(ws + oNs);
+  s.esc = reinterpret_cast<float*>(ws + oEsc);
   s.P = P;
   s.h = h;
   s.rh = rh;

@@ -35,6 +35,7 @@ struct LactState {
   float* part;     // token-segment partial products [S][P][3][rh*h]
   float* U;        // the write before Newton-Schulz [P][3][rh*h] (scratch)
   float* ns;       // global NS5 scratch [P][3][NSZ] (large-h path)
+  float* esc;      // power-of-two step-size scales of the gradient segments [chunk][P][S]
   int P, h, rh, NU;
   int64_t NSZ;
 };
