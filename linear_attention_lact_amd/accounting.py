@@ -94,12 +94,12 @@ def profiled_traffic(root: str, kernel_class: str, stem: str):
     sources changed since it was taken."""
     import glob
     import os
-    symbol = {"lact_update": "lact_update_kernel", "lact_grad": "grad_rd_kernel", "lact_apply": "apply_rd_kernel",
-              "linattn_delta": "grad_rd_kernel", "linattn_apply": "apply_rd_kernel",
-              "linattn_scan": "linattn_scan_kernel", "lact_update_apply": "lact_update_apply_kernel",
-              "linattn_fused": "linattn_fused_kernel"}
-    sym = symbol.get(kernel_class)
-    if sym is None:
+    symbol = {"lact_update": ("lact_update_kernel",), "lact_grad": ("grad_ws_kernel", "grad_rd_kernel"),
+              "lact_apply": ("apply_rd_kernel",), "linattn_delta": ("grad_rd_kernel",),
+              "linattn_apply": ("apply_rd_kernel",), "linattn_scan": ("linattn_scan_kernel",),
+              "lact_update_apply": ("lact_update_apply_kernel",), "linattn_fused": ("linattn_fused_kernel",)}
+    syms = symbol.get(kernel_class)
+    if syms is None:
         return None
     cur = kernel_source_hash(root)
     for path in glob.glob(os.path.join(root, "profiles", stem + "_hbm_counters.txt")):
@@ -108,7 +108,7 @@ def profiled_traffic(root: str, kernel_class: str, stem: str):
         if not tag or tag[0].split(":", 1)[1].strip() != cur:
             continue
         for l in lines:
-            if l.startswith("#") or sym not in l:
+            if l.startswith("#") or not any(sym in l for sym in syms):
                 continue
             parts = l.split()
             try:
