@@ -407,9 +407,20 @@ __global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) zero(acc[i][j]);
+  // fp32 state rows of pass p (64 rows x 128 columns, 8 float4 per thread), requested ahead
+  const int tid = threadIdx.x;
+  auto loadw = [&](int pass, f32x4 (&wv)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int f = tid + 256 * q, row = f >> 5, c4 = (f & 31) * 4;
+      wv[q] = *reinterpret_cast<const f32x4*>(g.Wf + (int64_t)(m0 + 64 * pass + row) * g.ldw + n0 + c4);
+    }
+  };
+  f32x4 wv[8];
   for (int kb = 0; kb < nkb; ++kb) {
     issue(kb);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kb == nkb - 1) loadw(0, wv);  // in flight during the last block's products
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 af[4], bfr[2];
@@ -424,12 +435,11 @@ __global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the stage is reloaded next
   }
-  // W += alpha * acc through LDS in four passes of 64 rows (16-byte runs of the fp32 state)
+  // W += alpha * acc through LDS in four passes of 64 rows (16-byte runs of the fp32 state); the
+  // state rows of pass p + 1 are requested as soon as pass p has consumed its own
   constexpr int LDE = PP_BN + 4;
   float* ep = reinterpret_cast<float*>(smem);
-  const int tid = threadIdx.x;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
+  auto pass_rmw = [&](int pass) {
     if (wm == (pass >> 1)) {
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
@@ -441,13 +451,7 @@ __global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
             ep[(32 * ii + acc_row(r, lane)) * LDE + wn * 64 + 32 * j + acc_col(lane)] = acc[i][j][r];
       }
     }
-    __syncthreads();
-    f32x4 wv[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int f = tid + 256 * q, row = f >> 5, c4 = (f & 31) * 4;
-      wv[q] = *reinterpret_cast<const f32x4*>(g.Wf + (int64_t)(m0 + 64 * pass + row) * g.ldw + n0 + c4);
-    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // (the state requests stay in flight)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int f = tid + 256 * q, row = f >> 5, c4 = (f & 31) * 4;
@@ -460,8 +464,11 @@ __global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
                          static_cast<__bf16>(v[3])};
       *reinterpret_cast<bf16x4*>(g.Wsh + idx) = s4;
     }
-    __syncthreads();
-  }
+    if (pass + 1 < 4) loadw(pass + 1, wv);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the staging area is rewritten next
+  };
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) pass_rmw(pass);
 }
 }  // namespace gemm2
 
