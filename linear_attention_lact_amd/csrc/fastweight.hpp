@@ -929,7 +929,8 @@ __device__ __forceinline__ void apply_rd_body(const ApplyArgs& a, int bid, unsig
   constexpr int QS = 32 / M::KSTEP;         // K steps over a 32-unit hidden half block
   constexpr int CB = H / 32;
   constexpr int VW = 16 / (int)sizeof(OpT); // elements per 16-byte chunk
-  constexpr int NCHK = 3 * AJ * H / VW;     // 16-byte chunks of one staged block
+  constexpr int NCPM = AJ * H / VW;         // 16-byte chunks of one matrix's slice
+  constexpr int NCHK = 3 * NCPM;            // 16-byte chunks of one staged block
   constexpr int CPT = (NCHK + 511) / 512;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int slot = bid >> 3;
@@ -958,7 +959,9 @@ __device__ __forceinline__ void apply_rd_body(const ApplyArgs& a, int bid, unsig
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + 512 * i;
       if (NCHK % 512 == 0 || ch < NCHK) {
-        const int m = ch / (AJ * H / VW), r = (ch / (H / VW)) % AJ, c = (ch % (H / VW)) * VW;
+        // matrix of chunk i: a compile-time constant when every 512-chunk step stays in one matrix
+        const int m = NCPM % 512 == 0 ? 512 * i / NCPM : ch / NCPM;
+        const int r = (ch / (H / VW)) % AJ, c = (ch % (H / VW)) * VW;
         const OpT* src = (m == 0 ? w0g : m == 1 ? w2g : w1g) + (int64_t)(jb * AJ + r) * H + c;
         sv[i] = *reinterpret_cast<const u32x4*>(src);
       }
@@ -969,7 +972,8 @@ __device__ __forceinline__ void apply_rd_body(const ApplyArgs& a, int bid, unsig
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + 512 * i;
       if (NCHK % 512 == 0 || ch < NCHK) {
-        const int m = ch / (AJ * H / VW), r = (ch / (H / VW)) % AJ, c = (ch % (H / VW)) * VW;
+        const int m = NCPM % 512 == 0 ? 512 * i / NCPM : ch / NCPM;
+        const int r = (ch / (H / VW)) % AJ, c = (ch % (H / VW)) * VW;
         OpT* dst = m < 2 ? b + m * AJ * LDW + r * LDW + c : b + 2 * AJ * LDW + r * LD1 + c;
         *reinterpret_cast<u32x4*>(dst) = sv[i];
       }
