@@ -22,6 +22,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // bfloat16 bit pattern stored in memory (I/O dtype TTT_BF16).
 struct bf16_t { uint16_t bits; };
@@ -221,6 +222,35 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(u32x4 raw) {
     o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
   }
   return __builtin_bit_cast(f16x8, o);
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 values to fp16, round to nearest even (one packed conversion)
+__device__ __forceinline__ f16x2 f32x2_to_f16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_convertvector((f2){a, b}, f16x2);
+}
+
+// two fp32 values to a packed bf16 pair (a in the low half), round to nearest even
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
+}
+
+// 8 bf16 values times s, rounded to fp16 (round to nearest even)
+__device__ __forceinline__ f16x8 bf16x8_scaled_f16x8(u32x4 raw, float s) {
+  f16x8 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, raw[i] << 16) * s;
+    const float hi = __builtin_bit_cast(float, raw[i] & 0xffff0000u) * s;
+    const f16x2 h = f32x2_to_f16x2(lo, hi);
+    o[2 * i] = h[0];
+    o[2 * i + 1] = h[1];
+  }
+  return o;
 }
 
 template <> struct Io<bf16_t> {

@@ -6,8 +6,8 @@
 //   dS_c = phi(K_c)^T diag(eta_c) V_c,   S_c = W1 + sum_{j<c} dS_j (apply-then-update; j <= c for
 //   update-then-apply),   O_c = phi(Q_c) S_c.
 // One launch, one workgroup per (pair, group of G consecutive chunks); a group behaves as one
-// chunk of G*chunk tokens for the scan (its aggregate is the sum of its chunks' aggregates, added
-// in chunk order) while each chunk's queries still read their own state:
+// chunk of G*chunk tokens for the scan (its aggregate sums all its tokens; the partial sums at its
+// chunk boundaries are kept too) while each chunk's queries still read their own state:
 //   A. the chunk aggregate dS_c from K_c, V_c, eta_c (hidden-row ownership: wave (jb, th) holds
 //      W0^T / W2^T rows jb*32.. as MFMA fragments and sums its token half; halves combined in a
 //      fixed order), published to L2 with a flag;
@@ -81,12 +81,12 @@ struct FusedLayout {
   static constexpr int LDW = H + Pad<OpT>::v;       // W0^T / W2^T rows
   static constexpr int LD1 = tr_ld<OpT>(H);         // S rows (transpose reads)
   static constexpr int TILE = TT * LDK;             // elements of one staged token tile
-  static constexpr int TILES_B = 4 * TILE * (int)sizeof(OpT);                 // 2 buffers x (K, V)
-  static constexpr int COMB_B = NJB * 32 * H * 4;                            // token-half combine
+  static constexpr int NB = 3;                                               // token-tile buffers
+  static constexpr int TILES_B = NB * 2 * TILE * (int)sizeof(OpT);           // NB x (K, eta*V)
   static constexpr int OST_B = NW * 32 * (H + 8) * 2;                         // output staging
-  static constexpr int R0 = TILES_B > COMB_B ? (TILES_B > OST_B ? TILES_B : OST_B) : (COMB_B > OST_B ? COMB_B : OST_B);
-  static constexpr int ETA_O = R0;                                           // [2][TT] floats
-  static constexpr int WT_O = ETA_O + 2 * TT * 4;                            // W0^T, W2^T [RH][LDW]
+  static constexpr int R0 = TILES_B > OST_B ? TILES_B : OST_B;
+  static constexpr int COMB_O = R0;                                          // token-half combine
+  static constexpr int WT_O = COMB_O + NJB * 32 * H * 4;                     // W0^T, W2^T [RH][LDW]
   static constexpr int SS_O = WT_O + 2 * RH * LDW * (int)sizeof(OpT);        // S [RH][LD1]
   static constexpr int bytes = SS_O + RH * LD1 * (int)sizeof(OpT) + 16;
 };
@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   typedef typename M::frag frag;
   typedef FusedLayout<OpT, H, RH> L;
   constexpr int NJB = L::NJB, NW = L::NW, NT = L::NT;
-  constexpr int LDK = L::LDK, LDW = L::LDW, LD1 = L::LD1, TILE = L::TILE;
+  constexpr int LDK = L::LDK, LDW = L::LDW, LD1 = L::LD1, TILE = L::TILE, NB = L::NB;
   constexpr int KS = H / M::KSTEP;          // K steps over h
   constexpr int QS = 32 / M::KSTEP;         // K steps over 32 tokens / 32 hidden units
   constexpr int CB = H / 32;                // 32-column blocks of h
@@ -111,12 +111,12 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   constexpr int NS4 = RH * H / 4;           // float4 groups of the state
   constexpr int SPT = (NS4 + NT - 1) / NT;
   static_assert(RH % 32 == 0 && H % 32 == 0 && NT <= 1024, "shape");
+  static_assert(std::is_same<IoT, bf16_t>::value && std::is_same<OpT, _Float16>::value, "bf16 I/O, fp16 operands");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  OpT* tiles = reinterpret_cast<OpT*>(smem);                       // [2][K, V][TT][LDK]
-  float* comb = reinterpret_cast<float*>(smem);                    // phase A combine (after tiles)
+  OpT* tiles = reinterpret_cast<OpT*>(smem);                       // [NB][K, eta*V][TT][LDK]
+  float* comb = reinterpret_cast<float*>(smem + L::COMB_O);        // phase A token-half combine
   bf16_t* ost = reinterpret_cast<bf16_t*>(smem);                   // phase C output staging
-  float* eta_s = reinterpret_cast<float*>(smem + L::ETA_O);        // [2][TT]
   OpT* Wt = reinterpret_cast<OpT*>(smem + L::WT_O);                // [2][RH][LDW]
   OpT* Ss = reinterpret_cast<OpT*>(smem + L::SS_O);                // [RH][LD1]
   int* ctl = reinterpret_cast<int*>(smem + L::bytes - 16);         // ticket, stop, bad
@@ -148,50 +148,51 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   float* aggp = a.agg + (int64_t)pair * a.nch * n;
   float* inclp = a.incl + (int64_t)pair * a.nch * n;
 
-  // ---- token-tile staging of K, V, eta (rows past the chunk end are zero); NPF register sets
-  // rotate, so a tile is requested NPF tiles before it is stored to LDS ----
+  // ---- token-tile staging of K and eta*V: NPF register sets rotate, so a tile is requested NPF
+  // tiles before it is stored to LDS. Buffer loads over the group's rows return zero past its end,
+  // so the staging has no branches. ----
   struct Staged {
     u32x4 k[CPT], v[CPT];
-    float e;
+    float e[CPT];
   };
   constexpr int NPF = 4;
   Staged sg4[NPF];
-  auto fetch = [&](int t0, Staged& sg) {
-    u32x4* sk = sg.k;
-    u32x4* sv = sg.v;
-    if (t0 >= cend) return;
+  const int gbytes = (cend - cbase) * H * (int)sizeof(IoT);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<IoT*>(Kp + (int64_t)cbase * H), (short)0, gbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<IoT*>(Vp + (int64_t)cbase * H), (short)0, gbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ep + cbase), (short)0, (cend - cbase) * 4, 0x00020000);
+  auto fetch = [&](int tile, Staged& sg) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c16 = tid + NT * i;
-      const int row = c16 / (H / VE), col = (c16 % (H / VE)) * VE;
-      const bool in = (NCK % NT == 0 || c16 < NCK) && t0 + row < cend;
-      sk[i] = in ? *reinterpret_cast<const u32x4*>(Kp + (int64_t)(t0 + row) * H + col) : u32x4{0u, 0u, 0u, 0u};
-      sv[i] = in ? *reinterpret_cast<const u32x4*>(Vp + (int64_t)(t0 + row) * H + col) : u32x4{0u, 0u, 0u, 0u};
+      const int row = tile * TT + c16 / (H / VE), col = (c16 % (H / VE)) * VE;
+      const int off = (row * H + col) * (int)sizeof(IoT);
+      sg.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      sg.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+      sg.e[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, row * 4, 0, 0));
     }
-    if (tid < TT) sg.e = (t0 + tid < cend) ? ep[t0 + tid] : 0.f;
   };
   auto put = [&](int buf, const Staged& sg) {
-    const u32x4* sk = sg.k;
-    const u32x4* sv = sg.v;
     OpT* kb = tiles + buf * 2 * TILE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c16 = tid + NT * i;
       if (NCK % NT == 0 || c16 < NCK) {
         const int row = c16 / (H / VE), col = (c16 % (H / VE)) * VE;
-        TileStage<IoT, OpT, H>::put(sk[i], kb + row * LDK + col);
-        TileStage<IoT, OpT, H>::put(sv[i], kb + TILE + row * LDK + col);
+        *reinterpret_cast<f16x8*>(kb + row * LDK + col) = bf16x8_to_f16x8(sg.k[i]);
+        *reinterpret_cast<f16x8*>(kb + TILE + row * LDK + col) = bf16x8_scaled_f16x8(sg.v[i], sg.e[i]);
       }
     }
-    if (tid < TT) eta_s[buf * TT + tid] = sg.e;
   };
 
   const int ntile = (G * a.chunk + TT - 1) / TT;
 #pragma unroll
-  for (int k = 0; k < NPF; ++k) fetch(cbase + k * TT, sg4[k]);
+  for (int k = 0; k < NPF; ++k) fetch(k, sg4[k]);
 
   // ---- fast-weight fragments of hidden rows jb*32 + (lane & 31): MFMA B operands in phase A,
-  // A operands in phase C (same lane layout); W0^T / W2^T also go to LDS for phase C ----
+  // A operands in phase C (same lane layout); W0^T / W2^T also go to LDS for phase C. W0 is
+  // scaled by -log2(e) and W2 by -ln(2): with u = x W0 (-log2 e) and v = x W2 (-ln 2),
+  // silu(x W0) (x W2) = u v / (1 + 2^u). ----
   const int jb = w % NJB, th = w / NJB;
   frag wf[2][KS];
   {
@@ -199,63 +200,77 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float* src = m == 0 ? W0p : W2p;
+      const float sc = m == 0 ? -1.4426950408889634f : -0.6931471805599453f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int k0 = s * M::KSTEP + (lane >> 5) * M::KSUB;
-        if constexpr (M::KSUB == 8) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) wf[m][s][e] = M::from_f32(src[(int64_t)(k0 + e) * RH + j]);
-          if (th == 0) *reinterpret_cast<frag*>(Wt + (m * RH + j) * LDW + k0) = wf[m][s];
-        } else {
-          wf[m][s] = src[(int64_t)k0 * RH + j];
-          if (th == 0) Wt[(m * RH + j) * LDW + k0] = wf[m][s];
-        }
+        for (int e = 0; e < 8; ++e) wf[m][s][e] = M::from_f32(src[(int64_t)(k0 + e) * RH + j] * sc);
+        if (th == 0) *reinterpret_cast<frag*>(Wt + (m * RH + j) * LDW + k0) = wf[m][s];
       }
     }
   }
 
-  // ---- A. chunk aggregate dS = phi(K)^T diag(eta) V ----
+  // ---- A. chunk aggregate dS = phi(K)^T diag(eta) V. Token tiles rotate through NB = 3 LDS
+  // buffers; iteration i stores tile i+2, reads K of tile i+1 and eta*V of tile i, issues the
+  // pre-activation products of tile i+1 between the epilogue instructions of tile i (the matrix
+  // cores and the vector ALUs work at the same time), then adds tile i into the aggregate. One
+  // barrier per tile. ----
   f32x16 acc[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) zero(acc[c]);
-  auto tile_step = [&](int i, Staged& sg) {
-    __syncthreads();  // the buffer written next is no longer read
-    put(i & 1, sg);
-    fetch(cbase + (i + NPF) * TT, sg);
-    __syncthreads();
-    const OpT* kb = tiles + (i & 1) * 2 * TILE;
-    const OpT* vb = kb + TILE;
-    const float* es = eta_s + (i & 1) * TT;
-    f32x16 fa, fb;
-    zero(fa);
-    zero(fb);
-    const OpT* kr = kb + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
+  const OpT* krow = tiles + (th * 32 + (lane & 31)) * LDK + (lane >> 5) * M::KSUB;
+  f32x16 pu[2], pv[2];  // pre-activations u, v of the current and the next tile
+  auto tile_iter = [&](int i, int bc, Staged& sp, f32x16& uc, f32x16& vc, f32x16& un, f32x16& vn) {
+    const int bn = bc == NB - 1 ? 0 : bc + 1, bp = bn == NB - 1 ? 0 : bn + 1;
+    put(bp, sp);  // tile i+2 (past the end: unread)
+    fetch(i + 2 + NPF, sp);
+    frag kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = M::load(krow + bn * 2 * TILE + s * M::KSTEP);
+    frag vf[QS][CB];
+    const OpT* vh = tiles + bc * 2 * TILE + TILE + th * 32 * LDK;
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+#pragma unroll
+      for (int c = 0; c < CB; ++c) vf[q][c] = acc_kfrag_tr<OpT>(vh + c * 32, LDK, q, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    frag hf[QS];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float x0 = uc[r], x1 = uc[r + 1];
+      const float y0 = x0 * vc[r] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x0));
+      const float y1 = x1 * vc[r + 1] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x1));
+      const f16x2 h = f32x2_to_f16x2(y0, y1);
+      hf[r >> 3][r & 7] = h[0];
+      hf[r >> 3][(r & 7) + 1] = h[1];
+    }
+    zero(un);
+    zero(vn);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const frag kf = M::load(kr + s * M::KSTEP);
-      fa = M::mma(kf, wf[0][s], fa);
-      fb = M::mma(kf, wf[1][s], fb);
+      un = M::mma(kf[s], wf[0][s], un);
+      vn = M::mma(kf[s], wf[1][s], vn);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float A = fa[r];
-      fa[r] = es[th * 32 + acc_row(r, lane)] * (A * sigmoid_fast(A)) * fb[r];
-    }
-    const OpT* vh = vb + th * 32 * LDK;
+    for (int q = 0; q < QS; ++q)
 #pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const frag af = acc_to_afrag<OpT>(fa, q);
+      for (int c = 0; c < CB; ++c) acc[c] = M::mma(hf[q], vf[q][c], acc[c]);
+    // schedule: the pre-activation products spread over the epilogue, then the contraction
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
-      for (int c = 0; c < CB; ++c) acc[c] = M::mma(af, acc_kfrag_tr<OpT>(vh + c * 32, LDK, q, lane), acc[c]);
+    for (int m = 0; m < 2 * KS; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 88 / (2 * KS), 0);
     }
-  };
-  // token halves: wave (jb, 1) hands its sums to wave (jb, 0), which adds them in a fixed order.
-  // Chunk i of the group: aggregate to slot ch*G + i for i < G-1; the group's sum (the chunks'
-  // aggregates added in order) to slot ch*G + G-1. The combine area overlays the token tiles, whose
-  // buffers are both free between the chunk's last step and the next step's store.
-  f32x16 tot[CB];
-  auto combine = [&](int i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, QS * CB, 0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+  };
+  // The sums run over the whole group. At the end of the group's chunk i, wave (jb, 1) hands its
+  // sums to wave (jb, 0), which adds them (in a fixed order) and stores the group's partial sum
+  // through chunk i to slot ch*G + i; slot ch*G + G-1 holds the group's aggregate.
+  auto combine = [&](int i) {
     if (th == 1) {
 #pragma unroll
       for (int c = 0; c < CB; ++c)
@@ -264,55 +279,66 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
     }
     __syncthreads();
     if (th == 0) {
+      float* ag = aggp + ((int64_t)ch * G + i) * n + (int64_t)jb * 32 * H;
 #pragma unroll
       for (int c = 0; c < CB; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = acc[c][r] + comb[((jb * CB + c) * 16 + r) * 64 + lane];
-          tot[c][r] = i == 0 ? v : tot[c][r] + v;
-          acc[c][r] = v;
-        }
-      if (i < G - 1) {
-        float* ag = aggp + ((int64_t)ch * G + i) * n + (int64_t)jb * 32 * H;
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ag[acc_row(r, lane) * H + c * 32 + acc_col(lane)] = acc[c][r];
-      }
+        for (int r = 0; r < 16; ++r)
+          ag[acc_row(r, lane) * H + c * 32 + acc_col(lane)] = acc[c][r] + comb[((jb * CB + c) * 16 + r) * 64 + lane];
     }
-#pragma unroll
-    for (int c = 0; c < CB; ++c) zero(acc[c]);
   };
-  const int tpc = a.chunk / TT;  // tiles per chunk (G > 1: whole tiles)
-  for (int i = 0; i < ntile; i += NPF) {
+  put(0, sg4[0]);
+  fetch(NPF, sg4[0]);
+  put(1, sg4[1]);
+  fetch(NPF + 1, sg4[1]);
+  __syncthreads();
+  {
+    zero(pu[0]);
+    zero(pv[0]);
 #pragma unroll
-    for (int k = 0; k < NPF; ++k)
-      if (i + k < ntile) {
-        tile_step(i + k, sg4[k]);
-        if (G > 1 && (i + k + 1) % tpc == 0 && i + k + 1 < ntile) combine((i + k) / tpc);
-      }
+    for (int s = 0; s < KS; ++s) {
+      const frag kf = M::load(krow + s * M::KSTEP);
+      pu[0] = M::mma(kf, wf[0][s], pu[0]);
+      pv[0] = M::mma(kf, wf[1][s], pv[0]);
+    }
+  }
+  const int tpc = a.chunk / TT;  // tiles per chunk (G > 1: whole tiles)
+  int bc = 0;                    // buffer of tile i
+  // whole blocks of NPF tiles run without branches between the staging loads and their use, so
+  // the loads stay in flight across iterations; the remainder follows
+  const int nfull = ntile - ntile % NPF;
+  int i0 = 0;
+  for (; i0 < nfull; i0 += NPF) {
+#pragma unroll
+    for (int k = 0; k < NPF; ++k) {
+      const int i = i0 + k;
+      tile_iter(i, bc, sg4[(k + 2) % NPF], pu[k & 1], pv[k & 1], pu[(k + 1) & 1], pv[(k + 1) & 1]);
+      bc = bc == NB - 1 ? 0 : bc + 1;
+      if (G > 1 && (i + 1) % tpc == 0 && i + 1 < ntile) combine(i / tpc);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NPF - 1; ++k) {
+    const int i = i0 + k;
+    if (i < ntile) {
+      tile_iter(i, bc, sg4[(k + 2) % NPF], pu[k & 1], pv[k & 1], pu[(k + 1) & 1], pv[(k + 1) & 1]);
+      bc = bc == NB - 1 ? 0 : bc + 1;
+    }
   }
   combine(G - 1);
-  if (th == 0) {
-    float* ag = aggp + ((int64_t)ch * G + G - 1) * n + (int64_t)jb * 32 * H;
-#pragma unroll
-    for (int c = 0; c < CB; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ag[acc_row(r, lane) * H + c * 32 + acc_col(lane)] = tot[c][r];
-  }
   drain_stores();
   __syncthreads();
   if (tid == 0) __hip_atomic_store(fl + ch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // the first query pass's rows are requested now and arrive during the lookback
-  static_assert(std::is_same<IoT, bf16_t>::value && std::is_same<OpT, _Float16>::value, "bf16 I/O");
   u32x4 qa[KS], qb[KS];
-  auto load_q = [&](int t0, u32x4 (&qr)[KS]) {
-    const int t = t0 + 32 * w + (lane & 31);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<IoT*>(Qp + (int64_t)cbase * H), (short)0, gbytes, 0x00020000);
+  auto load_q = [&](int t0, u32x4 (&qr)[KS]) {  // rows past the group's end read zero
+    const int t = t0 - cbase + 32 * w + (lane & 31);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int c = s * M::KSTEP + (lane >> 5) * M::KSUB;
-      qr[s] = (t0 < cend && t < cend) ? *reinterpret_cast<const u32x4*>(Qp + (int64_t)t * H + c) : u32x4{0u, 0u, 0u, 0u};
+      qr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (t * H + c) * (int)sizeof(IoT), 0, 0));
     }
   };
   load_q(cbase, qa);
@@ -353,7 +379,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   const bool bad = ctl[2] != 0;
   const __amdgpu_buffer_rsrc_t ra = dev_rsrc(aggp, (int)(a.nch * n * 4));
   const __amdgpu_buffer_rsrc_t ri = dev_rsrc(inclp, (int)(a.nch * n * 4));
-  f32x4 run[SPT], ginc[SPT];  // state before the group's current chunk; the group's inclusive prefix
+  f32x4 run[SPT];  // state before the group
   {
     // prefix = (inclusive prefix at `stop`, or W1) + aggregates stop+1 .. ch-1, left to right;
     // loads of eight aggregates are in flight together
@@ -380,105 +406,152 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 #pragma unroll
           for (int i = 0; i < SPT; ++i) s[i] += t[jj][i];
     }
+    f32x4 own[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) own[i] = dev_load4(ra, (int)(((ch * G + G - 1) * n + 4 * (tid + NT * i)) * 4));
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int e = 4 * (tid + NT * i);
       if (NS4 % NT != 0 && e >= 4 * NS4) continue;
-      const f32x4 inc = s[i] + dev_load4(ra, (int)(((ch * G + G - 1) * n + e) * 4));
+      const f32x4 inc = s[i] + own[i];
       *reinterpret_cast<f32x4*>(inclp + (int64_t)ch * n + e) = inc;
       if (ch == ngr - 1 && a.S_out) *reinterpret_cast<f32x4*>(a.S_out + (int64_t)pair * n + e) = inc;
       run[i] = s[i];
-      ginc[i] = inc;
     }
   }
   drain_stores();
   __syncthreads();
   if (tid == 0) __hip_atomic_store(fl + ch, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- C. O = phi(Q) S for the chunk's query tokens, wave w: 32 tokens per pass ----
-  const float poison = bad ? __builtin_nanf("") : 0.f;
-  int oend = cend;  // end of the chunk whose outputs are written
+  // ---- C. O = phi(Q) S for the chunk's query tokens, wave w: 32 tokens per pass, the fast
+  // weights and S read from LDS. The hidden blocks are pipelined: the pre-activation products of
+  // block j2+1 are issued between the epilogue instructions of block j2. ----
+  IoT* Op = reinterpret_cast<IoT*>(a.O) + (int64_t)pair * a.N * H;
+  int ocur = cbase;  // first row of the chunk whose outputs are written
+  __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(Op + (int64_t)cbase * H, (short)0, a.chunk * H * (int)sizeof(IoT), 0x00020000);
+  auto wload = [&](int j2, frag (&a0)[KS], frag (&a2)[KS]) {
+    const OpT* r0 = Wt + (j2 * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      a0[s] = M::load(r0 + s * M::KSTEP);
+      a2[s] = M::load(r0 + RH * LDW + s * M::KSTEP);
+    }
+  };
   auto pass = [&](int t0, const u32x4 (&qcur)[KS], u32x4 (&qnext)[KS]) {
     load_q(t0 + NW * 32, qnext);
     const int tw = t0 + 32 * w;
-    if (tw < oend) {
+    {
       frag qf[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = bf16x8_to_f16x8(qcur[s]);
-      f32x16 o[CB];
+      f32x16 o[CB];  // O^T: rows are output columns c*32.., columns the wave's 32 tokens
 #pragma unroll
       for (int c = 0; c < CB; ++c) zero(o[c]);
-#pragma unroll
-      for (int j2 = 0; j2 < NJB; ++j2) {
-        f32x16 c0, c2;
-        zero(c0);
-        zero(c2);
-        const OpT* r0 = Wt + (j2 * 32 + (lane & 31)) * LDW + (lane >> 5) * M::KSUB;
-        const OpT* r2 = r0 + RH * LDW;
+      f32x16 pu[2], pv[2];
+      {
+        frag a0[KS], a2[KS];
+        wload(0, a0, a2);
+        zero(pu[0]);
+        zero(pv[0]);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          c0 = M::mma(M::load(r0 + s * M::KSTEP), qf[s], c0);
-          c2 = M::mma(M::load(r2 + s * M::KSTEP), qf[s], c2);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float A = c0[r];
-          c0[r] = A * sigmoid_fast(A) * c2[r];
-        }
-        const OpT* sr = Ss + j2 * 32 * LD1;
-#pragma unroll
-        for (int q = 0; q < QS; ++q) {
-          const frag hf = acc_to_afrag<OpT>(c0, q);
-#pragma unroll
-          for (int c = 0; c < CB; ++c) o[c] = M::mma(hf, acc_kfrag_tr<OpT>(sr + c * 32, LD1, q, lane), o[c]);
+          pu[0] = M::mma(a0[s], qf[s], pu[0]);
+          pv[0] = M::mma(a2[s], qf[s], pv[0]);
         }
       }
-      // stage the wave's 32 x h output tile in LDS, then write whole 16-byte runs
-      if constexpr (sizeof(IoT) == 2) {
-        bf16_t* os = ost + w * 32 * (H + 8);
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
+      for (int j2 = 0; j2 < NJB; ++j2) {
+        f32x16& uc = pu[j2 & 1];
+        f32x16& vc = pv[j2 & 1];
+        f32x16& un = pu[(j2 + 1) & 1];
+        f32x16& vn = pv[(j2 + 1) & 1];
+        const bool nx = j2 + 1 < NJB;
+        frag a0[KS], a2[KS];
+        if (nx) wload(j2 + 1, a0, a2);
+        frag sf[QS][CB];
+        const OpT* sr = Ss + j2 * 32 * LD1;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) os[acc_row(r, lane) * (H + 8) + c * 32 + acc_col(lane)].bits = f32_to_bf16(o[c][r] + poison);
-        IoT* Op = reinterpret_cast<IoT*>(a.O) + (int64_t)pair * a.N * H;
+        for (int q = 0; q < QS; ++q)
 #pragma unroll
-        for (int i = lane; i < 32 * H / 8; i += 64) {
-          const int row = i / (H / 8), col = (i % (H / 8)) * 8;
-          if (tw + row < oend)
-            *reinterpret_cast<u32x4*>(Op + (int64_t)(tw + row) * H + col) =
-                *reinterpret_cast<const u32x4*>(os + row * (H + 8) + col);
+          for (int c = 0; c < CB; ++c) sf[q][c] = acc_kfrag_tr<OpT>(sr + c * 32, LD1, q, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        frag hf[QS];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float x0 = uc[r], x1 = uc[r + 1];
+          const float y0 = x0 * vc[r] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x0));
+          const float y1 = x1 * vc[r + 1] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x1));
+          const f16x2 h = f32x2_to_f16x2(y0, y1);
+          hf[r >> 3][r & 7] = h[0];
+          hf[r >> 3][(r & 7) + 1] = h[1];
         }
-      } else {
-        IoT* Op = reinterpret_cast<IoT*>(a.O) + (int64_t)pair * a.N * H;
+        if (nx) {
+          zero(un);
+          zero(vn);
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tt = tw + acc_row(r, lane);
-            if (tt < oend) Io<IoT>::store(Op + (int64_t)tt * H + c * 32 + acc_col(lane), o[c][r] + poison);
+          for (int s = 0; s < KS; ++s) {
+            un = M::mma(a0[s], qf[s], un);
+            vn = M::mma(a2[s], qf[s], vn);
           }
+        }
+#pragma unroll
+        for (int q = 0; q < QS; ++q)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) o[c] = M::mma(sf[q][c], hf[q], o[c]);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        if (nx) {
+#pragma unroll
+          for (int m = 0; m < 2 * KS; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 88 / (2 * KS), 0);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, QS * CB, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // stage the wave's 32 x h output tile in LDS (each lane holds four consecutive columns of a
+      // token row), then write whole 16-byte row runs; rows past the chunk end fall outside the
+      // store range and are dropped
+      bf16_t* os = ost + w * 32 * (H + 8) + (lane & 31) * (H + 8) + 4 * (lane >> 5);
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = f32x2_to_bf16x2_bits(o[c][4 * g], o[c][4 * g + 1]);
+          const uint32_t hi = f32x2_to_bf16x2_bits(o[c][4 * g + 2], o[c][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(os + c * 32 + 8 * g) = u32x2{lo, hi};
+        }
+      const bf16_t* ow = ost + w * 32 * (H + 8);
+#pragma unroll
+      for (int i = lane; i < 32 * H / 8; i += 64) {
+        const int row = i / (H / 8), col = (i % (H / 8)) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ow + row * (H + 8) + col);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, ((tw - ocur + row) * H + col) * (int)sizeof(IoT), 0, 0);
       }
     }
   };
-  // chunk i of the group reads S = run (+ its own aggregate when inclusive); run then advances by
-  // the chunk's aggregate (the last chunk's inclusive state is the group's inclusive prefix)
+  // chunk i of the group reads S = run + the group's partial sum through chunk i-1 (through chunk i
+  // when inclusive; the last chunk's inclusive state is then the group's inclusive prefix)
   int np = 0;  // passes so far: even passes read qa and prefetch into qb, odd ones the reverse
   for (int i = 0; i < G; ++i) {
+    const int slot = i - (a.inclusive ? 0 : 1);  // group partial sum through chunk `slot`
+    f32x4 part[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) part[k] = dev_load4(ra, (int)(((ch * G + (slot < 0 ? 0 : slot)) * n + 4 * (tid + NT * k)) * 4));
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
       const int e = 4 * (tid + NT * k);
       if (NS4 % NT != 0 && e >= 4 * NS4) continue;
-      const f32x4 nxt = i == G - 1 ? ginc[k] : run[k] + dev_load4(ra, (int)(((ch * G + i) * n + e) * 4));
-      const f32x4 sc = a.inclusive ? nxt : run[k];
+      f32x4 sc = slot < 0 ? run[k] : run[k] + part[k];
+      if (bad) sc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       const int j = e / H, c = e % H;
 #pragma unroll
       for (int q = 0; q < 4; ++q) Ss[j * LD1 + c + q] = M::from_f32(sc[q]);
-      run[k] = nxt;
     }
     __syncthreads();  // S of chunk i in LDS
-    const int c0 = cbase + i * a.chunk;
-    oend = c0 + a.chunk;
-    for (int t0 = c0; t0 < oend; t0 += NW * 32, ++np) {
+    ocur = cbase + i * a.chunk;
+    ro = __builtin_amdgcn_make_buffer_rsrc(Op + (int64_t)ocur * H, (short)0, a.chunk * H * (int)sizeof(IoT), 0x00020000);
+    for (int t0 = ocur; t0 < ocur + a.chunk; t0 += NW * 32, ++np) {
       if (np & 1)
         pass(t0, qb, qa);
       else
