@@ -383,7 +383,9 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   {
     // prefix = (inclusive prefix at `stop`, or W1) + aggregates stop+1 .. ch-1, left to right;
     // loads of eight aggregates are in flight together
-    f32x4 s[SPT];
+    f32x4 s[SPT], own[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) own[i] = dev_load4(ra, (int)(((ch * G + G - 1) * n + 4 * (tid + NT * i)) * 4));
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int e = 4 * (tid + NT * i);
@@ -406,9 +408,6 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 #pragma unroll
           for (int i = 0; i < SPT; ++i) s[i] += t[jj][i];
     }
-    f32x4 own[SPT];
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) own[i] = dev_load4(ra, (int)(((ch * G + G - 1) * n + 4 * (tid + NT * i)) * 4));
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int e = 4 * (tid + NT * i);
