@@ -34,6 +34,10 @@ CASES = [
     ("bf16 h256 r1", dict(h=256, r=1, N=256, chunk=128), 6),
     ("fp32 AU h64", dict(h=64, N=512, chunk=128, dtype=FP32), 7),
     ("fp32 UA h128 r1", dict(h=128, r=1, N=256, chunk=64, dtype=FP32, order=1), 8),
+    # single-pass kernel shapes: chunks shorter than one 64-token tile, one tile, rh = 4h
+    ("bf16 h32 r4 chunk 32", dict(h=32, r=4, N=320, chunk=32), 9),
+    ("bf16 h32 r4 UA chunk 160", dict(h=32, r=4, N=640, chunk=160, order=1), 10),
+    ("bf16 h64 one tile UA", dict(h=64, N=64, chunk=64, order=1), 11),
 ]
 
 
@@ -83,6 +87,23 @@ def test_grouped_chunks_many_pairs(lib, order):
     sel = lambda a: np.stack([a[b, h] for b, h in pairs])
     eo, es = max_abs_rel(sel(host(O)), sel(ref["O"])), max_abs_rel(sel(host(S)), sel(ref["S"]))
     print(f"grouped order={order} O={eo:.2e} S={es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+def test_eight_chunks_per_workgroup(lib):
+    """32 pairs x 64 chunks of 256 tokens: the single-pass kernel groups eight chunks per
+    workgroup (its largest group), so each workgroup stores seven partial sums before its
+    aggregate; sampled pairs against the oracle, apply-then-update order."""
+    p = LactProblem(B=4, H=8, h=64, r=2, Nq=16384, Nk=16384, chunk_q=256, chunk_kv=256, dtype=BF16,
+                    update_mask=UPD_W1, weight_norm=False)
+    announce("linattn eight chunks per workgroup B4 H8 N16384 chunk256")
+    x = make_lact_inputs(p, 450)
+    O, S = _lin_gpu(lib, p, x)
+    pairs = [(0, 1), (2, 4), (3, 7)]
+    ref = _lin_ref(p, x, pairs=pairs)
+    sel = lambda a: np.stack([a[b, h] for b, h in pairs])
+    eo, es = max_abs_rel(sel(host(O)), sel(ref["O"])), max_abs_rel(sel(host(S)), sel(ref["S"]))
+    print(f"eight chunks per group O={eo:.2e} S={es:.2e}")
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
