@@ -132,9 +132,9 @@ def test_runs_are_bitwise_deterministic(lib):
 
 
 def test_config2_full_size_sampled_pairs(lib):
-    """BASELINE's headline configuration (B4 H8 h128 r2, seq 32768, chunk 2048, momentum 0.9,
-    Muon, renorm) at full size in the benchmark's launch configuration; the oracle evaluates
-    three of the 32 independent pairs."""
+    """The LM-layer workload (B4 H8 h128 r2, seq 32768, chunk 2048, momentum 0.9, Muon, renorm)
+    at full size in the benchmark's launch configuration; the oracle evaluates three of the 32
+    independent pairs."""
     p = CONFIGS[2]
     announce("lact config2 full size")
     x = make_lact_inputs(p, 2)
