@@ -41,7 +41,8 @@ struct FusedArgs {
   const float* W1;          // [b][rh][h]
   void* O;                  // [pair][N][H]
   float* S_out;             // [pair][rh][h] final state, or null
-  float* agg;               // [pair][nch][rh*h] chunk aggregates (workspace)
+  float* agg;               // [pair][nch][rh*h] per group of G chunks: its partial sums at each chunk end,
+                            // the last one the group's aggregate (workspace)
   float* incl;              // [pair][nch][rh*h] inclusive prefixes (workspace)
   unsigned* flags;          // [pair][nch]: 1 aggregate published, 2 inclusive prefix published
   unsigned* tickets;        // [8] per-XCD work counters, then the error word at [8]
