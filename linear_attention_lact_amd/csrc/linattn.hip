@@ -232,7 +232,8 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   const size_t opsz = bf16 ? 2 : 4;
   // single pass for bf16 I/O and (h, rh) in {(32, 64), (32, 128), (64, 128)}
   const bool fused = bf16 && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
-                     (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31;  // buffer offsets are 32-bit
+                     (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31 &&  // buffer offsets are 32-bit
+                     (int64_t)q.N * q.h * 2 < (int64_t)1 << 31;
   WorkspacePlan plan;
   size_t oSh = 0, odS = 0, oSt = 0, oAgg = 0, oIncl = 0, oFl = 0, oTk = 0;
   if (fused) {
