@@ -156,7 +156,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
     u32x4 k[CPT], v[CPT];
     float e[CPT];
   };
-  constexpr int NPF = 4;
+  constexpr int NPF = 2;  // measured at the scan workload: as fast as 3 or 4 sets, fewer registers
   Staged sg4[NPF];
   const int gbytes = (cend - cbase) * H * (int)sizeof(IoT);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<IoT*>(Kp + (int64_t)cbase * H), (short)0, gbytes, 0x00020000);
