@@ -15,6 +15,15 @@ For the LaCT fast weight, phi(x) = silu(x W0) * (x W2) and the last layer is
 W1, so with the loss -eta <f(k), v> the value is g = eta v and a chunk adds
 dS_c = phi(K_c)^T diag(eta_c) V_c. Apply-then-update sees the exclusive prefix
 (S_c = W1 + sum_{j<c} dS_j); update-then-apply the inclusive one (j <= c).
+
+With momentum (same summary page, Theorem 5.3) the value written at step i is
+carried into every later state with the cumulative coefficient
+beta_{ji}, so the effective write is dS_i * sum_{j=i}^{t} beta_{ji}. Reading:
+one heavy-ball step per chunk with a constant coefficient alpha, so
+beta_{ji} = alpha^(j-i) and the state that chunk c reads is
+S_c = W1 + sum_{i<c} dS_i sum_{j=i}^{c-1} alpha^(j-i) (apply-then-update; the
+inner sums run to c, and i <= c, for update-then-apply). alpha = 0 gives the
+plain prefix above.
 """
 from __future__ import annotations
 
@@ -32,29 +41,42 @@ def phi(X: np.ndarray, W0: np.ndarray, W2: np.ndarray) -> np.ndarray:
     return A * (0.5 * (1.0 + np.tanh(0.5 * A))) * (X @ W2)
 
 
+def momentum_weight(c: int, i: int, alpha: float, order: int) -> float:
+    """Theorem 5.3's cumulative coefficient of chunk i's write in the state chunk c reads:
+    sum_{j=i}^{last} alpha^(j-i) with last = c-1 (apply-then-update) or c (update-then-apply);
+    zero when chunk i comes after that."""
+    last = c - 1 if order == APPLY_THEN_UPDATE else c
+    return float(sum(alpha ** (j - i) for j in range(i, last + 1)))
+
+
 def linattn_pair(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                 dtype=np.float64):
-    """Chunked linear attention for one pair. Returns (O, S_final)."""
+                 momentum: float = 0.0, dtype=np.float64):
+    """Chunked linear attention for one pair. Returns (O, S_final); S_final is the state
+    after the last chunk's write."""
     Q, K, V, eta, W0, W1, W2 = (np.asarray(a, dtype=dtype) for a in (Q, K, V, eta, W0, W1, W2))
     n_chunks = K.shape[0] // chunk
     dS = []
     for c in range(n_chunks):
         sl = slice(c * chunk, (c + 1) * chunk)
         dS.append(phi(K[sl], W0, W2).T @ (eta[sl, None] * V[sl]))
+
+    def state(c, ord_):
+        S = W1.copy()
+        for i in range(n_chunks):
+            w = momentum_weight(c, i, momentum, ord_)
+            if w != 0.0:
+                S = S + w * dS[i]
+        return S
+
     O = np.zeros((Q.shape[0], W1.shape[1]), dtype=dtype)
-    S = W1.copy()
     for c in range(n_chunks):
         sl = slice(c * chunk, (c + 1) * chunk)
-        if order == UPDATE_THEN_APPLY:
-            S = S + dS[c]
-        O[sl] = phi(Q[sl], W0, W2) @ S
-        if order == APPLY_THEN_UPDATE:
-            S = S + dS[c]
-    return O, S
+        O[sl] = phi(Q[sl], W0, W2) @ state(c, order)
+    return O, state(n_chunks - 1, UPDATE_THEN_APPLY) if n_chunks else W1.copy()
 
 
 def linattn_forward(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                    pairs=None, dtype=np.float64) -> Dict[str, np.ndarray]:
+                    momentum: float = 0.0, pairs=None, dtype=np.float64) -> Dict[str, np.ndarray]:
     """All pairs. Q/K/V [B,H,N,h], eta [B,H,N], W0/W2 [H,h,rh], W1 [H,rh,h]
     (or [B,H,...] per sequence). Returns O [B,H,N,h] and S [B,H,rh,h]."""
     B, H, N, h = Q.shape
@@ -66,15 +88,16 @@ def linattn_forward(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_
     for (b, hd) in todo:
         w0, w1, w2 = ((w[b, hd] if per_seq else w[hd]) for w in (W0, W1, W2))
         O[b, hd], S[b, hd] = linattn_pair(Q[b, hd], K[b, hd], V[b, hd], eta[b, hd], w0, w1, w2,
-                                          chunk=chunk, order=order, dtype=dtype)
+                                          chunk=chunk, order=order, momentum=momentum, dtype=dtype)
     return dict(O=O, S=S)
 
 
 def linattn_masked_quadratic(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                             dtype=np.float64) -> np.ndarray:
+                             momentum: float = 0.0, dtype=np.float64) -> np.ndarray:
     """The parallel matrix form for one pair on small N:
     O = phi(Q) W1 + (M * phi(Q) phi(K)^T) diag(eta) V with the chunk mask
-    M[t, s] = 1 iff chunk(s) < chunk(t) (apply-then-update) or <= (update-then-apply).
+    M[t, s] = 1 iff chunk(s) < chunk(t) (apply-then-update) or <= (update-then-apply);
+    with momentum M[t, s] is the cumulative coefficient of chunk(s) seen from chunk(t).
 
     Press article, section 4: the parallel form built from a block mask, a
     learning-rate vector and scaled values.
@@ -82,6 +105,9 @@ def linattn_masked_quadratic(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int
     Q, K, V, eta, W0, W1, W2 = (np.asarray(a, dtype=dtype) for a in (Q, K, V, eta, W0, W1, W2))
     ct = np.arange(Q.shape[0]) // chunk
     cs = np.arange(K.shape[0]) // chunk
-    mask = (cs[None, :] < ct[:, None]) if order == APPLY_THEN_UPDATE else (cs[None, :] <= ct[:, None])
+    if momentum == 0.0:
+        mask = (cs[None, :] < ct[:, None]) if order == APPLY_THEN_UPDATE else (cs[None, :] <= ct[:, None])
+    else:
+        mask = np.array([[momentum_weight(a, b, momentum, order) for b in cs] for a in ct])
     pq, pk = phi(Q, W0, W2), phi(K, W0, W2)
     return pq @ W1 + (mask * (pq @ pk.T)) @ (eta[:, None] * V)
