@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--momentum", type=float, default=0.0,
+                    help="scan workload only: heavy-ball momentum per chunk (the momentum form)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -80,7 +82,7 @@ def cpu_baseline_linattn(p, x, budget_s):
     pairs = [(b, h) for b in range(p.B) for h in range(p.H)]
     for (b, h) in pairs:
         LA.linattn_pair(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["eta"][b, h], x["W0"][h], x["W1"][h],
-                        x["W2"][h], chunk=p.chunk_kv, order=p.order, dtype=np.float32)
+                        x["W2"][h], chunk=p.chunk_kv, order=p.order, momentum=p.momentum, dtype=np.float32)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -175,6 +177,14 @@ def main():
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
     k = args.config
     p = CONFIGS[k]
+    stem = PROFILE_STEMS[k]
+    if args.momentum != 0.0:
+        if k != 1:
+            print("--momentum applies to the scan workload (--config 1) only", file=sys.stderr)
+            sys.exit(2)
+        from dataclasses import replace
+        p = replace(p, momentum=args.momentum)
+        stem = "linattn_scan_momentum_b4h8_h64_seq8192_chunk512"
     if k == 4:
         x = make_inplace_inputs(p, k)
         Hs, Wg, Wu, Vb = (t(x[n], torch.bfloat16) for n in ("Hs", "W_gate", "W_up", "Vbar"))
@@ -199,7 +209,8 @@ def main():
         W0, W1, W2 = (t(x[n], torch.float32) for n in ("W0", "W1", "W2"))
         if k == 1:
             def step():
-                return ttt.linattn_forward(Q, K, V, eta, W0, W2, W1, chunk=p.chunk_kv, order=p.order, stream=stream)
+                return ttt.linattn_forward(Q, K, V, eta, W0, W2, W1, chunk=p.chunk_kv, order=p.order,
+                                           momentum=p.momentum, stream=stream)
             flops = acc.linattn_flops(p.B, p.H, p.Nk, p.h, p.r)
             nbytes = acc.linattn_bytes(p.B, p.H, p.Nk, p.h, p.r)
             P, rh, nch = p.B * p.H, p.rh, p.Nk // p.chunk_kv
@@ -209,6 +220,8 @@ def main():
                     "linattn_fused": nbytes}
             bound, peak, unit = "hbm", acc.PEAK_HBM_GBS, "GB/s"
             metric = "linear-attention scan form tokens/sec (h=64, r=2, chunk 512), bf16; % of HBM roofline"
+            if p.momentum:
+                metric = metric.replace("scan form", f"scan form with momentum {p.momentum:g}")
         else:
             def step():
                 return ttt.lact_forward(Q, K, V, eta, W0, W1, W2, chunk_q=p.chunk_q, chunk_kv=p.chunk_kv,
@@ -234,6 +247,9 @@ def main():
                "order": "apply-then-update" if p.order == 0 else "update-then-apply"}
         if k != 1:
             cfg.update({"momentum": p.momentum, "muon": p.muon, "weight_norm": p.weight_norm})
+        elif p.momentum:
+            cfg["workload"] += f" + momentum {p.momentum:g}"
+            cfg["momentum"] = p.momentum
     cfg["parallelism"] = "single GPU"
 
     if args.copy_calibration:
@@ -246,7 +262,7 @@ def main():
     ms = time_steps(step, args.steps, args.warmup, stream)
     kern = kernel_breakdown(ttt, step, args.steps)
     roof = roofline(kern, work, bound, peak, unit)
-    roof["traffic"] = acc.profiled_traffic(ROOT, roof["kernel"], PROFILE_STEMS[k])
+    roof["traffic"] = acc.profiled_traffic(ROOT, roof["kernel"], stem)
     out = {
         "metric": metric,
         "value": round(tokens / (ms * 1e-3), 1),

@@ -150,6 +150,12 @@ ttt_status ttt_lact_forward(const ttt_lact_params* p,
  * Per pair and chunk c: phi(X) = silu(X W0) * (X W2), dS_c = phi(K_c)^T diag(eta_c) V_c,
  *   S_c = W1 + sum_{j<c} dS_j (TTT_APPLY_THEN_UPDATE) or sum_{j<=c} (TTT_UPDATE_THEN_APPLY),
  *   O_c = phi(Q_c) S_c.
+ * With momentum alpha (same summary page, Theorem 5.3, read as one heavy-ball step per chunk
+ * with a constant coefficient): chunk j's write enters S_c with the cumulative coefficient
+ * sum_{i=j}^{last} alpha^(i-j), last = c-1 (apply-then-update) or c (update-then-apply);
+ * equivalently M_j = alpha M_{j-1} + dS_j, W_{j+1} = W_j + M_j. 0 <= momentum < 1, else
+ * TTT_ERR_ARG; momentum 0 is the plain scan (single-pass kernel where the shape allows;
+ * a momentum other than 0 always takes the multi-launch path).
  * Arguments: Q, K, V [B, H, N, h] I/O dtype; eta [B, H, N] float32; W0, W2 [H, h, rh] and
  * W1 [H, rh, h] float32 (or [B, H, ...] with w_batch_stride as above); O [B, H, N, h] I/O
  * dtype; S_out [B, H, rh, h] float32, nullable: the state after the last chunk.
@@ -161,6 +167,7 @@ typedef struct {
   int32_t order;
   int32_t dtype;
   int64_t w_batch_stride;
+  float momentum;        /* heavy-ball coefficient alpha per chunk; 0: none */
 } ttt_linattn_params;
 
 ttt_status ttt_linattn_forward(const ttt_linattn_params* p,

@@ -45,7 +45,7 @@ class LactParams(ctypes.Structure):
 class LinattnParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("chunk", ctypes.c_int32), ("order", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("w_batch_stride", ctypes.c_int64)]
+                ("dtype", ctypes.c_int32), ("w_batch_stride", ctypes.c_int64), ("momentum", ctypes.c_float)]
 
 
 class InplaceParams(ctypes.Structure):
@@ -218,9 +218,10 @@ def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[i
 
 
 def linattn_forward(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                    want_state: bool = True, stream=None):
+                    momentum: float = 0.0, want_state: bool = True, stream=None):
     """Last-layer-only linear-attention scan. Q/K/V [B,H,N,h], eta [B,H,N], W0/W2 [(B,)H,h,rh],
-    W1 [(B,)H,rh,h]. Returns (O, S_out) with S_out [B,H,rh,h] (None if not want_state)."""
+    W1 [(B,)H,rh,h]; momentum: heavy-ball coefficient per chunk (0 <= momentum < 1).
+    Returns (O, S_out) with S_out [B,H,rh,h] (None if not want_state)."""
     torch = _torch()
     lib = load()
     B, H, N, h = Q.shape
@@ -236,7 +237,8 @@ def linattn_forward(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_
         raise ValueError("Q/K/V must share [B,H,N,h] and eta be [B,H,N]")
     if rh % h:
         raise ValueError("rh must be a multiple of h")
-    p = LinattnParams(B, H, N, h, rh // h, chunk, order, _io_dtype(Q), H * h * rh if per_seq else 0)
+    p = LinattnParams(B, H, N, h, rh // h, chunk, order, _io_dtype(Q), H * h * rh if per_seq else 0,
+                      float(momentum))
     O = torch.empty_like(Q)
     S = torch.empty((B, H, rh, h), dtype=torch.float32, device=dev) if want_state else None
     base = [ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(eta), _ptr(W0), _ptr(W2), _ptr(W1), _ptr(O), _ptr(S)]

@@ -6,6 +6,7 @@
 // details"; press article, section 4). Per pair:
 //   dS_c = phi(K_c)^T diag(eta_c) V_c                    (grad_kernel, linear-attention mode)
 //   S_c  = W1 + sum_{j<c} dS_j   (apply-then-update)  or  sum_{j<=c} (update-then-apply)
+//          (with momentum, each dS_j weighted by its cumulative coefficient, Theorem 5.3)
 //   O_c  = phi(Q_c) S_c                                   (apply_kernel with per-chunk S_c)
 // The chunk prefix is an exclusive (or inclusive) scan over the chunks of each pair.
 #include "fastweight.hpp"
@@ -15,41 +16,67 @@
 
 namespace ttt {
 
-// Operand shadows W0T, W2T [rh][h] per pair from the row-form W0, W2 [h][rh].
+// Operand shadows W0T, W2T [rh][h] per pair from the row-form W0, W2 [h][rh]: one 32 x 32
+// tile per workgroup, read along rows of W and written along rows of W^T through LDS.
+// grid (rh/32 * h/32, 2, P), block 256 (each thread 4 elements).
 template <class OpT>
-__global__ void __launch_bounds__(256) linattn_prep_kernel(const float* W0, const float* W2, OpT* sh, int H,
-                                                          int h, int rh, int64_t w_batch_stride) {
-  const int mat = blockIdx.x, pair = blockIdx.y;
+__global__ void __launch_bounds__(256) linattn_prep_kernel(const float* __restrict__ W0, const float* __restrict__ W2,
+                                                          OpT* __restrict__ sh, int H, int h, int rh,
+                                                          int64_t w_batch_stride) {
+  __shared__ float tile[32][33];
+  const int mat = blockIdx.y, pair = blockIdx.z;
+  const int tj = blockIdx.x % (rh / 32), tc = blockIdx.x / (rh / 32);  // tile of j (rh) and c (h)
   const int b = pair / H, head = pair % H;
   const int64_t n = (int64_t)rh * h;
   const float* src = (mat == 0 ? W0 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
   OpT* dst = sh + ((int64_t)pair * 2 + mat) * n;
-  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
-    const int j = (int)(e / h), c = (int)(e % h);
-    dst[e] = Mfma<OpT>::from_f32(src[(int64_t)c * rh + j]);
-  }
+  const int x = threadIdx.x % 32, y = threadIdx.x / 32;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tile[y + 8 * k][x] = src[(int64_t)(tc * 32 + y + 8 * k) * rh + tj * 32 + x];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    dst[(int64_t)(tj * 32 + y + 8 * k) * h + tc * 32 + x] = Mfma<OpT>::from_f32(tile[x][y + 8 * k]);
 }
 
 // Chunk prefix scan, one thread per state element [j][c]: writes S_c per chunk as an operand
-// shadow, [rh][h] (ROWS) or transposed [h][rh], and optionally the final state.
+// shadow, [rh][h] (ROWS) or transposed [h][rh], and optionally the final state. With a
+// momentum coefficient alpha each chunk's write passes through the heavy-ball buffer
+// m <- alpha m + dS_k, s <- s + m, which gives chunk k's write the cumulative coefficient
+// sum_{i>=k} alpha^(i-k) of Theorem 5.3; alpha = 0 leaves m = dS_k, the plain prefix.
 // grid (ceil(rh*h/256), P), block 256.
 template <class OpT, bool ROWS>
-__global__ void __launch_bounds__(256) linattn_scan_kernel(const float* W1, const float* dS, OpT* St, float* S_out,
+__global__ void __launch_bounds__(256) linattn_scan_kernel(const float* __restrict__ W1, const float* __restrict__ dS,
+                                                          OpT* __restrict__ St, float* __restrict__ S_out,
                                                           int H, int h, int rh, int nch, int inclusive,
-                                                          int64_t w_batch_stride) {
+                                                          float alpha, int64_t w_batch_stride) {
   const int pair = blockIdx.y;
   const int64_t n = (int64_t)rh * h;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
   const int b = pair / H, head = pair % H;
   const int j = (int)(e / h), c = (int)(e % h);
-  float s = W1[(int64_t)b * w_batch_stride + (int64_t)head * n + e];
+  float s = W1[(int64_t)b * w_batch_stride + (int64_t)head * n + e], m = 0.f;
   const float* d = dS + (int64_t)pair * nch * n + e;
   OpT* o = St + (int64_t)pair * nch * n + (ROWS ? e : (int64_t)c * rh + j);
-  for (int k = 0; k < nch; ++k) {
-    if (inclusive) s += d[k * n];
-    o[k * n] = Mfma<OpT>::from_f32(s);
-    if (!inclusive) s += d[k * n];
+  // the chunk increments are loaded eight at a time so that their latencies overlap
+  for (int k0 = 0; k0 < nch; k0 += 8) {
+    float dk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dk[u] = k0 + u < nch ? d[(int64_t)(k0 + u) * n] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (k0 + u >= nch) break;
+      if (inclusive) {
+        m = fmaf(alpha, m, dk[u]);
+        s += m;
+      }
+      o[(int64_t)(k0 + u) * n] = Mfma<OpT>::from_f32(s);
+      if (!inclusive) {
+        m = fmaf(alpha, m, dk[u]);
+        s += m;
+      }
+    }
   }
   if (S_out) S_out[(int64_t)pair * n + e] = s;
 }
@@ -82,8 +109,8 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
 
   {
     LaunchTimer lt(K_LIN_PREP, st);
-    hipLaunchKernelGGL(linattn_prep_kernel<OpT>, dim3(2, P), dim3(256), 0, st, W0, W2, sh, p.H, H, rh,
-                       p.w_batch_stride);
+    hipLaunchKernelGGL(linattn_prep_kernel<OpT>, dim3((unsigned)((rh / 32) * (H / 32)), 2, P), dim3(256), 0, st,
+                       W0, W2, sh, p.H, H, rh, p.w_batch_stride);
     TTT_HIP(hipGetLastError());
   }
   GradArgs ga{};
@@ -118,7 +145,8 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
     LaunchTimer lt(K_LIN_SCAN, st);
     auto sk = linattn_scan_kernel<OpT, ARD>;
     hipLaunchKernelGGL(sk, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
-                       St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.w_batch_stride);
+                       St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.momentum,
+                       p.w_batch_stride);
     TTT_HIP(hipGetLastError());
   }
   ApplyArgs aa{};
@@ -219,6 +247,7 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   if (q.order != TTT_APPLY_THEN_UPDATE && q.order != TTT_UPDATE_THEN_APPLY) return TTT_ERR_ARG;
   if (q.dtype != TTT_FP32 && q.dtype != TTT_BF16) return TTT_ERR_ARG;
   if (q.w_batch_stride < 0) return TTT_ERR_ARG;
+  if (!(q.momentum >= 0.f && q.momentum < 1.f)) return TTT_ERR_ARG;  // also rejects NaN
   if (q.N % q.chunk) return TTT_ERR_SHAPE;
   const int64_t rh64 = (int64_t)q.r * q.h;
   if (q.h % 32 || rh64 % 64 || rh64 > 1024) return TTT_ERR_SHAPE;
@@ -230,8 +259,8 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   if (P > 0 && nch > 0 && (!Q || !K || !V || !eta || !O)) return TTT_ERR_ARG;
   const int64_t n = rh64 * q.h;
   const size_t opsz = bf16 ? 2 : 4;
-  // single pass for bf16 I/O and (h, rh) in {(32, 64), (32, 128), (64, 128)}
-  const bool fused = bf16 && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
+  // single pass for bf16 I/O, no momentum and (h, rh) in {(32, 64), (32, 128), (64, 128)}
+  const bool fused = bf16 && q.momentum == 0.f && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
                      (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31 &&  // buffer offsets are 32-bit
                      (int64_t)q.N * q.h * 2 < (int64_t)1 << 31;
   WorkspacePlan plan;

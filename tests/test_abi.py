@@ -130,6 +130,17 @@ def test_linattn_query_and_validation(lib):
     assert _lin(lib, dtype=ttt.FP32, h=256)[0] == ttt.TTT_ERR_UNSUPPORTED
 
 
+def test_linattn_momentum_validation(lib):
+    for bad in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert _lin(lib, momentum=bad)[0] == ttt.TTT_ERR_ARG, bad
+    st0, single_pass = _lin(lib)
+    st1, multi = _lin(lib, momentum=0.9)
+    assert st0 == st1 == ttt.TTT_OK
+    # momentum takes the multi-launch path, whose workspace holds per-chunk states
+    assert multi != single_pass and multi > 0
+    assert ctypes.sizeof(ttt.LinattnParams) == 48
+
+
 def _inp(lib, **kw):
     base = dict(B=1, N=32768, d_model=4096, d_hidden=14336, chunk=1024, eta=1e-3, dtype=ttt.BF16,
                 wdown_batch_stride=0)

@@ -16,13 +16,14 @@ def _lin_gpu(lib, p, x, V=None, eta=None):
     return lib.linattn_forward(dev(x["Q"], io), dev(x["K"], io), dev(x["V"] if V is None else V, io),
                                dev(x["eta"] if eta is None else eta, torch.float32),
                                dev(x["W0"], torch.float32), dev(x["W2"], torch.float32),
-                               dev(x["W1"], torch.float32), chunk=p.chunk_kv, order=p.order)
+                               dev(x["W1"], torch.float32), chunk=p.chunk_kv, order=p.order,
+                               momentum=p.momentum)
 
 
 def _lin_ref(p, x, pairs=None, V=None):
     from oracle import linattn as LA
     return LA.linattn_forward(x["Q"], x["K"], x["V"] if V is None else V, x["eta"], x["W0"], x["W1"], x["W2"],
-                              chunk=p.chunk_kv, order=p.order, pairs=pairs)
+                              chunk=p.chunk_kv, order=p.order, momentum=p.momentum, pairs=pairs)
 
 
 CASES = [
@@ -144,3 +145,66 @@ def test_gradient_ascent_is_a_value_sign_flip(lib, dtype):
     print(f"ascent flip ({dtype}) {err:.2e}")
     assert err <= tol
     assert max_abs_rel(op, o0) > 0.05  # the writes are visible
+
+
+MOMENTUM_CASES = [
+    ("bf16 AU h64 a0.9", dict(h=64, N=1024, chunk=128, momentum=0.9), 21),
+    ("bf16 UA h32 r4 a0.5", dict(h=32, r=4, N=640, chunk=160, order=1, momentum=0.5), 22),
+    ("bf16 h128 ragged tile a0.9", dict(h=128, N=480, chunk=96, momentum=0.9), 23),
+    ("fp32 AU h64 a0.9", dict(h=64, N=512, chunk=64, dtype=FP32, momentum=0.9), 24),
+    ("fp32 UA h32 a0.99", dict(h=32, N=512, chunk=32, dtype=FP32, order=1, momentum=0.99), 25),
+]
+
+
+@pytest.mark.parametrize("label,kw,seed", MOMENTUM_CASES, ids=[c[0] for c in MOMENTUM_CASES])
+def test_momentum_cases(lib, label, kw, seed):
+    """Theorem 5.3's momentum form (heavy-ball per chunk) against the oracle's cumulative
+    coefficients, plain and with eta x100 so that the momentum-weighted writes dominate."""
+    kw = dict(kw)
+    N, chunk = kw.pop("N"), kw.pop("chunk")
+    base = dict(B=2, H=2, h=64, r=2, Nq=N, Nk=N, chunk_q=chunk, chunk_kv=chunk, dtype=BF16,
+                update_mask=UPD_W1, weight_norm=False)
+    base.update(kw)
+    p = LactProblem(**base)
+    announce(f"linattn momentum {label}")
+    for variant, xs in (("plain", dict()), ("eta x100", dict(eta_scale=1.0))):
+        x = make_lact_inputs(p, 500 + seed, **xs)
+        O, S = _lin_gpu(lib, p, x)
+        ref = _lin_ref(p, x)
+        eo, es = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(S), ref["S"])
+        print(f"{label} [{variant}] O={eo:.2e} S={es:.2e}", flush=True)
+        tol = BF16_TOL if p.dtype == BF16 else FP32_TOL
+        assert eo <= tol and es <= tol, (variant, eo, es)
+
+
+def test_momentum_config1_shape(lib):
+    """The scan workload's shape (B4 H8 h64 r2, 8192 tokens, chunks of 512) with momentum 0.9,
+    sampled pairs against the oracle; and the same inputs without momentum differ."""
+    from dataclasses import replace
+    p = replace(CONFIGS[1], momentum=0.9)
+    announce("linattn momentum 0.9 at B4 H8 h64 r2 N8192 chunk512")
+    x = make_lact_inputs(p, 1)
+    O, S = _lin_gpu(lib, p, x)
+    pairs = [(0, 0), (1, 3), (3, 7)]
+    ref = _lin_ref(p, x, pairs=pairs)
+    sel = lambda a: np.stack([a[b, h] for b, h in pairs])
+    eo, es = max_abs_rel(sel(host(O)), sel(ref["O"])), max_abs_rel(sel(host(S)), sel(ref["S"]))
+    print(f"momentum config1 shape O={eo:.2e} S={es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+    O0, _ = _lin_gpu(lib, replace(p, momentum=0.0), x)
+    assert max_abs_rel(host(O), host(O0)) > 1e-3
+
+
+def test_momentum_scan_equals_recurrent_layer_on_gpu(lib):
+    """Theorem 5.3 on the device: the LaCT layer writing only W1 with heavy-ball momentum 0.9,
+    without renormalisation or Muon, gives the momentum scan form's outputs."""
+    for order in (0, 1):
+        p = LactProblem(B=2, H=2, h=64, r=2, Nq=1024, Nk=1024, chunk_q=256, chunk_kv=256, dtype=BF16,
+                        update_mask=UPD_W1, weight_norm=False, momentum=0.9, order=order)
+        announce(f"linattn momentum vs recurrent layer order={order}")
+        x = make_lact_inputs(p, 310 + order, eta_scale=1.0)
+        Ol, _ = _lin_gpu(lib, p, x)
+        Or = lact_on_gpu(lib, p, x)[0]
+        err = max_abs_rel(host(Ol), host(Or))
+        print(f"order {order}: momentum scan vs recurrent {err:.2e}")
+        assert err <= BF16_TOL
