@@ -208,3 +208,19 @@ def test_momentum_scan_equals_recurrent_layer_on_gpu(lib):
         err = max_abs_rel(host(Ol), host(Or))
         print(f"order {order}: momentum scan vs recurrent {err:.2e}")
         assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("momentum", [0.0, 0.9])
+def test_no_learning_rate_variant(lib, momentum):
+    """The simplification without a per-token learning rate (summary page, step 4): eta = 1
+    for every token, through the single-pass kernel (momentum 0) and the multi-launch path."""
+    p = LactProblem(B=2, H=2, h=64, r=2, Nq=1024, Nk=1024, chunk_q=256, chunk_kv=256, dtype=BF16,
+                    update_mask=UPD_W1, weight_norm=False, momentum=momentum)
+    announce(f"linattn eta = 1 momentum={momentum}")
+    x = make_lact_inputs(p, 600)
+    x["eta"] = np.ones_like(x["eta"])
+    O, S = _lin_gpu(lib, p, x)
+    ref = _lin_ref(p, x)
+    eo, es = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(S), ref["S"])
+    print(f"eta=1 momentum={momentum} O={eo:.2e} S={es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
