@@ -154,8 +154,8 @@ ttt_status ttt_lact_forward(const ttt_lact_params* p,
  * with a constant coefficient): chunk j's write enters S_c with the cumulative coefficient
  * sum_{i=j}^{last} alpha^(i-j), last = c-1 (apply-then-update) or c (update-then-apply);
  * equivalently M_j = alpha M_{j-1} + dS_j, W_{j+1} = W_j + M_j. 0 <= momentum < 1, else
- * TTT_ERR_ARG; momentum 0 is the plain scan (single-pass kernel where the shape allows;
- * a momentum other than 0 always takes the multi-launch path).
+ * TTT_ERR_ARG; momentum 0 is the plain scan. With momentum the workspace holds one more
+ * [B*H, N/chunk, rh, h] float32 region on the single-pass path.
  * Arguments: Q, K, V [B, H, N, h] I/O dtype; eta [B, H, N] float32; W0, W2 [H, h, rh] and
  * W1 [H, rh, h] float32 (or [B, H, ...] with w_batch_stride as above); O [B, H, N, h] I/O
  * dtype; S_out [B, H, rh, h] float32, nullable: the state after the last chunk.

@@ -182,12 +182,12 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
 }
 
 // Single-pass path (linattn_fused.hpp) for rh <= 128.
-template <class IoT, class OpT, int H, int RH>
-static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_t oAgg, size_t oIncl, size_t oFl,
-                                    size_t oTk, const void* Q, const void* K, const void* V, const float* eta,
-                                    const float* W0, const float* W2, const float* W1, void* O, float* S_out,
-                                    hipStream_t st) {
-  auto fk = linattn_fused_kernel<IoT, OpT, H, RH>;
+template <class IoT, class OpT, int H, int RH, bool MOM>
+static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_t oAgg, size_t oIncl, size_t oInclM,
+                                    size_t oFl, size_t oTk, const void* Q, const void* K, const void* V,
+                                    const float* eta, const float* W0, const float* W2, const float* W1, void* O,
+                                    float* S_out, hipStream_t st) {
+  auto fk = linattn_fused_kernel<IoT, OpT, H, RH, MOM>;
   constexpr int lds = linattn_fused_lds_bytes<OpT, H, RH>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = allow_lds(fk, lds);
@@ -205,6 +205,8 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
   fa.S_out = S_out;
   fa.agg = reinterpret_cast<float*>(ws + oAgg);
   fa.incl = reinterpret_cast<float*>(ws + oIncl);
+  fa.inclm = MOM ? reinterpret_cast<float*>(ws + oInclM) : nullptr;
+  fa.alpha = p.momentum;
   fa.flags = reinterpret_cast<unsigned*>(ws + oFl);
   fa.tickets = reinterpret_cast<unsigned*>(ws + oTk);
   fa.P = P;
@@ -259,15 +261,17 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   if (P > 0 && nch > 0 && (!Q || !K || !V || !eta || !O)) return TTT_ERR_ARG;
   const int64_t n = rh64 * q.h;
   const size_t opsz = bf16 ? 2 : 4;
-  // single pass for bf16 I/O, no momentum and (h, rh) in {(32, 64), (32, 128), (64, 128)}
-  const bool fused = bf16 && q.momentum == 0.f && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
+  // single pass for bf16 I/O and (h, rh) in {(32, 64), (32, 128), (64, 128)}
+  const bool fused = bf16 && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
                      (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31 &&  // buffer offsets are 32-bit
                      (int64_t)q.N * q.h * 2 < (int64_t)1 << 31;
   WorkspacePlan plan;
-  size_t oSh = 0, odS = 0, oSt = 0, oAgg = 0, oIncl = 0, oFl = 0, oTk = 0;
+  size_t oSh = 0, odS = 0, oSt = 0, oAgg = 0, oIncl = 0, oInclM = 0, oFl = 0, oTk = 0;
+  const bool mom = q.momentum != 0.f;
   if (fused) {
     oAgg = plan.add((size_t)P * nch * n * 4);
     oIncl = plan.add((size_t)P * nch * n * 4);
+    if (mom) oInclM = plan.add((size_t)P * nch * n * 4);
     oFl = plan.add((size_t)P * nch * 4);
     oTk = plan.add(16 * 4);
   } else {
@@ -293,9 +297,12 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   char* ws = static_cast<char*>(workspace);
   if (fused) {
     try {
-#define TTT_FUSED(IOT, OPT, HH, RR) \
-  if (q.h == HH && rh64 == RR)      \
-    return linattn_fused_run<IOT, OPT, HH, RR>(q, ws, oAgg, oIncl, oFl, oTk, Q, K, V, eta, W0, W2, W1, O, S_out, st);
+#define TTT_FUSED(IOT, OPT, HH, RR)                                                                         \
+  if (q.h == HH && rh64 == RR)                                                                              \
+    return mom ? linattn_fused_run<IOT, OPT, HH, RR, true>(q, ws, oAgg, oIncl, oInclM, oFl, oTk, Q, K, V, eta, \
+                                                           W0, W2, W1, O, S_out, st)                        \
+               : linattn_fused_run<IOT, OPT, HH, RR, false>(q, ws, oAgg, oIncl, oInclM, oFl, oTk, Q, K, V,  \
+                                                            eta, W0, W2, W1, O, S_out, st);
       TTT_FUSED(bf16_t, _Float16, 32, 64)
       TTT_FUSED(bf16_t, _Float16, 32, 128)
       TTT_FUSED(bf16_t, _Float16, 64, 128)

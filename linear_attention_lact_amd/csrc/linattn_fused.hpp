@@ -44,6 +44,8 @@ struct FusedArgs {
   float* agg;               // [pair][nch][rh*h] per group of G chunks: its partial sums at each chunk end,
                             // the last one the group's aggregate (workspace)
   float* incl;              // [pair][nch][rh*h] inclusive prefixes (workspace)
+  float* inclm;             // [pair][nch][rh*h] momentum at each inclusive prefix (with momentum)
+  float alpha;              // heavy-ball coefficient per chunk (with momentum)
   unsigned* flags;          // [pair][nch]: 1 aggregate published, 2 inclusive prefix published
   unsigned* tickets;        // [8] per-XCD work counters, then the error word at [8]
   int P, heads, N, chunk, nch, inclusive;
@@ -96,7 +98,13 @@ template <class OpT, int H, int RH>
 constexpr int linattn_fused_lds_bytes() { return FusedLayout<OpT, H, RH>::bytes; }
 
 // grid: 8 * ceil(P / 8) * (nch / G) workgroups; block NT = 128 * RH / 32 threads.
-template <class IoT, class OpT, int H, int RH>
+// MOM: heavy-ball momentum per chunk. The carried state is then the pair (S, m): a group of G
+// chunks with partial sums P_0..P_{G-1} maps it to (S + A_S + sigma_G m, alpha^G m + A_m), with
+// A_S = sum_j alpha^(G-1-j) P_j, A_m = sum_j alpha^(G-1-j) (P_j - P_{j-1}) and
+// sigma_L = alpha + ... + alpha^L; the state after L of the group's chunks is
+// S + sigma_L m + sum_{j<L} alpha^(L-1-j) P_j. Readers rebuild these sums from the stored
+// partial sums, so the aggregate phase is the same as without momentum.
+template <class IoT, class OpT, int H, int RH, bool MOM = false>
 __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArgs a) {
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
@@ -380,8 +388,69 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   const bool bad = ctl[2] != 0;
   const __amdgpu_buffer_rsrc_t ra = dev_rsrc(aggp, (int)(a.nch * n * 4));
   const __amdgpu_buffer_rsrc_t ri = dev_rsrc(inclp, (int)(a.nch * n * 4));
-  f32x4 run[SPT];  // state before the group
-  {
+  f32x4 run[SPT];                // state before the group
+  f32x4 mrun[MOM ? SPT : 1];     // momentum before the group
+  const float al = a.alpha;
+  if constexpr (MOM) {
+    // (S, m) = the inclusive prefix at `stop` (or (W1, 0)), then the groups stop+1 .. ch in
+    // order, each through its affine map rebuilt from its G partial sums (loaded together)
+    const __amdgpu_buffer_rsrc_t rim = dev_rsrc(a.inclm + (int64_t)pair * a.nch * n, (int)(a.nch * n * 4));
+    float aG = 1.f, sG = 0.f;
+    for (int k = 0; k < G; ++k) {
+      aG *= al;
+      sG += aG;
+    }
+    f32x4 s[SPT], m[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int e = 4 * (tid + NT * i);
+      if (NS4 % NT != 0 && e >= 4 * NS4) continue;
+      s[i] = stop >= 0 ? dev_load4(ri, (int)((stop * n + e) * 4)) : *reinterpret_cast<const f32x4*>(W1p + e);
+      m[i] = stop >= 0 ? dev_load4(rim, (int)((stop * n + e) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int g = stop + 1; g <= ch; ++g) {
+      f32x4 pj[8][SPT];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < SPT; ++i)
+          pj[j][i] = j < G ? dev_load4(ra, (int)(((g * G + j) * n + 4 * (tid + NT * i)) * 4))
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 aw[SPT], am[SPT];
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        aw[i] = pj[0][i];
+        am[i] = pj[0][i];
+      }
+#pragma unroll
+      for (int j = 1; j < 8; ++j)
+        if (j < G)
+#pragma unroll
+          for (int i = 0; i < SPT; ++i) {
+            aw[i] = al * aw[i] + pj[j][i];
+            am[i] = al * am[i] + (pj[j][i] - pj[j - 1][i]);
+          }
+      if (g == ch)
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+          run[i] = s[i];
+          mrun[i] = m[i];
+        }
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        s[i] = s[i] + aw[i] + sG * m[i];
+        m[i] = aG * m[i] + am[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int e = 4 * (tid + NT * i);
+      if (NS4 % NT != 0 && e >= 4 * NS4) continue;
+      *reinterpret_cast<f32x4*>(inclp + (int64_t)ch * n + e) = s[i];
+      *reinterpret_cast<f32x4*>(a.inclm + ((int64_t)pair * a.nch + ch) * n + e) = m[i];
+      if (ch == ngr - 1 && a.S_out) *reinterpret_cast<f32x4*>(a.S_out + (int64_t)pair * n + e) = s[i];
+    }
+  } else {
     // prefix = (inclusive prefix at `stop`, or W1) + aggregates stop+1 .. ch-1, left to right;
     // loads of eight aggregates are in flight together
     f32x4 s[SPT], own[SPT];
@@ -536,13 +605,31 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   for (int i = 0; i < G; ++i) {
     const int slot = i - (a.inclusive ? 0 : 1);  // group partial sum through chunk `slot`
     f32x4 part[SPT];
+    float sL = 0.f;  // with momentum: sigma_L for the L = slot + 1 chunk writes before this state
+    if constexpr (MOM) {
+      // part = sum_{j<=slot} alpha^(slot-j) P_j (Horner over the group's partial sums)
 #pragma unroll
-    for (int k = 0; k < SPT; ++k) part[k] = dev_load4(ra, (int)(((ch * G + (slot < 0 ? 0 : slot)) * n + 4 * (tid + NT * k)) * 4));
+      for (int k = 0; k < SPT; ++k) part[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float pw = 1.f;
+      for (int j = 0; j <= slot; ++j) {
+        f32x4 pj[SPT];
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) pj[k] = dev_load4(ra, (int)(((ch * G + j) * n + 4 * (tid + NT * k)) * 4));
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) part[k] = al * part[k] + pj[k];
+        pw *= al;
+        sL += pw;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) part[k] = dev_load4(ra, (int)(((ch * G + (slot < 0 ? 0 : slot)) * n + 4 * (tid + NT * k)) * 4));
+    }
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
       const int e = 4 * (tid + NT * k);
       if (NS4 % NT != 0 && e >= 4 * NS4) continue;
       f32x4 sc = slot < 0 ? run[k] : run[k] + part[k];
+      if constexpr (MOM) sc = run[k] + sL * mrun[MOM ? k : 0] + part[k];
       if (bad) sc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       const int j = e / H, c = e % H;
 #pragma unroll
