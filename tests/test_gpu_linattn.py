@@ -74,13 +74,15 @@ def test_config1_full_size(lib):
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
+@pytest.mark.parametrize("momentum", [0.0, 0.9])
 @pytest.mark.parametrize("order", [0, 1])
-def test_grouped_chunks_many_pairs(lib, order):
+def test_grouped_chunks_many_pairs(lib, order, momentum):
     """64 sequence-head pairs x 16 chunks: the single-pass kernel handles four chunks per
-    workgroup (one round of workgroups); both orders, sampled pairs against the oracle."""
+    workgroup (one round of workgroups); both orders, with and without momentum, sampled pairs
+    against the oracle."""
     p = LactProblem(B=8, H=8, h=64, r=2, Nq=4096, Nk=4096, chunk_q=256, chunk_kv=256, dtype=BF16,
-                    update_mask=UPD_W1, weight_norm=False, order=order)
-    announce(f"linattn grouped chunks B8 H8 N4096 chunk256 order={order}")
+                    update_mask=UPD_W1, weight_norm=False, order=order, momentum=momentum)
+    announce(f"linattn grouped chunks B8 H8 N4096 chunk256 order={order} momentum={momentum}")
     x = make_lact_inputs(p, 400 + order)
     O, S = _lin_gpu(lib, p, x)
     pairs = [(0, 0), (3, 5), (7, 7)]
@@ -91,13 +93,15 @@ def test_grouped_chunks_many_pairs(lib, order):
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
-def test_eight_chunks_per_workgroup(lib):
+@pytest.mark.parametrize("order,momentum", [(0, 0.0), (1, 0.8)])
+def test_eight_chunks_per_workgroup(lib, order, momentum):
     """32 pairs x 64 chunks of 256 tokens: the single-pass kernel groups eight chunks per
     workgroup (its largest group), so each workgroup stores seven partial sums before its
-    aggregate; sampled pairs against the oracle, apply-then-update order."""
+    aggregate; sampled pairs against the oracle, plain apply-then-update and
+    update-then-apply with momentum (eight-chunk affine group maps)."""
     p = LactProblem(B=4, H=8, h=64, r=2, Nq=16384, Nk=16384, chunk_q=256, chunk_kv=256, dtype=BF16,
-                    update_mask=UPD_W1, weight_norm=False)
-    announce("linattn eight chunks per workgroup B4 H8 N16384 chunk256")
+                    update_mask=UPD_W1, weight_norm=False, order=order, momentum=momentum)
+    announce(f"linattn eight chunks per workgroup B4 H8 N16384 chunk256 order={order} momentum={momentum}")
     x = make_lact_inputs(p, 450)
     O, S = _lin_gpu(lib, p, x)
     pairs = [(0, 1), (2, 4), (3, 7)]
