@@ -228,3 +228,21 @@ def test_no_learning_rate_variant(lib, momentum):
     eo, es = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(S), ref["S"])
     print(f"eta=1 momentum={momentum} O={eo:.2e} S={es:.2e}")
     assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+@pytest.mark.parametrize("h,momentum", [(64, 0.0), (64, 0.9), (128, 0.9)])
+def test_per_sequence_weights(lib, h, momentum):
+    """Weights given per sequence ([B, H, ...], w_batch_stride = H*h*rh): the single-pass kernel
+    (h = 64) and the multi-launch path (h = 128), with and without momentum."""
+    p = LactProblem(B=2, H=2, h=h, r=2, Nq=1024, Nk=1024, chunk_q=256, chunk_kv=256, dtype=BF16,
+                    update_mask=UPD_W1, weight_norm=False, momentum=momentum)
+    announce(f"linattn per-sequence weights h={h} momentum={momentum}")
+    x = make_lact_inputs(p, 700 + h)
+    rng = np.random.default_rng(701)
+    for k in ("W0", "W1", "W2"):
+        x[k] = np.stack([x[k], x[k] * (1.0 + 0.2 * rng.standard_normal(x[k].shape))]).astype(np.float32)
+    O, S = _lin_gpu(lib, p, x)
+    ref = _lin_ref(p, x)
+    eo, es = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(S), ref["S"])
+    print(f"per-sequence weights h={h} momentum={momentum} O={eo:.2e} S={es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
