@@ -20,9 +20,11 @@
  *   H, Vbar) and of the In-Place slow weights. Fast-weight state, momentum and step sizes are
  *   always float32. Accumulation is always float32.
  * - Ownership: the caller owns every buffer. The entry points never allocate, free or
- *   synchronise device memory; apart from the optional timing recorder (ttt_timing_*) the
- *   library keeps no mutable global state and is re-entrant for calls with distinct
- *   workspaces. Inputs are read only. Outputs are fully overwritten and must not alias inputs.
+ *   synchronise device memory, create no streams or events, and launch only on `stream`;
+ *   apart from the optional timing recorder (ttt_timing_*) the library keeps no mutable
+ *   global state and is re-entrant for calls with distinct workspaces (concurrent calls on
+ *   different streams give the same results as sequential calls). Inputs are read only.
+ *   Outputs are fully overwritten and must not alias inputs.
  * - Workspace: pass workspace == NULL to query; the required size in bytes is written to
  *   *workspace_bytes, TTT_OK is returned and nothing is launched. Otherwise *workspace_bytes
  *   must hold the size of the buffer (at least the queried size, 256-byte aligned base).
@@ -111,10 +113,16 @@ typedef int32_t ttt_status;
  * Shape rules: Nq/chunk_q == Nk/chunk_kv (number of chunks); a ragged last chunk is rejected
  * (TTT_ERR_SHAPE); h a multiple of 32 and r >= 1 with r*h a multiple of 64, r*h <= 1024;
  * this build implements h <= 192 in TTT_BF16 mode and h <= 64 in TTT_FP32 mode
- * (TTT_ERR_UNSUPPORTED otherwise).
+ * (TTT_ERR_UNSUPPORTED otherwise). 0 <= momentum < 1 and finite eps_norm, eps_ns >= 0, else
+ * TTT_ERR_ARG (NaN included).
  * Precision: in TTT_BF16 mode the per-chunk products use fp16 MFMA operands (bf16 inputs
  * convert exactly) and Newton-Schulz uses split-bf16 operands; fp32 state throughout. In
- * TTT_FP32 mode all operands are fp32.
+ * TTT_FP32 mode all operands are fp32, Newton-Schulz included.
+ * Range (TTT_BF16 mode): because the product operands are fp16, Q, K, V and the fast weights
+ * must lie within the fp16 range, |x| <= 65504 (the step-size-scaled intermediates are rescaled
+ * by a power of two per token segment and are not limited). Larger values are not representable
+ * as operands and give undefined results; the library does not read the inputs on the host and
+ * does not check this.
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t B, H;
@@ -160,7 +168,12 @@ ttt_status ttt_lact_forward(const ttt_lact_params* p,
  * W1 [H, rh, h] float32 (or [B, H, ...] with w_batch_stride as above); O [B, H, N, h] I/O
  * dtype; S_out [B, H, rh, h] float32, nullable: the state after the last chunk.
  * Shape rules: N % chunk == 0; h a multiple of 32, 32 <= h <= 256; r*h a multiple of 64,
- * r*h <= 1024. Operands are bf16 (TTT_BF16) or fp32 (TTT_FP32), fp32 accumulation and state.
+ * r*h <= 1024. fp32 accumulation and state. Operands: in TTT_FP32 mode fp32; in TTT_BF16 mode
+ * bf16, except on the single-pass path (h = 32 with r*h in {64, 128}, h = 64 with r*h = 128),
+ * whose operands are fp16: there Q, K, eta*V, the fast weights and the states must lie within
+ * the fp16 range, |x| <= 65504 (not checked; larger values give undefined results).
+ * The single-pass path claims its work from per-XCD lists and falls back to the other lists,
+ * so it is correct for any XCD count and dispatch order.
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t B, H, N, h, r, chunk;
@@ -190,8 +203,9 @@ ttt_status ttt_linattn_forward(const ttt_linattn_params* p,
  * the embeddings, built by the caller); W_gate, W_up [d_hidden, d_model] bf16; W_down
  * [d_model, d_hidden] float32 (shared, or [B, ...] with wdown_batch_stride); O [B, N, d_model]
  * bf16; W_down_out [B, d_model, d_hidden] float32, nullable.
- * Shape rules: N % chunk == 0; d_model and d_hidden multiples of 256; chunk a multiple of 64.
- * Only TTT_BF16 is implemented (TTT_FP32 gives TTT_ERR_UNSUPPORTED).
+ * Shape rules: N % chunk == 0; d_model and d_hidden multiples of 256; chunk a multiple of 128.
+ * Only TTT_BF16 is implemented (TTT_FP32 gives TTT_ERR_UNSUPPORTED). Every launch goes to
+ * `stream`; the next chunk's Z is formed in the same launch as the current chunk's apply.
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t B, N, d_model, d_hidden, chunk;
@@ -215,6 +229,8 @@ ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p,
  * for the recorded events, writes one entry per class that ran (name: static string,
  * launches, summed milliseconds) and clears the record. The recorder is process-wide state
  * owned by the library; it is not meant for concurrent use from several host threads.
+ * ttt_timing_enable(0) also destroys the events the recorder holds (call it after the last
+ * ttt_timing_collect, so that no HIP object of the library outlives the caller's use of it).
  * Returns TTT_ERR_HIP if an event cannot be created or read.
  * ---------------------------------------------------------------------------------------- */
 typedef struct {

@@ -173,6 +173,21 @@ def _io_dtype(t):
     raise ValueError(f"token tensors must be bfloat16 or float32, got {t.dtype}")
 
 
+def _check_weights(W0, W1, W2, B, H, h):
+    """W0/W2 [H,h,rh] and W1 [H,rh,h] shared by the batch, or all three [B,H,...] per
+    sequence; rh a multiple of h. Checked before any launch: a wrong shape would make the
+    kernels read past the end of a buffer."""
+    per_seq = W0.dim() == 4
+    lead = (B, H) if per_seq else (H,)
+    rh = W0.shape[-1]
+    if tuple(W0.shape) != lead + (h, rh) or tuple(W2.shape) != lead + (h, rh) or tuple(W1.shape) != lead + (rh, h):
+        raise ValueError(f"W0/W2 must be {'[B,H,h,rh]' if per_seq else '[H,h,rh]'} and W1 "
+                         f"{'[B,H,rh,h]' if per_seq else '[H,rh,h]'} with h={h}, all shared or all per sequence; "
+                         f"got {tuple(W0.shape)}, {tuple(W1.shape)}, {tuple(W2.shape)}")
+    if rh % h:
+        raise ValueError("rh must be a multiple of h")
+
+
 def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[int] = None,
                  order: int = APPLY_THEN_UPDATE, update_mask: int = 7, weight_norm: bool = True,
                  muon: bool = False, momentum: float = 0.0, eps_norm: float = 1e-5, eps_ns: float = 1e-7,
@@ -196,11 +211,11 @@ def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[i
         _check(t, n, torch.float32, dev)
     if K.shape != (B, H, Nk, h) or V.shape != K.shape or eta.shape != (B, H, Nk):
         raise ValueError("K/V must be [B,H,Nk,h] and eta [B,H,Nk]")
-    wshape = ((B,) if per_seq else ()) + (H,)
-    if W0.shape != wshape + (h, rh) or W2.shape != W0.shape or W1.shape != wshape + (rh, h):
-        raise ValueError("W0/W2 must be [(B,)H,h,rh] and W1 [(B,)H,rh,h]")
-    if rh % h:
-        raise ValueError("rh must be a multiple of h")
+    _check_weights(W0, W1, W2, B, H, h)
+    if M_in is not None and tuple(M_in.shape) != (B, H, 3, h * rh):
+        raise ValueError("M_in must be [B,H,3,h*rh]")
+    if not (0.0 <= momentum < 1.0):
+        raise ValueError("momentum must lie in [0, 1)")
     p = LactParams(B, H, Nq, Nk, h, rh // h, chunk_q, chunk_kv, order, _io_dtype(Q), update_mask,
                    int(bool(weight_norm)), int(bool(muon)), momentum, eps_norm, eps_ns,
                    H * h * rh if per_seq else 0)
@@ -235,8 +250,9 @@ def linattn_forward(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_
         _check(t, n, torch.float32, dev)
     if K.shape != Q.shape or V.shape != Q.shape or eta.shape != (B, H, N):
         raise ValueError("Q/K/V must share [B,H,N,h] and eta be [B,H,N]")
-    if rh % h:
-        raise ValueError("rh must be a multiple of h")
+    _check_weights(W0, W1, W2, B, H, h)
+    if not (0.0 <= momentum < 1.0):
+        raise ValueError("momentum must lie in [0, 1)")
     p = LinattnParams(B, H, N, h, rh // h, chunk, order, _io_dtype(Q), H * h * rh if per_seq else 0,
                       float(momentum))
     O = torch.empty_like(Q)

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <cfloat>
 #include <cstddef>
 #include <cstdint>
 #include "../../include/ttt_lact.h"

@@ -286,12 +286,10 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
 
   const dim3 agrid(8u * (unsigned)((P + 7) / 8) * (unsigned)aa.ntiles);
   auto apply = [&]() -> ttt_status {
-    LaunchTimer lt(K_LACT_APPLY, st);
     if constexpr (ARD)
-      hipLaunchKernelGGL(akr, agrid, dim3(512), alds, st, aa);
+      TTT_HIP(launch_k(K_LACT_APPLY, akr, agrid, dim3(512), alds, st, aa));
     else
-      hipLaunchKernelGGL(ak, agrid, dim3(256), alds, st, aa);
-    TTT_HIP(hipGetLastError());
+      TTT_HIP(launch_k(K_LACT_APPLY, ak, agrid, dim3(256), alds, st, aa));
     return TTT_OK;
   };
   auto set_apply_weights = [&](const OpT* b) {
@@ -318,33 +316,26 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     ga.eta_scale = s.esc + (int64_t)c * P * S;
     ga.t_limit = (c + 1) * p.chunk_kv;
     {
-      LaunchTimer lt(K_LACT_GRAD, st);
-      if constexpr (WS) {
-        const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
-        hipLaunchKernelGGL(gkw, dim3(grid), dim3(512), glds, st, ga, S, P);
-      } else if constexpr (RD) {
-        const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
-        hipLaunchKernelGGL(gkr, dim3(grid), dim3(256), glds, st, ga, S, P);
-      } else {
-        hipLaunchKernelGGL(gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga);
-      }
-      TTT_HIP(hipGetLastError());
+      const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
+      if constexpr (WS)
+        TTT_HIP(launch_k(K_LACT_GRAD, gkw, dim3(grid), dim3(512), glds, st, ga, S, P));
+      else if constexpr (RD)
+        TTT_HIP(launch_k(K_LACT_GRAD, gkr, dim3(grid), dim3(256), glds, st, ga, S, P));
+      else
+        TTT_HIP(launch_k(K_LACT_GRAD, gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga));
     }
     if (fuse_ua) {
-      LaunchTimer lt(K_LACT_UPD_APPLY, st);
       int nu = nupd;
       void* args[] = {&ua, &aa, &nu};
-      TTT_HIP(hipLaunchKernel(uak, dim3((unsigned)nupd + agrid.x), dim3(512), args, (size_t)ualds, st));
+      TTT_HIP(launch_raw(K_LACT_UPD_APPLY, uak, dim3((unsigned)nupd + agrid.x), dim3(512), args, (size_t)ualds, st));
       continue;
     }
-    {
-      LaunchTimer lt(K_LACT_UPDATE, st);
+    if (uk) {
       void* args[] = {&ua};
-      if (uk) {
-        TTT_HIP(hipLaunchKernel(uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
-      } else {
-        TTT_HIP(tu_run<OpT>(ua, st));
-      }
+      TTT_HIP(launch_raw(K_LACT_UPDATE, uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
+    } else {
+      LaunchTimer lt(K_LACT_UPDATE, st);
+      TTT_HIP(tu_run<OpT>(ua, st));
     }
     if (p.order == TTT_UPDATE_THEN_APPLY) {
       set_apply_weights(wr);
@@ -377,6 +368,9 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   if (q.dtype != TTT_FP32 && q.dtype != TTT_BF16) return TTT_ERR_ARG;
   if (q.update_mask & ~7u) return TTT_ERR_ARG;
   if (q.w_batch_stride < 0) return TTT_ERR_ARG;
+  // heavy-ball coefficient in [0, 1), epsilons finite and >= 0 (the comparisons reject NaN)
+  if (!(q.momentum >= 0.f && q.momentum < 1.f)) return TTT_ERR_ARG;
+  if (!(q.eps_norm >= 0.f && q.eps_norm <= FLT_MAX) || !(q.eps_ns >= 0.f && q.eps_ns <= FLT_MAX)) return TTT_ERR_ARG;
   if (q.Nq % q.chunk_q || q.Nk % q.chunk_kv) return TTT_ERR_SHAPE;
   if (q.Nq / q.chunk_q != q.Nk / q.chunk_kv) return TTT_ERR_SHAPE;
   const int64_t rh64 = (int64_t)q.r * q.h;

@@ -91,6 +91,12 @@ def test_lact_workspace_query(lib):
     (dict(h=256), ttt.TTT_ERR_UNSUPPORTED),
     (dict(dtype=ttt.FP32, h=128), ttt.TTT_ERR_UNSUPPORTED),
     (dict(w_batch_stride=5), ttt.TTT_ERR_SHAPE),
+    (dict(momentum=-0.5), ttt.TTT_ERR_ARG),
+    (dict(momentum=1.0), ttt.TTT_ERR_ARG),
+    (dict(momentum=float("nan")), ttt.TTT_ERR_ARG),
+    (dict(eps_norm=-1e-5), ttt.TTT_ERR_ARG),
+    (dict(eps_ns=float("inf")), ttt.TTT_ERR_ARG),
+    (dict(eps_ns=float("nan")), ttt.TTT_ERR_ARG),
 ])
 def test_lact_rejects_bad_arguments(lib, kw, code):
     assert _lact(lib, _lp(**kw))[0] == code
@@ -159,6 +165,69 @@ def test_inplace_query_and_validation(lib):
     assert _inp(lib, N=32768 + 512)[0] == ttt.TTT_ERR_SHAPE
     assert _inp(lib, d_model=4000)[0] == ttt.TTT_ERR_SHAPE
     assert _inp(lib, chunk=-4)[0] == ttt.TTT_ERR_ARG
+    assert _inp(lib, chunk=64, N=32768)[0] == ttt.TTT_ERR_SHAPE  # the chunk must be a multiple of 128
+    assert _inp(lib, chunk=128, N=32768)[0] == ttt.TTT_OK
+
+
+class _FakeCuda:
+    """Stands in for a device tensor in the binding's checks (they run before any launch)."""
+    is_cuda = True
+
+    def __init__(self, shape, dtype):
+        import torch
+        self.shape, self.dtype, self.device = tuple(shape), dtype, torch.device("cuda:0")
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return len(self.shape)
+
+
+def _fake_call_guard(monkeypatch):
+    """Any attempt to reach the library after the checks fails the test."""
+    def boom(*a, **k):
+        raise AssertionError("the binding reached the library despite a bad argument")
+    monkeypatch.setattr(ttt, "_call", boom)
+
+
+@pytest.mark.parametrize("bad", ["W1 shared, W0 per sequence", "W0 wrong h", "W2 wrong heads", "W1 transposed"])
+def test_linattn_binding_checks_weight_shapes_before_any_launch(monkeypatch, lib, bad):
+    import torch
+    _fake_call_guard(monkeypatch)
+    B, H, N, h, rh = 2, 4, 256, 64, 128
+    bf, f32 = torch.bfloat16, torch.float32
+    Q = _FakeCuda((B, H, N, h), bf)
+    eta = _FakeCuda((B, H, N), f32)
+    W0, W2, W1 = _FakeCuda((H, h, rh), f32), _FakeCuda((H, h, rh), f32), _FakeCuda((H, rh, h), f32)
+    if bad == "W1 shared, W0 per sequence":
+        W0 = W2 = _FakeCuda((B, H, h, rh), f32)
+    elif bad == "W0 wrong h":
+        W0 = _FakeCuda((H, 32, rh), f32)
+    elif bad == "W2 wrong heads":
+        W2 = _FakeCuda((H + 1, h, rh), f32)
+    else:
+        W1 = _FakeCuda((H, h, rh), f32)
+    with pytest.raises(ValueError):
+        ttt.linattn_forward(Q, Q, Q, eta, W0, W2, W1, chunk=64)
+
+
+@pytest.mark.parametrize("bad", ["M_in shape", "momentum 1", "momentum nan"])
+def test_lact_binding_checks_momentum_before_any_launch(monkeypatch, lib, bad):
+    import torch
+    _fake_call_guard(monkeypatch)
+    B, H, N, h, rh = 1, 2, 256, 64, 128
+    bf, f32 = torch.bfloat16, torch.float32
+    Q = _FakeCuda((B, H, N, h), bf)
+    eta = _FakeCuda((B, H, N), f32)
+    W0, W1 = _FakeCuda((H, h, rh), f32), _FakeCuda((H, rh, h), f32)
+    kw = dict(chunk_q=64, momentum=0.9)
+    if bad == "M_in shape":
+        kw["M_in"] = _FakeCuda((B, H, h * rh), f32)
+    else:
+        kw["momentum"] = 1.0 if bad == "momentum 1" else float("nan")
+    with pytest.raises(ValueError):
+        ttt.lact_forward(Q, Q, Q, eta, W0, W1, W0, **kw)
 
 
 def test_product_code_never_touches_the_oracle():
