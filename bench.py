@@ -14,7 +14,10 @@ the host cores on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
 
 --config 1 / 3 / 4 time the linear-attention scan, the view-synthesis shape and the In-Place
-update instead (their lines are reported separately; the default line is config 2).
+update instead. The default run (the LM layer) also measures those three workloads and adds
+them to its JSON line under "other_workloads" (--no-extras skips them). The scan workload's
+136 MB fit in the 256 MB last-level cache, so it is timed both warm and with a 512 MB buffer
+read between repetitions (flushed; its headline figure).
 """
 from __future__ import annotations
 
@@ -40,6 +43,8 @@ def parse():
                     help="scan workload only: heavy-ball momentum per chunk (the momentum form)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default run: do not measure the other three workloads")
     return ap.parse_args()
 
 
@@ -49,6 +54,16 @@ def blas_threads():
         return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         return os.cpu_count() or 1
+
+
+def blas_vendor():
+    """The BLAS library NumPy uses (name and version), as threadpoolctl reports it."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs) or "unknown"
+    except Exception:  # pragma: no cover
+        return "unknown"
 
 
 def cpu_baseline_lact(p, x, budget_s):
@@ -71,6 +86,7 @@ def cpu_baseline_lact(p, x, budget_s):
     el = time.perf_counter() - t0
     tokens = done * p.Nk / p.H  # one pair carries 1/H of each token's heads
     return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "blas": blas_vendor(),
             "sample": f"{done} of {len(pairs)} (sequence, head) pairs, all {p.Nk // p.chunk_kv} chunks each, "
                       f"float32 NumPy oracle, {el:.1f} s"}
 
@@ -88,7 +104,8 @@ def cpu_baseline_linattn(p, x, budget_s):
             break
     el = time.perf_counter() - t0
     return {"value": round(done * p.Nk / p.H / el, 1), "unit": "tokens/s", "cores": int(blas_threads()),
-            "kind": "oracle", "sample": f"{done} of {len(pairs)} pairs, float32 NumPy oracle, {el:.1f} s"}
+            "kind": "oracle", "blas": blas_vendor(),
+            "sample": f"{done} of {len(pairs)} pairs, float32 NumPy oracle, {el:.1f} s"}
 
 
 def cpu_baseline_inplace(p, x, budget_s):
@@ -106,7 +123,8 @@ def cpu_baseline_inplace(p, x, budget_s):
             break
     el = time.perf_counter() - t0
     return {"value": round(done * p.chunk / el, 1), "unit": "tokens/s", "cores": int(blas_threads()),
-            "kind": "oracle", "sample": f"first {done} of {p.N // p.chunk} chunks, float32 NumPy oracle, {el:.1f} s"}
+            "kind": "oracle", "blas": blas_vendor(),
+            "sample": f"first {done} of {p.N // p.chunk} chunks, float32 NumPy oracle, {el:.1f} s"}
 
 
 def time_steps(step, steps, warmup, stream):
@@ -123,14 +141,49 @@ def time_steps(step, steps, warmup, stream):
     return ev0.elapsed_time(ev1) / steps
 
 
-def kernel_breakdown(ttt, step, steps):
-    """Per kernel class: launches and average launch time (HIP events on the launch stream)."""
+def flush_buffer(flush_bytes):
     import torch
+    return torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda:0") if flush_bytes else None
+
+
+def flush(buf):
+    """Read a buffer larger than the last-level cache (256 MB): the cache then holds none of
+    the step's inputs and no dirty lines of the flush itself (a written flush buffer would leave
+    its write-backs to the timed step)."""
+    buf.max()
+
+
+def time_steps_flushed(step, steps, stream, flush_bytes=512 << 20):
+    """Each step timed alone after a 512 MB read pass, so that the step's inputs come from HBM;
+    returns the mean step time in ms."""
+    import torch
+    buf = flush_buffer(flush_bytes)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    step()
+    for i in range(steps):
+        flush(buf)
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    del buf
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def kernel_breakdown(ttt, step, steps, flush_bytes=0):
+    """Per kernel class: launches and average launch time. The hot kernels are launched with
+    start/stop events attached to the dispatch itself (the kernel's own begin and end
+    timestamps, the figures a kernel trace reports); see ttt_timing_enable in the C header.
+    With flush_bytes a buffer that large is read before every step."""
+    import torch
+    buf = flush_buffer(flush_bytes)
     torch.cuda.synchronize()
     ttt.timing_collect()
     ttt.timing_enable(True)
     try:
-        for _ in range(steps):
+        for i in range(steps):
+            if buf is not None:
+                flush(buf)
             step()
         torch.cuda.synchronize()
         rec = ttt.timing_collect()
@@ -143,6 +196,12 @@ def kernel_breakdown(ttt, step, steps):
 # profiles/<stem>_*.txt: the committed rocprofv3 summaries of each workload
 PROFILE_STEMS = {1: "linattn_scan_b4h8_h64_seq8192_chunk512", 2: "lact_lm_layer_b4h8_h128_seq32768_chunk2048",
                  3: "lact_nvs_b1h4_h192_ctx196608_q4096", 4: "inplace_down_d4096_dh14336_seq32768_chunk1024"}
+
+DTYPES = {
+    "lact": "bf16 I/O; fp16 MFMA operands for the per-chunk products; split-bf16 Newton-Schulz; fp32 accumulate/state",
+    "linattn": "bf16 I/O; fp16 MFMA operands; fp32 accumulate/state",
+    "inplace": "bf16 I/O and MFMA operands; fp32 accumulate and W_down state",
+}
 
 
 def roofline(kern, work, bound, peak, unit):
@@ -158,32 +217,23 @@ def roofline(kern, work, bound, peak, unit):
             "work_per_launch": per_launch, "avg_launch_us": kern[dom]["avg_us"]}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
-              "(sequence, head) pairs shard across GPUs without communication, see DESIGN.md",
-              file=sys.stderr)
-        sys.exit(2)
+def measure(k, args, momentum=0.0, cpu=True):
+    """One workload: its JSON record (without the fields common to every line)."""
     import numpy as np
     import torch
     import linear_attention_lact_amd as ttt
     from linear_attention_lact_amd import accounting as acc
     from workloads import CONFIGS, CONFIG_NAMES, make_inplace_inputs, make_lact_inputs
 
-    ttt.load()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
-    k = args.config
     p = CONFIGS[k]
     stem = PROFILE_STEMS[k]
-    if args.momentum != 0.0:
-        if k != 1:
-            print("--momentum applies to the scan workload (--config 1) only", file=sys.stderr)
-            sys.exit(2)
+    flush_bytes = 0
+    if momentum != 0.0:
         from dataclasses import replace
-        p = replace(p, momentum=args.momentum)
+        p = replace(p, momentum=momentum)
         stem = "linattn_scan_momentum_b4h8_h64_seq8192_chunk512"
     if k == 4:
         x = make_inplace_inputs(p, k)
@@ -194,13 +244,13 @@ def main():
             return ttt.inplace_down_forward(Hs, Wg, Wu, Wd, Vb, chunk=p.chunk, eta=float(x["eta"]), stream=stream)
         tokens = p.B * p.N
         flops = acc.inplace_flops(p.B, p.N, p.d_model, p.d_hidden)
-        nch = p.N // p.chunk
         per = 2.0 * p.chunk * p.d_model * p.d_hidden
-        work = {"inplace_z": 2 * per, "inplace_apply": per, "inplace_update": per}
+        work = {"inplace_z": 2 * per, "inplace_apply": per, "inplace_update": per, "inplace_apply_z": 3 * per}
         bound, peak, unit = "mfma", acc.PEAK_BF16_TFLOPS, "TFLOP/s"
         metric = "In-Place TTT W_down update tokens/sec (d_model 4096, d_hidden 14336, chunk 1024), bf16"
         cfg = {"workload": CONFIG_NAMES[4], "B": p.B, "seq_len": p.N, "d_model": p.d_model,
                "d_hidden": p.d_hidden, "chunk": p.chunk, "eta": p.eta}
+        dtype = DTYPES["inplace"]
     else:
         x = make_lact_inputs(p, k)
         io = torch.bfloat16 if p.dtype == 1 else torch.float32
@@ -222,6 +272,8 @@ def main():
             metric = "linear-attention scan form tokens/sec (h=64, r=2, chunk 512), bf16; % of HBM roofline"
             if p.momentum:
                 metric = metric.replace("scan form", f"scan form with momentum {p.momentum:g}")
+            flush_bytes = 512 << 20
+            dtype = DTYPES["linattn"]
         else:
             def step():
                 return ttt.lact_forward(Q, K, V, eta, W0, W1, W2, chunk_q=p.chunk_q, chunk_kv=p.chunk_kv,
@@ -239,6 +291,7 @@ def main():
             bound, peak, unit = "mfma", acc.PEAK_BF16_TFLOPS, "TFLOP/s"
             metric = ("TTT-layer tokens/sec at h=128, chunk 2048 bf16; % of bf16 MFMA peak" if k == 2 else
                       "TTT-layer tokens/sec, view-synthesis shape (h=192, 196608 context + 4096 query), bf16")
+            dtype = DTYPES["lact"]
         # every token of the LM layer is both a query and a key; the scene has distinct context
         # (written) and query (read) tokens
         tokens = p.B * (p.Nk if p.Nq == p.Nk else p.Nk + p.Nq)
@@ -259,37 +312,57 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    ms = time_steps(step, args.steps, args.warmup, stream)
-    kern = kernel_breakdown(ttt, step, args.steps)
+    ms_warm = time_steps(step, args.steps, args.warmup, stream)
+    ms = time_steps_flushed(step, args.steps, stream, flush_bytes) if flush_bytes else ms_warm
+    kern = kernel_breakdown(ttt, step, args.steps, flush_bytes)
     roof = roofline(kern, work, bound, peak, unit)
     roof["traffic"] = acc.profiled_traffic(ROOT, roof["kernel"], stem)
-    out = {
-        "metric": metric,
-        "value": round(tokens / (ms * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": cfg,
-        "roofline": roof,
-        "step_flops": flops,
-        "step_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-        "step_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS, 4),
-        "kernels": kern,
-    }
-    if not args.no_cpu_baseline:
+    rec = {"metric": metric, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+           "dtype": dtype, "config": cfg, "roofline": roof, "step_flops": flops,
+           "step_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "step_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS, 4), "kernels": kern}
+    if flush_bytes:
+        rec["timing"] = f"flushed: a {flush_bytes >> 20} MiB buffer read before each timed step"
+        rec["warm"] = {"ms_per_step": round(ms_warm, 4), "value": round(tokens / (ms_warm * 1e-3), 1)}
+    if cpu:
         if k == 4:
-            out["cpu_baseline"] = cpu_baseline_inplace(p, x, args.cpu_seconds)
+            rec["cpu_baseline"] = cpu_baseline_inplace(p, x, args.cpu_seconds)
         elif k == 1:
-            out["cpu_baseline"] = cpu_baseline_linattn(p, x, args.cpu_seconds)
+            rec["cpu_baseline"] = cpu_baseline_linattn(p, x, args.cpu_seconds)
         else:
-            out["cpu_baseline"] = cpu_baseline_lact(p, x, args.cpu_seconds)
+            rec["cpu_baseline"] = cpu_baseline_lact(p, x, args.cpu_seconds)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
+              "(sequence, head) pairs shard across GPUs without communication, see DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.momentum != 0.0 and args.config != 1:
+        print("--momentum applies to the scan workload (--config 1) only", file=sys.stderr)
+        sys.exit(2)
+    import linear_attention_lact_amd as ttt
+    ttt.load()
+    rec = measure(args.config, args, args.momentum, cpu=not args.no_cpu_baseline)
+    out = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec.pop("dtype"),
+           "data": "synthetic", "config": rec.pop("config"), "roofline": rec.pop("roofline")}
+    if "cpu_baseline" in rec:
+        out["cpu_baseline"] = rec.pop("cpu_baseline")
+    out.update(rec)
+    if args.config == 2 and not args.no_extras:
+        others = {}
+        for k in (1, 3, 4):
+            r = measure(k, args, cpu=False)
+            others[r["config"]["workload"]] = {
+                "metric": r["metric"], "value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
+                "roofline": {key: r["roofline"][key] for key in ("bound", "kernel", "achieved", "peak", "unit", "frac")},
+                **({"warm": r["warm"], "timing": r["timing"]} if "warm" in r else {})}
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 
 

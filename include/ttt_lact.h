@@ -172,8 +172,8 @@ ttt_status ttt_lact_forward(const ttt_lact_params* p,
  * bf16, except on the single-pass path (h = 32 with r*h in {64, 128}, h = 64 with r*h = 128),
  * whose operands are fp16: there Q, K, eta*V, the fast weights and the states must lie within
  * the fp16 range, |x| <= 65504 (not checked; larger values give undefined results).
- * The single-pass path claims its work from per-XCD lists and falls back to the other lists,
- * so it is correct for any XCD count and dispatch order.
+ * The single-pass path runs on devices with 8 XCDs (hipDeviceAttributeNumberOfXccs); other
+ * devices take the multi-launch path (same results, more launches).
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t B, H, N, h, r, chunk;
@@ -244,6 +244,11 @@ ttt_status ttt_timing_collect(ttt_kernel_time* out, int32_t capacity, int32_t* c
 
 /* Human-readable name of a status code (static string). */
 const char* ttt_status_string(ttt_status s);
+
+/* Diagnostic text of the last HIP failure an entry point of this library met on the calling
+ * host thread (the failing HIP call, its error name and the source location), or "" if none.
+ * The string is owned by the library and stays valid until the next failure on the thread. */
+const char* ttt_last_error(void);
 
 #ifdef __cplusplus
 }

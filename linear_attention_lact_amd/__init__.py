@@ -26,7 +26,7 @@ FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
 
 EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_inplace_down_forward", "ttt_status_string",
-            "ttt_timing_enable", "ttt_timing_collect")
+            "ttt_last_error", "ttt_timing_enable", "ttt_timing_collect")
 
 
 class KernelTime(ctypes.Structure):
@@ -62,7 +62,8 @@ _szp = ctypes.POINTER(ctypes.c_size_t)
 class TTTError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
-        super().__init__(f"{fn} failed with status {status} ({status_string(status)})")
+        detail = f": {last_error()}" if status == TTT_ERR_HIP else ""
+        super().__init__(f"{fn} failed with status {status} ({status_string(status)}){detail}")
 
 
 def load(path: Optional[str] = None) -> ctypes.CDLL:
@@ -74,6 +75,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise RuntimeError(f"HIP library not built: {p} is missing (run __graft_entry__.build() "
                            "or python -m linear_attention_lact_amd.build)")
+    # torch first: the library and torch's ROCm build both name their HIP runtime
+    # libamdhip64.so.7, and the first one loaded serves the whole process. Loading torch's
+    # first keeps one runtime, the one that owns the device memory and streams we are given.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     lib.ttt_lact_forward.argtypes = [ctypes.POINTER(LactParams)] + [_vp] * 13 + [_vp, _szp, _vp]
     lib.ttt_lact_forward.restype = ctypes.c_int32
@@ -83,6 +88,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ttt_inplace_down_forward.restype = ctypes.c_int32
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
     lib.ttt_status_string.restype = ctypes.c_char_p
+    lib.ttt_last_error.argtypes = []
+    lib.ttt_last_error.restype = ctypes.c_char_p
     lib.ttt_timing_enable.argtypes = [ctypes.c_int32]
     lib.ttt_timing_enable.restype = ctypes.c_int32
     lib.ttt_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -93,6 +100,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
 
 def status_string(s: int) -> str:
     return load().ttt_status_string(s).decode()
+
+
+def last_error() -> str:
+    """The last HIP failure the library met on this thread (empty if none)."""
+    return load().ttt_last_error().decode()
 
 
 def timing_enable(on: bool = True) -> None:

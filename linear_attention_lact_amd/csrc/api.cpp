@@ -1,5 +1,7 @@
 // api.cpp -- status strings and the optional kernel-timing recorder of the C ABI.
 #include <hip/hip_runtime.h>
+#include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <vector>
 #include "../../include/ttt_lact.h"
@@ -19,10 +21,25 @@ extern "C" const char* ttt_status_string(ttt_status s) {
 
 namespace ttt {
 namespace {
+thread_local char last_error[512] = "";
+}  // namespace
+
+void note_hip_error(const char* what, hipError_t e, const char* file, int line) {
+  const char* base = std::strrchr(file, '/');
+  std::snprintf(last_error, sizeof last_error, "%s (%s) at %s:%d: %s", hipGetErrorName(e), hipGetErrorString(e),
+                base ? base + 1 : file, line, what);
+}
+}  // namespace ttt
+
+extern "C" const char* ttt_last_error(void) { return ttt::last_error; }
+
+namespace ttt {
+namespace {
 const char* kClassNames[K_NUM_CLASSES] = {
     "lact_init", "lact_grad", "lact_update", "lact_apply", "lact_final",
     "linattn_prep", "linattn_delta", "linattn_scan", "linattn_apply", "linattn_fused",
-    "inplace_prep", "inplace_z", "inplace_apply", "inplace_update", "lact_update_apply"};
+    "inplace_prep", "inplace_z", "inplace_apply", "inplace_update", "lact_update_apply",
+    "inplace_apply_z"};
 struct Rec { int cls; hipEvent_t a, b; };
 std::mutex mu;
 bool on = false;
@@ -53,6 +70,14 @@ void timing_record(int cls, hipEvent_t a, hipEvent_t b) {
 extern "C" ttt_status ttt_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> g(ttt::mu);
   ttt::on = enable != 0;
+  if (!ttt::on && ttt::recs.empty()) {
+    // release the pooled events while the runtime is alive (none is left for process teardown)
+    ttt_status st = TTT_OK;
+    for (hipEvent_t e : ttt::pool)
+      if (hipEventDestroy(e) != hipSuccess) st = TTT_ERR_HIP;
+    ttt::pool.clear();
+    return st;
+  }
   return TTT_OK;
 }
 

@@ -9,10 +9,16 @@
 
 namespace ttt {
 
-#define TTT_HIP(expr)                          \
-  do {                                         \
-    hipError_t _e = (expr);                    \
-    if (_e != hipSuccess) return TTT_ERR_HIP;  \
+// Records the failing HIP call for ttt_last_error() (per host thread).
+void note_hip_error(const char* what, hipError_t e, const char* file, int line);
+
+#define TTT_HIP(expr)                                        \
+  do {                                                       \
+    hipError_t _e = (expr);                                  \
+    if (_e != hipSuccess) {                                  \
+      ::ttt::note_hip_error(#expr, _e, __FILE__, __LINE__);  \
+      return TTT_ERR_HIP;                                    \
+    }                                                        \
   } while (0)
 
 // Sub-allocations of the caller's workspace, each 256-byte aligned.

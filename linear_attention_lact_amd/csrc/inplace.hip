@@ -8,8 +8,6 @@
 // All three are "TN" products C[M x N] = A[M x K] B[N x K]^T with K-contiguous operands:
 // Z is written both token-major (for the apply, contracting over d_hidden) and hidden-major
 // (for the update, contracting over tokens); Vbar is transposed once per sequence.
-#include <mutex>
-
 #include "common.hpp"
 #include "host.hpp"
 #include "timing.hpp"
@@ -181,14 +179,12 @@ __device__ __forceinline__ int chunk_pos(int c, int row) { return c ^ (row & 7) 
 // Wave w: rows (w & 1) * 128.. of the A tile; B rows (w >> 1) * 64.. (SwiGLU: gate rows
 // (w >> 1) * 32.. and the same up rows, so each wave holds both factors of its outputs).
 template <int EPI>
-__global__ void __launch_bounds__(512) gemm_big_kernel(Args g, int ksplit, float* part) {
+__device__ __forceinline__ void gemm_big_body(const Args& g, int ksplit, float* part, int bid, unsigned char* smem) {
   constexpr bool SW = EPI == EPI_SWIGLU;
   constexpr int TN = tile_n<EPI>();
-  extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
   const int ntn = g.N / TN;
-  int bid = blockIdx.x;
   const int ks = bid % ksplit;
   bid /= ksplit;
   const int m0 = (bid / ntn) * BM, n0 = (bid % ntn) * TN;
@@ -338,6 +334,24 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(Args g, int ksplit, float
       }
     }
   }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(512) gemm_big_kernel(Args g, int ksplit, float* part) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  gemm_big_body<EPI>(g, ksplit, part, blockIdx.x, smem);
+}
+
+// Two independent products in one launch: the first nfirst workgroups form product g1 (epilogue
+// E1, no K split), the others product g2 (epilogue E2, ksplit-way K split into part). Used to
+// produce the next chunk's Z beside the current chunk's apply on the caller's stream.
+template <int E1, int E2>
+__global__ void __launch_bounds__(512) gemm_big_pair_kernel(Args g1, int nfirst, Args g2, int ksplit, float* part) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x < nfirst)
+    gemm_big_body<E1>(g1, 1, part, blockIdx.x, smem);
+  else
+    gemm_big_body<E2>(g2, ksplit, part, blockIdx.x - nfirst, smem);
 }
 
 // C[m][n] = bf16(sum over splits of part[s][m][n]), splits in order. grid-stride over float4.
@@ -496,62 +510,28 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(const __bf16* src, 
   }
 }
 
-// Helper stream and events of the In-Place path, one set per device, created on first use and
-// kept for the life of the process. The stream has the default priority.
-struct InplaceStreams {
-  hipStream_t zs = nullptr;
-  hipEvent_t start = nullptr, zdone[2] = {nullptr, nullptr}, zfree[2] = {nullptr, nullptr};
-};
-static hipError_t inplace_streams(InplaceStreams** out) {
-  static std::mutex mu;
-  static InplaceStreams sets[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  InplaceStreams& s = sets[dev];
-  if (!s.zs) {
-    InplaceStreams t;
-    e = hipStreamCreateWithFlags(&t.zs, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&t.start, hipEventDisableTiming);
-    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
-      e = hipEventCreateWithFlags(&t.zdone[i], hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&t.zfree[i], hipEventDisableTiming);
-    }
-    if (e != hipSuccess) return e;
-    s = t;
-  }
-  *out = &s;
-  return hipSuccess;
-}
-
 // One TN GEMM: the large-tile kernel where the shape fits its tile, else the 128 x 128 kernel.
 // EPI_STORE with ksplit > 1 goes through fp32 partials in `part` and the split sum.
 template <int EPI>
-static hipError_t run_gemm(const gemm::Args& g, int ksplit, float* part, hipStream_t st) {
+static hipError_t run_gemm(int cls, const gemm::Args& g, int ksplit, float* part, hipStream_t st) {
   if (EPI == gemm::EPI_RMW && g.M % gemm2::BM == 0 && g.N % gemm2::PP_BN == 0 && g.K % gemm2::BK == 0 &&
       g.K >= gemm2::BK) {
     const unsigned tiles = (unsigned)((g.M / gemm2::BM) * (g.N / gemm2::PP_BN));
-    hipLaunchKernelGGL(gemm2::gemm_rmw_pp_kernel, dim3(tiles), dim3(256), gemm2::PP_LDS, st, g);
-    return hipGetLastError();
+    return launch_k(cls, gemm2::gemm_rmw_pp_kernel, dim3(tiles), dim3(256), gemm2::PP_LDS, st, g);
   }
   if (gemm2::fits<EPI>(g)) {
     const unsigned tiles = (unsigned)((g.M / gemm2::BM) * (g.N / gemm2::tile_n<EPI>()));
     if (EPI == gemm::EPI_STORE && ksplit > 1) {
-      hipLaunchKernelGGL(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, dim3(tiles * ksplit), dim3(gemm2::THREADS),
-                         gemm2::LDS, st, g, ksplit, part);
-      hipError_t e = hipGetLastError();
+      hipError_t e = launch_k(cls, gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, dim3(tiles * ksplit),
+                              dim3(gemm2::THREADS), gemm2::LDS, st, g, ksplit, part);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(gemm2::ksplit_sum_kernel, dim3(1024), dim3(256), 0, st, part, ksplit, g.M, g.N, g.C, g.ldc);
-    } else {
-      hipLaunchKernelGGL(gemm2::gemm_big_kernel<EPI>, dim3(tiles), dim3(gemm2::THREADS), gemm2::LDS, st, g, 1, part);
+      return hipGetLastError();
     }
-  } else {
-    const dim3 grid((unsigned)(g.N / gemm::BN), (unsigned)(g.M / gemm::BM));
-    hipLaunchKernelGGL(gemm::gemm_tn_kernel<EPI>, grid, dim3(256), gemm::lds_bytes<EPI>(), st, g);
+    return launch_k(cls, gemm2::gemm_big_kernel<EPI>, dim3(tiles), dim3(gemm2::THREADS), gemm2::LDS, st, g, 1, part);
   }
-  return hipGetLastError();
+  const dim3 grid((unsigned)(g.N / gemm::BN), (unsigned)(g.M / gemm::BM));
+  return launch_k(cls, gemm::gemm_tn_kernel<EPI>, grid, dim3(256), gemm::lds_bytes<EPI>(), st, g);
 }
 
 }  // namespace ttt
@@ -622,15 +602,14 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
   const __bf16* Vb = static_cast<const __bf16*>(Vbar);
   __bf16* Ob = static_cast<__bf16*>(O);
   const int nch = q.N / q.chunk;
-  // Z depends only on the inputs and W_gate / W_up, so it runs on a helper stream: Z of chunk i
-  // into buffer i % 2 after the chunk that last read that buffer was written (event zfree), and
-  // the caller's stream waits for it (event zdone) before the chunk's apply.
-  InplaceStreams* hs = nullptr;
-  TTT_HIP(inplace_streams(&hs));
-  hipStream_t zs = hs->zs;
-  TTT_HIP(hipEventRecord(hs->start, st));
-  TTT_HIP(hipStreamWaitEvent(zs, hs->start, 0));
-  bool freed[2] = {false, false};
+  // Z of a chunk depends only on H and W_gate / W_up. Where both products take the large-tile
+  // kernel, chunk i + 1's Z (into buffer (i + 1) % 2, whose last readers -- chunk i - 1's apply
+  // and update -- came earlier on the stream) is formed in the same launch as chunk i's apply, so
+  // the two fill the chip together; everything runs on the caller's stream.
+  const bool paired = gemm2::fits<EPI_SWIGLU>(za) && gemm2::fits<EPI_STORE>(aa) && ks_apply > 1;
+  const unsigned ztiles = (unsigned)((za.M / gemm2::BM) * (za.N / gemm2::tile_n<EPI_SWIGLU>()));
+  const unsigned atiles = (unsigned)((aa.M / gemm2::BM) * (aa.N / gemm2::tile_n<EPI_STORE>())) * (unsigned)ks_apply;
+  if (paired) TTT_HIP(allow_lds(gemm2::gemm_big_pair_kernel<EPI_SWIGLU, gemm2::EPI_PARTIAL>, gemm2::LDS));
   for (int b = 0; b < q.B; ++b) {
     float* Wf = W_down_out ? W_down_out + (int64_t)b * nW : reinterpret_cast<float*>(ws + oWf);
     TTT_HIP(hipMemcpyAsync(Wf, W_down + (int64_t)b * q.wdown_batch_stride, (size_t)nW * 4,
@@ -644,13 +623,9 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
                          Vb + (int64_t)b * q.N * q.d_model, Vt, q.N, q.d_model);
       TTT_HIP(hipGetLastError());
     }
-    for (int i = 0; i < nch; ++i) {
-      const int64_t t0 = (int64_t)i * q.chunk;
-      const int zb = i & 1;
-      __bf16* Z = Zb[zb];
-      __bf16* Zt = Ztb[zb];
+    auto zargs = [&](int i) {
       Args z{};
-      z.A = Hb + ((int64_t)b * q.N + t0) * q.d_model;
+      z.A = Hb + ((int64_t)b * q.N + (int64_t)i * q.chunk) * q.d_model;
       z.lda = q.d_model;
       z.B0 = static_cast<const __bf16*>(W_gate);
       z.B1 = static_cast<const __bf16*>(W_up);
@@ -658,19 +633,18 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       z.M = q.chunk;
       z.N = q.d_hidden;
       z.K = q.d_model;
-      z.C = Z;
+      z.C = Zb[i & 1];
       z.ldc = q.d_hidden;
-      z.Ct = Zt;
+      z.Ct = Ztb[i & 1];
       z.ldct = q.chunk;
-      if (freed[zb]) TTT_HIP(hipStreamWaitEvent(zs, hs->zfree[zb], 0));
-      {
-        LaunchTimer lt(K_INP_Z, zs);
-        TTT_HIP(run_gemm<EPI_SWIGLU>(z, 1, part, zs));
-      }
-      TTT_HIP(hipEventRecord(hs->zdone[zb], zs));
-      TTT_HIP(hipStreamWaitEvent(st, hs->zdone[zb], 0));
+      return z;
+    };
+    if (paired) TTT_HIP(run_gemm<EPI_SWIGLU>(K_INP_Z, zargs(0), 1, part, st));
+    for (int i = 0; i < nch; ++i) {
+      const int64_t t0 = (int64_t)i * q.chunk;
+      const int zb = i & 1;
       Args a{};
-      a.A = Z;
+      a.A = Zb[zb];
       a.lda = q.d_hidden;
       a.B0 = Wsh;
       a.ldb = q.d_hidden;
@@ -679,14 +653,24 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       a.K = q.d_hidden;
       a.C = Ob + ((int64_t)b * q.N + t0) * q.d_model;
       a.ldc = q.d_model;
-      {
-        LaunchTimer lt(K_INP_APPLY, st);
-        TTT_HIP(run_gemm<EPI_STORE>(a, ks_apply, part, st));
+      if (paired) {
+        // apply of chunk i (K-split partials) with the Z of chunk i + 1, then the split sum
+        const bool next = i + 1 < nch;
+        const Args zn = next ? zargs(i + 1) : Args{};
+        TTT_HIP(launch_k(next ? K_INP_APPLY_Z : K_INP_APPLY, gemm2::gemm_big_pair_kernel<EPI_SWIGLU, gemm2::EPI_PARTIAL>,
+                         dim3((next ? ztiles : 0u) + atiles), dim3(gemm2::THREADS), gemm2::LDS, st, zn,
+                         (int)(next ? ztiles : 0u), a, ks_apply, part));
+        hipLaunchKernelGGL(gemm2::ksplit_sum_kernel, dim3(1024), dim3(256), 0, st, part, ks_apply, a.M, a.N, a.C,
+                           a.ldc);
+        TTT_HIP(hipGetLastError());
+      } else {
+        TTT_HIP(run_gemm<EPI_SWIGLU>(K_INP_Z, zargs(i), 1, part, st));
+        TTT_HIP(run_gemm<EPI_STORE>(K_INP_APPLY, a, ks_apply, part, st));
       }
       Args u{};
       u.A = Vt + t0;
       u.lda = q.N;
-      u.B0 = Zt;
+      u.B0 = Ztb[zb];
       u.ldb = q.chunk;
       u.M = q.d_model;
       u.N = q.d_hidden;
@@ -695,12 +679,7 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       u.Wsh = Wsh;
       u.ldw = q.d_hidden;
       u.alpha = q.eta;
-      {
-        LaunchTimer lt(K_INP_UPDATE, st);
-        TTT_HIP(run_gemm<EPI_RMW>(u, 1, part, st));
-      }
-      TTT_HIP(hipEventRecord(hs->zfree[zb], st));
-      freed[zb] = true;
+      TTT_HIP(run_gemm<EPI_RMW>(K_INP_UPDATE, u, 1, part, st));
     }
   }
   return TTT_OK;

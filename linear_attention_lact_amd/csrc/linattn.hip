@@ -217,10 +217,14 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
   fa.inclusive = p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0;
   fa.w_batch_stride = p.w_batch_stride;
   // chunks per workgroup: the workgroups hold one CU each (LDS), so groups of G chunks bring the
-  // grid down to one round of 256 where the chunk splits into whole query passes
+  // grid down to one round over the device's CUs where the chunk splits into whole query passes
   constexpr int PASS = FusedLayout<OpT, H, RH>::NW * 32;
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || ncu <= 0)
+    return TTT_ERR_HIP;
   int G = 1;
-  while (G < 8 && (int64_t)8 * ((P + 7) / 8) * (nch / G) > 256 && nch % (2 * G) == 0 && p.chunk % PASS == 0)
+  while (G < 8 && (int64_t)8 * ((P + 7) / 8) * (nch / G) > ncu && nch % (2 * G) == 0 && p.chunk % PASS == 0)
     G *= 2;
   fa.group = G;
   {
@@ -228,10 +232,8 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
     hipLaunchKernelGGL(linattn_fused_reset, dim3(1), dim3(256), 0, st, fa.tickets, fa.flags, P * nch);
     TTT_HIP(hipGetLastError());
   }
-  LaunchTimer lt(K_LIN_FUSED, st);
   const unsigned grid = 8u * (unsigned)((P + 7) / 8) * (unsigned)(nch / G);
-  hipLaunchKernelGGL(fk, dim3(grid), dim3(FusedLayout<OpT, H, RH>::NT), lds, st, fa);
-  TTT_HIP(hipGetLastError());
+  TTT_HIP(launch_k(K_LIN_FUSED, fk, dim3(grid), dim3(FusedLayout<OpT, H, RH>::NT), lds, st, fa));
   return TTT_OK;
 }
 
@@ -262,28 +264,33 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   const int64_t n = rh64 * q.h;
   const size_t opsz = bf16 ? 2 : 4;
   // single pass for bf16 I/O and (h, rh) in {(32, 64), (32, 128), (64, 128)}
-  const bool fused = bf16 && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
-                     (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31 &&  // buffer offsets are 32-bit
-                     (int64_t)q.N * q.h * 2 < (int64_t)1 << 31;
-  WorkspacePlan plan;
-  size_t oSh = 0, odS = 0, oSt = 0, oAgg = 0, oIncl = 0, oInclM = 0, oFl = 0, oTk = 0;
+  // the single-pass kernel keeps each pair's chunks on one XCD (its L2 is where the chunks
+  // exchange their sums): it needs a device of 8 XCDs, which dispatches workgroups to them in turn
+  int dev = 0, nxcc = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess)
+    nxcc = 0;
+  const bool fused_shape = bf16 && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
+                           (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31 &&  // buffer offsets are 32-bit
+                           (int64_t)q.N * q.h * 2 < (int64_t)1 << 31;
+  const bool fused = fused_shape && nxcc == 8;
+  // both plans; the size asked for covers the larger where the single-pass shape applies, so a
+  // query gives the same answer on any device (and without one)
+  WorkspacePlan fplan, mplan;
   const bool mom = q.momentum != 0.f;
-  if (fused) {
-    oAgg = plan.add((size_t)P * nch * n * 4);
-    oIncl = plan.add((size_t)P * nch * n * 4);
-    if (mom) oInclM = plan.add((size_t)P * nch * n * 4);
-    oFl = plan.add((size_t)P * nch * 4);
-    oTk = plan.add(16 * 4);
-  } else {
-    oSh = plan.add((size_t)P * 2 * n * opsz);
-    odS = plan.add((size_t)P * nch * n * 4);
-    oSt = plan.add((size_t)P * nch * n * opsz);
-  }
+  const size_t oAgg = fplan.add((size_t)P * nch * n * 4);
+  const size_t oIncl = fplan.add((size_t)P * nch * n * 4);
+  const size_t oInclM = mom ? fplan.add((size_t)P * nch * n * 4) : 0;
+  const size_t oFl = fplan.add((size_t)P * nch * 4);
+  const size_t oTk = fplan.add(16 * 4);
+  const size_t oSh = mplan.add((size_t)P * 2 * n * opsz);
+  const size_t odS = mplan.add((size_t)P * nch * n * 4);
+  const size_t oSt = mplan.add((size_t)P * nch * n * opsz);
+  const size_t need = fused_shape ? std::max(fplan.total, mplan.total) : mplan.total;
   if (!workspace) {
-    *workspace_bytes = plan.total;
+    *workspace_bytes = need;
     return TTT_OK;
   }
-  if (*workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TTT_ERR_WORKSPACE;
+  if (*workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TTT_ERR_WORKSPACE;
   if (P == 0) return TTT_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (nch == 0) {  // empty sequences: the final state is W1

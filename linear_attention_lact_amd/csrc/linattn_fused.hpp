@@ -22,9 +22,13 @@
 // Cross-workgroup visibility: all chunks of a pair run on one XCD, whose L2 is the point of
 // coherence. A writer drains its stores (s_waitcnt vmcnt(0)) before a relaxed device-scope flag
 // store; readers poll the flag with device-scope loads and read the data with device-scope loads,
-// which miss in the per-CU L1. Forward progress: a workgroup takes a ticket from its XCD's counter
-// (hardware XCC id) and works on the ticket-th (pair, chunk) of that XCD in chunk order, so every
-// predecessor it may wait for holds a smaller ticket, i.e. has started. Waits are bounded; a timeout
+// which miss in the per-CU L1. Work lists: list x holds the (pair, group) items of the pairs
+// p = x (mod 8) in pair-then-group order; a workgroup takes a ticket from the counter of its XCD
+// (hardware XCC id) and works on that item of list x, so a pair's groups share one L2 (the L2s of
+// different XCDs are not coherent with each other for these accesses). This needs a device of 8
+// XCDs that dispatches the workgroups of a launch to the XCDs in turn (grid / 8 per XCD); the host
+// takes this path only on such a device. Forward progress: every predecessor a workgroup may wait
+// for holds a smaller ticket of the same list, i.e. has started. Waits are bounded; a timeout
 // raises the error word and the chunk's outputs are written as NaN.
 #pragma once
 #include "fastweight.hpp"

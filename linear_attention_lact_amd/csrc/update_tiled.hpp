@@ -8,8 +8,10 @@
 // instead of one workgroup per matrix.
 //
 // Newton-Schulz takes the explicit form X <- aX + (bA + cA^2) X with A = X X^T, X the h x rh
-// transpose of the write. Operands are fp32 in an L2-resident scratch; each product is the
-// split-bf16 MFMA (hi*hi + hi*lo + lo*hi, fp32 accumulation). A tile is 4 waves, each summing
+// transpose of the write. Operands are fp32 in an L2-resident scratch; with 16-bit I/O each
+// product is the split-bf16 MFMA (hi*hi + hi*lo + lo*hi, fp32 accumulation), with fp32 I/O the
+// fp32 MFMA (exact fp32 products: the iteration amplifies rounding in weak singular directions
+// by up to 3.4445^5, which a 2^-16 split would carry into the result). A tile is 4 waves, each summing
 // a quarter of the contraction; the quarters are added in wave order, so results do not depend
 // on scheduling. A and B = bA + cA^2 are symmetric: their upper-triangle tiles are computed and
 // mirrored.
@@ -103,6 +105,7 @@ struct TuLds {
   float tile[32][33];
 };
 
+template <bool EXACT>
 __device__ __forceinline__ void tu_partial(TuLds& L, const float* a, int lda, const float* b, int ldb, int K) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nk = K / 16;
@@ -126,7 +129,13 @@ __device__ __forceinline__ void tu_partial(TuLds& L, const float* a, int lda, co
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (kb + 16 * j < k1) {
+      if (EXACT && kb + 16 * j < k1) {
+        // fp32 MFMA, K step 2: in step e lane half g supplies element 8 g + e of its 8 loaded
+        // values, the same permutation for both operands, so the 8 steps cover the 16 k
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j][e >> 2][e & 3], bv[j][e >> 2][e & 3], acc, 0, 0, 0);
+      } else if (kb + 16 * j < k1) {
         bf16x8 ah, al, bh, bl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -163,6 +172,7 @@ __device__ __forceinline__ void tu_tri(int t, int hb, int& ib, int& kb) {
 }
 
 // A = X X^T. grid (hb(hb+1)/2, 3, P).
+template <bool EXACT>
 __global__ void __launch_bounds__(256) tu_gram_kernel(UpdateArgs u, int cur) {
   const LactState& s = u.s;
   const int mat = blockIdx.y, pair = blockIdx.z;
@@ -173,7 +183,7 @@ __global__ void __launch_bounds__(256) tu_gram_kernel(UpdateArgs u, int cur) {
   int ib, kb;
   tu_tri(blockIdx.x, h / 32, ib, kb);
   const float* X = nv.X[cur];
-  tu_partial(L, X + (int64_t)ib * 32 * rh, rh, X + (int64_t)kb * 32 * rh, rh, rh);
+  tu_partial<EXACT>(L, X + (int64_t)ib * 32 * rh, rh, X + (int64_t)kb * 32 * rh, rh, rh);
   const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
   f32x4 v, m;
 #pragma unroll
@@ -186,6 +196,7 @@ __global__ void __launch_bounds__(256) tu_gram_kernel(UpdateArgs u, int cur) {
 }
 
 // B = b A + c A A (A symmetric, so (AA)[i][k] = sum_m A[i][m] A[k][m]). grid (hb(hb+1)/2, 3, P).
+template <bool EXACT>
 __global__ void __launch_bounds__(256) tu_poly_kernel(UpdateArgs u) {
   const LactState& s = u.s;
   const int mat = blockIdx.y, pair = blockIdx.z;
@@ -195,7 +206,7 @@ __global__ void __launch_bounds__(256) tu_poly_kernel(UpdateArgs u) {
   const int h = s.h;
   int ib, kb;
   tu_tri(blockIdx.x, h / 32, ib, kb);
-  tu_partial(L, nv.A + ib * 32 * h, h, nv.A + kb * 32 * h, h, h);
+  tu_partial<EXACT>(L, nv.A + ib * 32 * h, h, nv.A + kb * 32 * h, h, h);
   const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
   const f32x4 a = *reinterpret_cast<const f32x4*>(nv.A + (ib * 32 + r) * h + kb * 32 + c4);
   const f32x4 at = *reinterpret_cast<const f32x4*>(nv.A + (kb * 32 + r) * h + ib * 32 + c4);
@@ -210,6 +221,7 @@ __global__ void __launch_bounds__(256) tu_poly_kernel(UpdateArgs u) {
 }
 
 // X' = a X + B X, written as X' [h][rh] and Y' = X'^T [rh][h]. grid (h/32 * rh/32, 3, P).
+template <bool EXACT>
 __global__ void __launch_bounds__(256) tu_xupd_kernel(UpdateArgs u, int cur) {
   const LactState& s = u.s;
   const int mat = blockIdx.y, pair = blockIdx.z;
@@ -218,7 +230,7 @@ __global__ void __launch_bounds__(256) tu_xupd_kernel(UpdateArgs u, int cur) {
   const NsView nv = ns_view(s, pair, mat);
   const int h = s.h, rh = s.rh, rb = rh / 32;
   const int ib = blockIdx.x / rb, jb = blockIdx.x % rb;
-  tu_partial(L, nv.B + ib * 32 * h, h, nv.Y[cur] + (int64_t)jb * 32 * h, h, h);
+  tu_partial<EXACT>(L, nv.B + ib * 32 * h, h, nv.Y[cur] + (int64_t)jb * 32 * h, h, h);
   const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
   const int64_t xo = (int64_t)(ib * 32 + r) * rh + jb * 32 + c4;
   const f32x4 x = *reinterpret_cast<const f32x4*>(nv.X[cur] + xo);
@@ -337,9 +349,10 @@ static hipError_t tu_run(const UpdateArgs& ua, hipStream_t st) {
   if (ua.muon) {
     hipLaunchKernelGGL(tu_scale_kernel, dim3(nt, 3, P), blk, 0, st, ua, (int)nt);
     for (int it = 0; it < NS_STEPS; ++it) {
-      hipLaunchKernelGGL(tu_gram_kernel, dim3(ntri, 3, P), blk, 0, st, ua, cur);
-      hipLaunchKernelGGL(tu_poly_kernel, dim3(ntri, 3, P), blk, 0, st, ua);
-      hipLaunchKernelGGL(tu_xupd_kernel, dim3(nt, 3, P), blk, 0, st, ua, cur);
+      constexpr bool EXACT = std::is_same<OpT, float>::value;
+      hipLaunchKernelGGL(tu_gram_kernel<EXACT>, dim3(ntri, 3, P), blk, 0, st, ua, cur);
+      hipLaunchKernelGGL(tu_poly_kernel<EXACT>, dim3(ntri, 3, P), blk, 0, st, ua);
+      hipLaunchKernelGGL(tu_xupd_kernel<EXACT>, dim3(nt, 3, P), blk, 0, st, ua, cur);
       cur ^= 1;
     }
   }

@@ -1,6 +1,6 @@
 """GPU parity of ttt_inplace_down_forward against the CPU oracle: full recurrence at small
 sizes; at the full In-Place size (d_model 4096, d_hidden 14336, seq 32768, chunk 1024) sampled
-final fast-weight columns and output rows of the first two chunks."""
+final fast-weight columns and output rows of the first two, a middle and the last chunk."""
 import numpy as np
 import pytest
 
@@ -46,7 +46,10 @@ def test_config4_full_size_sampled(lib):
     x = make_inplace_inputs(p, 4)
     O, W = _gpu(lib, p, x)
     cols = [0, 777, 8191, 14335]
-    rows = [0, 511, 1023, 1024, 1500, 2047]
+    # rows of the first two chunks, a middle chunk (16) and the last chunk (31): the late rows
+    # see the writes of every earlier chunk
+    rows = [0, 511, 1023, 1024, 1500, 2047, 16 * 1024 + 3, 16 * 1024 + 700, 31 * 1024, 31 * 1024 + 555,
+            32 * 1024 - 1]
     f32 = np.float32
     refW = IP.final_wdown_columns(x["Hs"][0], x["W_gate"], x["W_up"], x["W_down"], x["Vbar"][0],
                                   float(x["eta"]), cols, dtype=f32)

@@ -11,12 +11,22 @@ pytestmark = pytest.mark.gpu
 
 
 def _compare(gpu, ref, tol, pairs=None, label=""):
+    """Every output of the call against the oracle: O, the final fast weights and the final
+    momentum (M_out [B,H,3,h*rh] holds W0 [h,rh], W1 [rh,h], W2 [h,rh] in row form)."""
     O, W0, W1, W2, M = gpu
     errs = {}
     sel = (lambda a: a) if pairs is None else (lambda a: np.stack([a[b, h] for b, h in pairs]))
     errs["O"] = max_abs_rel(sel(host(O)), sel(ref["O"]))
     for name, g in (("W0", W0), ("W1", W1), ("W2", W2)):
         errs[name] = max_abs_rel(sel(host(g)), sel(ref[name]))
+    Mh = host(M)
+    for i, name in enumerate(("M0", "M1", "M2")):
+        m = sel(Mh[:, :, i].reshape(ref[name].shape))
+        r = sel(ref[name])
+        if np.max(np.abs(r)) == 0.0:  # no momentum, or a matrix outside the update mask
+            assert np.all(m == 0.0), (label, name)
+        else:
+            errs[name] = max_abs_rel(m, r)
     print(f"{label} errors: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     for k, v in errs.items():
         assert v <= tol, (label, k, v)
@@ -48,6 +58,11 @@ CASES = [
     ("bf16 single chunk UA", dict(h=64, Nq=256, Nk=256, chunk_q=256, chunk_kv=256, muon=True, order=1), 10),
     ("fp32 h64 muon mom", dict(h=64, Nq=256, Nk=256, chunk_q=64, chunk_kv=64, dtype=FP32, muon=True, momentum=0.9), 11),
     ("fp32 h32 UA ragged", dict(h=32, Nq=200, Nk=200, chunk_q=40, chunk_kv=40, dtype=FP32, order=1, momentum=0.9), 12),
+    # as many chunks as the LM and tiny workloads have (16), with Muon and momentum, in fp32
+    ("fp32 h64 muon mom 16 chunks", dict(h=64, Nq=1024, Nk=1024, chunk_q=64, chunk_kv=64, dtype=FP32, muon=True,
+                                         momentum=0.9), 13),
+    ("fp32 h32 muon mom renorm 16 chunks UA", dict(h=32, Nq=1024, Nk=1024, chunk_q=64, chunk_kv=64, dtype=FP32,
+                                                   muon=True, momentum=0.9, order=1), 14),
 ]
 
 
