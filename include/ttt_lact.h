@@ -190,6 +190,29 @@ ttt_status ttt_linattn_forward(const ttt_linattn_params* p,
                                void* workspace, size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * ttt_linattn_forward_noalloc
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same operation, arguments, layouts and results as
+ * ttt_linattn_forward, without a workspace: the scratch (chunk aggregates, prefixes, flags and
+ * ticket counters) lives in a device array inside the library, TTT_NOALLOC_SCRATCH_BYTES per GPU,
+ * created with the library's code object on each GPU it runs on and held until the process ends.
+ * The entry point calls no allocating routine. A call that needs more scratch than that (the
+ * size ttt_linattn_forward's workspace query reports) returns TTT_ERR_WORKSPACE before any
+ * launch, with the sizes in ttt_last_error(). Every call on a GPU uses that GPU's one array and
+ * leaves its contents behind (what must start at zero is cleared by a kernel at the start of
+ * each call): calls that overlap in time on one GPU race and give undefined results, so issue
+ * them on one stream or otherwise one after another. The first call on a device looks up the
+ * array's address (one hipGetSymbolAddress per device, then cached).
+ * ---------------------------------------------------------------------------------------- */
+#define TTT_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+ttt_status ttt_linattn_forward_noalloc(const ttt_linattn_params* p,
+                                       const void* Q, const void* K, const void* V, const float* eta,
+                                       const float* W0, const float* W2, const float* W1,
+                                       void* O, float* S_out, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * ttt_inplace_down_forward
  *
  * Defined by: "In-Place Test-Time Training" reading notes, section 3.1 / Eq. 2 (gated MLP

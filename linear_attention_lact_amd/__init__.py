@@ -25,8 +25,9 @@ APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
 FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
 
-EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_inplace_down_forward", "ttt_status_string",
-            "ttt_last_error", "ttt_timing_enable", "ttt_timing_collect")
+EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_linattn_forward_noalloc", "ttt_inplace_down_forward",
+            "ttt_status_string", "ttt_last_error", "ttt_timing_enable", "ttt_timing_collect")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TTT_NOALLOC_SCRATCH_BYTES
 
 
 class KernelTime(ctypes.Structure):
@@ -62,7 +63,7 @@ _szp = ctypes.POINTER(ctypes.c_size_t)
 class TTTError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
-        detail = f": {last_error()}" if status == TTT_ERR_HIP else ""
+        detail = f": {last_error()}" if status in (TTT_ERR_HIP, TTT_ERR_WORKSPACE) and last_error() else ""
         super().__init__(f"{fn} failed with status {status} ({status_string(status)}){detail}")
 
 
@@ -84,6 +85,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ttt_lact_forward.restype = ctypes.c_int32
     lib.ttt_linattn_forward.argtypes = [ctypes.POINTER(LinattnParams)] + [_vp] * 9 + [_vp, _szp, _vp]
     lib.ttt_linattn_forward.restype = ctypes.c_int32
+    lib.ttt_linattn_forward_noalloc.argtypes = [ctypes.POINTER(LinattnParams)] + [_vp] * 9 + [_vp]
+    lib.ttt_linattn_forward_noalloc.restype = ctypes.c_int32
     lib.ttt_inplace_down_forward.argtypes = [ctypes.POINTER(InplaceParams)] + [_vp] * 7 + [_vp, _szp, _vp]
     lib.ttt_inplace_down_forward.restype = ctypes.c_int32
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -249,6 +252,18 @@ def linattn_forward(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_
     """Last-layer-only linear-attention scan. Q/K/V [B,H,N,h], eta [B,H,N], W0/W2 [(B,)H,h,rh],
     W1 [(B,)H,rh,h]; momentum: heavy-ball coefficient per chunk (0 <= momentum < 1).
     Returns (O, S_out) with S_out [B,H,rh,h] (None if not want_state)."""
+    return _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, want_state, stream, noalloc=False)
+
+
+def linattn_forward_noalloc(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_THEN_UPDATE,
+                            momentum: float = 0.0, want_state: bool = True, stream=None):
+    """linattn_forward without a workspace: the library's per-device scratch array
+    (NOALLOC_SCRATCH_BYTES) serves as the workspace, so the call allocates no device memory
+    besides the outputs it returns. Calls on one GPU share the array: do not overlap them."""
+    return _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, want_state, stream, noalloc=True)
+
+
+def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, want_state, stream, noalloc):
     torch = _torch()
     lib = load()
     B, H, N, h = Q.shape
@@ -270,7 +285,12 @@ def linattn_forward(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_
     O = torch.empty_like(Q)
     S = torch.empty((B, H, rh, h), dtype=torch.float32, device=dev) if want_state else None
     base = [ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(eta), _ptr(W0), _ptr(W2), _ptr(W1), _ptr(O), _ptr(S)]
-    _call("ttt_linattn_forward", lib.ttt_linattn_forward, base, base, dev, stream)
+    if noalloc:
+        st = lib.ttt_linattn_forward_noalloc(*base, _stream(stream))
+        if st != TTT_OK:
+            raise TTTError("ttt_linattn_forward_noalloc", st)
+    else:
+        _call("ttt_linattn_forward", lib.ttt_linattn_forward, base, base, dev, stream)
     return O, S
 
 

@@ -1,5 +1,6 @@
 // api.cpp -- status strings and the optional kernel-timing recorder of the C ABI.
 #include <hip/hip_runtime.h>
+#include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -28,6 +29,13 @@ void note_hip_error(const char* what, hipError_t e, const char* file, int line) 
   const char* base = std::strrchr(file, '/');
   std::snprintf(last_error, sizeof last_error, "%s (%s) at %s:%d: %s", hipGetErrorName(e), hipGetErrorString(e),
                 base ? base + 1 : file, line, what);
+}
+
+void note_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(last_error, sizeof last_error, fmt, ap);
+  va_end(ap);
 }
 }  // namespace ttt
 

@@ -11,6 +11,8 @@ namespace ttt {
 
 // Records the failing HIP call for ttt_last_error() (per host thread).
 void note_hip_error(const char* what, hipError_t e, const char* file, int line);
+// Records a printf-style message for ttt_last_error() (per host thread).
+void note_error(const char* fmt, ...);
 
 #define TTT_HIP(expr)                                        \
   do {                                                       \

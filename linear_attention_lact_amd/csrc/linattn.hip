@@ -9,6 +9,8 @@
 //          (with momentum, each dS_j weighted by its cumulative coefficient, Theorem 5.3)
 //   O_c  = phi(Q_c) S_c                                   (apply_kernel with per-chunk S_c)
 // The chunk prefix is an exclusive (or inclusive) scan over the chunks of each pair.
+#include <mutex>
+
 #include "fastweight.hpp"
 #include "linattn_fused.hpp"
 #include "host.hpp"
@@ -348,4 +350,54 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
     return TTT_ERR_HIP;
   }
 #undef TTT_LIN_CASE
+}
+
+// ---------------------------------------------------------------------------------------
+// Allocation-free variant: the workspace is a file-scope device array of fixed size, one copy
+// per GPU the library runs on (held until the process ends). Its device address is looked up
+// once per device with that device current; host code uses only that address.
+namespace ttt {
+namespace {
+__device__ __align__(256) unsigned char noalloc_scratch[TTT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+}  // namespace ttt
+
+extern "C" ttt_status ttt_linattn_forward_noalloc(const ttt_linattn_params* p, const void* Q, const void* K,
+                                                  const void* V, const float* eta, const float* W0,
+                                                  const float* W2, const float* W1, void* O, float* S_out,
+                                                  void* stream) {
+  size_t need = 0;
+  const ttt_status q = ttt_linattn_forward(p, Q, K, V, eta, W0, W2, W1, O, S_out, nullptr, &need, stream);
+  if (q != TTT_OK) return q;
+  if (need > (size_t)TTT_NOALLOC_SCRATCH_BYTES) {
+    note_error("ttt_linattn_forward_noalloc: the call needs %zu bytes of scratch, more than the %zu the "
+               "library holds per device; use ttt_linattn_forward with a workspace",
+               need, (size_t)TTT_NOALLOC_SCRATCH_BYTES);
+    return TTT_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  TTT_HIP(noalloc_scratch_ptr(&ws));
+  size_t have = TTT_NOALLOC_SCRATCH_BYTES;
+  return ttt_linattn_forward(p, Q, K, V, eta, W0, W2, W1, O, S_out, ws, &have, stream);
 }
