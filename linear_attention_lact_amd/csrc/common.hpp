@@ -292,6 +292,11 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
+// The XCD (accelerator complex die) this wave runs on (HW_REG_XCC_ID[3:0]).
+__device__ __forceinline__ unsigned hw_xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15;
+}
+
 // Workgroup barrier that orders LDS accesses only: global memory operations of the waves may
 // still be in flight when it releases (__syncthreads would wait for them as well).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -561,8 +561,10 @@ constexpr int grad_ws_lds_bytes() {
   return 3 * 2 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + 3 * TT * 4 + 2 * 4 * 3 * 2 * 64 * 16;
 }
 
+// Workgroup index bid: XCD slot bid & 7; slot = bid >> 3 holds hidden block slot % njb of the
+// (pair, segment) group (bid & 7) + 8 (slot / njb), group = pair * nseg + segment.
 template <class IoT, class OpT, int H, bool SCALE_MID>
-__global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int npairs) {
+__device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int npairs, int bid, unsigned char* smem) {
   static_assert(std::is_same<OpT, _Float16>::value && (H == 64 || H == 128), "fp16 operands, h = 64 or 128");
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
@@ -574,14 +576,13 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
   constexpr int KS = H / M::KSTEP;          // forward K steps over h
   constexpr int QS = 32 / M::KSTEP;         // contraction K steps over a 32-token half
 
-  extern __shared__ __align__(16) unsigned char smem[];
   OpT* tiles = reinterpret_cast<OpT*>(smem);                      // [3 buffers][K, V][TT][LD]
   float* eta_s = reinterpret_cast<float*>(tiles + 3 * 2 * TILE);  // [3 buffers][TT] scaled step sizes
   frag* inter = reinterpret_cast<frag*>(eta_s + 3 * TT);          // [2][4 forward waves][3][QS][64]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int njb = a.rh / RB;
-  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int xcd = bid & 7, slot = bid >> 3;
   const int jb = slot % njb;
   const int group = xcd + 8 * (slot / njb);
   if (group >= npairs * nseg) return;
@@ -746,6 +747,12 @@ __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int 
       for (int r = 0; r < 16; ++r) o[acc_row(r, lane) * H + acc_col(lane)] = acc[m][cc][r] * inv;
     }
   }
+}
+
+template <class IoT, class OpT, int H, bool SCALE_MID>
+__global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int npairs) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  grad_ws_body<IoT, OpT, H, SCALE_MID>(a, nseg, npairs, blockIdx.x, smem);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -59,9 +59,6 @@ struct FusedArgs {
 
 constexpr long FUSED_SPIN_LIMIT = 1l << 20;
 
-__device__ __forceinline__ unsigned hw_xcc_id() {
-  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15;  // HW_REG_XCC_ID[3:0]
-}
 __device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ unsigned flag_load(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

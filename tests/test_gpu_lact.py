@@ -63,6 +63,13 @@ CASES = [
                                          momentum=0.9), 13),
     ("fp32 h32 muon mom renorm 16 chunks UA", dict(h=32, Nq=1024, Nk=1024, chunk_q=64, chunk_kv=64, dtype=FP32,
                                                    muon=True, momentum=0.9, order=1), 14),
+    # larger chunks with pair counts that do not fill the XCDs evenly (4, 6, 12 pairs)
+    ("bf16 h128 chunk 512", dict(h=128, Nq=2048, Nk=2048, chunk_q=512, chunk_kv=512, muon=True,
+                                               momentum=0.9), 15),
+    ("bf16 h64 chunk 1024 6 pairs", dict(B=2, H=3, h=64, Nq=4096, Nk=4096, chunk_q=1024,
+                                                       chunk_kv=1024, muon=True, momentum=0.9), 16),
+    ("bf16 h128 sgd 12 pairs", dict(B=3, H=4, h=128, Nq=2048, Nk=2048, chunk_q=1024, chunk_kv=1024,
+                                                  momentum=0.5), 17),
 ]
 
 
@@ -135,10 +142,13 @@ def test_empty_sequence_returns_initial_state(lib):
     assert np.all(host(Mo) == 0)
 
 
-def test_runs_are_bitwise_deterministic(lib):
-    p = LactProblem(B=2, H=2, h=128, r=2, Nq=1024, Nk=1024, chunk_q=256, chunk_kv=256, dtype=BF16,
+@pytest.mark.parametrize("chunk", [256, 512])
+def test_runs_are_bitwise_deterministic(lib, chunk):
+    """Fixed-order reductions make repeated calls bit-identical (two chunk sizes, so two segment
+    splits of the gradient)."""
+    p = LactProblem(B=2, H=4, h=128, r=2, Nq=2048, Nk=2048, chunk_q=chunk, chunk_kv=chunk, dtype=BF16,
                     muon=True, momentum=0.9, v_normalised=False)
-    announce("lact determinism")
+    announce(f"lact determinism chunk {chunk}")
     x = make_lact_inputs(p, 51)
     a = lact_on_gpu(lib, p, x)
     b = lact_on_gpu(lib, p, x)
