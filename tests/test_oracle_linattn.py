@@ -113,3 +113,82 @@ def test_momentum_weight_is_geometric_sum(order):
                 n = c - i + (1 if order == 1 else 0)
                 want = 0.0 if n <= 0 else (float(n) if alpha == 1.0 else (1 - alpha ** n) / (1 - alpha))
                 assert abs(LA.momentum_weight(c, i, alpha, order) - want) < 1e-14, (alpha, c, i)
+
+
+# ---- Variant 3: phi = identity, one linear fast-weight layer with an h x h state ----
+
+def _identity_inputs(seed, h=8, N=48, B=2, H=2):
+    p = LactProblem(B=B, H=H, h=h, r=1, Nq=N, Nk=N, chunk_q=N, chunk_kv=N)
+    x = make_lact_inputs(p, seed)
+    x["eta"] = x["eta"] * 20
+    return p, x
+
+
+def _recurrent_linear_fast_weight(Q, K, V, eta, S0, chunk, order, momentum):
+    """Variant 3 as test-time training, written without the scan: the fast weight is the single
+    linear layer f(x) = x W; each chunk takes one gradient step on
+    L_c(W) = -sum_t eta_t <k_t W, v_t> at the chunk-start W (gradient from torch autograd), through
+    the heavy-ball buffer M <- alpha M + G, W <- W - M; apply-then-update reads W before the step,
+    update-then-apply after it."""
+    import torch
+    t = lambda a: torch.tensor(np.asarray(a), dtype=torch.float64)
+    Q, K, V, eta = t(Q), t(K), t(V), t(eta)
+    W = t(S0)
+    M = torch.zeros_like(W)
+    O = torch.zeros(Q.shape[0], W.shape[1], dtype=torch.float64)
+    for c in range(K.shape[0] // chunk):
+        sl = slice(c * chunk, (c + 1) * chunk)
+        if order == 0:
+            O[sl] = Q[sl] @ W
+        Wv = W.clone().requires_grad_(True)
+        loss = -(eta[sl, None] * (K[sl] @ Wv) * V[sl]).sum()
+        (G,) = torch.autograd.grad(loss, Wv)
+        M = momentum * M + G
+        W = W - M
+        if order == 1:
+            O[sl] = Q[sl] @ W
+    return O.numpy(), W.numpy()
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("momentum", [0.0, 0.6])
+@pytest.mark.parametrize("chunk", [1, 8, 48])
+def test_identity_scan_equals_recurrent_linear_fast_weight(order, momentum, chunk):
+    p, x = _identity_inputs(21)
+    for b in range(p.B):
+        for hd in range(p.H):
+            args = [x[k][b, hd] for k in ("Q", "K", "V", "eta")]
+            o, s = LA.linattn_pair(*args, None, x["W1"][hd], None, chunk=chunk, order=order,
+                                   momentum=momentum, feature_map="identity")
+            ro, rs = _recurrent_linear_fast_weight(*args, x["W1"][hd], chunk, order, momentum)
+            np.testing.assert_allclose(o, ro, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(s, rs, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("momentum", [0.0, 0.7])
+@pytest.mark.parametrize("chunk", [1, 4, 16])
+def test_identity_scan_equals_masked_quadratic_form(order, momentum, chunk):
+    p, x = _identity_inputs(22)
+    args = [x[k][0, 1] for k in ("Q", "K", "V", "eta")]
+    o, _ = LA.linattn_pair(*args, None, x["W1"][1], None, chunk=chunk, order=order, momentum=momentum,
+                           feature_map="identity")
+    q = LA.linattn_masked_quadratic(*args, None, x["W1"][1], None, chunk=chunk, order=order,
+                                    momentum=momentum, feature_map="identity")
+    np.testing.assert_allclose(o, q, rtol=1e-11, atol=1e-12)
+
+
+def test_identity_token_chunks_update_then_apply_is_causal_linear_attention():
+    """Chunks of one token with update-then-apply: textbook causal linear attention,
+    o_t = q_t (S0 + sum_{s <= t} k_s^T (eta_s v_s)), accumulated token by token."""
+    p, x = _identity_inputs(23, h=16, N=40, B=1, H=1)
+    Q, K, V, eta = (x[k][0, 0].astype(np.float64) for k in ("Q", "K", "V", "eta"))
+    S0 = x["W1"][0].astype(np.float64)
+    out = LA.linattn_forward(x["Q"], x["K"], x["V"], x["eta"], None, x["W1"], None, chunk=1, order=1,
+                             feature_map="identity")
+    state = S0.copy()
+    for t in range(40):
+        state += eta[t] * np.outer(K[t], V[t])
+        np.testing.assert_allclose(out["O"][0, 0, t], Q[t] @ state, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(out["S"][0, 0], state, rtol=1e-12, atol=1e-13)
+    assert out["S"].shape == (1, 1, 16, 16)

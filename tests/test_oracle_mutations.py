@@ -106,6 +106,10 @@ def _update_before_apply(orig):
     return f
 
 
+def _identity_scaled(orig):
+    return lambda X, W0=None, W2=None: X / np.sqrt(X.shape[1])  # an attention-style 1/sqrt(h)
+
+
 MUTATIONS = [
     # (label, module, attribute, mutation, pin that must fail)
     ("G0 sign flipped", L, "chunk_gradients", _flip_g0, lambda: TL.test_gradients_match_torch_autograd(3)),
@@ -128,6 +132,8 @@ MUTATIONS = [
      lambda: TLA.test_scan_equals_masked_quadratic_form(0, 4)),
     ("momentum coefficient exponent", LA, "momentum_weight", _momentum_exponent,
      lambda: TLA.test_momentum_scan_equals_recurrent_heavy_ball(1, 0.5)),
+    ("identity kernel rescaled", LA, "phi_identity", _identity_scaled,
+     lambda: TLA.test_identity_scan_equals_recurrent_linear_fast_weight(0, 0.0, 8)),
     ("In-Place update before apply", IP, "inplace_sequence", _update_before_apply,
      lambda: TI.test_first_chunk_is_the_plain_mlp()),
 ]
