@@ -14,8 +14,9 @@ the host cores on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
 
 --config 1 / 3 / 4 time the linear-attention scan, the view-synthesis shape and the In-Place
-update instead. The default run (the LM layer) also measures those three workloads and adds
-them to its JSON line under "other_workloads" (--no-extras skips them). The scan workload's
+update instead (--config 1 --feature-map identity: the scan with one linear fast-weight layer,
+an h x h state). The default run (the LM layer) also measures those workloads and adds them to
+its JSON line under "other_workloads" (--no-extras skips them). The scan workload's
 136 MB fit in the 256 MB last-level cache, so it is timed both warm and with a 512 MB buffer
 read between repetitions (flushed; its headline figure).
 """
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--momentum", type=float, default=0.0,
                     help="scan workload only: heavy-ball momentum per chunk (the momentum form)")
+    ap.add_argument("--feature-map", default="swiglu", choices=["swiglu", "identity"],
+                    help="scan workload only: the identity map is one linear fast-weight layer (h x h state)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--no-extras", action="store_true",
@@ -91,14 +94,16 @@ def cpu_baseline_lact(p, x, budget_s):
                       f"float32 NumPy oracle, {el:.1f} s"}
 
 
-def cpu_baseline_linattn(p, x, budget_s):
+def cpu_baseline_linattn(p, x, budget_s, feature_map="swiglu"):
     import numpy as np
     from oracle import linattn as LA
     done, t0 = 0, time.perf_counter()
     pairs = [(b, h) for b in range(p.B) for h in range(p.H)]
+    ident = feature_map == "identity"
     for (b, h) in pairs:
-        LA.linattn_pair(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["eta"][b, h], x["W0"][h], x["W1"][h],
-                        x["W2"][h], chunk=p.chunk_kv, order=p.order, momentum=p.momentum, dtype=np.float32)
+        LA.linattn_pair(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["eta"][b, h], None if ident else x["W0"][h],
+                        x["W1"][h], None if ident else x["W2"][h], chunk=p.chunk_kv, order=p.order,
+                        momentum=p.momentum, feature_map=feature_map, dtype=np.float32)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -217,7 +222,7 @@ def roofline(kern, work, bound, peak, unit):
             "work_per_launch": per_launch, "avg_launch_us": kern[dom]["avg_us"]}
 
 
-def measure(k, args, momentum=0.0, cpu=True):
+def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu"):
     """One workload: its JSON record (without the fields common to every line)."""
     import numpy as np
     import torch
@@ -235,6 +240,11 @@ def measure(k, args, momentum=0.0, cpu=True):
         from dataclasses import replace
         p = replace(p, momentum=momentum)
         stem = "linattn_scan_momentum_b4h8_h64_seq8192_chunk512"
+    ident = k == 1 and feature_map == "identity"
+    if ident:
+        from dataclasses import replace
+        p = replace(p, r=1)
+        stem = "linattn_identity_b4h8_h64_seq8192_chunk512" + ("_momentum" if momentum else "")
     if k == 4:
         x = make_inplace_inputs(p, k)
         Hs, Wg, Wu, Vb = (t(x[n], torch.bfloat16) for n in ("Hs", "W_gate", "W_up", "Vbar"))
@@ -258,11 +268,17 @@ def measure(k, args, momentum=0.0, cpu=True):
         eta = t(x["eta"], torch.float32)
         W0, W1, W2 = (t(x[n], torch.float32) for n in ("W0", "W1", "W2"))
         if k == 1:
+            fw0, fw2 = (None, None) if ident else (W0, W2)
+
             def step():
-                return ttt.linattn_forward(Q, K, V, eta, W0, W2, W1, chunk=p.chunk_kv, order=p.order,
-                                           momentum=p.momentum, stream=stream)
-            flops = acc.linattn_flops(p.B, p.H, p.Nk, p.h, p.r)
-            nbytes = acc.linattn_bytes(p.B, p.H, p.Nk, p.h, p.r)
+                return ttt.linattn_forward(Q, K, V, eta, fw0, fw2, W1, chunk=p.chunk_kv, order=p.order,
+                                           momentum=p.momentum, feature_map=feature_map, stream=stream)
+            if ident:
+                flops = acc.linattn_identity_flops(p.B, p.H, p.Nk, p.h)
+                nbytes = acc.linattn_identity_bytes(p.B, p.H, p.Nk, p.h)
+            else:
+                flops = acc.linattn_flops(p.B, p.H, p.Nk, p.h, p.r)
+                nbytes = acc.linattn_bytes(p.B, p.H, p.Nk, p.h, p.r)
             P, rh, nch = p.B * p.H, p.rh, p.Nk // p.chunk_kv
             work = {"linattn_delta": P * 2.0 * p.Nk * p.h * 2 + P * p.Nk * 4 + P * nch * rh * p.h * 4,
                     "linattn_scan": P * nch * rh * p.h * (4 + 2),
@@ -270,6 +286,9 @@ def measure(k, args, momentum=0.0, cpu=True):
                     "linattn_fused": nbytes}
             bound, peak, unit = "hbm", acc.PEAK_HBM_GBS, "GB/s"
             metric = "linear-attention scan form tokens/sec (h=64, r=2, chunk 512), bf16; % of HBM roofline"
+            if ident:
+                metric = ("linear-attention scan form, identity feature map (h x h state, h=64, chunk 512), "
+                          "bf16; % of HBM roofline")
             if p.momentum:
                 metric = metric.replace("scan form", f"scan form with momentum {p.momentum:g}")
             flush_bytes = 512 << 20
@@ -300,9 +319,13 @@ def measure(k, args, momentum=0.0, cpu=True):
                "order": "apply-then-update" if p.order == 0 else "update-then-apply"}
         if k != 1:
             cfg.update({"momentum": p.momentum, "muon": p.muon, "weight_norm": p.weight_norm})
-        elif p.momentum:
-            cfg["workload"] += f" + momentum {p.momentum:g}"
-            cfg["momentum"] = p.momentum
+        else:
+            if ident:
+                cfg["workload"] += ", identity feature map"
+                cfg["feature_map"] = "identity"
+            if p.momentum:
+                cfg["workload"] += f" + momentum {p.momentum:g}"
+                cfg["momentum"] = p.momentum
     cfg["parallelism"] = "single GPU"
 
     if args.copy_calibration:
@@ -328,7 +351,7 @@ def measure(k, args, momentum=0.0, cpu=True):
         if k == 4:
             rec["cpu_baseline"] = cpu_baseline_inplace(p, x, args.cpu_seconds)
         elif k == 1:
-            rec["cpu_baseline"] = cpu_baseline_linattn(p, x, args.cpu_seconds)
+            rec["cpu_baseline"] = cpu_baseline_linattn(p, x, args.cpu_seconds, feature_map)
         else:
             rec["cpu_baseline"] = cpu_baseline_lact(p, x, args.cpu_seconds)
     return rec
@@ -341,12 +364,12 @@ def main():
               "(sequence, head) pairs shard across GPUs without communication, see DESIGN.md",
               file=sys.stderr)
         sys.exit(2)
-    if args.momentum != 0.0 and args.config != 1:
-        print("--momentum applies to the scan workload (--config 1) only", file=sys.stderr)
+    if (args.momentum != 0.0 or args.feature_map != "swiglu") and args.config != 1:
+        print("--momentum and --feature-map apply to the scan workload (--config 1) only", file=sys.stderr)
         sys.exit(2)
     import linear_attention_lact_amd as ttt
     ttt.load()
-    rec = measure(args.config, args, args.momentum, cpu=not args.no_cpu_baseline)
+    rec = measure(args.config, args, args.momentum, cpu=not args.no_cpu_baseline, feature_map=args.feature_map)
     out = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec.pop("ms_per_step"),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec.pop("dtype"),
@@ -356,8 +379,8 @@ def main():
     out.update(rec)
     if args.config == 2 and not args.no_extras:
         others = {}
-        for k in (1, 3, 4):
-            r = measure(k, args, cpu=False)
+        for k, fm in ((1, "swiglu"), (1, "identity"), (3, "swiglu"), (4, "swiglu")):
+            r = measure(k, args, cpu=False, feature_map=fm)
             others[r["config"]["workload"]] = {
                 "metric": r["metric"], "value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
                 "roofline": {key: r["roofline"][key] for key in ("bound", "kernel", "achieved", "peak", "unit", "frac")},

@@ -174,13 +174,25 @@ ttt_status ttt_lact_forward(const ttt_lact_params* p,
  * the fp16 range, |x| <= 65504 (not checked; larger values give undefined results).
  * The single-pass path runs on devices with 8 XCDs (hipDeviceAttributeNumberOfXccs); other
  * devices take the multi-launch path (same results, more launches).
+ * feature_map = TTT_PHI_IDENTITY (the same summary page's simplification ladder, "Method step
+ * details", step 3: the fast weight is one linear layer f(x) = x W): phi(X) = X, so
+ * dS_c = K_c^T diag(eta_c) V_c, S_c as above and O_c = Q_c S_c, with the h x h state W1 = S_0
+ * [H, h, h] (or [B, H, h, h]); r must be 1 (else TTT_ERR_ARG); W0 and W2 are not read and may be
+ * NULL; S_out is [B, H, h, h]. It runs on the single-pass path only: TTT_BF16 with h in {64, 128}
+ * on an 8-XCD device (fp16 operands as above); anything else returns TTT_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------------------------- */
+typedef enum {
+  TTT_PHI_SWIGLU = 0,    /* phi(x) = silu(x W0) * (x W2), state [rh, h] */
+  TTT_PHI_IDENTITY = 1   /* phi(x) = x: one linear fast-weight layer, state [h, h] (r = 1) */
+} ttt_feature_map;
+
 typedef struct {
   int32_t B, H, N, h, r, chunk;
   int32_t order;
   int32_t dtype;
   int64_t w_batch_stride;
   float momentum;        /* heavy-ball coefficient alpha per chunk; 0: none */
+  int32_t feature_map;   /* ttt_feature_map; 0 (zero-initialised struct): TTT_PHI_SWIGLU */
 } ttt_linattn_params;
 
 ttt_status ttt_linattn_forward(const ttt_linattn_params* p,

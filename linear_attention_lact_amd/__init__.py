@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libttt_lact.so")
 
 TTT_OK, TTT_ERR_ARG, TTT_ERR_SHAPE, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP = 0, -1, -2, -3, -4, -5
 APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
+FEATURE_MAPS = {"swiglu": 0, "identity": 1}  # ttt_feature_map
 FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
 
@@ -46,7 +47,8 @@ class LactParams(ctypes.Structure):
 class LinattnParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("chunk", ctypes.c_int32), ("order", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("w_batch_stride", ctypes.c_int64), ("momentum", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("w_batch_stride", ctypes.c_int64), ("momentum", ctypes.c_float),
+                ("feature_map", ctypes.c_int32)]
 
 
 class InplaceParams(ctypes.Structure):
@@ -248,40 +250,54 @@ def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[i
 
 
 def linattn_forward(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                    momentum: float = 0.0, want_state: bool = True, stream=None):
+                    momentum: float = 0.0, feature_map: str = "swiglu", want_state: bool = True, stream=None):
     """Last-layer-only linear-attention scan. Q/K/V [B,H,N,h], eta [B,H,N], W0/W2 [(B,)H,h,rh],
     W1 [(B,)H,rh,h]; momentum: heavy-ball coefficient per chunk (0 <= momentum < 1).
+    feature_map "identity": phi(x) = x (one linear fast-weight layer), W0/W2 None, W1 [(B,)H,h,h].
     Returns (O, S_out) with S_out [B,H,rh,h] (None if not want_state)."""
-    return _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, want_state, stream, noalloc=False)
+    return _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want_state, stream,
+                    noalloc=False)
 
 
 def linattn_forward_noalloc(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                            momentum: float = 0.0, want_state: bool = True, stream=None):
+                            momentum: float = 0.0, feature_map: str = "swiglu", want_state: bool = True,
+                            stream=None):
     """linattn_forward without a workspace: the library's per-device scratch array
     (NOALLOC_SCRATCH_BYTES) serves as the workspace, so the call allocates no device memory
     besides the outputs it returns. Calls on one GPU share the array: do not overlap them."""
-    return _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, want_state, stream, noalloc=True)
+    return _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want_state, stream,
+                    noalloc=True)
 
 
-def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, want_state, stream, noalloc):
+def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want_state, stream, noalloc):
     torch = _torch()
     lib = load()
     B, H, N, h = Q.shape
-    per_seq = W0.dim() == 4
-    rh = W0.shape[-1]
+    if feature_map not in FEATURE_MAPS:
+        raise ValueError(f"feature_map must be one of {sorted(FEATURE_MAPS)}")
+    ident = feature_map == "identity"
+    per_seq = W1.dim() == 4
+    rh = W1.shape[-2]
     dev = Q.device
     for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
         _check(t, n, Q.dtype, dev)
     _check(eta, "eta", torch.float32, dev)
-    for t, n in ((W0, "W0"), (W1, "W1"), (W2, "W2")):
-        _check(t, n, torch.float32, dev)
     if K.shape != Q.shape or V.shape != Q.shape or eta.shape != (B, H, N):
         raise ValueError("Q/K/V must share [B,H,N,h] and eta be [B,H,N]")
-    _check_weights(W0, W1, W2, B, H, h)
+    if ident:
+        _check(W1, "W1", torch.float32, dev)
+        if W0 is not None or W2 is not None:
+            raise ValueError("the identity feature map takes no W0/W2")
+        if tuple(W1.shape) != ((B, H) if per_seq else (H,)) + (h, h):
+            raise ValueError(f"W1 must be [(B,)H,h,h] with h={h} for the identity feature map; got {tuple(W1.shape)}")
+    else:
+        for t, n in ((W0, "W0"), (W1, "W1"), (W2, "W2")):
+            _check(t, n, torch.float32, dev)
+        _check_weights(W0, W1, W2, B, H, h)
     if not (0.0 <= momentum < 1.0):
         raise ValueError("momentum must lie in [0, 1)")
     p = LinattnParams(B, H, N, h, rh // h, chunk, order, _io_dtype(Q), H * h * rh if per_seq else 0,
-                      float(momentum))
+                      float(momentum), FEATURE_MAPS[feature_map])
     O = torch.empty_like(Q)
     S = torch.empty((B, H, rh, h), dtype=torch.float32, device=dev) if want_state else None
     base = [ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(eta), _ptr(W0), _ptr(W2), _ptr(W1), _ptr(O), _ptr(S)]

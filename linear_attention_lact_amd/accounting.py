@@ -63,6 +63,17 @@ def linattn_bytes(B, H, N, h, r, io_bytes=2) -> float:
     return B * H * (4 * N * h * io_bytes + 4 * N + 4 * h * rh * 4)
 
 
+def linattn_identity_flops(B, H, N, h) -> float:
+    """Identity feature map (h x h state): dS = K^T diag(eta) V and O = Q S, 2 products of 2 N h h."""
+    return B * H * 2 * 2.0 * N * h * h
+
+
+def linattn_identity_bytes(B, H, N, h, io_bytes=2) -> float:
+    """Q, K, V read and O written once, eta once, the initial state read and the final state
+    written (fp32)."""
+    return B * H * (4 * N * h * io_bytes + 4 * N + 2 * h * h * 4)
+
+
 def inplace_flops(B, N, d_model, d_hidden) -> float:
     """Z (2 products), apply (1), update (1): 4 products of 2 N d_model d_hidden."""
     return B * 4 * 2.0 * N * d_model * d_hidden

@@ -184,13 +184,14 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
 }
 
 // Single-pass path (linattn_fused.hpp) for rh <= 128.
-template <class IoT, class OpT, int H, int RH, bool MOM>
+template <class IoT, class OpT, int H, int RH, bool MOM, bool ID = false>
 static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_t oAgg, size_t oIncl, size_t oInclM,
                                     size_t oFl, size_t oTk, const void* Q, const void* K, const void* V,
                                     const float* eta, const float* W0, const float* W2, const float* W1, void* O,
                                     float* S_out, hipStream_t st) {
-  auto fk = linattn_fused_kernel<IoT, OpT, H, RH, MOM>;
-  constexpr int lds = linattn_fused_lds_bytes<OpT, H, RH>();
+  typedef FusedLayout<OpT, H, RH, ID> FL;
+  auto fk = linattn_fused_kernel<IoT, OpT, H, RH, MOM, ID>;
+  constexpr int lds = linattn_fused_lds_bytes<OpT, H, RH, ID>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = allow_lds(fk, lds);
   TTT_HIP(lds_ok);
@@ -220,13 +221,14 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
   fa.w_batch_stride = p.w_batch_stride;
   // chunks per workgroup: the workgroups hold one CU each (LDS), so groups of G chunks bring the
   // grid down to one round over the device's CUs where the chunk splits into whole query passes
-  constexpr int PASS = FusedLayout<OpT, H, RH>::NW * 32;
+  constexpr int PASS = FL::NW * 32;
+  constexpr int GLIM = MOM ? FL::GMAX : 8;  // the momentum lookback holds up to GMAX partial sums
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                hipSuccess || ncu <= 0)
     return TTT_ERR_HIP;
   int G = 1;
-  while (G < 8 && (int64_t)8 * ((P + 7) / 8) * (nch / G) > ncu && nch % (2 * G) == 0 && p.chunk % PASS == 0)
+  while (G < GLIM && (int64_t)8 * ((P + 7) / 8) * (nch / G) > ncu && nch % (2 * G) == 0 && p.chunk % PASS == 0)
     G *= 2;
   fa.group = G;
   {
@@ -235,7 +237,7 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
     TTT_HIP(hipGetLastError());
   }
   const unsigned grid = 8u * (unsigned)((P + 7) / 8) * (unsigned)(nch / G);
-  TTT_HIP(launch_k(K_LIN_FUSED, fk, dim3(grid), dim3(FusedLayout<OpT, H, RH>::NT), lds, st, fa));
+  TTT_HIP(launch_k(K_LIN_FUSED, fk, dim3(grid), dim3(FL::NT), lds, st, fa));
   return TTT_OK;
 }
 
@@ -254,14 +256,17 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   if (q.dtype != TTT_FP32 && q.dtype != TTT_BF16) return TTT_ERR_ARG;
   if (q.w_batch_stride < 0) return TTT_ERR_ARG;
   if (!(q.momentum >= 0.f && q.momentum < 1.f)) return TTT_ERR_ARG;  // also rejects NaN
+  if (q.feature_map != TTT_PHI_SWIGLU && q.feature_map != TTT_PHI_IDENTITY) return TTT_ERR_ARG;
+  const bool ident = q.feature_map == TTT_PHI_IDENTITY;
+  if (ident && q.r != 1) return TTT_ERR_ARG;  // the identity map's state is h x h
   if (q.N % q.chunk) return TTT_ERR_SHAPE;
   const int64_t rh64 = (int64_t)q.r * q.h;
-  if (q.h % 32 || rh64 % 64 || rh64 > 1024) return TTT_ERR_SHAPE;
+  if (q.h % 32 || (!ident && rh64 % 64) || rh64 > 1024) return TTT_ERR_SHAPE;
   if (q.w_batch_stride != 0 && q.w_batch_stride != (int64_t)q.H * rh64 * q.h) return TTT_ERR_SHAPE;
   const bool bf16 = q.dtype == TTT_BF16;
   if (bf16 ? (q.h > 256) : (q.h > 128)) return TTT_ERR_UNSUPPORTED;
   const int P = q.B * q.H, nch = q.N / q.chunk;
-  if (P > 0 && (!W0 || !W1 || !W2)) return TTT_ERR_ARG;
+  if (P > 0 && (!W1 || (!ident && (!W0 || !W2)))) return TTT_ERR_ARG;
   if (P > 0 && nch > 0 && (!Q || !K || !V || !eta || !O)) return TTT_ERR_ARG;
   const int64_t n = rh64 * q.h;
   const size_t opsz = bf16 ? 2 : 4;
@@ -271,10 +276,14 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   int dev = 0, nxcc = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess)
     nxcc = 0;
-  const bool fused_shape = bf16 && ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128)) &&
+  // the identity map: single pass only, h in {64, 128}
+  const bool shape_ok = ident ? (q.h == 64 || q.h == 128)
+                              : ((q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128));
+  const bool fused_shape = bf16 && shape_ok &&
                            (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31 &&  // buffer offsets are 32-bit
                            (int64_t)q.N * q.h * 2 < (int64_t)1 << 31;
   const bool fused = fused_shape && nxcc == 8;
+  if (ident && !fused_shape) return TTT_ERR_UNSUPPORTED;
   // both plans; the size asked for covers the larger where the single-pass shape applies, so a
   // query gives the same answer on any device (and without one)
   WorkspacePlan fplan, mplan;
@@ -287,7 +296,7 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   const size_t oSh = mplan.add((size_t)P * 2 * n * opsz);
   const size_t odS = mplan.add((size_t)P * nch * n * 4);
   const size_t oSt = mplan.add((size_t)P * nch * n * opsz);
-  const size_t need = fused_shape ? std::max(fplan.total, mplan.total) : mplan.total;
+  const size_t need = ident ? fplan.total : fused_shape ? std::max(fplan.total, mplan.total) : mplan.total;
   if (!workspace) {
     *workspace_bytes = need;
     return TTT_OK;
@@ -304,6 +313,11 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
     return TTT_OK;
   }
   char* ws = static_cast<char*>(workspace);
+  if (ident && !fused) {
+    note_error("ttt_linattn_forward: the identity feature map runs on the single-pass path only, which "
+               "needs a device with 8 XCDs");
+    return TTT_ERR_UNSUPPORTED;
+  }
   if (fused) {
     try {
 #define TTT_FUSED(IOT, OPT, HH, RR)                                                                         \
@@ -312,6 +326,20 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
                                                            W0, W2, W1, O, S_out, st)                        \
                : linattn_fused_run<IOT, OPT, HH, RR, false>(q, ws, oAgg, oIncl, oInclM, oFl, oTk, Q, K, V,  \
                                                             eta, W0, W2, W1, O, S_out, st);
+      if (ident) {
+        if (q.h == 64)
+          return mom ? linattn_fused_run<bf16_t, _Float16, 64, 64, true, true>(q, ws, oAgg, oIncl, oInclM, oFl, oTk,
+                                                                               Q, K, V, eta, W0, W2, W1, O, S_out, st)
+                     : linattn_fused_run<bf16_t, _Float16, 64, 64, false, true>(q, ws, oAgg, oIncl, oInclM, oFl, oTk,
+                                                                                Q, K, V, eta, W0, W2, W1, O, S_out, st);
+        if (q.h == 128)
+          return mom ? linattn_fused_run<bf16_t, _Float16, 128, 128, true, true>(q, ws, oAgg, oIncl, oInclM, oFl, oTk,
+                                                                                 Q, K, V, eta, W0, W2, W1, O, S_out, st)
+                     : linattn_fused_run<bf16_t, _Float16, 128, 128, false, true>(q, ws, oAgg, oIncl, oInclM, oFl,
+                                                                                  oTk, Q, K, V, eta, W0, W2, W1, O,
+                                                                                  S_out, st);
+        return TTT_ERR_UNSUPPORTED;
+      }
       TTT_FUSED(bf16_t, _Float16, 32, 64)
       TTT_FUSED(bf16_t, _Float16, 32, 128)
       TTT_FUSED(bf16_t, _Float16, 64, 128)

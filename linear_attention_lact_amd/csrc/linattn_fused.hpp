@@ -78,25 +78,32 @@ __global__ void __launch_bounds__(256) linattn_fused_reset(unsigned* tickets, un
   for (int i = threadIdx.x; i < nflags; i += 256) flags[i] = 0u;
 }
 
-template <class OpT, int H, int RH>
+// ID: the identity feature map (RH == H): no fast-weight rows, no token-half combine, and S kept
+// transposed ([h][LDT], row reads) for phase C.
+template <class OpT, int H, int RH, bool ID = false>
 struct FusedLayout {
   static constexpr int NJB = RH / 32, NW = 2 * NJB, NT = 64 * NW;
   static constexpr int LDK = H + Pad<OpT>::v;       // token tiles (row reads and transpose reads)
   static constexpr int LDW = H + Pad<OpT>::v;       // W0^T / W2^T rows
-  static constexpr int LD1 = tr_ld<OpT>(H);         // S rows (transpose reads)
+  static constexpr int LD1 = ID ? H + Pad<OpT>::v : tr_ld<OpT>(H);  // S rows (transpose reads), S^T rows (ID)
   static constexpr int TILE = TT * LDK;             // elements of one staged token tile
   static constexpr int NB = 3;                                               // token-tile buffers
   static constexpr int TILES_B = NB * 2 * TILE * (int)sizeof(OpT);           // NB x (K, eta*V)
   static constexpr int OST_B = NW * 32 * (H + 8) * 2;                         // output staging
   static constexpr int R0 = TILES_B > OST_B ? TILES_B : OST_B;
   static constexpr int COMB_O = R0;                                          // token-half combine
-  static constexpr int WT_O = COMB_O + NJB * 32 * H * 4;                     // W0^T, W2^T [RH][LDW]
-  static constexpr int SS_O = WT_O + 2 * RH * LDW * (int)sizeof(OpT);        // S [RH][LD1]
+  static constexpr int WT_O = COMB_O + (ID ? 0 : NJB * 32 * H * 4);          // W0^T, W2^T [RH][LDW]
+  static constexpr int SS_O = WT_O + (ID ? 0 : 2 * RH * LDW * (int)sizeof(OpT));  // S [RH][LD1]
   static constexpr int bytes = SS_O + RH * LD1 * (int)sizeof(OpT) + 16;
+  // state float4 groups per thread, aggregates loaded together in the lookback, and the largest
+  // group of chunks the momentum lookback holds in registers
+  static constexpr int SPT = (RH * H / 4 + NT - 1) / NT;
+  static constexpr int LB = SPT >= 8 ? 2 : 8;
+  static constexpr int GMAX = SPT >= 8 ? 1 : 8;
 };
 
-template <class OpT, int H, int RH>
-constexpr int linattn_fused_lds_bytes() { return FusedLayout<OpT, H, RH>::bytes; }
+template <class OpT, int H, int RH, bool ID = false>
+constexpr int linattn_fused_lds_bytes() { return FusedLayout<OpT, H, RH, ID>::bytes; }
 
 // grid: 8 * ceil(P / 8) * (nch / G) workgroups; block NT = 128 * RH / 32 threads.
 // MOM: heavy-ball momentum per chunk. The carried state is then the pair (S, m): a group of G
@@ -105,11 +112,14 @@ constexpr int linattn_fused_lds_bytes() { return FusedLayout<OpT, H, RH>::bytes;
 // sigma_L = alpha + ... + alpha^L; the state after L of the group's chunks is
 // S + sigma_L m + sum_{j<L} alpha^(L-1-j) P_j. Readers rebuild these sums from the stored
 // partial sums, so the aggregate phase is the same as without momentum.
-template <class IoT, class OpT, int H, int RH, bool MOM = false>
+// ID: the identity feature map (RH == H): phase A contracts K and eta*V straight from the staged
+// tiles (wave (jb, half) owns rows jb*32.. and half of the columns of dS over all 64 tokens of a
+// tile), phase C multiplies the query rows by S.
+template <class IoT, class OpT, int H, int RH, bool MOM = false, bool ID = false>
 __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArgs a) {
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
-  typedef FusedLayout<OpT, H, RH> L;
+  typedef FusedLayout<OpT, H, RH, ID> L;
   constexpr int NJB = L::NJB, NW = L::NW, NT = L::NT;
   constexpr int LDK = L::LDK, LDW = L::LDW, LD1 = L::LD1, TILE = L::TILE, NB = L::NB;
   constexpr int KS = H / M::KSTEP;          // K steps over h
@@ -119,8 +129,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   constexpr int NCK = TT * H / VE;          // 16-byte chunks of one token tile
   constexpr int CPT = (NCK + NT - 1) / NT;
   constexpr int NS4 = RH * H / 4;           // float4 groups of the state
-  constexpr int SPT = (NS4 + NT - 1) / NT;
+  constexpr int SPT = L::SPT, LB = L::LB, GMAX = L::GMAX;
+  constexpr int CBH = CB / 2;               // ID: 32-column blocks of dS per wave
   static_assert(RH % 32 == 0 && H % 32 == 0 && NT <= 1024, "shape");
+  static_assert(!ID || (RH == H && H % 64 == 0), "identity map: h x h state, h a multiple of 64");
   static_assert(std::is_same<IoT, bf16_t>::value && std::is_same<OpT, _Float16>::value, "bf16 I/O, fp16 operands");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -203,9 +215,9 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   // A operands in phase C (same lane layout); W0^T / W2^T also go to LDS for phase C. W0 is
   // scaled by -log2(e) and W2 by -ln(2): with u = x W0 (-log2 e) and v = x W2 (-ln 2),
   // silu(x W0) (x W2) = u v / (1 + 2^u). ----
-  const int jb = w % NJB, th = w / NJB;
+  const int jb = w % NJB, th = w / NJB;  // ID: th is the wave's column half of dS
   frag wf[2][KS];
-  {
+  if constexpr (!ID) {
     const int j = jb * 32 + (lane & 31);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -277,10 +289,44 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
+  // ID: iteration i stores tile i+2 and contracts tile i: acc[c] += K^T (eta V) over its 64 tokens
+  // (both operands transpose-read with the same token permutation)
+  auto tile_id = [&](int bc, Staged& sp, int inext) {
+    const int bp = bc == 0 ? NB - 1 : bc - 1;  // buffer of tile i+2 (that of tile i-1)
+    put(bp, sp);
+    fetch(inext, sp);
+    const OpT* kt = tiles + bc * 2 * TILE;
+    const OpT* vt = kt + TILE;
+    frag hf[2][QS], vf[2][QS][CBH];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        hf[t2][q] = acc_kfrag_tr<OpT>(kt + t2 * 32 * LDK + jb * 32, LDK, q, lane);
+#pragma unroll
+        for (int c = 0; c < CBH; ++c)
+          vf[t2][q][c] = acc_kfrag_tr<OpT>(vt + t2 * 32 * LDK + (th * CBH + c) * 32, LDK, q, lane);
+      }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+#pragma unroll
+        for (int c = 0; c < CBH; ++c) acc[c] = M::mma(hf[t2][q], vf[t2][q][c], acc[c]);
+    __syncthreads();
+  };
   // The sums run over the whole group. At the end of the group's chunk i, wave (jb, 1) hands its
   // sums to wave (jb, 0), which adds them (in a fixed order) and stores the group's partial sum
   // through chunk i to slot ch*G + i; slot ch*G + G-1 holds the group's aggregate.
   auto combine = [&](int i) {
+    if constexpr (ID) {
+      float* ag = aggp + ((int64_t)ch * G + i) * n + (int64_t)jb * 32 * H;
+#pragma unroll
+      for (int c = 0; c < CBH; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ag[acc_row(r, lane) * H + (th * CBH + c) * 32 + acc_col(lane)] = acc[c][r];
+      return;
+    }
     if (th == 1) {
 #pragma unroll
       for (int c = 0; c < CB; ++c)
@@ -302,7 +348,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   put(1, sg4[1]);
   fetch(NPF + 1, sg4[1]);
   __syncthreads();
-  {
+  if constexpr (!ID) {
     zero(pu[0]);
     zero(pv[0]);
 #pragma unroll
@@ -322,7 +368,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
 #pragma unroll
     for (int k = 0; k < NPF; ++k) {
       const int i = i0 + k;
-      tile_iter(i, bc, sg4[(k + 2) % NPF], pu[k & 1], pv[k & 1], pu[(k + 1) & 1], pv[(k + 1) & 1]);
+      if constexpr (ID)
+        tile_id(bc, sg4[(k + 2) % NPF], i + 2 + NPF);
+      else
+        tile_iter(i, bc, sg4[(k + 2) % NPF], pu[k & 1], pv[k & 1], pu[(k + 1) & 1], pv[(k + 1) & 1]);
       bc = bc == NB - 1 ? 0 : bc + 1;
       if (G > 1 && (i + 1) % tpc == 0 && i + 1 < ntile) combine(i / tpc);
     }
@@ -331,7 +380,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   for (int k = 0; k < NPF - 1; ++k) {
     const int i = i0 + k;
     if (i < ntile) {
-      tile_iter(i, bc, sg4[(k + 2) % NPF], pu[k & 1], pv[k & 1], pu[(k + 1) & 1], pv[(k + 1) & 1]);
+      if constexpr (ID)
+        tile_id(bc, sg4[(k + 2) % NPF], i + 2 + NPF);
+      else
+        tile_iter(i, bc, sg4[(k + 2) % NPF], pu[k & 1], pv[k & 1], pu[(k + 1) & 1], pv[(k + 1) & 1]);
       bc = bc == NB - 1 ? 0 : bc + 1;
     }
   }
@@ -410,9 +462,9 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
       m[i] = stop >= 0 ? dev_load4(rim, (int)((stop * n + e) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     for (int g = stop + 1; g <= ch; ++g) {
-      f32x4 pj[8][SPT];
+      f32x4 pj[GMAX][SPT];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < GMAX; ++j)
 #pragma unroll
         for (int i = 0; i < SPT; ++i)
           pj[j][i] = j < G ? dev_load4(ra, (int)(((g * G + j) * n + 4 * (tid + NT * i)) * 4))
@@ -424,7 +476,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
         am[i] = pj[0][i];
       }
 #pragma unroll
-      for (int j = 1; j < 8; ++j)
+      for (int j = 1; j < GMAX; ++j)
         if (j < G)
 #pragma unroll
           for (int i = 0; i < SPT; ++i) {
@@ -463,10 +515,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
       if (NS4 % NT != 0 && e >= 4 * NS4) continue;
       s[i] = stop >= 0 ? dev_load4(ri, (int)((stop * n + e) * 4)) : *reinterpret_cast<const f32x4*>(W1p + e);
     }
-    for (int j0 = stop + 1; j0 < ch; j0 += 8) {
-      f32x4 t[8][SPT];
+    for (int j0 = stop + 1; j0 < ch; j0 += LB) {
+      f32x4 t[LB][SPT];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
+      for (int jj = 0; jj < LB; ++jj)
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
           const int e = 4 * (tid + NT * i);
@@ -474,7 +526,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
                                     : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
+      for (int jj = 0; jj < LB; ++jj)
         if (j0 + jj < ch)
 #pragma unroll
           for (int i = 0; i < SPT; ++i) s[i] += t[jj][i];
@@ -514,6 +566,31 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
       frag qf[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = bf16x8_to_f16x8(qcur[s]);
+      // stage the wave's 32 x h output tile in LDS (each lane holds four consecutive columns of a
+      // token row), then write whole 16-byte row runs; rows past the chunk end fall outside the
+      // store range and are dropped
+      bf16_t* os = ost + w * 32 * (H + 8) + (lane & 31) * (H + 8) + 4 * (lane >> 5);
+      auto stage = [&](int c, const f32x16& oc) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = f32x2_to_bf16x2_bits(oc[4 * g], oc[4 * g + 1]);
+          const uint32_t hi = f32x2_to_bf16x2_bits(oc[4 * g + 2], oc[4 * g + 3]);
+          *reinterpret_cast<u32x2*>(os + c * 32 + 8 * g) = u32x2{lo, hi};
+        }
+      };
+      if constexpr (ID) {
+        // O^T = S^T Q^T one 32-column block at a time: S^T rows from LDS, the query rows as the
+        // B operand
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+          f32x16 oc;
+          zero(oc);
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            oc = M::mma(M::load(Ss + (c * 32 + (lane & 31)) * LD1 + s * M::KSTEP + (lane >> 5) * M::KSUB), qf[s], oc);
+          stage(c, oc);
+        }
+      } else {
       f32x16 o[CB];  // O^T: rows are output columns c*32.., columns the wave's 32 tokens
 #pragma unroll
       for (int c = 0; c < CB; ++c) zero(o[c]);
@@ -579,18 +656,9 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
         __builtin_amdgcn_sched_group_barrier(0x008, QS * CB, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // stage the wave's 32 x h output tile in LDS (each lane holds four consecutive columns of a
-      // token row), then write whole 16-byte row runs; rows past the chunk end fall outside the
-      // store range and are dropped
-      bf16_t* os = ost + w * 32 * (H + 8) + (lane & 31) * (H + 8) + 4 * (lane >> 5);
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t lo = f32x2_to_bf16x2_bits(o[c][4 * g], o[c][4 * g + 1]);
-          const uint32_t hi = f32x2_to_bf16x2_bits(o[c][4 * g + 2], o[c][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(os + c * 32 + 8 * g) = u32x2{lo, hi};
-        }
+      for (int c = 0; c < CB; ++c) stage(c, o[c]);
+      }
       const bf16_t* ow = ost + w * 32 * (H + 8);
 #pragma unroll
       for (int i = lane; i < 32 * H / 8; i += 64) {
@@ -603,7 +671,7 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   // chunk i of the group reads S = run + the group's partial sum through chunk i-1 (through chunk i
   // when inclusive; the last chunk's inclusive state is then the group's inclusive prefix)
   int np = 0;  // passes so far: even passes read qa and prefetch into qb, odd ones the reverse
-  for (int i = 0; i < G; ++i) {
+  for (int i = 0; i < (MOM && GMAX == 1 ? 1 : G); ++i) {  // (the host keeps G <= GMAX with momentum)
     const int slot = i - (a.inclusive ? 0 : 1);  // group partial sum through chunk `slot`
     f32x4 part[SPT];
     float sL = 0.f;  // with momentum: sigma_L for the L = slot + 1 chunk writes before this state
@@ -634,7 +702,12 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
       if (bad) sc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       const int j = e / H, c = e % H;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Ss[j * LD1 + c + q] = M::from_f32(sc[q]);
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (ID)
+          Ss[(c + q) * LD1 + j] = M::from_f32(sc[q]);
+        else
+          Ss[j * LD1 + c + q] = M::from_f32(sc[q]);
+      }
     }
     __syncthreads();  // S of chunk i in LDS
     ocur = cbase + i * a.chunk;

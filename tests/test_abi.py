@@ -117,13 +117,13 @@ def test_lact_empty_batch_is_a_no_op(lib):
     assert _lact(lib, _lp(B=0), ws=ctypes.c_void_p(0x100000), size=max(size, 256))[0] == ttt.TTT_OK
 
 
-def _lin(lib, **kw):
+def _lin(lib, W0=FAKE, W2=FAKE, ws=None, size=0, **kw):
     base = dict(B=4, H=8, N=8192, h=64, r=2, chunk=512, order=0, dtype=ttt.BF16, w_batch_stride=0)
     base.update(kw)
     p = ttt.LinattnParams(**base)
-    sz = ctypes.c_size_t(0)
-    st = lib.ttt_linattn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                                 None, ctypes.byref(sz), None)
+    sz = ctypes.c_size_t(size)
+    st = lib.ttt_linattn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, W0, W2, FAKE, FAKE, None,
+                                 ws, ctypes.byref(sz), None)
     return st, sz.value
 
 
@@ -145,6 +145,23 @@ def test_linattn_momentum_validation(lib):
     # with momentum the single-pass workspace holds the momentum of each inclusive prefix too
     assert multi == single_pass + 4 * 8 * 16 * 128 * 64 * 4
     assert ctypes.sizeof(ttt.LinattnParams) == 48
+
+
+def test_linattn_identity_feature_map_validation(lib):
+    ID = ttt.FEATURE_MAPS["identity"]
+    st, size = _lin(lib, r=1, feature_map=ID)
+    # single-pass workspace only: aggregates and inclusive prefixes of 64 x 64 states
+    assert st == ttt.TTT_OK and 2 * 32 * 16 * 64 * 64 * 4 <= size < _lin(lib)[1]
+    assert _lin(lib, r=1, feature_map=ID, W0=None, W2=None) == (ttt.TTT_OK, size)  # W0/W2 not read
+    assert _lin(lib, W0=None)[0] == ttt.TTT_ERR_ARG                                   # but required by SwiGLU
+    assert _lin(lib, r=2, feature_map=ID)[0] == ttt.TTT_ERR_ARG                       # state must be h x h
+    for bad in (-1, 2, 7):
+        assert _lin(lib, feature_map=bad)[0] == ttt.TTT_ERR_ARG
+    for kw in (dict(h=96), dict(h=32), dict(h=256), dict(dtype=ttt.FP32)):
+        assert _lin(lib, r=1, feature_map=ID, **kw)[0] == ttt.TTT_ERR_UNSUPPORTED, kw
+    # no 8-XCD device here: a real call is refused before any launch, with a reason
+    assert _lin(lib, r=1, feature_map=ID, ws=FAKE, size=size)[0] == ttt.TTT_ERR_UNSUPPORTED
+    assert "single-pass" in ttt.last_error()
 
 
 def _inp(lib, **kw):
@@ -210,6 +227,28 @@ def test_linattn_binding_checks_weight_shapes_before_any_launch(monkeypatch, lib
         W1 = _FakeCuda((H, h, rh), f32)
     with pytest.raises(ValueError):
         ttt.linattn_forward(Q, Q, Q, eta, W0, W2, W1, chunk=64)
+
+
+@pytest.mark.parametrize("bad", ["W0 given", "W1 rh x h", "W1 heads", "unknown map"])
+def test_identity_binding_checks_before_any_launch(monkeypatch, lib, bad):
+    import torch
+    _fake_call_guard(monkeypatch)
+    B, H, N, h = 2, 4, 256, 64
+    bf, f32 = torch.bfloat16, torch.float32
+    Q = _FakeCuda((B, H, N, h), bf)
+    eta = _FakeCuda((B, H, N), f32)
+    W0, W1 = None, _FakeCuda((H, h, h), f32)
+    fm = "identity"
+    if bad == "W0 given":
+        W0 = _FakeCuda((H, h, h), f32)
+    elif bad == "W1 rh x h":
+        W1 = _FakeCuda((H, 2 * h, h), f32)
+    elif bad == "W1 heads":
+        W1 = _FakeCuda((H - 1, h, h), f32)
+    else:
+        fm = "relu"
+    with pytest.raises(ValueError):
+        ttt.linattn_forward(Q, Q, Q, eta, W0, None, W1, chunk=64, feature_map=fm)
 
 
 @pytest.mark.parametrize("bad", ["M_in shape", "momentum 1", "momentum nan"])

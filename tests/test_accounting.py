@@ -120,6 +120,16 @@ def test_linattn_counter_equals_the_oracles_products(monkeypatch):
     assert n == acc.linattn_flops(1, 1, 64, 8, 2)
 
 
+def test_linattn_identity_counter_equals_the_oracles_products(monkeypatch):
+    from oracle import linattn as LA
+    p = LactProblem(B=1, H=1, h=8, r=1, Nq=64, Nk=64, chunk_q=16, chunk_kv=16)
+    x = make_lact_inputs(p, 6)
+    n = _count(LA, monkeypatch, lambda: LA.linattn_pair(
+        x["Q"][0, 0], x["K"][0, 0], x["V"][0, 0], x["eta"][0, 0], None, x["W1"][0], None, chunk=16,
+        feature_map="identity"))
+    assert n == acc.linattn_identity_flops(1, 1, 64, 8)
+
+
 def test_inplace_counter_equals_the_oracles_products(monkeypatch):
     from oracle import inplace as IP
     rng = np.random.default_rng(5)
@@ -141,3 +151,12 @@ def test_linattn_bytes_are_the_calls_arrays():
                   np.zeros((rh, h), np.float32)]
     total = sum(a.nbytes for a in arrays) + B * H * sum(a.nbytes for a in per_pair_w)
     assert acc.linattn_bytes(B, H, N, h, r) == total
+
+
+def test_linattn_identity_bytes_are_the_calls_arrays():
+    """Identity map: Q, K, V, O in bf16, eta, the initial and the final h x h state in fp32."""
+    B, H, N, h = 2, 3, 64, 16
+    tok = np.zeros((B, H, N, h), np.uint16)
+    arrays = [tok, tok, tok, tok, np.zeros((B, H, N), np.float32), np.zeros((B, H, h, h), np.float32),
+              np.zeros((B, H, h, h), np.float32)]
+    assert acc.linattn_identity_bytes(B, H, N, h) == sum(a.nbytes for a in arrays)
