@@ -40,6 +40,25 @@ supports):
    matrices.
 9. Input axis = axis 0 of the row-form matrices (each output column is
    normalised over its inputs).
+
+Variants of the same loop (the reading notes' section 2.3 update-order table
+and section 2.4; the In-Place notes, section 3.4; the notes' section 2.1 symbol
+table; the summary page's "Experimental results"):
+
+10. Per-chunk write mask: an apply-only chunk (the autoregressive-video row's
+    noisy chunks) is applied with the current weights and writes nothing:
+    weights and momentum are left as they are.
+11. Per-chunk reset (a document boundary inside a packed sequence): before the
+    chunk is applied or written, the weights return to the call's initial
+    weights and the momentum to zero, as if a new call started there.
+12. eta per matrix ("may be predicted separately for the three matrices"): the
+    gradient of matrix X is that of the chunk loss weighted by eta_X,
+    L_X = -sum_i eta_{X,i} <f(k_i), v_i>; one eta shared by the three is the
+    default.
+13. Several inner steps per chunk: the chunk's write (gradient at the current
+    weights, momentum, Newton-Schulz, subtract, renorm) is repeated that many
+    times on the same tokens; apply-then-update applies before the first step,
+    update-then-apply after the last.
 """
 from __future__ import annotations
 
@@ -53,6 +72,7 @@ NS_STEPS = 5
 APPLY_THEN_UPDATE = 0
 UPDATE_THEN_APPLY = 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
+CHUNK_NO_UPDATE, CHUNK_RESET = 1, 2  # per-chunk flags (readings 10, 11)
 
 
 def sigmoid(a: np.ndarray) -> np.ndarray:
@@ -147,7 +167,7 @@ def lact_pair(Q: np.ndarray, K: np.ndarray, V: np.ndarray, eta: np.ndarray,
               update_mask: int = 7, weight_norm: bool = True, muon: bool = False,
               momentum: float = 0.0, eps_norm: float = 1e-5, eps_ns: float = 1e-7,
               M_in: Optional[Dict[str, np.ndarray]] = None, ascent: bool = False,
-              dtype=np.float64):
+              chunk_flags=None, inner_steps: int = 1, dtype=np.float64):
     """The chunk recurrence for one (sequence, head) pair.
 
     Steps per chunk c (notes section 2.3 for the order; section 2.2 for the
@@ -155,12 +175,16 @@ def lact_pair(Q: np.ndarray, K: np.ndarray, V: np.ndarray, eta: np.ndarray,
       AU: O_c = f_W(Q_c), then update W with (K_c, V_c, eta_c);
       UA: update first, then O_c = f_W(Q_c).
     ``ascent`` flips the sign of the write (summary page, "Experimental
-    results": gradient ascent in the inner loop).
+    results": gradient ascent in the inner loop). ``eta`` is [Nk] (shared) or
+    [3, Nk] (one row per matrix W0, W1, W2; reading 12). ``chunk_flags`` holds
+    one CHUNK_NO_UPDATE / CHUNK_RESET bit set per chunk (readings 10, 11);
+    ``inner_steps`` writes per chunk (reading 13).
     Returns (O, W0, W1, W2, M) with M = {"W0":..., "W1":..., "W2":...}.
     """
     Q, K, V, eta = (np.asarray(a, dtype=dtype) for a in (Q, K, V, eta))
-    W = {"W0": np.array(W0, dtype=dtype), "W1": np.array(W1, dtype=dtype),
-         "W2": np.array(W2, dtype=dtype)}
+    init = {"W0": np.array(W0, dtype=dtype), "W1": np.array(W1, dtype=dtype),
+            "W2": np.array(W2, dtype=dtype)}
+    W = {n: w.copy() for n, w in init.items()}
     bits = {"W0": UPD_W0, "W1": UPD_W1, "W2": UPD_W2}
     updated = [n for n in ("W0", "W1", "W2") if update_mask & bits[n]]
     nu = {n: input_dim_norms(W[n]) for n in updated}
@@ -174,22 +198,34 @@ def lact_pair(Q: np.ndarray, K: np.ndarray, V: np.ndarray, eta: np.ndarray,
         q = Q[c * chunk_q:(c + 1) * chunk_q]
         O[c * chunk_q:(c + 1) * chunk_q] = swiglu_apply(q, W["W0"], W["W1"], W["W2"])
 
+    def gradients(sl):
+        """The chunk loss's gradients; with one eta row per matrix, each matrix's gradient of
+        the loss weighted by its own eta (reading 12)."""
+        if eta.ndim == 1:
+            return dict(zip(("W0", "W1", "W2"), chunk_gradients(K[sl], V[sl], eta[sl], W["W0"], W["W1"], W["W2"])))
+        per = [chunk_gradients(K[sl], V[sl], eta[x, sl], W["W0"], W["W1"], W["W2"]) for x in range(3)]
+        return {"W0": per[0][0], "W1": per[1][1], "W2": per[2][2]}
+
     for c in range(n_chunks):
+        flag = 0 if chunk_flags is None else int(chunk_flags[c])
+        if flag & CHUNK_RESET:
+            W = {n: w.copy() for n, w in init.items()}
+            M = {n: np.zeros_like(w) for n, w in init.items()}
         if order == APPLY_THEN_UPDATE:
             apply(c)
         sl = slice(c * chunk_kv, (c + 1) * chunk_kv)
-        G = dict(zip(("W0", "W1", "W2"),
-                     chunk_gradients(K[sl], V[sl], eta[sl], W["W0"], W["W1"], W["W2"])))
-        for n in updated:
-            U = G[n]
-            if momentum != 0.0:
-                M[n] = momentum * M[n] + G[n]
-                U = M[n]
-            if muon:
-                U = newton_schulz5(U, eps_ns)
-            W[n] = W[n] + U if ascent else W[n] - U
-            if weight_norm:
-                W[n] = renorm_input_dim(W[n], nu[n], eps_norm)
+        for _ in range(0 if flag & CHUNK_NO_UPDATE else inner_steps):
+            G = gradients(sl)
+            for n in updated:
+                U = G[n]
+                if momentum != 0.0:
+                    M[n] = momentum * M[n] + G[n]
+                    U = M[n]
+                if muon:
+                    U = newton_schulz5(U, eps_ns)
+                W[n] = W[n] + U if ascent else W[n] - U
+                if weight_norm:
+                    W[n] = renorm_input_dim(W[n], nu[n], eps_norm)
         if order == UPDATE_THEN_APPLY:
             apply(c)
     return O, W["W0"], W["W1"], W["W2"], M
@@ -198,13 +234,15 @@ def lact_pair(Q: np.ndarray, K: np.ndarray, V: np.ndarray, eta: np.ndarray,
 def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q, chunk_kv, order=APPLY_THEN_UPDATE,
                  update_mask=7, weight_norm=True, muon=False, momentum=0.0,
                  eps_norm=1e-5, eps_ns=1e-7, M_in=None, pairs=None, ascent=False,
-                 dtype=np.float64) -> Dict[str, np.ndarray]:
+                 chunk_flags=None, inner_steps=1, dtype=np.float64) -> Dict[str, np.ndarray]:
     """All (sequence, head) pairs of a call; each pair is independent.
 
-    Q [B,H,Nq,h], K/V [B,H,Nk,h], eta [B,H,Nk]; W0/W2 [H,h,rh] and W1 [H,rh,h]
-    shared across the batch, or [B,H,...] per sequence. ``M_in`` (optional) is a
-    dict of [B,H,...] momentum buffers. ``pairs`` restricts the computation to a
-    list of (b, head) pairs; the outputs of other pairs are left as NaN.
+    Q [B,H,Nq,h], K/V [B,H,Nk,h], eta [B,H,Nk] (or [B,H,3,Nk], one row per
+    matrix); W0/W2 [H,h,rh] and W1 [H,rh,h] shared across the batch, or
+    [B,H,...] per sequence. ``M_in`` (optional) is a dict of [B,H,...] momentum
+    buffers. ``chunk_flags`` (optional) is [B, n_chunks]: one flag set per
+    sequence and chunk, shared by its heads. ``pairs`` restricts the computation
+    to a list of (b, head) pairs; the outputs of other pairs are left as NaN.
     """
     B, H, Nq, h = Q.shape
     per_seq = np.ndim(W0) == 4
@@ -221,7 +259,8 @@ def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q, chunk_kv, order=APPLY_THE
             Q[b, hd], K[b, hd], V[b, hd], eta[b, hd], w[0], w[1], w[2],
             chunk_q=chunk_q, chunk_kv=chunk_kv, order=order, update_mask=update_mask,
             weight_norm=weight_norm, muon=muon, momentum=momentum, eps_norm=eps_norm,
-            eps_ns=eps_ns, M_in=m_in, ascent=ascent, dtype=dtype)
+            eps_ns=eps_ns, M_in=m_in, ascent=ascent,
+            chunk_flags=None if chunk_flags is None else chunk_flags[b], inner_steps=inner_steps, dtype=dtype)
         O[b, hd] = o
         Wout["W0"][b, hd], Wout["W1"][b, hd], Wout["W2"][b, hd] = w0, w1, w2
         for n in Mout:

@@ -15,6 +15,7 @@ from oracle import lact as L
 from oracle import linattn as LA
 from tests import test_oracle_inplace as TI
 from tests import test_oracle_lact as TL
+from tests import test_oracle_lact_variants as TLV
 from tests import test_oracle_linattn as TLA
 
 
@@ -106,6 +107,28 @@ def _update_before_apply(orig):
     return f
 
 
+def _drop_flag(bit):
+    def mutate(orig):
+        def f(*a, chunk_flags=None, **k):
+            flags = None if chunk_flags is None else (np.asarray(chunk_flags).astype(np.int64) & ~bit)
+            return orig(*a, chunk_flags=flags, **k)
+        return f
+    return mutate
+
+
+def _one_inner_step(orig):
+    def f(*a, inner_steps=1, **k):
+        return orig(*a, **k)
+    return f
+
+
+def _eta_rows_swapped(orig):
+    def f(Q, K, V, eta, *a, **k):
+        eta = np.asarray(eta)
+        return orig(Q, K, V, eta[[2, 1, 0]] if eta.ndim == 2 else eta, *a, **k)
+    return f
+
+
 def _identity_scaled(orig):
     return lambda X, W0=None, W2=None: X / np.sqrt(X.shape[1])  # an attention-style 1/sqrt(h)
 
@@ -132,6 +155,14 @@ MUTATIONS = [
      lambda: TLA.test_scan_equals_masked_quadratic_form(0, 4)),
     ("momentum coefficient exponent", LA, "momentum_weight", _momentum_exponent,
      lambda: TLA.test_momentum_scan_equals_recurrent_heavy_ball(1, 0.5)),
+    ("reset flag ignored", L, "lact_pair", _drop_flag(L.CHUNK_RESET),
+     lambda: TLV.test_reset_equals_a_fresh_call(0)),
+    ("apply-only flag ignored", L, "lact_pair", _drop_flag(L.CHUNK_NO_UPDATE),
+     lambda: TLV.test_apply_only_chunk_equals_removing_its_writes(1)),
+    ("inner steps ignored", L, "lact_pair", _one_inner_step,
+     lambda: TLV.test_inner_steps_equal_repeated_chunks(0, 2)),
+    ("eta rows of W0 and W2 swapped", L, "lact_pair", _eta_rows_swapped,
+     lambda: TLV.test_eta_per_matrix_write_is_each_rows_autograd_gradient()),
     ("identity kernel rescaled", LA, "phi_identity", _identity_scaled,
      lambda: TLA.test_identity_scan_equals_recurrent_linear_fast_weight(0, 0.0, 8)),
     ("In-Place update before apply", IP, "inplace_sequence", _update_before_apply,
