@@ -138,7 +138,31 @@ typedef struct {
   float eps_norm;        /* default 1e-5 */
   float eps_ns;          /* default 1e-7 */
   int64_t w_batch_stride;/* 0: weights shared by the batch; else element stride per sequence */
+  /* Loop variants. A zero-initialised tail gives the plain loop above. */
+  const uint8_t* chunk_flags; /* device [B, Nk/chunk_kv] or NULL: TTT_CHUNK_* bits per sequence and chunk */
+  int32_t inner_steps;   /* writes per chunk; 0 or 1: one */
+  int32_t eta_per_matrix;/* 0: eta [B, H, Nk]; 1: eta [B, H, 3, Nk], one row per matrix W0, W1, W2 */
 } ttt_lact_params;
+
+/* Per-chunk flags (chunk_flags), shared by the heads of a sequence:
+ *   TTT_CHUNK_NO_UPDATE  the chunk is applied with the current weights and writes nothing:
+ *                        weights and momentum are left as they are (apply-only chunks, e.g.
+ *                        the noisy chunks of autoregressive video: "Test-Time Training Done
+ *                        Right" notes, section 2.3 update-order table and section 2.4);
+ *   TTT_CHUNK_RESET      before the chunk is applied or written, the weights return to the
+ *                        call's initial weights (W0, W1, W2 of this sequence) and the momentum
+ *                        to zero, as if a new call started there (a document boundary inside a
+ *                        packed sequence: "In-Place Test-Time Training" notes, section 3.4).
+ * Both may be set (reset, then apply only). The flags live on the device and are read by the
+ * kernels only (not validated on the host); other bits are ignored. The array must stay valid
+ * until the call's work on the stream has finished.
+ * inner_steps (KV-binding summary page, "Motivation": more inner-loop iterations per chunk)
+ * repeats the chunk's write that many times on the same tokens (gradient
+ * at the current weights, momentum, Newton-Schulz, subtract, renorm); apply-then-update applies
+ * before the first write, update-then-apply after the last. 1 <= inner_steps <= 64 (0 means 1),
+ * else TTT_ERR_ARG. eta_per_matrix (notes, section 2.1: eta may be predicted separately for the
+ * three matrices): matrix X takes the gradient of the chunk loss weighted by its own row eta_X. */
+enum { TTT_CHUNK_NO_UPDATE = 1, TTT_CHUNK_RESET = 2 };
 
 ttt_status ttt_lact_forward(const ttt_lact_params* p,
                             const void* Q, const void* K, const void* V, const float* eta,

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libttt_lact.so")
 
 TTT_OK, TTT_ERR_ARG, TTT_ERR_SHAPE, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP = 0, -1, -2, -3, -4, -5
 APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
+CHUNK_NO_UPDATE, CHUNK_RESET = 1, 2  # per-chunk flags of lact_forward
 FEATURE_MAPS = {"swiglu": 0, "identity": 1}  # ttt_feature_map
 FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
@@ -41,7 +42,8 @@ class LactParams(ctypes.Structure):
                 ("chunk_kv", ctypes.c_int32), ("order", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("update_mask", ctypes.c_uint32), ("weight_norm", ctypes.c_int32), ("muon", ctypes.c_int32),
                 ("momentum", ctypes.c_float), ("eps_norm", ctypes.c_float), ("eps_ns", ctypes.c_float),
-                ("w_batch_stride", ctypes.c_int64)]
+                ("w_batch_stride", ctypes.c_int64), ("chunk_flags", ctypes.c_void_p),
+                ("inner_steps", ctypes.c_int32), ("eta_per_matrix", ctypes.c_int32)]
 
 
 class LinattnParams(ctypes.Structure):
@@ -208,9 +210,11 @@ def _check_weights(W0, W1, W2, B, H, h):
 def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[int] = None,
                  order: int = APPLY_THEN_UPDATE, update_mask: int = 7, weight_norm: bool = True,
                  muon: bool = False, momentum: float = 0.0, eps_norm: float = 1e-5, eps_ns: float = 1e-7,
-                 M_in=None, want_state: bool = True, stream=None):
-    """Chunked LaCT layer. Q [B,H,Nq,h], K/V [B,H,Nk,h] (bf16 or fp32), eta [B,H,Nk] fp32,
-    W0/W2 [H,h,rh] and W1 [H,rh,h] fp32 (or [B,H,...] per sequence), M_in [B,H,3,h*rh] or None.
+                 M_in=None, chunk_flags=None, inner_steps: int = 1, want_state: bool = True, stream=None):
+    """Chunked LaCT layer. Q [B,H,Nq,h], K/V [B,H,Nk,h] (bf16 or fp32), eta [B,H,Nk] fp32
+    (or [B,H,3,Nk]: one row per matrix W0, W1, W2), W0/W2 [H,h,rh] and W1 [H,rh,h] fp32 (or
+    [B,H,...] per sequence), M_in [B,H,3,h*rh] or None. chunk_flags: None or a uint8 device
+    tensor [B, Nk/chunk_kv] of CHUNK_NO_UPDATE / CHUNK_RESET bits; inner_steps: writes per chunk.
     Returns (O, W0_out, W1_out, W2_out, M_out); the last four are None if not want_state."""
     torch = _torch()
     lib = load()
@@ -226,8 +230,15 @@ def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[i
     _check(eta, "eta", torch.float32, dev)
     for t, n in ((W0, "W0"), (W1, "W1"), (W2, "W2"), (M_in, "M_in")):
         _check(t, n, torch.float32, dev)
-    if K.shape != (B, H, Nk, h) or V.shape != K.shape or eta.shape != (B, H, Nk):
-        raise ValueError("K/V must be [B,H,Nk,h] and eta [B,H,Nk]")
+    eta3 = eta.dim() == 4
+    if K.shape != (B, H, Nk, h) or V.shape != K.shape or tuple(eta.shape) != ((B, H, 3, Nk) if eta3 else (B, H, Nk)):
+        raise ValueError("K/V must be [B,H,Nk,h] and eta [B,H,Nk] (or [B,H,3,Nk], one row per matrix)")
+    if chunk_flags is not None:
+        _check(chunk_flags, "chunk_flags", torch.uint8, dev)
+        if chunk_kv <= 0 or tuple(chunk_flags.shape) != (B, Nk // chunk_kv):
+            raise ValueError("chunk_flags must be uint8 [B, Nk/chunk_kv]")
+    if not (1 <= inner_steps <= 64):
+        raise ValueError("inner_steps must lie in [1, 64]")
     _check_weights(W0, W1, W2, B, H, h)
     if M_in is not None and tuple(M_in.shape) != (B, H, 3, h * rh):
         raise ValueError("M_in must be [B,H,3,h*rh]")
@@ -235,7 +246,7 @@ def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[i
         raise ValueError("momentum must lie in [0, 1)")
     p = LactParams(B, H, Nq, Nk, h, rh // h, chunk_q, chunk_kv, order, _io_dtype(Q), update_mask,
                    int(bool(weight_norm)), int(bool(muon)), momentum, eps_norm, eps_ns,
-                   H * h * rh if per_seq else 0)
+                   H * h * rh if per_seq else 0, _ptr(chunk_flags), int(inner_steps), int(eta3))
     O = torch.empty_like(Q)
     outs = [None] * 4
     if want_state:

@@ -25,16 +25,20 @@ namespace ttt {
 // operand shadow buffers (a matrix outside the update mask keeps its initial shadow in each).
 // grid (rh/32 * h/32, 3, P), block 256: one 32 x 32 tile of the state (rows j, columns c);
 // W0/W2 and their momentum arrive in row form [h][rh] and are transposed through LDS.
+// With flags (reset mode, before chunk c): only the pairs whose sequence has TTT_CHUNK_RESET set
+// at chunk c return to the initial weights, with zero momentum (M_in is then null).
 template <class OpT>
 __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float* W0, const float* W1,
                                                        const float* W2, const float* M_in, int H,
-                                                       int64_t w_batch_stride) {
+                                                       int64_t w_batch_stride, const uint8_t* flags, int nch,
+                                                       int c) {
   __shared__ float tw[32][33], tm[32][33];
   const int mat = blockIdx.y, pair = blockIdx.z;
   const int h = s.h, rh = s.rh, hb = h / 32;
   const int64_t n = (int64_t)rh * h;
   const int j0 = (blockIdx.x / hb) * 32, c0 = (blockIdx.x % hb) * 32;
   const int b = pair / H, head = pair % H;
+  if (flags && !(flags[(int64_t)b * nch + c] & TTT_CHUNK_RESET)) return;
   const float* src = (mat == 0 ? W0 : mat == 1 ? W1 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
   const float* msrc = M_in ? M_in + ((int64_t)pair * 3 + mat) * n : nullptr;
   const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
@@ -69,6 +73,44 @@ __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float
 #pragma unroll
       for (int q = 0; q < 4; ++q) dt[q] = Mfma<OpT>::from_f32(tw[c4 + q][r]);
     }
+  }
+}
+
+// Apply-only chunks (TTT_CHUNK_NO_UPDATE at chunk c): before the chunk's writes the state and
+// momentum of the flagged pairs are saved to bak [2][P][3][rh*h]; after them they are put back
+// and the shadow buffer the next reads use (sh) is rebuilt from them, so the writes (computed for
+// every pair of the launch) leave no trace on those pairs. grid (rh/32 * h/32, 3, P), block 256.
+template <class OpT>
+__global__ void __launch_bounds__(256) lact_hold_kernel(LactState s, float* bak, const uint8_t* flags, int nch, int c,
+                                                       int H, int restore, OpT* sh) {
+  __shared__ float tw[32][33];
+  const int mat = blockIdx.y, pair = blockIdx.z;
+  if (!(flags[(int64_t)(pair / H) * nch + c] & TTT_CHUNK_NO_UPDATE)) return;
+  const int h = s.h, rh = s.rh, hb = h / 32;
+  const int64_t n = (int64_t)rh * h;
+  const int j0 = (blockIdx.x / hb) * 32, c0 = (blockIdx.x % hb) * 32;
+  const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+  const int64_t e = ((int64_t)pair * 3 + mat) * n + (int64_t)(j0 + r) * h + c0 + c4;
+  float* bw = bak + e;
+  float* bm = bak + (int64_t)s.P * 3 * n + e;
+  if (!restore) {
+    *reinterpret_cast<f32x4*>(bw) = *reinterpret_cast<const f32x4*>(s.W + e);
+    *reinterpret_cast<f32x4*>(bm) = *reinterpret_cast<const f32x4*>(s.M + e);
+    return;
+  }
+  const f32x4 v = *reinterpret_cast<const f32x4*>(bw);
+  *reinterpret_cast<f32x4*>(s.W + e) = v;
+  *reinterpret_cast<f32x4*>(s.M + e) = *reinterpret_cast<const f32x4*>(bm);
+  OpT* d = sh + (int64_t)pair * 4 * n + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + (int64_t)(j0 + r) * h + c0 + c4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = Mfma<OpT>::from_f32(v[q]);
+  if (mat == 1) {  // W1^T [h][rh]: row c0 + r, columns j0 + c4..
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tw[r][c4 + q] = v[q];
+    __syncthreads();
+    OpT* dt = sh + (int64_t)pair * 4 * n + 3 * n + (int64_t)(c0 + r) * rh + j0 + c4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dt[q] = Mfma<OpT>::from_f32(tw[c4 + q][r]);
   }
 }
 
@@ -156,7 +198,7 @@ __global__ void __launch_bounds__(256) lact_final_kernel(LactState s, float* W0o
 
 // ---------------------------------------------------------------------------------------
 template <class IoT, class OpT, int H>
-static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, const void* Q,
+static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, float* bak, const void* Q,
                            const void* K, const void* V, const float* eta, const float* W0,
                            const float* W1, const float* W2, const float* M_in, void* O, float* W0o,
                            float* W1o, float* W2o, float* Mo, hipStream_t st) {
@@ -187,7 +229,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   {
     LaunchTimer lt(K_LACT_INIT, st);
     hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3((unsigned)(n / 1024), 3, P), dim3(256), 0, st, s, W0, W1,
-                       W2, M_in, p.H, p.w_batch_stride);
+                       W2, M_in, p.H, p.w_batch_stride, nullptr, 0, 0);
     TTT_HIP(hipGetLastError());
     hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
     TTT_HIP(hipGetLastError());
@@ -298,14 +340,22 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     aa.W1 = b + 2 * n;
     aa.W1T = b + 3 * n;
   };
+  // per-chunk flags (resets before the chunk, apply-only chunks held) and inner steps: the k-th
+  // write of the call reads shadow buffer k & 1 and writes the other
+  const uint8_t* flags = p.chunk_flags;
+  const int steps = p.inner_steps > 1 ? p.inner_steps : 1;
+  const dim3 tgrid((unsigned)(n / 1024), 3, P);
+  int it = 0;
   for (int c = 0; c < nch; ++c) {
-    const OpT* rd = sh + (c & 1) * shb;
-    const OpT* wr = sh + ((c + 1) & 1) * shb;
-    set_apply_weights(rd);
-    ga.W0T = rd;
-    ga.W2T = rd + n;
-    ga.W1 = rd + 2 * n;
-    ua.s.sh = const_cast<OpT*>(wr);
+    if (flags) {
+      LaunchTimer lt(K_LACT_INIT, st);
+      hipLaunchKernelGGL(lact_init_kernel<OpT>, tgrid, dim3(256), 0, st, s, W0, W1, W2, nullptr, p.H,
+                         p.w_batch_stride, flags, nch, c);
+      TTT_HIP(hipGetLastError());
+      hipLaunchKernelGGL(lact_hold_kernel<OpT>, tgrid, dim3(256), 0, st, s, bak, flags, nch, c, p.H, 0, nullptr);
+      TTT_HIP(hipGetLastError());
+    }
+    set_apply_weights(sh + (it & 1) * shb);
     aa.t_base = c * p.chunk_q;
     aa.t_limit = (c + 1) * p.chunk_q;
     if (p.order == TTT_APPLY_THEN_UPDATE && !fuse_ua) {
@@ -315,30 +365,42 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
     ga.t_base = c * p.chunk_kv;
     ga.eta_scale = s.esc + (int64_t)c * P * S;
     ga.t_limit = (c + 1) * p.chunk_kv;
-    {
-      const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
-      if constexpr (WS)
-        TTT_HIP(launch_k(K_LACT_GRAD, gkw, dim3(grid), dim3(512), glds, st, ga, S, P));
-      else if constexpr (RD)
-        TTT_HIP(launch_k(K_LACT_GRAD, gkr, dim3(grid), dim3(256), glds, st, ga, S, P));
-      else
-        TTT_HIP(launch_k(K_LACT_GRAD, gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga));
+    for (int k = 0; k < steps; ++k, ++it) {
+      const OpT* rd = sh + (it & 1) * shb;
+      const OpT* wr = sh + ((it + 1) & 1) * shb;
+      ga.W0T = rd;
+      ga.W2T = rd + n;
+      ga.W1 = rd + 2 * n;
+      ua.s.sh = const_cast<OpT*>(wr);
+      {
+        const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
+        if constexpr (WS)
+          TTT_HIP(launch_k(K_LACT_GRAD, gkw, dim3(grid), dim3(512), glds, st, ga, S, P));
+        else if constexpr (RD)
+          TTT_HIP(launch_k(K_LACT_GRAD, gkr, dim3(grid), dim3(256), glds, st, ga, S, P));
+        else
+          TTT_HIP(launch_k(K_LACT_GRAD, gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga));
+      }
+      if (fuse_ua && k == 0) {  // the chunk's apply reads the chunk-start weights (buffer rd)
+        int nu = nupd;
+        void* args[] = {&ua, &aa, &nu};
+        TTT_HIP(launch_raw(K_LACT_UPD_APPLY, uak, dim3((unsigned)nupd + agrid.x), dim3(512), args, (size_t)ualds, st));
+      } else if (uk) {
+        void* args[] = {&ua};
+        TTT_HIP(launch_raw(K_LACT_UPDATE, uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
+      } else {
+        LaunchTimer lt(K_LACT_UPDATE, st);
+        TTT_HIP(tu_run<OpT>(ua, st));
+      }
     }
-    if (fuse_ua) {
-      int nu = nupd;
-      void* args[] = {&ua, &aa, &nu};
-      TTT_HIP(launch_raw(K_LACT_UPD_APPLY, uak, dim3((unsigned)nupd + agrid.x), dim3(512), args, (size_t)ualds, st));
-      continue;
-    }
-    if (uk) {
-      void* args[] = {&ua};
-      TTT_HIP(launch_raw(K_LACT_UPDATE, uk, dim3(ugrid), dim3(512), args, (size_t)ulds, st));
-    } else {
-      LaunchTimer lt(K_LACT_UPDATE, st);
-      TTT_HIP(tu_run<OpT>(ua, st));
+    if (flags) {
+      LaunchTimer lt(K_LACT_INIT, st);
+      hipLaunchKernelGGL(lact_hold_kernel<OpT>, tgrid, dim3(256), 0, st, s, bak, flags, nch, c, p.H, 1,
+                         const_cast<OpT*>(sh + (it & 1) * shb));
+      TTT_HIP(hipGetLastError());
     }
     if (p.order == TTT_UPDATE_THEN_APPLY) {
-      set_apply_weights(wr);
+      set_apply_weights(sh + (it & 1) * shb);
       const ttt_status e = apply();
       if (e != TTT_OK) return e;
     }
@@ -371,6 +433,9 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   // heavy-ball coefficient in [0, 1), epsilons finite and >= 0 (the comparisons reject NaN)
   if (!(q.momentum >= 0.f && q.momentum < 1.f)) return TTT_ERR_ARG;
   if (!(q.eps_norm >= 0.f && q.eps_norm <= FLT_MAX) || !(q.eps_ns >= 0.f && q.eps_ns <= FLT_MAX)) return TTT_ERR_ARG;
+  if (q.inner_steps < 0 || q.inner_steps > 64) return TTT_ERR_ARG;
+  if (q.eta_per_matrix != 0 && q.eta_per_matrix != 1) return TTT_ERR_ARG;
+  if (q.eta_per_matrix) return TTT_ERR_UNSUPPORTED;
   if (q.Nq % q.chunk_q || q.Nk % q.chunk_kv) return TTT_ERR_SHAPE;
   if (q.Nq / q.chunk_q != q.Nk / q.chunk_kv) return TTT_ERR_SHAPE;
   const int64_t rh64 = (int64_t)q.r * q.h;
@@ -416,6 +481,7 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   const int64_t NSZ = 4 * n + 2 * (int64_t)h * h + TU_SS;
   const size_t oNs = plan.add((size_t)P * 3 * NSZ * 4);
   const size_t oEsc = plan.add((size_t)nch * P * S * 4);
+  const size_t oBak = q.chunk_flags ? plan.add((size_t)2 * P * 3 * n * 4) : 0;  // held state of apply-only chunks
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -444,8 +510,8 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   }
 #define TTT_LACT_CASE(IOT, OPT, HH)                                                                  \
   case HH:                                                                                         \
-    return lact_run<IOT, OPT, HH>(qq, s, S, Q, K, V, eta, W0, W1, W2, M_in, O, W0_out, W1_out, W2_out, \
-                                  M_out, st);
+    return lact_run<IOT, OPT, HH>(qq, s, S, q.chunk_flags ? reinterpret_cast<float*>(ws + oBak) : nullptr, Q, K, \
+                                  V, eta, W0, W1, W2, M_in, O, W0_out, W1_out, W2_out, M_out, st);
   try {
     if (bf16) {
       switch (h) {

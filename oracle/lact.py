@@ -43,7 +43,8 @@ supports):
 
 Variants of the same loop (the reading notes' section 2.3 update-order table
 and section 2.4; the In-Place notes, section 3.4; the notes' section 2.1 symbol
-table; the summary page's "Experimental results"):
+table; the KV-binding summary page, "Motivation", on more inner-loop
+iterations):
 
 10. Per-chunk write mask: an apply-only chunk (the autoregressive-video row's
     noisy chunks) is applied with the current weights and writes nothing:

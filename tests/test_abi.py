@@ -117,6 +117,19 @@ def test_lact_empty_batch_is_a_no_op(lib):
     assert _lact(lib, _lp(B=0), ws=ctypes.c_void_p(0x100000), size=max(size, 256))[0] == ttt.TTT_OK
 
 
+def test_lact_loop_variant_fields(lib):
+    # the struct's tail: flags pointer, inner steps, eta per matrix (a zero tail is the plain loop)
+    assert ctypes.sizeof(ttt.LactParams) == 88
+    st, plain = _lact(lib, _lp())
+    assert st == ttt.TTT_OK
+    st, flagged = _lact(lib, _lp(chunk_flags=0x2000))
+    # apply-only chunks hold the state and momentum of every pair: 2 x 32 pairs x 3 x 128 x 256 fp32
+    assert st == ttt.TTT_OK and flagged == plain + 2 * 32 * 3 * 128 * 256 * 4
+    assert _lact(lib, _lp(inner_steps=4)) == (ttt.TTT_OK, plain)
+    for bad in (dict(inner_steps=-1), dict(inner_steps=65), dict(eta_per_matrix=2), dict(eta_per_matrix=-1)):
+        assert _lact(lib, _lp(**bad))[0] == ttt.TTT_ERR_ARG, bad
+
+
 def _lin(lib, W0=FAKE, W2=FAKE, ws=None, size=0, **kw):
     base = dict(B=4, H=8, N=8192, h=64, r=2, chunk=512, order=0, dtype=ttt.BF16, w_batch_stride=0)
     base.update(kw)
@@ -249,6 +262,28 @@ def test_identity_binding_checks_before_any_launch(monkeypatch, lib, bad):
         fm = "relu"
     with pytest.raises(ValueError):
         ttt.linattn_forward(Q, Q, Q, eta, W0, None, W1, chunk=64, feature_map=fm)
+
+
+@pytest.mark.parametrize("bad", ["flags dtype", "flags shape", "inner steps 0", "eta rows"])
+def test_lact_binding_checks_loop_variants_before_any_launch(monkeypatch, lib, bad):
+    import torch
+    _fake_call_guard(monkeypatch)
+    B, H, N, h, rh = 2, 2, 256, 64, 128
+    bf, f32 = torch.bfloat16, torch.float32
+    Q = _FakeCuda((B, H, N, h), bf)
+    eta = _FakeCuda((B, H, N), f32)
+    W0, W1 = _FakeCuda((H, h, rh), f32), _FakeCuda((H, rh, h), f32)
+    kw = dict(chunk_q=64)
+    if bad == "flags dtype":
+        kw["chunk_flags"] = _FakeCuda((B, 4), torch.int32)
+    elif bad == "flags shape":
+        kw["chunk_flags"] = _FakeCuda((B, 5), torch.uint8)
+    elif bad == "inner steps 0":
+        kw["inner_steps"] = 0
+    else:
+        eta = _FakeCuda((B, H, 2, N), f32)
+    with pytest.raises(ValueError):
+        ttt.lact_forward(Q, Q, Q, eta, W0, W1, W0, **kw)
 
 
 @pytest.mark.parametrize("bad", ["M_in shape", "momentum 1", "momentum nan"])
