@@ -53,7 +53,10 @@ struct GradArgs {
   int64_t out_mat_stride; // between P0 / P1 / P2 (= rh*H)
   const float* eta_scale; // [pair][segment] power-of-two step-size scales of the region
                           // (grad_ws_kernel; the other kernels derive them themselves)
+  int64_t eta_mat_stride; // E3 kernels: between the step-size rows of W0, W1, W2 (eta [pair][3][N])
 };
+// E3 (eta per matrix): the gradient of W_X uses its own step-size row eta_X: eta_1 scales H in
+// P1 = (eta_1 H)^T V, eta_0 and eta_2 scale D in X0 and X2.
 
 // K-major fragment: element (k, n) at base[k * ld + n]; lane l receives n = l & 31 and the
 // k values of its K step (16-bit: LDS transpose read; fp32: one strided element).
@@ -163,12 +166,13 @@ __device__ __forceinline__ typename Mfma<T>::frag tile_kfrag_tr(const T* tile, i
 }
 
 // LDS bytes of grad_kernel<OpT, H, LINATTN>.
-template <class OpT, int H, bool LINATTN>
+template <class OpT, int H, bool LINATTN, bool E3 = false>
 constexpr int grad_lds_bytes() {
   constexpr int P = Pad<OpT>::v;
   constexpr int nW = LINATTN ? 2 : 3;
   constexpr int nMid = LINATTN ? 1 : 3;
-  return (nW * RB * (H + P) + 2 * TT * (H + P) + nMid * RB * (TT + P)) * (int)sizeof(OpT) + TT * 4 + 16 * 4;
+  return (nW * RB * (H + P) + 2 * TT * (H + P) + nMid * RB * (TT + P)) * (int)sizeof(OpT) + (E3 ? 3 : 1) * TT * 4 +
+         16 * 4;
 }
 
 // grid: x = hidden block (rh/64), y = token segment, z = pair. block: 256 threads (4 waves).
@@ -177,8 +181,10 @@ constexpr int grad_lds_bytes() {
 // th*32.. (operands: fast-weight rows and token rows, both K-contiguous), the SwiGLU / silu'
 // epilogue writes eta*H, X0, X2 as [j][t] tiles, and the token contractions read K and V
 // K-major through the LDS transpose read.
-template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID>
+template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID, bool E3 = false>
 __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
+  static_assert(!(E3 && LINATTN), "one step size per token in linear-attention mode");
+  constexpr int NE = E3 ? 3 : 1;  // step-size rows
   typedef Mfma<OpT> M;
   constexpr int P = Pad<OpT>::v;
   constexpr int LDW = H + P;        // W block / token tile row stride
@@ -196,8 +202,8 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   OpT* Ks = Wb + nW * RB * LDW;                              // [TT][LDW]
   OpT* Vs = Ks + TT * LDW;                                   // [TT][LDW]
   OpT* Mid = Vs + TT * LDW;                                  // [nMid][RB][LDT]
-  float* eta_s = reinterpret_cast<float*>(Mid + nMid * RB * LDT);  // [TT]
-  float* red = eta_s + TT;                                   // [16]
+  float* eta_s = reinterpret_cast<float*>(Mid + nMid * RB * LDT);  // [NE][TT]
+  float* red = eta_s + NE * TT;                              // [16]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int jb = blockIdx.x, seg = blockIdx.y, pair = blockIdx.z;
@@ -230,7 +236,8 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   float scale = 1.f;
   if constexpr (SCALE_MID) {
     float mx = 0.f;
-    for (int t = t_begin + tid; t < t_end; t += 256) mx = fmaxf(mx, ep[t]);
+    for (int e = 0; e < NE; ++e)
+      for (int t = t_begin + tid; t < t_end; t += 256) mx = fmaxf(mx, ep[e * a.eta_mat_stride + t]);
     mx = block_max(mx, red);
     if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
   }
@@ -243,7 +250,10 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     __syncthreads();  // previous tile's LDS reads are done
     stage.store(Ks, Vs, LDW, tid);
-    if (tid < TT) eta_s[tid] = (t0 + tid < t_end) ? ep[t0 + tid] * scale : 0.f;
+    if (tid < NE * TT) {
+      const int e = tid / TT, t = tid % TT;
+      eta_s[tid] = (t0 + t < t_end) ? ep[e * a.eta_mat_stride + t0 + t] * scale : 0.f;
+    }
     __syncthreads();
     if (t0 + TT < t_end) stage.load(Kp, Vp, t0 + TT, t_end, tid);  // in flight during the MFMAs
 
@@ -267,7 +277,8 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
       }
       // epilogue: element (j, t) with j = jh*32 + acc_row, t = th*32 + lane&31
       const int tl = th * 32 + (lane & 31);
-      const float e = eta_s[tl];
+      const float e = eta_s[(E3 ? TT : 0) + tl];                 // eta (eta_1 with E3)
+      const float e0 = E3 ? eta_s[tl] : e, e2 = E3 ? eta_s[2 * TT + tl] : e;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = jh * 32 + acc_row(r, lane);
@@ -276,9 +287,8 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
         const float sil = A * sg;
         Mid[(0 * RB + j) * LDT + tl] = M::from_f32(e * sil * Bm);  // eta * H
         if constexpr (!LINATTN) {
-          const float D = e * fd[r];
-          Mid[(1 * RB + j) * LDT + tl] = M::from_f32(D * Bm * (sg * (1.f + A * (1.f - sg))));  // X0
-          Mid[(2 * RB + j) * LDT + tl] = M::from_f32(D * sil);                                 // X2
+          Mid[(1 * RB + j) * LDT + tl] = M::from_f32(e0 * fd[r] * Bm * (sg * (1.f + A * (1.f - sg))));  // X0
+          Mid[(2 * RB + j) * LDT + tl] = M::from_f32(e2 * fd[r] * sil);                                 // X2
         }
       }
     }
@@ -333,14 +343,15 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
 // Block mapping: the hidden blocks of one (pair, segment) are workgroups w, w+8, ..., i.e. on
 // one XCD, so its K / V tiles are fetched from HBM once per XCD.
 // grid: x = rh/64 * 8 * ceil(P * nseg / 8); block 256.
-template <class OpT, int H, bool LINATTN>
+template <class OpT, int H, bool LINATTN, bool E3 = false>
 constexpr int grad_rd_lds_bytes() {
   constexpr int P = Pad<OpT>::v;
   constexpr int NMAT = LINATTN ? 1 : 3;
   constexpr int QS = 32 / Mfma<OpT>::KSTEP;
   constexpr int FRAG = (int)sizeof(typename Mfma<OpT>::frag);
   (void)P;
-  return 4 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + (2 * TT + 16) * 4 + NWAVE * NMAT * QS * 64 * FRAG;
+  return 4 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + (2 * (E3 ? 3 : 1) * TT + 16) * 4 +
+         NWAVE * NMAT * QS * 64 * FRAG;
 }
 
 // sigmoid through the hardware exp2 and reciprocal (about 1 ulp each; the results feed 16-bit
@@ -349,9 +360,11 @@ __device__ __forceinline__ float sigmoid_fast(float a) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
 }
 
-template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID>
+template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID, bool E3 = false>
 __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int npairs) {
   static_assert(H <= 128, "register budget");
+  static_assert(!(E3 && LINATTN), "one step size per token in linear-attention mode");
+  constexpr int NE = E3 ? 3 : 1;  // step-size rows
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
   constexpr int P = Pad<OpT>::v;
@@ -367,8 +380,8 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
 
   extern __shared__ __align__(16) unsigned char smem[];
   OpT* tiles = reinterpret_cast<OpT*>(smem);                  // [2 buffers][K, V][TT][LDK]
-  float* eta_s = reinterpret_cast<float*>(tiles + 4 * TILE);  // [2 buffers][TT]
-  float* red = eta_s + 2 * TT;                                // [16]
+  float* eta_s = reinterpret_cast<float*>(tiles + 4 * TILE);  // [2 buffers][NE][TT]
+  float* red = eta_s + 2 * NE * TT;                           // [16]
   frag* xch = reinterpret_cast<frag*>(red + 16);              // [NWAVE][NMAT][QS][64]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -393,7 +406,10 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
   auto fetch = [&](int i) {
     const int t0 = t_begin + i * TT;
     stage.load(Kp, Vp, t0, t_end, tid);
-    if (tid < TT) ev = (t0 + tid < t_end) ? ep[t0 + tid] : 0.f;
+    if (tid < NE * TT) {
+      const int e = tid / TT, t = tid % TT;
+      ev = (t0 + t < t_end) ? ep[e * a.eta_mat_stride + t0 + t] : 0.f;
+    }
   };
   if (ntiles > 0) fetch(0);
 
@@ -414,14 +430,15 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
   float scale = 1.f;
   if constexpr (SCALE_MID) {
     float mx = 0.f;
-    for (int t = t_begin + tid; t < t_end; t += 256) mx = fmaxf(mx, ep[t]);
+    for (int e = 0; e < NE; ++e)
+      for (int t = t_begin + tid; t < t_end; t += 256) mx = fmaxf(mx, ep[e * a.eta_mat_stride + t]);
     mx = block_max(mx, red);
     if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
   }
   auto put = [&](int i) {
     OpT* b = tiles + (i & 1) * 2 * TILE;
     stage.template store_at<TL>(b, b + TILE, tid);
-    if (tid < TT) eta_s[(i & 1) * TT + tid] = ev * scale;
+    if (tid < NE * TT) eta_s[(i & 1) * NE * TT + tid] = ev * scale;
   };
 
   f32x16 acc[NMAT][CH];
@@ -448,7 +465,8 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
       if constexpr (DO_EPI) {
 #pragma unroll
         for (int r = 16 * s / KS; r < 16 * (s + 1) / KS; ++r) {
-          const float e = er[8 * (r >> 2) + (r & 3)];
+          const int ti = 8 * (r >> 2) + (r & 3);
+          const float e = er[(E3 ? TT : 0) + ti];  // eta (eta_1 with E3)
           const float A = Fp[0][r], Bm = Fp[1][r];
           const float sg = sigmoid_fast(A);
           const float sil = A * sg;
@@ -456,8 +474,9 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
           Fp[0][r] = sil * eB;
           if constexpr (!LINATTN) {
             const float Dr = Fp[2][r];
-            Fp[1][r] = (eB * Dr) * (sg * fmaf(A, 1.f - sg, 1.f));
-            Fp[2][r] = (e * sil) * Dr;
+            const float e0 = E3 ? er[ti] : e, e2 = E3 ? er[2 * TT + ti] : e;
+            Fp[1][r] = ((E3 ? e0 * Bm : eB) * Dr) * (sg * fmaf(A, 1.f - sg, 1.f));
+            Fp[2][r] = (e2 * sil) * Dr;
           }
         }
       }
@@ -510,7 +529,7 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
       if (i + 2 < ntiles) fetch(i + 2);
     }
     __syncthreads();  // tile i+1 published
-    fwd_epi(tiles + ((i + 1) & 1) * 2 * TILE, Fn, Fc, eta_s + (i & 1) * TT, std::true_type{});
+    fwd_epi(tiles + ((i + 1) & 1) * 2 * TILE, Fn, Fc, eta_s + (i & 1) * NE * TT, std::true_type{});
     contract(tiles + (i & 1) * 2 * TILE, Fc);
   };
 
@@ -556,15 +575,16 @@ __global__ void __launch_bounds__(256) grad_rd_kernel(GradArgs a, int nseg, int 
 //       fp16), then P1 += (eta H)^T V, P0 += X0^T K, P2 += X2^T K over the tile.
 // One barrier per step: the forward of tile i+1 runs beside the contraction of tile i, and each
 // role orders its work so that its VALU phase meets the other role's MFMA phase.
-template <class OpT, int H>
+template <class OpT, int H, bool E3 = false>
 constexpr int grad_ws_lds_bytes() {
-  return 3 * 2 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + 3 * TT * 4 + 2 * 4 * 3 * 2 * 64 * 16;
+  return 3 * 2 * TT * TileLayout<OpT, H>::LD * (int)sizeof(OpT) + 3 * (E3 ? 3 : 1) * TT * 4 + 2 * 4 * 3 * 2 * 64 * 16;
 }
 
 // Workgroup index bid: XCD slot bid & 7; slot = bid >> 3 holds hidden block slot % njb of the
 // (pair, segment) group (bid & 7) + 8 (slot / njb), group = pair * nseg + segment.
-template <class IoT, class OpT, int H, bool SCALE_MID>
+template <class IoT, class OpT, int H, bool SCALE_MID, bool E3 = false>
 __device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int npairs, int bid, unsigned char* smem) {
+  constexpr int NE = E3 ? 3 : 1;  // step-size rows
   static_assert(std::is_same<OpT, _Float16>::value && (H == 64 || H == 128), "fp16 operands, h = 64 or 128");
   typedef Mfma<OpT> M;
   typedef typename M::frag frag;
@@ -577,8 +597,8 @@ __device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int np
   constexpr int QS = 32 / M::KSTEP;         // contraction K steps over a 32-token half
 
   OpT* tiles = reinterpret_cast<OpT*>(smem);                      // [3 buffers][K, V][TT][LD]
-  float* eta_s = reinterpret_cast<float*>(tiles + 3 * 2 * TILE);  // [3 buffers][TT] scaled step sizes
-  frag* inter = reinterpret_cast<frag*>(eta_s + 3 * TT);          // [2][4 forward waves][3][QS][64]
+  float* eta_s = reinterpret_cast<float*>(tiles + 3 * 2 * TILE);  // [3 buffers][NE][TT] scaled step sizes
+  frag* inter = reinterpret_cast<frag*>(eta_s + 3 * NE * TT);     // [2][4 forward waves][3][QS][64]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int njb = a.rh / RB;
@@ -606,7 +626,10 @@ __device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int np
   auto fetch = [&](int i, Stage& stg, float& ev) {
     const int t0 = t_begin + i * TT;
     stg.load(Kp, Vp, t0, t_end, ctid);
-    if (ctid < TT) ev = (t0 + ctid < t_end) ? ep[t0 + ctid] : 0.f;
+    if (ctid < NE * TT) {
+      const int e = ctid / TT, t = ctid % TT;
+      ev = (t0 + t < t_end) ? ep[e * a.eta_mat_stride + t0 + t] : 0.f;
+    }
   };
   if (fwd) {
     const OpT* src[3] = {reinterpret_cast<const OpT*>(a.W0T), reinterpret_cast<const OpT*>(a.W2T),
@@ -646,7 +669,7 @@ __device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int np
           F[2] = M::mma(vf, wf[2][s], F[2]);
         }
         // epilogue: F[0] <- eta*H, F[1] <- X0, F[2] <- X2, as contraction fragments
-        const float* er = eta_s + fb * TT + th * 32 + 4 * (lane >> 5);
+        const float* er = eta_s + fb * NE * TT + th * 32 + 4 * (lane >> 5);
         frag* dst = inter + (size_t)((((i + 1) & 1) * 4 + w) * 3) * QS * 64 + lane;
 #pragma unroll
         for (int q = 0; q < QS; ++q) {
@@ -654,14 +677,17 @@ __device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int np
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * q + e;
-            const float ev = er[8 * (r >> 2) + (r & 3)];
+            const int ti = 8 * (r >> 2) + (r & 3);
+            const float ev = er[(E3 ? TT : 0) + ti];  // eta (eta_1 with E3)
             const float A = F[0][r], Bm = F[1][r], Dr = F[2][r];
             const float sg = sigmoid_fast(A);
             const float sil = A * sg;
             const float eB = ev * Bm;
             o0[e] = M::from_f32(sil * eB);
-            o1[e] = M::from_f32((eB * Dr) * fmaf(sil, 1.f - sg, sg));  // silu'(A) = sg + silu(A) (1 - sg)
-            o2[e] = M::from_f32((ev * sil) * Dr);
+            const float e0B = E3 ? er[ti] * Bm : eB;
+            const float e2 = E3 ? er[2 * TT + ti] : ev;
+            o1[e] = M::from_f32((e0B * Dr) * fmaf(sil, 1.f - sg, sg));  // silu'(A) = sg + silu(A) (1 - sg)
+            o2[e] = M::from_f32((e2 * sil) * Dr);
           }
           dst[(0 * QS + q) * 64] = o0;
           dst[(1 * QS + q) * 64] = o1;
@@ -679,7 +705,7 @@ __device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int np
   auto put = [&](int buf, const Stage& stg, float ev) {
     OpT* b = tiles + buf * 2 * TILE;
     stg.template store_at<TL>(b, b + TILE, ctid);
-    if (ctid < TT) eta_s[buf * TT + ctid] = ev * scale;
+    if (ctid < NE * TT) eta_s[buf * NE * TT + ctid] = ev * scale;
   };
 
   f32x16 acc[3][CH];
@@ -749,10 +775,10 @@ __device__ __forceinline__ void grad_ws_body(const GradArgs& a, int nseg, int np
   }
 }
 
-template <class IoT, class OpT, int H, bool SCALE_MID>
+template <class IoT, class OpT, int H, bool SCALE_MID, bool E3 = false>
 __global__ void __launch_bounds__(512) grad_ws_kernel(GradArgs a, int nseg, int npairs) {
   extern __shared__ __align__(16) unsigned char smem[];
-  grad_ws_body<IoT, OpT, H, SCALE_MID>(a, nseg, npairs, blockIdx.x, smem);
+  grad_ws_body<IoT, OpT, H, SCALE_MID, E3>(a, nseg, npairs, blockIdx.x, smem);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -147,17 +147,19 @@ __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const floa
 }
 
 // power-of-two step-size scales of the gradient's token segments: for chunk c, pair p and
-// segment g, 2^-floor(log2(max eta)) over the segment's tokens (1 when the maximum is 0).
-// grid (P, nch), block 256; out [nch][P][S].
-__global__ void __launch_bounds__(256) lact_eta_scale_kernel(const float* eta, int64_t eta_pair_stride, int chunk,
-                                                            int seg_len, int S, float* out) {
+// segment g, 2^-floor(log2(max eta)) over the segment's tokens and the nrow step-size rows
+// (one, or one per matrix; 1 when the maximum is 0). grid (P, nch), block 256; out [nch][P][S].
+__global__ void __launch_bounds__(256) lact_eta_scale_kernel(const float* eta, int64_t eta_pair_stride,
+                                                            int64_t row_stride, int nrow, int chunk, int seg_len,
+                                                            int S, float* out) {
   __shared__ float red[16];
   const int pair = blockIdx.x, c = blockIdx.y, P = gridDim.x;
   const float* ep = eta + pair * eta_pair_stride;
   for (int g = 0; g < S; ++g) {
     const int t0 = c * chunk + g * seg_len, t1 = min(t0 + seg_len, (c + 1) * chunk);
     float mx = 0.f;
-    for (int t = t0 + threadIdx.x; t < t1; t += 256) mx = fmaxf(mx, ep[t]);
+    for (int e = 0; e < nrow; ++e)
+      for (int t = t0 + threadIdx.x; t < t1; t += 256) mx = fmaxf(mx, ep[e * row_stride + t]);
     mx = block_max(mx, red);
     if (threadIdx.x == 0) out[((int64_t)c * P + pair) * S + g] = mx > 0.f ? exp2f(-floorf(log2f(mx))) : 1.f;
   }
@@ -205,23 +207,41 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   constexpr bool SCALE = sizeof(OpT) == 2;
   constexpr bool RD = H <= 128;  // register-direct gradient kernel
   constexpr bool WS = std::is_same<OpT, _Float16>::value && (H == 64 || H == 128);  // its role-split form
-  auto gk = grad_kernel<IoT, OpT, H, false, SCALE>;
-  auto gkr = grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE>;
-  auto gkw = grad_ws_kernel<typename std::conditional<WS, IoT, bf16_t>::type, _Float16, (WS ? H : 128), true>;
+  // eta per matrix: the E3 instances of the gradient kernels
+  typedef typename std::conditional<WS, IoT, bf16_t>::type WIoT;
+  const bool e3 = p.eta_per_matrix != 0;
+  auto gk = e3 ? grad_kernel<IoT, OpT, H, false, SCALE, true> : grad_kernel<IoT, OpT, H, false, SCALE, false>;
+  auto gkr = e3 ? grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, true>
+                : grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, false>;
+  auto gkw = e3 ? grad_ws_kernel<WIoT, _Float16, (WS ? H : 128), true, true>
+                : grad_ws_kernel<WIoT, _Float16, (WS ? H : 128), true, false>;
   auto ak = apply_kernel<IoT, OpT, H>;
   // register-direct apply where its double-buffered weight blocks fit in LDS
   constexpr bool ARD = H <= 128 && apply_rd_lds_bytes<OpT, (H <= 128 ? H : 128)>() <= 160 * 1024;
   auto akr = apply_rd_kernel<IoT, OpT, (ARD ? H : 64)>;
-  constexpr int glds = WS   ? grad_ws_lds_bytes<_Float16, (WS ? H : 128)>()
-                       : RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false>()
-                            : grad_lds_bytes<OpT, H, false>();
+  constexpr int glds1 = WS   ? grad_ws_lds_bytes<_Float16, (WS ? H : 128)>()
+                        : RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false>()
+                             : grad_lds_bytes<OpT, H, false>();
+  constexpr int glds3 = WS   ? grad_ws_lds_bytes<_Float16, (WS ? H : 128), true>()
+                        : RD ? grad_rd_lds_bytes<OpT, (RD ? H : 128), false, true>()
+                             : grad_lds_bytes<OpT, H, false, true>();
+  constexpr int glds = glds3;  // the larger of the two
   constexpr int alds = ARD ? apply_rd_lds_bytes<OpT, (ARD ? H : 64)>() : apply_lds_bytes<OpT, H>();
   static_assert(glds <= 160 * 1024 && alds <= 160 * 1024, "LDS budget");
   static const hipError_t lds_ok = [&] {
-    hipError_t e = WS ? allow_lds(gkw, glds) : RD ? allow_lds(gkr, glds) : allow_lds(gk, glds);
+    hipError_t e = hipSuccess;
+    for (int v = 0; v < 2 && e == hipSuccess; ++v) {
+      auto k = v ? grad_ws_kernel<WIoT, _Float16, (WS ? H : 128), true, true>
+                 : grad_ws_kernel<WIoT, _Float16, (WS ? H : 128), true, false>;
+      auto kr = v ? grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, true>
+                  : grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, false>;
+      auto kg = v ? grad_kernel<IoT, OpT, H, false, SCALE, true> : grad_kernel<IoT, OpT, H, false, SCALE, false>;
+      e = WS ? allow_lds(k, glds) : RD ? allow_lds(kr, glds) : allow_lds(kg, glds);
+    }
     return e != hipSuccess ? e : (ARD ? allow_lds(akr, alds) : allow_lds(ak, alds));
   }();
   TTT_HIP(lds_ok);
+  const int gl = e3 ? glds3 : glds1;
 
   const int P = s.P, rh = s.rh;
   const int64_t n = (int64_t)rh * H;
@@ -263,14 +283,15 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   ga.V = V;
   ga.eta = eta;
   ga.tok_pair_stride = (int64_t)p.Nk * H;
-  ga.eta_pair_stride = p.Nk;
+  ga.eta_pair_stride = (int64_t)(e3 ? 3 : 1) * p.Nk;  // eta [pair][Nk] or [pair][3][Nk]
+  ga.eta_mat_stride = p.Nk;
   const int ntile = (p.chunk_kv + TT - 1) / TT;
   const int tiles_per_seg = (ntile + S - 1) / S;
   ga.seg_len = tiles_per_seg * TT;
   if (WS && nch > 0) {  // the role-split gradient kernel reads its segments' step-size scales
     LaunchTimer lt(K_LACT_INIT, st);
     hipLaunchKernelGGL(lact_eta_scale_kernel, dim3((unsigned)P, (unsigned)nch), dim3(256), 0, st, eta,
-                       (int64_t)p.Nk, p.chunk_kv, ga.seg_len, S, s.esc);
+                       ga.eta_pair_stride, (int64_t)p.Nk, e3 ? 3 : 1, p.chunk_kv, ga.seg_len, S, s.esc);
     TTT_HIP(hipGetLastError());
   }
   ga.W0T = sh;
@@ -375,11 +396,11 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
       {
         const unsigned grid = (unsigned)(rh / RB) * 8u * (unsigned)((P * S + 7) / 8);
         if constexpr (WS)
-          TTT_HIP(launch_k(K_LACT_GRAD, gkw, dim3(grid), dim3(512), glds, st, ga, S, P));
+          TTT_HIP(launch_k(K_LACT_GRAD, gkw, dim3(grid), dim3(512), gl, st, ga, S, P));
         else if constexpr (RD)
-          TTT_HIP(launch_k(K_LACT_GRAD, gkr, dim3(grid), dim3(256), glds, st, ga, S, P));
+          TTT_HIP(launch_k(K_LACT_GRAD, gkr, dim3(grid), dim3(256), gl, st, ga, S, P));
         else
-          TTT_HIP(launch_k(K_LACT_GRAD, gk, dim3(rh / RB, S, P), dim3(256), glds, st, ga));
+          TTT_HIP(launch_k(K_LACT_GRAD, gk, dim3(rh / RB, S, P), dim3(256), gl, st, ga));
       }
       if (fuse_ua && k == 0) {  // the chunk's apply reads the chunk-start weights (buffer rd)
         int nu = nupd;
@@ -435,7 +456,6 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   if (!(q.eps_norm >= 0.f && q.eps_norm <= FLT_MAX) || !(q.eps_ns >= 0.f && q.eps_ns <= FLT_MAX)) return TTT_ERR_ARG;
   if (q.inner_steps < 0 || q.inner_steps > 64) return TTT_ERR_ARG;
   if (q.eta_per_matrix != 0 && q.eta_per_matrix != 1) return TTT_ERR_ARG;
-  if (q.eta_per_matrix) return TTT_ERR_UNSUPPORTED;
   if (q.Nq % q.chunk_q || q.Nk % q.chunk_kv) return TTT_ERR_SHAPE;
   if (q.Nq / q.chunk_q != q.Nk / q.chunk_kv) return TTT_ERR_SHAPE;
   const int64_t rh64 = (int64_t)q.r * q.h;

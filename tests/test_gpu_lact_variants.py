@@ -1,13 +1,13 @@
 """GPU parity of the LaCT loop variants against the CPU oracle: per-chunk apply-only and reset
-flags, several inner steps per chunk, and both together. Same tolerances as the plain loop
+flags, several inner steps per chunk, both together, and one step-size row per matrix. Same tolerances as the plain loop
 (max-abs-relative 2e-2 in bf16 mode, 1e-4 in fp32 mode); every output is compared: O, the final
 fast weights and the final momentum."""
 import numpy as np
 import pytest
 
-from tests._helpers import BF16_TOL, FP32_TOL, announce, dev, lact_on_gpu, lact_oracle
+from tests._helpers import BF16_TOL, FP32_TOL, announce, dev, host, lact_on_gpu, lact_oracle
 from tests.test_gpu_lact import _compare
-from workloads import BF16, FP32, LactProblem, make_lact_inputs
+from workloads import BF16, FP32, LactProblem, make_lact_inputs, max_abs_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +89,54 @@ def test_lm_shape_with_document_boundaries(lib):
     pairs = [(1, 2), (2, 5), (3, 7)]
     ref = lact_oracle(p, x, pairs=pairs, chunk_flags=flags)
     _compare(gpu, ref, BF16_TOL, pairs=pairs, label="LM shape flags")
+
+
+ETA3_CASES = [
+    # (label, problem kwargs, seed): the role-split gradient kernel (h 64, 128), the register-direct
+    # one (h 32, fp32) and the LDS one (h 192)
+    ("bf16 AU muon mom h128", dict(h=128, N=1024, chunk=256, muon=True, momentum=0.9), 11),
+    ("bf16 UA muon h64", dict(h=64, N=512, chunk=128, muon=True, order=1), 12),
+    ("bf16 AU mom h32", dict(h=32, N=384, chunk=96, momentum=0.5), 13),
+    ("bf16 AU muon h192", dict(h=192, N=512, chunk=256, muon=True), 14),
+    ("fp32 AU muon mom h64", dict(h=64, N=256, chunk=64, muon=True, momentum=0.9, dtype=FP32), 15),
+]
+
+
+@pytest.mark.parametrize("label,kw,seed", ETA3_CASES, ids=[c[0] for c in ETA3_CASES])
+def test_eta_per_matrix(lib, label, kw, seed):
+    """One step-size row per matrix (eta [B,H,3,Nk]): rows of different scales, so that a row
+    applied to the wrong matrix shows."""
+    kw = dict(kw)
+    N, chunk = kw.pop("N"), kw.pop("chunk")
+    base = dict(B=2, H=2, h=64, r=2, Nq=N, Nk=N, chunk_q=chunk, chunk_kv=chunk, dtype=BF16, v_normalised=False)
+    base.update(kw)
+    p = LactProblem(**base)
+    x = make_lact_inputs(p, 980 + seed)
+    rng = np.random.default_rng(seed)
+    e = x["eta"]
+    x["eta"] = np.stack([0.25 * e, 2.0 * e, e * rng.uniform(0.5, 1.5, e.shape).astype(np.float32)], axis=2)
+    announce(f"lact eta per matrix {label}")
+    gpu = lact_on_gpu(lib, p, x)
+    ref = lact_oracle(p, x)
+    _compare(gpu, ref, BF16_TOL if p.dtype == BF16 else FP32_TOL, label=label)
+
+
+@pytest.mark.parametrize("h,dtype", [(128, BF16), (32, BF16), (192, BF16), (64, FP32)])
+def test_eta_per_matrix_with_equal_rows_matches_shared_eta(lib, h, dtype):
+    """Three equal rows give the shared-eta results. The per-matrix kernels do the same
+    arithmetic, but the compiler may round an epilogue product to fp16 once (a fused multiply
+    and convert) where the shared-eta build rounds it to fp32 first, so single intermediates can
+    differ by one fp16 unit. Bounds: the fp32 states within 1e-4 max-abs-relative, O (bf16)
+    within one bf16 unit (2^-8 of the largest output); a row applied to the wrong matrix moves
+    them by the rows' ratio, here x1."""
+    p = LactProblem(B=2, H=4, h=h, r=2, Nq=512, Nk=512, chunk_q=128, chunk_kv=128, dtype=dtype, muon=False,
+                    momentum=0.9, v_normalised=False)
+    announce(f"lact eta per matrix: equal rows vs shared h{h} dtype {dtype}")
+    x = make_lact_inputs(p, 990)
+    shared = lact_on_gpu(lib, p, x)
+    y = dict(x)
+    y["eta"] = np.stack([x["eta"]] * 3, axis=2)
+    per = lact_on_gpu(lib, p, y)
+    errs = {n: max_abs_rel(host(b), host(a)) for n, a, b in zip(("O", "W0", "W1", "W2", "M"), shared, per)}
+    print("equal rows vs shared:", errs, flush=True)
+    assert errs["O"] <= 2.0 ** -8 and all(errs[k] <= 1e-4 for k in ("W0", "W1", "W2", "M")), errs
