@@ -16,6 +16,16 @@ Reading of the transpose conventions (Eq. 2 writes "Z W_down", the chunk
 steps and Eq. 4 write "Z W_down^T" and "Vbar^T Z"): W_down is
 d_model x d_hidden, O = Z W_down^T, dW = eta Vbar^T Z -- three of the four
 formulas agree on this.
+
+* Section 3.2, Eq. 3 (the LM-aligned target): Vbar = Conv1D(X0) W_target with a
+  1-D convolution over the sequence and a d_model x d_model projection; taps
+  that put weight 1 on the next token and 0 elsewhere with W_target = I give
+  the next-token target. Reading: the convolution is depthwise (one weight per
+  channel and tap, the projection mixes the channels) and tap tau multiplies
+  X0_{t+tau} (tau = 0 is the token itself, tau = 1 the next one), with zeros
+  past the end of the sequence (section 3.4: the padding keeps the target
+  within the sequence); W_target is given in nn.Linear layout [out, in], so
+  Vbar_t = (sum_tau taps[tau] * X0_{t+tau}) W_target^T.
 """
 from __future__ import annotations
 
@@ -31,6 +41,17 @@ def silu(a):
 def gated_activation(Hs, W_gate, W_up):
     """Z = silu(H W_gate^T) * (H W_up^T)  (section 3.1)."""
     return silu(Hs @ W_gate.T) * (Hs @ W_up.T)
+
+
+def lm_aligned_target(X0, taps, W_target=None, dtype=np.float64):
+    """Vbar [N, d_model] of one sequence from the token embeddings X0 [N, d_model], the
+    depthwise taps [k, d_model] and W_target [d_model(out), d_model(in)] (None: identity)."""
+    X0, taps = np.asarray(X0, dtype=dtype), np.asarray(taps, dtype=dtype)
+    N = X0.shape[0]
+    conv = np.zeros_like(X0)
+    for tau in range(taps.shape[0]):
+        conv[:N - tau] += taps[tau][None, :] * X0[tau:]
+    return conv if W_target is None else conv @ np.asarray(W_target, dtype=dtype).T
 
 
 def inplace_sequence(Hs, W_gate, W_up, W_down, Vbar, eta, *, chunk: int, dtype=np.float64):

@@ -91,3 +91,52 @@ def test_sampled_evaluators_agree_with_the_full_recurrence():
         IP.output_rows(x["Hs"][0], x["W_gate"], x["W_up"], x["W_down"], x["Vbar"][0], p.eta,
                        chunk=p.chunk, rows=rows),
         o[rows], rtol=1e-11, atol=1e-13)
+
+
+# ---- the LM-aligned target (section 3.2, Eq. 3) ----
+
+def _target_inputs(seed, N=40, d=12, k=3):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((N, d)), rng.standard_normal((k, d)), rng.standard_normal((d, d)) / np.sqrt(d)
+
+
+def test_next_token_taps_with_identity_projection_are_the_next_token_shift():
+    X0, _, _ = _target_inputs(1)
+    taps = np.zeros((2, X0.shape[1]))
+    taps[1] = 1.0
+    V = IP.lm_aligned_target(X0, taps)
+    np.testing.assert_array_equal(V[:-1], X0[1:])
+    np.testing.assert_array_equal(V[-1], 0.0)
+    from workloads import InplaceProblem, make_inplace_inputs
+    p = InplaceProblem(B=1, N=64, d_model=16, d_hidden=32, chunk=16, eta=1e-3)
+    x = make_inplace_inputs(p, 3)
+    # the generator's next-token target is this case of the general target
+    np.testing.assert_array_equal(IP.lm_aligned_target(x["X0"][0], np.stack([np.zeros(16), np.ones(16)])),
+                                  x["Vbar"][0])
+
+
+def test_target_conv_equals_torch_depthwise_conv1d():
+    """The convolution is torch's grouped (depthwise) conv1d over the sequence, right-padded with
+    k - 1 zeros, with the taps in cross-correlation order; the projection is torch's linear."""
+    import torch
+    X0, taps, W = _target_inputs(2)
+    k, d = taps.shape
+    x = torch.tensor(X0.T[None], dtype=torch.float64)                   # [1, d, N]
+    x = torch.nn.functional.pad(x, (0, k - 1))
+    w = torch.tensor(taps.T[:, None, :], dtype=torch.float64)            # [d, 1, k]
+    conv = torch.nn.functional.conv1d(x, w, groups=d)[0].T               # [N, d]
+    ref = torch.nn.functional.linear(conv, torch.tensor(W, dtype=torch.float64)).numpy()
+    np.testing.assert_allclose(IP.lm_aligned_target(X0, taps, W), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_target_row_sees_only_its_window():
+    """Vbar_t depends on X0_t .. X0_{t+k-1} and on nothing else (the window the taps cover)."""
+    X0, taps, W = _target_inputs(3, k=4)
+    base = IP.lm_aligned_target(X0, taps, W)
+    for s in (0, 7, 20, 39):
+        Y = X0.copy()
+        Y[s] += 1.0
+        moved = np.any(IP.lm_aligned_target(Y, taps, W) != base, axis=1)
+        expect = np.zeros(X0.shape[0], bool)
+        expect[max(0, s - 3):s + 1] = True
+        np.testing.assert_array_equal(moved, expect)

@@ -129,6 +129,16 @@ def _eta_rows_swapped(orig):
     return f
 
 
+def _target_taps_backward(orig):
+    def f(X0, taps, W_target=None, dtype=np.float64):  # tap tau on X0_{t - tau} instead of X0_{t + tau}
+        X0, taps = np.asarray(X0, dtype=dtype), np.asarray(taps, dtype=dtype)
+        conv = np.zeros_like(X0)
+        for tau in range(taps.shape[0]):
+            conv[tau:] += taps[tau][None, :] * X0[:X0.shape[0] - tau]
+        return conv if W_target is None else conv @ np.asarray(W_target, dtype=dtype).T
+    return f
+
+
 def _identity_scaled(orig):
     return lambda X, W0=None, W2=None: X / np.sqrt(X.shape[1])  # an attention-style 1/sqrt(h)
 
@@ -165,6 +175,8 @@ MUTATIONS = [
      lambda: TLV.test_eta_per_matrix_write_is_each_rows_autograd_gradient()),
     ("identity kernel rescaled", LA, "phi_identity", _identity_scaled,
      lambda: TLA.test_identity_scan_equals_recurrent_linear_fast_weight(0, 0.0, 8)),
+    ("target taps on past tokens", IP, "lm_aligned_target", _target_taps_backward,
+     lambda: TI.test_next_token_taps_with_identity_projection_are_the_next_token_shift()),
     ("In-Place update before apply", IP, "inplace_sequence", _update_before_apply,
      lambda: TI.test_first_chunk_is_the_plain_mlp()),
 ]

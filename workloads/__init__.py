@@ -191,7 +191,7 @@ def make_inplace_inputs(p: InplaceProblem, seed: int, *, eta: Optional[float] = 
 
     Returns float32 arrays (bf16-representable for bf16 problems):
       Hs [B,N,d_model], W_gate/W_up [d_hidden,d_model], W_down [d_model,d_hidden],
-      Vbar [B,N,d_model] = next-token shift of X0 with a zero last row.
+      Vbar [B,N,d_model] = next-token shift of X0 with a zero last row, X0 [B,N,d_model].
     The next-token target is the causal Conv1D with taps (0, 1) and an identity
     projection ("In-Place Test-Time Training" notes, section 3.2 / Eq. 3).
     """
@@ -202,11 +202,11 @@ def make_inplace_inputs(p: InplaceProblem, seed: int, *, eta: Optional[float] = 
     Wu = _normal(rng, (dh, dm), 1.0 / math.sqrt(dm))
     Wd = _normal(rng, (dm, dh), 1.0 / math.sqrt(dh))
     X0 = _normal(rng, (B, N, dm))
+    if p.dtype == BF16:
+        Hs, Wg, Wu, Wd, X0 = (bf16_round(a) for a in (Hs, Wg, Wu, Wd, X0))
     Vbar = np.zeros_like(X0)
     Vbar[:, :-1] = X0[:, 1:]
-    if p.dtype == BF16:
-        Hs, Wg, Wu, Wd, Vbar = (bf16_round(a) for a in (Hs, Wg, Wu, Wd, Vbar))
-    return dict(Hs=Hs, W_gate=Wg, W_up=Wu, W_down=Wd, Vbar=Vbar,
+    return dict(Hs=Hs, W_gate=Wg, W_up=Wu, W_down=Wd, Vbar=Vbar, X0=X0,
                 eta=np.float32(p.eta if eta is None else eta))
 
 
