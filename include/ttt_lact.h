@@ -265,12 +265,26 @@ ttt_status ttt_linattn_forward_noalloc(const ttt_linattn_params* p,
  * Shape rules: N % chunk == 0; d_model and d_hidden multiples of 256; chunk a multiple of 128.
  * Only TTT_BF16 is implemented (TTT_FP32 gives TTT_ERR_UNSUPPORTED). Every launch goes to
  * `stream`; the next chunk's Z is formed in the same launch as the current chunk's apply.
+ * LM-aligned target (section 3.2 / Eq. 3: Vbar = Conv1D(X0) W_target): when X0 is set the
+ * library builds Vbar itself and the Vbar argument must be NULL (else TTT_ERR_ARG). Per sequence,
+ *   Vbar_t = (sum_{tau < conv_k} conv_taps[tau] * X0_{t+tau}) W_target^T
+ * a depthwise convolution over the sequence (tap tau weights the token tau positions ahead,
+ * tau = 0 the token itself; rows past the end read zero) followed by the projection. X0
+ * [B, N, d_model] bf16; conv_taps [conv_k, d_model] float32, 1 <= conv_k <= 16 (else
+ * TTT_ERR_ARG); W_target [d_model(out), d_model(in)] bf16 in nn.Linear layout, or NULL for the
+ * identity. conv_k = 2 with taps (0, 1) and no W_target is the next-token target. The
+ * convolution accumulates in float32 and rounds Vbar to bf16, as a given Vbar would be.
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t B, N, d_model, d_hidden, chunk;
   float eta;
   int32_t dtype;
   int64_t wdown_batch_stride;
+  /* LM-aligned target; a zero-initialised tail means Vbar is given */
+  const void* X0;          /* [B, N, d_model] bf16 or NULL */
+  const float* conv_taps;  /* [conv_k, d_model] float32 */
+  const void* W_target;    /* [d_model, d_model] bf16 (nn.Linear layout) or NULL: identity */
+  int32_t conv_k;
 } ttt_inplace_params;
 
 ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p,

@@ -56,7 +56,9 @@ class LinattnParams(ctypes.Structure):
 class InplaceParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_hidden", ctypes.c_int32), ("chunk", ctypes.c_int32), ("eta", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("wdown_batch_stride", ctypes.c_int64)]
+                ("dtype", ctypes.c_int32), ("wdown_batch_stride", ctypes.c_int64),
+                ("X0", ctypes.c_void_p), ("conv_taps", ctypes.c_void_p), ("W_target", ctypes.c_void_p),
+                ("conv_k", ctypes.c_int32)]
 
 
 _lib = None
@@ -322,23 +324,39 @@ def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want
 
 
 def inplace_down_forward(Hs, W_gate, W_up, W_down, Vbar, *, chunk: int, eta: float,
-                         want_state: bool = True, stream=None):
+                         X0=None, conv_taps=None, W_target=None, want_state: bool = True, stream=None):
     """In-Place TTT down-projection update. Hs/Vbar [B,N,d_model] bf16, W_gate/W_up
-    [d_hidden,d_model] bf16, W_down [(B,)d_model,d_hidden] fp32. Returns (O, W_down_out)."""
+    [d_hidden,d_model] bf16, W_down [(B,)d_model,d_hidden] fp32. Returns (O, W_down_out).
+    LM-aligned target: pass Vbar=None with X0 [B,N,d_model] bf16, conv_taps [k,d_model] fp32
+    (tap tau weights the token tau positions ahead) and optionally W_target [d_model,d_model] bf16
+    (nn.Linear layout); the library then builds Vbar = Conv1D(X0) W_target^T."""
     torch = _torch()
     lib = load()
     B, N, dm = Hs.shape
     dh = W_gate.shape[0]
     dev = Hs.device
-    for t, n in ((Hs, "Hs"), (W_gate, "W_gate"), (W_up, "W_up"), (Vbar, "Vbar")):
+    for t, n in ((Hs, "Hs"), (W_gate, "W_gate"), (W_up, "W_up"), (Vbar, "Vbar"), (X0, "X0"),
+                 (W_target, "W_target")):
         _check(t, n, torch.bfloat16, dev)
+    _check(conv_taps, "conv_taps", torch.float32, dev)
     _check(W_down, "W_down", torch.float32, dev)
     per_seq = W_down.dim() == 3
-    if W_gate.shape != (dh, dm) or W_up.shape != (dh, dm) or Vbar.shape != Hs.shape:
+    if W_gate.shape != (dh, dm) or W_up.shape != (dh, dm):
         raise ValueError("shape mismatch")
+    if (Vbar is None) == (X0 is None):
+        raise ValueError("give either Vbar or X0 (with conv_taps) for the target")
+    if Vbar is not None and Vbar.shape != Hs.shape:
+        raise ValueError("Vbar must be [B,N,d_model]")
+    if X0 is not None:
+        if X0.shape != Hs.shape or conv_taps is None or conv_taps.dim() != 2 or conv_taps.shape[1] != dm \
+                or not (1 <= conv_taps.shape[0] <= 16):
+            raise ValueError("X0 must be [B,N,d_model] and conv_taps [k,d_model] with 1 <= k <= 16")
+        if W_target is not None and tuple(W_target.shape) != (dm, dm):
+            raise ValueError("W_target must be [d_model,d_model]")
     if W_down.shape[-2:] != (dm, dh):
         raise ValueError("W_down must be [(B,)d_model,d_hidden]")
-    p = InplaceParams(B, N, dm, dh, chunk, eta, BF16, dm * dh if per_seq else 0)
+    p = InplaceParams(B, N, dm, dh, chunk, eta, BF16, dm * dh if per_seq else 0, _ptr(X0), _ptr(conv_taps),
+                      _ptr(W_target), 0 if conv_taps is None else conv_taps.shape[0])
     O = torch.empty_like(Hs)
     Wout = torch.empty((B, dm, dh), dtype=torch.float32, device=dev) if want_state else None
     base = [ctypes.byref(p), _ptr(Hs), _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Vbar), _ptr(O), _ptr(Wout)]

@@ -510,6 +510,35 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(const __bf16* src, 
   }
 }
 
+// LM-aligned target of one sequence: C[t][c] = sum_{tau < k} taps[tau][c] * X0[t + tau][c] (zero
+// past row N - 1), accumulated in float32 and rounded to bf16. TRANS writes C^T [dm][N] (the
+// layout the update reads Vbar in), else C [N][dm]. grid (dm / 64, N / 64), block 256: a 64 x 64
+// output tile from a (64 + k - 1) x 64 window of X0 staged in LDS.
+template <bool TRANS>
+__global__ void __launch_bounds__(256) target_conv_kernel(const __bf16* __restrict__ X0, const float* __restrict__ taps,
+                                                         int k, int N, int dm, __bf16* __restrict__ out) {
+  __shared__ float win[64 + 15][65];
+  __shared__ float tp[16][64];
+  const int c0 = blockIdx.x * 64, t0 = blockIdx.y * 64, tid = threadIdx.x;
+  for (int i = tid; i < (64 + k - 1) * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    win[r][c] = t0 + r < N ? static_cast<float>(X0[(int64_t)(t0 + r) * dm + c0 + c]) : 0.f;
+  }
+  for (int i = tid; i < k * 64; i += 256) tp[i / 64][i % 64] = taps[(int64_t)(i / 64) * dm + c0 + i % 64];
+  __syncthreads();
+  for (int i = tid; i < 64 * 64; i += 256) {
+    // TRANS: consecutive threads take consecutive tokens of one channel (coalesced along N)
+    const int r = TRANS ? i % 64 : i / 64, c = TRANS ? i / 64 : i % 64;
+    float acc = 0.f;
+    for (int tau = 0; tau < k; ++tau) acc = fmaf(tp[tau][c], win[r + tau][c], acc);
+    const __bf16 v = static_cast<__bf16>(acc);
+    if (TRANS)
+      out[(int64_t)(c0 + c) * N + t0 + r] = v;
+    else
+      out[(int64_t)(t0 + r) * dm + c0 + c] = v;
+  }
+}
+
 // One TN GEMM: the large-tile kernel where the shape fits its tile, else the 128 x 128 kernel.
 // EPI_STORE with ksplit > 1 goes through fp32 partials in `part` and the split sum.
 template <int EPI>
@@ -554,8 +583,10 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
   if (q.d_model % 256 || q.d_hidden % 256 || q.chunk % 128) return TTT_ERR_SHAPE;
   const int64_t nW = (int64_t)q.d_model * q.d_hidden;
   if (q.wdown_batch_stride != 0 && q.wdown_batch_stride != nW) return TTT_ERR_SHAPE;
+  const bool target = q.X0 != nullptr;  // the LM-aligned target is built here
+  if (target && (Vbar || !q.conv_taps || q.conv_k < 1 || q.conv_k > 16)) return TTT_ERR_ARG;
   if (q.B > 0 && !W_down) return TTT_ERR_ARG;
-  if (q.B > 0 && q.N > 0 && (!Hs || !W_gate || !W_up || !Vbar || !O)) return TTT_ERR_ARG;
+  if (q.B > 0 && q.N > 0 && (!Hs || !W_gate || !W_up || (!Vbar && !target) || !O)) return TTT_ERR_ARG;
   // GEMM shapes of one chunk: Z [C x d_H] (K d), apply [C x d] (K d_H), update [d x d_H] (K C)
   gemm::Args za{}, aa{}, ua{};
   za.M = q.chunk, za.N = q.d_hidden, za.K = q.d_model;
@@ -570,6 +601,7 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
   const size_t oPart = plan.add(ks_apply > 1 ? (size_t)ks_apply * q.chunk * q.d_model * 4 : 0);
   const size_t oSh = plan.add((size_t)nW * 2);
   const size_t oVt = plan.add((size_t)q.d_model * q.N * 2);
+  const size_t oC = plan.add(target && q.W_target ? (size_t)q.N * q.d_model * 2 : 0);  // Conv1D(X0) before W_target
   // Z and Z^T double-buffered: chunk i + 1's Z is produced while chunk i is applied and written
   const size_t oZ = plan.add((size_t)2 * q.chunk * q.d_hidden * 2);
   const size_t oZt = plan.add((size_t)2 * q.chunk * q.d_hidden * 2);
@@ -619,9 +651,42 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       LaunchTimer lt(K_INP_PREP, st);
       hipLaunchKernelGGL(to_bf16_kernel, dim3(2048), dim3(256), 0, st, Wf, Wsh, nW);
       TTT_HIP(hipGetLastError());
-      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(q.d_model / 64, q.N / 64), dim3(256), 0, st,
-                         Vb + (int64_t)b * q.N * q.d_model, Vt, q.N, q.d_model);
-      TTT_HIP(hipGetLastError());
+      if (!target) {
+        hipLaunchKernelGGL(transpose_bf16_kernel, dim3(q.d_model / 64, q.N / 64), dim3(256), 0, st,
+                           Vb + (int64_t)b * q.N * q.d_model, Vt, q.N, q.d_model);
+        TTT_HIP(hipGetLastError());
+      }
+    }
+    if (target) {
+      // Vbar^T [d_model][N]: the convolution written transposed, or its row-major result C
+      // through Vbar^T = W_target C^T (a TN product: A = W_target [out][in], B = C [N][in])
+      const __bf16* X0b = static_cast<const __bf16*>(q.X0) + (int64_t)b * q.N * q.d_model;
+      const dim3 cgrid((unsigned)(q.d_model / 64), (unsigned)(q.N / 64));
+      if (!q.W_target) {
+        LaunchTimer lt(K_INP_PREP, st);
+        hipLaunchKernelGGL(target_conv_kernel<true>, cgrid, dim3(256), 0, st, X0b, q.conv_taps, q.conv_k, q.N,
+                           q.d_model, Vt);
+        TTT_HIP(hipGetLastError());
+      } else {
+        __bf16* Cb = reinterpret_cast<__bf16*>(ws + oC);
+        {
+          LaunchTimer lt(K_INP_PREP, st);
+          hipLaunchKernelGGL(target_conv_kernel<false>, cgrid, dim3(256), 0, st, X0b, q.conv_taps, q.conv_k, q.N,
+                             q.d_model, Cb);
+          TTT_HIP(hipGetLastError());
+        }
+        Args t{};
+        t.A = static_cast<const __bf16*>(q.W_target);
+        t.lda = q.d_model;
+        t.B0 = Cb;
+        t.ldb = q.d_model;
+        t.M = q.d_model;
+        t.N = q.N;
+        t.K = q.d_model;
+        t.C = Vt;
+        t.ldc = q.N;
+        TTT_HIP(run_gemm<EPI_STORE>(K_INP_PREP, t, 1, part, st));
+      }
     }
     auto zargs = [&](int i) {
       Args z{};

@@ -177,15 +177,28 @@ def test_linattn_identity_feature_map_validation(lib):
     assert "single-pass" in ttt.last_error()
 
 
-def _inp(lib, **kw):
+def _inp(lib, Vbar=FAKE, **kw):
     base = dict(B=1, N=32768, d_model=4096, d_hidden=14336, chunk=1024, eta=1e-3, dtype=ttt.BF16,
                 wdown_batch_stride=0)
     base.update(kw)
     p = ttt.InplaceParams(**base)
     sz = ctypes.c_size_t(0)
-    st = lib.ttt_inplace_down_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+    st = lib.ttt_inplace_down_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, Vbar, FAKE, None, None,
                                       ctypes.byref(sz), None)
     return st, sz.value
+
+
+def test_inplace_lm_aligned_target_fields(lib):
+    assert ctypes.sizeof(ttt.InplaceParams) == 72
+    st, given = _inp(lib)
+    tgt = dict(Vbar=None, X0=0x3000, conv_taps=0x4000, conv_k=2)
+    assert _inp(lib, **tgt) == (ttt.TTT_OK, given)  # the convolution is written straight into Vbar^T
+    st, proj = _inp(lib, **tgt, W_target=0x5000)
+    assert st == ttt.TTT_OK and proj == given + 32768 * 4096 * 2  # Conv1D(X0) before the projection
+    assert _inp(lib, **{**tgt, "Vbar": FAKE})[0] == ttt.TTT_ERR_ARG  # target given twice
+    for bad in (dict(conv_k=0), dict(conv_k=17), dict(conv_taps=None)):
+        assert _inp(lib, **{**tgt, **bad})[0] == ttt.TTT_ERR_ARG, bad
+    assert _inp(lib, Vbar=None)[0] == ttt.TTT_ERR_ARG  # no target at all
 
 
 def test_inplace_query_and_validation(lib):

@@ -59,3 +59,54 @@ def test_config4_full_size_sampled(lib):
     eo = max_abs_rel(host(O[0][rows]), refO)
     print(f"config4 sampled: W cols {ew:.2e}, O rows {eo:.2e}")
     assert ew <= BF16_TOL and eo <= BF16_TOL
+
+
+# ---- the LM-aligned target built on the device (section 3.2, Eq. 3) ----
+
+def _gpu_target(lib, p, x, taps, W_target=None):
+    import torch
+    return lib.inplace_down_forward(dev(x["Hs"], torch.bfloat16), dev(x["W_gate"], torch.bfloat16),
+                                    dev(x["W_up"], torch.bfloat16), dev(x["W_down"], torch.float32), None,
+                                    chunk=p.chunk, eta=float(x["eta"]), X0=dev(x["X0"], torch.bfloat16),
+                                    conv_taps=dev(taps, torch.float32),
+                                    W_target=None if W_target is None else dev(W_target, torch.bfloat16))
+
+
+def test_next_token_target_is_bitwise_the_given_shift(lib):
+    """Taps (0, 1) and no projection: the device builds exactly the next-token shift, so the call
+    equals the one that is handed the shifted embeddings, bit for bit."""
+    import torch
+    p = InplaceProblem(B=2, N=512, d_model=256, d_hidden=512, chunk=128, eta=1e-2)
+    announce(f"inplace next-token target on the device {p}")
+    x = make_inplace_inputs(p, 610)
+    taps = np.stack([np.zeros(p.d_model, np.float32), np.ones(p.d_model, np.float32)])
+    O1, W1 = _gpu(lib, p, x)
+    O2, W2 = _gpu_target(lib, p, x, taps)
+    assert torch.equal(O1, O2) and torch.equal(W1, W2)
+
+
+@pytest.mark.parametrize("kw,k,proj", [
+    (dict(B=2, N=512, d_model=256, d_hidden=512, chunk=128, eta=5e-2), 3, False),
+    (dict(B=1, N=1024, d_model=512, d_hidden=768, chunk=256, eta=5e-2), 4, True),
+    # projection product 1024 x 2048 over K = 1024: the large-tile kernel
+    (dict(B=1, N=2048, d_model=1024, d_hidden=2048, chunk=256, eta=2e-2), 2, True),
+])
+def test_general_target(lib, kw, k, proj):
+    """General taps and a projection, against the oracle's target and recurrence. The step size is
+    raised so that the writes carry weight in the outputs."""
+    from oracle import inplace as IP
+    from workloads import bf16_round
+    p = InplaceProblem(**kw)
+    announce(f"inplace LM-aligned target k={k} projection={proj} {p}")
+    x = make_inplace_inputs(p, 620 + k)
+    rng = np.random.default_rng(k)
+    taps = rng.uniform(-1.0, 1.0, (k, p.d_model)).astype(np.float32)
+    W_target = bf16_round((rng.standard_normal((p.d_model, p.d_model)) / np.sqrt(p.d_model)).astype(np.float32)) \
+        if proj else None
+    O, W = _gpu_target(lib, p, x, taps, W_target)
+    Vbar = np.stack([IP.lm_aligned_target(x["X0"][b], taps, W_target) for b in range(p.B)])
+    ref = IP.inplace_forward(x["Hs"], x["W_gate"], x["W_up"], x["W_down"], Vbar, float(x["eta"]), chunk=p.chunk)
+    eo, ew = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(W), ref["W_down"])
+    print(f"inplace target O={eo:.2e} W={ew:.2e}", flush=True)
+    assert eo <= BF16_TOL and ew <= BF16_TOL
+    assert max_abs_rel(ref["W_down"][0], x["W_down"]) > 1e-2  # the writes are visible
