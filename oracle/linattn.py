@@ -137,3 +137,93 @@ def linattn_masked_quadratic(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int
         mask = np.array([[momentum_weight(a, b, momentum, order) for b in cs] for a in ct])
     pq, pk = feat(Q, W0, W2), feat(K, W0, W2)
     return pq @ W1 + (mask * (pq @ pk.T)) @ (eta[:, None] * V)
+
+
+# ---- backward of the scan form (the gradients the parallel form trains through) ----
+# The forward above is O_c = phi(Q_c) S_c with S_c = W1 + sum_j w(c, j) dS_j,
+# dS_j = phi(K_j)^T diag(eta_j) V_j and w = momentum_weight. Given dL/dO:
+#   G_c = phi(Q_c)^T dO_c                       (the gradient reaching S_c)
+#   dW1 = sum_c G_c
+#   R_j = sum_c w(c, j) G_c                     (the gradient reaching dS_j)
+#   dphi(Q_c) = dO_c S_c^T
+#   dphi(K_j) = diag(eta_j) V_j R_j^T,   d(eta V)_j = phi(K_j) R_j
+#   dV_t = eta_t d(eta V)_t,   deta_t = <d(eta V)_t, V_t>
+# and through phi(X) = silu(A) * Bm with A = X W0, Bm = X W2:
+#   dA = dphi * Bm * silu'(A),  dBm = dphi * silu(A),  dX = dA W0^T + dBm W2^T,
+#   dW0 = sum X^T dA,  dW2 = sum X^T dBm  (over the queries and the keys).
+
+def _silu_parts(A):
+    s = 0.5 * (1.0 + np.tanh(0.5 * A))
+    return A * s, s * (1.0 + A * (1.0 - s))  # silu(A), silu'(A)
+
+
+def linattn_backward_pair(Q, K, V, eta, W0, W1, W2, dO, *, chunk: int, order: int = APPLY_THEN_UPDATE,
+                          momentum: float = 0.0, feature_map: str = "swiglu", dtype=np.float64):
+    """Gradients of sum(O * dO) for one pair: dict(dQ, dK, dV, deta, dW0, dW1, dW2); dW0/dW2 are
+    None for the identity map."""
+    Q, K, V, eta, W0, W1, W2, dO = (_as(a, dtype) for a in (Q, K, V, eta, W0, W1, W2, dO))
+    ident = feature_map == "identity"
+    n = K.shape[0] // chunk
+    sl = [slice(c * chunk, (c + 1) * chunk) for c in range(n)]
+
+    def feat(X):
+        if ident:
+            return X, None, None
+        A, Bm = X @ W0, X @ W2
+        sil, dsil = _silu_parts(A)
+        return sil * Bm, (A, Bm, sil, dsil), X
+
+    def feat_back(dphi, cache, X):
+        if ident:
+            return dphi, None, None
+        A, Bm, sil, dsil = cache
+        dA, dBm = dphi * Bm * dsil, dphi * sil
+        return dA @ W0.T + dBm @ W2.T, X.T @ dA, X.T @ dBm
+
+    fq = [feat(Q[s]) for s in sl]
+    fk = [feat(K[s]) for s in sl]
+    dS = [fk[c][0].T @ (eta[sl[c], None] * V[sl[c]]) for c in range(n)]
+    S = [W1 + sum((momentum_weight(c, j, momentum, order) * dS[j] for j in range(n)), np.zeros_like(W1))
+         for c in range(n)]
+    G = [fq[c][0].T @ dO[sl[c]] for c in range(n)]
+    R = [sum((momentum_weight(c, j, momentum, order) * G[c] for c in range(n)), np.zeros_like(W1)) for j in range(n)]
+    out = dict(dQ=np.zeros_like(Q), dK=np.zeros_like(K), dV=np.zeros_like(V), deta=np.zeros_like(eta),
+               dW1=sum(G, np.zeros_like(W1)),
+               dW0=None if ident else np.zeros_like(W0), dW2=None if ident else np.zeros_like(W2))
+    for c in range(n):
+        dX, g0, g2 = feat_back(dO[sl[c]] @ S[c].T, fq[c][1], fq[c][2])
+        out["dQ"][sl[c]] = dX
+        dEV = fk[c][0] @ R[c]
+        out["dV"][sl[c]] = eta[sl[c], None] * dEV
+        out["deta"][sl[c]] = np.sum(dEV * V[sl[c]], axis=1)
+        dX, h0, h2 = feat_back((eta[sl[c], None] * V[sl[c]]) @ R[c].T, fk[c][1], fk[c][2])
+        out["dK"][sl[c]] = dX
+        if not ident:
+            out["dW0"] += g0 + h0
+            out["dW2"] += g2 + h2
+    return out
+
+
+def linattn_backward(Q, K, V, eta, W0, W1, W2, dO, *, chunk: int, order: int = APPLY_THEN_UPDATE,
+                     momentum: float = 0.0, feature_map: str = "swiglu", dtype=np.float64) -> Dict[str, np.ndarray]:
+    """All pairs: dQ, dK, dV [B,H,N,h], deta [B,H,N]; the weight gradients in the weights' own
+    layout, summed over the batch when the weights are shared ([H,...]) and per sequence when
+    they are [B,H,...]."""
+    B, H, N, h = Q.shape
+    per_seq = np.ndim(W1) == 4
+    res = {k: [] for k in ("dQ", "dK", "dV", "deta", "dW0", "dW1", "dW2")}
+    for b in range(B):
+        for hd in range(H):
+            w0, w1, w2 = ((None if w is None else (w[b, hd] if per_seq else w[hd])) for w in (W0, W1, W2))
+            r = linattn_backward_pair(Q[b, hd], K[b, hd], V[b, hd], eta[b, hd], w0, w1, w2, dO[b, hd], chunk=chunk,
+                                      order=order, momentum=momentum, feature_map=feature_map, dtype=dtype)
+            for k in res:
+                res[k].append(r[k])
+    out = {k: np.stack(res[k]).reshape((B, H) + res[k][0].shape) for k in ("dQ", "dK", "dV", "deta")}
+    for k in ("dW0", "dW1", "dW2"):
+        if res[k][0] is None:
+            out[k] = None
+            continue
+        g = np.stack(res[k]).reshape((B, H) + res[k][0].shape)
+        out[k] = g if per_seq else g.sum(axis=0)
+    return out

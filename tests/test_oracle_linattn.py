@@ -192,3 +192,70 @@ def test_identity_token_chunks_update_then_apply_is_causal_linear_attention():
         np.testing.assert_allclose(out["O"][0, 0, t], Q[t] @ state, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(out["S"][0, 0], state, rtol=1e-12, atol=1e-13)
     assert out["S"].shape == (1, 1, 16, 16)
+
+
+# ---- backward of the scan form, pinned against torch autograd ----
+
+def _torch_scan_forward(Q, K, V, eta, W0, W1, W2, chunk, order, momentum, ident):
+    """The scan form written with torch ops and the heavy-ball recurrence (m <- alpha m + dS_c,
+    S <- S + m), independent of the oracle's coefficient form."""
+    import torch
+    feat = (lambda X: X) if ident else (lambda X: torch.nn.functional.silu(X @ W0) * (X @ W2))
+    S = W1.clone()
+    m = torch.zeros_like(W1)
+    outs = []
+    for c in range(K.shape[0] // chunk):
+        s = slice(c * chunk, (c + 1) * chunk)
+        dS = feat(K[s]).T @ (eta[s, None] * V[s])
+        if order == 1:
+            m = momentum * m + dS
+            S = S + m
+        outs.append(feat(Q[s]) @ S)
+        if order == 0:
+            m = momentum * m + dS
+            S = S + m
+    return torch.cat(outs)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("momentum", [0.0, 0.7])
+@pytest.mark.parametrize("ident", [False, True])
+def test_backward_equals_torch_autograd(order, momentum, ident):
+    import torch
+    h, r = 8, (1 if ident else 2)
+    p = LactProblem(B=1, H=1, h=h, r=r, Nq=48, Nk=48, chunk_q=12, chunk_kv=12)
+    x = make_lact_inputs(p, 31)
+    x["eta"] = x["eta"] * 30
+    dO = np.random.default_rng(32).standard_normal((48, h))
+    t = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    args = [t(x[k][0, 0]) for k in ("Q", "K", "V", "eta")] + [t(x[k][0]) for k in ("W0", "W1", "W2")]
+    O = _torch_scan_forward(*args, 12, order, momentum, ident)
+    grads = torch.autograd.grad((O * torch.tensor(dO)).sum(), args, allow_unused=True)
+    ref = dict(zip(("dQ", "dK", "dV", "deta", "dW0", "dW1", "dW2"), grads))
+    w0, w2 = (None, None) if ident else (x["W0"][0], x["W2"][0])
+    got = LA.linattn_backward_pair(x["Q"][0, 0], x["K"][0, 0], x["V"][0, 0], x["eta"][0, 0], w0, x["W1"][0], w2, dO,
+                                   chunk=12, order=order, momentum=momentum,
+                                   feature_map="identity" if ident else "swiglu")
+    for k, v in ref.items():
+        if ident and k in ("dW0", "dW2"):
+            assert got[k] is None
+            continue
+        np.testing.assert_allclose(got[k], v.numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
+
+
+def test_backward_batch_layouts():
+    """Shared weights: the weight gradients are summed over the batch; per-sequence weights keep
+    one gradient per sequence, equal to the single-pair gradients."""
+    p = LactProblem(B=2, H=2, h=8, r=2, Nq=24, Nk=24, chunk_q=8, chunk_kv=8)
+    x = make_lact_inputs(p, 33)
+    dO = np.random.default_rng(34).standard_normal((2, 2, 24, 8))
+    shared = LA.linattn_backward(x["Q"], x["K"], x["V"], x["eta"], x["W0"], x["W1"], x["W2"], dO, chunk=8)
+    per = {k: np.stack([x[k]] * 2) for k in ("W0", "W1", "W2")}
+    ps = LA.linattn_backward(x["Q"], x["K"], x["V"], x["eta"], per["W0"], per["W1"], per["W2"], dO, chunk=8)
+    for k in ("dW0", "dW1", "dW2"):
+        np.testing.assert_allclose(shared[k], ps[k].sum(axis=0), rtol=1e-12, atol=1e-14)
+        one = LA.linattn_backward_pair(x["Q"][1, 0], x["K"][1, 0], x["V"][1, 0], x["eta"][1, 0], x["W0"][0],
+                                       x["W1"][0], x["W2"][0], dO[1, 0], chunk=8)
+        np.testing.assert_allclose(ps[k][1, 0], one[k], rtol=1e-12, atol=1e-14)
+    for k in ("dQ", "dK", "dV", "deta"):
+        assert np.array_equal(shared[k], ps[k])

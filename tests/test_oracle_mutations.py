@@ -139,6 +139,13 @@ def _target_taps_backward(orig):
     return f
 
 
+def _backward_silu_prime_dropped(orig):
+    def f(A):
+        sil, _ = orig(A)
+        return sil, 0.5 * (1.0 + np.tanh(0.5 * A))  # silu' -> sigmoid
+    return f
+
+
 def _identity_scaled(orig):
     return lambda X, W0=None, W2=None: X / np.sqrt(X.shape[1])  # an attention-style 1/sqrt(h)
 
@@ -173,6 +180,8 @@ MUTATIONS = [
      lambda: TLV.test_inner_steps_equal_repeated_chunks(0, 2)),
     ("eta rows of W0 and W2 swapped", L, "lact_pair", _eta_rows_swapped,
      lambda: TLV.test_eta_per_matrix_write_is_each_rows_autograd_gradient()),
+    ("backward silu' term dropped", LA, "_silu_parts", _backward_silu_prime_dropped,
+     lambda: TLA.test_backward_equals_torch_autograd(0, 0.0, False)),
     ("identity kernel rescaled", LA, "phi_identity", _identity_scaled,
      lambda: TLA.test_identity_scan_equals_recurrent_linear_fast_weight(0, 0.0, 8)),
     ("target taps on past tokens", IP, "lm_aligned_target", _target_taps_backward,
