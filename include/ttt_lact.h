@@ -226,6 +226,36 @@ ttt_status ttt_linattn_forward(const ttt_linattn_params* p,
                                void* workspace, size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * ttt_linattn_backward
+ *
+ * Defined by: the same pages as ttt_linattn_forward (the parallel form is what the model trains
+ * through: KV-binding summary page, "Experimental results", end-to-end training with the
+ * parallel form; press article, section 4). Gradients of sum(O * dO) with respect to every
+ * input of ttt_linattn_forward, for the same parameters:
+ *   G_c = phi(Q_c)^T dO_c,  R_j = sum_c w(c, j) G_c (w: the forward's coefficient of chunk j's
+ *   write in the state chunk c reads), dW1 = sum_c G_c;
+ *   query side: dphi(Q_c) = dO_c S_c^T;  key side: dphi(K_j) = diag(eta_j) V_j R_j^T,
+ *   d(eta V)_j = phi(K_j) R_j, dV = eta d(eta V), deta_t = <d(eta V)_t, V_t>;
+ *   through phi: dA = dphi * Bm * silu'(A), dBm = dphi * silu(A) (A = X W0, Bm = X W2),
+ *   dX = dA W0^T + dBm W2^T, dW0 = sum X^T dA, dW2 = sum X^T dBm over queries and keys.
+ * Arguments: Q, K, V, eta, W0, W2, W1 as for ttt_linattn_forward; dO [B, H, N, h] bf16 (the
+ * gradient of the output); dQ, dK, dV [B, H, N, h] bf16; deta [B, H, N] float32; dW0, dW2
+ * [H, h, rh] and dW1 [H, rh, h] float32, summed over the batch when the weights are shared
+ * (w_batch_stride 0), else [B, H, ...] per sequence (dW0/dW2/dW1 nullable: not written).
+ * Built for TTT_BF16 with the SwiGLU map and (h, r*h) in {(32, 64), (32, 128), (64, 128)}, any
+ * order and momentum; other combinations return TTT_ERR_UNSUPPORTED. fp32 accumulation, fp16
+ * MFMA operands (the fp16 range note of ttt_linattn_forward applies, to dO too). Weight
+ * gradients are reduced in a fixed order: repeated calls give identical bits. Workspace and
+ * errors as for ttt_linattn_forward.
+ * ---------------------------------------------------------------------------------------- */
+ttt_status ttt_linattn_backward(const ttt_linattn_params* p,
+                                const void* Q, const void* K, const void* V, const float* eta,
+                                const float* W0, const float* W2, const float* W1, const void* dO,
+                                void* dQ, void* dK, void* dV, float* deta,
+                                float* dW0, float* dW2, float* dW1,
+                                void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * ttt_linattn_forward_noalloc
  *
  * For callers that cannot allocate device memory: code under HIP graph capture, tight serving

@@ -27,7 +27,8 @@ FEATURE_MAPS = {"swiglu": 0, "identity": 1}  # ttt_feature_map
 FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
 
-EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_linattn_forward_noalloc", "ttt_inplace_down_forward",
+EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_linattn_forward_noalloc", "ttt_linattn_backward",
+            "ttt_inplace_down_forward",
             "ttt_status_string", "ttt_last_error", "ttt_timing_enable", "ttt_timing_collect")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # TTT_NOALLOC_SCRATCH_BYTES
 
@@ -93,6 +94,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ttt_linattn_forward.restype = ctypes.c_int32
     lib.ttt_linattn_forward_noalloc.argtypes = [ctypes.POINTER(LinattnParams)] + [_vp] * 9 + [_vp]
     lib.ttt_linattn_forward_noalloc.restype = ctypes.c_int32
+    lib.ttt_linattn_backward.argtypes = [ctypes.POINTER(LinattnParams)] + [_vp] * 15 + [_vp, _szp, _vp]
+    lib.ttt_linattn_backward.restype = ctypes.c_int32
     lib.ttt_inplace_down_forward.argtypes = [ctypes.POINTER(InplaceParams)] + [_vp] * 7 + [_vp, _szp, _vp]
     lib.ttt_inplace_down_forward.restype = ctypes.c_int32
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -321,6 +324,38 @@ def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want
     else:
         _call("ttt_linattn_forward", lib.ttt_linattn_forward, base, base, dev, stream)
     return O, S
+
+
+def linattn_backward(Q, K, V, eta, W0, W2, W1, dO, *, chunk: int, order: int = APPLY_THEN_UPDATE,
+                     momentum: float = 0.0, stream=None):
+    """Gradients of sum(O * dO) of linattn_forward (SwiGLU map). Returns dict(dQ, dK, dV, deta,
+    dW0, dW2, dW1); the weight gradients have the weights' shape (summed over the batch when the
+    weights are shared)."""
+    torch = _torch()
+    lib = load()
+    B, H, N, h = Q.shape
+    dev = Q.device
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO")):
+        _check(t, n, Q.dtype, dev)
+    _check(eta, "eta", torch.float32, dev)
+    for t, n in ((W0, "W0"), (W1, "W1"), (W2, "W2")):
+        _check(t, n, torch.float32, dev)
+    if K.shape != Q.shape or V.shape != Q.shape or dO.shape != Q.shape or eta.shape != (B, H, N):
+        raise ValueError("Q/K/V/dO must share [B,H,N,h] and eta be [B,H,N]")
+    _check_weights(W0, W1, W2, B, H, h)
+    if not (0.0 <= momentum < 1.0):
+        raise ValueError("momentum must lie in [0, 1)")
+    per_seq = W0.dim() == 4
+    rh = W0.shape[-1]
+    p = LinattnParams(B, H, N, h, rh // h, chunk, order, _io_dtype(Q), H * h * rh if per_seq else 0,
+                      float(momentum), 0)
+    out = dict(dQ=torch.empty_like(Q), dK=torch.empty_like(K), dV=torch.empty_like(V),
+               deta=torch.empty_like(eta), dW0=torch.empty_like(W0), dW2=torch.empty_like(W2),
+               dW1=torch.empty_like(W1))
+    base = [ctypes.byref(p)] + [_ptr(t) for t in (Q, K, V, eta, W0, W2, W1, dO)] + \
+        [_ptr(out[k]) for k in ("dQ", "dK", "dV", "deta", "dW0", "dW2", "dW1")]
+    _call("ttt_linattn_backward", lib.ttt_linattn_backward, base, base, dev, stream)
+    return out
 
 
 def inplace_down_forward(Hs, W_gate, W_up, W_down, Vbar, *, chunk: int, eta: float,

@@ -177,6 +177,24 @@ def test_linattn_identity_feature_map_validation(lib):
     assert "single-pass" in ttt.last_error()
 
 
+def test_linattn_backward_query_and_validation(lib):
+    def q(**kw):
+        base = dict(B=4, H=8, N=8192, h=64, r=2, chunk=512, order=0, dtype=ttt.BF16, w_batch_stride=0)
+        base.update(kw)
+        p = ttt.LinattnParams(**base)
+        sz = ctypes.c_size_t(0)
+        st = lib.ttt_linattn_backward(ctypes.byref(p), *([FAKE] * 15), None, ctypes.byref(sz), None)
+        return st, sz.value
+    st, size = q()
+    assert st == ttt.TTT_OK and size > 0
+    assert q(momentum=0.9, order=1)[0] == ttt.TTT_OK
+    for kw in (dict(dtype=ttt.FP32), dict(h=128, r=2), dict(h=64, r=1), dict(r=1, feature_map=1)):
+        assert q(**kw)[0] == ttt.TTT_ERR_UNSUPPORTED, kw
+    assert q(N=8000)[0] == ttt.TTT_ERR_SHAPE
+    assert q(momentum=1.0)[0] == ttt.TTT_ERR_ARG
+    assert q(feature_map=3)[0] == ttt.TTT_ERR_ARG
+
+
 def _inp(lib, Vbar=FAKE, **kw):
     base = dict(B=1, N=32768, d_model=4096, d_hidden=14336, chunk=1024, eta=1e-3, dtype=ttt.BF16,
                 wdown_batch_stride=0)
