@@ -15,7 +15,7 @@ the host cores on a bounded sample of the same workload.
 
 --config 1 / 3 / 4 time the linear-attention scan, the view-synthesis shape and the In-Place
 update instead (--config 1 --feature-map identity: the scan with one linear fast-weight layer,
-an h x h state). The default run (the LM layer) also measures those workloads and adds them to
+an h x h state; --config 1 --backward: the gradients of the scan form). The default run (the LM layer) also measures those workloads and adds them to
 its JSON line under "other_workloads" (--no-extras skips them). The scan workload's
 136 MB fit in the 256 MB last-level cache, so it is timed both warm and with a 512 MB buffer
 read between repetitions (flushed; its headline figure).
@@ -44,10 +44,12 @@ def parse():
                     help="scan workload only: heavy-ball momentum per chunk (the momentum form)")
     ap.add_argument("--feature-map", default="swiglu", choices=["swiglu", "identity"],
                     help="scan workload only: the identity map is one linear fast-weight layer (h x h state)")
+    ap.add_argument("--backward", action="store_true",
+                    help="scan workload only: time the backward (gradients of every input) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="default run: do not measure the other three workloads")
+                    help="default run: do not measure the other workloads")
     return ap.parse_args()
 
 
@@ -111,6 +113,25 @@ def cpu_baseline_linattn(p, x, budget_s, feature_map="swiglu"):
     return {"value": round(done * p.Nk / p.H / el, 1), "unit": "tokens/s", "cores": int(blas_threads()),
             "kind": "oracle", "blas": blas_vendor(),
             "sample": f"{done} of {len(pairs)} pairs, float32 NumPy oracle, {el:.1f} s"}
+
+
+def cpu_baseline_linattn_backward(p, x, budget_s):
+    import numpy as np
+    from oracle import linattn as LA
+    dO = np.random.default_rng(11).standard_normal(x["Q"].shape[2:]).astype(np.float32)
+    done, t0 = 0, time.perf_counter()
+    pairs = [(b, h) for b in range(p.B) for h in range(p.H)]
+    for (b, h) in pairs:
+        LA.linattn_backward_pair(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["eta"][b, h], x["W0"][h], x["W1"][h],
+                                 x["W2"][h], dO, chunk=p.chunk_kv, order=p.order, momentum=p.momentum,
+                                 dtype=np.float32)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done * p.Nk / p.H / el, 1), "unit": "tokens/s", "cores": int(blas_threads()),
+            "kind": "oracle", "blas": blas_vendor(),
+            "sample": f"{done} of {len(pairs)} pairs, float32 NumPy oracle backward, {el:.1f} s"}
 
 
 def cpu_baseline_inplace(p, x, budget_s):
@@ -222,7 +243,7 @@ def roofline(kern, work, bound, peak, unit):
             "work_per_launch": per_launch, "avg_launch_us": kern[dom]["avg_us"]}
 
 
-def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu"):
+def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu", backward=False):
     """One workload: its JSON record (without the fields common to every line)."""
     import numpy as np
     import torch
@@ -245,6 +266,8 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu"):
         from dataclasses import replace
         p = replace(p, r=1)
         stem = "linattn_identity_b4h8_h64_seq8192_chunk512" + ("_momentum" if momentum else "")
+    if k == 1 and backward:
+        stem = "linattn_backward_b4h8_h64_seq8192_chunk512"
     if k == 4:
         x = make_inplace_inputs(p, k)
         Hs, Wg, Wu, Vb = (t(x[n], torch.bfloat16) for n in ("Hs", "W_gate", "W_up", "Vbar"))
@@ -267,7 +290,22 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu"):
         Q, K, V = (t(x[n], io) for n in ("Q", "K", "V"))
         eta = t(x["eta"], torch.float32)
         W0, W1, W2 = (t(x[n], torch.float32) for n in ("W0", "W1", "W2"))
-        if k == 1:
+        if k == 1 and backward:
+            dO = t(np.random.default_rng(11).standard_normal(x["Q"].shape).astype(np.float32), io)
+
+            def step():
+                return ttt.linattn_backward(Q, K, V, eta, W0, W2, W1, dO, chunk=p.chunk_kv, order=p.order,
+                                            momentum=p.momentum, stream=stream)
+            flops = acc.linattn_backward_flops(p.B, p.H, p.Nk, p.h, p.r)
+            P, rh = p.B * p.H, p.rh
+            unit_p = P * 2.0 * p.Nk * p.h * rh  # one product of 2 N h rh over all pairs
+            # per launch: the aggregate kernel (phi and one contraction: 3 products), the token
+            # kernels (query side 7, key side 8: 7.5 on average)
+            work = {"linattn_delta": 3 * unit_p, "linattn_apply": 7.5 * unit_p}
+            bound, peak, unit = "mfma", acc.PEAK_BF16_TFLOPS, "TFLOP/s"
+            metric = "linear-attention scan form backward tokens/sec (h=64, r=2, chunk 512), bf16"
+            dtype = DTYPES["linattn"]
+        elif k == 1:
             fw0, fw2 = (None, None) if ident else (W0, W2)
 
             def step():
@@ -323,6 +361,9 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu"):
             if ident:
                 cfg["workload"] += ", identity feature map"
                 cfg["feature_map"] = "identity"
+            if backward:
+                cfg["workload"] += ", backward"
+                cfg["pass"] = "backward"
             if p.momentum:
                 cfg["workload"] += f" + momentum {p.momentum:g}"
                 cfg["momentum"] = p.momentum
@@ -340,6 +381,13 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu"):
     kern = kernel_breakdown(ttt, step, args.steps, flush_bytes)
     roof = roofline(kern, work, bound, peak, unit)
     roof["traffic"] = acc.profiled_traffic(ROOT, roof["kernel"], stem)
+    # the same class's average duration in the committed rocprofv3 profile (the profiler slows the
+    # kernels a little): its roofline fraction beside the live one
+    prof_us = acc.profiled_avg_us(ROOT, roof["kernel"], stem)
+    if prof_us:
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        roof["profiled_avg_us"] = round(prof_us, 3)
+        roof["frac_profiled"] = round(roof["work_per_launch"] / (prof_us * 1e-6) / scale / peak, 4)
     rec = {"metric": metric, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
            "dtype": dtype, "config": cfg, "roofline": roof, "step_flops": flops,
            "step_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -350,6 +398,8 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu"):
     if cpu:
         if k == 4:
             rec["cpu_baseline"] = cpu_baseline_inplace(p, x, args.cpu_seconds)
+        elif k == 1 and backward:
+            rec["cpu_baseline"] = cpu_baseline_linattn_backward(p, x, args.cpu_seconds)
         elif k == 1:
             rec["cpu_baseline"] = cpu_baseline_linattn(p, x, args.cpu_seconds, feature_map)
         else:
@@ -364,12 +414,16 @@ def main():
               "(sequence, head) pairs shard across GPUs without communication, see DESIGN.md",
               file=sys.stderr)
         sys.exit(2)
-    if (args.momentum != 0.0 or args.feature_map != "swiglu") and args.config != 1:
-        print("--momentum and --feature-map apply to the scan workload (--config 1) only", file=sys.stderr)
+    if (args.momentum != 0.0 or args.feature_map != "swiglu" or args.backward) and args.config != 1:
+        print("--momentum, --feature-map and --backward apply to the scan workload (--config 1) only", file=sys.stderr)
+        sys.exit(2)
+    if args.backward and args.feature_map != "swiglu":
+        print("--backward is built for the SwiGLU feature map", file=sys.stderr)
         sys.exit(2)
     import linear_attention_lact_amd as ttt
     ttt.load()
-    rec = measure(args.config, args, args.momentum, cpu=not args.no_cpu_baseline, feature_map=args.feature_map)
+    rec = measure(args.config, args, args.momentum, cpu=not args.no_cpu_baseline, feature_map=args.feature_map,
+                  backward=args.backward)
     out = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec.pop("ms_per_step"),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec.pop("dtype"),
@@ -379,8 +433,9 @@ def main():
     out.update(rec)
     if args.config == 2 and not args.no_extras:
         others = {}
-        for k, fm in ((1, "swiglu"), (1, "identity"), (3, "swiglu"), (4, "swiglu")):
-            r = measure(k, args, cpu=False, feature_map=fm)
+        for k, fm, bwd in ((1, "swiglu", False), (1, "identity", False), (1, "swiglu", True), (3, "swiglu", False),
+                           (4, "swiglu", False)):
+            r = measure(k, args, cpu=False, feature_map=fm, backward=bwd)
             others[r["config"]["workload"]] = {
                 "metric": r["metric"], "value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
                 "roofline": {key: r["roofline"][key] for key in ("bound", "kernel", "achieved", "peak", "unit", "frac")},

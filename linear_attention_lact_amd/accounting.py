@@ -63,6 +63,14 @@ def linattn_bytes(B, H, N, h, r, io_bytes=2) -> float:
     return B * H * (4 * N * h * io_bytes + 4 * N + 4 * h * rh * 4)
 
 
+def linattn_backward_flops(B, H, N, h, r) -> float:
+    """Backward of the scan form: phi(Q), phi(K) (4 products), dS (1), G = phi(Q)^T dO (1),
+    dphi(Q) = dO S^T (1), dphi(K) and d(eta V) (2), and through each feature map dX (2) and the
+    weight gradients (2), i.e. 17 products of 2 N h rh (the GPU recomputes phi(Q) and phi(K)
+    once more: 21)."""
+    return B * H * 17 * 2.0 * N * h * (r * h)
+
+
 def linattn_identity_flops(B, H, N, h) -> float:
     """Identity feature map (h x h state): dS = K^T diag(eta) V and O = Q S, 2 products of 2 N h h."""
     return B * H * 2 * 2.0 * N * h * h
@@ -99,17 +107,46 @@ def kernel_source_hash(root: str) -> str:
     return h.hexdigest()
 
 
+KERNEL_SYMBOLS = {"lact_update": ("lact_update_kernel",), "lact_grad": ("grad_ws_kernel", "grad_rd_kernel", "grad_kernel"),
+                  "lact_apply": ("apply_rd_kernel",), "linattn_delta": ("grad_rd_kernel",),
+                  "linattn_apply": ("apply_rd_kernel", "linattn_bwd_tok_kernel"), "linattn_scan": ("linattn_scan_kernel",),
+                  "lact_update_apply": ("lact_update_apply_kernel",), "linattn_fused": ("linattn_fused_kernel",),
+                  "inplace_apply_z": ("gemm_big_pair_kernel",), "inplace_update": ("gemm_rmw_pp_kernel",)}
+
+
+def profiled_avg_us(root: str, kernel_class: str, stem: str):
+    """Average duration (us) of a kernel class's dispatches in the committed rocprofv3 kernel
+    statistics profiles/<stem>_kernel_stats.txt (the call-weighted mean over the matching
+    kernels), or None when there is none or the kernel sources changed since it was taken."""
+    import os
+    syms = KERNEL_SYMBOLS.get(kernel_class)
+    path = os.path.join(root, "profiles", stem + "_kernel_stats.txt")
+    if syms is None or not os.path.exists(path):
+        return None
+    lines = open(path).read().splitlines()
+    tag = [l for l in lines if l.startswith("# kernel sources sha1:")]
+    if not tag or tag[0].split(":", 1)[1].strip() != kernel_source_hash(root):
+        return None
+    calls = tot = 0.0
+    for l in lines:
+        if l.startswith("#") or not l.strip() or not any(sym in l for sym in syms):
+            continue
+        parts = l.split()
+        try:
+            calls += float(parts[0])
+            tot += float(parts[4]) * 1e3  # total ms -> us
+        except (ValueError, IndexError):
+            return None
+    return tot / calls if calls else None
+
+
 def profiled_traffic(root: str, kernel_class: str, stem: str):
     """HBM bytes per launch (read + write) of a kernel class from the committed counter profile
     profiles/<stem>_hbm_counters.txt, or None when there is none for this class or the kernel
     sources changed since it was taken."""
     import glob
     import os
-    symbol = {"lact_update": ("lact_update_kernel",), "lact_grad": ("grad_ws_kernel", "grad_rd_kernel"),
-              "lact_apply": ("apply_rd_kernel",), "linattn_delta": ("grad_rd_kernel",),
-              "linattn_apply": ("apply_rd_kernel",), "linattn_scan": ("linattn_scan_kernel",),
-              "lact_update_apply": ("lact_update_apply_kernel",), "linattn_fused": ("linattn_fused_kernel",)}
-    syms = symbol.get(kernel_class)
+    syms = KERNEL_SYMBOLS.get(kernel_class)
     if syms is None:
         return None
     cur = kernel_source_hash(root)

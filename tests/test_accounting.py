@@ -120,6 +120,16 @@ def test_linattn_counter_equals_the_oracles_products(monkeypatch):
     assert n == acc.linattn_flops(1, 1, 64, 8, 2)
 
 
+def test_linattn_backward_counter_equals_the_oracles_products(monkeypatch):
+    from oracle import linattn as LA
+    p = LactProblem(B=1, H=1, h=8, r=2, Nq=64, Nk=64, chunk_q=16, chunk_kv=16)
+    x = make_lact_inputs(p, 7)
+    dO = np.random.default_rng(8).standard_normal((64, 8))
+    n = _count(LA, monkeypatch, lambda: LA.linattn_backward_pair(
+        x["Q"][0, 0], x["K"][0, 0], x["V"][0, 0], x["eta"][0, 0], x["W0"][0], x["W1"][0], x["W2"][0], dO, chunk=16))
+    assert n == acc.linattn_backward_flops(1, 1, 64, 8, 2)
+
+
 def test_linattn_identity_counter_equals_the_oracles_products(monkeypatch):
     from oracle import linattn as LA
     p = LactProblem(B=1, H=1, h=8, r=1, Nq=64, Nk=64, chunk_q=16, chunk_kv=16)
