@@ -28,7 +28,6 @@ struct BwdTokArgs {
   const bf16_t* L;        // [pair][N][H] dO (query side) or V (key side)
   const float* eta;       // [pair][N] (key side)
   const _Float16* M;      // [pair][nch][RH][H] S_c (query side) or R_c (key side), rows j
-  const _Float16* Mt;     // [pair][nch][H][RH] R_c transposed (key side)
   const _Float16* W0T;    // [pair][RH][H] (W0^T, W2^T shadows, rows j)
   const _Float16* W2T;
   const _Float16* W0r;    // [pair][H][RH] row-form shadows
@@ -43,7 +42,7 @@ struct BwdTokArgs {
 
 template <int H, int RH>
 constexpr int bwd_tok_lds_bytes() {
-  return (2 * TT * (H + 8) + 3 * TT * (RH + 8)) * 2 + (H / 32) * TT * 4;
+  return (3 * TT * (H + 8) + 3 * TT * (RH + 8)) * 2 + (H / 32) * TT * 4;
 }
 
 // grid P * nch, block 256 (4 waves). KEY selects the key side.
@@ -59,6 +58,7 @@ __global__ void __launch_bounds__(256) linattn_bwd_tok_kernel(BwdTokArgs a) {
   constexpr int NT5 = 2 * TC * TJ;          // [c][j] tiles of dW0 and dW2
   constexpr int PW5 = (NT5 + 3) / 4;        // per wave
   static_assert(H % 32 == 0 && RH % 32 == 0 && NT5 <= 4 * 4, "shape");
+  static_assert(4 % TJ == 0 && 4 % TC == 0, "a wave's tiles share one j block and one c block");
 
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* Xs = reinterpret_cast<_Float16*>(smem);   // [TT][LDX]
@@ -66,7 +66,8 @@ __global__ void __launch_bounds__(256) linattn_bwd_tok_kernel(BwdTokArgs a) {
   _Float16* Ps = Ls + TT * LDX;                        // [TT][LDJ] phi (key side)
   _Float16* dAs = Ps + TT * LDJ;                       // [TT][LDJ]
   _Float16* dBs = dAs + TT * LDJ;                      // [TT][LDJ]
-  float* red = reinterpret_cast<float*>(dBs + TT * LDJ);  // [TC][TT] deta partials
+  bf16_t* Vs = reinterpret_cast<bf16_t*>(dBs + TT * LDJ);  // [TT][LDX] V as given (key side)
+  float* red = reinterpret_cast<float*>(Vs + TT * LDX);      // [TC][TT] deta partials
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int pair = blockIdx.x / a.nch, c = blockIdx.x % a.nch;
@@ -75,49 +76,92 @@ __global__ void __launch_bounds__(256) linattn_bwd_tok_kernel(BwdTokArgs a) {
   const int cb = c * a.chunk, ce = cb + a.chunk;
   const int64_t n = (int64_t)RH * H;
   const _Float16* Mc = a.M + ((int64_t)pair * a.nch + c) * n;
-  const _Float16* Mtc = KEY ? a.Mt + ((int64_t)pair * a.nch + c) * n : nullptr;
   const _Float16* w0t = a.W0T + pair * a.wstride;
   const _Float16* w2t = a.W2T + pair * a.wstride;
   const _Float16* w0r = a.W0r + pair * a.wstride;
   const _Float16* w2r = a.W2r + pair * a.wstride;
 
+  // the operand fragments of the fast weights and of the chunk's state that this wave's tiles
+  // use: constant over the chunk, so loaded once (a wave's [t][j] tiles share the j block
+  // w % TJ, its [t][c] tiles the c block w % TC)
+  const int wj = w % TJ, wc = w % TC;
+  frag w0f[KS], w2f[KS], mf[KS], w0rf[KJ], w2rf[KJ], mtf[KEY ? KJ : 1];
+  {
+    const int64_t jr = (int64_t)(wj * 32 + (lane & 31)) * H + (lane >> 5) * M::KSUB;
+    const int64_t cr = (int64_t)(wc * 32 + (lane & 31)) * RH + (lane >> 5) * M::KSUB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      w0f[s] = M::load(w0t + jr + s * M::KSTEP);
+      w2f[s] = M::load(w2t + jr + s * M::KSTEP);
+      mf[s] = M::load(Mc + jr + s * M::KSTEP);
+    }
+#pragma unroll
+    for (int s = 0; s < KJ; ++s) {
+      w0rf[s] = M::load(w0r + cr + s * M::KSTEP);
+      w2rf[s] = M::load(w2r + cr + s * M::KSTEP);
+      if constexpr (KEY) {
+        // R^T rows c, K = j: gathered from the rows j of R (once per workgroup)
+        const int cc = wc * 32 + (lane & 31), j0 = s * M::KSTEP + (lane >> 5) * M::KSUB;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mtf[s][e] = Mc[(int64_t)(j0 + e) * H + cc];
+      }
+    }
+  }
+
   f32x16 acc5[PW5];
 #pragma unroll
   for (int i = 0; i < PW5; ++i) zero(acc5[i]);
 
-  for (int t0 = cb; t0 < ce; t0 += TT) {
-    // ---- stage X and L (key side: eta * V) for tokens t0 .. t0 + 63 of the chunk ----
-    for (int i = tid; i < TT * H / 8; i += 256) {
-      const int r = i / (H / 8), col = (i % (H / 8)) * 8;
-      const int t = t0 + r;
-      u32x4 xr = {0u, 0u, 0u, 0u}, lr = {0u, 0u, 0u, 0u};
-      float e = 0.f;
+  // staging of X and L (key side: eta * V) through registers: the next tile is requested
+  // before the current one is worked on
+  constexpr int NCH = TT * H / 8 / 256;  // 16-byte chunks per thread and tensor
+  static_assert(TT * H % (8 * 256) == 0, "staging map");
+  u32x4 xg[NCH], lg[NCH];
+  float eg[NCH];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int i = tid + 256 * k, r = i / (H / 8), col = (i % (H / 8)) * 8, t = t0 + r;
+      xg[k] = lg[k] = u32x4{0u, 0u, 0u, 0u};
+      eg[k] = 0.f;
       if (t < ce) {
-        xr = *reinterpret_cast<const u32x4*>(a.X + tok + (int64_t)t * H + col);
-        lr = *reinterpret_cast<const u32x4*>(a.L + tok + (int64_t)t * H + col);
-        if (KEY) e = a.eta[(int64_t)pair * a.N + t];
+        xg[k] = *reinterpret_cast<const u32x4*>(a.X + tok + (int64_t)t * H + col);
+        lg[k] = *reinterpret_cast<const u32x4*>(a.L + tok + (int64_t)t * H + col);
+        if (KEY) eg[k] = a.eta[(int64_t)pair * a.N + t];
       }
-      *reinterpret_cast<f16x8*>(Xs + r * LDX + col) = bf16x8_to_f16x8(xr);
-      *reinterpret_cast<f16x8*>(Ls + r * LDX + col) = KEY ? bf16x8_scaled_f16x8(lr, e) : bf16x8_to_f16x8(lr);
     }
+  };
+  fetch(cb);
+  for (int t0 = cb; t0 < ce; t0 += TT) {
+    // ---- stage X and L for tokens t0 .. t0 + 63 of the chunk; request the next tile ----
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int i = tid + 256 * k, r = i / (H / 8), col = (i % (H / 8)) * 8;
+      *reinterpret_cast<f16x8*>(Xs + r * LDX + col) = bf16x8_to_f16x8(xg[k]);
+      *reinterpret_cast<f16x8*>(Ls + r * LDX + col) = KEY ? bf16x8_scaled_f16x8(lg[k], eg[k]) : bf16x8_to_f16x8(lg[k]);
+      if (KEY) *reinterpret_cast<u32x4*>(Vs + r * LDX + col) = lg[k];
+    }
+    if (t0 + TT < ce) fetch(t0 + TT);
     __syncthreads();
 
     // ---- A = X W0, Bm = X W2, D = L M^T per [t][j] tile; dA, dBm (and phi) to LDS ----
-    for (int q = w; q < NT1; q += 4) {
-      const int tt = q / TJ, tj = q % TJ;
+#pragma unroll
+    for (int i = 0; i < (NT1 + 3) / 4; ++i) {
+      const int q = w + 4 * i;
+      if (q >= NT1) break;
+      const int tt = q / TJ, tj = wj;
       f32x16 fa, fb, fd;
       zero(fa);
       zero(fb);
       zero(fd);
       const _Float16* xr = Xs + (tt * 32 + (lane & 31)) * LDX + (lane >> 5) * M::KSUB;
       const _Float16* lr = Ls + (tt * 32 + (lane & 31)) * LDX + (lane >> 5) * M::KSUB;
-      const int64_t jr = (int64_t)(tj * 32 + (lane & 31)) * H + (lane >> 5) * M::KSUB;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const frag xf = M::load(xr + s * M::KSTEP);
-        fa = M::mma(xf, M::load(w0t + jr + s * M::KSTEP), fa);
-        fb = M::mma(xf, M::load(w2t + jr + s * M::KSTEP), fb);
-        fd = M::mma(M::load(lr + s * M::KSTEP), M::load(Mc + jr + s * M::KSTEP), fd);
+        fa = M::mma(xf, w0f[s], fa);
+        fb = M::mma(xf, w2f[s], fb);
+        fd = M::mma(M::load(lr + s * M::KSTEP), mf[s], fd);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -133,17 +177,19 @@ __global__ void __launch_bounds__(256) linattn_bwd_tok_kernel(BwdTokArgs a) {
     __syncthreads();
 
     // ---- dX = dA W0^T + dBm W2^T per [t][c] tile; key side: d(eta V) = phi R, dV, deta ----
-    for (int q = w; q < NT4; q += 4) {
-      const int tt = q / TC, tc = q % TC;
+#pragma unroll
+    for (int i = 0; i < (NT4 + 3) / 4; ++i) {
+      const int q = w + 4 * i;
+      if (q >= NT4) break;
+      const int tt = q / TC, tc = wc;
       f32x16 fx;
       zero(fx);
       const _Float16* ar = dAs + (tt * 32 + (lane & 31)) * LDJ + (lane >> 5) * M::KSUB;
       const _Float16* br = dBs + (tt * 32 + (lane & 31)) * LDJ + (lane >> 5) * M::KSUB;
-      const int64_t cr = (int64_t)(tc * 32 + (lane & 31)) * RH + (lane >> 5) * M::KSUB;
 #pragma unroll
       for (int s = 0; s < KJ; ++s) {
-        fx = M::mma(M::load(ar + s * M::KSTEP), M::load(w0r + cr + s * M::KSTEP), fx);
-        fx = M::mma(M::load(br + s * M::KSTEP), M::load(w2r + cr + s * M::KSTEP), fx);
+        fx = M::mma(M::load(ar + s * M::KSTEP), w0rf[s], fx);
+        fx = M::mma(M::load(br + s * M::KSTEP), w2rf[s], fx);
       }
       const int col = tc * 32 + acc_col(lane);
 #pragma unroll
@@ -156,7 +202,7 @@ __global__ void __launch_bounds__(256) linattn_bwd_tok_kernel(BwdTokArgs a) {
         zero(fe);
         const _Float16* pr = Ps + (tt * 32 + (lane & 31)) * LDJ + (lane >> 5) * M::KSUB;
 #pragma unroll
-        for (int s = 0; s < KJ; ++s) fe = M::mma(M::load(pr + s * M::KSTEP), M::load(Mtc + cr + s * M::KSTEP), fe);
+        for (int s = 0; s < KJ; ++s) fe = M::mma(M::load(pr + s * M::KSTEP), mtf[s], fe);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int tl = tt * 32 + acc_row(r, lane), t = t0 + tl;
@@ -164,7 +210,7 @@ __global__ void __launch_bounds__(256) linattn_bwd_tok_kernel(BwdTokArgs a) {
           if (t < ce) {
             const float e = a.eta[(int64_t)pair * a.N + t];
             Io<bf16_t>::store(a.dV + tok + (int64_t)t * H + col, e * fe[r]);
-            dv = fe[r] * bf16_to_f32(a.L[tok + (int64_t)t * H + col].bits);
+            dv = fe[r] * bf16_to_f32(Vs[tl * LDX + col].bits);
           }
           // sum over the tile's 32 columns (the lanes of one half-wave), in a fixed order
 #pragma unroll
@@ -226,55 +272,69 @@ __global__ void __launch_bounds__(256) linattn_bwd_wrow_kernel(const float* W0, 
 
 // Reverse heavy-ball scan of the state gradients, one thread per state element [j][c]:
 // R_j = T_j + alpha R_{j+1} with T_j = sum_{c > j} G_c (apply-then-update) or sum_{c >= j}
-// (update-then-apply); writes R_j as fp16 rows [j][c] and transposed [c][j], and the pair's
-// dW1 = sum_c G_c (float32). grid (ceil(n / 256), P), block 256.
-__global__ void __launch_bounds__(256) linattn_bwd_rscan_kernel(const float* G, _Float16* R, _Float16* Rt, float* dW1p,
-                                                               int h, int rh, int nch, int inclusive, float alpha) {
+// (update-then-apply); writes R_j as fp16 rows [j][c] and the pair's dW1 = sum_c G_c
+// (float32). grid (ceil(n / 256), P), block 256; the chunk increments are loaded eight at a time.
+__global__ void __launch_bounds__(256) linattn_bwd_rscan_kernel(const float* G, _Float16* R, float* dW1p, int h,
+                                                               int rh, int nch, int inclusive, float alpha) {
   const int pair = blockIdx.y;
   const int64_t n = (int64_t)rh * h;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
-  const int j = (int)(e / h), cc = (int)(e % h);
   const float* g = G + (int64_t)pair * nch * n + e;
   float T = 0.f, Rv = 0.f, tot = 0.f;
-  for (int k = nch - 1; k >= 0; --k) {
-    const float gk = g[(int64_t)k * n];
-    if (inclusive) T += gk;
-    Rv = T + alpha * Rv;
-    R[((int64_t)pair * nch + k) * n + e] = static_cast<_Float16>(Rv);
-    Rt[((int64_t)pair * nch + k) * n + (int64_t)cc * rh + j] = static_cast<_Float16>(Rv);
-    if (!inclusive) T += gk;
-    tot += gk;
+  for (int k0 = nch - 1; k0 >= 0; k0 -= 8) {
+    float gk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gk[u] = k0 - u >= 0 ? g[(int64_t)(k0 - u) * n] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 - u;
+      if (k < 0) break;
+      if (inclusive) T += gk[u];
+      Rv = T + alpha * Rv;
+      R[((int64_t)pair * nch + k) * n + e] = static_cast<_Float16>(Rv);
+      if (!inclusive) T += gk[u];
+      tot += gk[u];
+    }
   }
   dW1p[(int64_t)pair * n + e] = tot;
 }
 
 // Weight gradients in the weights' layout: dW0 / dW2 [B?][H][h][rh] = sum over the sequences
 // sharing the weights (all of them when w_batch_stride is 0, else one), the two sides and the
-// chunks, in that fixed order; dW1 [B?][H][rh][h] likewise from the per-pair sums.
-// grid (ceil(n / 256), 3, Hw) with Hw = H (shared) or B * H, block 256.
+// chunks, in that fixed order; dW1 [B?][H][rh][h] likewise from the per-pair sums. Four
+// consecutive elements per thread, the partials of eight chunks requested together.
+// grid (ceil(n / 1024), 3, Hw) with Hw = H (shared) or B * H, block 256.
 __global__ void __launch_bounds__(256) linattn_bwd_wreduce_kernel(const float* partq, const float* partk,
                                                                  const float* dW1p, float* dW0, float* dW2,
                                                                  float* dW1, int B, int H, int nch, int64_t n,
                                                                  int shared) {
   const int mat = blockIdx.y, slot = blockIdx.z;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= n) return;
+  float* out = mat == 0 ? dW0 : mat == 1 ? dW2 : dW1;
+  if (!out) return;
   const int nb = shared ? B : 1;
-  float s = 0.f;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
   for (int bi = 0; bi < nb; ++bi) {
     const int pair = shared ? bi * H + slot : slot;
     if (mat == 2) {
-      s += dW1p[(int64_t)pair * n + e];
+      s += *reinterpret_cast<const f32x4*>(dW1p + (int64_t)pair * n + e);
       continue;
     }
     for (int side = 0; side < 2; ++side) {
       const float* p = (side == 0 ? partq : partk) + (int64_t)pair * nch * 2 * n + (int64_t)mat * n + e;
-      for (int k = 0; k < nch; ++k) s += p[(int64_t)k * 2 * n];
+      for (int k0 = 0; k0 < nch; k0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = k0 + u < nch ? *reinterpret_cast<const f32x4*>(p + (int64_t)(k0 + u) * 2 * n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
     }
   }
-  float* out = mat == 0 ? dW0 : mat == 1 ? dW2 : dW1;
-  if (out) out[(int64_t)slot * n + e] = s;
+  *reinterpret_cast<f32x4*>(out + (int64_t)slot * n + e) = s;
 }
 
 __global__ void __launch_bounds__(256) fill_kernel(float* p, float v, int64_t n) {
@@ -307,7 +367,6 @@ static ttt_status linattn_bwd_run(const ttt_linattn_params& p, char* ws, const s
   float* dS = reinterpret_cast<float*>(ws + off[2]); // [P][nch][n] forward aggregates, then G_c
   OpT* St = reinterpret_cast<OpT*>(ws + off[3]);     // [P][nch][n] forward states (rows)
   OpT* Rr = reinterpret_cast<OpT*>(ws + off[4]);     // [P][nch][n] R_c rows
-  OpT* Rt = reinterpret_cast<OpT*>(ws + off[5]);     // [P][nch][n] R_c transposed
   float* partq = reinterpret_cast<float*>(ws + off[6]);
   float* partk = reinterpret_cast<float*>(ws + off[7]);
   float* dW1p = reinterpret_cast<float*>(ws + off[8]);
@@ -361,7 +420,7 @@ static ttt_status linattn_bwd_run(const ttt_linattn_params& p, char* ws, const s
   TTT_HIP(launch_k(K_LIN_DELTA, gkr, dim3(ggrid), dim3(256), glds, st, gq, nch, P));
   {
     LaunchTimer lt(K_LIN_SCAN, st);
-    hipLaunchKernelGGL(linattn_bwd_rscan_kernel, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, dS, Rr, Rt,
+    hipLaunchKernelGGL(linattn_bwd_rscan_kernel, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, dS, Rr,
                        dW1p, H, RH, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.momentum);
     TTT_HIP(hipGetLastError());
   }
@@ -385,7 +444,6 @@ static ttt_status linattn_bwd_run(const ttt_linattn_params& p, char* ws, const s
   ak.L = static_cast<const bf16_t*>(V);
   ak.eta = eta;
   ak.M = Rr;
-  ak.Mt = Rt;
   ak.dX = static_cast<bf16_t*>(dK);
   ak.dV = static_cast<bf16_t*>(dV);
   ak.deta = deta;
@@ -396,7 +454,7 @@ static ttt_status linattn_bwd_run(const ttt_linattn_params& p, char* ws, const s
   {
     LaunchTimer lt(K_LIN_SCAN, st);
     const int shared = p.w_batch_stride == 0 ? 1 : 0;
-    hipLaunchKernelGGL(linattn_bwd_wreduce_kernel, dim3((unsigned)((n + 255) / 256), 3, shared ? p.H : P), dim3(256), 0,
+    hipLaunchKernelGGL(linattn_bwd_wreduce_kernel, dim3((unsigned)((n + 1023) / 1024), 3, shared ? p.H : P), dim3(256), 0,
                        st, partq, partk, dW1p, dW0, dW2, dW1, p.B, p.H, nch, n, shared);
     TTT_HIP(hipGetLastError());
   }
@@ -438,7 +496,7 @@ extern "C" ttt_status ttt_linattn_backward(const ttt_linattn_params* p, const vo
   off[2] = plan.add((size_t)P * nch * n * 4);
   off[3] = plan.add((size_t)P * nch * n * 2);
   off[4] = plan.add((size_t)P * nch * n * 2);
-  off[5] = plan.add((size_t)P * nch * n * 2);
+  off[5] = plan.add(0);  // (unused)
   off[6] = plan.add((size_t)P * nch * 2 * n * 4);
   off[7] = plan.add((size_t)P * nch * 2 * n * 4);
   off[8] = plan.add((size_t)P * n * 4);
