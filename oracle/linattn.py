@@ -69,10 +69,18 @@ def _as(a, dtype):
     return None if a is None else np.asarray(a, dtype=dtype)
 
 
+CHUNK_NO_UPDATE, CHUNK_RESET = 1, 2  # per-chunk flags, as in the LaCT loop
+
+
 def linattn_pair(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                 momentum: float = 0.0, feature_map: str = "swiglu", dtype=np.float64):
+                 momentum: float = 0.0, feature_map: str = "swiglu", chunk_flags=None, dtype=np.float64):
     """Chunked linear attention for one pair. Returns (O, S_final); S_final is the state
-    after the last chunk's write. feature_map "identity": phi(x) = x, W1 is h x h."""
+    after the last chunk's write. feature_map "identity": phi(x) = x, W1 is h x h.
+
+    chunk_flags (one per chunk; the LaCT loop's apply-only and reset flags, read for the scan
+    form): an apply-only chunk writes nothing and takes no momentum step; a reset chunk starts
+    from W1 with zero momentum, as a fresh call would. With flags the states follow the
+    heavy-ball recurrence chunk by chunk (m <- alpha m + dS_c, S <- S + m)."""
     Q, K, V, eta, W0, W1, W2 = (_as(a, dtype) for a in (Q, K, V, eta, W0, W1, W2))
     feat = feature_map_fn(feature_map)
     n_chunks = K.shape[0] // chunk
@@ -80,6 +88,23 @@ def linattn_pair(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_THE
     for c in range(n_chunks):
         sl = slice(c * chunk, (c + 1) * chunk)
         dS.append(feat(K[sl], W0, W2).T @ (eta[sl, None] * V[sl]))
+    if chunk_flags is not None:
+        O = np.zeros((Q.shape[0], W1.shape[1]), dtype=dtype)
+        S, m = W1.copy(), np.zeros_like(W1)
+        for c in range(n_chunks):
+            f = int(chunk_flags[c])
+            if f & CHUNK_RESET:
+                S, m = W1.copy(), np.zeros_like(W1)
+            write = not f & CHUNK_NO_UPDATE
+            if order == UPDATE_THEN_APPLY and write:
+                m = momentum * m + dS[c]
+                S = S + m
+            sl = slice(c * chunk, (c + 1) * chunk)
+            O[sl] = feat(Q[sl], W0, W2) @ S
+            if order == APPLY_THEN_UPDATE and write:
+                m = momentum * m + dS[c]
+                S = S + m
+        return O, S
 
     def state(c, ord_):
         S = W1.copy()
@@ -97,7 +122,7 @@ def linattn_pair(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_THE
 
 
 def linattn_forward(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                    momentum: float = 0.0, feature_map: str = "swiglu", pairs=None,
+                    momentum: float = 0.0, feature_map: str = "swiglu", pairs=None, chunk_flags=None,
                     dtype=np.float64) -> Dict[str, np.ndarray]:
     """All pairs. Q/K/V [B,H,N,h], eta [B,H,N], W0/W2 [H,h,rh], W1 [H,rh,h]
     (or [B,H,...] per sequence). Returns O [B,H,N,h] and S [B,H,rh,h]. With
@@ -112,7 +137,8 @@ def linattn_forward(Q, K, V, eta, W0, W1, W2, *, chunk: int, order: int = APPLY_
         w0, w1, w2 = ((None if w is None else (w[b, hd] if per_seq else w[hd])) for w in (W0, W1, W2))
         O[b, hd], S[b, hd] = linattn_pair(Q[b, hd], K[b, hd], V[b, hd], eta[b, hd], w0, w1, w2,
                                           chunk=chunk, order=order, momentum=momentum,
-                                          feature_map=feature_map, dtype=dtype)
+                                          feature_map=feature_map, dtype=dtype,
+                                          chunk_flags=None if chunk_flags is None else chunk_flags[b])
     return dict(O=O, S=S)
 
 

@@ -259,3 +259,62 @@ def test_backward_batch_layouts():
         np.testing.assert_allclose(ps[k][1, 0], one[k], rtol=1e-12, atol=1e-14)
     for k in ("dQ", "dK", "dV", "deta"):
         assert np.array_equal(shared[k], ps[k])
+
+
+# ---- per-chunk flags in the scan form ----
+
+def _flag_inputs(seed):
+    p = LactProblem(B=1, H=2, h=8, r=2, Nq=60, Nk=60, chunk_q=12, chunk_kv=12)
+    x = make_lact_inputs(p, seed)
+    x["eta"] = x["eta"] * 20
+    return p, x
+
+
+def _lin(x, sl=None, **kw):
+    take = (lambda a: a[:, :, sl]) if sl is not None else (lambda a: a)
+    return LA.linattn_forward(take(x["Q"]), take(x["K"]), take(x["V"]), take(x["eta"]), x["W0"], x["W1"], x["W2"],
+                              chunk=12, **kw)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("momentum", [0.0, 0.8])
+def test_scan_flags_clear_equal_the_coefficient_form(order, momentum):
+    p, x = _flag_inputs(41)
+    a = _lin(x, order=order, momentum=momentum)
+    b = _lin(x, order=order, momentum=momentum, chunk_flags=np.zeros((1, 5), np.uint8))
+    np.testing.assert_allclose(b["O"], a["O"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(b["S"], a["S"], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("momentum", [0.0, 0.8])
+def test_scan_reset_equals_a_fresh_call(order, momentum):
+    p, x = _flag_inputs(42)
+    flags = np.zeros((1, 5), np.uint8)
+    flags[0, [2, 4]] = LA.CHUNK_RESET
+    full = _lin(x, order=order, momentum=momentum, chunk_flags=flags)
+    for s0, s1 in ((0, 2), (2, 4), (4, 5)):
+        seg = _lin(x, sl=slice(12 * s0, 12 * s1), order=order, momentum=momentum)
+        np.testing.assert_allclose(full["O"][:, :, 12 * s0:12 * s1], seg["O"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(full["S"], seg["S"], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("momentum", [0.0, 0.8])
+def test_scan_apply_only_chunk_equals_removing_its_write(order, momentum):
+    p, x = _flag_inputs(43)
+    flags = np.zeros((1, 5), np.uint8)
+    flags[0, [1, 3]] = LA.CHUNK_NO_UPDATE
+    full = _lin(x, order=order, momentum=momentum, chunk_flags=flags)
+    kept = np.concatenate([np.arange(12 * c, 12 * c + 12) for c in (0, 2, 4)])
+    rest = _lin(x, sl=kept, order=order, momentum=momentum)
+    for i, c in enumerate((0, 2, 4)):
+        np.testing.assert_allclose(full["O"][:, :, 12 * c:12 * c + 12], rest["O"][:, :, 12 * i:12 * i + 12],
+                                   rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(full["S"], rest["S"], rtol=1e-11, atol=1e-12)
+    for c, before in ((1, [0]), (3, [0, 2])):  # its queries read the state the earlier writes left
+        prev = _lin(x, sl=np.concatenate([np.arange(12 * k, 12 * k + 12) for k in before]), order=order,
+                    momentum=momentum)
+        for hd in range(2):
+            o = LA.phi(x["Q"][0, hd, 12 * c:12 * c + 12].astype(np.float64), x["W0"][hd], x["W2"][hd]) @ prev["S"][0, hd]
+            np.testing.assert_allclose(full["O"][0, hd, 12 * c:12 * c + 12], o, rtol=1e-11, atol=1e-12)

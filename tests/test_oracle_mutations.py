@@ -180,6 +180,10 @@ MUTATIONS = [
      lambda: TLV.test_inner_steps_equal_repeated_chunks(0, 2)),
     ("eta rows of W0 and W2 swapped", L, "lact_pair", _eta_rows_swapped,
      lambda: TLV.test_eta_per_matrix_write_is_each_rows_autograd_gradient()),
+    ("scan reset flag ignored", LA, "linattn_pair", _drop_flag(LA.CHUNK_RESET),
+     lambda: TLA.test_scan_reset_equals_a_fresh_call(0, 0.8)),
+    ("scan apply-only flag ignored", LA, "linattn_pair", _drop_flag(LA.CHUNK_NO_UPDATE),
+     lambda: TLA.test_scan_apply_only_chunk_equals_removing_its_write(1, 0.0)),
     ("backward silu' term dropped", LA, "_silu_parts", _backward_silu_prime_dropped,
      lambda: TLA.test_backward_equals_torch_autograd(0, 0.0, False)),
     ("identity kernel rescaled", LA, "phi_identity", _identity_scaled,
