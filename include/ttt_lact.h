@@ -204,6 +204,11 @@ ttt_status ttt_lact_forward(const ttt_lact_params* p,
  * [H, h, h] (or [B, H, h, h]); r must be 1 (else TTT_ERR_ARG); W0 and W2 are not read and may be
  * NULL; S_out is [B, H, h, h]. It runs on the single-pass path only: TTT_BF16 with h in {64, 128}
  * on an 8-XCD device (fp16 operands as above); anything else returns TTT_ERR_UNSUPPORTED.
+ * chunk_flags (the per-chunk flags of ttt_lact_forward, read for the scan form): an apply-only
+ * chunk writes nothing and takes no momentum step; a reset chunk starts from W1 with zero
+ * momentum, as a fresh call would. Calls with flags take the multi-launch path (the SwiGLU map;
+ * with the identity map they return TTT_ERR_UNSUPPORTED); ttt_linattn_backward does not take
+ * flags (TTT_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------------------------- */
 typedef enum {
   TTT_PHI_SWIGLU = 0,    /* phi(x) = silu(x W0) * (x W2), state [rh, h] */
@@ -217,6 +222,7 @@ typedef struct {
   int64_t w_batch_stride;
   float momentum;        /* heavy-ball coefficient alpha per chunk; 0: none */
   int32_t feature_map;   /* ttt_feature_map; 0 (zero-initialised struct): TTT_PHI_SWIGLU */
+  const uint8_t* chunk_flags; /* device [B, N/chunk] or NULL: TTT_CHUNK_* bits, as for ttt_lact_forward */
 } ttt_linattn_params;
 
 ttt_status ttt_linattn_forward(const ttt_linattn_params* p,

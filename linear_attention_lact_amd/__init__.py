@@ -51,7 +51,7 @@ class LinattnParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("chunk", ctypes.c_int32), ("order", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("w_batch_stride", ctypes.c_int64), ("momentum", ctypes.c_float),
-                ("feature_map", ctypes.c_int32)]
+                ("feature_map", ctypes.c_int32), ("chunk_flags", ctypes.c_void_p)]
 
 
 class InplaceParams(ctypes.Structure):
@@ -266,13 +266,15 @@ def lact_forward(Q, K, V, eta, W0, W1, W2, *, chunk_q: int, chunk_kv: Optional[i
 
 
 def linattn_forward(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_THEN_UPDATE,
-                    momentum: float = 0.0, feature_map: str = "swiglu", want_state: bool = True, stream=None):
+                    momentum: float = 0.0, feature_map: str = "swiglu", chunk_flags=None, want_state: bool = True,
+                    stream=None):
     """Last-layer-only linear-attention scan. Q/K/V [B,H,N,h], eta [B,H,N], W0/W2 [(B,)H,h,rh],
     W1 [(B,)H,rh,h]; momentum: heavy-ball coefficient per chunk (0 <= momentum < 1).
     feature_map "identity": phi(x) = x (one linear fast-weight layer), W0/W2 None, W1 [(B,)H,h,h].
+    chunk_flags: None or a uint8 device tensor [B, N/chunk] of CHUNK_NO_UPDATE / CHUNK_RESET bits.
     Returns (O, S_out) with S_out [B,H,rh,h] (None if not want_state)."""
     return _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want_state, stream,
-                    noalloc=False)
+                    noalloc=False, chunk_flags=chunk_flags)
 
 
 def linattn_forward_noalloc(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int = APPLY_THEN_UPDATE,
@@ -285,7 +287,8 @@ def linattn_forward_noalloc(Q, K, V, eta, W0, W2, W1, *, chunk: int, order: int 
                     noalloc=True)
 
 
-def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want_state, stream, noalloc):
+def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want_state, stream, noalloc,
+             chunk_flags=None):
     torch = _torch()
     lib = load()
     B, H, N, h = Q.shape
@@ -312,8 +315,12 @@ def _linattn(Q, K, V, eta, W0, W2, W1, chunk, order, momentum, feature_map, want
         _check_weights(W0, W1, W2, B, H, h)
     if not (0.0 <= momentum < 1.0):
         raise ValueError("momentum must lie in [0, 1)")
+    if chunk_flags is not None:
+        _check(chunk_flags, "chunk_flags", torch.uint8, dev)
+        if chunk <= 0 or tuple(chunk_flags.shape) != (B, N // chunk):
+            raise ValueError("chunk_flags must be uint8 [B, N/chunk]")
     p = LinattnParams(B, H, N, h, rh // h, chunk, order, _io_dtype(Q), H * h * rh if per_seq else 0,
-                      float(momentum), FEATURE_MAPS[feature_map])
+                      float(momentum), FEATURE_MAPS[feature_map], _ptr(chunk_flags))
     O = torch.empty_like(Q)
     S = torch.empty((B, H, rh, h), dtype=torch.float32, device=dev) if want_state else None
     base = [ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(eta), _ptr(W0), _ptr(W2), _ptr(W1), _ptr(O), _ptr(S)]

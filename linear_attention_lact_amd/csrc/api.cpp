@@ -124,5 +124,5 @@ extern "C" ttt_status ttt_timing_collect(ttt_kernel_time* out, int32_t capacity,
 
 // the parameter structs' layouts are part of the ABI (the Python binding mirrors them)
 static_assert(sizeof(ttt_lact_params) == 88, "ttt_lact_params layout");
-static_assert(sizeof(ttt_linattn_params) == 48, "ttt_linattn_params layout");
+static_assert(sizeof(ttt_linattn_params) == 56, "ttt_linattn_params layout");
 static_assert(sizeof(ttt_inplace_params) == 72, "ttt_inplace_params layout");

@@ -84,7 +84,7 @@ static ttt_status linattn_run(const ttt_linattn_params& p, char* ws, size_t oSh,
     auto sk = linattn_scan_kernel<OpT, ARD>;
     hipLaunchKernelGGL(sk, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
                        St, S_out, p.H, H, rh, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.momentum,
-                       p.w_batch_stride);
+                       p.w_batch_stride, p.chunk_flags);
     TTT_HIP(hipGetLastError());
   }
   ApplyArgs aa{};
@@ -218,8 +218,11 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   const bool fused_shape = bf16 && shape_ok &&
                            (int64_t)nch * rh64 * q.h * 4 < (int64_t)1 << 31 &&  // buffer offsets are 32-bit
                            (int64_t)q.N * q.h * 2 < (int64_t)1 << 31;
-  const bool fused = fused_shape && nxcc == 8;
-  if (ident && !fused_shape) return TTT_ERR_UNSUPPORTED;
+  // per-chunk flags run on the multi-launch path (its scan walks the chunks one by one); the
+  // identity map has no such path
+  const bool flagged = q.chunk_flags != nullptr;
+  if (ident && (flagged || !fused_shape)) return TTT_ERR_UNSUPPORTED;
+  const bool fused = fused_shape && nxcc == 8 && !flagged;
   // both plans; the size asked for covers the larger where the single-pass shape applies, so a
   // query gives the same answer on any device (and without one)
   WorkspacePlan fplan, mplan;
@@ -232,7 +235,7 @@ extern "C" ttt_status ttt_linattn_forward(const ttt_linattn_params* p, const voi
   const size_t oSh = mplan.add((size_t)P * 2 * n * opsz);
   const size_t odS = mplan.add((size_t)P * nch * n * 4);
   const size_t oSt = mplan.add((size_t)P * nch * n * opsz);
-  const size_t need = ident ? fplan.total : fused_shape ? std::max(fplan.total, mplan.total) : mplan.total;
+  const size_t need = ident ? fplan.total : (fused_shape && !flagged) ? std::max(fplan.total, mplan.total) : mplan.total;
   if (!workspace) {
     *workspace_bytes = need;
     return TTT_OK;

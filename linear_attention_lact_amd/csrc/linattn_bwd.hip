@@ -408,7 +408,7 @@ static ttt_status linattn_bwd_run(const ttt_linattn_params& p, char* ws, const s
     auto sk = linattn_scan_kernel<OpT, true>;
     hipLaunchKernelGGL(sk, dim3((unsigned)((n + 255) / 256), P), dim3(256), 0, st, W1, dS,
                        St, nullptr, p.H, H, RH, nch, p.order == TTT_UPDATE_THEN_APPLY ? 1 : 0, p.momentum,
-                       p.w_batch_stride);
+                       p.w_batch_stride, static_cast<const uint8_t*>(nullptr));
     TTT_HIP(hipGetLastError());
   }
   // G_c = phi(Q_c)^T dO_c: the aggregate kernel with K := Q, V := dO and unit step sizes
@@ -484,7 +484,7 @@ extern "C" ttt_status ttt_linattn_backward(const ttt_linattn_params* p, const vo
   if (q.w_batch_stride != 0 && q.w_batch_stride != (int64_t)q.H * rh64 * q.h) return TTT_ERR_SHAPE;
   // built: bf16, the SwiGLU map, (h, rh) in {(32, 64), (32, 128), (64, 128)}
   const bool shape_ok = (q.h == 32 && (rh64 == 64 || rh64 == 128)) || (q.h == 64 && rh64 == 128);
-  if (q.dtype != TTT_BF16 || q.feature_map != TTT_PHI_SWIGLU || !shape_ok) return TTT_ERR_UNSUPPORTED;
+  if (q.dtype != TTT_BF16 || q.feature_map != TTT_PHI_SWIGLU || !shape_ok || q.chunk_flags) return TTT_ERR_UNSUPPORTED;
   const int P = q.B * q.H, nch = q.N / q.chunk;
   if (P > 0 && (!W0 || !W1 || !W2)) return TTT_ERR_ARG;
   if (P > 0 && nch > 0 && (!Q || !K || !V || !eta || !dO || !dQ || !dK || !dV || !deta)) return TTT_ERR_ARG;

@@ -2,6 +2,7 @@
 // operand shadows of W0 / W2 and the chunk prefix scan of the states each chunk reads.
 #pragma once
 #include "fastweight.hpp"
+#include "host.hpp"
 
 namespace ttt {
 
@@ -33,19 +34,24 @@ __global__ void __launch_bounds__(256) linattn_prep_kernel(const float* __restri
 // momentum coefficient alpha each chunk's write passes through the heavy-ball buffer
 // m <- alpha m + dS_k, s <- s + m, which gives chunk k's write the cumulative coefficient
 // sum_{i>=k} alpha^(i-k) of Theorem 5.3; alpha = 0 leaves m = dS_k, the plain prefix.
+// flags (nullable, [B][nch]): TTT_CHUNK_RESET restarts from W1 with m = 0 before chunk k,
+// TTT_CHUNK_NO_UPDATE skips chunk k's write and its momentum step.
 // grid (ceil(rh*h/256), P), block 256.
 template <class OpT, bool ROWS>
 __global__ void __launch_bounds__(256) linattn_scan_kernel(const float* __restrict__ W1, const float* __restrict__ dS,
                                                           OpT* __restrict__ St, float* __restrict__ S_out,
                                                           int H, int h, int rh, int nch, int inclusive,
-                                                          float alpha, int64_t w_batch_stride) {
+                                                          float alpha, int64_t w_batch_stride,
+                                                          const uint8_t* flags) {
   const int pair = blockIdx.y;
   const int64_t n = (int64_t)rh * h;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
   const int b = pair / H, head = pair % H;
   const int j = (int)(e / h), c = (int)(e % h);
-  float s = W1[(int64_t)b * w_batch_stride + (int64_t)head * n + e], m = 0.f;
+  const float s0 = W1[(int64_t)b * w_batch_stride + (int64_t)head * n + e];
+  float s = s0, m = 0.f;
+  const uint8_t* fl = flags ? flags + (int64_t)b * nch : nullptr;
   const float* d = dS + (int64_t)pair * nch * n + e;
   OpT* o = St + (int64_t)pair * nch * n + (ROWS ? e : (int64_t)c * rh + j);
   // the chunk increments are loaded eight at a time so that their latencies overlap
@@ -56,12 +62,18 @@ __global__ void __launch_bounds__(256) linattn_scan_kernel(const float* __restri
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (k0 + u >= nch) break;
-      if (inclusive) {
+      const int f = fl ? fl[k0 + u] : 0;
+      if (f & TTT_CHUNK_RESET) {
+        s = s0;
+        m = 0.f;
+      }
+      const bool write = !(f & TTT_CHUNK_NO_UPDATE);
+      if (inclusive && write) {
         m = fmaf(alpha, m, dk[u]);
         s += m;
       }
       o[(int64_t)(k0 + u) * n] = Mfma<OpT>::from_f32(s);
-      if (!inclusive) {
+      if (!inclusive && write) {
         m = fmaf(alpha, m, dk[u]);
         s += m;
       }

@@ -157,7 +157,7 @@ def test_linattn_momentum_validation(lib):
     assert st0 == st1 == ttt.TTT_OK
     # with momentum the single-pass workspace holds the momentum of each inclusive prefix too
     assert multi == single_pass + 4 * 8 * 16 * 128 * 64 * 4
-    assert ctypes.sizeof(ttt.LinattnParams) == 48
+    assert ctypes.sizeof(ttt.LinattnParams) == 56
 
 
 def test_linattn_identity_feature_map_validation(lib):
@@ -177,6 +177,16 @@ def test_linattn_identity_feature_map_validation(lib):
     assert "single-pass" in ttt.last_error()
 
 
+def test_linattn_flags_take_the_multi_launch_path(lib):
+    st, plain = _lin(lib)
+    st2, flagged = _lin(lib, chunk_flags=0x6000)
+    assert st == st2 == ttt.TTT_OK
+    # the multi-launch plan: W0/W2 shadows, chunk aggregates (fp32) and per-chunk states (fp16)
+    P, nch, n = 32, 16, 128 * 64
+    assert flagged >= P * 2 * n * 2 + P * nch * n * 4 + P * nch * n * 2
+    assert _lin(lib, r=1, feature_map=ttt.FEATURE_MAPS["identity"], chunk_flags=0x6000)[0] == ttt.TTT_ERR_UNSUPPORTED
+
+
 def test_linattn_backward_query_and_validation(lib):
     def q(**kw):
         base = dict(B=4, H=8, N=8192, h=64, r=2, chunk=512, order=0, dtype=ttt.BF16, w_batch_stride=0)
@@ -193,6 +203,7 @@ def test_linattn_backward_query_and_validation(lib):
     assert q(N=8000)[0] == ttt.TTT_ERR_SHAPE
     assert q(momentum=1.0)[0] == ttt.TTT_ERR_ARG
     assert q(feature_map=3)[0] == ttt.TTT_ERR_ARG
+    assert q(chunk_flags=0x6000)[0] == ttt.TTT_ERR_UNSUPPORTED
 
 
 def _inp(lib, Vbar=FAKE, **kw):

@@ -254,3 +254,30 @@ def test_per_sequence_weights(lib, h, momentum):
     eo, es = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(S), ref["S"])
     print(f"per-sequence weights h={h} momentum={momentum} O={eo:.2e} S={es:.2e}")
     assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+# ---- per-chunk flags (apply-only chunks, resets) in the scan form: the multi-launch path ----
+
+@pytest.mark.parametrize("dtype,order,momentum", [(BF16, 0, 0.0), (BF16, 1, 0.9), (FP32, 0, 0.9), (FP32, 1, 0.0)])
+def test_chunk_flags(lib, dtype, order, momentum):
+    import torch
+    from oracle import linattn as LA
+    p = LactProblem(B=3, H=2, h=64, r=2, Nq=1024, Nk=1024, chunk_q=128, chunk_kv=128, dtype=dtype,
+                    update_mask=UPD_W1, weight_norm=False, order=order, momentum=momentum)
+    flags = np.zeros((3, 8), np.uint8)
+    flags[0, 4] = LA.CHUNK_RESET
+    flags[1, [1, 5]] = LA.CHUNK_NO_UPDATE
+    flags[2, [0, 3]] = LA.CHUNK_NO_UPDATE | LA.CHUNK_RESET
+    flags[2, 6] = LA.CHUNK_RESET
+    announce(f"linattn flags dtype={dtype} order={order} momentum={momentum}: {flags.tolist()}")
+    x = make_lact_inputs(p, 470 + order, eta_scale=1.0)
+    io = torch.bfloat16 if dtype == BF16 else torch.float32
+    O, S = lib.linattn_forward(dev(x["Q"], io), dev(x["K"], io), dev(x["V"], io), dev(x["eta"], torch.float32),
+                               dev(x["W0"], torch.float32), dev(x["W2"], torch.float32), dev(x["W1"], torch.float32),
+                               chunk=128, order=order, momentum=momentum, chunk_flags=dev(flags, torch.uint8))
+    ref = LA.linattn_forward(x["Q"], x["K"], x["V"], x["eta"], x["W0"], x["W1"], x["W2"], chunk=128, order=order,
+                             momentum=momentum, chunk_flags=flags)
+    eo, es = max_abs_rel(host(O), ref["O"]), max_abs_rel(host(S), ref["S"])
+    print(f"flags O={eo:.2e} S={es:.2e}", flush=True)
+    tol = BF16_TOL if dtype == BF16 else FP32_TOL
+    assert eo <= tol and es <= tol
