@@ -129,3 +129,57 @@ def output_rows(Hs, W_gate, W_up, W_down, Vbar, eta, *, chunk: int, rows: Sequen
         G = G * (np.arange(last * chunk)[None, :] < lim[:, None])
         out = out + eta * (G @ Vp)
     return out
+
+
+# ---- backward (the gradients the chunked update trains through) ----
+# Forward per sequence: W_0 = W_down, Z_i = silu(A_i) * U_i with A_i = H_i W_gate^T,
+# U_i = H_i W_up^T, O_i = Z_i W_i^T, W_{i+1} = W_i + eta Vbar_i^T Z_i. Given dL/dO:
+#   G_i = dO_i^T Z_i            (the gradient reaching W_i through chunk i's output)
+#   R_i = sum_{k > i} G_k       (the gradient reaching chunk i's write eta Vbar_i^T Z_i)
+#   dW_down = sum_i G_i
+#   dZ_i = dO_i W_i + eta Vbar_i R_i,   dVbar_i = eta Z_i R_i^T
+#   dA = dZ * U * silu'(A),  dU = dZ * silu(A),  dH = dA W_gate + dU W_up,
+#   dW_gate = sum dA^T H,  dW_up = sum dU^T H.
+
+def inplace_backward_sequence(Hs, W_gate, W_up, W_down, Vbar, eta, dO, *, chunk: int, dtype=np.float64):
+    """Gradients of sum(O * dO) for one sequence: dict(dH, dW_gate, dW_up, dW_down, dVbar)."""
+    Hs, Wg, Wu, W, Vbar, dO = (np.asarray(a, dtype=dtype) for a in (Hs, W_gate, W_up, W_down, Vbar, dO))
+    n = Hs.shape[0] // chunk
+    sl = [slice(i * chunk, (i + 1) * chunk) for i in range(n)]
+    A = [Hs[s] @ Wg.T for s in sl]
+    U = [Hs[s] @ Wu.T for s in sl]
+    Z = [silu(a) * u for a, u in zip(A, U)]
+    Ws = [W.copy()]
+    for i in range(n - 1):
+        Ws.append(Ws[-1] + eta * (Vbar[sl[i]].T @ Z[i]))
+    G = [dO[s].T @ z for s, z in zip(sl, Z)]
+    out = dict(dH=np.zeros_like(Hs), dW_gate=np.zeros_like(Wg), dW_up=np.zeros_like(Wu),
+               dW_down=sum(G, np.zeros_like(W)), dVbar=np.zeros_like(Vbar))
+    R = np.zeros_like(W)
+    for i in reversed(range(n)):
+        dZ = dO[sl[i]] @ Ws[i] + eta * (Vbar[sl[i]] @ R)
+        out["dVbar"][sl[i]] = eta * (Z[i] @ R.T)
+        sg = 0.5 * (1.0 + np.tanh(0.5 * A[i]))
+        dA = dZ * U[i] * sg * (1.0 + A[i] * (1.0 - sg))
+        dU = dZ * A[i] * sg
+        out["dH"][sl[i]] = dA @ Wg + dU @ Wu
+        out["dW_gate"] += dA.T @ Hs[sl[i]]
+        out["dW_up"] += dU.T @ Hs[sl[i]]
+        R = R + G[i]
+    return out
+
+
+def inplace_backward(Hs, W_gate, W_up, W_down, Vbar, eta, dO, *, chunk: int,
+                     dtype=np.float64) -> Dict[str, np.ndarray]:
+    """All sequences: dH, dVbar [B,N,d_model]; dW_gate, dW_up summed over the batch; dW_down
+    summed over the batch when W_down is shared ([d_model,d_hidden]), per sequence when it is
+    [B,d_model,d_hidden]."""
+    B = Hs.shape[0]
+    per_seq = np.ndim(W_down) == 3
+    res = [inplace_backward_sequence(Hs[b], W_gate, W_up, W_down[b] if per_seq else W_down, Vbar[b], eta, dO[b],
+                                     chunk=chunk, dtype=dtype) for b in range(B)]
+    out = {k: np.stack([r[k] for r in res]) for k in ("dH", "dVbar")}
+    out["dW_gate"] = sum(r["dW_gate"] for r in res)
+    out["dW_up"] = sum(r["dW_up"] for r in res)
+    out["dW_down"] = np.stack([r["dW_down"] for r in res]) if per_seq else sum(r["dW_down"] for r in res)
+    return out

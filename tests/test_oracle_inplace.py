@@ -140,3 +140,30 @@ def test_target_row_sees_only_its_window():
         expect = np.zeros(X0.shape[0], bool)
         expect[max(0, s - 3):s + 1] = True
         np.testing.assert_array_equal(moved, expect)
+
+
+# ---- backward, pinned against torch autograd of an independent torch forward ----
+
+@pytest.mark.parametrize("per_seq", [False, True])
+def test_backward_equals_torch_autograd(per_seq):
+    import torch
+    rng = np.random.default_rng(51)
+    B, N, d, dh, C, eta = 2, 48, 8, 12, 12, 0.3
+    Hs, Vb, dO = rng.standard_normal((B, N, d)), rng.standard_normal((B, N, d)), rng.standard_normal((B, N, d))
+    Wg, Wu = rng.standard_normal((dh, d)) / 3, rng.standard_normal((dh, d)) / 3
+    Wd = rng.standard_normal((B, d, dh) if per_seq else (d, dh)) / 3
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    th, tg, tu, td, tv = t(Hs), t(Wg), t(Wu), t(Wd), t(Vb)
+    outs = []
+    for b in range(B):
+        W = td[b] if per_seq else td
+        for i in range(N // C):
+            s = slice(i * C, (i + 1) * C)
+            Z = torch.nn.functional.silu(th[b, s] @ tg.T) * (th[b, s] @ tu.T)
+            outs.append(Z @ W.T)
+            W = W + eta * (tv[b, s].T @ Z)
+    O = torch.stack(outs).reshape(B, N, d)
+    grads = torch.autograd.grad((O * torch.tensor(dO)).sum(), (th, tg, tu, td, tv))
+    got = IP.inplace_backward(Hs, Wg, Wu, Wd, Vb, eta, dO, chunk=C)
+    for k, g in zip(("dH", "dW_gate", "dW_up", "dW_down", "dVbar"), grads):
+        np.testing.assert_allclose(got[k], g.numpy(), rtol=1e-10, atol=1e-11, err_msg=k)

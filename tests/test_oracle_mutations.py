@@ -146,6 +146,12 @@ def _backward_silu_prime_dropped(orig):
     return f
 
 
+def _inplace_backward_no_write_term(orig):
+    def f(Hs, W_gate, W_up, W_down, Vbar, eta, dO, *, chunk, dtype=np.float64):
+        return orig(Hs, W_gate, W_up, W_down, np.zeros_like(np.asarray(Vbar)), eta, dO, chunk=chunk, dtype=dtype)
+    return f
+
+
 def _identity_scaled(orig):
     return lambda X, W0=None, W2=None: X / np.sqrt(X.shape[1])  # an attention-style 1/sqrt(h)
 
@@ -190,6 +196,8 @@ MUTATIONS = [
      lambda: TLA.test_identity_scan_equals_recurrent_linear_fast_weight(0, 0.0, 8)),
     ("target taps on past tokens", IP, "lm_aligned_target", _target_taps_backward,
      lambda: TI.test_next_token_taps_with_identity_projection_are_the_next_token_shift()),
+    ("In-Place backward without the writes' terms", IP, "inplace_backward_sequence",
+     _inplace_backward_no_write_term, lambda: TI.test_backward_equals_torch_autograd(False)),
     ("In-Place update before apply", IP, "inplace_sequence", _update_before_apply,
      lambda: TI.test_first_chunk_is_the_plain_mlp()),
 ]
