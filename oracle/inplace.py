@@ -183,3 +183,35 @@ def inplace_backward(Hs, W_gate, W_up, W_down, Vbar, eta, dO, *, chunk: int,
     out["dW_up"] = sum(r["dW_up"] for r in res)
     out["dW_down"] = np.stack([r["dW_down"] for r in res]) if per_seq else sum(r["dW_down"] for r in res)
     return out
+
+
+def backward_hidden_units(Hs, W_gate, W_up, W_down, Vbar, eta, dO, units: Sequence[int], *, chunk: int,
+                          dtype=np.float64) -> Dict[str, np.ndarray]:
+    """dW_gate[j], dW_up[j] and dW_down[:, j] of one sequence for the hidden units j in `units`
+    (dict of [len(units), d_model] arrays). Every quantity of unit j depends on column j of Z
+    alone: W_i[:, j] = W_down[:, j] + eta sum_{k<i} Vbar_k^T Z_k[:, j],
+    R_i[:, j] = sum_{k>i} dO_k^T Z_k[:, j], dZ_i[:, j] = dO_i W_i[:, j] + eta Vbar_i R_i[:, j],
+    so sampled units cost O(N d_model) each at any d_hidden."""
+    Hs, Vbar, dO = (np.asarray(a, dtype=dtype) for a in (Hs, Vbar, dO))
+    n = Hs.shape[0] // chunk
+    sl = [slice(i * chunk, (i + 1) * chunk) for i in range(n)]
+    out = {k: np.zeros((len(units), Hs.shape[1]), dtype) for k in ("dW_gate", "dW_up", "dW_down")}
+    for u_idx, j in enumerate(units):
+        a = Hs @ np.asarray(W_gate[j], dtype)
+        u = Hs @ np.asarray(W_up[j], dtype)
+        z = silu(a) * u
+        writes = [Vbar[s].T @ z[s] for s in sl]  # column j of Vbar_k^T Z_k
+        g = [dO[s].T @ z[s] for s in sl]  # column j of G_k
+        w = np.asarray(W_down[:, j], dtype).copy()
+        r = sum(g[1:], np.zeros_like(w))
+        dz = np.zeros_like(a)
+        for i in range(n):
+            dz[sl[i]] = dO[sl[i]] @ w + eta * (Vbar[sl[i]] @ r)
+            w = w + eta * writes[i]
+            if i + 1 < n:
+                r = r - g[i + 1]
+        sg = 0.5 * (1.0 + np.tanh(0.5 * a))
+        out["dW_gate"][u_idx] = (dz * u * sg * (1.0 + a * (1.0 - sg))) @ Hs
+        out["dW_up"][u_idx] = (dz * a * sg) @ Hs
+        out["dW_down"][u_idx] = sum(g, np.zeros_like(w))
+    return out

@@ -167,3 +167,18 @@ def test_backward_equals_torch_autograd(per_seq):
     got = IP.inplace_backward(Hs, Wg, Wu, Wd, Vb, eta, dO, chunk=C)
     for k, g in zip(("dH", "dW_gate", "dW_up", "dW_down", "dVbar"), grads):
         np.testing.assert_allclose(got[k], g.numpy(), rtol=1e-10, atol=1e-11, err_msg=k)
+
+
+def test_hidden_unit_gradients_equal_the_full_backward():
+    """The per-unit evaluator used at full size against the full backward (itself pinned to
+    autograd above), on units at both ends and in the middle."""
+    rng = np.random.default_rng(52)
+    N, d, dh, C, eta = 60, 10, 14, 12, 0.2
+    Hs, Vb, dO = rng.standard_normal((N, d)), rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    Wg, Wu, Wd = rng.standard_normal((dh, d)) / 3, rng.standard_normal((dh, d)) / 3, rng.standard_normal((d, dh)) / 3
+    full = IP.inplace_backward_sequence(Hs, Wg, Wu, Wd, Vb, eta, dO, chunk=C)
+    units = [0, 5, dh - 1]
+    got = IP.backward_hidden_units(Hs, Wg, Wu, Wd, Vb, eta, dO, units, chunk=C)
+    np.testing.assert_allclose(got["dW_gate"], full["dW_gate"][units], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(got["dW_up"], full["dW_up"][units], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(got["dW_down"], full["dW_down"][:, units].T, rtol=1e-11, atol=1e-12)
