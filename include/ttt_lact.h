@@ -330,6 +330,30 @@ ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p,
                                     void* workspace, size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * ttt_inplace_down_backward
+ *
+ * Defined by: the same notes as ttt_inplace_down_forward (sections 3.1, 3.2 / Eq. 4 and 3.4: the
+ * chunked update is what the model trains through). Gradients of sum(O * dO) of
+ * ttt_inplace_down_forward with respect to Hs, W_gate, W_up, W_down and Vbar, for the same
+ * parameters. With G_i = dO_i^T Z_i and R_i = sum_{k > i} G_k: dW_down = sum_i G_i;
+ * dZ_i = dO_i W_i + eta Vbar_i R_i; dVbar_i = eta Z_i R_i^T; through the gate,
+ * dA = dZ * U * silu'(A), dU = dZ * silu(A) (A = H W_gate^T, U = H W_up^T), dHs = dA W_gate +
+ * dU W_up, dW_gate = sum dA^T H, dW_up = sum dU^T H.
+ * Arguments: Hs, W_gate, W_up, W_down, Vbar as for ttt_inplace_down_forward; dO [B, N, d_model]
+ * bf16; dHs, dVbar [B, N, d_model] bf16; dW_gate, dW_up [d_hidden, d_model] float32 (summed over
+ * the batch); dW_down [d_model, d_hidden] float32 (summed over the batch) or [B, d_model,
+ * d_hidden] when wdown_batch_stride != 0. Shape rules as for the forward. TTT_BF16 only; a
+ * target built from X0 (the LM-aligned target) returns TTT_ERR_UNSUPPORTED. The workspace holds
+ * every chunk's Z (both orientations) and its state W_i^T in bf16: about
+ * 2 N d_hidden + (N / chunk) d_model d_hidden bf16 elements plus a few d_model x d_hidden fp32
+ * buffers (8 GB at d_model 4096, d_hidden 14336, N 32768, chunk 1024).
+ * ---------------------------------------------------------------------------------------- */
+ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, const void* Hs, const void* W_gate,
+                                     const void* W_up, const float* W_down, const void* Vbar, const void* dO,
+                                     void* dHs, float* dW_gate, float* dW_up, float* dW_down, void* dVbar,
+                                     void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Kernel timing (instrumentation; off by default)
  *
  * For callers that need per-kernel durations (the benchmark's roofline figures). While

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI, without the ``ttt_`` prefix):
 * :func:`lact_forward`          -- the chunked LaCT layer
 * :func:`linattn_forward`       -- the last-layer-only linear-attention scan form
 * :func:`inplace_down_forward`  -- the In-Place TTT down-projection update
+* :func:`linattn_backward`, :func:`inplace_down_backward` -- their gradients
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
 
 EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_linattn_forward_noalloc", "ttt_linattn_backward",
-            "ttt_inplace_down_forward",
+            "ttt_inplace_down_forward", "ttt_inplace_down_backward",
             "ttt_status_string", "ttt_last_error", "ttt_timing_enable", "ttt_timing_collect")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # TTT_NOALLOC_SCRATCH_BYTES
 
@@ -98,6 +99,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ttt_linattn_backward.restype = ctypes.c_int32
     lib.ttt_inplace_down_forward.argtypes = [ctypes.POINTER(InplaceParams)] + [_vp] * 7 + [_vp, _szp, _vp]
     lib.ttt_inplace_down_forward.restype = ctypes.c_int32
+    lib.ttt_inplace_down_backward.argtypes = [ctypes.POINTER(InplaceParams)] + [_vp] * 11 + [_vp, _szp, _vp]
+    lib.ttt_inplace_down_backward.restype = ctypes.c_int32
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_last_error.argtypes = []
@@ -404,3 +407,35 @@ def inplace_down_forward(Hs, W_gate, W_up, W_down, Vbar, *, chunk: int, eta: flo
     base = [ctypes.byref(p), _ptr(Hs), _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Vbar), _ptr(O), _ptr(Wout)]
     _call("ttt_inplace_down_forward", lib.ttt_inplace_down_forward, base, base, dev, stream)
     return O, Wout
+
+
+def inplace_down_backward(Hs, W_gate, W_up, W_down, Vbar, dO, *, chunk: int, eta: float, stream=None):
+    """Gradients of sum(O * dO) of inplace_down_forward (explicit Vbar, bf16). Returns dict(dHs,
+    dW_gate, dW_up, dW_down, dVbar): dHs/dVbar bf16 [B,N,d_model]; dW_gate/dW_up fp32
+    [d_hidden,d_model] summed over the batch; dW_down fp32 with W_down's shape (summed over the
+    batch when W_down is shared)."""
+    torch = _torch()
+    lib = load()
+    B, N, dm = Hs.shape
+    dh = W_gate.shape[0]
+    dev = Hs.device
+    for t, n in ((Hs, "Hs"), (W_gate, "W_gate"), (W_up, "W_up"), (Vbar, "Vbar"), (dO, "dO")):
+        _check(t, n, torch.bfloat16, dev)
+    _check(W_down, "W_down", torch.float32, dev)
+    if Vbar is None or dO is None:
+        raise ValueError("Vbar and dO are required")
+    if W_gate.shape != (dh, dm) or W_up.shape != (dh, dm):
+        raise ValueError("shape mismatch")
+    if Vbar.shape != Hs.shape or dO.shape != Hs.shape:
+        raise ValueError("Vbar and dO must be [B,N,d_model]")
+    if W_down.shape[-2:] != (dm, dh) or W_down.dim() not in (2, 3) or (W_down.dim() == 3 and W_down.shape[0] != B):
+        raise ValueError("W_down must be [(B,)d_model,d_hidden]")
+    per_seq = W_down.dim() == 3
+    p = InplaceParams(B, N, dm, dh, chunk, eta, BF16, dm * dh if per_seq else 0, None, None, None, 0)
+    out = dict(dHs=torch.empty_like(Hs), dW_gate=torch.empty((dh, dm), dtype=torch.float32, device=dev),
+               dW_up=torch.empty((dh, dm), dtype=torch.float32, device=dev), dW_down=torch.empty_like(W_down),
+               dVbar=torch.empty_like(Vbar))
+    base = [ctypes.byref(p)] + [_ptr(t) for t in (Hs, W_gate, W_up, W_down, Vbar, dO)] + \
+        [_ptr(out[k]) for k in ("dHs", "dW_gate", "dW_up", "dW_down", "dVbar")]
+    _call("ttt_inplace_down_backward", lib.ttt_inplace_down_backward, base, base, dev, stream)
+    return out

@@ -17,7 +17,7 @@ namespace ttt {
 namespace gemm {
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int LDS_LD = BK + 8;  // padded row (elements)
-enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_RMW = 2 };
+enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_RMW = 2, EPI_SWIGLU_BWD = 4 };
 
 struct Args {
   const __bf16* A;  int64_t lda;    // [M][K]
@@ -28,18 +28,22 @@ struct Args {
   __bf16* Ct; int64_t ldct;         // SWIGLU transposed output [N][M]
   float* Wf; __bf16* Wsh; int64_t ldw;  // RMW state and shadow [M][N]
   float alpha;
+  // SWIGLU_BWD: the incoming gradient dZ [M][N] and the second pair of outputs (C, Ct: dA; C2,
+  // Ct2: dU, row-major and transposed like C / Ct)
+  const __bf16* dZ; int64_t lddz;
+  __bf16* C2; __bf16* Ct2;
 };
 
 template <int EPI>
 constexpr int lds_bytes() {
-  return (EPI == EPI_SWIGLU ? 3 : 2) * BM * LDS_LD * 2;
+  return (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD ? 3 : 2) * BM * LDS_LD * 2;
 }
 
 // grid: tiles of 128x128 (x over N tiles, y over M tiles). block 256 = 4 waves (2x2), each
 // wave a 64x64 quadrant = 2x2 MFMA tiles of 32x32.
 template <int EPI>
 __global__ void __launch_bounds__(256) gemm_tn_kernel(Args g) {
-  constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
+  constexpr int NB = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* As = reinterpret_cast<__bf16*>(smem);  // [BM][LDS_LD]
   __bf16* Bs = As + BM * LDS_LD;                 // [NB][BN][LDS_LD]
@@ -130,6 +134,28 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(Args g) {
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           bf16x4 v4 = {zv[0], zv[1], zv[2], zv[3]};
           *reinterpret_cast<bf16x4*>(dst) = v4;
+        }
+      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        // dA = dZ * U * silu'(A), dU = dZ * silu(A) for the products A (gate) and U (up)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __bf16 da[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q + e;
+            const int64_t m = mb + acc_row(r, lane);
+            const float a = acc[0][i][j][r], u = acc[1][i][j][r];
+            const float dz = static_cast<float>(g.dZ[m * g.lddz + n]);
+            const float sg = sigmoidf_(a);
+            da[e] = static_cast<__bf16>(dz * u * (sg * (1.f + a * (1.f - sg))));
+            du[e] = static_cast<__bf16>(dz * a * sg);
+            g.C[m * g.ldc + n] = da[e];
+            g.C2[m * g.ldc + n] = du[e];
+          }
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const int64_t to = (int64_t)n * g.ldct + mb + acc_row(4 * q, lane);
+          *reinterpret_cast<bf16x4*>(g.Ct + to) = bf16x4{da[0], da[1], da[2], da[3]};
+          *reinterpret_cast<bf16x4*>(g.Ct2 + to) = bf16x4{du[0], du[1], du[2], du[3]};
         }
       } else if constexpr (EPI == EPI_STORE) {
 #pragma unroll
@@ -539,6 +565,28 @@ __global__ void __launch_bounds__(256) target_conv_kernel(const __bf16* __restri
   }
 }
 
+// [R][C] float32 -> [C][R] float32 and its bf16 copy, through a 64 x 64 LDS tile.
+// grid (C / 64, R / 64), block 256.
+__global__ void __launch_bounds__(256) transpose_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                           __bf16* __restrict__ dsh, int R, int C) {
+  __shared__ float t[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) t[i / 64][i % 64] = src[(int64_t)(r0 + i / 64) * C + c0 + i % 64];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const float v = t[i % 64][i / 64];
+    const int64_t o = (int64_t)(c0 + i / 64) * R + r0 + i % 64;
+    dst[o] = v;
+    dsh[o] = static_cast<__bf16>(v);
+  }
+}
+
+// dst[i] = 0 (add == 0) or dst[i] += src[i] (add == 1) over n floats. grid-stride.
+__global__ void __launch_bounds__(256) f32_zero_add_kernel(float* dst, const float* src, int64_t n, int add) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = add ? dst[i] + src[i] : 0.f;
+}
+
 // One TN GEMM: the large-tile kernel where the shape fits its tile, else the 128 x 128 kernel.
 // EPI_STORE with ksplit > 1 goes through fp32 partials in `part` and the split sum.
 template <int EPI>
@@ -745,6 +793,196 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
       u.ldw = q.d_hidden;
       u.alpha = q.eta;
       TTT_HIP(run_gemm<EPI_RMW>(K_INP_UPDATE, u, 1, part, st));
+    }
+  }
+  return TTT_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Backward of the In-Place update: two sweeps per sequence over the chunks, every product a TN
+// GEMM of the kernels above. Forward sweep: each chunk's Z, Z^T and the transposed state W_i^T
+// (bf16) are kept. Reverse sweep with R = sum_{k > i} dO_k^T Z_k kept in both orientations:
+//   dZ_i = dO_i W_i + eta Vbar_i R,  dVbar_i = eta Z_i R^T,  R += dO_i^T Z_i,
+//   dA, dU from dZ_i (SwiGLU backward epilogue on the recomputed gate and up products),
+//   dH_i = dA W_gate + dU W_up,  dW_gate += dA^T H_i,  dW_up += dU^T H_i;  dW_down = R at the end.
+extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, const void* Hs, const void* W_gate,
+                                                const void* W_up, const float* W_down, const void* Vbar,
+                                                const void* dO, void* dHs, float* dW_gate, float* dW_up,
+                                                float* dW_down, void* dVbar, void* workspace,
+                                                size_t* workspace_bytes, void* stream) {
+  using namespace gemm;
+  if (!p || !workspace_bytes) return TTT_ERR_ARG;
+  const ttt_inplace_params& q = *p;
+  if (q.B < 0 || q.N < 0 || q.d_model <= 0 || q.d_hidden <= 0 || q.chunk <= 0) return TTT_ERR_ARG;
+  if (q.dtype != TTT_FP32 && q.dtype != TTT_BF16) return TTT_ERR_ARG;
+  if (q.wdown_batch_stride < 0) return TTT_ERR_ARG;
+  if (q.dtype != TTT_BF16 || q.X0) return TTT_ERR_UNSUPPORTED;  // a device-built target has no backward here
+  if (q.N % q.chunk) return TTT_ERR_SHAPE;
+  if (q.d_model % 256 || q.d_hidden % 256 || q.chunk % 128) return TTT_ERR_SHAPE;
+  const int64_t dm = q.d_model, dh = q.d_hidden, C = q.chunk, N = q.N, nW = dm * dh;
+  if (q.wdown_batch_stride != 0 && q.wdown_batch_stride != nW) return TTT_ERR_SHAPE;
+  if (q.B > 0 && (!W_down || !dW_down || !dW_gate || !dW_up)) return TTT_ERR_ARG;
+  if (q.B > 0 && N > 0 && (!Hs || !W_gate || !W_up || !Vbar || !dO || !dHs || !dVbar)) return TTT_ERR_ARG;
+  const int nch = (int)(N / C);
+  WorkspacePlan plan;
+  const size_t oZ = plan.add((size_t)nch * C * dh * 2), oZt = plan.add((size_t)nch * C * dh * 2);
+  const size_t oWtSh = plan.add((size_t)nch * nW * 2), oWt = plan.add((size_t)nW * 4);
+  const size_t oR = plan.add((size_t)nW * 4), oRsh = plan.add((size_t)nW * 2);
+  const size_t oRt = plan.add((size_t)nW * 4), oRtsh = plan.add((size_t)nW * 2);
+  const size_t odZf = plan.add((size_t)C * dh * 4), odZ = plan.add((size_t)C * dh * 2);
+  const size_t odA = plan.add((size_t)C * dh * 2), odAt = plan.add((size_t)C * dh * 2);
+  const size_t odU = plan.add((size_t)C * dh * 2), odUt = plan.add((size_t)C * dh * 2);
+  const size_t odVf = plan.add((size_t)C * dm * 4), odHf = plan.add((size_t)C * dm * 4);
+  const size_t oVt = plan.add((size_t)dm * N * 2), odOt = plan.add((size_t)dm * N * 2), oHt = plan.add((size_t)dm * N * 2);
+  const size_t oWgT = plan.add((size_t)nW * 2), oWuT = plan.add((size_t)nW * 2), oSink = plan.add((size_t)nW * 2);
+  if (!workspace) {
+    *workspace_bytes = plan.total;
+    return TTT_OK;
+  }
+  if (*workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TTT_ERR_WORKSPACE;
+  if (q.B == 0) return TTT_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto bfp = [&](size_t o) { return reinterpret_cast<__bf16*>(ws + o); };
+  auto f32p = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  static const hipError_t lds_ok = [] {
+    hipError_t e = allow_lds(gemm_tn_kernel<EPI_SWIGLU>, lds_bytes<EPI_SWIGLU>());
+    if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_SWIGLU_BWD>, lds_bytes<EPI_SWIGLU_BWD>());
+    if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_STORE>, lds_bytes<EPI_STORE>());
+    if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_RMW>, lds_bytes<EPI_RMW>());
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_RMW>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel, gemm2::PP_LDS);
+    return e;
+  }();
+  TTT_HIP(lds_ok);
+  const bool shared = q.wdown_batch_stride == 0;
+  auto zero = [&](float* d, int64_t n) -> hipError_t {
+    hipLaunchKernelGGL(f32_zero_add_kernel, dim3(1024), dim3(256), 0, st, d, static_cast<const float*>(nullptr), n, 0);
+    return hipGetLastError();
+  };
+  auto rmw = [&](const __bf16* A, int64_t lda, const __bf16* B, int64_t ldb, int64_t M, int64_t Nn, int64_t K, float* Wf,
+                 __bf16* Wsh, int64_t ldw, float alpha) -> hipError_t {
+    Args u{};
+    u.A = A;
+    u.lda = lda;
+    u.B0 = B;
+    u.ldb = ldb;
+    u.M = (int)M;
+    u.N = (int)Nn;
+    u.K = (int)K;
+    u.Wf = Wf;
+    u.Wsh = Wsh;
+    u.ldw = ldw;
+    u.alpha = alpha;
+    return run_gemm<EPI_RMW>(K_INP_UPDATE, u, 1, nullptr, st);
+  };
+  const __bf16* Wg = static_cast<const __bf16*>(W_gate);
+  const __bf16* Wu = static_cast<const __bf16*>(W_up);
+  {
+    LaunchTimer lt(K_INP_PREP, st);
+    TTT_HIP(zero(dW_gate, nW));
+    TTT_HIP(zero(dW_up, nW));
+    if (shared) TTT_HIP(zero(dW_down, nW));
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(dm / 64), (unsigned)(dh / 64)), dim3(256), 0, st, Wg,
+                       bfp(oWgT), (int)dh, (int)dm);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(dm / 64), (unsigned)(dh / 64)), dim3(256), 0, st, Wu,
+                       bfp(oWuT), (int)dh, (int)dm);
+    TTT_HIP(hipGetLastError());
+  }
+  for (int b = 0; b < q.B; ++b) {
+    const __bf16* Hb = static_cast<const __bf16*>(Hs) + (int64_t)b * N * dm;
+    const __bf16* Vb = static_cast<const __bf16*>(Vbar) + (int64_t)b * N * dm;
+    const __bf16* dOb = static_cast<const __bf16*>(dO) + (int64_t)b * N * dm;
+    __bf16* dHb = static_cast<__bf16*>(dHs) + (int64_t)b * N * dm;
+    __bf16* dVb = static_cast<__bf16*>(dVbar) + (int64_t)b * N * dm;
+    float* R = f32p(oR);
+    float* Rt = f32p(oRt);
+    if (nch == 0) {
+      if (!shared) TTT_HIP(zero(dW_down + (int64_t)b * nW, nW));
+      continue;
+    }
+    {
+      LaunchTimer lt(K_INP_PREP, st);
+      const dim3 tg((unsigned)(dm / 64), (unsigned)(N / 64));
+      hipLaunchKernelGGL(transpose_bf16_kernel, tg, dim3(256), 0, st, Hb, bfp(oHt), (int)N, (int)dm);
+      hipLaunchKernelGGL(transpose_bf16_kernel, tg, dim3(256), 0, st, Vb, bfp(oVt), (int)N, (int)dm);
+      hipLaunchKernelGGL(transpose_bf16_kernel, tg, dim3(256), 0, st, dOb, bfp(odOt), (int)N, (int)dm);
+      hipLaunchKernelGGL(transpose_f32_kernel, dim3((unsigned)(dh / 64), (unsigned)(dm / 64)), dim3(256), 0, st,
+                         W_down + (int64_t)b * q.wdown_batch_stride, f32p(oWt), bfp(oWtSh), (int)dm, (int)dh);
+      TTT_HIP(hipGetLastError());
+      TTT_HIP(zero(R, nW));
+      TTT_HIP(zero(Rt, nW));
+    }
+    // forward sweep: Z_i, Z_i^T and the states W_i^T (bf16)
+    for (int i = 0; i < nch; ++i) {
+      Args z{};
+      z.A = Hb + (int64_t)i * C * dm;
+      z.lda = dm;
+      z.B0 = Wg;
+      z.B1 = Wu;
+      z.ldb = dm;
+      z.M = (int)C;
+      z.N = (int)dh;
+      z.K = (int)dm;
+      z.C = bfp(oZ) + (int64_t)i * C * dh;
+      z.ldc = dh;
+      z.Ct = bfp(oZt) + (int64_t)i * C * dh;
+      z.ldct = C;
+      TTT_HIP(run_gemm<EPI_SWIGLU>(K_INP_Z, z, 1, nullptr, st));
+      if (i + 1 < nch)  // W_{i+1}^T = W_i^T + eta Z_i^T Vbar_i
+        TTT_HIP(rmw(bfp(oZt) + (int64_t)i * C * dh, C, bfp(oVt) + (int64_t)i * C, N, dh, dm, C, f32p(oWt),
+                    bfp(oWtSh) + (int64_t)(i + 1) * nW, dm, q.eta));
+    }
+    // reverse sweep
+    for (int i = nch - 1; i >= 0; --i) {
+      const int64_t t0 = (int64_t)i * C;
+      const __bf16* Zi = bfp(oZ) + (int64_t)i * C * dh;
+      const __bf16* Zti = bfp(oZt) + (int64_t)i * C * dh;
+      const bool later = i + 1 < nch;  // R holds the writes' gradient of later chunks
+      TTT_HIP(zero(f32p(odZf), C * dh));
+      TTT_HIP(rmw(dOb + t0 * dm, dm, bfp(oWtSh) + (int64_t)i * nW, dm, C, dh, dm, f32p(odZf), bfp(odZ), dh, 1.f));
+      if (later) {
+        TTT_HIP(rmw(Vb + t0 * dm, dm, bfp(oRtsh), dm, C, dh, dm, f32p(odZf), bfp(odZ), dh, q.eta));
+        TTT_HIP(zero(f32p(odVf), C * dm));
+        TTT_HIP(rmw(Zi, dh, bfp(oRsh), dh, C, dm, dh, f32p(odVf), dVb + t0 * dm, dm, q.eta));
+      } else {
+        TTT_HIP(zero(reinterpret_cast<float*>(dVb + t0 * dm), C * dm / 2));  // no later chunk reads its write
+      }
+      TTT_HIP(rmw(bfp(odOt) + t0, N, Zti, C, dm, dh, C, R, bfp(oRsh), dh, 1.f));
+      TTT_HIP(rmw(Zti, C, bfp(odOt) + t0, N, dh, dm, C, Rt, bfp(oRtsh), dm, 1.f));
+      {
+        Args g{};
+        g.A = Hb + t0 * dm;
+        g.lda = dm;
+        g.B0 = Wg;
+        g.B1 = Wu;
+        g.ldb = dm;
+        g.M = (int)C;
+        g.N = (int)dh;
+        g.K = (int)dm;
+        g.dZ = bfp(odZ);
+        g.lddz = dh;
+        g.C = bfp(odA);
+        g.C2 = bfp(odU);
+        g.ldc = dh;
+        g.Ct = bfp(odAt);
+        g.Ct2 = bfp(odUt);
+        g.ldct = C;
+        TTT_HIP(launch_k(K_INP_APPLY, gemm_tn_kernel<EPI_SWIGLU_BWD>, dim3((unsigned)(dh / BN), (unsigned)(C / BM)),
+                         dim3(256), lds_bytes<EPI_SWIGLU_BWD>(), st, g));
+      }
+      TTT_HIP(zero(f32p(odHf), C * dm));
+      TTT_HIP(rmw(bfp(odA), dh, bfp(oWgT), dh, C, dm, dh, f32p(odHf), dHb + t0 * dm, dm, 1.f));
+      TTT_HIP(rmw(bfp(odU), dh, bfp(oWuT), dh, C, dm, dh, f32p(odHf), dHb + t0 * dm, dm, 1.f));
+      TTT_HIP(rmw(bfp(odAt), C, bfp(oHt) + t0, N, dh, dm, C, dW_gate, bfp(oSink), dm, 1.f));
+      TTT_HIP(rmw(bfp(odUt), C, bfp(oHt) + t0, N, dh, dm, C, dW_up, bfp(oSink), dm, 1.f));
+    }
+    if (shared) {
+      hipLaunchKernelGGL(f32_zero_add_kernel, dim3(1024), dim3(256), 0, st, dW_down, static_cast<const float*>(R), nW, 1);
+      TTT_HIP(hipGetLastError());
+    } else {
+      TTT_HIP(hipMemcpyAsync(dW_down + (int64_t)b * nW, R, (size_t)nW * 4, hipMemcpyDeviceToDevice, st));
     }
   }
   return TTT_OK;

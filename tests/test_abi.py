@@ -29,7 +29,8 @@ def _declared():
 
 def test_header_declares_the_three_entry_points():
     d = _declared()
-    for name in ("ttt_lact_forward", "ttt_linattn_forward", "ttt_inplace_down_forward"):
+    for name in ("ttt_lact_forward", "ttt_linattn_forward", "ttt_inplace_down_forward", "ttt_linattn_backward",
+                 "ttt_inplace_down_backward"):
         assert name in d
 
 
@@ -239,6 +240,32 @@ def test_inplace_query_and_validation(lib):
     assert _inp(lib, chunk=-4)[0] == ttt.TTT_ERR_ARG
     assert _inp(lib, chunk=64, N=32768)[0] == ttt.TTT_ERR_SHAPE  # the chunk must be a multiple of 128
     assert _inp(lib, chunk=128, N=32768)[0] == ttt.TTT_OK
+
+
+def _inp_bwd(lib, **kw):
+    base = dict(B=1, N=32768, d_model=4096, d_hidden=14336, chunk=1024, eta=1e-3, dtype=ttt.BF16,
+                wdown_batch_stride=0)
+    base.update(kw)
+    p = ttt.InplaceParams(**base)
+    sz = ctypes.c_size_t(0)
+    st = lib.ttt_inplace_down_backward(ctypes.byref(p), *([FAKE] * 11), None, ctypes.byref(sz), None)
+    return st, sz.value
+
+
+def test_inplace_backward_query_and_validation(lib):
+    st, size = _inp_bwd(lib)
+    assert st == ttt.TTT_OK
+    # every chunk's Z in both orientations and every chunk's state W_i^T in bf16 dominate
+    nch, nW = 32, 4096 * 14336
+    assert size >= 2 * 32768 * 14336 * 2 + nch * nW * 2 and size < 9 << 30
+    assert _inp_bwd(lib, wdown_batch_stride=4096 * 14336)[0] == ttt.TTT_OK
+    assert _inp_bwd(lib, wdown_batch_stride=7)[0] == ttt.TTT_ERR_SHAPE
+    assert _inp_bwd(lib, dtype=ttt.FP32)[0] == ttt.TTT_ERR_UNSUPPORTED
+    assert _inp_bwd(lib, X0=0x3000, conv_taps=0x4000, conv_k=2)[0] == ttt.TTT_ERR_UNSUPPORTED
+    assert _inp_bwd(lib, N=32768 + 512)[0] == ttt.TTT_ERR_SHAPE
+    assert _inp_bwd(lib, d_hidden=14336 + 128)[0] == ttt.TTT_ERR_SHAPE
+    assert _inp_bwd(lib, chunk=-4)[0] == ttt.TTT_ERR_ARG
+    assert _inp_bwd(lib, B=0)[0] == ttt.TTT_OK
 
 
 class _FakeCuda:

@@ -110,3 +110,92 @@ def test_general_target(lib, kw, k, proj):
     print(f"inplace target O={eo:.2e} W={ew:.2e}", flush=True)
     assert eo <= BF16_TOL and ew <= BF16_TOL
     assert max_abs_rel(ref["W_down"][0], x["W_down"]) > 1e-2  # the writes are visible
+
+
+# ---- backward (ttt_inplace_down_backward) ----
+
+BWD_NAMES = ("dHs", "dW_gate", "dW_up", "dW_down", "dVbar")
+
+
+def _gpu_bwd(lib, p, x, dO, W_down=None):
+    import torch
+    return lib.inplace_down_backward(dev(x["Hs"], torch.bfloat16), dev(x["W_gate"], torch.bfloat16),
+                                     dev(x["W_up"], torch.bfloat16),
+                                     dev(x["W_down"] if W_down is None else W_down, torch.float32),
+                                     dev(x["Vbar"], torch.bfloat16), dev(dO, torch.bfloat16), chunk=p.chunk,
+                                     eta=float(x["eta"]))
+
+
+@pytest.mark.parametrize("kw,per_seq", [
+    (dict(B=2, N=512, d_model=256, d_hidden=512, chunk=128, eta=1e-3), False),
+    (dict(B=2, N=512, d_model=256, d_hidden=512, chunk=128, eta=1e-2), True),
+    (dict(B=1, N=1024, d_model=512, d_hidden=768, chunk=256, eta=3e-3), False),
+    (dict(B=1, N=256, d_model=256, d_hidden=256, chunk=256, eta=1e-3), False),  # one chunk: no write reaches O
+    # products whose M and N are multiples of 256 (the large-tile update kernel)
+    (dict(B=1, N=1024, d_model=512, d_hidden=1024, chunk=256, eta=2e-3), True),
+])
+def test_backward_small_cases(lib, kw, per_seq):
+    from oracle import inplace as IP
+    from workloads import bf16_round
+    p = InplaceProblem(**kw)
+    announce(f"inplace backward {p} per_seq={per_seq}")
+    x = make_inplace_inputs(p, 600 + p.N + p.d_hidden)
+    rng = np.random.default_rng(p.N + p.d_model)
+    dO = bf16_round(rng.standard_normal((p.B, p.N, p.d_model)).astype(np.float32))
+    Wd = np.stack([x["W_down"]] * p.B) if per_seq else x["W_down"]
+    if per_seq:
+        Wd = bf16_round(Wd * (1.0 + 0.1 * np.arange(p.B, dtype=np.float32))[:, None, None])
+    got = _gpu_bwd(lib, p, x, dO, W_down=Wd)
+    ref = IP.inplace_backward(x["Hs"], x["W_gate"], x["W_up"], Wd, x["Vbar"], float(x["eta"]), dO, chunk=p.chunk)
+    ref["dHs"] = ref.pop("dH")
+    errs = {k: max_abs_rel(host(got[k]), ref[k]) for k in BWD_NAMES}
+    print("inplace backward: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+    if p.N > p.chunk:  # the writes' terms are visible in the gradients
+        flat = IP.inplace_backward(x["Hs"], x["W_gate"], x["W_up"], Wd, x["Vbar"], 0.0, dO, chunk=p.chunk)
+        assert max_abs_rel(flat["dH"], ref["dHs"]) > 0.05
+        assert np.abs(ref["dVbar"]).max() > 0
+
+
+def test_backward_full_width_two_chunks(lib):
+    """The In-Place widths (d_model 4096, d_hidden 14336, chunk 1024) over two chunks: every
+    gradient against the oracle (in float32, the only size it finishes in seconds)."""
+    from oracle import inplace as IP
+    from workloads import bf16_round
+    p = InplaceProblem(B=1, N=2048, d_model=4096, d_hidden=14336, chunk=1024, eta=1e-4)
+    announce(f"inplace backward full width {p}")
+    x = make_inplace_inputs(p, 640)
+    dO = bf16_round(np.random.default_rng(41).standard_normal((1, p.N, p.d_model)).astype(np.float32))
+    got = _gpu_bwd(lib, p, x, dO)
+    ref = IP.inplace_backward(x["Hs"], x["W_gate"], x["W_up"], x["W_down"], x["Vbar"], float(x["eta"]), dO,
+                              chunk=p.chunk, dtype=np.float32)
+    ref["dHs"] = ref.pop("dH")
+    errs = {k: max_abs_rel(host(got[k]), ref[k]) for k in BWD_NAMES}
+    print("full width: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+def test_backward_full_size_sampled_units(lib):
+    """The full In-Place size (seq 32768, 32 chunks): the weight gradients of sampled hidden units
+    (rows of dW_gate and dW_up, columns of dW_down) against the oracle's per-unit evaluator;
+    dVbar of the last chunk is zero (no later chunk reads its write); repeated calls bit for bit."""
+    import torch
+    from oracle import inplace as IP
+    from workloads import bf16_round
+    p = CONFIGS[4]
+    announce("inplace backward config4 full size (sampled units)")
+    x = make_inplace_inputs(p, 4)
+    dO = bf16_round(np.random.default_rng(42).standard_normal((p.B, p.N, p.d_model)).astype(np.float32))
+    got = _gpu_bwd(lib, p, x, dO)
+    units = [0, 777, 8191, 14335]
+    ref = IP.backward_hidden_units(x["Hs"][0], x["W_gate"], x["W_up"], x["W_down"], x["Vbar"][0], float(x["eta"]),
+                                   dO[0], units, chunk=p.chunk)
+    errs = dict(dW_gate=max_abs_rel(host(got["dW_gate"][units]), ref["dW_gate"]),
+                dW_up=max_abs_rel(host(got["dW_up"][units]), ref["dW_up"]),
+                dW_down=max_abs_rel(host(got["dW_down"][:, units]).T, ref["dW_down"]))
+    print("config4 sampled units: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+    assert not bool(got["dVbar"][0, -p.chunk:].any())
+    again = _gpu_bwd(lib, p, x, dO)
+    for k in BWD_NAMES:
+        assert torch.equal(got[k], again[k]), k
