@@ -15,8 +15,9 @@ the host cores on a bounded sample of the same workload.
 
 --config 1 / 3 / 4 time the linear-attention scan, the view-synthesis shape and the In-Place
 update instead (--config 1 --feature-map identity: the scan with one linear fast-weight layer,
-an h x h state; --config 1 --backward: the gradients of the scan form). The default run (the LM layer) also measures those workloads and adds them to
-its JSON line under "other_workloads" (--no-extras skips them). The scan workload's
+an h x h state; --config 1 --backward, --config 4 --backward: the gradients of the scan form,
+of the In-Place update). The default run (the LM layer) also measures those workloads and adds
+them to its JSON line under "other_workloads" (--no-extras skips them). The scan workload's
 136 MB fit in the 256 MB last-level cache, so it is timed both warm and with a 512 MB buffer
 read between repetitions (flushed; its headline figure).
 """
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--feature-map", default="swiglu", choices=["swiglu", "identity"],
                     help="scan workload only: the identity map is one linear fast-weight layer (h x h state)")
     ap.add_argument("--backward", action="store_true",
-                    help="scan workload only: time the backward (gradients of every input) instead")
+                    help="scan workload and In-Place update: time the backward (gradients of every input) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--no-extras", action="store_true",
@@ -151,6 +152,23 @@ def cpu_baseline_inplace(p, x, budget_s):
     return {"value": round(done * p.chunk / el, 1), "unit": "tokens/s", "cores": int(blas_threads()),
             "kind": "oracle", "blas": blas_vendor(),
             "sample": f"first {done} of {p.N // p.chunk} chunks, float32 NumPy oracle, {el:.1f} s"}
+
+
+def cpu_baseline_inplace_backward(p, x, n_chunks=4):
+    """The oracle's backward over the first n_chunks chunks of the sequence, taken as a sequence
+    of its own (the backward's work per chunk does not depend on the sequence length)."""
+    import numpy as np
+    from oracle import inplace as IP
+    T = n_chunks * p.chunk
+    dO = np.random.default_rng(12).standard_normal((T, p.d_model)).astype(np.float32)
+    t0 = time.perf_counter()
+    IP.inplace_backward_sequence(x["Hs"][0, :T], x["W_gate"], x["W_up"], x["W_down"], x["Vbar"][0, :T],
+                                 float(x["eta"]), dO, chunk=p.chunk, dtype=np.float32)
+    el = time.perf_counter() - t0
+    return {"value": round(T / el, 1), "unit": "tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "blas": blas_vendor(),
+            "sample": f"backward of the first {n_chunks} of {p.N // p.chunk} chunks as one sequence, float32 "
+                      f"NumPy oracle, {el:.1f} s"}
 
 
 def time_steps(step, steps, warmup, stream):
@@ -273,16 +291,30 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu", backward=Fals
         Hs, Wg, Wu, Vb = (t(x[n], torch.bfloat16) for n in ("Hs", "W_gate", "W_up", "Vbar"))
         Wd = t(x["W_down"], torch.float32)
 
-        def step():
-            return ttt.inplace_down_forward(Hs, Wg, Wu, Wd, Vb, chunk=p.chunk, eta=float(x["eta"]), stream=stream)
+        per = 2.0 * p.chunk * p.d_model * p.d_hidden  # one chunk-sized product
+        work = {"inplace_z": 2 * per, "inplace_apply": per, "inplace_update": per, "inplace_apply_z": 3 * per,
+                "inplace_swiglu_bwd": 2 * per}
+        if backward:
+            dO = t(np.random.default_rng(12).standard_normal(x["Hs"].shape).astype(np.float32), torch.bfloat16)
+            stem = "inplace_backward_d4096_dh14336_seq32768_chunk1024"
+
+            def step():
+                return ttt.inplace_down_backward(Hs, Wg, Wu, Wd, Vb, dO, chunk=p.chunk, eta=float(x["eta"]),
+                                                 stream=stream)
+            flops = acc.inplace_backward_flops(p.B, p.N, p.d_model, p.d_hidden)
+            metric = "In-Place TTT W_down update backward tokens/sec (d_model 4096, d_hidden 14336, chunk 1024), bf16"
+        else:
+            def step():
+                return ttt.inplace_down_forward(Hs, Wg, Wu, Wd, Vb, chunk=p.chunk, eta=float(x["eta"]),
+                                                stream=stream)
+            flops = acc.inplace_flops(p.B, p.N, p.d_model, p.d_hidden)
+            metric = "In-Place TTT W_down update tokens/sec (d_model 4096, d_hidden 14336, chunk 1024), bf16"
         tokens = p.B * p.N
-        flops = acc.inplace_flops(p.B, p.N, p.d_model, p.d_hidden)
-        per = 2.0 * p.chunk * p.d_model * p.d_hidden
-        work = {"inplace_z": 2 * per, "inplace_apply": per, "inplace_update": per, "inplace_apply_z": 3 * per}
         bound, peak, unit = "mfma", acc.PEAK_BF16_TFLOPS, "TFLOP/s"
-        metric = "In-Place TTT W_down update tokens/sec (d_model 4096, d_hidden 14336, chunk 1024), bf16"
-        cfg = {"workload": CONFIG_NAMES[4], "B": p.B, "seq_len": p.N, "d_model": p.d_model,
-               "d_hidden": p.d_hidden, "chunk": p.chunk, "eta": p.eta}
+        cfg = {"workload": CONFIG_NAMES[4] + (", backward" if backward else ""), "B": p.B, "seq_len": p.N,
+               "d_model": p.d_model, "d_hidden": p.d_hidden, "chunk": p.chunk, "eta": p.eta}
+        if backward:
+            cfg["pass"] = "backward"
         dtype = DTYPES["inplace"]
     else:
         x = make_lact_inputs(p, k)
@@ -396,7 +428,9 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu", backward=Fals
         rec["timing"] = f"flushed: a {flush_bytes >> 20} MiB buffer read before each timed step"
         rec["warm"] = {"ms_per_step": round(ms_warm, 4), "value": round(tokens / (ms_warm * 1e-3), 1)}
     if cpu:
-        if k == 4:
+        if k == 4 and backward:
+            rec["cpu_baseline"] = cpu_baseline_inplace_backward(p, x)
+        elif k == 4:
             rec["cpu_baseline"] = cpu_baseline_inplace(p, x, args.cpu_seconds)
         elif k == 1 and backward:
             rec["cpu_baseline"] = cpu_baseline_linattn_backward(p, x, args.cpu_seconds)
@@ -414,8 +448,12 @@ def main():
               "(sequence, head) pairs shard across GPUs without communication, see DESIGN.md",
               file=sys.stderr)
         sys.exit(2)
-    if (args.momentum != 0.0 or args.feature_map != "swiglu" or args.backward) and args.config != 1:
-        print("--momentum, --feature-map and --backward apply to the scan workload (--config 1) only", file=sys.stderr)
+    if (args.momentum != 0.0 or args.feature_map != "swiglu") and args.config != 1:
+        print("--momentum and --feature-map apply to the scan workload (--config 1) only", file=sys.stderr)
+        sys.exit(2)
+    if args.backward and args.config not in (1, 4):
+        print("--backward applies to the scan workload (--config 1) and the In-Place update (--config 4)",
+              file=sys.stderr)
         sys.exit(2)
     if args.backward and args.feature_map != "swiglu":
         print("--backward is built for the SwiGLU feature map", file=sys.stderr)
@@ -434,7 +472,7 @@ def main():
     if args.config == 2 and not args.no_extras:
         others = {}
         for k, fm, bwd in ((1, "swiglu", False), (1, "identity", False), (1, "swiglu", True), (3, "swiglu", False),
-                           (4, "swiglu", False)):
+                           (4, "swiglu", False), (4, "swiglu", True)):
             r = measure(k, args, cpu=False, feature_map=fm, backward=bwd)
             others[r["config"]["workload"]] = {
                 "metric": r["metric"], "value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],

@@ -87,6 +87,14 @@ def inplace_flops(B, N, d_model, d_hidden) -> float:
     return B * 4 * 2.0 * N * d_model * d_hidden
 
 
+def inplace_backward_flops(B, N, d_model, d_hidden) -> float:
+    """The products the gradients need, each 2 N d_model d_hidden: the forward's Z (2) and the
+    chunk states (1) recomputed, dZ (2: through the chunk's own output and through the later
+    chunks' reads of its write), dVbar (1), the summed output gradient G (1), dHs (2) and the two
+    frozen projections' gradients (2): 11 per sequence."""
+    return B * 11 * 2.0 * N * d_model * d_hidden
+
+
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 / fp16 MFMA (AMD public figure)
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
@@ -111,7 +119,8 @@ KERNEL_SYMBOLS = {"lact_update": ("lact_update_kernel",), "lact_grad": ("grad_ws
                   "lact_apply": ("apply_rd_kernel",), "linattn_delta": ("grad_rd_kernel",),
                   "linattn_apply": ("apply_rd_kernel", "linattn_bwd_tok_kernel"), "linattn_scan": ("linattn_scan_kernel",),
                   "lact_update_apply": ("lact_update_apply_kernel",), "linattn_fused": ("linattn_fused_kernel",),
-                  "inplace_apply_z": ("gemm_big_pair_kernel",), "inplace_update": ("gemm_rmw_pp_kernel",)}
+                  "inplace_apply_z": ("gemm_big_pair_kernel",), "inplace_update": ("gemm_rmw_pp_kernel",),
+                  "inplace_swiglu_bwd": ("gemm_tn_kernelILi4E",)}
 
 
 def profiled_avg_us(root: str, kernel_class: str, stem: str):

@@ -969,7 +969,7 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
         g.Ct = bfp(odAt);
         g.Ct2 = bfp(odUt);
         g.ldct = C;
-        TTT_HIP(launch_k(K_INP_APPLY, gemm_tn_kernel<EPI_SWIGLU_BWD>, dim3((unsigned)(dh / BN), (unsigned)(C / BM)),
+        TTT_HIP(launch_k(K_INP_SWIGLU_BWD, gemm_tn_kernel<EPI_SWIGLU_BWD>, dim3((unsigned)(dh / BN), (unsigned)(C / BM)),
                          dim3(256), lds_bytes<EPI_SWIGLU_BWD>(), st, g));
       }
       TTT_HIP(zero(f32p(odHf), C * dm));
