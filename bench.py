@@ -292,9 +292,15 @@ def measure(k, args, momentum=0.0, cpu=True, feature_map="swiglu", backward=Fals
         Wd = t(x["W_down"], torch.float32)
 
         per = 2.0 * p.chunk * p.d_model * p.d_hidden  # one chunk-sized product
-        work = {"inplace_z": 2 * per, "inplace_apply": per, "inplace_update": per, "inplace_apply_z": 3 * per,
-                "inplace_swiglu_bwd": 2 * per}
+        work = {"inplace_z": 2 * per, "inplace_apply": per, "inplace_update": per, "inplace_apply_z": 3 * per}
         if backward:
+            nch = p.N // p.chunk
+            # per launch, averaged over a step: dZ is two products but one for the last chunk
+            # (no later chunk); the apply class holds dVbar (one product, all chunks but the last)
+            # and dH (two products); the weight gradients are one product over all chunks each
+            work.update({"inplace_swiglu_bwd": (2 * (nch - 1) + 1) * per / nch,
+                         "inplace_apply": ((nch - 1) + 2 * nch) * per / (2 * nch - 1),
+                         "inplace_wgrad": nch * per})
             dO = t(np.random.default_rng(12).standard_normal(x["Hs"].shape).astype(np.float32), torch.bfloat16)
             stem = "inplace_backward_d4096_dh14336_seq32768_chunk1024"
 

@@ -343,10 +343,11 @@ ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p,
  * bf16; dHs, dVbar [B, N, d_model] bf16; dW_gate, dW_up [d_hidden, d_model] float32 (summed over
  * the batch); dW_down [d_model, d_hidden] float32 (summed over the batch) or [B, d_model,
  * d_hidden] when wdown_batch_stride != 0. Shape rules as for the forward. TTT_BF16 only; a
- * target built from X0 (the LM-aligned target) returns TTT_ERR_UNSUPPORTED. The workspace holds
- * every chunk's Z (both orientations) and its state W_i^T in bf16: about
- * 2 N d_hidden + (N / chunk) d_model d_hidden bf16 elements plus a few d_model x d_hidden fp32
- * buffers (8 GB at d_model 4096, d_hidden 14336, N 32768, chunk 1024).
+ * target built from X0 (the LM-aligned target) returns TTT_ERR_UNSUPPORTED. The workspace holds,
+ * per sequence in turn, every chunk's Z (both orientations), gate and up products, the
+ * transposed dA and dU, and every chunk's state W_i^T, all bf16: about
+ * 6 N d_hidden + (N / chunk) d_model d_hidden bf16 elements plus a few d_model x d_hidden
+ * buffers (11.3 GB at d_model 4096, d_hidden 14336, N 32768, chunk 1024).
  * ---------------------------------------------------------------------------------------- */
 ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, const void* Hs, const void* W_gate,
                                      const void* W_up, const float* W_down, const void* Vbar, const void* dO,

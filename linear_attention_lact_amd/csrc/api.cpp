@@ -47,7 +47,7 @@ const char* kClassNames[K_NUM_CLASSES] = {
     "lact_init", "lact_grad", "lact_update", "lact_apply", "lact_final",
     "linattn_prep", "linattn_delta", "linattn_scan", "linattn_apply", "linattn_fused",
     "inplace_prep", "inplace_z", "inplace_apply", "inplace_update", "lact_update_apply",
-    "inplace_apply_z", "inplace_swiglu_bwd"};
+    "inplace_apply_z", "inplace_swiglu_bwd", "inplace_wgrad"};
 struct Rec { int cls; hipEvent_t a, b; };
 std::mutex mu;
 bool on = false;

@@ -28,22 +28,45 @@ struct Args {
   __bf16* Ct; int64_t ldct;         // SWIGLU transposed output [N][M]
   float* Wf; __bf16* Wsh; int64_t ldw;  // RMW state and shadow [M][N]
   float alpha;
-  // SWIGLU_BWD: the incoming gradient dZ [M][N] and the second pair of outputs (C, Ct: dA; C2,
-  // Ct2: dU, row-major and transposed like C / Ct)
-  const __bf16* dZ; int64_t lddz;
+  // Concatenated K (K1 > 0): K blocks k >= K1 read A2 / B2 at k - K1 (same leading dimensions),
+  // so C = A B^T + A2 B2^T in one product.
+  const __bf16* A2; const __bf16* B2; int K1;
+  // SWIGLU: when Ga is set, the gate and up products are also stored (bf16, [M][N], ld ldc).
+  // SWIGLU_BWD: the accumulator is dZ; Ga / Gu hold the stored gate and up products, and the
+  // outputs are dA (C, Ct) and dU (C2, Ct2), row-major [M][N] (ld ldc) and transposed (ld ldct).
+  __bf16* Ga; __bf16* Gu;
   __bf16* C2; __bf16* Ct2;
+  // RMW of the two-workgroups-per-CU kernel only: the shadow is bf16(shscale * W) (0 means 1),
+  // Wsh may be null, and Wsht (if set) receives the shadow transposed ([N][M], ld ldwt).
+  float shscale;
+  __bf16* Wsht; int64_t ldwt;
 };
+
+// operand base of the K block starting at k (concatenated-K products switch at K1)
+__device__ __forceinline__ const __bf16* a_at(const Args& g, int k) {
+  return (g.K1 > 0 && k >= g.K1) ? g.A2 + (k - g.K1) : g.A + k;
+}
+__device__ __forceinline__ const __bf16* b_at(const Args& g, int k) {
+  return (g.K1 > 0 && k >= g.K1) ? g.B2 + (k - g.K1) : g.B0 + k;
+}
+
+// dA = dZ * U * silu'(A), dU = dZ * silu(A) for the gate product a and the up product u
+__device__ __forceinline__ void swiglu_bwd(float dz, float a, float u, float& da, float& du) {
+  const float sg = sigmoidf_(a);
+  da = dz * u * (sg * (1.f + a * (1.f - sg)));
+  du = dz * a * sg;
+}
 
 template <int EPI>
 constexpr int lds_bytes() {
-  return (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD ? 3 : 2) * BM * LDS_LD * 2;
+  return (EPI == EPI_SWIGLU ? 3 : 2) * BM * LDS_LD * 2;
 }
 
 // grid: tiles of 128x128 (x over N tiles, y over M tiles). block 256 = 4 waves (2x2), each
 // wave a 64x64 quadrant = 2x2 MFMA tiles of 32x32.
 template <int EPI>
 __global__ void __launch_bounds__(256) gemm_tn_kernel(Args g) {
-  constexpr int NB = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD ? 2 : 1;
+  constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* As = reinterpret_cast<__bf16*>(smem);  // [BM][LDS_LD]
   __bf16* Bs = As + BM * LDS_LD;                 // [NB][BN][LDS_LD]
@@ -55,13 +78,14 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(Args g) {
   const int lr = tid >> 3, lc = (tid & 7) * 8;
   u32x4 ra[4], rb[NB][4];
   auto gload = [&](int k0) {
+    const __bf16* Ab = a_at(g, k0);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      ra[v] = *reinterpret_cast<const u32x4*>(g.A + (int64_t)(m0 + lr + 32 * v) * g.lda + k0 + lc);
+      ra[v] = *reinterpret_cast<const u32x4*>(Ab + (int64_t)(m0 + lr + 32 * v) * g.lda + lc);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const __bf16* Bp = b == 0 ? g.B0 : g.B1;
-        rb[b][v] = *reinterpret_cast<const u32x4*>(Bp + (int64_t)(n0 + lr + 32 * v) * g.ldb + k0 + lc);
+        const __bf16* Bp = b == 0 ? b_at(g, k0) : g.B1 + k0;
+        rb[b][v] = *reinterpret_cast<const u32x4*>(Bp + (int64_t)(n0 + lr + 32 * v) * g.ldb + lc);
       }
     }
   };
@@ -127,7 +151,12 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(Args g) {
             const int r = 4 * q + e;
             const float gt = acc[0][i][j][r], up = acc[1][i][j][r];
             zv[e] = static_cast<__bf16>(gt * sigmoidf_(gt) * up);
-            g.C[(int64_t)(mb + acc_row(r, lane)) * g.ldc + n] = zv[e];
+            const int64_t o = (int64_t)(mb + acc_row(r, lane)) * g.ldc + n;
+            g.C[o] = zv[e];
+            if (g.Ga) {
+              g.Ga[o] = static_cast<__bf16>(gt);
+              g.Gu[o] = static_cast<__bf16>(up);
+            }
           }
           // 4 consecutive rows m -> 4 consecutive elements of row n of the transposed copy
           __bf16* dst = g.Ct + (int64_t)n * g.ldct + mb + acc_row(4 * q, lane);
@@ -136,21 +165,19 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(Args g) {
           *reinterpret_cast<bf16x4*>(dst) = v4;
         }
       } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        // dA = dZ * U * silu'(A), dU = dZ * silu(A) for the products A (gate) and U (up)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           __bf16 da[4], du[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q + e;
-            const int64_t m = mb + acc_row(r, lane);
-            const float a = acc[0][i][j][r], u = acc[1][i][j][r];
-            const float dz = static_cast<float>(g.dZ[m * g.lddz + n]);
-            const float sg = sigmoidf_(a);
-            da[e] = static_cast<__bf16>(dz * u * (sg * (1.f + a * (1.f - sg))));
-            du[e] = static_cast<__bf16>(dz * a * sg);
-            g.C[m * g.ldc + n] = da[e];
-            g.C2[m * g.ldc + n] = du[e];
+            const int64_t o = (int64_t)(mb + acc_row(r, lane)) * g.ldc + n;
+            float fa, fu;
+            swiglu_bwd(acc[0][i][j][r], static_cast<float>(g.Ga[o]), static_cast<float>(g.Gu[o]), fa, fu);
+            da[e] = static_cast<__bf16>(fa);
+            du[e] = static_cast<__bf16>(fu);
+            g.C[o] = da[e];
+            g.C2[o] = du[e];
           }
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const int64_t to = (int64_t)n * g.ldct + mb + acc_row(4 * q, lane);
@@ -219,24 +246,26 @@ __device__ __forceinline__ void gemm_big_body(const Args& g, int ksplit, float* 
   // staging: instruction j of wave w fills rows 32w + 8j .. +8 of each operand tile; lane l
   // takes row + l/8 and LDS chunk l%8
   const int lr = lane >> 3;
-  const __bf16* asrc[4];
-  const __bf16* bsrc[4];
+  int64_t aoff[4], boff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 32 * w + 8 * j + lr;
     const int ch = chunk_pos(lane & 7, row);
-    asrc[j] = g.A + (int64_t)(m0 + row) * g.lda + kbeg + ch * 8;
+    aoff[j] = (int64_t)(m0 + row) * g.lda + ch * 8;
     // B tile rows: SwiGLU rows 0..127 gate, 128..255 up (same hidden units n0..n0+127)
-    bsrc[j] = SW ? (row < 128 ? g.B0 : g.B1) + (int64_t)(n0 + (row & 127)) * g.ldb + kbeg + ch * 8
-                 : g.B0 + (int64_t)(n0 + row) * g.ldb + kbeg + ch * 8;
+    boff[j] = (int64_t)(n0 + (SW ? (row & 127) : row)) * g.ldb + ch * 8;
   }
   auto issue = [&](int kb, int stage) {
     unsigned char* sa = smem + stage * STAGE + (32 * w) * ROWB;
     unsigned char* sb = smem + stage * STAGE + (BM + 32 * w) * ROWB;
+    const int k = kbeg + kb * BK;
+    const __bf16* Ab = a_at(g, k);
+    // SwiGLU: waves 0-3 stage gate rows, waves 4-7 up rows
+    const __bf16* Bb = SW ? (w < 4 ? g.B0 : g.B1) + k : b_at(g, k);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_global_load_lds(asrc[j] + kb * BK, sa + 8 * j * ROWB, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bsrc[j] + kb * BK, sb + 8 * j * ROWB, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Ab + aoff[j], sa + 8 * j * ROWB, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Bb + boff[j], sb + 8 * j * ROWB, 16, 0, 0);
     }
   };
 
@@ -317,7 +346,7 @@ __device__ __forceinline__ void gemm_big_body(const Args& g, int ksplit, float* 
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         const bf16x4 s4 = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
                            static_cast<__bf16>(v[3])};
-        *reinterpret_cast<bf16x4*>(g.Wsh + idx) = s4;
+        if (g.Wsh) *reinterpret_cast<bf16x4*>(g.Wsh + idx) = s4;
       }
       __syncthreads();
     }
@@ -338,11 +367,42 @@ __device__ __forceinline__ void gemm_big_body(const Args& g, int ksplit, float* 
           const int r = 4 * q + e;
           const float gt = acc[i][0][r], up = acc[i][1][r];
           zv[e] = static_cast<__bf16>(gt * sigmoidf_(gt) * up);
-          g.C[(int64_t)(mb + acc_row(r, lane)) * g.ldc + n] = zv[e];
+          const int64_t o = (int64_t)(mb + acc_row(r, lane)) * g.ldc + n;
+          g.C[o] = zv[e];
+          if (g.Ga) {
+            g.Ga[o] = static_cast<__bf16>(gt);
+            g.Gu[o] = static_cast<__bf16>(up);
+          }
         }
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         const bf16x4 v4 = {zv[0], zv[1], zv[2], zv[3]};
         *reinterpret_cast<bf16x4*>(g.Ct + (int64_t)n * g.ldct + mb + acc_row(4 * q, lane)) = v4;
+      }
+    } else if constexpr (EPI == gemm::EPI_SWIGLU_BWD) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + 32 * j + acc_col(lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __bf16 da[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q + e;
+            const int64_t o = (int64_t)(mb + acc_row(r, lane)) * g.ldc + n;
+            float fa, fu;
+            gemm::swiglu_bwd(acc[i][j][r], static_cast<float>(g.Ga[o]), static_cast<float>(g.Gu[o]), fa, fu);
+            da[e] = static_cast<__bf16>(fa);
+            du[e] = static_cast<__bf16>(fu);
+            g.C[o] = da[e];
+            g.C2[o] = du[e];
+          }
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const int64_t to = (int64_t)n * g.ldct + mb + acc_row(4 * q, lane);
+          *reinterpret_cast<bf16x4*>(g.Ct + to) = bf16x4{da[0], da[1], da[2], da[3]};
+          *reinterpret_cast<bf16x4*>(g.Ct2 + to) = bf16x4{du[0], du[1], du[2], du[3]};
+        }
+        // keeps the compiler from hoisting every tile's operand loads ahead (register spills)
+        asm volatile("" ::: "memory");
       }
     } else {
 #pragma unroll
@@ -414,8 +474,15 @@ inline int choose_ksplit(const Args& g, int tiles) {
 // workgroup's fp32 read-modify-write epilogue overlaps the other's products.
 constexpr int PP_BN = 128;
 constexpr int PP_LDS = (BM + PP_BN) * ROWB;  // 48 KB
+constexpr int PP_LDE = PP_BN + 4;            // padded fp32 row of the epilogue tile
+constexpr int PP_LDT = 64 + 2;               // transposed-shadow tile row (bf16)
+// with a transposed shadow: the epilogue tile, then the transposed bf16 tile [128][PP_LDT]
+constexpr int PP_LDS_T = 64 * PP_LDE * 4 + PP_BN * PP_LDT * 2;
+static_assert(PP_LDS_T <= 80 * 1024, "two workgroups per CU");
 
-__global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
+// TSH: also the scaled and transposed shadows (Args::shscale, Args::Wsht); Wsh may be null.
+template <bool TSH>
+__global__ void __launch_bounds__(256, 2) gemm_rmw_pp_kernel(Args g) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
@@ -477,8 +544,10 @@ __global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
   }
   // W += alpha * acc through LDS in four passes of 64 rows (16-byte runs of the fp32 state); the
   // state rows of pass p + 1 are requested as soon as pass p has consumed its own
-  constexpr int LDE = PP_BN + 4;
+  constexpr int LDE = PP_LDE;
   float* ep = reinterpret_cast<float*>(smem);
+  __bf16* tp = reinterpret_cast<__bf16*>(smem + 64 * LDE * 4);  // [PP_BN][PP_LDT] transposed shadow
+  const float shs = !TSH || g.shscale == 0.f ? 1.f : g.shscale;
   auto pass_rmw = [&](int pass) {
     if (wm == (pass >> 1)) {
 #pragma unroll
@@ -500,11 +569,24 @@ __global__ void __launch_bounds__(256) gemm_rmw_pp_kernel(Args g) {
       const int64_t idx = (int64_t)(m0 + 64 * pass + row) * g.ldw + n0 + c4;
       *reinterpret_cast<f32x4*>(g.Wf + idx) = v;
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      const bf16x4 s4 = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                         static_cast<__bf16>(v[3])};
-      *reinterpret_cast<bf16x4*>(g.Wsh + idx) = s4;
+      const bf16x4 s4 = {static_cast<__bf16>(shs * v[0]), static_cast<__bf16>(shs * v[1]),
+                         static_cast<__bf16>(shs * v[2]), static_cast<__bf16>(shs * v[3])};
+      if (!TSH || g.Wsh) *reinterpret_cast<bf16x4*>(g.Wsh + idx) = s4;
+      if (TSH && g.Wsht) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tp[(c4 + e) * PP_LDT + row] = s4[e];
+      }
     }
     if (pass + 1 < 4) loadw(pass + 1, wv);
+    if (TSH && g.Wsht) {  // the pass's 64 x 128 shadow tile, transposed: 128 rows of 64 bf16 (4 bytes per thread step)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int f = tid + 256 * q, n = f >> 5, m2 = (f & 31) * 2;
+        *reinterpret_cast<uint32_t*>(g.Wsht + (int64_t)(n0 + n) * g.ldwt + m0 + 64 * pass + m2) =
+            *reinterpret_cast<const uint32_t*>(tp + n * PP_LDT + m2);
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the staging area is rewritten next
   };
 #pragma unroll
@@ -594,7 +676,7 @@ static hipError_t run_gemm(int cls, const gemm::Args& g, int ksplit, float* part
   if (EPI == gemm::EPI_RMW && g.M % gemm2::BM == 0 && g.N % gemm2::PP_BN == 0 && g.K % gemm2::BK == 0 &&
       g.K >= gemm2::BK) {
     const unsigned tiles = (unsigned)((g.M / gemm2::BM) * (g.N / gemm2::PP_BN));
-    return launch_k(cls, gemm2::gemm_rmw_pp_kernel, dim3(tiles), dim3(256), gemm2::PP_LDS, st, g);
+    return launch_k(cls, gemm2::gemm_rmw_pp_kernel<false>, dim3(tiles), dim3(256), gemm2::PP_LDS, st, g);
   }
   if (gemm2::fits<EPI>(g)) {
     const unsigned tiles = (unsigned)((g.M / gemm2::BM) * (g.N / gemm2::tile_n<EPI>()));
@@ -672,7 +754,7 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_RMW>, gemm2::LDS);
-    if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel, gemm2::PP_LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel<false>, gemm2::PP_LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, gemm2::LDS);
     return e;
   }();
@@ -799,12 +881,19 @@ extern "C" ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p, cons
 }
 
 // ---------------------------------------------------------------------------------------------
-// Backward of the In-Place update: two sweeps per sequence over the chunks, every product a TN
-// GEMM of the kernels above. Forward sweep: each chunk's Z, Z^T and the transposed state W_i^T
-// (bf16) are kept. Reverse sweep with R = sum_{k > i} dO_k^T Z_k kept in both orientations:
-//   dZ_i = dO_i W_i + eta Vbar_i R,  dVbar_i = eta Z_i R^T,  R += dO_i^T Z_i,
-//   dA, dU from dZ_i (SwiGLU backward epilogue on the recomputed gate and up products),
-//   dH_i = dA W_gate + dU W_up,  dW_gate += dA^T H_i,  dW_up += dU^T H_i;  dW_down = R at the end.
+// Backward of the In-Place update, per sequence in two sweeps over the chunks, every product a TN
+// GEMM of the kernels above. With G_i = dO_i^T Z_i and R_i = sum_{k > i} G_k:
+//   dZ_i = dO_i W_i + eta Vbar_i R_i,  dVbar_i = eta Z_i R_i^T,  dW_down = sum_i G_i,
+//   dA = dZ * U * silu'(A), dU = dZ * silu(A),  dH_i = dA W_gate + dU W_up,
+//   dW_gate = sum_i dA_i^T H_i,  dW_up = sum_i dU_i^T H_i.
+// Forward sweep: Z_i (token-major and transposed), the gate and up products A_i, U_i and the
+// transposed states W_i^T (bf16) are kept. Reverse sweep per chunk: dZ_i as one product over the
+// concatenated K [dO_i | Vbar_i] x [W_i^T | eta R^T]^T whose epilogue applies the SwiGLU backward
+// to the stored A_i, U_i and writes dA, dU token-major and transposed (the transposed copies of all
+// chunks are kept); dVbar_i against the bf16 shadow of eta R (K split); R += dO_i^T Z_i in fp32
+// with both bf16 shadows (eta R and eta R^T, the transposed one from the epilogue); dH_i over the
+// concatenated K [dA | dU] x [W_gate^T | W_up^T]^T (K split). After the sweep, dW_gate and dW_up are
+// one product each over all tokens of the sequence (K = N), accumulated in fp32 over sequences.
 extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, const void* Hs, const void* W_gate,
                                                 const void* W_up, const float* W_down, const void* Vbar,
                                                 const void* dO, void* dHs, float* dW_gate, float* dW_up,
@@ -824,17 +913,27 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
   if (q.B > 0 && (!W_down || !dW_down || !dW_gate || !dW_up)) return TTT_ERR_ARG;
   if (q.B > 0 && N > 0 && (!Hs || !W_gate || !W_up || !Vbar || !dO || !dHs || !dVbar)) return TTT_ERR_ARG;
   const int nch = (int)(N / C);
+  // K splits of the two token-major products whose K is d_hidden-long (dVbar: K = d_hidden, dH:
+  // K = 2 d_hidden), chosen as for the forward's apply
+  auto ks_of = [&](int64_t K) {
+    Args t{};
+    t.M = (int)C;
+    t.N = (int)dm;
+    t.K = (int)K;
+    if (!gemm2::fits<EPI_STORE>(t)) return 1;
+    return gemm2::choose_ksplit(t, (int)((C / gemm2::BM) * (dm / gemm2::BN)));
+  };
+  const int ks_dv = ks_of(dh), ks_dh = ks_of(2 * dh);
   WorkspacePlan plan;
-  const size_t oZ = plan.add((size_t)nch * C * dh * 2), oZt = plan.add((size_t)nch * C * dh * 2);
+  const size_t oZ = plan.add((size_t)N * dh * 2), oZt = plan.add((size_t)N * dh * 2);  // per chunk [C][dh], [dh][C]
+  const size_t oGa = plan.add((size_t)N * dh * 2), oGu = plan.add((size_t)N * dh * 2);
   const size_t oWtSh = plan.add((size_t)nch * nW * 2), oWt = plan.add((size_t)nW * 4);
-  const size_t oR = plan.add((size_t)nW * 4), oRsh = plan.add((size_t)nW * 2);
-  const size_t oRt = plan.add((size_t)nW * 4), oRtsh = plan.add((size_t)nW * 2);
-  const size_t odZf = plan.add((size_t)C * dh * 4), odZ = plan.add((size_t)C * dh * 2);
-  const size_t odA = plan.add((size_t)C * dh * 2), odAt = plan.add((size_t)C * dh * 2);
-  const size_t odU = plan.add((size_t)C * dh * 2), odUt = plan.add((size_t)C * dh * 2);
-  const size_t odVf = plan.add((size_t)C * dm * 4), odHf = plan.add((size_t)C * dm * 4);
+  const size_t oR = plan.add((size_t)nW * 4), oRsh = plan.add((size_t)nW * 2), oRtsh = plan.add((size_t)nW * 2);
+  const size_t odA = plan.add((size_t)C * dh * 2), odU = plan.add((size_t)C * dh * 2);
+  const size_t odAt = plan.add((size_t)dh * N * 2), odUt = plan.add((size_t)dh * N * 2);  // [dh][N]
+  const size_t oPart = plan.add((size_t)std::max(ks_dv, ks_dh) * C * dm * 4);
   const size_t oVt = plan.add((size_t)dm * N * 2), odOt = plan.add((size_t)dm * N * 2), oHt = plan.add((size_t)dm * N * 2);
-  const size_t oWgT = plan.add((size_t)nW * 2), oWuT = plan.add((size_t)nW * 2), oSink = plan.add((size_t)nW * 2);
+  const size_t oWgT = plan.add((size_t)nW * 2), oWuT = plan.add((size_t)nW * 2);
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -851,8 +950,11 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
     if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_STORE>, lds_bytes<EPI_STORE>());
     if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_RMW>, lds_bytes<EPI_RMW>());
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU_BWD>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel<true>, gemm2::PP_LDS_T);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_RMW>, gemm2::LDS);
-    if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel, gemm2::PP_LDS);
     return e;
   }();
   TTT_HIP(lds_ok);
@@ -861,8 +963,10 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
     hipLaunchKernelGGL(f32_zero_add_kernel, dim3(1024), dim3(256), 0, st, d, static_cast<const float*>(nullptr), n, 0);
     return hipGetLastError();
   };
+  // fp32 read-modify-write W += alpha A B^T (two workgroups per CU; every shape here fits it)
   auto rmw = [&](const __bf16* A, int64_t lda, const __bf16* B, int64_t ldb, int64_t M, int64_t Nn, int64_t K, float* Wf,
-                 __bf16* Wsh, int64_t ldw, float alpha) -> hipError_t {
+                 __bf16* Wsh, float alpha, float shs = 1.f, __bf16* Wsht = nullptr,
+                 int cls = K_INP_UPDATE) -> hipError_t {
     Args u{};
     u.A = A;
     u.lda = lda;
@@ -873,9 +977,36 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
     u.K = (int)K;
     u.Wf = Wf;
     u.Wsh = Wsh;
-    u.ldw = ldw;
+    u.ldw = Nn;
     u.alpha = alpha;
-    return run_gemm<EPI_RMW>(K_INP_UPDATE, u, 1, nullptr, st);
+    u.shscale = shs;
+    u.Wsht = Wsht;
+    u.ldwt = M;
+    if (K > 16 * C) {  // a long K (the weight gradients over a whole sequence): the double-buffered kernel
+      const unsigned tiles = (unsigned)((M / gemm2::BM) * (Nn / gemm2::BN));
+      return launch_k(cls, gemm2::gemm_big_kernel<EPI_RMW>, dim3(tiles), dim3(gemm2::THREADS), gemm2::LDS, st, u, 1,
+                      static_cast<float*>(nullptr));
+    }
+    const unsigned tiles = (unsigned)((M / gemm2::BM) * (Nn / gemm2::PP_BN));
+    return launch_k(cls, gemm2::gemm_rmw_pp_kernel<true>, dim3(tiles), dim3(256), gemm2::PP_LDS_T, st, u);
+  };
+  // bf16 C [M][Nn] = A B^T (+ A2 B2^T over the concatenated K), K-split through fp32 partials
+  auto store = [&](const __bf16* A, const __bf16* B, const __bf16* A2, const __bf16* B2, int64_t lda, int64_t K1,
+                   int64_t K, int64_t Nn, __bf16* Cout, int ks) -> hipError_t {
+    Args t{};
+    t.A = A;
+    t.lda = lda;
+    t.B0 = B;
+    t.ldb = lda;
+    t.A2 = A2;
+    t.B2 = B2;
+    t.K1 = (int)K1;
+    t.M = (int)C;
+    t.N = (int)Nn;
+    t.K = (int)K;
+    t.C = Cout;
+    t.ldc = Nn;
+    return run_gemm<EPI_STORE>(K_INP_APPLY, t, ks, f32p(oPart), st);
   };
   const __bf16* Wg = static_cast<const __bf16*>(W_gate);
   const __bf16* Wu = static_cast<const __bf16*>(W_up);
@@ -897,7 +1028,6 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
     __bf16* dHb = static_cast<__bf16*>(dHs) + (int64_t)b * N * dm;
     __bf16* dVb = static_cast<__bf16*>(dVbar) + (int64_t)b * N * dm;
     float* R = f32p(oR);
-    float* Rt = f32p(oRt);
     if (nch == 0) {
       if (!shared) TTT_HIP(zero(dW_down + (int64_t)b * nW, nW));
       continue;
@@ -912,10 +1042,10 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
                          W_down + (int64_t)b * q.wdown_batch_stride, f32p(oWt), bfp(oWtSh), (int)dm, (int)dh);
       TTT_HIP(hipGetLastError());
       TTT_HIP(zero(R, nW));
-      TTT_HIP(zero(Rt, nW));
     }
-    // forward sweep: Z_i, Z_i^T and the states W_i^T (bf16)
+    // forward sweep: Z_i, Z_i^T, A_i, U_i and the states W_i^T (bf16)
     for (int i = 0; i < nch; ++i) {
+      const int64_t zo = (int64_t)i * C * dh;
       Args z{};
       z.A = Hb + (int64_t)i * C * dm;
       z.lda = dm;
@@ -925,59 +1055,58 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
       z.M = (int)C;
       z.N = (int)dh;
       z.K = (int)dm;
-      z.C = bfp(oZ) + (int64_t)i * C * dh;
+      z.C = bfp(oZ) + zo;
       z.ldc = dh;
-      z.Ct = bfp(oZt) + (int64_t)i * C * dh;
+      z.Ct = bfp(oZt) + zo;
       z.ldct = C;
+      z.Ga = bfp(oGa) + zo;
+      z.Gu = bfp(oGu) + zo;
       TTT_HIP(run_gemm<EPI_SWIGLU>(K_INP_Z, z, 1, nullptr, st));
       if (i + 1 < nch)  // W_{i+1}^T = W_i^T + eta Z_i^T Vbar_i
-        TTT_HIP(rmw(bfp(oZt) + (int64_t)i * C * dh, C, bfp(oVt) + (int64_t)i * C, N, dh, dm, C, f32p(oWt),
-                    bfp(oWtSh) + (int64_t)(i + 1) * nW, dm, q.eta));
+        TTT_HIP(rmw(bfp(oZt) + zo, C, bfp(oVt) + (int64_t)i * C, N, dh, dm, C, f32p(oWt),
+                    bfp(oWtSh) + (int64_t)(i + 1) * nW, q.eta));
     }
     // reverse sweep
     for (int i = nch - 1; i >= 0; --i) {
-      const int64_t t0 = (int64_t)i * C;
-      const __bf16* Zi = bfp(oZ) + (int64_t)i * C * dh;
-      const __bf16* Zti = bfp(oZt) + (int64_t)i * C * dh;
-      const bool later = i + 1 < nch;  // R holds the writes' gradient of later chunks
-      TTT_HIP(zero(f32p(odZf), C * dh));
-      TTT_HIP(rmw(dOb + t0 * dm, dm, bfp(oWtSh) + (int64_t)i * nW, dm, C, dh, dm, f32p(odZf), bfp(odZ), dh, 1.f));
-      if (later) {
-        TTT_HIP(rmw(Vb + t0 * dm, dm, bfp(oRtsh), dm, C, dh, dm, f32p(odZf), bfp(odZ), dh, q.eta));
-        TTT_HIP(zero(f32p(odVf), C * dm));
-        TTT_HIP(rmw(Zi, dh, bfp(oRsh), dh, C, dm, dh, f32p(odVf), dVb + t0 * dm, dm, q.eta));
-      } else {
-        TTT_HIP(zero(reinterpret_cast<float*>(dVb + t0 * dm), C * dm / 2));  // no later chunk reads its write
-      }
-      TTT_HIP(rmw(bfp(odOt) + t0, N, Zti, C, dm, dh, C, R, bfp(oRsh), dh, 1.f));
-      TTT_HIP(rmw(Zti, C, bfp(odOt) + t0, N, dh, dm, C, Rt, bfp(oRtsh), dm, 1.f));
+      const int64_t t0 = (int64_t)i * C, zo = (int64_t)i * C * dh;
+      const bool later = i + 1 < nch;  // R (the later chunks' gradient) is nonzero
       {
         Args g{};
-        g.A = Hb + t0 * dm;
+        g.A = dOb + t0 * dm;
         g.lda = dm;
-        g.B0 = Wg;
-        g.B1 = Wu;
+        g.B0 = bfp(oWtSh) + (int64_t)i * nW;
         g.ldb = dm;
+        if (later) {
+          g.A2 = Vb + t0 * dm;
+          g.B2 = bfp(oRtsh);  // bf16(eta R^T)
+          g.K1 = (int)dm;
+        }
         g.M = (int)C;
         g.N = (int)dh;
-        g.K = (int)dm;
-        g.dZ = bfp(odZ);
-        g.lddz = dh;
+        g.K = (int)(later ? 2 * dm : dm);
+        g.Ga = bfp(oGa) + zo;
+        g.Gu = bfp(oGu) + zo;
         g.C = bfp(odA);
         g.C2 = bfp(odU);
         g.ldc = dh;
-        g.Ct = bfp(odAt);
-        g.Ct2 = bfp(odUt);
-        g.ldct = C;
-        TTT_HIP(launch_k(K_INP_SWIGLU_BWD, gemm_tn_kernel<EPI_SWIGLU_BWD>, dim3((unsigned)(dh / BN), (unsigned)(C / BM)),
-                         dim3(256), lds_bytes<EPI_SWIGLU_BWD>(), st, g));
+        g.Ct = bfp(odAt) + t0;
+        g.Ct2 = bfp(odUt) + t0;
+        g.ldct = N;
+        TTT_HIP(run_gemm<EPI_SWIGLU_BWD>(K_INP_SWIGLU_BWD, g, 1, nullptr, st));
       }
-      TTT_HIP(zero(f32p(odHf), C * dm));
-      TTT_HIP(rmw(bfp(odA), dh, bfp(oWgT), dh, C, dm, dh, f32p(odHf), dHb + t0 * dm, dm, 1.f));
-      TTT_HIP(rmw(bfp(odU), dh, bfp(oWuT), dh, C, dm, dh, f32p(odHf), dHb + t0 * dm, dm, 1.f));
-      TTT_HIP(rmw(bfp(odAt), C, bfp(oHt) + t0, N, dh, dm, C, dW_gate, bfp(oSink), dm, 1.f));
-      TTT_HIP(rmw(bfp(odUt), C, bfp(oHt) + t0, N, dh, dm, C, dW_up, bfp(oSink), dm, 1.f));
+      if (later) {  // dVbar_i = Z_i bf16(eta R)^T
+        TTT_HIP(store(bfp(oZ) + zo, bfp(oRsh), nullptr, nullptr, dh, 0, dh, dm, dVb + t0 * dm, ks_dv));
+      } else {
+        TTT_HIP(zero(reinterpret_cast<float*>(dVb + t0 * dm), C * dm / 2));  // no later chunk reads its write
+      }
+      // R += dO_i^T Z_i (shadows eta R and eta R^T for the earlier chunks)
+      TTT_HIP(rmw(bfp(odOt) + t0, N, bfp(oZt) + zo, C, dm, dh, C, R, bfp(oRsh), 1.f, q.eta, bfp(oRtsh)));
+      // dH_i = dA W_gate + dU W_up
+      TTT_HIP(store(bfp(odA), bfp(oWgT), bfp(odU), bfp(oWuT), dh, dh, 2 * dh, dm, dHb + t0 * dm, ks_dh));
     }
+    // dW_gate += dA^T H, dW_up += dU^T H over all tokens of the sequence
+    TTT_HIP(rmw(bfp(odAt), N, bfp(oHt), N, dh, dm, N, dW_gate, nullptr, 1.f, 1.f, nullptr, K_INP_WGRAD));
+    TTT_HIP(rmw(bfp(odUt), N, bfp(oHt), N, dh, dm, N, dW_up, nullptr, 1.f, 1.f, nullptr, K_INP_WGRAD));
     if (shared) {
       hipLaunchKernelGGL(f32_zero_add_kernel, dim3(1024), dim3(256), 0, st, dW_down, static_cast<const float*>(R), nW, 1);
       TTT_HIP(hipGetLastError());

@@ -13,7 +13,8 @@ enum KernelClass {
   K_INP_PREP, K_INP_Z, K_INP_APPLY, K_INP_UPDATE,
   K_LACT_UPD_APPLY,  // weight update and the chunk's apply in one launch
   K_INP_APPLY_Z,     // In-Place apply of a chunk and the next chunk's Z in one launch
-  K_INP_SWIGLU_BWD,  // In-Place backward: the gate and up products with the SwiGLU-backward epilogue
+  K_INP_SWIGLU_BWD,  // In-Place backward: dZ with the SwiGLU-backward epilogue
+  K_INP_WGRAD,       // In-Place backward: the gate and up projections' gradients over a sequence
   K_NUM_CLASSES
 };
 
