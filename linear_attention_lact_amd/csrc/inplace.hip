@@ -954,6 +954,7 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel<true>, gemm2::PP_LDS_T);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel<false>, gemm2::PP_LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_RMW>, gemm2::LDS);
     return e;
   }();
@@ -988,6 +989,8 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
                       static_cast<float*>(nullptr));
     }
     const unsigned tiles = (unsigned)((M / gemm2::BM) * (Nn / gemm2::PP_BN));
+    if (!Wsht && Wsh && shs == 1.f)  // a plain update: the forward's instance (no spills)
+      return launch_k(cls, gemm2::gemm_rmw_pp_kernel<false>, dim3(tiles), dim3(256), gemm2::PP_LDS, st, u);
     return launch_k(cls, gemm2::gemm_rmw_pp_kernel<true>, dim3(tiles), dim3(256), gemm2::PP_LDS_T, st, u);
   };
   // bf16 C [M][Nn] = A B^T (+ A2 B2^T over the concatenated K), K-split through fp32 partials
