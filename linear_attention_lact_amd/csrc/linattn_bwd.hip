@@ -509,10 +509,12 @@ extern "C" ttt_status ttt_linattn_backward(const ttt_linattn_params* p, const vo
   if (P == 0) return TTT_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int nw = q.w_batch_stride == 0 ? q.H : P;  // weight slots
-  if (nch == 0) {  // no tokens: every gradient is zero
-    if (dW0) TTT_HIP(hipMemsetAsync(dW0, 0, (size_t)nw * n * 4, st));
-    if (dW2) TTT_HIP(hipMemsetAsync(dW2, 0, (size_t)nw * n * 4, st));
-    if (dW1) TTT_HIP(hipMemsetAsync(dW1, 0, (size_t)nw * n * 4, st));
+  if (nch == 0) {  // no tokens: every gradient is zero (a fill kernel: safe under graph capture)
+    for (float* d : {dW0, dW2, dW1}) {
+      if (!d) continue;
+      hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((nw * n + 255) / 256)), dim3(256), 0, st, d, 0.f, (int64_t)nw * n);
+      TTT_HIP(hipGetLastError());
+    }
     return TTT_OK;
   }
   char* ws = static_cast<char*>(workspace);

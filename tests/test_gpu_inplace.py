@@ -199,3 +199,20 @@ def test_backward_full_size_sampled_units(lib):
     again = _gpu_bwd(lib, p, x, dO)
     for k in BWD_NAMES:
         assert torch.equal(got[k], again[k]), k
+
+
+@pytest.mark.parametrize("per_seq", [False, True])
+def test_backward_empty_sequence(lib, per_seq):
+    """No tokens: every weight gradient is exactly zero (shared or per-sequence W_down)."""
+    p = InplaceProblem(B=2, N=256, d_model=256, d_hidden=512, chunk=128, eta=1e-3)
+    announce(f"inplace backward empty sequence per_seq={per_seq}")
+    x = make_inplace_inputs(p, 650)
+    for k in ("Hs", "Vbar"):
+        x[k] = x[k][:, :0]
+    dO = np.zeros((2, 0, 256), np.float32)
+    Wd = np.stack([x["W_down"]] * 2) if per_seq else x["W_down"]
+    got = _gpu_bwd(lib, p.replace(N=0), x, dO, W_down=Wd)
+    assert tuple(got["dW_down"].shape) == Wd.shape
+    for k in ("dW_gate", "dW_up", "dW_down"):
+        assert not bool(got[k].any()), k
+    assert got["dHs"].numel() == 0 and got["dVbar"].numel() == 0

@@ -92,3 +92,24 @@ def test_scan_workload_shape(lib):
     again, _ = _run(lib, p, x, dO)
     for k in NAMES:
         assert torch.equal(got[k], again[k]), k
+
+
+@pytest.mark.parametrize("per_seq", [False, True])
+def test_empty_sequence_gives_zero_weight_gradients(lib, per_seq):
+    """No tokens: the weight gradients are exactly zero (per-sequence or shared shapes) and the
+    token gradients are empty."""
+    import torch
+    p = LactProblem(B=2, H=2, h=64, r=2, Nq=256, Nk=256, chunk_q=128, chunk_kv=128, dtype=BF16, weight_norm=False)
+    announce(f"linattn backward empty sequence per_seq={per_seq}")
+    x = make_lact_inputs(p, 840)
+    empty = {k: x[k][:, :, :0] for k in ("Q", "K", "V", "eta")}
+    y = dict(x, **empty)
+    dO = np.zeros((2, 2, 0, 64), np.float32)
+    got, W = _run(lib, LactProblem(B=2, H=2, h=64, r=2, Nq=0, Nk=0, chunk_q=128, chunk_kv=128, dtype=BF16,
+                                   weight_norm=False), y, dO, per_seq=per_seq)
+    for k in ("dW0", "dW2", "dW1"):
+        assert tuple(got[k].shape) == W[k.replace("d", "", 1)].shape
+        assert not bool(got[k].any()), k
+    for k in ("dQ", "dK", "dV", "deta"):
+        assert got[k].numel() == 0
+    torch.cuda.synchronize()
