@@ -221,6 +221,10 @@ constexpr int ROWB = BK * 2;                    // bytes per staged row
 constexpr int STAGE = (BM + BN) * ROWB;         // 64 KB: A rows, then B rows
 constexpr int LDS = 2 * STAGE;
 constexpr int THREADS = 512;
+constexpr int BWD_LDR = BN + 8;                 // SwiGLU-backward epilogue: padded bf16 row
+constexpr int BWD_LDS = 4 * 64 * BWD_LDR * 2;   // its four staged 64-row tiles (132 KB)
+template <int EPI>
+constexpr int lds_of() { return EPI == gemm::EPI_SWIGLU_BWD && BWD_LDS > LDS ? BWD_LDS : LDS; }
 constexpr int EPI_PARTIAL = 3;                  // fp32 partial of one K split
 
 template <int EPI>
@@ -310,6 +314,68 @@ __device__ __forceinline__ void gemm_big_body(const Args& g, int ksplit, float* 
     if (kb + 2 < nkb) issue(kb + 2, kb & 1);
   }
 
+  if constexpr (EPI == gemm::EPI_SWIGLU_BWD) {
+    // dA, dU through LDS in four passes of 64 rows: the stored gate and up products are read and
+    // the token-major outputs written in 16-byte runs; the transposed outputs go out from the
+    // accumulators (four consecutive rows per lane, 8-byte stores)
+    constexpr int LDR = BWD_LDR;
+    __bf16* gaS = reinterpret_cast<__bf16*>(smem);  // [64][LDR] each
+    __bf16* guS = gaS + 64 * LDR;
+    __bf16* daS = guS + 64 * LDR;
+    __bf16* duS = daS + 64 * LDR;
+    const int tid = threadIdx.x;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int r0 = m0 + 64 * pass;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = tid + THREADS * q, row = f >> 5, c8 = (f & 31) * 8;
+        const int64_t o = (int64_t)(r0 + row) * g.ldc + n0 + c8;
+        *reinterpret_cast<u32x4*>(gaS + row * LDR + c8) = *reinterpret_cast<const u32x4*>(g.Ga + o);
+        *reinterpret_cast<u32x4*>(guS + row * LDR + c8) = *reinterpret_cast<const u32x4*>(g.Gu + o);
+      }
+      __syncthreads();
+      if (wm == (pass >> 1)) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * (pass & 1) + ii;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int cl = wn * 64 + 32 * j + acc_col(lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              __bf16 da[4], du[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q + e, lo = (32 * ii + acc_row(r, lane)) * LDR + cl;
+                float fa, fu;
+                gemm::swiglu_bwd(acc[i][j][r], static_cast<float>(gaS[lo]), static_cast<float>(guS[lo]), fa, fu);
+                da[e] = static_cast<__bf16>(fa);
+                du[e] = static_cast<__bf16>(fu);
+                daS[lo] = da[e];
+                duS[lo] = du[e];
+              }
+              const int64_t to = (int64_t)(n0 + cl) * g.ldct + r0 + 32 * ii + acc_row(4 * q, lane);
+              *reinterpret_cast<bf16x4*>(g.Ct + to) = bf16x4{da[0], da[1], da[2], da[3]};
+              *reinterpret_cast<bf16x4*>(g.Ct2 + to) = bf16x4{du[0], du[1], du[2], du[3]};
+            }
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = tid + THREADS * q, row = f >> 5, c8 = (f & 31) * 8;
+        const int64_t o = (int64_t)(r0 + row) * g.ldc + n0 + c8;
+        *reinterpret_cast<u32x4*>(g.C + o) = *reinterpret_cast<const u32x4*>(daS + row * LDR + c8);
+        *reinterpret_cast<u32x4*>(g.C2 + o) = *reinterpret_cast<const u32x4*>(duS + row * LDR + c8);
+      }
+      __syncthreads();  // the staging tiles are rewritten by the next pass
+    }
+    return;
+  }
+
   if constexpr (EPI == EPI_RMW) {
     // W += alpha * acc through LDS in four passes of 64 rows, so that the fp32 state is read and
     // written in whole 16-byte runs per lane (1 KB per row) with eight loads in flight per thread
@@ -377,32 +443,6 @@ __device__ __forceinline__ void gemm_big_body(const Args& g, int ksplit, float* 
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         const bf16x4 v4 = {zv[0], zv[1], zv[2], zv[3]};
         *reinterpret_cast<bf16x4*>(g.Ct + (int64_t)n * g.ldct + mb + acc_row(4 * q, lane)) = v4;
-      }
-    } else if constexpr (EPI == gemm::EPI_SWIGLU_BWD) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + 32 * j + acc_col(lane);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          __bf16 da[4], du[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q + e;
-            const int64_t o = (int64_t)(mb + acc_row(r, lane)) * g.ldc + n;
-            float fa, fu;
-            gemm::swiglu_bwd(acc[i][j][r], static_cast<float>(g.Ga[o]), static_cast<float>(g.Gu[o]), fa, fu);
-            da[e] = static_cast<__bf16>(fa);
-            du[e] = static_cast<__bf16>(fu);
-            g.C[o] = da[e];
-            g.C2[o] = du[e];
-          }
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const int64_t to = (int64_t)n * g.ldct + mb + acc_row(4 * q, lane);
-          *reinterpret_cast<bf16x4*>(g.Ct + to) = bf16x4{da[0], da[1], da[2], da[3]};
-          *reinterpret_cast<bf16x4*>(g.Ct2 + to) = bf16x4{du[0], du[1], du[2], du[3]};
-        }
-        // keeps the compiler from hoisting every tile's operand loads ahead (register spills)
-        asm volatile("" ::: "memory");
       }
     } else {
 #pragma unroll
@@ -687,7 +727,8 @@ static hipError_t run_gemm(int cls, const gemm::Args& g, int ksplit, float* part
       hipLaunchKernelGGL(gemm2::ksplit_sum_kernel, dim3(1024), dim3(256), 0, st, part, ksplit, g.M, g.N, g.C, g.ldc);
       return hipGetLastError();
     }
-    return launch_k(cls, gemm2::gemm_big_kernel<EPI>, dim3(tiles), dim3(gemm2::THREADS), gemm2::LDS, st, g, 1, part);
+    return launch_k(cls, gemm2::gemm_big_kernel<EPI>, dim3(tiles), dim3(gemm2::THREADS), gemm2::lds_of<EPI>(), st, g,
+                    1, part);
   }
   const dim3 grid((unsigned)(g.N / gemm::BN), (unsigned)(g.M / gemm::BM));
   return launch_k(cls, gemm::gemm_tn_kernel<EPI>, grid, dim3(256), gemm::lds_bytes<EPI>(), st, g);
@@ -950,7 +991,7 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
     if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_STORE>, lds_bytes<EPI_STORE>());
     if (e == hipSuccess) e = allow_lds(gemm_tn_kernel<EPI_RMW>, lds_bytes<EPI_RMW>());
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU>, gemm2::LDS);
-    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU_BWD>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_SWIGLU_BWD>, gemm2::lds_of<EPI_SWIGLU_BWD>());
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<gemm2::EPI_PARTIAL>, gemm2::LDS);
     if (e == hipSuccess) e = allow_lds(gemm2::gemm_rmw_pp_kernel<true>, gemm2::PP_LDS_T);
