@@ -618,13 +618,14 @@ __global__ void __launch_bounds__(256, 2) gemm_rmw_pp_kernel(Args g) {
       }
     }
     if (pass + 1 < 4) loadw(pass + 1, wv);
-    if (TSH && g.Wsht) {  // the pass's 64 x 128 shadow tile, transposed: 128 rows of 64 bf16 (4 bytes per thread step)
+    if (TSH && g.Wsht) {  // the pass's 64 x 128 shadow tile, transposed: 128 rows of 64 bf16, 16 bytes per store
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int f = tid + 256 * q, n = f >> 5, m2 = (f & 31) * 2;
-        *reinterpret_cast<uint32_t*>(g.Wsht + (int64_t)(n0 + n) * g.ldwt + m0 + 64 * pass + m2) =
-            *reinterpret_cast<const uint32_t*>(tp + n * PP_LDT + m2);
+      for (int q = 0; q < 4; ++q) {
+        const int f = tid + 256 * q, n = f >> 3, m8 = (f & 7) * 8;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(tp + n * PP_LDT + m8);  // 4-byte aligned rows
+        const u32x4 v = {src[0], src[1], src[2], src[3]};
+        *reinterpret_cast<u32x4*>(g.Wsht + (int64_t)(n0 + n) * g.ldwt + m0 + 64 * pass + m8) = v;
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the staging area is rewritten next
