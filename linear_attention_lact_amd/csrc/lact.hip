@@ -14,6 +14,7 @@
 // so the renormalisation of W0 / W2 is a row norm here and that of W1 a column norm.
 #include "fastweight.hpp"
 #include "host.hpp"
+#include "lact_large.hpp"
 #include "timing.hpp"
 #include "update.hpp"
 #include "update_tiled.hpp"
@@ -433,6 +434,129 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   return TTT_OK;
 }
 
+// ---------------------------------------------------------------------------------------
+// Heads wider than 192 (16-bit I/O): every chunk step composed of fp16 TN products
+// (lact_large.hpp), one pair at a time, with the tiled update. Scratch of one pair, reused.
+struct LargeWs {
+  _Float16 *Kh, *Vh, *Kt, *Vt;  // chunk tokens [bk][h] and transposed [h][bk]
+  float *Af, *Bf, *Df;          // forward products [bk][rh]
+  _Float16 *EH, *X0, *X2;       // gradient intermediates, transposed [rh][bk]
+  _Float16 *Qh, *Hq;            // apply: queries [bq][h], hidden [bq][rh]
+};
+
+static ttt_status lact_run_large(const ttt_lact_params& p, const LactState& s, const LargeWs& L, const void* Q,
+                                 const void* K, const void* V, const float* eta, const float* W0, const float* W1,
+                                 const float* W2, const float* M_in, void* O, float* W0o, float* W1o, float* W2o,
+                                 float* Mo, hipStream_t st) {
+  using namespace large;
+  typedef _Float16 f16;
+  const int P = s.P, h = s.h, rh = s.rh, bq = p.chunk_q, bk = p.chunk_kv;
+  const int64_t n = (int64_t)rh * h;
+  const int nch = p.Nk / p.chunk_kv;
+  {
+    LaunchTimer lt(K_LACT_INIT, st);
+    hipLaunchKernelGGL(lact_init_kernel<f16>, dim3((unsigned)(n / 1024), 3, P), dim3(256), 0, st, s, W0, W1, W2,
+                       M_in, p.H, p.w_batch_stride, nullptr, 0, 0);
+    hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
+    if (nch > 0)
+      hipLaunchKernelGGL(lact_eta_scale_kernel, dim3((unsigned)P, (unsigned)nch), dim3(256), 0, st, eta,
+                         (int64_t)p.Nk, (int64_t)p.Nk, 1, bk, bk, 1, s.esc);
+    TTT_HIP(hipGetLastError());
+  }
+  auto gemm = [&](int epi, const f16* A, int64_t lda, const f16* B0, const f16* B1, int64_t ldb, int M, int N, int Kd,
+                  void* C, int64_t ldc, const float* inv) -> hipError_t {
+    GArgs g{};
+    g.A = A;
+    g.lda = lda;
+    g.B0 = B0;
+    g.B1 = B1;
+    g.ldb = ldb;
+    g.M = M;
+    g.N = N;
+    g.K = Kd;
+    g.C = C;
+    g.ldc = ldc;
+    g.alpha = 1.f;
+    g.inv_dev = inv;
+    const dim3 grid((unsigned)(N / BN), (unsigned)(M / BM));
+    if (epi == G_F32) hipLaunchKernelGGL((gemm16_kernel<G_F32, float>), grid, dim3(256), lds_bytes<G_F32>(), st, g);
+    else if (epi == G_SWI) hipLaunchKernelGGL((gemm16_kernel<G_SWI, f16>), grid, dim3(256), lds_bytes<G_SWI>(), st, g);
+    else hipLaunchKernelGGL((gemm16_kernel<G_OUT, bf16_t>), grid, dim3(256), lds_bytes<G_OUT>(), st, g);
+    return hipGetLastError();
+  };
+  const f16* sh = reinterpret_cast<const f16*>(s.sh);
+  const int64_t shb = (int64_t)P * 4 * n;
+  // O of chunk c from the weights in shadow buffer `buf`
+  auto apply = [&](int c, const f16* buf) -> hipError_t {
+    LaunchTimer lt(K_LACT_APPLY, st);
+    for (int pr = 0; pr < P; ++pr) {
+      const int64_t t0 = (int64_t)pr * p.Nq + (int64_t)c * bq;
+      const f16* w = buf + (int64_t)pr * 4 * n;  // W0T, W2T, W1, W1T
+      hipLaunchKernelGGL(tok16_kernel, dim3((unsigned)(h / 32), (unsigned)(bq / 32)), dim3(256), 0, st,
+                         static_cast<const bf16_t*>(Q) + t0 * h, h, L.Qh, static_cast<f16*>(nullptr), (int64_t)0);
+      hipError_t e = hipGetLastError();
+      if (e == hipSuccess) e = gemm(G_SWI, L.Qh, h, w, w + n, h, bq, rh, h, L.Hq, rh, nullptr);
+      if (e == hipSuccess) e = gemm(G_OUT, L.Hq, rh, w + 3 * n, nullptr, rh, bq, h, rh, static_cast<bf16_t*>(O) + t0 * h, h,
+                                    nullptr);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  // segment partials (one segment) of chunk c at the weights in shadow buffer `buf`
+  auto grad = [&](int c, const f16* buf) -> hipError_t {
+    LaunchTimer lt(K_LACT_GRAD, st);
+    for (int pr = 0; pr < P; ++pr) {
+      const int64_t t0 = (int64_t)pr * p.Nk + (int64_t)c * bk;
+      const f16* w = buf + (int64_t)pr * 4 * n;
+      const dim3 tg((unsigned)(h / 32), (unsigned)(bk / 32));
+      hipLaunchKernelGGL(tok16_kernel, tg, dim3(256), 0, st, static_cast<const bf16_t*>(K) + t0 * h, h, L.Kh, L.Kt,
+                         (int64_t)bk);
+      hipLaunchKernelGGL(tok16_kernel, tg, dim3(256), 0, st, static_cast<const bf16_t*>(V) + t0 * h, h, L.Vh, L.Vt,
+                         (int64_t)bk);
+      hipError_t e = hipGetLastError();
+      if (e == hipSuccess) e = gemm(G_F32, L.Kh, h, w, nullptr, h, bk, rh, h, L.Af, rh, nullptr);          // K W0
+      if (e == hipSuccess) e = gemm(G_F32, L.Kh, h, w + n, nullptr, h, bk, rh, h, L.Bf, rh, nullptr);      // K W2
+      if (e == hipSuccess) e = gemm(G_F32, L.Vh, h, w + 2 * n, nullptr, h, bk, rh, h, L.Df, rh, nullptr);  // V W1^T
+      if (e != hipSuccess) return e;
+      const float* sc = s.esc + (int64_t)c * P + pr;
+      hipLaunchKernelGGL(lgrad_epi_kernel, dim3((unsigned)(rh / 32), (unsigned)(bk / 32)), dim3(256), 0, st, L.Af,
+                         L.Bf, L.Df, eta + t0, sc, rh, bk, L.EH, L.X0, L.X2);
+      e = hipGetLastError();
+      float* part = s.part + (int64_t)pr * 3 * n;  // P0, P1, P2 of this pair (rows j, columns c)
+      if (e == hipSuccess) e = gemm(G_F32, L.EH, bk, L.Vt, nullptr, bk, rh, h, bk, part + n, h, sc);      // (eta H)^T V
+      if (e == hipSuccess) e = gemm(G_F32, L.X0, bk, L.Kt, nullptr, bk, rh, h, bk, part, h, sc);          // X0^T K
+      if (e == hipSuccess) e = gemm(G_F32, L.X2, bk, L.Kt, nullptr, bk, rh, h, bk, part + 2 * n, h, sc);  // X2^T K
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  UpdateArgs ua{};
+  ua.s = s;
+  ua.S = 1;
+  ua.mask = p.update_mask;
+  ua.muon = p.muon;
+  ua.weight_norm = p.weight_norm;
+  ua.momentum = p.momentum;
+  ua.eps_norm = p.eps_norm;
+  ua.eps_ns = p.eps_ns;
+  for (int c = 0; c < nch; ++c) {
+    const f16* rd = sh + (c & 1) * shb;
+    const f16* wr = sh + ((c + 1) & 1) * shb;
+    if (p.order == TTT_APPLY_THEN_UPDATE) TTT_HIP(apply(c, rd));
+    TTT_HIP(grad(c, rd));
+    ua.s.sh = const_cast<f16*>(wr);
+    {
+      LaunchTimer lt(K_LACT_UPDATE, st);
+      TTT_HIP(tu_run<f16>(ua, st));
+    }
+    if (p.order == TTT_UPDATE_THEN_APPLY) TTT_HIP(apply(c, wr));
+  }
+  LaunchTimer lt_fin(K_LACT_FINAL, st);
+  hipLaunchKernelGGL(lact_final_kernel, dim3((unsigned)(n / 1024), 3, P), dim3(256), 0, st, s, W0o, W1o, W2o, Mo);
+  TTT_HIP(hipGetLastError());
+  return TTT_OK;
+}
+
 }  // namespace ttt
 
 using namespace ttt;
@@ -459,10 +583,17 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   if (q.Nq % q.chunk_q || q.Nk % q.chunk_kv) return TTT_ERR_SHAPE;
   if (q.Nq / q.chunk_q != q.Nk / q.chunk_kv) return TTT_ERR_SHAPE;
   const int64_t rh64 = (int64_t)q.r * q.h;
-  if (q.h % 32 || rh64 % 64 || rh64 > 1024) return TTT_ERR_SHAPE;
-  if (q.w_batch_stride != 0 && q.w_batch_stride != (int64_t)q.H * rh64 * q.h) return TTT_ERR_SHAPE;
   const bool bf16 = q.dtype == TTT_BF16;
-  if (bf16 ? (q.h > 192) : (q.h > 64)) return TTT_ERR_UNSUPPORTED;
+  // heads wider than the LDS-resident kernels hold: the composed path (16-bit I/O)
+  const bool large = bf16 && q.h > 192;
+  if (q.h % 32 || rh64 % 64 || rh64 > (large ? 2048 : 1024)) return TTT_ERR_SHAPE;
+  if (q.w_batch_stride != 0 && q.w_batch_stride != (int64_t)q.H * rh64 * q.h) return TTT_ERR_SHAPE;
+  if (!bf16 && q.h > 64) return TTT_ERR_UNSUPPORTED;
+  if (large) {
+    if (q.h > TU_HMAX || q.chunk_flags || q.inner_steps > 1 || q.eta_per_matrix) return TTT_ERR_UNSUPPORTED;
+    if (q.h % 128 || rh64 % 128 || q.chunk_q % 128 || q.chunk_kv % 128 || rh64 * q.h / 1024 > TU_SS)
+      return TTT_ERR_SHAPE;
+  }
   const int P = q.B * q.H, h = q.h, rh = (int)rh64;
   const int64_t n = rh64 * h;
   const int nch = q.chunk_kv ? q.Nk / q.chunk_kv : 0;
@@ -502,6 +633,15 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
   const size_t oNs = plan.add((size_t)P * 3 * NSZ * 4);
   const size_t oEsc = plan.add((size_t)nch * P * S * 4);
   const size_t oBak = q.chunk_flags ? plan.add((size_t)2 * P * 3 * n * 4) : 0;  // held state of apply-only chunks
+  size_t oL[12] = {0};
+  if (large) {  // one pair's scratch of the composed path
+    const size_t bk = (size_t)q.chunk_kv, bq = (size_t)q.chunk_q, hh = (size_t)h, rr = (size_t)rh;
+    for (int i = 0; i < 4; ++i) oL[i] = plan.add(bk * hh * 2);       // Kh, Vh, Kt, Vt
+    for (int i = 4; i < 7; ++i) oL[i] = plan.add(bk * rr * 4);       // Af, Bf, Df
+    for (int i = 7; i < 10; ++i) oL[i] = plan.add(rr * bk * 2);      // EH, X0, X2
+    oL[10] = plan.add(bq * hh * 2);                                   // Qh
+    oL[11] = plan.add(bq * rr * 2);                                   // Hq
+  }
   if (!workspace) {
     *workspace_bytes = plan.total;
     return TTT_OK;
@@ -533,6 +673,13 @@ extern "C" ttt_status ttt_lact_forward(const ttt_lact_params* p, const void* Q, 
     return lact_run<IOT, OPT, HH>(qq, s, S, q.chunk_flags ? reinterpret_cast<float*>(ws + oBak) : nullptr, Q, K, \
                                   V, eta, W0, W1, W2, M_in, O, W0_out, W1_out, W2_out, M_out, st);
   try {
+    if (large) {
+      auto f16p = [&](int i) { return reinterpret_cast<_Float16*>(ws + oL[i]); };
+      auto f32p = [&](int i) { return reinterpret_cast<float*>(ws + oL[i]); };
+      const LargeWs L{f16p(0), f16p(1), f16p(2), f16p(3), f32p(4), f32p(5), f32p(6),
+                      f16p(7), f16p(8), f16p(9), f16p(10), f16p(11)};
+      return lact_run_large(qq, s, L, Q, K, V, eta, W0, W1, W2, M_in, O, W0_out, W1_out, W2_out, M_out, st);
+    }
     if (bf16) {
       switch (h) {
         TTT_LACT_CASE(bf16_t, _Float16, 32)

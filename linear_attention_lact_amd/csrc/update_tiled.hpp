@@ -20,7 +20,8 @@
 
 namespace ttt {
 
-constexpr int TU_SS = 1024;  // scratch floats for per-tile sums of squares (n / 1024 <= 192)
+constexpr int TU_SS = 2048;  // scratch floats for per-tile sums of squares (n / 1024 <= 2048)
+constexpr int TU_HMAX = 1024;  // widest state row (h) the final kernels handle
 
 struct NsView {
   float* X[2];  // [h][rh]
@@ -249,13 +250,15 @@ __global__ void __launch_bounds__(256) tu_xupd_kernel(UpdateArgs u, int cur) {
 // W -= update for 32 state rows; W0T / W2T rows are renormalised over their h inputs and their
 // shadows written here. W1 is renormalised per column over all rh rows: this kernel leaves the
 // block's column sums of squares in the scratch (A's space) and tu_final_w1_kernel finishes.
-// grid (rh/32, 3, P), 256 threads: wave w takes rows 8w..8w+7, lane l columns 4l..4l+3.
+// grid (rh/32, 3, P), 256 threads: wave w takes rows 8w..8w+7, lane l columns 256 k + 4l..+3 of
+// each 256-column part k of the row (one part up to h = 256).
 template <class OpT>
 __global__ void __launch_bounds__(256) tu_final_kernel(UpdateArgs u, int ucur) {
+  constexpr int NPART = TU_HMAX / 256;
   const LactState& s = u.s;
   const int mat = blockIdx.y, pair = blockIdx.z;
   if (!tu_active(u, mat)) return;
-  __shared__ float colp[4][192];
+  __shared__ float colp[4][TU_HMAX];
   const NsView nv = ns_view(s, pair, mat);
   const int h = s.h, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t n = (int64_t)s.rh * h;
@@ -263,32 +266,49 @@ __global__ void __launch_bounds__(256) tu_final_kernel(UpdateArgs u, int ucur) {
   const float* U = nv.Y[ucur];
   const float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
   OpT* dst = reinterpret_cast<OpT*>(s.sh) + (int64_t)pair * 4 * n + (mat == 0 ? 0 : 1) * n;
-  const bool live = lane * 4 < h;
-  f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+  const int nparts = (h + 255) / 256;
+  f32x4 cs[NPART];
+#pragma unroll
+  for (int k = 0; k < NPART; ++k) cs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int rr = 0; rr < 8; ++rr) {
     const int j = blockIdx.x * 32 + w * 8 + rr;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
-      v = *reinterpret_cast<const f32x4*>(W + (int64_t)j * h + lane * 4) -
-          *reinterpret_cast<const f32x4*>(U + (int64_t)j * h + lane * 4);
+    f32x4 v[NPART];
+    float sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPART; ++k) {
+      const int c = 256 * k + lane * 4;
+      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < nparts && c < h)
+        v[k] = *reinterpret_cast<const f32x4*>(W + (int64_t)j * h + c) -
+               *reinterpret_cast<const f32x4*>(U + (int64_t)j * h + c);
+      sq += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
     }
     if (mat != 1 && u.weight_norm) {
-      const float ss = wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
-      v = v * (nu[j] / (sqrtf(ss) + u.eps_norm));
-    }
-    if (mat == 1) cs += v * v;
-    if (live) {
-      *reinterpret_cast<f32x4*>(W + (int64_t)j * h + lane * 4) = v;
-      if (mat != 1) {
+      const float f = nu[j] / (sqrtf(wave_sum(sq)) + u.eps_norm);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[(int64_t)j * h + lane * 4 + q] = Mfma<OpT>::from_f32(v[q]);
+      for (int k = 0; k < NPART; ++k) v[k] = v[k] * f;
+    }
+#pragma unroll
+    for (int k = 0; k < NPART; ++k) {
+      const int c = 256 * k + lane * 4;
+      if (mat == 1) cs[k] += v[k] * v[k];
+      if (k < nparts && c < h) {
+        *reinterpret_cast<f32x4*>(W + (int64_t)j * h + c) = v[k];
+        if (mat != 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[(int64_t)j * h + c + q] = Mfma<OpT>::from_f32(v[k][q]);
+        }
       }
     }
   }
   if (mat == 1 && u.weight_norm) {
-    if (live) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) colp[w][lane * 4 + q] = cs[q];
+    for (int k = 0; k < NPART; ++k) {
+      const int c = 256 * k + lane * 4;
+      if (k < nparts && c < h) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) colp[w][c + q] = cs[k][q];
+      }
     }
     __syncthreads();
     for (int c = threadIdx.x; c < h; c += 256)
@@ -300,10 +320,11 @@ __global__ void __launch_bounds__(256) tu_final_kernel(UpdateArgs u, int ucur) {
 // grid (rh/32, P), 256 threads.
 template <class OpT>
 __global__ void __launch_bounds__(256) tu_final_w1_kernel(UpdateArgs u) {
+  constexpr int CW = 192;  // columns per part of the transposed shadow write
   const LactState& s = u.s;
   const int pair = blockIdx.y;
-  __shared__ float f[192];
-  __shared__ float tile[32][193];
+  __shared__ float f[TU_HMAX];
+  __shared__ float tile[32][CW + 1];
   const NsView nv = ns_view(s, pair, 1);
   const int h = s.h, rh = s.rh, rb = rh / 32;
   const int64_t n = (int64_t)rh * h;
@@ -321,18 +342,22 @@ __global__ void __launch_bounds__(256) tu_final_w1_kernel(UpdateArgs u) {
   }
   __syncthreads();
   const int j0 = blockIdx.x * 32;
-  for (int i = threadIdx.x; i < 32 * h; i += 256) {
-    const int r = i / h, c = i % h;
-    const int64_t o = (int64_t)(j0 + r) * h + c;
-    const float v = W[o] * f[c];
-    W[o] = v;
-    sh[2 * n + o] = Mfma<OpT>::from_f32(v);
-    tile[r][c] = v;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 32 * h; i += 256) {
-    const int c = i / 32, r = i % 32;
-    sh[3 * n + (int64_t)c * rh + j0 + r] = Mfma<OpT>::from_f32(tile[r][c]);
+  for (int c0 = 0; c0 < h; c0 += CW) {  // columns c0 .. c0 + cw - 1
+    const int cw = min(CW, h - c0);
+    for (int i = threadIdx.x; i < 32 * cw; i += 256) {
+      const int r = i / cw, c = c0 + i % cw;
+      const int64_t o = (int64_t)(j0 + r) * h + c;
+      const float v = W[o] * f[c];
+      W[o] = v;
+      sh[2 * n + o] = Mfma<OpT>::from_f32(v);
+      tile[r][c - c0] = v;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 32 * cw; i += 256) {
+      const int c = i / 32, r = i % 32;
+      sh[3 * n + (int64_t)(c0 + c) * rh + j0 + r] = Mfma<OpT>::from_f32(tile[r][c]);
+    }
+    __syncthreads();  // the tile is rewritten by the next part
   }
 }
 

@@ -72,6 +72,17 @@ def _lp(**kw):
     return ttt.LactParams(**base)
 
 
+def test_lact_wide_heads_take_the_composed_path(lib):
+    """Heads wider than 192 (the pages' d = 768 defaults): accepted in bf16 with the plain loop;
+    the loop variants are not built there."""
+    for kw in (dict(h=256), dict(h=768, r=2, B=1, H=1), dict(h=768, r=1, B=1, H=4)):
+        st, size = _lact(lib, _lp(**kw))
+        assert st == ttt.TTT_OK and size > 0, kw
+    assert _lact(lib, _lp(h=768, r=1, dtype=ttt.FP32))[0] == ttt.TTT_ERR_UNSUPPORTED
+    for kw in (dict(inner_steps=2), dict(eta_per_matrix=1), dict(chunk_flags=0x6000)):
+        assert _lact(lib, _lp(h=256, **kw))[0] == ttt.TTT_ERR_UNSUPPORTED, kw
+
+
 def test_lact_workspace_query(lib):
     st, size = _lact(lib, _lp())
     assert st == ttt.TTT_OK and size > 0
@@ -88,8 +99,11 @@ def test_lact_workspace_query(lib):
     (dict(Nk=32768 + 64), ttt.TTT_ERR_SHAPE),              # ragged last chunk
     (dict(Nq=16384, chunk_q=2048), ttt.TTT_ERR_SHAPE),     # chunk counts differ
     (dict(h=100), ttt.TTT_ERR_SHAPE),
-    (dict(h=256, r=8), ttt.TTT_ERR_SHAPE),                 # rh > 1024
-    (dict(h=256), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(h=128, r=16), ttt.TTT_ERR_SHAPE),                # rh > 1024 (h <= 192)
+    (dict(h=256, r=16), ttt.TTT_ERR_SHAPE),                # rh > 2048 (wider heads)
+    (dict(h=1152, r=1), ttt.TTT_ERR_UNSUPPORTED),          # wider than the composed path
+    (dict(h=224), ttt.TTT_ERR_SHAPE),                      # wider heads come in multiples of 128
+    (dict(h=256, chunk_q=192, chunk_kv=192, Nq=192 * 16, Nk=192 * 16), ttt.TTT_ERR_SHAPE),
     (dict(dtype=ttt.FP32, h=128), ttt.TTT_ERR_UNSUPPORTED),
     (dict(w_batch_stride=5), ttt.TTT_ERR_SHAPE),
     (dict(momentum=-0.5), ttt.TTT_ERR_ARG),

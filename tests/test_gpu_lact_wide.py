@@ -1,0 +1,47 @@
+"""GPU parity of ttt_lact_forward for heads wider than 192 (the LaCT notes' own d = 768 defaults),
+which run the composed path (fp16 products, tiled Newton-Schulz), against the CPU oracle at the
+bf16 bar (max-abs-relative 2e-2); every output is compared: O, the final fast weights and the
+final momentum."""
+import numpy as np
+import pytest
+
+from tests._helpers import BF16_TOL, announce, lact_on_gpu, lact_oracle
+from tests.test_gpu_lact import _compare
+from workloads import BF16, LactProblem, UPD_W1, make_lact_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (label, problem kwargs, input variant, seed)
+    ("h256 r2 AU muon mom renorm", dict(B=1, H=2, h=256, r=2, N=512, chunk=128, muon=True, momentum=0.9), {}, 1),
+    ("h256 r1 UA sgd", dict(B=1, H=2, h=256, r=1, N=512, chunk=256, order=1), {}, 2),
+    ("h384 r2 AU W1 only eta x100", dict(B=2, H=1, h=384, r=2, N=256, chunk=128, update_mask=UPD_W1),
+     dict(eta_scale=1.0), 3),
+    ("h768 r1 AU muon mom renorm", dict(B=1, H=1, h=768, r=1, N=512, chunk=256, muon=True, momentum=0.9), {}, 4),
+    ("h768 r2 UA muon", dict(B=1, H=1, h=768, r=2, N=256, chunk=128, muon=True, order=1), {}, 5),
+]
+
+
+@pytest.mark.parametrize("label,kw,xs,seed", CASES, ids=[c[0] for c in CASES])
+def test_wide_heads(lib, label, kw, xs, seed):
+    kw = dict(kw)
+    N, chunk = kw.pop("N"), kw.pop("chunk")
+    base = dict(Nq=N, Nk=N, chunk_q=chunk, chunk_kv=chunk, dtype=BF16, v_normalised=False)
+    base.update(kw)
+    p = LactProblem(**base)
+    announce(f"lact wide heads {label}")
+    x = make_lact_inputs(p, 1100 + seed, **xs)
+    gpu = lact_on_gpu(lib, p, x)
+    ref = lact_oracle(p, x)
+    _compare(gpu, ref, BF16_TOL, label=label)
+
+
+def test_wide_heads_repeat_bitwise(lib):
+    import torch
+    p = LactProblem(B=1, H=2, h=256, r=2, Nq=256, Nk=256, chunk_q=128, chunk_kv=128, dtype=BF16, muon=True,
+                    momentum=0.9, v_normalised=False)
+    announce("lact wide heads h256 repeat")
+    x = make_lact_inputs(p, 1120)
+    a, b = lact_on_gpu(lib, p, x), lact_on_gpu(lib, p, x)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
