@@ -112,8 +112,11 @@ typedef int32_t ttt_status;
  *   M_out   [B, H, 3, h*rh] float32, nullable: final momentum
  * Shape rules: Nq/chunk_q == Nk/chunk_kv (number of chunks); a ragged last chunk is rejected
  * (TTT_ERR_SHAPE); h a multiple of 32 and r >= 1 with r*h a multiple of 64, r*h <= 1024;
- * this build implements h <= 192 in TTT_BF16 mode and h <= 64 in TTT_FP32 mode
- * (TTT_ERR_UNSUPPORTED otherwise). 0 <= momentum < 1 and finite eps_norm, eps_ns >= 0, else
+ * this build implements h <= 192 in TTT_BF16 mode and h <= 64 in TTT_FP32 mode. Wider heads
+ * (the LaCT notes' d = 768 defaults, section 2.5) run a slower composed path in TTT_BF16 mode:
+ * 192 < h <= 1024 with h, r*h, chunk_q and chunk_kv multiples of 128, r*h <= 2048 and
+ * r*h*h <= 2^21, without chunk_flags, inner_steps > 1 or eta_per_matrix (TTT_ERR_SHAPE or
+ * TTT_ERR_UNSUPPORTED otherwise; TTT_ERR_UNSUPPORTED for other unbuilt combinations). 0 <= momentum < 1 and finite eps_norm, eps_ns >= 0, else
  * TTT_ERR_ARG (NaN included).
  * Precision: in TTT_BF16 mode the per-chunk products use fp16 MFMA operands (bf16 inputs
  * convert exactly) and Newton-Schulz uses split-bf16 operands; fp32 state throughout. In
