@@ -45,3 +45,37 @@ def test_wide_heads_repeat_bitwise(lib):
     a, b = lact_on_gpu(lib, p, x), lact_on_gpu(lib, p, x)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_wide_heads_per_sequence_weights_and_initial_momentum(lib):
+    """Per-sequence fast weights and a given initial momentum on the composed path (h 256)."""
+    import torch
+    from tests._helpers import dev, host
+    from oracle import lact as Lo
+    from workloads import max_abs_rel
+    p = LactProblem(B=2, H=1, h=256, r=2, Nq=256, Nk=256, chunk_q=128, chunk_kv=128, dtype=BF16, muon=True,
+                    momentum=0.9, v_normalised=False)
+    announce("lact wide heads h256 per-sequence weights, initial momentum")
+    x = make_lact_inputs(p, 1130)
+    rng = np.random.default_rng(31)
+    W = {k: np.stack([x[k] * (1.0 + 0.2 * b) for b in range(2)]).astype(np.float32) for k in ("W0", "W1", "W2")}
+    n = p.h * p.rh
+    M = (0.01 * rng.standard_normal((2, 1, 3, n))).astype(np.float32)
+    io = torch.bfloat16
+    O, W0o, W1o, W2o, Mo = lib.lact_forward(
+        dev(x["Q"], io), dev(x["K"], io), dev(x["V"], io), dev(x["eta"], torch.float32), dev(W["W0"], torch.float32),
+        dev(W["W1"], torch.float32), dev(W["W2"], torch.float32), M_in=dev(M, torch.float32), chunk_q=128,
+        chunk_kv=128, order=0, update_mask=7, weight_norm=True, muon=True, momentum=0.9, eps_norm=p.eps_norm,
+        eps_ns=p.eps_ns)
+    Md = {"W0": M[:, :, 0].reshape(2, 1, p.h, p.rh), "W1": M[:, :, 1].reshape(2, 1, p.rh, p.h),
+          "W2": M[:, :, 2].reshape(2, 1, p.h, p.rh)}
+    ref = Lo.lact_forward(x["Q"], x["K"], x["V"], x["eta"], W["W0"], W["W1"], W["W2"], chunk_q=128, chunk_kv=128,
+                          order=0, update_mask=7, weight_norm=True, muon=True, momentum=0.9, eps_norm=p.eps_norm,
+                          eps_ns=p.eps_ns, M_in=Md)
+    errs = dict(O=max_abs_rel(host(O), ref["O"]), W0=max_abs_rel(host(W0o), ref["W0"]),
+                W1=max_abs_rel(host(W1o), ref["W1"]), W2=max_abs_rel(host(W2o), ref["W2"]))
+    Mh = host(Mo)
+    for i in range(3):
+        errs[f"M{i}"] = max_abs_rel(Mh[:, :, i].reshape(ref[f"M{i}"].shape), ref[f"M{i}"])
+    print("per-sequence: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
