@@ -200,7 +200,11 @@ ttt_status ttt_lact_forward(const ttt_lact_params* p,
  * whose operands are fp16: there Q, K, eta*V, the fast weights and the states must lie within
  * the fp16 range, |x| <= 65504 (not checked; larger values give undefined results).
  * The single-pass path runs on devices with 8 XCDs (hipDeviceAttributeNumberOfXccs); other
- * devices take the multi-launch path (same results, more launches).
+ * devices take the multi-launch path (same results, more launches). Test hook: when the
+ * environment variable TTT_LOOKBACK_STRESS holds a nonzero integer at call time, every group of
+ * the single-pass path waits a pseudo-random time (seeded by it, up to about 0.1 ms) before each
+ * publication, so the chunk-prefix lookback meets other arrival orders; results are unchanged
+ * bit for bit.
  * feature_map = TTT_PHI_IDENTITY (the same summary page's simplification ladder, "Method step
  * details", step 3: the fast weight is one linear layer f(x) = x W): phi(X) = X, so
  * dS_c = K_c^T diag(eta_c) V_c, S_c as above and O_c = Q_c S_c, with the h x h state W1 = S_0

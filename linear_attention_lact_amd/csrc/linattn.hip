@@ -9,6 +9,7 @@
 //          (with momentum, each dS_j weighted by its cumulative coefficient, Theorem 5.3)
 //   O_c  = phi(Q_c) S_c                                   (apply_kernel with per-chunk S_c)
 // The chunk prefix is an exclusive (or inclusive) scan over the chunks of each pair.
+#include <cstdlib>
 #include <mutex>
 
 #include "fastweight.hpp"
@@ -167,6 +168,10 @@ static ttt_status linattn_fused_run(const ttt_linattn_params& p, char* ws, size_
   while (G < GLIM && (int64_t)8 * ((P + 7) / 8) * (nch / G) > ncu && nch % (2 * G) == 0 && p.chunk % PASS == 0)
     G *= 2;
   fa.group = G;
+  {  // test hook: the lookback stress seed (see linattn_fused.hpp)
+    const char* sv = std::getenv("TTT_LOOKBACK_STRESS");
+    fa.stress = sv ? (unsigned)std::strtoul(sv, nullptr, 10) : 0u;
+  }
   {
     LaunchTimer lt(K_LIN_PREP, st);
     hipLaunchKernelGGL(linattn_fused_reset, dim3(1), dim3(256), 0, st, fa.tickets, fa.flags, P * nch);

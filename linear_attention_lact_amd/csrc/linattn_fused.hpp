@@ -55,9 +55,23 @@ struct FusedArgs {
   int P, heads, N, chunk, nch, inclusive;
   int group;                // chunks per workgroup G (nch % G == 0; G > 1 needs chunk % (NW*32) == 0)
   int64_t w_batch_stride;
+  unsigned stress;          // lookback stress (a test hook): nonzero seeds a random delay before
+                            // every flag publication, so the lookback meets other orders
 };
 
 constexpr long FUSED_SPIN_LIMIT = 1l << 20;
+
+// Lookback stress: a delay of 0 .. 127 sleeps of about a microsecond, from a hash of the seed
+// and the publishing (pair, group). Results do not depend on it (the lookback sums in a fixed
+// order); only the order in which groups publish changes.
+__device__ __forceinline__ void stress_delay(unsigned seed, unsigned key) {
+  if (!seed) return;
+  unsigned x = key * 2654435761u ^ seed;
+  x ^= x >> 15;
+  x *= 0x2c1b3c6du;
+  x ^= x >> 12;
+  for (unsigned k = 0; k < (x & 127u); ++k) __builtin_amdgcn_s_sleep(32);
+}
 
 __device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ unsigned flag_load(const unsigned* p) {
@@ -390,7 +404,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   combine(G - 1);
   drain_stores();
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(fl + ch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    stress_delay(a.stress, (unsigned)(pair * a.nch + ch) * 2u);
+    __hip_atomic_store(fl + ch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // the first query pass's rows are requested now and arrive during the lookback
   u32x4 qa[KS], qb[KS];
@@ -543,7 +560,10 @@ __global__ void __launch_bounds__(128 * (RH / 32)) linattn_fused_kernel(FusedArg
   }
   drain_stores();
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(fl + ch, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    stress_delay(a.stress, (unsigned)(pair * a.nch + ch) * 2u + 1u);
+    __hip_atomic_store(fl + ch, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // ---- C. O = phi(Q) S for the chunk's query tokens, wave w: 32 tokens per pass, the fast
   // weights and S read from LDS. The hidden blocks are pipelined: the pre-activation products of

@@ -281,3 +281,28 @@ def test_chunk_flags(lib, dtype, order, momentum):
     print(f"flags O={eo:.2e} S={es:.2e}", flush=True)
     tol = BF16_TOL if dtype == BF16 else FP32_TOL
     assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("feature_map,momentum,order", [("swiglu", 0.0, 0), ("swiglu", 0.9, 1), ("identity", 0.9, 0)])
+def test_lookback_stress_is_bitwise_the_plain_run(lib, monkeypatch, feature_map, momentum, order):
+    """The single-pass kernel with random delays before every publication (the lookback meets
+    other arrival orders, groups of one and of several chunks): O and the final state equal the
+    undelayed call bit for bit."""
+    import torch
+    ident = feature_map == "identity"
+    p = LactProblem(B=4, H=8, h=64, r=1 if ident else 2, Nq=8192, Nk=8192, chunk_q=512, chunk_kv=512, dtype=BF16,
+                    weight_norm=False, order=order, momentum=momentum)
+    announce(f"linattn lookback stress {feature_map} momentum={momentum} order={order}")
+    x = make_lact_inputs(p, 460 + order)
+    args = [dev(x[k], torch.bfloat16) for k in ("Q", "K", "V")] + [dev(x["eta"], torch.float32)]
+    W = [None, None] if ident else [dev(x["W0"], torch.float32), dev(x["W2"], torch.float32)]
+    call = lambda: lib.linattn_forward(*args, *W, dev(x["W1"], torch.float32), chunk=512, order=order,
+                                       momentum=momentum, feature_map=feature_map)
+    monkeypatch.delenv("TTT_LOOKBACK_STRESS", raising=False)
+    O0, S0 = call()
+    for seed in ("1", "77"):
+        monkeypatch.setenv("TTT_LOOKBACK_STRESS", seed)
+        O1, S1 = call()
+        torch.cuda.synchronize()
+        assert torch.equal(O0, O1) and torch.equal(S0, S1), seed
+    monkeypatch.delenv("TTT_LOOKBACK_STRESS")
