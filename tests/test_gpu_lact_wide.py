@@ -19,6 +19,9 @@ CASES = [
      dict(eta_scale=1.0), 3),
     ("h768 r1 AU muon mom renorm", dict(B=1, H=1, h=768, r=1, N=512, chunk=256, muon=True, momentum=0.9), {}, 4),
     ("h768 r2 UA muon", dict(B=1, H=1, h=768, r=2, N=256, chunk=128, muon=True, order=1), {}, 5),
+    # the view-synthesis pattern: one write from every context token, then the queries (UA)
+    ("h256 r2 UA scene 1024 context 128 queries",
+     dict(B=1, H=2, h=256, r=2, N=1024, chunk=1024, Nq=128, chunk_q=128, muon=True, order=1), {}, 6),
 ]
 
 
@@ -26,7 +29,8 @@ CASES = [
 def test_wide_heads(lib, label, kw, xs, seed):
     kw = dict(kw)
     N, chunk = kw.pop("N"), kw.pop("chunk")
-    base = dict(Nq=N, Nk=N, chunk_q=chunk, chunk_kv=chunk, dtype=BF16, v_normalised=False)
+    Nq, chunk_q = kw.pop("Nq", N), kw.pop("chunk_q", chunk)
+    base = dict(Nq=Nq, Nk=N, chunk_q=chunk_q, chunk_kv=chunk, dtype=BF16, v_normalised=False)
     base.update(kw)
     p = LactProblem(**base)
     announce(f"lact wide heads {label}")
