@@ -54,6 +54,27 @@ def lm_aligned_target(X0, taps, W_target=None, dtype=np.float64):
     return conv if W_target is None else conv @ np.asarray(W_target, dtype=dtype).T
 
 
+def lm_aligned_target_backward(X0, taps, W_target, dVbar, dtype=np.float64):
+    """Gradients of sum(Vbar * dVbar) of lm_aligned_target for one sequence: (dX0 [N, d_model],
+    dtaps [k, d_model], dW_target [d_model, d_model] or None). With C = Conv1D(X0):
+    dC = dVbar W_target (dVbar without a projection), dW_target = dVbar^T C,
+    dX0[s] = sum_tau taps[tau] * dC[s - tau] (s - tau >= 0), dtaps[tau] = sum_t dC[t] * X0[t + tau]."""
+    X0, taps, dV = (np.asarray(a, dtype=dtype) for a in (X0, taps, dVbar))
+    N = X0.shape[0]
+    conv = lm_aligned_target(X0, taps, None, dtype=dtype)
+    if W_target is None:
+        dC, dW = dV, None
+    else:
+        Wt = np.asarray(W_target, dtype=dtype)
+        dC, dW = dV @ Wt, dV.T @ conv
+    dX0 = np.zeros_like(X0)
+    dtaps = np.zeros_like(taps)
+    for tau in range(taps.shape[0]):
+        dX0[tau:] += taps[tau][None, :] * dC[:N - tau]
+        dtaps[tau] = (dC[:N - tau] * X0[tau:]).sum(axis=0)
+    return dX0, dtaps, dW
+
+
 def inplace_sequence(Hs, W_gate, W_up, W_down, Vbar, eta, *, chunk: int, dtype=np.float64):
     """Sequential chunk loop for one sequence. Returns (O [N,d_model], W_final)."""
     Hs, W_gate, W_up, W, Vbar = (np.asarray(a, dtype=dtype) for a in (Hs, W_gate, W_up, W_down, Vbar))

@@ -182,3 +182,30 @@ def test_hidden_unit_gradients_equal_the_full_backward():
     np.testing.assert_allclose(got["dW_gate"], full["dW_gate"][units], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(got["dW_up"], full["dW_up"][units], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(got["dW_down"], full["dW_down"][:, units].T, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("proj", [False, True])
+def test_target_backward_equals_torch_autograd(proj):
+    """The target's gradients against torch autograd of torch's depthwise conv1d and linear."""
+    import torch
+    X0, taps, W = _target_inputs(4, k=3)
+    W = W if proj else None
+    dV = np.random.default_rng(9).standard_normal(X0.shape)
+    k, d = taps.shape
+    tx = torch.tensor(X0, dtype=torch.float64, requires_grad=True)
+    tt = torch.tensor(taps, dtype=torch.float64, requires_grad=True)
+    xin = torch.nn.functional.pad(tx.T[None], (0, k - 1))
+    conv = torch.nn.functional.conv1d(xin, tt.T[:, None, :], groups=d)[0].T
+    leaves = [tx, tt]
+    if proj:
+        tw = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+        leaves.append(tw)
+        conv = torch.nn.functional.linear(conv, tw)
+    grads = torch.autograd.grad((conv * torch.tensor(dV)).sum(), leaves)
+    dX0, dtaps, dW = IP.lm_aligned_target_backward(X0, taps, W, dV)
+    np.testing.assert_allclose(dX0, grads[0].numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dtaps, grads[1].numpy(), rtol=1e-12, atol=1e-12)
+    if proj:
+        np.testing.assert_allclose(dW, grads[2].numpy(), rtol=1e-12, atol=1e-12)
+    else:
+        assert dW is None

@@ -198,6 +198,9 @@ MUTATIONS = [
      lambda: TI.test_next_token_taps_with_identity_projection_are_the_next_token_shift()),
     ("In-Place backward without the writes' terms", IP, "inplace_backward_sequence",
      _inplace_backward_no_write_term, lambda: TI.test_backward_equals_torch_autograd(False)),
+    ("target backward without the projection's transpose", IP, "lm_aligned_target_backward",
+     lambda orig: (lambda X0, taps, Wt, dV, **k: orig(X0, taps, None if Wt is None else np.asarray(Wt).T, dV, **k)),
+     lambda: TI.test_target_backward_equals_torch_autograd(True)),
     ("In-Place per-unit gradients without the writes", IP, "backward_hidden_units",
      lambda orig: (lambda Hs, Wg, Wu, Wd, Vb, eta, dO, units, **k: orig(Hs, Wg, Wu, Wd, Vb, 0.0, dO, units, **k)),
      lambda: TI.test_hidden_unit_gradients_equal_the_full_backward()),
