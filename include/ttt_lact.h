@@ -350,7 +350,8 @@ ttt_status ttt_inplace_down_forward(const ttt_inplace_params* p,
  * bf16; dHs, dVbar [B, N, d_model] bf16; dW_gate, dW_up [d_hidden, d_model] float32 (summed over
  * the batch); dW_down [d_model, d_hidden] float32 (summed over the batch) or [B, d_model,
  * d_hidden] when wdown_batch_stride != 0. Shape rules as for the forward. TTT_BF16 only; a
- * target built from X0 (the LM-aligned target) returns TTT_ERR_UNSUPPORTED. The workspace holds,
+ * target built from X0 (the LM-aligned target) returns TTT_ERR_UNSUPPORTED here: build Vbar with
+ * ttt_inplace_target_forward, pass it, and take dVbar through ttt_inplace_target_backward. The workspace holds,
  * per sequence in turn, every chunk's Z (both orientations), gate and up products, the
  * transposed dA and dU, and every chunk's state W_i^T, all bf16: about
  * 6 N d_hidden + (N / chunk) d_model d_hidden bf16 elements plus a few d_model x d_hidden
@@ -360,6 +361,30 @@ ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, const void* Hs
                                      const void* W_up, const float* W_down, const void* Vbar, const void* dO,
                                      void* dHs, float* dW_gate, float* dW_up, float* dW_down, void* dVbar,
                                      void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * ttt_inplace_target_forward / ttt_inplace_target_backward
+ *
+ * Defined by: "In-Place Test-Time Training" reading notes, section 3.2 / Eq. 3 (the LM-aligned
+ * target; the same readings as ttt_inplace_down_forward with X0 given). The target on its own, so
+ * that its inputs can be trained: ttt_inplace_target_forward writes Vbar [B, N, d_model] bf16
+ * (token-major) from p->X0, p->conv_taps, p->conv_k and p->W_target (NULL: identity); pass it to
+ * ttt_inplace_down_backward as Vbar. ttt_inplace_target_backward takes that call's dVbar
+ * [B, N, d_model] bf16 and writes the gradients of sum(Vbar * dVbar): dX0 [B, N, d_model] bf16,
+ * dtaps [conv_k, d_model] float32 and dW_target [d_model, d_model] float32 (both summed over the
+ * batch; dW_target must be NULL exactly when p->W_target is). With C = Conv1D(X0):
+ * dC = dVbar W_target, dW_target = sum dVbar^T C, dX0[s] = sum_tau taps[tau] * dC[s - tau],
+ * dtaps[tau] = sum_t dC[t] * X0[t + tau]. Fields used: B, N, d_model, dtype (TTT_BF16 only, else
+ * TTT_ERR_UNSUPPORTED), X0, conv_taps, conv_k (1..16), W_target; d_model a multiple of 256 and N
+ * a multiple of 128 (TTT_ERR_SHAPE). Workspace: one sequence's Conv1D (forward, with a
+ * projection); C^T, dVbar^T, dC and W_target^T (backward, with a projection) and the per-tile tap
+ * partials, B * N / 64 * conv_k * d_model float32.
+ * ---------------------------------------------------------------------------------------- */
+ttt_status ttt_inplace_target_forward(const ttt_inplace_params* p, void* Vbar, void* workspace,
+                                      size_t* workspace_bytes, void* stream);
+ttt_status ttt_inplace_target_backward(const ttt_inplace_params* p, const void* dVbar, void* dX0,
+                                       float* dtaps, float* dW_target, void* workspace,
+                                       size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (instrumentation; off by default)

@@ -29,7 +29,8 @@ FP32, BF16 = 0, 1
 UPD_W0, UPD_W1, UPD_W2 = 1, 2, 4
 
 EXPORTED = ("ttt_lact_forward", "ttt_linattn_forward", "ttt_linattn_forward_noalloc", "ttt_linattn_backward",
-            "ttt_inplace_down_forward", "ttt_inplace_down_backward",
+            "ttt_inplace_down_forward", "ttt_inplace_down_backward", "ttt_inplace_target_forward",
+            "ttt_inplace_target_backward",
             "ttt_status_string", "ttt_last_error", "ttt_timing_enable", "ttt_timing_collect")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # TTT_NOALLOC_SCRATCH_BYTES
 
@@ -101,6 +102,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ttt_inplace_down_forward.restype = ctypes.c_int32
     lib.ttt_inplace_down_backward.argtypes = [ctypes.POINTER(InplaceParams)] + [_vp] * 11 + [_vp, _szp, _vp]
     lib.ttt_inplace_down_backward.restype = ctypes.c_int32
+    lib.ttt_inplace_target_forward.argtypes = [ctypes.POINTER(InplaceParams), _vp, _vp, _szp, _vp]
+    lib.ttt_inplace_target_forward.restype = ctypes.c_int32
+    lib.ttt_inplace_target_backward.argtypes = [ctypes.POINTER(InplaceParams)] + [_vp] * 4 + [_vp, _szp, _vp]
+    lib.ttt_inplace_target_backward.restype = ctypes.c_int32
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_last_error.argtypes = []
@@ -438,4 +443,47 @@ def inplace_down_backward(Hs, W_gate, W_up, W_down, Vbar, dO, *, chunk: int, eta
     base = [ctypes.byref(p)] + [_ptr(t) for t in (Hs, W_gate, W_up, W_down, Vbar, dO)] + \
         [_ptr(out[k]) for k in ("dHs", "dW_gate", "dW_up", "dW_down", "dVbar")]
     _call("ttt_inplace_down_backward", lib.ttt_inplace_down_backward, base, base, dev, stream)
+    return out
+
+
+def _target_params(X0, conv_taps, W_target):
+    torch = _torch()
+    B, N, dm = X0.shape
+    dev = X0.device
+    _check(X0, "X0", torch.bfloat16, dev)
+    _check(W_target, "W_target", torch.bfloat16, dev)
+    _check(conv_taps, "conv_taps", torch.float32, dev)
+    if conv_taps is None or conv_taps.dim() != 2 or conv_taps.shape[1] != dm or not (1 <= conv_taps.shape[0] <= 16):
+        raise ValueError("conv_taps must be [k,d_model] with 1 <= k <= 16")
+    if W_target is not None and tuple(W_target.shape) != (dm, dm):
+        raise ValueError("W_target must be [d_model,d_model]")
+    return InplaceParams(B, N, dm, 0, 1, 0.0, BF16, 0, _ptr(X0), _ptr(conv_taps), _ptr(W_target),
+                         conv_taps.shape[0]), dev
+
+
+def inplace_target_forward(X0, conv_taps, W_target=None, stream=None):
+    """The LM-aligned target Vbar = Conv1D(X0) W_target^T, token-major [B,N,d_model] bf16."""
+    torch = _torch()
+    lib = load()
+    p, dev = _target_params(X0, conv_taps, W_target)
+    Vbar = torch.empty_like(X0)
+    base = [ctypes.byref(p), _ptr(Vbar)]
+    _call("ttt_inplace_target_forward", lib.ttt_inplace_target_forward, base, base, dev, stream)
+    return Vbar
+
+
+def inplace_target_backward(X0, conv_taps, dVbar, W_target=None, stream=None):
+    """Gradients of sum(Vbar * dVbar) of inplace_target_forward: dict(dX0 [B,N,d_model] bf16,
+    dtaps [k,d_model] fp32, dW_target [d_model,d_model] fp32 or None), summed over the batch."""
+    torch = _torch()
+    lib = load()
+    p, dev = _target_params(X0, conv_taps, W_target)
+    _check(dVbar, "dVbar", torch.bfloat16, dev)
+    if dVbar is None or dVbar.shape != X0.shape:
+        raise ValueError("dVbar must be [B,N,d_model]")
+    out = dict(dX0=torch.empty_like(X0), dtaps=torch.empty_like(conv_taps),
+               dW_target=None if W_target is None else torch.empty((X0.shape[2],) * 2, dtype=torch.float32,
+                                                                    device=dev))
+    base = [ctypes.byref(p), _ptr(dVbar), _ptr(out["dX0"]), _ptr(out["dtaps"]), _ptr(out["dW_target"])]
+    _call("ttt_inplace_target_backward", lib.ttt_inplace_target_backward, base, base, dev, stream)
     return out

@@ -1161,3 +1161,226 @@ extern "C" ttt_status ttt_inplace_down_backward(const ttt_inplace_params* p, con
   }
   return TTT_OK;
 }
+
+// ---------------------------------------------------------------------------------------------
+// The LM-aligned target on its own ("In-Place Test-Time Training" notes, section 3.2 / Eq. 3):
+// Vbar = Conv1D(X0) W_target^T built token-major (ttt_inplace_target_forward), and its gradients
+// from dVbar (ttt_inplace_target_backward), so that the target's inputs can be trained through the
+// backward of the update. With C = Conv1D(X0) (C[t] = sum_tau taps[tau] * X0[t + tau], zero past
+// the end): dC = dVbar W_target (dVbar without a projection), dW_target = sum dVbar^T C,
+// dX0[s] = sum_tau taps[tau] * dC[s - tau] (s - tau >= 0), dtaps[tau] = sum_t dC[t] * X0[t + tau].
+namespace ttt {
+
+// dX0 tile and per-tile tap partials of one sequence. grid (dm / 64, N / 64), block 256: a 64 x 64
+// tile of dX0 from the (64 + k - 1)-row window of dC ending at the tile's last row, and for every
+// tap tau the tile's sum over its 64 rows t of dC[t] * X0[t + tau] into part[tile][tau][dm].
+__global__ void __launch_bounds__(256) target_conv_bwd_kernel(const __bf16* __restrict__ dC, const __bf16* __restrict__ X0,
+                                                             const float* __restrict__ taps, int k, int N, int dm,
+                                                             __bf16* __restrict__ dX0, float* __restrict__ part) {
+  __shared__ float wd[64 + 15][65];  // dC rows t0 - (k - 1) .. t0 + 63
+  __shared__ float wx[64 + 15][65];  // X0 rows t0 .. t0 + 63 + (k - 1)
+  __shared__ float tp[16][64];
+  __shared__ float red[4][16][64];
+  const int c0 = blockIdx.x * 64, t0 = blockIdx.y * 64, tid = threadIdx.x;
+  for (int i = tid; i < (64 + k - 1) * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    const int td = t0 - (k - 1) + r, tx = t0 + r;
+    wd[r][c] = td >= 0 ? static_cast<float>(dC[(int64_t)td * dm + c0 + c]) : 0.f;
+    wx[r][c] = tx < N ? static_cast<float>(X0[(int64_t)tx * dm + c0 + c]) : 0.f;
+  }
+  for (int i = tid; i < k * 64; i += 256) tp[i / 64][i % 64] = taps[(int64_t)(i / 64) * dm + c0 + i % 64];
+  __syncthreads();
+  const int c = tid & 63, rq = tid >> 6;  // channel, quarter of the tile's rows
+  float acc[16];
+#pragma unroll
+  for (int tau = 0; tau < 16; ++tau) acc[tau] = 0.f;
+  for (int r = rq * 16; r < rq * 16 + 16; ++r) {
+    // dX0[t0 + r] = sum_tau taps[tau] dC[t0 + r - tau]; window row of dC[t0 + r - tau] is r + k - 1 - tau
+    float s = 0.f;
+    for (int tau = 0; tau < k; ++tau) s = fmaf(tp[tau][c], wd[r + k - 1 - tau][c], s);
+    dX0[(int64_t)(t0 + r) * dm + c0 + c] = static_cast<__bf16>(s);
+    const float d = wd[r + k - 1][c];  // dC[t0 + r]
+#pragma unroll
+    for (int tau = 0; tau < 16; ++tau)
+      if (tau < k) acc[tau] = fmaf(d, wx[r + tau][c], acc[tau]);
+  }
+#pragma unroll
+  for (int tau = 0; tau < 16; ++tau) red[rq][tau][c] = acc[tau];
+  __syncthreads();
+  for (int i = tid; i < k * 64; i += 256) {
+    const int tau = i / 64, cc = i % 64;
+    part[((int64_t)blockIdx.y * k + tau) * dm + c0 + cc] = ((red[0][tau][cc] + red[1][tau][cc]) + red[2][tau][cc]) +
+                                                           red[3][tau][cc];
+  }
+}
+
+// dtaps[tau][c] = sum over tiles (in order) of part[tile][tau][c]. grid-stride over k * dm.
+__global__ void __launch_bounds__(256) target_taps_sum_kernel(const float* __restrict__ part, int ntiles, int k, int dm,
+                                                             float* __restrict__ dtaps) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < k * dm; i += gridDim.x * 256) {
+    float s = 0.f;
+    for (int t = 0; t < ntiles; ++t) s += part[(int64_t)t * k * dm + i];
+    dtaps[i] = s;
+  }
+}
+
+static ttt_status target_check(const ttt_inplace_params& q) {
+  if (q.B < 0 || q.N < 0 || q.d_model <= 0) return TTT_ERR_ARG;
+  if (q.dtype != TTT_FP32 && q.dtype != TTT_BF16) return TTT_ERR_ARG;
+  if (!q.X0 || !q.conv_taps || q.conv_k < 1 || q.conv_k > 16) return TTT_ERR_ARG;
+  if (q.dtype != TTT_BF16) return TTT_ERR_UNSUPPORTED;
+  if (q.d_model % 256 || q.N % 128) return TTT_ERR_SHAPE;
+  return TTT_OK;
+}
+
+}  // namespace ttt
+
+extern "C" ttt_status ttt_inplace_target_forward(const ttt_inplace_params* p, void* Vbar, void* workspace,
+                                                 size_t* workspace_bytes, void* stream) {
+  using namespace gemm;
+  if (!p || !workspace_bytes) return TTT_ERR_ARG;
+  const ttt_inplace_params& q = *p;
+  const ttt_status chk = target_check(q);
+  if (chk != TTT_OK) return chk;
+  const int64_t dm = q.d_model, N = q.N;
+  if (q.B > 0 && N > 0 && !Vbar) return TTT_ERR_ARG;
+  WorkspacePlan plan;
+  const size_t oC = plan.add(q.W_target ? (size_t)N * dm * 2 : 0);  // Conv1D(X0) of one sequence
+  if (!workspace) {
+    *workspace_bytes = plan.total;
+    return TTT_OK;
+  }
+  if (*workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TTT_ERR_WORKSPACE;
+  if (q.B == 0 || N == 0) return TTT_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  static const hipError_t lds_ok = [] {
+    hipError_t e = allow_lds(gemm_tn_kernel<EPI_STORE>, lds_bytes<EPI_STORE>());
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
+    return e;
+  }();
+  TTT_HIP(lds_ok);
+  LaunchTimer lt(K_INP_PREP, st);
+  for (int b = 0; b < q.B; ++b) {
+    const __bf16* Xb = static_cast<const __bf16*>(q.X0) + (int64_t)b * N * dm;
+    __bf16* Vb = static_cast<__bf16*>(Vbar) + (int64_t)b * N * dm;
+    __bf16* Cb = q.W_target ? reinterpret_cast<__bf16*>(static_cast<char*>(workspace) + oC) : Vb;
+    hipLaunchKernelGGL(target_conv_kernel<false>, dim3((unsigned)(dm / 64), (unsigned)(N / 64)), dim3(256), 0, st, Xb,
+                       q.conv_taps, q.conv_k, (int)N, (int)dm, Cb);
+    TTT_HIP(hipGetLastError());
+    if (q.W_target) {  // Vbar = C W_target^T: A = C [N][in], B = W_target [out][in]
+      Args t{};
+      t.A = Cb;
+      t.lda = dm;
+      t.B0 = static_cast<const __bf16*>(q.W_target);
+      t.ldb = dm;
+      t.M = (int)N;
+      t.N = (int)dm;
+      t.K = (int)dm;
+      t.C = Vb;
+      t.ldc = dm;
+      TTT_HIP(run_gemm<EPI_STORE>(K_INP_PREP, t, 1, nullptr, st));
+    }
+  }
+  return TTT_OK;
+}
+
+extern "C" ttt_status ttt_inplace_target_backward(const ttt_inplace_params* p, const void* dVbar, void* dX0, float* dtaps,
+                                                  float* dW_target, void* workspace, size_t* workspace_bytes,
+                                                  void* stream) {
+  using namespace gemm;
+  if (!p || !workspace_bytes) return TTT_ERR_ARG;
+  const ttt_inplace_params& q = *p;
+  const ttt_status chk = target_check(q);
+  if (chk != TTT_OK) return chk;
+  const int64_t dm = q.d_model, N = q.N, k = q.conv_k;
+  if (q.B > 0 && (!dtaps || (q.W_target != nullptr) != (dW_target != nullptr))) return TTT_ERR_ARG;
+  if (q.B > 0 && N > 0 && (!dVbar || !dX0)) return TTT_ERR_ARG;
+  const int64_t nt = N / 64;  // token tiles of a sequence
+  WorkspacePlan plan;
+  const size_t odC = plan.add(q.W_target ? (size_t)N * dm * 2 : 0);   // dC = dVbar W_target
+  const size_t oCt = plan.add(q.W_target ? (size_t)dm * N * 2 : 0);   // C^T
+  const size_t odVt = plan.add(q.W_target ? (size_t)dm * N * 2 : 0);  // dVbar^T
+  const size_t oWtT = plan.add(q.W_target ? (size_t)dm * dm * 2 : 0); // W_target^T
+  const size_t oPart = plan.add((size_t)std::max<int64_t>(q.B * nt, 1) * k * dm * 4);
+  if (!workspace) {
+    *workspace_bytes = plan.total;
+    return TTT_OK;
+  }
+  if (*workspace_bytes < plan.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TTT_ERR_WORKSPACE;
+  if (q.B == 0) return TTT_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto bfp = [&](size_t o) { return reinterpret_cast<__bf16*>(ws + o); };
+  float* part = reinterpret_cast<float*>(ws + oPart);
+  static const hipError_t lds_ok = [] {
+    hipError_t e = allow_lds(gemm_tn_kernel<EPI_STORE>, lds_bytes<EPI_STORE>());
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_STORE>, gemm2::LDS);
+    if (e == hipSuccess) e = allow_lds(gemm2::gemm_big_kernel<EPI_RMW>, gemm2::LDS);
+    return e;
+  }();
+  TTT_HIP(lds_ok);
+  LaunchTimer lt(K_INP_PREP, st);
+  if (N == 0) {  // no tokens: zero gradients of the taps and the projection
+    hipLaunchKernelGGL(f32_zero_add_kernel, dim3(64), dim3(256), 0, st, dtaps, static_cast<const float*>(nullptr), k * dm, 0);
+    if (dW_target)
+      hipLaunchKernelGGL(f32_zero_add_kernel, dim3(1024), dim3(256), 0, st, dW_target, static_cast<const float*>(nullptr),
+                         dm * dm, 0);
+    TTT_HIP(hipGetLastError());
+    return TTT_OK;
+  }
+  if (q.W_target) {
+    hipLaunchKernelGGL(f32_zero_add_kernel, dim3(1024), dim3(256), 0, st, dW_target, static_cast<const float*>(nullptr),
+                       dm * dm, 0);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(dm / 64), (unsigned)(dm / 64)), dim3(256), 0, st,
+                       static_cast<const __bf16*>(q.W_target), bfp(oWtT), (int)dm, (int)dm);
+    TTT_HIP(hipGetLastError());
+  }
+  for (int b = 0; b < q.B; ++b) {
+    const __bf16* Xb = static_cast<const __bf16*>(q.X0) + (int64_t)b * N * dm;
+    const __bf16* dVb = static_cast<const __bf16*>(dVbar) + (int64_t)b * N * dm;
+    const __bf16* dC = dVb;
+    if (q.W_target) {
+      // dW_target += dVbar^T C: A = dVbar^T [out][N], B = C^T [in][N], K = N (one long product)
+      hipLaunchKernelGGL(target_conv_kernel<true>, dim3((unsigned)(dm / 64), (unsigned)(N / 64)), dim3(256), 0, st, Xb,
+                         q.conv_taps, (int)k, (int)N, (int)dm, bfp(oCt));
+      hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(dm / 64), (unsigned)(N / 64)), dim3(256), 0, st, dVb,
+                         bfp(odVt), (int)N, (int)dm);
+      TTT_HIP(hipGetLastError());
+      Args u{};
+      u.A = bfp(odVt);
+      u.lda = N;
+      u.B0 = bfp(oCt);
+      u.ldb = N;
+      u.M = (int)dm;
+      u.N = (int)dm;
+      u.K = (int)N;
+      u.Wf = dW_target;
+      u.Wsh = nullptr;
+      u.ldw = dm;
+      u.alpha = 1.f;
+      TTT_HIP(launch_k(K_INP_PREP, gemm2::gemm_big_kernel<EPI_RMW>, dim3((unsigned)((dm / 256) * (dm / 256))),
+                       dim3(gemm2::THREADS), gemm2::LDS, st, u, 1, static_cast<float*>(nullptr)));
+      // dC = dVbar W_target: A = dVbar [N][out], B = W_target^T [in][out]
+      Args t{};
+      t.A = dVb;
+      t.lda = dm;
+      t.B0 = bfp(oWtT);
+      t.ldb = dm;
+      t.M = (int)N;
+      t.N = (int)dm;
+      t.K = (int)dm;
+      t.C = bfp(odC);
+      t.ldc = dm;
+      TTT_HIP(run_gemm<EPI_STORE>(K_INP_PREP, t, 1, nullptr, st));
+      dC = bfp(odC);
+    }
+    hipLaunchKernelGGL(target_conv_bwd_kernel, dim3((unsigned)(dm / 64), (unsigned)nt), dim3(256), 0, st, dC, Xb,
+                       q.conv_taps, (int)k, (int)N, (int)dm, static_cast<__bf16*>(dX0) + (int64_t)b * N * dm,
+                       part + (int64_t)b * nt * k * dm);
+    TTT_HIP(hipGetLastError());
+  }
+  hipLaunchKernelGGL(target_taps_sum_kernel, dim3((unsigned)((k * dm + 255) / 256)), dim3(256), 0, st, part,
+                     (int)(q.B * nt), (int)k, (int)dm, dtaps);
+  TTT_HIP(hipGetLastError());
+  return TTT_OK;
+}

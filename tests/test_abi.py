@@ -283,6 +283,37 @@ def test_inplace_backward_query_and_validation(lib):
     assert _inp_bwd(lib, B=0)[0] == ttt.TTT_OK
 
 
+def test_inplace_target_entry_points_query_and_validation(lib):
+    def q(fn, **kw):
+        base = dict(B=1, N=32768, d_model=4096, d_hidden=0, chunk=1, eta=0.0, dtype=ttt.BF16, wdown_batch_stride=0,
+                    X0=0x3000, conv_taps=0x4000, W_target=None, conv_k=2)
+        base.update(kw)
+        p = ttt.InplaceParams(**base)
+        sz = ctypes.c_size_t(0)
+        if fn == "fwd":
+            st = lib.ttt_inplace_target_forward(ctypes.byref(p), FAKE, None, ctypes.byref(sz), None)
+        else:
+            st = lib.ttt_inplace_target_backward(ctypes.byref(p), FAKE, FAKE, FAKE,
+                                                 FAKE if base["W_target"] else None, None, ctypes.byref(sz), None)
+        return st, sz.value
+    for fn in ("fwd", "bwd"):
+        st, plain = q(fn)
+        assert st == ttt.TTT_OK, fn
+        st, proj = q(fn, W_target=0x5000)
+        assert st == ttt.TTT_OK and proj > plain, fn
+        assert q(fn, conv_k=0)[0] == ttt.TTT_ERR_ARG
+        assert q(fn, conv_k=17)[0] == ttt.TTT_ERR_ARG
+        assert q(fn, X0=None)[0] == ttt.TTT_ERR_ARG
+        assert q(fn, dtype=ttt.FP32)[0] == ttt.TTT_ERR_UNSUPPORTED
+        assert q(fn, d_model=4096 + 128)[0] == ttt.TTT_ERR_SHAPE
+        assert q(fn, N=32768 + 64)[0] == ttt.TTT_ERR_SHAPE
+    # the projection's gradient is written exactly when there is a projection
+    p = ttt.InplaceParams(1, 256, 256, 0, 1, 0.0, ttt.BF16, 0, 0x3000, 0x4000, 0x5000, 2)
+    sz = ctypes.c_size_t(0)
+    assert lib.ttt_inplace_target_backward(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, ctypes.byref(sz),
+                                           None) == ttt.TTT_ERR_ARG
+
+
 class _FakeCuda:
     """Stands in for a device tensor in the binding's checks (they run before any launch)."""
     is_cuda = True

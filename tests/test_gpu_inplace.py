@@ -216,3 +216,87 @@ def test_backward_empty_sequence(lib, per_seq):
     for k in ("dW_gate", "dW_up", "dW_down"):
         assert not bool(got[k].any()), k
     assert got["dHs"].numel() == 0 and got["dVbar"].numel() == 0
+
+
+# ---- the LM-aligned target on its own, and the gradients reaching X0, the taps, W_target ----
+
+def _target_case(seed, B=2, N=512, d=256, k=3, proj=True):
+    rng = np.random.default_rng(seed)
+    from workloads import bf16_round
+    X0 = bf16_round(rng.standard_normal((B, N, d)).astype(np.float32))
+    taps = rng.standard_normal((k, d)).astype(np.float32)
+    W = bf16_round((rng.standard_normal((d, d)) / np.sqrt(d)).astype(np.float32)) if proj else None
+    return X0, taps, W
+
+
+@pytest.mark.parametrize("proj,k", [(False, 2), (True, 3), (True, 16)])
+def test_target_forward_and_backward_against_the_oracle(lib, proj, k):
+    import torch
+    from oracle import inplace as IP
+    from workloads import bf16_round
+    X0, taps, W = _target_case(70 + k, k=k, proj=proj)
+    announce(f"inplace target forward/backward k={k} projection={proj}")
+    dX = dev(X0, torch.bfloat16)
+    dT = dev(taps, torch.float32)
+    dW = None if W is None else dev(W, torch.bfloat16)
+    V = lib.inplace_target_forward(dX, dT, dW)
+    refV = np.stack([IP.lm_aligned_target(X0[b], taps, W) for b in range(2)])
+    ev = max_abs_rel(host(V), refV)
+    dV = bf16_round(np.random.default_rng(k).standard_normal(X0.shape).astype(np.float32))
+    g = lib.inplace_target_backward(dX, dT, dev(dV, torch.bfloat16), dW)
+    refs = [IP.lm_aligned_target_backward(X0[b], taps, W, dV[b]) for b in range(2)]
+    errs = dict(V=ev, dX0=max_abs_rel(host(g["dX0"]), np.stack([r[0] for r in refs])),
+                dtaps=max_abs_rel(host(g["dtaps"]), sum(r[1] for r in refs)))
+    if proj:
+        errs["dW_target"] = max_abs_rel(host(g["dW_target"]), sum(r[2] for r in refs))
+    else:
+        assert g["dW_target"] is None
+    print("target: " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()), flush=True)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+def test_update_with_the_target_built_alone_matches_the_built_in_target(lib):
+    """ttt_inplace_down_forward with X0 given and with Vbar from ttt_inplace_target_forward give
+    the same outputs bit for bit (the projection's products, in either orientation, sum the same
+    terms in the same order)."""
+    import torch
+    p = InplaceProblem(B=2, N=512, d_model=256, d_hidden=512, chunk=128, eta=0.05)
+    announce("inplace target built alone vs built in")
+    x = make_inplace_inputs(p, 660)
+    X0, taps, W = _target_case(661, N=512, d=256, k=3)
+    dW = dev(W, torch.bfloat16)
+    args = [dev(x[k], torch.bfloat16) for k in ("Hs", "W_gate", "W_up")] + [dev(x["W_down"], torch.float32)]
+    V = lib.inplace_target_forward(dev(X0, torch.bfloat16), dev(taps, torch.float32), dW)
+    O1, W1 = lib.inplace_down_forward(*args, V, chunk=p.chunk, eta=p.eta)
+    O2, W2 = lib.inplace_down_forward(*args, None, chunk=p.chunk, eta=p.eta, X0=dev(X0, torch.bfloat16),
+                                      conv_taps=dev(taps, torch.float32), W_target=dW)
+    assert torch.equal(O1, O2) and torch.equal(W1, W2)
+
+
+def test_backward_through_the_lm_aligned_target(lib):
+    """Every gradient of the update with the LM-aligned target: the update's backward with Vbar
+    from ttt_inplace_target_forward, chained through ttt_inplace_target_backward, against the
+    oracle's chain (dX0, dtaps, dW_target and the update's own gradients)."""
+    import torch
+    from oracle import inplace as IP
+    from workloads import bf16_round
+    p = InplaceProblem(B=2, N=512, d_model=256, d_hidden=512, chunk=128, eta=0.02)
+    announce("inplace backward through the LM-aligned target")
+    x = make_inplace_inputs(p, 670)
+    X0, taps, W = _target_case(671, N=512, d=256, k=2)
+    dO = bf16_round(np.random.default_rng(672).standard_normal((2, 512, 256)).astype(np.float32))
+    dX, dT, dW = dev(X0, torch.bfloat16), dev(taps, torch.float32), dev(W, torch.bfloat16)
+    V = lib.inplace_target_forward(dX, dT, dW)
+    args = [dev(x[k], torch.bfloat16) for k in ("Hs", "W_gate", "W_up")] + [dev(x["W_down"], torch.float32)]
+    g = lib.inplace_down_backward(*args, V, dev(dO, torch.bfloat16), chunk=p.chunk, eta=p.eta)
+    t = lib.inplace_target_backward(dX, dT, g["dVbar"], dW)
+    Vref = np.stack([IP.lm_aligned_target(X0[b], taps, W) for b in range(2)])
+    ref = IP.inplace_backward(x["Hs"], x["W_gate"], x["W_up"], x["W_down"], Vref, p.eta, dO, chunk=p.chunk)
+    tref = [IP.lm_aligned_target_backward(X0[b], taps, W, ref["dVbar"][b]) for b in range(2)]
+    errs = dict(dHs=max_abs_rel(host(g["dHs"]), ref["dH"]), dW_gate=max_abs_rel(host(g["dW_gate"]), ref["dW_gate"]),
+                dW_down=max_abs_rel(host(g["dW_down"]), ref["dW_down"]),
+                dX0=max_abs_rel(host(t["dX0"]), np.stack([r[0] for r in tref])),
+                dtaps=max_abs_rel(host(t["dtaps"]), sum(r[1] for r in tref)),
+                dW_target=max_abs_rel(host(t["dW_target"]), sum(r[2] for r in tref)))
+    print("through the target: " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()), flush=True)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
