@@ -72,16 +72,16 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag_kmajor(const T* base
 // Staging of a 64-token tile of K and V: each thread moves NCH 16-byte chunks per tensor from
 // global memory (rows beyond the segment are zero) through registers into row-major LDS
 // [t][c], converting to the operand type on the way.
-template <class IoT, class OpT, int H>
+template <class IoT, class OpT, int H, int NTHR = 256>
 struct TileStage {
   static constexpr int VE = Io<IoT>::VEC;                 // elements per 16-byte chunk
-  static constexpr int NCH = TT * H / VE / 256;           // chunks per thread per tensor
-  static_assert(TT * H % (VE * 256) == 0, "staging map");
+  static constexpr int NCH = TT * H / VE / NTHR;          // chunks per thread per tensor (NTHR threads)
+  static_assert(TT * H % (VE * NTHR) == 0, "staging map");
   u32x4 k[NCH], v[NCH];
   __device__ __forceinline__ void load(const IoT* Kp, const IoT* Vp, int t0, int t_end, int tid) {
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int ch = tid + 256 * q;
+      const int ch = tid + NTHR * q;
       const int row = ch / (H / VE), col = (ch % (H / VE)) * VE;
       if (t0 + row < t_end) {
         k[q] = *reinterpret_cast<const u32x4*>(Kp + (int64_t)(t0 + row) * H + col);
@@ -109,7 +109,7 @@ struct TileStage {
   __device__ __forceinline__ void store_at(OpT* Ks, OpT* Vs, int tid) const {
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int ch = tid + 256 * q;
+      const int ch = tid + NTHR * q;
       const int row = ch / (H / VE), col = (ch % (H / VE)) * VE;
       put(k[q], Ks + TL::at(row, col));
       put(v[q], Vs + TL::at(row, col));
@@ -118,7 +118,7 @@ struct TileStage {
   __device__ __forceinline__ void store(OpT* Ks, OpT* Vs, int ld, int tid) const {
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int ch = tid + 256 * q;
+      const int ch = tid + NTHR * q;
       const int row = ch / (H / VE), col = (ch % (H / VE)) * VE;
       put(k[q], Ks + row * ld + col);
       put(v[q], Vs + row * ld + col);
@@ -175,14 +175,16 @@ constexpr int grad_lds_bytes() {
          16 * 4;
 }
 
-// grid: x = hidden block (rh/64), y = token segment, z = pair. block: 256 threads (4 waves).
-// Per 64-token tile: K and V are staged row-major in LDS (the next tile is prefetched into
-// registers meanwhile); wave (th, jh) forms A^T, Bm^T, D^T for hidden rows jh*32.. and tokens
-// th*32.. (operands: fast-weight rows and token rows, both K-contiguous), the SwiGLU / silu'
-// epilogue writes eta*H, X0, X2 as [j][t] tiles, and the token contractions read K and V
-// K-major through the LDS transpose read.
-template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID, bool E3 = false>
-__global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
+// grid: x = hidden block (rh/64), y = token segment, z = pair. block: 64 NWV threads (NWV waves).
+// Per 64-token tile: K and V are staged row-major in LDS by all threads (the next tile is
+// prefetched into registers meanwhile); wave (th, jh) < 4 forms A^T, Bm^T, D^T for hidden rows
+// jh*32.. and tokens th*32.. (operands: fast-weight rows and token rows, both K-contiguous), the
+// SwiGLU / silu' epilogue writes eta*H, X0, X2 as [j][t] tiles, and the token contractions, split
+// over all NWV waves, read K and V K-major through the LDS transpose read. With eight waves (two
+// per SIMD) each wave holds half the contraction accumulators of the four-wave form, and the
+// register file takes both.
+template <class IoT, class OpT, int H, bool LINATTN, bool SCALE_MID, bool E3 = false, int NWV = NWAVE>
+__global__ void __launch_bounds__(64 * NWV) grad_kernel(GradArgs a) {
   static_assert(!(E3 && LINATTN), "one step size per token in linear-attention mode");
   constexpr int NE = E3 ? 3 : 1;  // step-size rows
   typedef Mfma<OpT> M;
@@ -194,8 +196,9 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   constexpr int NMAT = LINATTN ? 1 : 3;
   constexpr int CB = H / 32;                       // 32-wide column blocks of H
   constexpr int NQ = NMAT * 2 * CB;                // gradient C tiles per workgroup
-  constexpr int NT = (NQ + NWAVE - 1) / NWAVE;     // per wave
+  constexpr int NT = (NQ + NWV - 1) / NWV;         // per wave
   constexpr int KS = H / M::KSTEP;                 // K steps over H
+  constexpr int NTH = 64 * NWV;                    // threads; waves 4.. only join the contractions
 
   extern __shared__ __align__(16) unsigned char smem[];
   OpT* Wb = reinterpret_cast<OpT*>(smem);                    // [nW][RB][LDW]
@@ -214,7 +217,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   const IoT* Vp = reinterpret_cast<const IoT*>(a.V) + pair * a.tok_pair_stride;
   const float* ep = a.eta + pair * a.eta_pair_stride;
 
-  TileStage<IoT, OpT, H> stage;
+  TileStage<IoT, OpT, H, NTH> stage;
   stage.load(Kp, Vp, t_begin, t_end, tid);
 
   // --- stage this hidden block of the fast weights ---------------------------------------
@@ -224,7 +227,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
     constexpr int VPR = H * (int)sizeof(OpT) / 16;  // 16-byte vectors per row
     for (int m = 0; m < nW; ++m) {
       const OpT* s = src[m] + pair * a.w_pair_stride + (int64_t)jb * RB * H;
-      for (int i = tid; i < RB * VPR; i += 256) {
+      for (int i = tid; i < RB * VPR; i += NTH) {
         const int row = i / VPR, v = i % VPR;
         *reinterpret_cast<u32x4*>(Wb + (m * RB + row) * LDW + v * (16 / sizeof(OpT))) =
             *reinterpret_cast<const u32x4*>(s + row * H + v * (16 / sizeof(OpT)));
@@ -237,7 +240,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   if constexpr (SCALE_MID) {
     float mx = 0.f;
     for (int e = 0; e < NE; ++e)
-      for (int t = t_begin + tid; t < t_end; t += 256) mx = fmaxf(mx, ep[e * a.eta_mat_stride + t]);
+      for (int t = t_begin + tid; t < t_end; t += NTH) mx = fmaxf(mx, ep[e * a.eta_mat_stride + t]);
     mx = block_max(mx, red);
     if (mx > 0.f) scale = exp2f(-floorf(log2f(mx)));
   }
@@ -258,7 +261,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
     if (t0 + TT < t_end) stage.load(Kp, Vp, t0 + TT, t_end, tid);  // in flight during the MFMAs
 
     // forward products for (hidden rows jh*32.., tokens th*32..): A^T, Bm^T, D^T
-    {
+    if (w < 4) {
       f32x16 fa, fb, fd;
       zero(fa);
       zero(fb);
@@ -297,7 +300,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
     // token contractions: P1 += (eta H)^T V, P0 += X0^T K, P2 += X2^T K (rows j, cols c)
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const int q = w + NWAVE * i;
+      const int q = w + NWV * i;
       if (q < NQ) {
         const int mat = q / (2 * CB), jhq = (q / CB) % 2, cb = q % CB;
         const OpT* am = Mid + (mat * RB + jhq * 32 + (lane & 31)) * LDT + (lane >> 5) * M::KSUB;
@@ -314,7 +317,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   float* ob = a.out + seg * a.out_y_stride + pair * a.out_pair_stride;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    const int q = w + NWAVE * i;
+    const int q = w + NWV * i;
     if (q < NQ) {
       const int mat = q / (2 * CB), jhq = (q / CB) % 2, cb = q % CB;
       const int omat = LINATTN ? 0 : (mat == 0 ? 1 : (mat == 1 ? 0 : 2));

@@ -211,7 +211,9 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   // eta per matrix: the E3 instances of the gradient kernels
   typedef typename std::conditional<WS, IoT, bf16_t>::type WIoT;
   const bool e3 = p.eta_per_matrix != 0;
-  auto gk = e3 ? grad_kernel<IoT, OpT, H, false, SCALE, true> : grad_kernel<IoT, OpT, H, false, SCALE, false>;
+  // the LDS-staged gradient kernel at h = 192: eight waves, the contractions split over all of them
+  constexpr int GW = H == 192 ? 8 : NWAVE;
+  auto gk = e3 ? grad_kernel<IoT, OpT, H, false, SCALE, true, GW> : grad_kernel<IoT, OpT, H, false, SCALE, false, GW>;
   auto gkr = e3 ? grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, true>
                 : grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, false>;
   auto gkw = e3 ? grad_ws_kernel<WIoT, _Float16, (WS ? H : 128), true, true>
@@ -236,7 +238,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
                  : grad_ws_kernel<WIoT, _Float16, (WS ? H : 128), true, false>;
       auto kr = v ? grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, true>
                   : grad_rd_kernel<IoT, OpT, (RD ? H : 128), false, SCALE, false>;
-      auto kg = v ? grad_kernel<IoT, OpT, H, false, SCALE, true> : grad_kernel<IoT, OpT, H, false, SCALE, false>;
+      auto kg = v ? grad_kernel<IoT, OpT, H, false, SCALE, true, GW> : grad_kernel<IoT, OpT, H, false, SCALE, false, GW>;
       e = WS ? allow_lds(k, glds) : RD ? allow_lds(kr, glds) : allow_lds(kg, glds);
     }
     return e != hipSuccess ? e : (ARD ? allow_lds(akr, alds) : allow_lds(ak, alds));
@@ -401,7 +403,7 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
         else if constexpr (RD)
           TTT_HIP(launch_k(K_LACT_GRAD, gkr, dim3(grid), dim3(256), gl, st, ga, S, P));
         else
-          TTT_HIP(launch_k(K_LACT_GRAD, gk, dim3(rh / RB, S, P), dim3(256), gl, st, ga));
+          TTT_HIP(launch_k(K_LACT_GRAD, gk, dim3(rh / RB, S, P), dim3(64 * GW), gl, st, ga));
       }
       if (fuse_ua && k == 0) {  // the chunk's apply reads the chunk-start weights (buffer rd)
         int nu = nupd;
