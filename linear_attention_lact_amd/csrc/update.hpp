@@ -18,6 +18,10 @@
 // workgroups need to exchange data. Products run in split-bf16 (x = hi + lo, three MFMA products
 // per multiply) because the iteration amplifies rounding in weak singular directions by up to
 // 3.4445^5; fp32 state, fp32 matrix masters in registers.
+// Every h x h matrix of the rounds (A_k, A_k^2, P_k, P_k A_k, Q) is a polynomial in A_0, hence
+// symmetric: each product forms only the 32 x 32 blocks on and above the diagonal (10 of 16 at
+// h = 128) and stores them, transposed, below it; an operand row block is read directly where it
+// lies on or below the diagonal and through the transpose read of its mirror block above it.
 #pragma once
 #include "common.hpp"
 #include "fastweight.hpp"
@@ -96,73 +100,122 @@ __device__ __forceinline__ void store4(T* p, f32x4 v) {
   }
 }
 
-// Split-bf16 product of Q consecutive 32 x 32 output blocks that share their A rows:
-//   c[q] += (Ah + Al)[32 x K] (Bh + Bl)[block q]^T, the lo*lo term dropped.
-// TA / TB: operand stored K-major (element (k, m) at base[k * ld + m], LDS transpose read);
-// otherwise row-major with K contiguous (element (m, k) at base[m * ld + k]).
-// B block q starts at Bh + q * 32 (TB) or Bh + q * 32 * ldb. The hi*hi and the cross products
-// accumulate in separate registers and are added at the end.
-template <int K, int Q, bool TA, bool TB>
-__device__ __forceinline__ void mma_split(f32x16 (&c)[Q], const bf16* Ah, const bf16* Al, int lda,
-                                          const bf16* Bh, const bf16* Bl, int ldb, int lane) {
-  typedef Mfma<bf16> M;
-  const int ro = lane & 31, ko = (lane >> 5) * 8;
+// Upper-triangle 32 x 32 blocks of an h x h symmetric product, as per-wave tasks: wave w forms
+// cnt (0..2) blocks (I0, J0) and (I1, J1), packed as I0 | J0 << 4 | I1 << 8 | J1 << 12 | cnt << 16.
+// A SIMD runs waves s and s + 4. The diagonal blocks, whose stores also make them exactly
+// symmetric (a second, masked store), sit alone on waves 4-7; at h = 128 the six blocks above the
+// diagonal go to waves 0-3, two of them in pairs that share an operand row block ((0,1) and
+// (0,2) share X rows 0; (0,3) and (1,3) share Y rows 3), so that no SIMD forms more than three
+// blocks and no wave both stores two blocks and symmetrizes one.
+template <int HB>
+__host__ __device__ constexpr int sym_task(int w) {
+  static_assert(HB >= 1 && HB <= 4, "h <= 128");
+  constexpr int S = 1 << 16, D = 2 << 16;
+  constexpr int T1[8] = {0 | 0 << 4 | S, 0, 0, 0, 0, 0, 0, 0};
+  constexpr int T2[8] = {0 | 1 << 4 | S, 0 | 0 << 4 | S, 1 | 1 << 4 | S, 0, 0, 0, 0, 0};
+  constexpr int T3[8] = {0 | 1 << 4 | S, 0 | 2 << 4 | S, 1 | 2 << 4 | S, 0,
+                         0 | 0 << 4 | S, 1 | 1 << 4 | S, 2 | 2 << 4 | S, 0};
+  constexpr int T4[8] = {0 | 1 << 4 | 0 << 8 | 2 << 12 | D, 0 | 3 << 4 | 1 << 8 | 3 << 12 | D, 1 | 2 << 4 | S,
+                         2 | 3 << 4 | S, 0 | 0 << 4 | S, 1 | 1 << 4 | S, 2 | 2 << 4 | S, 3 | 3 << 4 | S};
+  return HB == 1 ? T1[w] : HB == 2 ? T2[w] : HB == 3 ? T3[w] : T4[w];
+}
+
+// One K step (16) of a row-block operand of a symmetric matrix kept as its lower triangle of
+// 32 x 32 blocks in an [h][ld] slot: rows 32 B .. 32 B + 31, columns k .. k + 15. Blocks on or
+// below the diagonal (k / 32 <= B) are read as rows; above it the mirror block (k / 32, B) is read
+// K-major with the transpose read, which yields the same fragment layout. B is a template
+// argument and k a constant of a fully unrolled loop, so no branch remains.
+template <int B>
+__device__ __forceinline__ bf16x8 sym_frag(const __bf16* S, int ld, int k, int lane) {
+  if ((k >> 5) <= B) return Mfma<__bf16>::load(S + (32 * B + (lane & 31)) * ld + k + 8 * (lane >> 5));
+  return load_frag_tr<__bf16>(S + 32 * B, ld, k, lane);
+}
+
+// c[q] += X[rows of block Iq] Y[rows of block Jq]^T (q < Q) for symmetric X, Y in slots of row
+// stride ld (lower-triangle storage above), split-bf16 with the cross terms in separate
+// registers; X Y^T = X Y for symmetric Y. A row block shared by the two blocks is read once.
+template <int K, int Q, int I0, int J0, int I1, int J1>
+__device__ __forceinline__ void mma_sym(f32x16* c, const __bf16* Xh, const __bf16* Xl, const __bf16* Yh,
+                                        const __bf16* Yl, int ld, int lane) {
+  typedef Mfma<__bf16> M;
+  constexpr int NK = K / 16;
+  constexpr bool NA1 = Q == 2 && I1 != I0, NB1 = Q == 2 && J1 != J0;  // second blocks' own operands
   f32x16 d[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) zero(d[q]);
-#pragma unroll 8
-  for (int k = 0; k < K; k += 16) {
-    bf16x8 ah, al;
-    if constexpr (TA) {
-      ah = load_frag_tr<bf16>(Ah, lda, k, lane);
-      al = load_frag_tr<bf16>(Al, lda, k, lane);
-    } else {
-      ah = M::load(Ah + ro * lda + ko + k);
-      al = M::load(Al + ro * lda + ko + k);
+  // fragments of K step k + 1 are requested before the products of step k (two register sets),
+  // so that a wave alone on its SIMD does not wait on LDS between its products
+  bf16x8 f[2][8];
+  auto fetch = [&](bf16x8 (&g)[8], int k) {
+    g[0] = sym_frag<I0>(Xh, ld, k, lane);
+    g[1] = sym_frag<I0>(Xl, ld, k, lane);
+    g[2] = sym_frag<J0>(Yh, ld, k, lane);
+    g[3] = sym_frag<J0>(Yl, ld, k, lane);
+    if constexpr (NA1) {
+      g[4] = sym_frag<I1>(Xh, ld, k, lane);
+      g[5] = sym_frag<I1>(Xl, ld, k, lane);
     }
+    if constexpr (NB1) {
+      g[6] = sym_frag<J1>(Yh, ld, k, lane);
+      g[7] = sym_frag<J1>(Yl, ld, k, lane);
+    }
+  };
+  fetch(f[0], 0);
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      bf16x8 bh, bl;
-      if constexpr (TB) {
-        bh = load_frag_tr<bf16>(Bh + q * 32, ldb, k, lane);
-        bl = load_frag_tr<bf16>(Bl + q * 32, ldb, k, lane);
-      } else {
-        bh = M::load(Bh + (q * 32 + ro) * ldb + ko + k);
-        bl = M::load(Bl + (q * 32 + ro) * ldb + ko + k);
-      }
-      c[q] = M::mma(ah, bh, c[q]);
-      d[q] = M::mma(ah, bl, d[q]);
-      d[q] = M::mma(al, bh, d[q]);
+  for (int s = 0; s < NK; ++s) {
+    if (s + 1 < NK) fetch(f[(s + 1) & 1], 16 * (s + 1));
+    const bf16x8(&g)[8] = f[s & 1];
+    c[0] = M::mma(g[0], g[2], c[0]);
+    d[0] = M::mma(g[0], g[3], d[0]);
+    d[0] = M::mma(g[1], g[2], d[0]);
+    if constexpr (Q == 2) {
+      const bf16x8 ah = NA1 ? g[4] : g[0], al = NA1 ? g[5] : g[1];
+      const bf16x8 bh = NB1 ? g[6] : g[2], bl = NB1 ? g[7] : g[3];
+      c[1] = M::mma(ah, bh, c[1]);
+      d[1] = M::mma(ah, bl, d[1]);
+      d[1] = M::mma(al, bh, d[1]);
     }
   }
 #pragma unroll
   for (int q = 0; q < Q; ++q) c[q] += d[q];
 }
 
-// Blocks t = Q*w + q (q < Q) of an NB-block output grid with BPR blocks per row: block t is
-// (t / BPR, t % BPR), its A operand the 32-block t / BPR, its B operand the 32-block t % BPR.
-// A wave's blocks share their A operand when BPR % Q == 0; otherwise each is formed alone.
-template <int K, int Q, int BPR, int NB, bool TA, bool TB>
-__device__ __forceinline__ void mma_blocks(f32x16 (&c)[Q], int w, const bf16* Ah, const bf16* Al, int lda,
-                                           const bf16* Bh, const bf16* Bl, int ldb, int lane) {
-  auto aoff = [&](int b) { return TA ? b * 32 : b * 32 * lda; };
-  auto boff = [&](int b) { return TB ? b * 32 : b * 32 * ldb; };
-  if constexpr (BPR % Q == 0) {
-    const int t0 = Q * w;
-    if (t0 < NB)
-      mma_split<K, Q, TA, TB>(c, Ah + aoff(t0 / BPR), Al + aoff(t0 / BPR), lda, Bh + boff(t0 % BPR),
-                              Bl + boff(t0 % BPR), ldb, lane);
-  } else {
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int t = Q * w + q;
-      if (t < NB) {
-        f32x16 one[1] = {c[q]};
-        mma_split<K, 1, TA, TB>(one, Ah + aoff(t / BPR), Al + aoff(t / BPR), lda, Bh + boff(t % BPR),
-                                Bl + boff(t % BPR), ldb, lane);
-        c[q] = one[0];
-      }
-    }
+template <int K, int HB, int W>
+__device__ __forceinline__ void sym_product_w(f32x16* c, const __bf16* Xh, const __bf16* Xl, const __bf16* Yh,
+                                              const __bf16* Yl, int ld, int lane) {
+  constexpr int v = sym_task<HB>(W), CNT = v >> 16;
+  if constexpr (CNT > 0)
+    mma_sym<K, CNT, v & 15, (v >> 4) & 15, (v >> 8) & 15, (v >> 12) & 15>(c, Xh, Xl, Yh, Yl, ld, lane);
+}
+
+// the task of wave w (wave-uniform) of the symmetric product, each task its own unrolled code
+template <int K, int HB>
+__device__ __forceinline__ void sym_product(f32x16* c, int w, const __bf16* Xh, const __bf16* Xl,
+                                            const __bf16* Yh, const __bf16* Yl, int ld, int lane) {
+  switch (w) {
+    case 0: sym_product_w<K, HB, 0>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+    case 1: sym_product_w<K, HB, 1>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+    case 2: sym_product_w<K, HB, 2>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+    case 3: sym_product_w<K, HB, 3>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+    case 4: sym_product_w<K, HB, 4>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+    case 5: sym_product_w<K, HB, 5>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+    case 6: sym_product_w<K, HB, 6>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+    default: sym_product_w<K, HB, 7>(c, Xh, Xl, Yh, Yl, ld, lane); break;
+  }
+}
+
+// the task of a wave index known only at run time (a select chain, no indexed local array)
+template <int HB>
+__device__ __forceinline__ int sym_task_of(int w) {
+  switch (w) {
+    case 0: return sym_task<HB>(0);
+    case 1: return sym_task<HB>(1);
+    case 2: return sym_task<HB>(2);
+    case 3: return sym_task<HB>(3);
+    case 4: return sym_task<HB>(4);
+    case 5: return sym_task<HB>(5);
+    case 6: return sym_task<HB>(6);
+    default: return sym_task<HB>(7);
   }
 }
 
@@ -188,7 +241,7 @@ struct UpdLayout {
   static constexpr int HB = H / 32, NJ = RH / 32;
   static constexpr int NJW = (NJ + 7) / 8;     // state-row blocks per wave in the final product
   static constexpr int bytes = R + (8 * H + 32) * 4;      // + column-norm partials [8][H], [32]
-  static constexpr int NBA = HB * HB, QA = (NBA + 7) / 8;   // h x h blocks per wave
+  static constexpr int QS = HB == 4 ? 2 : 1;                // upper-triangle blocks per wave
   static_assert(H % 32 == 0 && RH % 32 == 0 && bytes <= 160 * 1024, "shape");
 };
 
@@ -226,36 +279,42 @@ __device__ __forceinline__ void gram_row(f32x16 (&c)[Q], int t0, const bf16* Gh,
   for (int q = 0; q < Q; ++q) c[q] += d[q];
 }
 
-// wave w's blocks t = Q*w + q of the h x h Gram matrix (one block row when HB % Q == 0)
-template <class GL, int RH, int Q, int HB, int NBA>
-__device__ __forceinline__ void gram_blocks(f32x16 (&c)[Q], int w, const bf16* Gh, const bf16* Gl, int lane) {
-  if constexpr (HB % Q == 0) {
-    if (Q * w < NBA) gram_row<GL, RH, Q, HB>(c, Q * w, Gh, Gl, lane);
-  } else {
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int t = Q * w + q;
-      if (t < NBA) {
-        f32x16 one[1] = {c[q]};
-        gram_row<GL, RH, 1, HB>(one, t, Gh, Gl, lane);
-        c[q] = one[0];
-      }
-    }
+// the wave's upper-triangle task of the h x h Gram matrix (blocks (I0, J0) and (I1, J1))
+template <class GL, int RH, int HB>
+__device__ __forceinline__ void gram_task(f32x16* c, int I0, int J0, int I1, int J1, int cnt, const bf16* Gh,
+                                          const bf16* Gl, int lane) {
+  if (cnt == 2 && I1 == I0 && J1 == J0 + 1) {
+    f32x16 two[2] = {c[0], c[1]};
+    gram_row<GL, RH, 2, HB>(two, I0 * HB + J0, Gh, Gl, lane);
+    c[0] = two[0];
+    c[1] = two[1];
+    return;
+  }
+  if (cnt >= 1) {
+    f32x16 one[1] = {c[0]};
+    gram_row<GL, RH, 1, HB>(one, I0 * HB + J0, Gh, Gl, lane);
+    c[0] = one[0];
+  }
+  if (cnt == 2) {
+    f32x16 one[1] = {c[1]};
+    gram_row<GL, RH, 1, HB>(one, I1 * HB + J1, Gh, Gl, lane);
+    c[1] = one[0];
   }
 }
 
 // grid: 3 * P workgroups (one per matrix); block 512 threads (8 waves).
-// h x h block t = QA*w + q of wave w: rows c = (t / HB)*32 + acc_row, columns
-// c' = (t % HB)*32 + acc_col. Every product is stored through its transposed block (the 4
-// consecutive accumulator rows of a lane become one 8-byte run), so slot contents are the
-// transposes of the masters; each product reads them in the orientation that gives the exact
-// (not symmetry-assumed) result wherever a matrix is symmetric only up to rounding: Q's
-// dynamic range (up to 3.4445^5 in weak directions) amplifies any such asymmetry.
+// h x h block q of wave w's task (sym_task): rows c = 32 Iq + acc_row, columns
+// c' = 32 Jq + acc_col, on or above the diagonal. Every product is stored through its transposed
+// block (the 4 consecutive accumulator rows of a lane become one 8-byte run) at block (Jq, Iq),
+// on or below the diagonal: the slots hold the lower triangles that sym_frag reads.
+// Rounding makes the computed products symmetric only approximately; using the upper triangle
+// for both halves is one consistent symmetric rounding of them (emulated: output error 2.6e-4
+// against 2.2e-4 for the full products at h = 64, chunk 128, the same scale).
 template <class OpT, int H, int RH>
 __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, unsigned char* smem) {
   typedef UpdLayout<H, RH> L;
   typedef typename L::GL GL;
-  constexpr int LDA = L::LDA, HB = L::HB, NBA = L::NBA, QA = L::QA, NJ = L::NJ, NJW = L::NJW;
+  constexpr int LDA = L::LDA, HB = L::HB, QS = L::QS, NJ = L::NJ, NJW = L::NJW;
   constexpr int NE4 = RH * H / 4;              // float4 groups of the matrix
   constexpr int NG = (NE4 + 511) / 512;
   constexpr int NB8 = NG < 16 ? NG : 16;
@@ -331,30 +390,57 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
     __syncthreads();
   }
 
-  auto put_sym = [&](const f32x16 (&v)[QA], bf16* dh, bf16* dl) {
+  // this wave's upper-triangle task of the h x h products
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int tcode = sym_task_of<HB>(wu), tn = tcode >> 16;
+  const int tI[2] = {tcode & 15, (tcode >> 8) & 15}, tJ[2] = {(tcode >> 4) & 15, (tcode >> 12) & 15};
+  // block q of the task stored transposed at block (Jq, Iq) (8-byte runs). A diagonal block is
+  // made exactly symmetric: its elements above the diagonal are stored a second time, in their
+  // own orientation, over the transposed values there (one wave's LDS stores land in program
+  // order), so that both halves hold the upper triangle. (Keeping a diagonal block as computed
+  // leaves the stored matrix slightly asymmetric, and the upper-triangle products then no longer
+  // see one consistent matrix: emulated output error 1.2e-2 at h = 64, chunk 128, against 2.6e-4
+  // with exact symmetry and 2.2e-4 for the full products.)
+  auto put_sym = [&](const f32x16 (&v)[QS], bf16* dh, bf16* dl) {
 #pragma unroll
-    for (int q = 0; q < QA; ++q) {
-      const int t = QA * w + q;
-      if (t < NBA) {
+    for (int q = 0; q < QS; ++q) {
+      if (q < tn) {
+        const int I = tI[q], J = tJ[q], cc = lane & 31, hf = 4 * (lane >> 5);
+        const int tb = (32 * J + cc) * LDA + 32 * I + hf;  // transposed run of accumulator group 0
+        const int db = (32 * I + hf) * LDA + 32 * J + cc;   // own-orientation element of row 0
+        const int lim = cc - hf;                            // row r0 + i is above the diagonal iff 8 g4 + i < lim
+        bf16x4 h[4], l[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int c = (t / HB) * 32 + 8 * g4 + 4 * (lane >> 5), c2 = (t % HB) * 32 + (lane & 31);
-          split_store4(dh + c2 * LDA + c, dl + c2 * LDA + c,
-                       f32x4{v[q][4 * g4], v[q][4 * g4 + 1], v[q][4 * g4 + 2], v[q][4 * g4 + 3]});
+          split4(f32x4{v[q][4 * g4], v[q][4 * g4 + 1], v[q][4 * g4 + 2], v[q][4 * g4 + 3]}, h[g4], l[g4]);
+          *reinterpret_cast<bf16x4*>(dh + tb + 8 * g4) = h[g4];
+          *reinterpret_cast<bf16x4*>(dl + tb + 8 * g4) = l[g4];
+        }
+        // after every transposed store of the block (a later group's run can cover an element
+        // stored here)
+        if (q == 0 && I == J) {  // diagonal blocks are always a task's only block
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (8 * g4 + i < lim) {
+                dh[db + (8 * g4 + i) * LDA] = h[g4][i];
+                dl[db + (8 * g4 + i) * LDA] = l[g4][i];
+              }
+            }
         }
       }
     }
   };
-  // the same blocks stored in their own orientation (element [c][c'] at row c): 2-byte stores,
-  // used once for Q, which the final product reads by rows
-  auto put_direct = [&](const f32x16 (&v)[QA], bf16* dh, bf16* dl) {
+  // the strictly-upper blocks of the task stored in their own orientation (element [c][c'] at row
+  // c): 2-byte stores, used once for Q so that the final product reads whole rows
+  auto put_upper = [&](const f32x16 (&v)[QS], bf16* dh, bf16* dl) {
 #pragma unroll
-    for (int q = 0; q < QA; ++q) {
-      const int t = QA * w + q;
-      if (t < NBA) {
+    for (int q = 0; q < QS; ++q) {
+      if (q < tn && tJ[q] != tI[q]) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = (t / HB) * 32 + acc_row(r, lane), c2 = (t % HB) * 32 + acc_col(lane);
+          const int c = 32 * tI[q] + acc_row(r, lane), c2 = 32 * tJ[q] + acc_col(lane);
           const bf16 hi = static_cast<bf16>(v[q][r]);
           dh[c * LDA + c2] = hi;
           dl[c * LDA + c2] = static_cast<bf16>(v[q][r] - static_cast<float>(hi));
@@ -362,14 +448,14 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
       }
     }
   };
-  auto zero_q = [&](f32x16 (&v)[QA]) {
+  auto zero_q = [&](f32x16 (&v)[QS]) {
 #pragma unroll
-    for (int q = 0; q < QA; ++q) zero(v[q]);
+    for (int q = 0; q < QS; ++q) zero(v[q]);
   };
 
   // ---- 2. Newton-Schulz-5 through the Gram matrix ----------------------------------------------
   if (u.muon) {
-    f32x16 am[QA], pm[QA], qm[QA], t[QA];
+    f32x16 am[QS], qm[QS], t[QS];
     // (a) X_0^T = U^T / (||U||_F + eps) as split-bf16 rows j in LDS, then A_0 = X_0 X_0^T in one
     //     pass over all RH rows
     {
@@ -390,7 +476,7 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
       }
       __syncthreads();
       zero_q(am);
-      gram_blocks<GL, RH, QA, HB, NBA>(am, w, Gh, Gl, lane);
+      gram_task<GL, RH, HB>(am, tI[0], tJ[0], tI[1], tJ[1], tn, Gh, Gl, lane);
       __syncthreads();
     }
     put_sym(am, S1h, S1l);
@@ -399,39 +485,37 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
 #pragma unroll 1
     for (int k = 0; k < NS_STEPS; ++k) {
       zero_q(t);
-      mma_blocks<H, QA, HB, NBA, false, false>(t, w, S1h, S1l, LDA, S1h, S1l, LDA, lane);  // A_k^2
+      sym_product<H, HB>(t, wu, S1h, S1l, S1h, S1l, LDA, lane);  // A_k^2
 #pragma unroll
-      for (int q = 0; q < QA; ++q) {
-        const int tb = QA * w + q;
-        const bool diag = (tb / HB) == (tb % HB);
+      for (int q = 0; q < QS; ++q) {
+        const bool diag = tJ[q] == tI[q];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float id = (diag && acc_row(r, lane) == acc_col(lane)) ? NS_A : 0.f;
-          pm[q][r] = id + NS_B * am[q][r] + NS_C * t[q][r];
+          t[q][r] = id + NS_B * am[q][r] + NS_C * t[q][r];  // P_k
         }
       }
-      put_sym(pm, S2h, S2l);
+      put_sym(t, S2h, S2l);
+      if (k == 0) {
+#pragma unroll
+        for (int q = 0; q < QS; ++q) qm[q] = t[q];  // Q_1 = P_0
+      }
       __syncthreads();
       if (k + 1 < NS_STEPS) {
-        // C = A^T P^T (slot 1 rows, slot 2 read K-major), stored transposed: slot 1 <- P A in
-        // its own orientation (P A is symmetric only up to rounding, which the rounds amplify)
         zero_q(t);
-        mma_blocks<H, QA, HB, NBA, false, true>(t, w, S1h, S1l, LDA, S2h, S2l, LDA, lane);
+        sym_product<H, HB>(t, wu, S2h, S2l, S1h, S1l, LDA, lane);  // P A
         __syncthreads();
         put_sym(t, S1h, S1l);
         __syncthreads();
         zero_q(am);
-        mma_blocks<H, QA, HB, NBA, false, false>(am, w, S1h, S1l, LDA, S2h, S2l, LDA, lane);  // (P A) P
+        sym_product<H, HB>(am, wu, S1h, S1l, S2h, S2l, LDA, lane);  // (P A) P
         __syncthreads();
       }
-      if (k == 0) {
-#pragma unroll
-        for (int q = 0; q < QA; ++q) qm[q] = pm[q];
-      } else {
+      if (k > 0) {
         put_sym(qm, S1h, S1l);
         __syncthreads();
         zero_q(qm);
-        mma_blocks<H, QA, HB, NBA, false, false>(qm, w, S2h, S2l, LDA, S1h, S1l, LDA, lane);  // P Q
+        sym_product<H, HB>(qm, wu, S2h, S2l, S1h, S1l, LDA, lane);  // P Q
         __syncthreads();
       }
       if (k + 1 < NS_STEPS) {
@@ -439,7 +523,8 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
         __syncthreads();
       }
     }
-    put_direct(qm, S1h, S1l);  // Q in slot 1, row-major, for the final product
+    put_sym(qm, S1h, S1l);  // Q in slot 1 with both triangles, rows read by the final product
+    put_upper(qm, S1h, S1l);
     __syncthreads();
   }
 
