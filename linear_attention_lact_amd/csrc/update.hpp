@@ -345,31 +345,52 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
   f32x4 keep[KEEP ? NG : 1];
   {
     const int64_t seg_stride = (int64_t)s.P * 3 * n;
+    static_assert(NE4 % 512 == 0, "whole float4 groups per thread");
+    // The partials stream through NB8 loads per thread that stay in flight: each value is added
+    // and its register immediately reloaded with the same element of the next segment (after the
+    // last segment, of the momentum), so the loads of segment k + 1 overlap the sums of segment k.
+    // Sums in segment order, then v = momentum * M - sum, as the plain loop would form them.
 #pragma unroll 1
     for (int b0 = 0; b0 < NG; b0 += NB8) {
-      f32x4 g[NB8], mv[NB8];
+      f32x4 g[NB8], ld[NB8];
+      auto at = [&](int i) { return 4 * (tid + 512 * (b0 + i)); };
 #pragma unroll
       for (int i = 0; i < NB8; ++i) {
         g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mv[i] = g[i];
-        const int e4 = tid + 512 * (b0 + i);
-        if (mom && e4 < NE4) mv[i] = *reinterpret_cast<const f32x4*>(Mm + 4 * e4);
+        if (b0 + i < NG) ld[i] = *reinterpret_cast<const f32x4*>(part0 + at(i));
       }
-      for (int k = 0; k < u.S; ++k) {
+      for (int k = 0; k + 1 < u.S; ++k) {
+        const float* nx = part0 + (k + 1) * seg_stride;
 #pragma unroll
         for (int i = 0; i < NB8; ++i) {
-          const int e4 = tid + 512 * (b0 + i);
-          if (e4 < NE4) g[i] += *reinterpret_cast<const f32x4*>(part0 + k * seg_stride + 4 * e4);
+          if (b0 + i < NG) {
+            g[i] += ld[i];
+            ld[i] = *reinterpret_cast<const f32x4*>(nx + at(i));
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its use
         }
+      }
+      if (mom) {
+#pragma unroll
+        for (int i = 0; i < NB8; ++i) {
+          if (b0 + i < NG) {
+            g[i] += ld[i];
+            ld[i] = *reinterpret_cast<const f32x4*>(Mm + at(i));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NB8; ++i)
+          if (b0 + i < NG) g[i] += ld[i];
       }
 #pragma unroll
       for (int i = 0; i < NB8; ++i) {
-        const int e4 = tid + 512 * (b0 + i);
+        if (b0 + i >= NG) continue;
         f32x4 v = -g[i];
-        if (mom) v = u.momentum * mv[i] + v;
+        if (mom) v = u.momentum * ld[i] + v;
         if constexpr (KEEP) keep[i] = v;
-        if (e4 >= NE4) continue;
-        *reinterpret_cast<f32x4*>(Ud + 4 * e4) = v;
+        *reinterpret_cast<f32x4*>(Ud + at(i)) = v;
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
       }
     }
