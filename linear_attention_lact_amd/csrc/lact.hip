@@ -66,14 +66,10 @@ __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float
   *reinterpret_cast<f32x4*>(s.M + ((int64_t)pair * 3 + mat) * n + e) = sm;
   for (int buf = 0; buf < 2; ++buf) {
     OpT* sh = reinterpret_cast<OpT*>(s.sh) + ((int64_t)buf * s.P + pair) * 4 * n;
-    OpT* d = sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + e;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = Mfma<OpT>::from_f32(sv[q]);
-    if (mat == 1) {  // W1^T [h][rh]: row c0 + r, columns j0 + c4..
-      OpT* dt = sh + 3 * n + (int64_t)(c0 + r) * rh + j0 + c4;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dt[q] = Mfma<OpT>::from_f32(tw[c4 + q][r]);
-    }
+    store4(sh + (mat == 0 ? 0 : mat == 2 ? 1 : 2) * n + e, sv);
+    if (mat == 1)  // W1^T [h][rh]: row c0 + r, columns j0 + c4..
+      store4(sh + 3 * n + (int64_t)(c0 + r) * rh + j0 + c4,
+             f32x4{tw[c4][r], tw[c4 + 1][r], tw[c4 + 2][r], tw[c4 + 3][r]});
   }
 }
 
@@ -129,9 +125,12 @@ __global__ void __launch_bounds__(512) lact_update_apply_kernel(UpdateArgs u, Ap
 }
 
 // renorm targets (column norms of the initial row-form weights over their input axis).
-// grid (3, P), block 256; the row loop is unrolled so that eight loads are in flight.
+// grid (3, P), block 256. With fewer than 256 columns the rows split into rs = 256 / cols
+// stripes (when that divides them), one thread per (stripe, column), 16 loads in flight each;
+// the stripes' partial sums add in stripe order through LDS.
 __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const float* W0, const float* W1,
                                                         const float* W2, int H, int64_t w_batch_stride) {
+  __shared__ float part[256];
   const int mat = blockIdx.x, pair = blockIdx.y;
   const int h = s.h, rh = s.rh;
   const int64_t n = (int64_t)rh * h;
@@ -139,11 +138,29 @@ __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const floa
   const float* src = (mat == 0 ? W0 : mat == 1 ? W1 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
   float* nu = s.nu + ((int64_t)pair * 3 + mat) * s.NU;
   const int cols = mat == 1 ? h : rh, rows = mat == 1 ? rh : h;  // row-form [rows][cols]
-  for (int j = threadIdx.x; j < cols; j += 256) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < rows; ++r) acc += src[(int64_t)r * cols + j] * src[(int64_t)r * cols + j];
-    nu[j] = sqrtf(acc);
+  int rs = cols < 256 ? 256 / cols : 1;
+  while (rs > 1 && rows % rs) --rs;
+  if (rs == 1) {
+    for (int j = threadIdx.x; j < cols; j += 256) {
+      float acc = 0.f;
+#pragma unroll 16
+      for (int r = 0; r < rows; ++r) acc += src[(int64_t)r * cols + j] * src[(int64_t)r * cols + j];
+      nu[j] = sqrtf(acc);
+    }
+    return;
+  }
+  const int t = threadIdx.x, j = t % cols, g = t / cols, len = rows / rs;
+  float acc = 0.f;
+  if (g < rs) {
+#pragma unroll 16
+    for (int r = g * len; r < (g + 1) * len; ++r) acc += src[(int64_t)r * cols + j] * src[(int64_t)r * cols + j];
+  }
+  part[t] = acc;
+  __syncthreads();
+  if (t < cols) {
+    float tot = 0.f;
+    for (int q = 0; q < rs; ++q) tot += part[q * cols + t];
+    nu[t] = sqrtf(tot);
   }
 }
 

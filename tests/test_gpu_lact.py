@@ -70,6 +70,13 @@ CASES = [
                                                        chunk_kv=1024, muon=True, momentum=0.9), 16),
     ("bf16 h128 sgd 12 pairs", dict(B=3, H=4, h=128, Nq=2048, Nk=2048, chunk_q=1024, chunk_kv=1024,
                                                   momentum=0.5), 17),
+    # every (h, rh) instance of the LDS-resident Newton-Schulz update: its upper-triangle task
+    # tables differ at h = 32 (one block), 64 (three), 96 (six) and 128 (ten)
+    ("bf16 h32 r2 muon mom", dict(h=32, Nq=512, Nk=512, chunk_q=128, chunk_kv=128, muon=True, momentum=0.9), 18),
+    ("bf16 h32 r4 muon UA", dict(h=32, r=4, Nq=512, Nk=512, chunk_q=128, chunk_kv=128, muon=True, order=1), 19),
+    ("bf16 h64 r4 muon mom", dict(h=64, r=4, Nq=512, Nk=512, chunk_q=128, chunk_kv=128, muon=True, momentum=0.9), 20),
+    ("bf16 h96 r4 muon mom", dict(h=96, r=4, Nq=768, Nk=768, chunk_q=192, chunk_kv=192, muon=True, momentum=0.9), 21),
+    ("bf16 h96 r2 muon all", dict(h=96, Nq=768, Nk=768, chunk_q=192, chunk_kv=192, muon=True), 22),
 ]
 
 
