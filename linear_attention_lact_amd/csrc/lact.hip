@@ -29,15 +29,13 @@ namespace ttt {
 // With flags (reset mode, before chunk c): only the pairs whose sequence has TTT_CHUNK_RESET set
 // at chunk c return to the initial weights, with zero momentum (M_in is then null).
 template <class OpT>
-__global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float* W0, const float* W1,
-                                                       const float* W2, const float* M_in, int H,
-                                                       int64_t w_batch_stride, const uint8_t* flags, int nch,
-                                                       int c) {
+__device__ __forceinline__ void lact_init_tile(const LactState& s, const float* W0, const float* W1, const float* W2,
+                                               const float* M_in, int H, int64_t w_batch_stride,
+                                               const uint8_t* flags, int nch, int c, int tile, int mat, int pair) {
   __shared__ float tw[32][33], tm[32][33];
-  const int mat = blockIdx.y, pair = blockIdx.z;
   const int h = s.h, rh = s.rh, hb = h / 32;
   const int64_t n = (int64_t)rh * h;
-  const int j0 = (blockIdx.x / hb) * 32, c0 = (blockIdx.x % hb) * 32;
+  const int j0 = (tile / hb) * 32, c0 = (tile % hb) * 32;
   const int b = pair / H, head = pair % H;
   if (flags && !(flags[(int64_t)b * nch + c] & TTT_CHUNK_RESET)) return;
   const float* src = (mat == 0 ? W0 : mat == 1 ? W1 : W2) + (int64_t)b * w_batch_stride + (int64_t)head * n;
@@ -71,6 +69,14 @@ __global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float
       store4(sh + 3 * n + (int64_t)(c0 + r) * rh + j0 + c4,
              f32x4{tw[c4][r], tw[c4 + 1][r], tw[c4 + 2][r], tw[c4 + 3][r]});
   }
+}
+
+template <class OpT>
+__global__ void __launch_bounds__(256) lact_init_kernel(LactState s, const float* W0, const float* W1,
+                                                       const float* W2, const float* M_in, int H,
+                                                       int64_t w_batch_stride, const uint8_t* flags, int nch,
+                                                       int c) {
+  lact_init_tile<OpT>(s, W0, W1, W2, M_in, H, w_batch_stride, flags, nch, c, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Apply-only chunks (TTT_CHUNK_NO_UPDATE at chunk c): before the chunk's writes the state and
@@ -128,10 +134,9 @@ __global__ void __launch_bounds__(512) lact_update_apply_kernel(UpdateArgs u, Ap
 // grid (3, P), block 256. With fewer than 256 columns the rows split into rs = 256 / cols
 // stripes (when that divides them), one thread per (stripe, column), 16 loads in flight each;
 // the stripes' partial sums add in stripe order through LDS.
-__global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const float* W0, const float* W1,
-                                                        const float* W2, int H, int64_t w_batch_stride) {
+__device__ __forceinline__ void lact_norms_body(const LactState& s, const float* W0, const float* W1, const float* W2,
+                                                int H, int64_t w_batch_stride, int mat, int pair) {
   __shared__ float part[256];
-  const int mat = blockIdx.x, pair = blockIdx.y;
   const int h = s.h, rh = s.rh;
   const int64_t n = (int64_t)rh * h;
   const int b = pair / H, head = pair % H;
@@ -167,11 +172,10 @@ __global__ void __launch_bounds__(256) lact_norms_kernel(LactState s, const floa
 // power-of-two step-size scales of the gradient's token segments: for chunk c, pair p and
 // segment g, 2^-floor(log2(max eta)) over the segment's tokens and the nrow step-size rows
 // (one, or one per matrix; 1 when the maximum is 0). grid (P, nch), block 256; out [nch][P][S].
-__global__ void __launch_bounds__(256) lact_eta_scale_kernel(const float* eta, int64_t eta_pair_stride,
-                                                            int64_t row_stride, int nrow, int chunk, int seg_len,
-                                                            int S, float* out) {
+__device__ __forceinline__ void lact_eta_scale_body(const float* eta, int64_t eta_pair_stride, int64_t row_stride,
+                                                    int nrow, int chunk, int seg_len, int S, float* out, int pair,
+                                                    int c, int P) {
   __shared__ float red[16];
-  const int pair = blockIdx.x, c = blockIdx.y, P = gridDim.x;
   const float* ep = eta + pair * eta_pair_stride;
   for (int g = 0; g < S; ++g) {
     const int t0 = c * chunk + g * seg_len, t1 = min(t0 + seg_len, (c + 1) * chunk);
@@ -180,6 +184,32 @@ __global__ void __launch_bounds__(256) lact_eta_scale_kernel(const float* eta, i
       for (int t = t0 + threadIdx.x; t < t1; t += 256) mx = fmaxf(mx, ep[e * row_stride + t]);
     mx = block_max(mx, red);
     if (threadIdx.x == 0) out[((int64_t)c * P + pair) * S + g] = mx > 0.f ? exp2f(-floorf(log2f(mx))) : 1.f;
+  }
+}
+
+// The call's prologue in one launch: workgroups [0, G) build the initial state tiles
+// (lact_init_tile, G = tiles * 3 * P), the next 3 P the renorm targets (lact_norms_body), and the
+// last P * nch, when nch > 0, the gradient segments' step-size scales (lact_eta_scale_body).
+struct PrologueArgs {
+  const float* eta;
+  int64_t eta_pair_stride, row_stride;
+  int nrow, chunk, seg_len, S, nch;
+  float* out;
+};
+template <class OpT>
+__global__ void __launch_bounds__(256) lact_prologue_kernel(LactState s, const float* W0, const float* W1,
+                                                           const float* W2, const float* M_in, int H,
+                                                           int64_t w_batch_stride, int tiles, PrologueArgs e) {
+  const int P = s.P, bid = blockIdx.x, g = tiles * 3 * P;
+  if (bid < g) {
+    lact_init_tile<OpT>(s, W0, W1, W2, M_in, H, w_batch_stride, nullptr, 0, 0, bid % tiles, (bid / tiles) % 3,
+                        bid / (3 * tiles));
+  } else if (bid < g + 3 * P) {
+    lact_norms_body(s, W0, W1, W2, H, w_batch_stride, (bid - g) % 3, (bid - g) / 3);
+  } else {
+    const int b = bid - g - 3 * P;
+    lact_eta_scale_body(e.eta, e.eta_pair_stride, e.row_stride, e.nrow, e.chunk, e.seg_len, e.S, e.out, b % P,
+                        b / P, P);
   }
 }
 
@@ -266,14 +296,6 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const int P = s.P, rh = s.rh;
   const int64_t n = (int64_t)rh * H;
   const int nch = p.Nk / p.chunk_kv;
-  {
-    LaunchTimer lt(K_LACT_INIT, st);
-    hipLaunchKernelGGL(lact_init_kernel<OpT>, dim3((unsigned)(n / 1024), 3, P), dim3(256), 0, st, s, W0, W1,
-                       W2, M_in, p.H, p.w_batch_stride, nullptr, 0, 0);
-    TTT_HIP(hipGetLastError());
-    hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
-    TTT_HIP(hipGetLastError());
-  }
 
   // operand shadows, double-buffered: chunk c's gradient and apply read buffer c & 1 while its
   // update writes buffer (c + 1) & 1
@@ -308,10 +330,15 @@ static ttt_status lact_run(const ttt_lact_params& p, const LactState& s, int S, 
   const int ntile = (p.chunk_kv + TT - 1) / TT;
   const int tiles_per_seg = (ntile + S - 1) / S;
   ga.seg_len = tiles_per_seg * TT;
-  if (WS && nch > 0) {  // the role-split gradient kernel reads its segments' step-size scales
+  {
+    // initial state, renorm targets and (for the role-split gradient kernel, which reads them)
+    // the segments' step-size scales, in one launch
     LaunchTimer lt(K_LACT_INIT, st);
-    hipLaunchKernelGGL(lact_eta_scale_kernel, dim3((unsigned)P, (unsigned)nch), dim3(256), 0, st, eta,
-                       ga.eta_pair_stride, (int64_t)p.Nk, e3 ? 3 : 1, p.chunk_kv, ga.seg_len, S, s.esc);
+    const int ne = WS ? nch : 0;
+    const PrologueArgs pe{eta, ga.eta_pair_stride, (int64_t)p.Nk, e3 ? 3 : 1, p.chunk_kv, ga.seg_len, S, ne, s.esc};
+    const int tiles = (int)(n / 1024);
+    hipLaunchKernelGGL(lact_prologue_kernel<OpT>, dim3((unsigned)(tiles * 3 * P + 3 * P + P * ne)), dim3(256), 0,
+                       st, s, W0, W1, W2, M_in, p.H, p.w_batch_stride, tiles, pe);
     TTT_HIP(hipGetLastError());
   }
   ga.W0T = sh;
@@ -474,12 +501,10 @@ static ttt_status lact_run_large(const ttt_lact_params& p, const LactState& s, c
   const int nch = p.Nk / p.chunk_kv;
   {
     LaunchTimer lt(K_LACT_INIT, st);
-    hipLaunchKernelGGL(lact_init_kernel<f16>, dim3((unsigned)(n / 1024), 3, P), dim3(256), 0, st, s, W0, W1, W2,
-                       M_in, p.H, p.w_batch_stride, nullptr, 0, 0);
-    hipLaunchKernelGGL(lact_norms_kernel, dim3(3, P), dim3(256), 0, st, s, W0, W1, W2, p.H, p.w_batch_stride);
-    if (nch > 0)
-      hipLaunchKernelGGL(lact_eta_scale_kernel, dim3((unsigned)P, (unsigned)nch), dim3(256), 0, st, eta,
-                         (int64_t)p.Nk, (int64_t)p.Nk, 1, bk, bk, 1, s.esc);
+    const PrologueArgs pe{eta, (int64_t)p.Nk, (int64_t)p.Nk, 1, bk, bk, 1, nch, s.esc};
+    const int tiles = (int)(n / 1024);
+    hipLaunchKernelGGL(lact_prologue_kernel<f16>, dim3((unsigned)(tiles * 3 * P + 3 * P + P * nch)), dim3(256), 0,
+                       st, s, W0, W1, W2, M_in, p.H, p.w_batch_stride, tiles, pe);
     TTT_HIP(hipGetLastError());
   }
   auto gemm = [&](int epi, const f16* A, int64_t lda, const f16* B0, const f16* B1, int64_t ldb, int M, int N, int Kd,
