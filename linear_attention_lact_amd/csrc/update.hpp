@@ -453,22 +453,6 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
       }
     }
   };
-  // the strictly-upper blocks of the task stored in their own orientation (element [c][c'] at row
-  // c): 2-byte stores, used once for Q so that the final product reads whole rows
-  auto put_upper = [&](const f32x16 (&v)[QS], bf16* dh, bf16* dl) {
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      if (q < tn && tJ[q] != tI[q]) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 32 * tI[q] + acc_row(r, lane), c2 = 32 * tJ[q] + acc_col(lane);
-          const bf16 hi = static_cast<bf16>(v[q][r]);
-          dh[c * LDA + c2] = hi;
-          dl[c * LDA + c2] = static_cast<bf16>(v[q][r] - static_cast<float>(hi));
-        }
-      }
-    }
-  };
   auto zero_q = [&](f32x16 (&v)[QS]) {
 #pragma unroll
     for (int q = 0; q < QS; ++q) zero(v[q]);
@@ -544,8 +528,7 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
         __syncthreads();
       }
     }
-    put_sym(qm, S1h, S1l);  // Q in slot 1 with both triangles, rows read by the final product
-    put_upper(qm, S1h, S1l);
+    put_sym(qm, S1h, S1l);  // Q in slot 1, read by rows in the final product
     __syncthreads();
   }
 
@@ -588,8 +571,16 @@ __device__ __forceinline__ void lact_update_body(const UpdateArgs& u, int mi, un
           for (int st = 0; st < KS; ++st) {
 #pragma unroll
             for (int cb = 0; cb < HB; ++cb) {
-              const int qo = (32 * cb + (lane & 31)) * LDA + 16 * st + 8 * (lane >> 5);
-              const bf16x8 qh = Mfma<bf16>::load(S1h + qo), ql = Mfma<bf16>::load(S1l + qo);
+              // rows of Q from its lower-triangle storage (cb and st are constants here)
+              bf16x8 qh, ql;
+              if (st / 2 <= cb) {
+                const int qo = (32 * cb + (lane & 31)) * LDA + 16 * st + 8 * (lane >> 5);
+                qh = Mfma<bf16>::load(S1h + qo);
+                ql = Mfma<bf16>::load(S1l + qo);
+              } else {
+                qh = load_frag_tr<bf16>(S1h + 32 * cb, LDA, 16 * st, lane);
+                ql = load_frag_tr<bf16>(S1l + 32 * cb, LDA, 16 * st, lane);
+              }
               if constexpr (RJ) {
                 wn[x][cb] = Mfma<bf16>::mma(uh[st], qh, wn[x][cb]);
                 dd[cb] = Mfma<bf16>::mma(uh[st], ql, dd[cb]);
